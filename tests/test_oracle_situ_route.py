@@ -1,0 +1,111 @@
+"""Pins of the oracle's SiTU-GLU and router.
+
+SiTU: "Kimi K3 engine (c/kimi_k3.c)", "Architecture notes":
+h = 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25). The identities below hold for that
+formula only: a swapped constant, a sigmoid of -g or a dropped factor breaks
+one of them.
+
+Router: same section (sigmoid scores, score-correction bias, top-16 on the
+biased scores, weights = raw scores renormalised) and "kimi-k3-in-c" README,
+"Three invariants" (the bias steers selection only).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.conftest import read_table
+
+GU = [(-30.0, 7.0), (-3.0, -2.0), (-0.5, 40.0), (0.25, 0.1), (1.0, -1.0), (2.5, 12.0), (9.0, 100.0)]
+
+
+@pytest.mark.parametrize("g,u", GU)
+def test_situ_odd_even_parts(g, u):
+    hp = oracle.situ(g, u)
+    hm = oracle.situ(-g, u)
+    # sigmoid(g) + sigmoid(-g) = 1  =>  h(g) - h(-g) = 100 tanh(g/4) tanh(u/25)
+    assert math.isclose(hp - hm, 100 * math.tanh(g / 4) * math.tanh(u / 25), rel_tol=1e-13, abs_tol=1e-300)
+    # sigmoid(g) - sigmoid(-g) = tanh(g/2)  =>  h(g) + h(-g) = 100 tanh(g/4) tanh(g/2) tanh(u/25)
+    assert math.isclose(hp + hm, 100 * math.tanh(g / 4) * math.tanh(g / 2) * math.tanh(u / 25),
+                        rel_tol=1e-12, abs_tol=1e-13)
+    # odd in u
+    assert oracle.situ(g, -u) == -hp
+
+
+def test_situ_zeros_and_limits():
+    assert oracle.situ(0.0, 3.0) == 0.0
+    assert oracle.situ(3.0, 0.0) == 0.0
+    # g -> +inf: 4 * 1 * 1 * 25 tanh(u/25); g, u -> +inf: 100
+    assert math.isclose(oracle.situ(200.0, 25.0), 100 * math.tanh(1.0), rel_tol=1e-15)
+    assert oracle.situ(1e3, 1e4) == 100.0
+    # g -> -inf: the sigmoid kills it
+    assert abs(oracle.situ(-200.0, 25.0)) < 1e-80
+
+
+def test_bias_fixture():
+    rows = read_table("route_bias_fixture.txt")
+    bias = np.array([0, 0, 0, 0, 0, 0, 0.5, 0.9], np.float32)
+    logits, want_b, want_u, want_w = [], [], [], []
+    for r in rows:
+        a, b, c, d = r.split("|")
+        logits.append([float(v) for v in a.split()])
+        want_b.append([int(v) for v in b.split()])
+        want_u.append([int(v) for v in c.split()])
+        want_w.append([float(v) for v in d.split()])
+    logits = np.array(logits)
+    idx, wts, _ = oracle.route_select(logits, bias, 2)
+    assert np.array_equal(idx, np.array(want_b))
+    # wts are float32: within half an ulp of the 9-digit values
+    assert np.allclose(wts, np.array(want_w), rtol=0, atol=6e-8)
+    idx0, _, _ = oracle.route_select(logits, np.zeros(8, np.float32), 2)
+    assert np.array_equal(idx0, np.array(want_u))
+    # the bias reorders the selection on five of the six rows
+    assert sum(not np.array_equal(a, b) for a, b in zip(idx, idx0)) == 5
+
+
+def test_zero_bias_selects_top_logits_and_weights_ignore_bias():
+    W, b = synth.router(21, 896, 256, 0.1)
+    x = synth.activations(21, 8, 256)
+    lg = oracle.route_logits(x, W)
+    idx0, w0, _ = oracle.route_select(lg, np.zeros(896, np.float32), 16)
+    for t in range(8):
+        order = np.lexsort((np.arange(896), -lg[t]))[:16]
+        assert np.array_equal(idx0[t], order)
+    assert np.allclose(w0.sum(1), 1.0, atol=1e-6)
+    idx, w, bsel = oracle.route_select(lg, b, 16)
+    # descending biased score
+    assert np.all(np.diff(bsel, axis=1) <= 0)
+    # weights: the unbiased sigmoid scores of the selected set, renormalised
+    sig = 1.0 / (1.0 + np.exp(-lg))
+    for t in range(8):
+        sc = sig[t, idx[t]]
+        assert np.allclose(w[t], sc / sc.sum(), rtol=1e-6, atol=0)
+        # the same selection with another bias gives the same weights
+    idx2, w2, _ = oracle.route_select(lg, b * 0, 16)
+    same = [t for t in range(8) if set(idx2[t]) == set(idx[t])]
+    for t in same:
+        assert np.allclose(np.sort(w2[t]), np.sort(w[t]), rtol=1e-7)
+
+
+def test_logits_fixed_order_and_exactness():
+    rng = np.random.default_rng(5)
+    # integer inputs: every partial sum is exact, so any order gives the same value
+    W = rng.integers(-50, 51, size=(30, 77)).astype(np.float32)
+    x = rng.integers(-50, 51, size=(3, 77)).astype(np.float32)
+    lg = oracle.route_logits(x, W)
+    assert np.array_equal(lg, x.astype(np.float64) @ W.astype(np.float64).T)
+    # random floats: products exact in double, so within a few ulp of the exact sum
+    W, _ = synth.router(9, 64, 3584, 0.1)
+    x = synth.activations(9, 2, 3584)
+    lg = oracle.route_logits(x, W)
+    ref = x.astype(np.float64) @ W.astype(np.float64).T
+    assert np.all(np.abs(lg - ref) <= 1e-13 * (np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T))
+    # the documented four-accumulator order, checked on a case where order matters
+    w = np.array([1e16, 1.0, -1e16, 1.0, 1.0], np.float32)
+    xv = np.ones((1, 5), np.float32)
+    # a0 = 1e16(+tail 1.0 later), a1 = 1, a2 = -1e16, a3 = 1 -> (a0+a1)+(a2+a3) = 0 in double, then + 1
+    got = oracle.route_logits(xv, w[None, :])[0, 0]
+    a0, a1, a2, a3 = float(np.float32(1e16)), 1.0, -float(np.float32(1e16)), 1.0
+    assert got == ((a0 + a1) + (a2 + a3)) + 1.0
