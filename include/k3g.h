@@ -1,0 +1,224 @@
+/*
+ * k3g.h -- C ABI of libk3g, the MI355X (gfx950) routed-expert MXFP4 library.
+ *
+ * Sources of the operations (pages, with their sections):
+ *   [KIC-README]  "kimi-k3-in-c" README (spark.entire.vc tools page)
+ *   [KIC-ARTICLE] "kimi-k3-in-c: 2.78 trillion parameters, one CPU, 8 GB of RAM"
+ *   [COLIBRI-K3]  "Kimi K3 engine (c/kimi_k3.c)" (colibri docs)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer (HBM of the current HIP device)
+ *    unless its comment says host. The caller owns all memory: weights,
+ *    inputs, outputs and workspace. The library allocates nothing and keeps
+ *    no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on `stream` and returns without
+ *    synchronising. Results are valid once the stream reaches that point.
+ *  - Arguments are validated on the host before anything is enqueued. A call
+ *    that fails validation returns a negative k3g_status and enqueues
+ *    nothing. Asynchronous device faults surface at the caller's next sync.
+ *  - Preconditions that cannot be checked without a device sync are stated
+ *    next to each call (e.g. idx values in [0, n_experts)).
+ *  - Re-entrant. Calls that overlap on the device (other streams) must use
+ *    distinct workspaces and outputs.
+ *  - No dimension has a default: a zero or negative size where a positive
+ *    one is needed is K3G_EINVAL ([KIC-README] "2. The config reader that
+ *    refuses to guess": an absent field is an error, never a default).
+ *
+ * MXFP4 matrix layout ([COLIBRI-K3] "Weights"; [KIC-ARTICLE] "Reduction one")
+ * --------------------------------------------------------------------------
+ *  W [rows x in], in a multiple of 32, is two row-major byte arrays:
+ *    packed [rows][in/2]: e2m1 codes, two per byte, the LOW nibble is the even
+ *                         column; bit 3 of a code is its sign;
+ *    scales [rows][in/32]: one ue8m0 byte s per 32 columns;
+ *  element value w = e2m1(code) * 2^(s-127); a group whose scale byte is 255
+ *  contributes nothing. The weights are read in this form; nothing expands
+ *  them to floats in HBM.
+ */
+#ifndef K3G_H
+#define K3G_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    K3G_OK = 0,
+    K3G_EINVAL = -1,       /* null pointer, bad size, bad enum, overlapping in/out */
+    K3G_EALIGN = -2,       /* a pointer misses its required alignment            */
+    K3G_ENOSPACE = -3,     /* workspace smaller than k3g_workspace_bytes()        */
+    K3G_EHIP = -4,         /* a HIP launch or runtime call failed                 */
+    K3G_EUNSUPPORTED = -5  /* shape beyond what the kernels handle, or not gfx950 */
+} k3g_status;
+
+/* EXACT: fp32 activations, exact e2m1 products, fp32 accumulation.
+ * IDOT:  activations quantised per 32-group to int8, int32 group dots on the
+ *        matrix cores ([COLIBRI-K3] "Streaming design", K3_IDOT). */
+typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
+
+typedef struct {
+    const uint8_t *packed; /* [rows][in/2], 16-byte aligned */
+    const uint8_t *scales; /* [rows][in/32]                 */
+    int32_t rows, in;
+} k3g_mxfp4;
+
+/* One routed expert: w1 (gate) and w3 (up) [inter x latent], w2 (down)
+ * [latent x inter]. Which of w1/w3 is the gate is not stated on the pages;
+ * w1 = gate is this library's reading. */
+typedef struct {
+    k3g_mxfp4 w1, w3, w2;
+} k3g_expert;
+
+/* A bank of experts resident in HBM. Expert e's six tensors are at
+ * base + e*stride + off[i], i = w1 packed, w1 scales, w3 packed, w3 scales,
+ * w2 packed, w2 scales (the pages store an expert's six tensors back to back,
+ * [COLIBRI-K3] "Streaming design"). k3g_bank_layout() gives the packing this
+ * library recommends; any offsets with 16-byte aligned packed tensors work. */
+typedef struct {
+    const uint8_t *base;
+    int64_t stride;
+    int32_t n_experts, latent, inter;
+    int64_t off[6];
+} k3g_expert_bank;
+
+/* Dense bf16 weights of the LatentMoE block ([COLIBRI-K3] "Architecture
+ * notes"): down [latent x hidden], up [hidden x latent], gamma [latent]
+ * (fp32), shared experts w1/w3 [sh_inter x hidden] and w2 [hidden x sh_inter],
+ * router [n_experts x hidden] fp32 and bias [n_experts] fp32. bf16 tensors
+ * are uint16 bit patterns, row-major, 16-byte aligned. */
+typedef struct {
+    const float *w_router, *bias;
+    const uint16_t *w_down, *w_up;
+    const float *gamma;
+    const uint16_t *sh_w1[2], *sh_w3[2], *sh_w2[2];
+    int32_t n_shared, hidden, sh_inter;
+    float rms_eps;
+    k3g_expert_bank bank;
+} k3g_block_weights;
+
+/* Operation codes for the workspace queries. */
+typedef enum {
+    K3G_OP_EXPERT_GLU = 1,
+    K3G_OP_MOE_ROUTE = 2,
+    K3G_OP_MOE_LAYER = 3,
+    K3G_OP_LATENT_BLOCK = 4
+} k3g_op;
+
+/* Sizes that fix a workspace. Fields an op does not use are ignored:
+ * EXPERT_GLU uses latent, inter, mode; MOE_ROUTE uses n_tokens, n_experts;
+ * MOE_LAYER adds top_k, latent, inter, mode; LATENT_BLOCK uses all. */
+typedef struct {
+    int32_t n_tokens, top_k, n_experts, latent, inter, hidden, sh_inter, mode;
+} k3g_shape;
+
+/* Byte offsets of the regions of a workspace, for the stage-by-stage checks
+ * of a test (0 = region absent; every region is 256-byte aligned). P =
+ * n_tokens * top_k pairs, sorted by (expert, token).
+ *   logits  double [T][n_experts]        router logits
+ *   counts  int32 [n_experts]            pairs per expert
+ *   offsets int32 [n_experts+1]          exclusive prefix sum of counts
+ *   perm    int32 [P]                    sorted position -> pair id t*top_k+k
+ *   inv     int32 [P]                    pair id -> sorted position
+ *   active  int32 [n_experts+1]          [0] = number of experts with pairs, then their ids ascending
+ *   xq, xs  int8 [T][latent], float [T][latent/32]   IDOT activations
+ *   h       float [P][inter]             SiTU output per sorted pair
+ *   hq, hs  int8 [P][inter], float [P][inter/32]      IDOT h
+ *   ypair   float [P][latent]            expert output per sorted pair, unweighted
+ *   idx, wts int32/float [T][top_k]      block routing
+ *   lat, agg, nrm  float [T][latent]     block stages
+ *   shh     float [T][sh_inter]          block shared-expert SiTU output
+ *   layer   the MoE layer's own workspace inside the block's */
+typedef struct {
+    size_t total;
+    size_t logits, counts, offsets, perm, inv, active;
+    size_t xq, xs, h, hq, hs, ypair;
+    size_t idx, wts, lat, agg, nrm, shh, layer;
+} k3g_ws_layout;
+
+/* Human-readable name of a status code (static storage). */
+const char *k3g_status_string(int status);
+
+/* Library version string and the device architecture it was built for. */
+const char *k3g_version(void);
+
+/* The recommended bank packing for experts of the given shape: six tensors
+ * back to back, each 256-byte aligned. Writes off[6] and *stride (host
+ * pointers). Returns K3G_OK or K3G_EINVAL. */
+int k3g_bank_layout(int latent, int inter, int64_t off[6], int64_t *stride);
+
+/* Workspace size in bytes for `op` at these sizes (0 when the arguments are
+ * invalid), and the region offsets within it (host pointers). */
+size_t k3g_workspace_bytes(int op, const k3g_shape *shape);
+int k3g_workspace_layout(k3g_ws_layout *out, int op, const k3g_shape *shape);
+
+/* ---- the hot path ------------------------------------------------------ */
+
+/* y[r] = sum_g [s_rg != 255] 2^(s_rg-127) * sum_{j in g} e2m1(n_rj) * x_j
+ * for one activation vector (batch 1): the pages' k3_matmul_mxfp4, same
+ * argument order ([KIC-ARTICLE] "Reduction one"). y fp32 [rows], x fp32 [in].
+ * group must be 32; in a positive multiple of 32; rows >= 1; packed 16-byte
+ * aligned; x 16-byte and y 4-byte aligned; y must not overlap x. fp32
+ * accumulation. */
+int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed,
+                   const uint8_t *scales, int in, int rows, int group, void *stream);
+
+/* One expert on one token: g = w1 x, u = w3 x, h = 4 tanh(g/4) sigmoid(g)
+ * 25 tanh(u/25) (SiTU-GLU, [COLIBRI-K3] "Architecture notes"), y = w2 h.
+ * y, x fp32 [latent], 16-byte aligned. In IDOT mode x and h are quantised per
+ * 32-group to int8 first. ws: k3g_workspace_bytes(K3G_OP_EXPERT_GLU, ...) bytes,
+ * 256-byte aligned. */
+int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Stable LatentMoE routing ([COLIBRI-K3] "Architecture notes"; [KIC-README]
+ * "Three invariants", 3): logit = W_router x (double accumulation),
+ * score = sigmoid(logit), biased = score + bias; the top_k experts by biased
+ * score, largest first, equal scores to the lower id; wts = scores of the
+ * selected experts / their sum. idx int32 [T][top_k], wts fp32 [T][top_k],
+ * x fp32 [T][in], w_router fp32 [n_experts][in], bias fp32 [n_experts].
+ * 1 <= top_k <= min(n_experts, 64); n_experts <= 4096. */
+int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_router,
+                  const float *bias, int n_tokens, int in, int n_experts, int top_k,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* The MoE layer for given routing: y[t] = sum_k wts[t][k] * E_{idx[t][k]}(x_t)
+ * with each expert a SiTU-GLU. Pairs are sorted by expert id so each selected
+ * expert's weights stream from HBM once for all of its tokens ([COLIBRI-K3]
+ * "Chunked prefill": each unique expert of a chunk is loaded once); the
+ * weighted combine runs in k order per token. y, x fp32 [T][latent]; idx,
+ * wts [T][top_k] as k3g_moe_route writes them. Precondition: idx values in
+ * [0, bank->n_experts) (not checked on the device). */
+int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts,
+                  const k3g_expert_bank *bank, int n_tokens, int top_k, int mode,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* The full LatentMoE block ([COLIBRI-K3] "Architecture notes"): route on x,
+ * lat = W_down x, agg = layer(lat), n = RMSNorm(agg) * gamma, out = W_up n +
+ * sum_s W2_s SiTU(W1_s x, W3_s x). out, x fp32 [T][hidden]. top_k as above. */
+int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w,
+                         int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* ---- stage hooks used by the bit-exact checks ----------------------------- */
+
+/* Per row and 32-group: s = max|x|/127 (fp32), q = rint(x/s) clamped to
+ * [-127, 127] with fp32 division and ties to even; max|x| = 0 gives s = 0,
+ * q = 0. q int8 [n_rows][in], s fp32 [n_rows][in/32]. */
+int k3g_quantize_i8_groups(int8_t *q, float *s, const float *x, int n_rows, int in,
+                           void *stream);
+
+/* Integer group sums of the IDOT product, computed on the matrix cores:
+ * sums[t][r][g] = sum_{j in g} q[t][j] * 2*e2m1(n_rj), int32 [T][rows][in/32].
+ * q int8 [T][in]. */
+int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed,
+                             int in, int rows, int n_tokens, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3G_H */

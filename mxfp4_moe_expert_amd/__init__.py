@@ -1,0 +1,310 @@
+"""Python binding of libk3g, the MI355X (gfx950) routed-expert MXFP4 library.
+
+Argument marshalling only: every function here checks dtypes, devices and
+contiguity of torch tensors, passes their device pointers and the current HIP
+stream to the C ABI declared in include/k3g.h, and raises K3GError on a
+non-zero status. All arithmetic runs in the library's HIP kernels; there is no
+fallback of any kind. PyTorch provides device memory and streams.
+
+The names match the C entry points: k3g_mxfp4_gemv, k3g_expert_glu,
+k3g_moe_route, k3g_moe_layer, k3g_latent_moe_block, k3g_quantize_i8_groups,
+k3g_mxfp4_idot_groupsums.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libk3g.so")
+
+EXACT = 0
+IDOT = 1
+OP_EXPERT_GLU = 1
+OP_MOE_ROUTE = 2
+OP_MOE_LAYER = 3
+OP_LATENT_BLOCK = 4
+GROUP = 32
+
+
+class K3GError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class Mxfp4(C.Structure):
+    _fields_ = [("packed", C.c_void_p), ("scales", C.c_void_p), ("rows", C.c_int32), ("in_", C.c_int32)]
+
+
+class Expert(C.Structure):
+    _fields_ = [("w1", Mxfp4), ("w3", Mxfp4), ("w2", Mxfp4)]
+
+
+class ExpertBank(C.Structure):
+    _fields_ = [("base", C.c_void_p), ("stride", C.c_int64), ("n_experts", C.c_int32),
+                ("latent", C.c_int32), ("inter", C.c_int32), ("off", C.c_int64 * 6)]
+
+
+class BlockWeights(C.Structure):
+    _fields_ = [("w_router", C.c_void_p), ("bias", C.c_void_p), ("w_down", C.c_void_p),
+                ("w_up", C.c_void_p), ("gamma", C.c_void_p), ("sh_w1", C.c_void_p * 2),
+                ("sh_w3", C.c_void_p * 2), ("sh_w2", C.c_void_p * 2), ("n_shared", C.c_int32),
+                ("hidden", C.c_int32), ("sh_inter", C.c_int32), ("rms_eps", C.c_float),
+                ("bank", ExpertBank)]
+
+
+class Shape(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in
+                ("n_tokens", "top_k", "n_experts", "latent", "inter", "hidden", "sh_inter", "mode")]
+
+
+_WS_FIELDS = ("total", "logits", "counts", "offsets", "perm", "inv", "active", "xq", "xs", "h", "hq",
+              "hs", "ypair", "idx", "wts", "lat", "agg", "nrm", "shh", "layer")
+
+
+class WsLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in _WS_FIELDS]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libk3g. Raises if the library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libk3g.so is not built ({LIB_PATH}); run "
+                              "`python -c 'import __graft_entry__ as g; g.build()'` first")
+        L = C.CDLL(LIB_PATH)
+        P, i, sz = C.c_void_p, C.c_int, C.c_size_t
+        L.k3g_status_string.restype = C.c_char_p
+        L.k3g_status_string.argtypes = [i]
+        L.k3g_version.restype = C.c_char_p
+        L.k3g_version.argtypes = []
+        L.k3g_bank_layout.argtypes = [i, i, P, P]
+        L.k3g_workspace_bytes.restype = sz
+        L.k3g_workspace_bytes.argtypes = [i, P]
+        L.k3g_workspace_layout.argtypes = [P, i, P]
+        L.k3g_mxfp4_gemv.argtypes = [P, P, P, P, i, i, i, P]
+        L.k3g_expert_glu.argtypes = [P, P, P, i, P, sz, P]
+        L.k3g_moe_route.argtypes = [P, P, P, P, P, i, i, i, i, P, sz, P]
+        L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
+        L.k3g_latent_moe_block.argtypes = [P, P, P, i, i, i, P, sz, P]
+        L.k3g_quantize_i8_groups.argtypes = [P, P, P, i, i, P]
+        L.k3g_mxfp4_idot_groupsums.argtypes = [P, P, P, i, i, i, P]
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise K3GError(fn, rc, lib().k3g_status_string(rc).decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def version() -> str:
+    return lib().k3g_version().decode()
+
+
+def bank_layout(latent: int, inter: int):
+    """(offsets[6], stride) of the recommended expert packing."""
+    off = (C.c_int64 * 6)()
+    stride = C.c_int64()
+    _check("k3g_bank_layout", lib().k3g_bank_layout(latent, inter, off, C.byref(stride)))
+    return list(off), stride.value
+
+
+def shape(n_tokens=0, top_k=0, n_experts=0, latent=0, inter=0, hidden=0, sh_inter=0, mode=EXACT) -> Shape:
+    return Shape(n_tokens, top_k, n_experts, latent, inter, hidden, sh_inter, mode)
+
+
+def workspace_bytes(op: int, sh: Shape) -> int:
+    return int(lib().k3g_workspace_bytes(op, C.byref(sh)))
+
+
+def workspace_layout(op: int, sh: Shape) -> dict:
+    L = WsLayout()
+    _check("k3g_workspace_layout", lib().k3g_workspace_layout(C.byref(L), op, C.byref(sh)))
+    return {n: getattr(L, n) for n in _WS_FIELDS}
+
+
+def workspace(op: int, sh: Shape, device="cuda") -> torch.Tensor:
+    """A uint8 device tensor of the size the op needs (256-byte aligned by the allocator)."""
+    n = workspace_bytes(op, sh)
+    if n == 0:
+        raise ValueError("invalid workspace shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mxfp4(packed: torch.Tensor, scales: torch.Tensor) -> Mxfp4:
+    _dev(packed, torch.uint8, "packed")
+    _dev(scales, torch.uint8, "scales")
+    rows, half = packed.shape
+    if scales.shape != (rows, half * 2 // GROUP):
+        raise ValueError("scales must be [rows, in/32]")
+    return Mxfp4(packed.data_ptr(), scales.data_ptr(), rows, half * 2)
+
+
+def expert_struct(ex: dict) -> Expert:
+    return Expert(mxfp4(ex["w1p"], ex["w1s"]), mxfp4(ex["w3p"], ex["w3s"]), mxfp4(ex["w2p"], ex["w2s"]))
+
+
+def bank_struct(base: torch.Tensor, n_experts: int, latent: int, inter: int, off=None, stride=None) -> ExpertBank:
+    _dev(base, torch.uint8, "bank")
+    if off is None:
+        off, stride = bank_layout(latent, inter)
+    if base.numel() < stride * n_experts:
+        raise ValueError("bank tensor too small")
+    return ExpertBank(base.data_ptr(), stride, n_experts, latent, inter, (C.c_int64 * 6)(*off))
+
+
+# ---- entry points ----------------------------------------------------------
+
+def k3g_mxfp4_gemv(y: torch.Tensor, x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                   group: int = GROUP, stream=None) -> torch.Tensor:
+    _dev(y, torch.float32, "y")
+    _dev(x, torch.float32, "x")
+    _dev(packed, torch.uint8, "packed")
+    _dev(scales, torch.uint8, "scales")
+    rows, half = packed.shape
+    if x.numel() != half * 2 or y.numel() != rows:
+        raise ValueError("shape mismatch")
+    _check("k3g_mxfp4_gemv", lib().k3g_mxfp4_gemv(_ptr(y), _ptr(x), _ptr(packed), _ptr(scales),
+                                                   half * 2, rows, group, _stream(stream)))
+    return y
+
+
+def k3g_expert_glu(y: torch.Tensor, x: torch.Tensor, ex: dict, mode: int, ws: torch.Tensor,
+                   stream=None) -> torch.Tensor:
+    _dev(y, torch.float32, "y")
+    _dev(x, torch.float32, "x")
+    _dev(ws, torch.uint8, "ws")
+    e = expert_struct(ex)
+    _check("k3g_expert_glu", lib().k3g_expert_glu(_ptr(y), _ptr(x), C.byref(e), mode, _ptr(ws),
+                                                   ws.numel(), _stream(stream)))
+    return y
+
+
+def k3g_moe_route(idx: torch.Tensor, wts: torch.Tensor, x: torch.Tensor, w_router: torch.Tensor,
+                  bias: torch.Tensor, top_k: int, ws: torch.Tensor, stream=None):
+    _dev(idx, torch.int32, "idx")
+    _dev(wts, torch.float32, "wts")
+    _dev(x, torch.float32, "x")
+    _dev(w_router, torch.float32, "w_router")
+    _dev(bias, torch.float32, "bias")
+    _dev(ws, torch.uint8, "ws")
+    T, n_in = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != n_in or bias.numel() != E or idx.shape != (T, top_k) or wts.shape != (T, top_k):
+        raise ValueError("shape mismatch")
+    _check("k3g_moe_route", lib().k3g_moe_route(_ptr(idx), _ptr(wts), _ptr(x), _ptr(w_router), _ptr(bias),
+                                                 T, n_in, E, top_k, _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, wts
+
+
+def k3g_moe_layer(y: torch.Tensor, x: torch.Tensor, idx: torch.Tensor, wts: torch.Tensor,
+                  bank: ExpertBank, mode: int, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    _dev(y, torch.float32, "y")
+    _dev(x, torch.float32, "x")
+    _dev(idx, torch.int32, "idx")
+    _dev(wts, torch.float32, "wts")
+    _dev(ws, torch.uint8, "ws")
+    T, latent = x.shape
+    K = idx.shape[1]
+    if latent != bank.latent or y.shape != x.shape or wts.shape != idx.shape or idx.shape[0] != T:
+        raise ValueError("shape mismatch")
+    _check("k3g_moe_layer", lib().k3g_moe_layer(_ptr(y), _ptr(x), _ptr(idx), _ptr(wts), C.byref(bank),
+                                                 T, K, mode, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def k3g_latent_moe_block(out: torch.Tensor, x: torch.Tensor, w: BlockWeights, top_k: int, mode: int,
+                         ws: torch.Tensor, stream=None) -> torch.Tensor:
+    _dev(out, torch.float32, "out")
+    _dev(x, torch.float32, "x")
+    _dev(ws, torch.uint8, "ws")
+    T = x.shape[0]
+    _check("k3g_latent_moe_block", lib().k3g_latent_moe_block(_ptr(out), _ptr(x), C.byref(w), T, top_k, mode,
+                                                               _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def k3g_quantize_i8_groups(q: torch.Tensor, s: torch.Tensor, x: torch.Tensor, stream=None):
+    _dev(q, torch.int8, "q")
+    _dev(s, torch.float32, "s")
+    _dev(x, torch.float32, "x")
+    n, n_in = x.shape
+    if q.shape != x.shape or s.shape != (n, n_in // GROUP):
+        raise ValueError("shape mismatch")
+    _check("k3g_quantize_i8_groups", lib().k3g_quantize_i8_groups(_ptr(q), _ptr(s), _ptr(x), n, n_in,
+                                                                   _stream(stream)))
+    return q, s
+
+
+def k3g_mxfp4_idot_groupsums(sums: torch.Tensor, q: torch.Tensor, packed: torch.Tensor, stream=None):
+    _dev(sums, torch.int32, "sums")
+    _dev(q, torch.int8, "q")
+    _dev(packed, torch.uint8, "packed")
+    T, n_in = q.shape
+    rows = packed.shape[0]
+    if packed.shape[1] * 2 != n_in or sums.shape != (T, rows, n_in // GROUP):
+        raise ValueError("shape mismatch")
+    _check("k3g_mxfp4_idot_groupsums", lib().k3g_mxfp4_idot_groupsums(_ptr(sums), _ptr(q), _ptr(packed), n_in,
+                                                                       rows, T, _stream(stream)))
+    return sums
+
+
+# ---- bank packing (data placement only) -------------------------------------
+
+def pack_bank(experts, n_experts: int, latent: int, inter: int, device="cuda", threads: int = 16):
+    """Place experts' six byte arrays at the library's recommended offsets.
+
+    `experts` is a callable e -> dict(w1p, w1s, w3p, w3s, w2p, w2s) of uint8
+    numpy arrays. Returns (bank uint8 device tensor, ExpertBank struct). The
+    host staging buffer is pinned; experts are produced by a thread pool.
+    """
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    off, stride = bank_layout(latent, inter)
+    keys = ("w1p", "w1s", "w3p", "w3s", "w2p", "w2s")
+    host = torch.empty(n_experts * stride, dtype=torch.uint8, pin_memory=(device != "cpu"))
+    hv = host.numpy()
+
+    def fill(e):
+        ex = experts(e)
+        base = e * stride
+        for k, o in zip(keys, off):
+            a = np.ascontiguousarray(ex[k], dtype=np.uint8).ravel()
+            hv[base + o: base + o + a.size] = a
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        list(pool.map(fill, range(n_experts)))
+    dev = host.to(device, non_blocking=False)
+    del host
+    return dev, bank_struct(dev, n_experts, latent, inter, off, stride)

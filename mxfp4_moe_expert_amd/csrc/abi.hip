@@ -1,0 +1,340 @@
+// abi.hip -- the extern "C" entry points of libk3g: validation, workspace
+// layout, and the launch sequence of each operation. No entry point
+// allocates, synchronises or copies to the host.
+#include <stdio.h>
+#include <string.h>
+
+#include "k3g_common.h"
+
+namespace k3g {
+// launchers (gemv.hip, route.hip, idot.hip)
+int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows, hipStream_t st);
+int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
+                        const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, hipStream_t st);
+int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
+                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                          hipStream_t st);
+int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
+                   int latent, hipStream_t st);
+int launch_logits(double *logits, const float *x, const float *W, int T, int in, int E, hipStream_t st);
+int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K, hipStream_t st);
+int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
+                  int T, int K, int E, hipStream_t st);
+int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, hipStream_t st);
+int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed, int in, int rows, int n_tokens,
+                          hipStream_t st);
+int launch_moe_up_idot(float *h, const int8_t *xq, const float *xs, const BankDev &bank, const int32_t *active,
+                       const int32_t *offsets, const int32_t *perm, int top_k, int latent, int inter, int max_slots,
+                       hipStream_t st);
+int launch_moe_down_idot(float *ypair, const int8_t *hq, const float *hs, const BankDev &bank, const int32_t *active,
+                         const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                         hipStream_t st);
+}  // namespace k3g
+
+using namespace k3g;
+
+namespace {
+
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxTopK = 64;
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// The library is built for gfx950 only; refuse other devices once per device.
+int check_device() {
+    static int cached[64];  // 0 unknown, 1 ok, -1 not gfx950
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return K3G_EHIP;
+    if (dev < 0 || dev >= 64) return K3G_EUNSUPPORTED;
+    if (cached[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return K3G_EHIP;
+        cached[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return cached[dev] == 1 ? K3G_OK : K3G_EUNSUPPORTED;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Carver {
+    size_t cur = 0;
+    size_t take(size_t bytes) {
+        if (bytes == 0) return 0;
+        cur = align_up(cur, 256);
+        const size_t at = cur;
+        cur += bytes;
+        return at;
+    }
+};
+
+bool shape_ok_layer(const k3g_shape &s) {
+    return s.n_tokens >= 0 && s.top_k >= 1 && s.top_k <= kMaxTopK && s.n_experts >= 1 &&
+           s.n_experts <= kMaxExperts && s.top_k <= s.n_experts && s.latent > 0 && s.inter > 0 &&
+           s.latent % kGroup == 0 && s.inter % kGroup == 0 && (s.mode == K3G_EXACT || s.mode == K3G_IDOT);
+}
+
+// Regions are laid out from offset 256 so that 0 can mean "absent".
+int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
+    memset(o, 0, sizeof *o);
+    Carver c;
+    c.cur = 256;
+    const size_t T = (size_t)(s.n_tokens > 0 ? s.n_tokens : 0);
+    switch (op) {
+        case K3G_OP_EXPERT_GLU: {
+            if (s.latent <= 0 || s.inter <= 0 || s.latent % kGroup || s.inter % kGroup ||
+                (s.mode != K3G_EXACT && s.mode != K3G_IDOT))
+                return K3G_EINVAL;
+            o->h = c.take(sizeof(float) * s.inter);
+            if (s.mode == K3G_IDOT) {
+                o->xq = c.take((size_t)s.latent);
+                o->xs = c.take(sizeof(float) * (s.latent / kGroup));
+                o->hq = c.take((size_t)s.inter);
+                o->hs = c.take(sizeof(float) * (s.inter / kGroup));
+            }
+            break;
+        }
+        case K3G_OP_MOE_ROUTE: {
+            if (s.n_tokens < 0 || s.n_experts < 1 || s.n_experts > kMaxExperts) return K3G_EINVAL;
+            o->logits = c.take(sizeof(double) * T * s.n_experts);
+            break;
+        }
+        case K3G_OP_MOE_LAYER:
+        case K3G_OP_LATENT_BLOCK: {
+            if (!shape_ok_layer(s)) return K3G_EINVAL;
+            const size_t P = T * s.top_k, E = s.n_experts;
+            if (op == K3G_OP_LATENT_BLOCK) {
+                if (s.hidden <= 0 || s.sh_inter <= 0 || s.hidden % kGroup || s.sh_inter % kGroup) return K3G_EINVAL;
+                o->logits = c.take(sizeof(double) * T * E);
+                o->idx = c.take(sizeof(int32_t) * P);
+                o->wts = c.take(sizeof(float) * P);
+                o->lat = c.take(sizeof(float) * T * s.latent);
+                o->agg = c.take(sizeof(float) * T * s.latent);
+                o->nrm = c.take(sizeof(float) * T * s.latent);
+                o->shh = c.take(sizeof(float) * T * s.sh_inter);
+            }
+            o->counts = c.take(sizeof(int32_t) * E);
+            o->offsets = c.take(sizeof(int32_t) * (E + 1));
+            o->perm = c.take(sizeof(int32_t) * (P ? P : 1));
+            o->inv = c.take(sizeof(int32_t) * (P ? P : 1));
+            o->active = c.take(sizeof(int32_t) * (E + 1));
+            o->h = c.take(sizeof(float) * (P ? P : 1) * s.inter);
+            o->ypair = c.take(sizeof(float) * (P ? P : 1) * s.latent);
+            if (s.mode == K3G_IDOT) {
+                o->xq = c.take((T ? T : 1) * (size_t)s.latent);
+                o->xs = c.take(sizeof(float) * (T ? T : 1) * (s.latent / kGroup));
+                o->hq = c.take((P ? P : 1) * (size_t)s.inter);
+                o->hs = c.take(sizeof(float) * (P ? P : 1) * (s.inter / kGroup));
+            }
+            o->layer = 0;
+            break;
+        }
+        default:
+            return K3G_EINVAL;
+    }
+    o->total = align_up(c.cur, 256);
+    return K3G_OK;
+}
+
+inline hipStream_t S(void *stream) { return (hipStream_t)stream; }
+
+BankDev bank_dev(const k3g_expert_bank &b) {
+    BankDev d;
+    d.base = b.base;
+    d.stride = b.stride;
+    for (int i = 0; i < 6; ++i) d.off[i] = b.off[i];
+    return d;
+}
+
+#define K3G_TRY(expr)               \
+    do {                            \
+        const int rc_ = (expr);     \
+        if (rc_ != K3G_OK) return rc_; \
+    } while (0)
+
+int mxfp4_ok(const uint8_t *packed, const uint8_t *scales, int in, int rows) {
+    if (!packed || !scales || in <= 0 || rows < 1 || in % kGroup) return K3G_EINVAL;
+    if (!aligned(packed, 16)) return K3G_EALIGN;
+    if (in / kGroup > 256) return K3G_EUNSUPPORTED;  // x must fit a wavefront's registers
+    return K3G_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *k3g_status_string(int status) {
+    switch (status) {
+        case K3G_OK: return "ok";
+        case K3G_EINVAL: return "invalid argument";
+        case K3G_EALIGN: return "misaligned pointer";
+        case K3G_ENOSPACE: return "workspace too small";
+        case K3G_EHIP: return "HIP error";
+        case K3G_EUNSUPPORTED: return "unsupported shape or device";
+        default: return "unknown status";
+    }
+}
+
+const char *k3g_version(void) { return "k3g 0.1 (gfx950)"; }
+
+int k3g_bank_layout(int latent, int inter, int64_t off[6], int64_t *stride) {
+    if (!off || !stride || latent <= 0 || inter <= 0 || latent % kGroup || inter % kGroup) return K3G_EINVAL;
+    Carver c;
+    const size_t up_p = (size_t)inter * latent / 2, up_s = (size_t)inter * (latent / kGroup);
+    const size_t dn_p = (size_t)latent * inter / 2, dn_s = (size_t)latent * (inter / kGroup);
+    off[0] = (int64_t)c.take(up_p);
+    off[1] = (int64_t)c.take(up_s);
+    off[2] = (int64_t)c.take(up_p);
+    off[3] = (int64_t)c.take(up_s);
+    off[4] = (int64_t)c.take(dn_p);
+    off[5] = (int64_t)c.take(dn_s);
+    *stride = (int64_t)align_up(c.cur, 256);
+    return K3G_OK;
+}
+
+size_t k3g_workspace_bytes(int op, const k3g_shape *shape) {
+    if (!shape) return 0;
+    k3g_ws_layout o;
+    return layout(&o, op, *shape) == K3G_OK ? o.total : 0;
+}
+
+int k3g_workspace_layout(k3g_ws_layout *out, int op, const k3g_shape *shape) {
+    if (!out || !shape) return K3G_EINVAL;
+    return layout(out, op, *shape);
+}
+
+int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
+                   int group, void *stream) {
+    if (!y || !x || group != kGroup) return K3G_EINVAL;
+    K3G_TRY(mxfp4_ok(packed, scales, in, rows));
+    if (!aligned(x, 16) || !aligned(y, 4)) return K3G_EALIGN;
+    if (overlap(y, sizeof(float) * rows, x, sizeof(float) * in)) return K3G_EINVAL;
+    K3G_TRY(check_device());
+    return launch_gemv(y, x, packed, scales, in, rows, S(stream));
+}
+
+int k3g_quantize_i8_groups(int8_t *q, float *s, const float *x, int n_rows, int in, void *stream) {
+    if (!q || !s || !x || n_rows < 0 || in <= 0 || in % kGroup) return K3G_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return K3G_EALIGN;
+    K3G_TRY(check_device());
+    return launch_quant_i8(q, s, x, n_rows, in, S(stream));
+}
+
+int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed, int in, int rows, int n_tokens,
+                             void *stream) {
+    if (!sums || !q || !packed || in <= 0 || in % kGroup || rows < 1 || n_tokens < 0) return K3G_EINVAL;
+    if (!aligned(packed, 16) || !aligned(q, 16) || !aligned(sums, 4)) return K3G_EALIGN;
+    K3G_TRY(check_device());
+    return launch_idot_groupsums(sums, q, packed, in, rows, n_tokens, S(stream));
+}
+
+int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void *ws, size_t ws_bytes,
+                   void *stream) {
+    if (!y || !x || !e || !ws) return K3G_EINVAL;
+    const int latent = e->w1.in, inter = e->w1.rows;
+    if (e->w3.in != latent || e->w3.rows != inter || e->w2.in != inter || e->w2.rows != latent) return K3G_EINVAL;
+    K3G_TRY(mxfp4_ok(e->w1.packed, e->w1.scales, latent, inter));
+    K3G_TRY(mxfp4_ok(e->w3.packed, e->w3.scales, latent, inter));
+    K3G_TRY(mxfp4_ok(e->w2.packed, e->w2.scales, inter, latent));
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return K3G_EALIGN;
+    if (overlap(y, sizeof(float) * latent, x, sizeof(float) * latent)) return K3G_EINVAL;
+    k3g_shape s = {1, 1, 1, latent, inter, 0, 0, mode};
+    k3g_ws_layout L;
+    K3G_TRY(layout(&L, K3G_OP_EXPERT_GLU, s));
+    if (ws_bytes < L.total) return K3G_ENOSPACE;
+    K3G_TRY(check_device());
+    // the expert as a one-expert bank: offsets relative to w1's packed bytes
+    BankDev b;
+    b.base = e->w1.packed;
+    b.stride = 0;
+    b.off[W1P] = 0;
+    b.off[W1S] = e->w1.scales - e->w1.packed;
+    b.off[W3P] = e->w3.packed - e->w1.packed;
+    b.off[W3S] = e->w3.scales - e->w1.packed;
+    b.off[W2P] = e->w2.packed - e->w1.packed;
+    b.off[W2S] = e->w2.scales - e->w1.packed;
+    char *w = (char *)ws;
+    float *h = (float *)(w + L.h);
+    hipStream_t st = S(stream);
+    if (mode == K3G_EXACT) {
+        K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, st));
+        return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, st);
+    }
+    int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
+    float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
+    K3G_TRY(launch_quant_i8(xq, xs, x, 1, latent, st));
+    K3G_TRY(launch_moe_up_idot(h, xq, xs, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, st));
+    K3G_TRY(launch_quant_i8(hq, hs, h, 1, inter, st));
+    return launch_moe_down_idot(y, hq, hs, b, nullptr, nullptr, nullptr, latent, inter, 1, st);
+}
+
+int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_router, const float *bias, int n_tokens,
+                  int in, int n_experts, int top_k, void *ws, size_t ws_bytes, void *stream) {
+    if (!idx || !wts || !x || !w_router || !bias || !ws) return K3G_EINVAL;
+    if (n_tokens < 0 || in <= 0 || n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > kMaxTopK ||
+        top_k > n_experts)
+        return K3G_EINVAL;
+    if (!aligned(x, 4) || !aligned(w_router, 4) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
+        return K3G_EALIGN;
+    k3g_shape s = {n_tokens, top_k, n_experts, 0, 0, 0, 0, 0};
+    k3g_ws_layout L;
+    K3G_TRY(layout(&L, K3G_OP_MOE_ROUTE, s));
+    if (ws_bytes < L.total) return K3G_ENOSPACE;
+    K3G_TRY(check_device());
+    double *logits = (double *)((char *)ws + L.logits);
+    hipStream_t st = S(stream);
+    K3G_TRY(launch_logits(logits, x, w_router, n_tokens, in, n_experts, st));
+    return launch_topk(idx, wts, logits, bias, n_tokens, n_experts, top_k, st);
+}
+
+int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts, const k3g_expert_bank *bank,
+                  int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes, void *stream) {
+    if (!y || !x || !idx || !wts || !bank || !bank->base || !ws) return K3G_EINVAL;
+    const int latent = bank->latent, inter = bank->inter, E = bank->n_experts;
+    k3g_shape s = {n_tokens, top_k, E, latent, inter, 0, 0, mode};
+    k3g_ws_layout L;
+    K3G_TRY(layout(&L, K3G_OP_MOE_LAYER, s));
+    if (ws_bytes < L.total) return K3G_ENOSPACE;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
+        return K3G_EALIGN;
+    if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
+    for (int i = 0; i < 6; i += 2)
+        if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
+    if (overlap(y, sizeof(float) * n_tokens * latent, x, sizeof(float) * n_tokens * latent) && n_tokens > 0)
+        return K3G_EINVAL;
+    K3G_TRY(check_device());
+    if (n_tokens == 0) return K3G_OK;
+    char *w = (char *)ws;
+    int32_t *counts = (int32_t *)(w + L.counts), *offsets = (int32_t *)(w + L.offsets);
+    int32_t *perm = (int32_t *)(w + L.perm), *inv = (int32_t *)(w + L.inv), *active = (int32_t *)(w + L.active);
+    float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
+    const int P = n_tokens * top_k;
+    const int max_slots = P < E ? P : E;
+    const BankDev b = bank_dev(*bank);
+    hipStream_t st = S(stream);
+    K3G_TRY(launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st));
+    if (mode == K3G_EXACT) {
+        K3G_TRY(launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P, st));
+        K3G_TRY(launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots, st));
+    } else {
+        int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
+        float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
+        K3G_TRY(launch_quant_i8(xq, xs, x, n_tokens, latent, st));
+        K3G_TRY(launch_moe_up_idot(h, xq, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st));
+        K3G_TRY(launch_quant_i8(hq, hs, h, P, inter, st));
+        K3G_TRY(launch_moe_down_idot(ypair, hq, hs, b, active, offsets, perm, latent, inter, max_slots, st));
+    }
+    return launch_combine(y, ypair, wts, inv, n_tokens, top_k, latent, st);
+}
+
+}  // extern "C"
+
+extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w, int n_tokens, int top_k,
+                                    int mode, void *ws, size_t ws_bytes, void *stream) {
+    (void)out; (void)x; (void)w; (void)n_tokens; (void)top_k; (void)mode; (void)ws; (void)ws_bytes; (void)stream;
+    return K3G_EUNSUPPORTED;
+}

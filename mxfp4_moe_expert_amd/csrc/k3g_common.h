@@ -1,0 +1,125 @@
+// k3g_common.h -- device helpers shared by the libk3g kernels (gfx950 only).
+//
+// Format facts used here ("Kimi K3 engine (c/kimi_k3.c)", section "Weights";
+// "kimi-k3-in-c: 2.78 trillion parameters, one CPU, 8 GB of RAM", section
+// "Reduction one"): e2m1 codes two per byte, low nibble = even column, bit 3 =
+// sign; one ue8m0 scale per 32 columns, w = v * 2^(s-127), scale 255 skips
+// the group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "k3g.h"
+
+namespace k3g {
+
+constexpr int kGroup = 32;          // columns per scale
+constexpr int kWave = 64;           // CDNA wavefront
+constexpr int kLutSlots = 64;       // LUT copies: one per lane, so no bank conflicts
+constexpr int kLutWords = 256 * kLutSlots;  // 64 KB of LDS
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int16_t_v __attribute__((ext_vector_type(16)));
+
+// Expert bank as the kernels see it: tensor i of expert e at base + e*stride + off[i].
+struct BankDev {
+    const uint8_t *base;
+    int64_t stride;
+    int64_t off[6];
+};
+
+enum { W1P = 0, W1S = 1, W3P = 2, W3S = 3, W2P = 4, W2S = 5 };
+
+// Value of an e2m1 code from its bit fields: sign bit 3, exponent bits 2..1
+// (bias 1), mantissa bit 0; exponent 0 is subnormal (0 or 0.5).
+__host__ __device__ constexpr float e2m1_value(unsigned c) {
+    const float mag = ((c >> 1) & 3u) == 0
+                          ? 0.5f * float(c & 1u)
+                          : float(1u << (((c >> 1) & 3u) - 1u)) * (1.0f + 0.5f * float(c & 1u));
+    return (c & 8u) ? -mag : mag;
+}
+
+// The byte-pair LUT: byte -> two f16 values (low half = even column = low
+// nibble, high half = odd column = high nibble). e2m1 values are exact in f16.
+// Stored 64 times interleaved (word e*64 + lane) so that each lane reads its own
+// bank: data-dependent indices never conflict.
+__device__ inline void build_pair_lut(uint32_t *lut) {
+    for (int i = threadIdx.x; i < kLutWords; i += blockDim.x) {
+        const unsigned b = unsigned(i) >> 6;
+        half2_t v;
+        v.x = (_Float16)e2m1_value(b & 15u);
+        v.y = (_Float16)e2m1_value(b >> 4);
+        lut[i] = __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// LDS byte address of byte k (0..3) of word w in this lane's LUT copy:
+// (byte << 8) | (lane << 2), built with one v_perm_b32.
+__device__ inline uint32_t lut_addr(uint32_t w, uint32_t lane_off, int k) {
+    return __builtin_amdgcn_perm(w, lane_off, 0x0C0C0000u | ((4u + (uint32_t)k) << 8));
+}
+
+__device__ inline half2_t lut_read(const uint32_t *lut, uint32_t addr) {
+    return __builtin_bit_cast(half2_t, *(const uint32_t *)((const char *)lut + addr));
+}
+
+// Sum of one group of 32 columns: 16 packed bytes (a uint4) against x[0..31].
+// Two accumulators (even and odd columns), combined at the end. fp32 FMAs with
+// the exact f16 weight widened inside the instruction (v_fma_mix_f32).
+__device__ inline float group_dot(const uint32_t *lut, uint32_t lane_off, uint4 w, const float *xg) {
+    float a0 = 0.f, a1 = 0.f;
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const half2_t v = lut_read(lut, lut_addr(d[q], lane_off, b));
+            a0 = __builtin_fmaf((float)v.x, xg[q * 8 + b * 2], a0);
+            a1 = __builtin_fmaf((float)v.y, xg[q * 8 + b * 2 + 1], a1);
+        }
+    }
+    return a0 + a1;
+}
+
+// Apply one group's ue8m0 scale: 2^(s-127) * sub, or nothing for s = 255.
+__device__ inline float apply_scale(float sub, uint32_t s) {
+    return s == 255u ? 0.0f : __builtin_ldexpf(sub, int(s) - 127);
+}
+
+// Full-wavefront sum, returned in every lane: DPP within each row of 16 lanes,
+// then the four row sums read out of lanes 0, 16, 32, 48.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float wave_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ inline double wave_sum_f64(double v) {
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// SiTU-GLU ("Kimi K3 engine (c/kimi_k3.c)", "Architecture notes"):
+// 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25), in fp32.
+__device__ inline float situ(float g, float u) {
+    const float sig = 1.0f / (1.0f + expf(-g));
+    return 4.0f * tanhf(g * 0.25f) * sig * (25.0f * tanhf(u / 25.0f));
+}
+
+__device__ inline uint4 load16(const uint8_t *p) { return *(const uint4 *)p; }
+
+}  // namespace k3g

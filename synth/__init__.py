@@ -5,7 +5,7 @@ decoding of nibbles, no scaling, no products): it produces raw bytes and
 floats with the shapes and distributions of the workloads, and both the GPU
 path and the CPU oracle consume exactly the same arrays.
 
-Every tensor is drawn from its own PCG64 stream keyed by
+Every tensor is drawn from its own PCG64-DXSM stream keyed by
 ``SeedSequence([seed, tensor_id, index])``, so any expert of a bank can be
 regenerated on its own, in any order, by any process.
 
@@ -47,8 +47,8 @@ _T_MISC = 11
 
 
 def rng(seed: int, *keys: int) -> np.random.Generator:
-    """Independent PCG64 stream for (seed, keys...)."""
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), *map(int, keys)])))
+    """Independent PCG64-DXSM stream for (seed, keys...)."""
+    return np.random.Generator(np.random.PCG64DXSM(np.random.SeedSequence([int(seed), *map(int, keys)])))
 
 
 def normal_f32(seed: int, shape, scale: float = 1.0, key: int = 0) -> np.ndarray:
@@ -63,8 +63,10 @@ def activations(seed: int, n_tokens: int, width: int = LATENT, key: int = 0) -> 
 
 
 def nibble_bytes(g: np.random.Generator, n: int) -> np.ndarray:
-    """n bytes uniform over 0..255, so both nibbles are uniform over the 16 codes."""
-    return np.frombuffer(g.bytes(n), dtype=np.uint8).copy()
+    """n bytes uniform over 0..255, so both nibbles are uniform over the 16 codes
+    (the raw 64-bit outputs of the generator, read as bytes)."""
+    words = g.bit_generator.random_raw((n + 7) // 8)
+    return words.view(np.uint8)[:n].copy()
 
 
 def scale_bytes(g: np.random.Generator, n: int, lo: int = 118, hi: int = 132,

@@ -1,0 +1,80 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched):
+the library loads, exports every function include/k3g.h declares, lays out
+banks and workspaces as documented, and rejects bad arguments before it
+touches a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "k3g.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(k3g_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def k3g():
+    import mxfp4_moe_expert_amd as k
+    return k
+
+
+def test_exports_every_declared_symbol(k3g):
+    L = k3g.lib()
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"libk3g.so does not export {n}"
+
+
+def test_bank_layout_matches_census(k3g):
+    off, stride = k3g.bank_layout(3584, 3072)
+    # six tensors back to back, 256-byte aligned; 17,547,264 bytes per expert
+    assert off == [0, 5505024, 5849088, 11354112, 11698176, 17203200]
+    assert stride == 17547264
+    assert all(o % 256 == 0 for o in off)
+
+
+def test_workspace_layout(k3g):
+    sh = k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584, inter=3072, mode=k3g.IDOT)
+    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
+    P = 4096 * 16
+    regions = {"counts": 896 * 4, "offsets": 897 * 4, "perm": P * 4, "inv": P * 4, "active": 897 * 4,
+               "h": P * 3072 * 4, "ypair": P * 3584 * 4, "xq": 4096 * 3584, "xs": 4096 * 112 * 4,
+               "hq": P * 3072, "hs": P * 96 * 4}
+    spans = sorted((L[n], L[n] + sz) for n, sz in regions.items())
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0, "regions overlap"
+    assert all(L[n] % 256 == 0 and L[n] > 0 for n in regions)
+    assert spans[-1][1] <= L["total"] == k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh)
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=1, top_k=0, n_experts=8,
+                                                            latent=64, inter=64)) == 0
+
+
+def test_rejects_bad_arguments_before_any_launch(k3g):
+    L = k3g.lib()
+    P = C.c_void_p
+    fake = P(256)  # never dereferenced: validation fails first
+    # group != 32, in % 32 != 0, rows < 1, null pointers
+    assert L.k3g_mxfp4_gemv(fake, fake, fake, fake, 64, 8, 16, None) == -1
+    assert L.k3g_mxfp4_gemv(fake, fake, fake, fake, 48, 8, 32, None) == -1
+    assert L.k3g_mxfp4_gemv(fake, fake, fake, fake, 64, 0, 32, None) == -1
+    assert L.k3g_mxfp4_gemv(None, fake, fake, fake, 64, 8, 32, None) == -1
+    # misaligned packed bytes
+    assert L.k3g_mxfp4_gemv(fake, fake, P(257), fake, 64, 8, 32, None) == -2
+    # y overlapping x
+    assert L.k3g_mxfp4_gemv(P(4096), P(4096 + 16), fake, fake, 64, 8, 32, None) == -1
+    # routing: top_k outside 1..n_experts
+    assert L.k3g_moe_route(fake, fake, fake, fake, fake, 1, 64, 8, 9, fake, 1 << 20, None) == -1
+    assert L.k3g_moe_route(fake, fake, fake, fake, fake, 1, 64, 8, 0, fake, 1 << 20, None) == -1
+    # routing: workspace too small
+    assert L.k3g_moe_route(fake, fake, fake, fake, fake, 4, 64, 8, 2, fake, 16, None) == -3
+    # layer: workspace too small / bad mode
+    bank = k3g.ExpertBank(4096, 4096, 8, 64, 64, (C.c_int64 * 6)(0, 2048, 2304, 4352, 4608, 6656))
+    assert L.k3g_moe_layer(fake, fake, fake, fake, C.byref(bank), 2, 2, 0, fake, 16, None) == -3
+    assert L.k3g_moe_layer(fake, fake, fake, fake, C.byref(bank), 2, 2, 7, fake, 1 << 24, None) == -1
+    assert L.k3g_status_string(-3) == b"workspace too small"

@@ -1,0 +1,290 @@
+"""GPU parity of the EXACT path against the oracle (through the C ABI).
+
+Bar: fp32 outputs within 1e-5 * sum_j |W_ij||a_j| of the oracle (a = the
+stage input the oracle saw); routing indices bit-exact, weights within 1e-6
+relative. Composite results are checked stage by stage from the workspace
+regions include/k3g.h documents.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import REL, ExpertSource, assert_norm_close, situ_tolerance
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def k3g():
+    import mxfp4_moe_expert_amd as k
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    k.lib()
+    return k
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ---- single matrix ------------------------------------------------------------
+
+GEMV_CASES = [
+    # rows, in, scale range, p255 -- several tiles, ragged tails, every groups-per-lane variant
+    (1, 32, 118, 132, 0.0),
+    (37, 96, 118, 132, 0.05),
+    (300, 2048, 110, 140, 0.01),
+    (513, 3584, 118, 132, 0.001),
+    (64, 4096, 118, 132, 0.01),
+    (129, 8192, 118, 132, 0.01),
+    (3072, 3584, 118, 132, 0.001),  # w1/w3 shape
+    (3584, 3072, 118, 132, 0.001),  # w2 shape
+]
+
+
+@pytest.mark.parametrize("rows,n_in,lo,hi,p", GEMV_CASES)
+def test_gemv_matches_oracle(k3g, rows, n_in, lo, hi, p):
+    print(f"gemv rows={rows} in={n_in}", flush=True)
+    pk, sc = synth.mxfp4_matrix(1000 + rows, 1, 0, rows, n_in, lo, hi, p)
+    x = synth.activations(1000 + rows, 1, n_in)[0]
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    k3g.k3g_mxfp4_gemv(y, dev(x), dev(pk), dev(sc))
+    yo, _, nrm = oracle.mxfp4_gemv(x, pk, sc, full=True)
+    assert_norm_close(host(y), yo, nrm, what=f"gemv {rows}x{n_in}")
+
+
+def test_gemv_edge_cases(k3g):
+    rows, n_in = 70, 256
+    pk, sc = synth.mxfp4_matrix(77, 1, 0, rows, n_in, 118, 132, 0.0)
+    x = synth.activations(77, 1, n_in)[0]
+    sc[5, :] = 255                        # an all-255 row gives exactly 0
+    sc[6, 2] = 255                        # one skipped group
+    x_bad = x.copy()
+    sc[7, 1] = 255
+    x_bad[32:64] = np.inf                 # non-finite x inside a skipped group of row 7 only
+    pk[8, :] = 0x88                       # -0 everywhere: exactly 0
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    k3g.k3g_mxfp4_gemv(y, dev(x), dev(pk), dev(sc))
+    yo, _, nrm = oracle.mxfp4_gemv(x, pk, sc, full=True)
+    yg = host(y)
+    assert yg[5] == 0.0 and yg[8] == 0.0
+    assert_norm_close(yg, yo, nrm)
+    # the scale-255 group is dropped, not multiplied by zero
+    y2 = torch.empty(1, dtype=torch.float32, device="cuda")
+    k3g.k3g_mxfp4_gemv(y2, dev(x_bad), dev(pk[7:8].copy()), dev(sc[7:8].copy()))
+    yo2, _, n2 = oracle.mxfp4_gemv(x_bad, pk[7:8], sc[7:8], full=True)
+    assert np.isfinite(host(y2)).all()
+    assert_norm_close(host(y2), yo2, n2)
+    # flipping every sign bit negates exactly
+    yn = torch.empty(rows, dtype=torch.float32, device="cuda")
+    k3g.k3g_mxfp4_gemv(yn, dev(x), dev(pk ^ np.uint8(0x88)), dev(sc))
+    assert np.array_equal(host(yn), -yg)
+
+
+def test_gemv_deterministic(k3g):
+    pk, sc = synth.mxfp4_matrix(5, 1, 0, 3072, 3584)
+    x = dev(synth.activations(5, 1, 3584)[0])
+    a = torch.empty(3072, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    P, S = dev(pk), dev(sc)
+    k3g.k3g_mxfp4_gemv(a, x, P, S)
+    k3g.k3g_mxfp4_gemv(b, x, P, S)
+    assert torch.equal(a, b)
+
+
+# ---- one expert -----------------------------------------------------------------
+
+def check_glu(k3g, ex, x, latent, inter, ws=None):
+    exd = {k: dev(v) for k, v in ex.items()}
+    y = torch.empty(latent, dtype=torch.float32, device="cuda")
+    sh = k3g.shape(latent=latent, inter=inter, mode=k3g.EXACT)
+    if ws is None:
+        ws = k3g.workspace(k3g.OP_EXPERT_GLU, sh)
+    L = k3g.workspace_layout(k3g.OP_EXPERT_GLU, sh)
+    k3g.k3g_expert_glu(y, dev(x), exd, k3g.EXACT, ws)
+    yg = host(y)
+    hg = host(ws[L["h"]:L["h"] + 4 * inter].view(torch.float32))
+    # stage 1: h against SiTU of the oracle's g, u, within the propagated bound
+    g, _, ng = oracle.mxfp4_gemv(x, ex["w1p"], ex["w1s"], full=True)
+    u, _, nu = oracle.mxfp4_gemv(x, ex["w3p"], ex["w3s"], full=True)
+    ho = oracle.situ_vec(g, u)
+    tol = situ_tolerance(g, u, ng, nu)
+    assert np.all(np.abs(hg.astype(np.float64) - ho) <= tol), "h outside the propagated bound"
+    # stage 2 (isolated): w2 applied to the GPU's own h
+    y2, _, n2 = oracle.mxfp4_gemv(hg, ex["w2p"], ex["w2s"], full=True)
+    assert_norm_close(yg, y2, n2, what="glu w2 stage")
+    # end to end: the oracle's y, within stage-2's bound plus the propagated h difference
+    full = oracle.expert_glu(x, ex, oracle.EXACT)
+    W2 = np.abs(oracle.mxfp4_dequant(ex["w2p"], ex["w2s"]))
+    bound = REL * n2 + W2 @ np.abs(hg.astype(np.float64) - full["h"])
+    assert np.all(np.abs(yg - full["y"]) <= bound * (1 + 1e-9) + 1e-30)
+    return yg
+
+
+@pytest.mark.parametrize("lo,hi", [(118, 132), (120, 122)])
+def test_expert_glu_full_size(k3g, lo, hi):
+    print(f"expert glu scales {lo}..{hi}", flush=True)
+    ex = synth.expert(synth.SEED_BASE, 0, lo=lo, hi=hi)
+    x = synth.activations(synth.SEED_BASE, 1)[0]
+    check_glu(k3g, ex, x, 3584, 3072)
+
+
+def test_expert_glu_small_ragged(k3g):
+    ex = synth.expert(41, 3, latent=96, inter=160, lo=121, hi=123, p255=0.02)
+    x = synth.activations(41, 1, 96)[0]
+    check_glu(k3g, ex, x, 96, 160)
+
+
+# ---- routing ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,n_in,E,K,bias", [(1, 3584, 896, 16, 0.1), (64, 3584, 896, 16, 0.01),
+                                             (100, 3584, 896, 16, 0.01), (7, 200, 40, 5, 0.3),
+                                             (33, 7168, 896, 16, 0.1), (3, 64, 64, 64, 0.0)])
+def test_route_matches_oracle(k3g, T, n_in, E, K, bias):
+    print(f"route T={T} in={n_in} E={E} K={K}", flush=True)
+    seed = 3000 + T
+    W, b = synth.router(seed, E, n_in, bias)
+    x = synth.activations(seed, T, n_in)
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    sh = k3g.shape(n_tokens=T, n_experts=E)
+    ws = k3g.workspace(k3g.OP_MOE_ROUTE, sh)
+    L = k3g.workspace_layout(k3g.OP_MOE_ROUTE, sh)
+    k3g.k3g_moe_route(idx, wts, dev(x), dev(W), dev(b), K, ws)
+    io, wo, lo = oracle.route(x, W, b, K)
+    lg = host(ws[L["logits"]:L["logits"] + 8 * T * E].view(torch.float64)).reshape(T, E)
+    # logits: double accumulation of exact products, so within a few ulp
+    nl = np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T
+    assert np.all(np.abs(lg - lo) <= 1e-14 * nl)
+    assert np.array_equal(host(idx), io)
+    assert np.allclose(host(wts), wo, rtol=1e-6, atol=0)
+
+
+# ---- the MoE layer --------------------------------------------------------------------
+
+def run_layer(k3g, x, idx, wts, bank, mode):
+    T = x.shape[0]
+    K = idx.shape[1]
+    y = torch.empty((T, bank.latent), dtype=torch.float32, device="cuda")
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=bank.n_experts, latent=bank.latent, inter=bank.inter, mode=mode)
+    ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
+    k3g.k3g_moe_layer(y, dev(x), dev(idx), dev(wts), bank, mode, ws)
+    return host(y), ws, L
+
+
+def ws_view(ws, L, name, count, dtype):
+    nbytes = count * np.dtype(dtype).itemsize
+    return host(ws[L[name]:L[name] + nbytes]).view(dtype)
+
+
+def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None):
+    T, K = idx.shape
+    latent, inter = bank.latent, bank.inter
+    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT)
+    P = T * K
+    E = bank.n_experts
+    perm = ws_view(ws, L, "perm", P, np.int32)
+    inv = ws_view(ws, L, "inv", P, np.int32)
+    offsets = ws_view(ws, L, "offsets", E + 1, np.int32)
+    counts = ws_view(ws, L, "counts", E, np.int32)
+    active = ws_view(ws, L, "active", E + 1, np.int32)
+    # bucket: exact, stable by token
+    pid = np.arange(P)
+    key = idx.ravel().astype(np.int64) * T + pid // K
+    assert np.array_equal(perm, pid[np.argsort(key, kind="stable")].astype(np.int32))
+    assert np.array_equal(inv[perm], pid.astype(np.int32))
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    assert active[0] == np.count_nonzero(counts)
+    assert np.array_equal(active[1:1 + active[0]], np.flatnonzero(counts))
+    h = ws_view(ws, L, "h", P * inter, np.float32).reshape(P, inter)
+    ypair = ws_view(ws, L, "ypair", P * latent, np.float32).reshape(P, latent)
+    tokens = range(T) if tokens is None else tokens
+    for t in tokens:
+        acc_ref = np.zeros(latent)
+        nrm_c = np.zeros(latent)
+        for k in range(K):
+            e = int(idx[t, k])
+            ex = src(e)
+            pos = inv[t * K + k]
+            g, _, ng = oracle.mxfp4_gemv(x[t], ex["w1p"], ex["w1s"], full=True)
+            u, _, nu = oracle.mxfp4_gemv(x[t], ex["w3p"], ex["w3s"], full=True)
+            ho = oracle.situ_vec(g, u)
+            assert np.all(np.abs(h[pos].astype(np.float64) - ho) <= situ_tolerance(g, u, ng, nu)), (t, k)
+            y2, _, n2 = oracle.mxfp4_gemv(h[pos], ex["w2p"], ex["w2s"], full=True)
+            assert_norm_close(ypair[pos], y2, n2, what=f"layer down t={t} k={k}")
+            acc_ref += float(wts[t, k]) * ypair[pos].astype(np.float64)
+            nrm_c += abs(float(wts[t, k])) * np.abs(ypair[pos].astype(np.float64))
+        # combine, isolated: the weighted sum of the GPU's own pair outputs
+        assert_norm_close(y[t], acc_ref, nrm_c, what=f"combine t={t}")
+    return y
+
+
+def make_bank(k3g, seed, E, latent, inter, lo=118, hi=132, p255=0.001):
+    src = ExpertSource(seed, latent, inter, lo, hi, p255)
+    bankt, bank = k3g.pack_bank(src, E, latent, inter)
+    return src, bankt, bank
+
+
+def test_layer_small_ragged(k3g):
+    E, latent, inter, T, K = 12, 128, 96, 9, 3
+    src, bankt, bank = make_bank(k3g, 51, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(51, T, latent)
+    W, b = synth.router(51, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K)
+    y = check_layer_exact(k3g, src, bankt, bank, x, idx, wts)
+    # and end to end against the oracle's layer
+    yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.EXACT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
+
+
+def test_layer_skewed_routing(k3g):
+    # many tokens on few experts: per-expert loops over several pairs
+    E, latent, inter, T, K = 6, 256, 128, 40, 2
+    src, bankt, bank = make_bank(k3g, 52, E, latent, inter, 120, 123, 0.0)
+    x = synth.activations(52, T, latent)
+    idx = np.stack([np.zeros(T, np.int32), (np.arange(T) % 5 + 1).astype(np.int32)], 1)
+    wts = np.full((T, K), 0.5, np.float32)
+    check_layer_exact(k3g, src, bankt, bank, x, idx, wts)
+
+
+@pytest.fixture(scope="module")
+def full_bank(k3g):
+    """The 896-expert bank of the decode workloads (15.7 GB of HBM)."""
+    seed = synth.SEED_BASE + 1
+    print("generating the 896-expert bank", flush=True)
+    src, bankt, bank = make_bank(k3g, seed, 896, 3584, 3072)
+    yield src, bankt, bank
+    del bankt
+    torch.cuda.empty_cache()
+
+
+def test_layer_decode_b1_full(k3g, full_bank):
+    src, bankt, bank = full_bank
+    W, b = synth.router(synth.SEED_BASE + 1, 896, 3584, 0.1)
+    x = synth.activations(synth.SEED_BASE + 1, 1, 3584)
+    idx = torch.empty((1, 16), dtype=torch.int32, device="cuda")
+    wts = torch.empty((1, 16), dtype=torch.float32, device="cuda")
+    ws = k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=1, n_experts=896))
+    k3g.k3g_moe_route(idx, wts, dev(x), dev(W), dev(b), 16, ws)
+    io, wo, _ = oracle.route(x, W, b, 16)
+    assert np.array_equal(host(idx), io)
+    check_layer_exact(k3g, src, None, bank, x, io, host(wts))
+
+
+def test_layer_decode_b64_full_sampled(k3g, full_bank):
+    src, bankt, bank = full_bank
+    seed = synth.SEED_BASE + 2
+    W, b = synth.router(seed, 896, 3584, 0.01)
+    x = synth.activations(seed, 64, 3584)
+    io, wo, _ = oracle.route(x, W, b, 16)
+    # sampled outputs: three tokens checked pair by pair
+    check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=[0, 31, 63])
