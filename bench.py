@@ -1,0 +1,266 @@
+"""Benchmark of the routed-expert MXFP4 hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+router logits (fp64) and top-16 selection, the stable bucket by expert, the
+grouped SiTU-GLU up-projection (w1, w3), the down-projection (w2) and the
+weighted combine. The default workload is one decode token through one
+LatentMoE layer whose 896 MXFP4 experts sit in HBM (15.72 GB); each step takes
+the next of 64 distinct tokens so that the experts it reads are not the ones
+the previous step left in the 256 MB Infinity Cache.
+
+Output: one JSON line (rank 0) with the whole-job throughput, the roofline of
+the dominant kernel (its HIP-event time on the stream it runs on) and the CPU
+oracle timed on a bounded sample on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_b1|prefill_4096_idot]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published (TOP/s)
+N_ROT = 64                 # distinct tokens the decode steps cycle through
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    return ap.parse_args()
+
+
+def expert_bytes(latent, inter):
+    """Bytes of one expert's w1 + w3 (up) and of its w2 (down)."""
+    up = 2 * inter * (latent // 2 + latent // 32)
+    dn = latent * (inter // 2 + inter // 32)
+    return up, dn
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the path on a single MI355X and has no "
+              "multi-GPU mode; run it with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_moe_expert_amd as k3g
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    k3g.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    L, I, E, K = synth.LATENT, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    seed_bank = synth.SEED_BASE + 1
+    wl_seed, T, bias_range, mode_name = synth.WORKLOADS[args.workload]
+    mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
+
+    t0 = time.time()
+    src = lambda e: synth.expert(seed_bank, e)  # noqa: E731
+    bankt, bank = k3g.pack_bank(src, E, L, I)
+    W, b = synth.router(wl_seed, E, L, bias_range)
+    Wd = torch.from_numpy(W).to(dev)
+    bd = torch.from_numpy(b).to(dev)
+    n_rot = N_ROT if T == 1 else 4
+    xs_host = [synth.activations(wl_seed, T, L, key=r) for r in range(n_rot)]
+    xs = [torch.from_numpy(x).to(dev) for x in xs_host]
+    print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
+
+    # per input batch r: its own routing, workspaces and output, so that any
+    # stage can be replayed over all batches
+    idx = [torch.empty((T, K), dtype=torch.int32, device=dev) for _ in range(n_rot)]
+    wts = [torch.empty((T, K), dtype=torch.float32, device=dev) for _ in range(n_rot)]
+    ys = [torch.empty((T, L), dtype=torch.float32, device=dev) for _ in range(n_rot)]
+    ws_r = [k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=T, n_experts=E)) for _ in range(n_rot)]
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=mode)
+    ws = [k3g.workspace(k3g.OP_MOE_LAYER, sh) for _ in range(n_rot)]
+
+    stages = [("route", None), ("bucket", k3g.STAGE_BUCKET)]
+    if mode == k3g.IDOT:
+        stages.append(("quant_x", k3g.STAGE_QUANT_X))
+    stages.append(("up", k3g.STAGE_UP))
+    if mode == k3g.IDOT:
+        stages.append(("quant_h", k3g.STAGE_QUANT_H))
+    stages += [("down", k3g.STAGE_DOWN), ("combine", k3g.STAGE_COMBINE)]
+
+    def stage(r, st):
+        if st is None:
+            k3g.k3g_moe_route(idx[r], wts[r], xs[r], Wd, bd, K, ws_r[r])
+        else:
+            k3g.k3g_moe_layer_stage(st, ys[r], xs[r], idx[r], wts[r], bank, mode, ws[r])
+
+    def step(r):
+        for _, st in stages:
+            stage(r, st)
+
+    # eager warm-up (also fills the library's per-device checks before capture)
+    for r in range(n_rot):
+        step(r)
+    torch.cuda.synchronize()
+
+    # one HIP graph per input batch holding the whole step
+    graphs = []
+    if not args.eager:
+        for r in range(n_rot):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % n_rot].replay()
+        else:
+            step(i % n_rot)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, host clock between two device syncs
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        run(args.warmup + i)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_per_step = 1e3 * t_total / args.steps
+
+    # per-kernel times: each stage replayed over every input batch inside one
+    # graph, bracketed by HIP events on the stream it runs on; the average
+    # launch time is the elapsed time over the number of launches
+    stream = torch.cuda.current_stream()
+    stage_ms = {}
+    reps = 3
+    for name, st in stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(n_rot):
+                stage(r, st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stage_ms[name] = e0.elapsed_time(e1) / (reps * n_rot)
+        del g
+    timing = (f"step: {len(graphs) and 'HIP graph per step' or 'eager'} replay; stages: HIP events around a graph "
+              f"of {n_rot} launches of the stage, {reps} replays")
+
+    # distinct experts per step (decode: always top_k; prefill: counted from the routing)
+    counts = None
+    if T > 1:
+        cnt = []
+        for r in range(n_rot):
+            cnt.append(len(np.unique(idx[r].cpu().numpy())))
+        counts = float(np.mean(cnt))
+    n_exp = float(K) if T == 1 else counts
+    up_b, dn_b = expert_bytes(L, I)
+    router_b = E * L * 4 + E * 4
+    alg_bytes = n_exp * (up_b + dn_b) + router_b + 2 * T * L * 4
+    P = T * K
+    up_alg = n_exp * up_b + T * L * 4 + P * I * 4       # weights once, x in, h out
+    if mode == k3g.IDOT:
+        up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * 4
+
+    gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    tok_s = T / (ms_per_step * 1e-3)
+    up_gbs = up_alg / (stage_ms["up"] * 1e-3) / 1e9
+
+    result = {
+        "metric": "MXFP4 expert GEMV HBM GB/s (batch 1); MoE-layer tokens/s at 4096 tokens",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if mode == k3g.EXACT else "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "tokens_per_step": T,
+            "experts": E, "top_k": K, "latent": L, "inter": I,
+            "mode": mode_name,
+            "distinct_experts_per_step": n_exp,
+            "algorithmic_bytes_per_step": int(alg_bytes),
+            "seed_bank": seed_bank, "seed_workload": wl_seed,
+        },
+        "tokens_per_s": round(tok_s, 1),
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "timing": timing,
+        "roofline": {
+            "kernel": "moe_up (w1, w3 and SiTU for every selected expert)",
+            "bound": "hbm",
+            "achieved": round(up_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(up_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(up_alg),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode):
+    """The oracle, as it is, on a bounded sample of the same workload: whole
+    steps (route + layer) for as many of the bench's tokens as fit the budget."""
+    import oracle
+
+    K = 16
+    done = 0
+    spent = 0.0
+    tokens = 0
+    xs_flat = np.concatenate(xs_host, 0)
+    while spent < args.cpu_seconds and done < xs_flat.shape[0]:
+        x = xs_flat[done:done + 1]
+        io, wo, _ = oracle.route(x, W, b, K)  # noqa: F841 (timed below with the layer)
+        experts = {int(e): src(int(e)) for e in io.ravel()}   # generation is not timed
+        t = time.perf_counter()
+        io, wo, _ = oracle.route(x, W, b, K)
+        oracle.moe_layer(x, io, wo, experts, 896, oracle.EXACT if mode == 0 else oracle.IDOT)
+        spent += time.perf_counter() - t
+        done += 1
+        tokens += 1
+    bytes_per_token = alg_bytes / T if T == 1 else None
+    return {
+        "value": round(bytes_per_token * tokens / spent / 1e9, 3) if bytes_per_token else round(tokens / spent, 3),
+        "unit": "GB/s" if bytes_per_token else "tokens/s",
+        "tokens_per_s": round(tokens / spent, 4),
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{tokens} decode tokens, each a whole step (fp64 router + top-16 + 16 SiTU-GLU experts "
+                  f"+ combine), {spent:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

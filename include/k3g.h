@@ -196,6 +196,30 @@ int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts
                   const k3g_expert_bank *bank, int n_tokens, int top_k, int mode,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* The layer's stages, in the order k3g_moe_layer runs them. Each stage is
+ * one kernel launch (stages a mode does not have enqueue nothing), so a
+ * caller can place events between them to time each kernel:
+ *   BUCKET   stable sort of the pairs by expert (counts, offsets, perm, inv, active)
+ *   QUANT_X  IDOT only: x -> xq, xs
+ *   UP       per expert and row: g = w1 a, u = w3 a, h = SiTU(g, u)
+ *   QUANT_H  IDOT only: h -> hq, hs
+ *   DOWN     per expert and row: ypair = w2 h
+ *   COMBINE  y[t] = sum_k wts[t][k] * ypair[inv[t*top_k+k]]
+ * Arguments as k3g_moe_layer; every stage validates them the same way and
+ * reads what the earlier stages left in ws. */
+typedef enum {
+    K3G_STAGE_BUCKET = 0,
+    K3G_STAGE_QUANT_X = 1,
+    K3G_STAGE_UP = 2,
+    K3G_STAGE_QUANT_H = 3,
+    K3G_STAGE_DOWN = 4,
+    K3G_STAGE_COMBINE = 5
+} k3g_stage;
+
+int k3g_moe_layer_stage(int stage, float *y, const float *x, const int32_t *idx, const float *wts,
+                        const k3g_expert_bank *bank, int n_tokens, int top_k, int mode,
+                        void *ws, size_t ws_bytes, void *stream);
+
 /* The full LatentMoE block ([COLIBRI-K3] "Architecture notes"): route on x,
  * lat = W_down x, agg = layer(lat), n = RMSNorm(agg) * gamma, out = W_up n +
  * sum_s W2_s SiTU(W1_s x, W3_s x). out, x fp32 [T][hidden]. top_k as above. */

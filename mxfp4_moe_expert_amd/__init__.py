@@ -94,6 +94,7 @@ def lib():
         L.k3g_expert_glu.argtypes = [P, P, P, i, P, sz, P]
         L.k3g_moe_route.argtypes = [P, P, P, P, P, i, i, i, i, P, sz, P]
         L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
+        L.k3g_moe_layer_stage.argtypes = [i, P, P, P, P, P, i, i, i, P, sz, P]
         L.k3g_latent_moe_block.argtypes = [P, P, P, i, i, i, P, sz, P]
         L.k3g_quantize_i8_groups.argtypes = [P, P, P, i, i, P]
         L.k3g_mxfp4_idot_groupsums.argtypes = [P, P, P, i, i, i, P]
@@ -240,6 +241,27 @@ def k3g_moe_layer(y: torch.Tensor, x: torch.Tensor, idx: torch.Tensor, wts: torc
         raise ValueError("shape mismatch")
     _check("k3g_moe_layer", lib().k3g_moe_layer(_ptr(y), _ptr(x), _ptr(idx), _ptr(wts), C.byref(bank),
                                                  T, K, mode, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+STAGE_BUCKET, STAGE_QUANT_X, STAGE_UP, STAGE_QUANT_H, STAGE_DOWN, STAGE_COMBINE = range(6)
+
+
+def k3g_moe_layer_stage(stage: int, y: torch.Tensor, x: torch.Tensor, idx: torch.Tensor, wts: torch.Tensor,
+                        bank: ExpertBank, mode: int, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """One stage (one kernel) of k3g_moe_layer; the same checks as the whole layer."""
+    _dev(y, torch.float32, "y")
+    _dev(x, torch.float32, "x")
+    _dev(idx, torch.int32, "idx")
+    _dev(wts, torch.float32, "wts")
+    _dev(ws, torch.uint8, "ws")
+    T, latent = x.shape
+    K = idx.shape[1]
+    if latent != bank.latent or y.shape != x.shape or wts.shape != idx.shape or idx.shape[0] != T:
+        raise ValueError("shape mismatch")
+    _check("k3g_moe_layer_stage", lib().k3g_moe_layer_stage(stage, _ptr(y), _ptr(x), _ptr(idx), _ptr(wts),
+                                                             C.byref(bank), T, K, mode, _ptr(ws), ws.numel(),
+                                                             _stream(stream)))
     return y
 
 

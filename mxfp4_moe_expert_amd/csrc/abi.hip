@@ -291,44 +291,77 @@ int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_route
     return launch_topk(idx, wts, logits, bias, n_tokens, n_experts, top_k, st);
 }
 
-int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts, const k3g_expert_bank *bank,
-                  int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes, void *stream) {
+static int layer_prepare(k3g_ws_layout *L, const float *y, const float *x, const int32_t *idx, const float *wts,
+                         const k3g_expert_bank *bank, int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes) {
     if (!y || !x || !idx || !wts || !bank || !bank->base || !ws) return K3G_EINVAL;
     const int latent = bank->latent, inter = bank->inter, E = bank->n_experts;
     k3g_shape s = {n_tokens, top_k, E, latent, inter, 0, 0, mode};
-    k3g_ws_layout L;
-    K3G_TRY(layout(&L, K3G_OP_MOE_LAYER, s));
-    if (ws_bytes < L.total) return K3G_ENOSPACE;
+    K3G_TRY(layout(L, K3G_OP_MOE_LAYER, s));
+    if (ws_bytes < L->total) return K3G_ENOSPACE;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
         return K3G_EALIGN;
     if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
     for (int i = 0; i < 6; i += 2)
         if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
-    if (overlap(y, sizeof(float) * n_tokens * latent, x, sizeof(float) * n_tokens * latent) && n_tokens > 0)
+    if (n_tokens > 0 && overlap(y, sizeof(float) * n_tokens * latent, x, sizeof(float) * n_tokens * latent))
         return K3G_EINVAL;
-    K3G_TRY(check_device());
+    return check_device();
+}
+
+// One stage of the layer: exactly one kernel launch (none for stages the mode
+// does not have).
+static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float *x, const int32_t *idx,
+                       const float *wts, const k3g_expert_bank *bank, int n_tokens, int top_k, int mode, void *ws,
+                       hipStream_t st) {
     if (n_tokens == 0) return K3G_OK;
+    const int latent = bank->latent, inter = bank->inter, E = bank->n_experts;
     char *w = (char *)ws;
     int32_t *counts = (int32_t *)(w + L.counts), *offsets = (int32_t *)(w + L.offsets);
     int32_t *perm = (int32_t *)(w + L.perm), *inv = (int32_t *)(w + L.inv), *active = (int32_t *)(w + L.active);
     float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
+    int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
+    float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
     const int P = n_tokens * top_k;
     const int max_slots = P < E ? P : E;
     const BankDev b = bank_dev(*bank);
-    hipStream_t st = S(stream);
-    K3G_TRY(launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st));
-    if (mode == K3G_EXACT) {
-        K3G_TRY(launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P, st));
-        K3G_TRY(launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots, st));
-    } else {
-        int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
-        float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
-        K3G_TRY(launch_quant_i8(xq, xs, x, n_tokens, latent, st));
-        K3G_TRY(launch_moe_up_idot(h, xq, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st));
-        K3G_TRY(launch_quant_i8(hq, hs, h, P, inter, st));
-        K3G_TRY(launch_moe_down_idot(ypair, hq, hs, b, active, offsets, perm, latent, inter, max_slots, st));
+    switch (stage) {
+        case K3G_STAGE_BUCKET:
+            return launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
+        case K3G_STAGE_QUANT_X:
+            return mode == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, st) : K3G_OK;
+        case K3G_STAGE_UP:
+            return mode == K3G_IDOT
+                       ? launch_moe_up_idot(h, xq, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
+                       : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P, st);
+        case K3G_STAGE_QUANT_H:
+            return mode == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, st) : K3G_OK;
+        case K3G_STAGE_DOWN:
+            return mode == K3G_IDOT
+                       ? launch_moe_down_idot(ypair, hq, hs, b, active, offsets, perm, latent, inter, max_slots, st)
+                       : launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots, st);
+        case K3G_STAGE_COMBINE:
+            return launch_combine(y, ypair, wts, inv, n_tokens, top_k, latent, st);
+        default:
+            return K3G_EINVAL;
     }
-    return launch_combine(y, ypair, wts, inv, n_tokens, top_k, latent, st);
+}
+
+int k3g_moe_layer_stage(int stage, float *y, const float *x, const int32_t *idx, const float *wts,
+                        const k3g_expert_bank *bank, int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes,
+                        void *stream) {
+    if (stage < K3G_STAGE_BUCKET || stage > K3G_STAGE_COMBINE) return K3G_EINVAL;
+    k3g_ws_layout L;
+    K3G_TRY(layer_prepare(&L, y, x, idx, wts, bank, n_tokens, top_k, mode, ws, ws_bytes));
+    return layer_stage(stage, L, y, x, idx, wts, bank, n_tokens, top_k, mode, ws, S(stream));
+}
+
+int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts, const k3g_expert_bank *bank,
+                  int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes, void *stream) {
+    k3g_ws_layout L;
+    K3G_TRY(layer_prepare(&L, y, x, idx, wts, bank, n_tokens, top_k, mode, ws, ws_bytes));
+    for (int stage = K3G_STAGE_BUCKET; stage <= K3G_STAGE_COMBINE; ++stage)
+        K3G_TRY(layer_stage(stage, L, y, x, idx, wts, bank, n_tokens, top_k, mode, ws, S(stream)));
+    return K3G_OK;
 }
 
 }  // extern "C"

@@ -22,39 +22,53 @@ struct RowData {
     uint32_t s[NG];
 };
 
+// Loads are unconditional so that the compiler can count them: a lane past
+// the last group reads group ngrp-1 again, and row_partial drops it (the
+// lane's `valid` bits).
 template <int NG>
 __device__ inline void load_row(RowData<NG> &d, const uint8_t *prow, const uint8_t *srow, int lane, int ngrp) {
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int g = lane * NG + i;
-        if (g < ngrp) {
-            d.w[i] = load16(prow + (size_t)g * 16);
-            d.s[i] = srow[g];
-        } else {
-            d.w[i] = make_uint4(0, 0, 0, 0);
-            d.s[i] = 255u;
-        }
+        const int gc = g < ngrp ? g : ngrp - 1;
+        d.w[i] = load16(prow + (size_t)gc * 16);
+        d.s[i] = srow[gc];
     }
 }
 
 template <int NG>
-__device__ inline float row_partial(const RowData<NG> &d, const uint32_t *lut, uint32_t lane_off, const float *xr) {
+__device__ inline float row_partial(const RowData<NG> &d, const uint32_t *lut, uint32_t lane_off, const float *xr,
+                                   uint32_t valid) {
     float p = 0.f;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) p += apply_scale(group_dot(lut, lane_off, d.w[i], xr + i * kGroup), d.s[i]);
+    for (int i = 0; i < NG; ++i) {
+        const float sub = group_dot(lut, lane_off, d.w[i], xr + i * kGroup);
+        p += ((valid >> i) & 1u) ? apply_scale(sub, d.s[i]) : 0.0f;
+    }
     return p;
 }
 
-// x columns owned by this lane: groups [lane*NG, lane*NG+NG) of a row of width ngrp*32.
+// Bit i set: group lane*NG+i exists in a row of ngrp groups.
+template <int NG>
+__device__ inline uint32_t valid_groups(int lane, int ngrp) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) v |= (lane * NG + i < ngrp ? 1u : 0u) << i;
+    return v;
+}
+
+// x columns owned by this lane: groups [lane*NG, lane*NG+NG) of a row of width
+// ngrp*32. A lane past the last group holds a copy of the last group (its
+// products are dropped by row_partial).
 template <int NG>
 __device__ inline void load_x(float *xr, const float *x, int lane, int ngrp) {
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int g = lane * NG + i;
+        const int gc = g < ngrp ? g : ngrp - 1;
 #pragma unroll
         for (int j = 0; j < kGroup; j += 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (g < ngrp) v = *(const float4 *)(x + (size_t)g * kGroup + j);
+            const float4 v = *(const float4 *)(x + (size_t)gc * kGroup + j);
             xr[i * kGroup + j + 0] = v.x;
             xr[i * kGroup + j + 1] = v.y;
             xr[i * kGroup + j + 2] = v.z;
@@ -77,19 +91,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(float *__restrict__ y, const 
     const uint32_t lane_off = uint32_t(lane) << 2;
     const int ngrp = in / kGroup;
     const size_t rowbytes = (size_t)in / 2;
+    const uint32_t valid = valid_groups<NG>(lane, ngrp);
     float xr[NG * kGroup];
     load_x<NG>(xr, x, lane, ngrp);
     const int n_items = (rows + rpi - 1) / rpi;
     for (int item = blockIdx.x * waves + wave; item < n_items; item += gridDim.x * waves) {
         const int r0 = item * rpi;
         const int r1 = min(rows, r0 + rpi);
-        RowData<NG> cur, nxt;
-        load_row<NG>(cur, packed + (size_t)r0 * rowbytes, scales + (size_t)r0 * ngrp, lane, ngrp);
-        for (int r = r0; r < r1; ++r) {
-            if (r + 1 < r1) load_row<NG>(nxt, packed + (size_t)(r + 1) * rowbytes, scales + (size_t)(r + 1) * ngrp, lane, ngrp);
-            const float s = wave_sum(row_partial<NG>(cur, lut, lane_off, xr));
-            if (lane == 0) y[r] = s;
-            cur = nxt;
+        auto P = [&](int r) { return packed + (size_t)min(r, r1 - 1) * rowbytes; };
+        auto Q = [&](int r) { return scales + (size_t)min(r, r1 - 1) * ngrp; };
+        RowData<NG> a, b;
+        load_row<NG>(a, P(r0), Q(r0), lane, ngrp);
+        load_row<NG>(b, P(r0 + 1), Q(r0 + 1), lane, ngrp);
+        for (int r = r0; r < r1; r += 2) {
+            const float sa = wave_sum(row_partial<NG>(a, lut, lane_off, xr, valid));
+            load_row<NG>(a, P(r + 2), Q(r + 2), lane, ngrp);
+            if (lane == 0) y[r] = sa;
+            if (r + 1 < r1) {
+                const float sb = wave_sum(row_partial<NG>(b, lut, lane_off, xr, valid));
+                if (lane == 0) y[r + 1] = sb;
+            }
+            load_row<NG>(b, P(r + 3), Q(r + 3), lane, ngrp);
         }
     }
 }
@@ -113,6 +135,7 @@ __global__ __launch_bounds__(256) void moe_up_exact_kernel(
     const uint32_t lane_off = uint32_t(lane) << 2;
     const int ngrp = latent / kGroup;
     const size_t rowbytes = (size_t)latent / 2;
+    const uint32_t valid = valid_groups<NG>(lane, ngrp);
     const int chunks = (inter + rpi - 1) / rpi;
     const int n_act = perm ? active[0] : 1;
     const int n_items = max_slots * chunks;
@@ -129,22 +152,31 @@ __global__ __launch_bounds__(256) void moe_up_exact_kernel(
         const uint8_t *w3p = eb + bank.off[W3P], *w3s = eb + bank.off[W3S];
         const int r0 = chunk * rpi;
         const int r1 = min(inter, r0 + rpi);
+        auto P1 = [&](int r) { return w1p + (size_t)min(r, r1 - 1) * rowbytes; };
+        auto S1 = [&](int r) { return w1s + (size_t)min(r, r1 - 1) * ngrp; };
+        auto P3 = [&](int r) { return w3p + (size_t)min(r, r1 - 1) * rowbytes; };
+        auto S3 = [&](int r) { return w3s + (size_t)min(r, r1 - 1) * ngrp; };
         for (int pos = p0; pos < p1; ++pos) {
             const int t = perm ? perm[pos] / top_k : 0;
             load_x<NG>(xr, x + (size_t)t * latent, lane, ngrp);
-            RowData<NG> c1, c3, n1, n3;
-            load_row<NG>(c1, w1p + (size_t)r0 * rowbytes, w1s + (size_t)r0 * ngrp, lane, ngrp);
-            load_row<NG>(c3, w3p + (size_t)r0 * rowbytes, w3s + (size_t)r0 * ngrp, lane, ngrp);
-            for (int r = r0; r < r1; ++r) {
+            RowData<NG> a1, a3, b1, b3;
+            load_row<NG>(a1, P1(r0), S1(r0), lane, ngrp);
+            load_row<NG>(a3, P3(r0), S3(r0), lane, ngrp);
+            load_row<NG>(b1, P1(r0 + 1), S1(r0 + 1), lane, ngrp);
+            load_row<NG>(b3, P3(r0 + 1), S3(r0 + 1), lane, ngrp);
+            for (int r = r0; r < r1; r += 2) {
+                const float ga = wave_sum(row_partial<NG>(a1, lut, lane_off, xr, valid));
+                const float ua = wave_sum(row_partial<NG>(a3, lut, lane_off, xr, valid));
+                load_row<NG>(a1, P1(r + 2), S1(r + 2), lane, ngrp);
+                load_row<NG>(a3, P3(r + 2), S3(r + 2), lane, ngrp);
+                if (lane == 0) h[(size_t)pos * inter + r] = situ(ga, ua);
                 if (r + 1 < r1) {
-                    load_row<NG>(n1, w1p + (size_t)(r + 1) * rowbytes, w1s + (size_t)(r + 1) * ngrp, lane, ngrp);
-                    load_row<NG>(n3, w3p + (size_t)(r + 1) * rowbytes, w3s + (size_t)(r + 1) * ngrp, lane, ngrp);
+                    const float gb = wave_sum(row_partial<NG>(b1, lut, lane_off, xr, valid));
+                    const float ub = wave_sum(row_partial<NG>(b3, lut, lane_off, xr, valid));
+                    if (lane == 0) h[(size_t)pos * inter + r + 1] = situ(gb, ub);
                 }
-                const float g = wave_sum(row_partial<NG>(c1, lut, lane_off, xr));
-                const float u = wave_sum(row_partial<NG>(c3, lut, lane_off, xr));
-                if (lane == 0) h[(size_t)pos * inter + r] = situ(g, u);
-                c1 = n1;
-                c3 = n3;
+                load_row<NG>(b1, P1(r + 3), S1(r + 3), lane, ngrp);
+                load_row<NG>(b3, P3(r + 3), S3(r + 3), lane, ngrp);
             }
         }
     }
@@ -166,6 +198,7 @@ __global__ __launch_bounds__(256) void moe_down_exact_kernel(
     const uint32_t lane_off = uint32_t(lane) << 2;
     const int ngrp = inter / kGroup;
     const size_t rowbytes = (size_t)inter / 2;
+    const uint32_t valid = valid_groups<NG>(lane, ngrp);
     const int chunks = (latent + rpi - 1) / rpi;
     const int n_act = perm ? active[0] : 1;
     const int n_items = max_slots * chunks;
@@ -181,15 +214,22 @@ __global__ __launch_bounds__(256) void moe_down_exact_kernel(
         const uint8_t *w2p = eb + bank.off[W2P], *w2s = eb + bank.off[W2S];
         const int r0 = chunk * rpi;
         const int r1 = min(latent, r0 + rpi);
+        auto P2 = [&](int r) { return w2p + (size_t)min(r, r1 - 1) * rowbytes; };
+        auto S2 = [&](int r) { return w2s + (size_t)min(r, r1 - 1) * ngrp; };
         for (int pos = p0; pos < p1; ++pos) {
             load_x<NG>(xr, h + (size_t)pos * inter, lane, ngrp);
-            RowData<NG> cur, nxt;
-            load_row<NG>(cur, w2p + (size_t)r0 * rowbytes, w2s + (size_t)r0 * ngrp, lane, ngrp);
-            for (int r = r0; r < r1; ++r) {
-                if (r + 1 < r1) load_row<NG>(nxt, w2p + (size_t)(r + 1) * rowbytes, w2s + (size_t)(r + 1) * ngrp, lane, ngrp);
-                const float s = wave_sum(row_partial<NG>(cur, lut, lane_off, xr));
-                if (lane == 0) ypair[(size_t)pos * latent + r] = s;
-                cur = nxt;
+            RowData<NG> a, b;
+            load_row<NG>(a, P2(r0), S2(r0), lane, ngrp);
+            load_row<NG>(b, P2(r0 + 1), S2(r0 + 1), lane, ngrp);
+            for (int r = r0; r < r1; r += 2) {
+                const float sa = wave_sum(row_partial<NG>(a, lut, lane_off, xr, valid));
+                load_row<NG>(a, P2(r + 2), S2(r + 2), lane, ngrp);
+                if (lane == 0) ypair[(size_t)pos * latent + r] = sa;
+                if (r + 1 < r1) {
+                    const float sb = wave_sum(row_partial<NG>(b, lut, lane_off, xr, valid));
+                    if (lane == 0) ypair[(size_t)pos * latent + r + 1] = sb;
+                }
+                load_row<NG>(b, P2(r + 3), S2(r + 3), lane, ngrp);
             }
         }
     }
@@ -203,15 +243,28 @@ __global__ __launch_bounds__(256) void combine_kernel(float *__restrict__ y, con
     const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (t >= n_tokens || i >= latent) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < top_k; ++k) {
-        const float w = wts[t * top_k + k];
-        const int pos = inv ? inv[t * top_k + k] : t * top_k + k;
-        if (pos < 0) continue;  // a dropped out-of-range expert id
-        const float4 v = *(const float4 *)(ypair + (size_t)pos * latent + i);
-        acc.x = __builtin_fmaf(w, v.x, acc.x);
-        acc.y = __builtin_fmaf(w, v.y, acc.y);
-        acc.z = __builtin_fmaf(w, v.z, acc.z);
-        acc.w = __builtin_fmaf(w, v.w, acc.w);
+    // in blocks of 16 pairs: all loads of a block are issued before the sums
+    for (int k0 = 0; k0 < top_k; k0 += 16) {
+        float w[16];
+        float4 v[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const int k = k0 + kk < top_k ? k0 + kk : top_k - 1;
+            const int pos = inv ? inv[t * top_k + k] : t * top_k + k;
+            // a pair past top_k, or a dropped out-of-range expert id, adds nothing
+            const bool live = k0 + kk < top_k && pos >= 0;
+            const float wv = wts[t * top_k + k];
+            const float4 yv = *(const float4 *)(ypair + (size_t)(pos >= 0 ? pos : 0) * latent + i);
+            w[kk] = live ? wv : 0.0f;
+            v[kk] = live ? yv : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            acc.x = __builtin_fmaf(w[kk], v[kk].x, acc.x);
+            acc.y = __builtin_fmaf(w[kk], v[kk].y, acc.y);
+            acc.z = __builtin_fmaf(w[kk], v[kk].z, acc.z);
+            acc.w = __builtin_fmaf(w[kk], v[kk].w, acc.w);
+        }
     }
     *(float4 *)(y + (size_t)t * latent + i) = acc;
 }

@@ -16,12 +16,51 @@
 namespace k3g {
 
 // ---- logits, few tokens: one wavefront per expert row ------------------------
-__global__ __launch_bounds__(256) void logits_rows_kernel(double *__restrict__ logits, const float *__restrict__ x,
-                                                          const float *__restrict__ W, int T, int in, int E) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-    const int n_waves = gridDim.x * blockDim.x / kWave;
-    for (int e = wave; e < E; e += n_waves) {
+// The row is read once with 16-byte loads into registers (in <= 64*4*RW
+// floats), then dotted with each token's x in fp64.
+template <int RW>
+__global__ __launch_bounds__(64) void logits_rows_kernel(double *__restrict__ logits, const float *__restrict__ x,
+                                                         const float *__restrict__ W, int T, int in, int E) {
+    const int lane = threadIdx.x;
+    const int n4 = in / 4;
+    for (int e = blockIdx.x; e < E; e += gridDim.x) {
+        const float4 *w4 = (const float4 *)(W + (size_t)e * in);
+        float4 wr[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            const int j = lane + i * kWave;
+            wr[i] = w4[j < n4 ? j : n4 - 1];
+        }
+        for (int t = 0; t < T; ++t) {
+            const float4 *x4 = (const float4 *)(x + (size_t)t * in);
+            float4 xr[RW];
+#pragma unroll
+            for (int i = 0; i < RW; ++i) {
+                const int j = lane + i * kWave;
+                xr[i] = x4[j < n4 ? j : n4 - 1];
+            }
+            double acc = 0.0;
+#pragma unroll
+            for (int i = 0; i < RW; ++i) {
+                // a lane past the row's end holds a duplicate of its last chunk: drop it
+                const double m = (lane + i * kWave < n4) ? 1.0 : 0.0;
+                double part = (double)wr[i].x * (double)xr[i].x;
+                part = __builtin_fma((double)wr[i].y, (double)xr[i].y, part);
+                part = __builtin_fma((double)wr[i].z, (double)xr[i].z, part);
+                part = __builtin_fma((double)wr[i].w, (double)xr[i].w, part);
+                acc = __builtin_fma(m, part, acc);
+            }
+            acc = wave_sum_f64(acc);
+            if (lane == 0) logits[(size_t)t * E + e] = acc;
+        }
+    }
+}
+
+// Any width: scalar loads, one wavefront per row.
+__global__ __launch_bounds__(64) void logits_rows_any_kernel(double *__restrict__ logits, const float *__restrict__ x,
+                                                             const float *__restrict__ W, int T, int in, int E) {
+    const int lane = threadIdx.x;
+    for (int e = blockIdx.x; e < E; e += gridDim.x) {
         const float *w = W + (size_t)e * in;
         for (int t = 0; t < T; ++t) {
             const float *xt = x + (size_t)t * in;
@@ -79,54 +118,69 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(double *__restrict__ 
         }
 }
 
-// ---- top-k: one wavefront per token --------------------------------------------
-// Biased scores in LDS; k rounds of a wavefront arg-max where a larger score
-// wins and equal scores go to the lower expert id; the winner is retired.
-__device__ inline bool better(double va, int ia, double vb, int ib) {
+// ---- top-k: one workgroup per token, bitonic sort in LDS ----------------------
+// Keys are (biased score, expert id) with "larger score first, equal scores to
+// the lower id" as the order; the sort is a bitonic network over the next
+// power of two >= E (padding sorts last), so the first top_k entries are the
+// selection in output order.
+constexpr int TK_THREADS = 1024;
+
+__device__ inline bool before(double va, int ia, double vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-__global__ __launch_bounds__(64) void topk_kernel(int32_t *__restrict__ idx, float *__restrict__ wts,
-                                                  const double *__restrict__ logits, const float *__restrict__ bias,
-                                                  int T, int E, int K) {
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(int32_t *__restrict__ idx, float *__restrict__ wts,
+                                                          const double *__restrict__ logits,
+                                                          const float *__restrict__ bias, int T, int E, int K,
+                                                          int n_pow2) {
     extern __shared__ double smem[];
-    double *bs = smem;                   // biased score, -inf once taken
-    double *sc = smem + E;               // raw sigmoid score
-    int *sel = (int *)(smem + 2 * E);    // selected ids, k order
-    const int lane = threadIdx.x;
+    double *key = smem;                       // [n_pow2] biased score
+    double *sc = smem + n_pow2;               // [E] raw sigmoid score by expert id
+    int *id = (int *)(smem + n_pow2 + E);     // [n_pow2] expert id
+    const int tid = threadIdx.x;
     for (int t = blockIdx.x; t < T; t += gridDim.x) {
-        for (int e = lane; e < E; e += kWave) {
-            const double s = 1.0 / (1.0 + exp(-logits[(size_t)t * E + e]));
-            sc[e] = s;
-            bs[e] = s + (double)bias[e];
+        for (int e = tid; e < n_pow2; e += TK_THREADS) {
+            if (e < E) {
+                const double s = 1.0 / (1.0 + exp(-logits[(size_t)t * E + e]));
+                sc[e] = s;
+                key[e] = s + (double)bias[e];
+                id[e] = e;
+            } else {
+                key[e] = -__builtin_inf();
+                id[e] = 0x7fffffff;
+            }
         }
         __syncthreads();
-        double sum = 0.0;
-        for (int k = 0; k < K; ++k) {
-            double bv = -__builtin_inf();
-            int bi = 0x7fffffff;
-            for (int e = lane; e < E; e += kWave) {
-                const double v = bs[e];
-                if (better(v, e, bv, bi)) { bv = v; bi = e; }
+        for (int k = 2; k <= n_pow2; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < n_pow2; i += TK_THREADS) {
+                    const int l = i ^ j;
+                    if (l > i) {
+                        const double a = key[i], b = key[l];
+                        const int ia = id[i], ib = id[l];
+                        // blocks with (i & k) == 0 end up in output order, the others reversed
+                        const bool want_first = (i & k) == 0;
+                        const bool l_first = before(b, ib, a, ia);
+                        if (want_first == l_first) {
+                            key[i] = b; key[l] = a;
+                            id[i] = ib; id[l] = ia;
+                        }
+                    }
+                }
+                __syncthreads();
             }
-            for (int m = 32; m >= 1; m >>= 1) {
-                const double ov = __shfl_xor(bv, m, kWave);
-                const int oi = __shfl_xor(bi, m, kWave);
-                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-            }
-            // every lane now holds the same winner; NaN logits (outside the
-            // contract) could leave none, so stay in bounds
-            if (bi >= E) bi = 0;
-            sum += sc[bi];
-            if (lane == 0) {
-                idx[(size_t)t * K + k] = bi;
-                sel[k] = bi;
-            }
-            __syncthreads();
-            if ((bi & (kWave - 1)) == lane) bs[bi] = -__builtin_inf();
-            __syncthreads();
         }
-        if (lane < K) wts[(size_t)t * K + lane] = (float)(sc[sel[lane]] / sum);
+        if (tid == 0) {
+            double sum = 0.0;
+            for (int k = 0; k < K; ++k) sum += sc[id[k]];
+            key[0] = sum;  // the sorted key is not needed any more
+        }
+        __syncthreads();
+        if (tid < K) {
+            const int e = id[tid];
+            idx[(size_t)t * K + tid] = e;
+            wts[(size_t)t * K + tid] = (float)(sc[e] / key[0]);
+        }
         __syncthreads();
     }
 }
@@ -138,20 +192,32 @@ __global__ __launch_bounds__(64) void topk_kernel(int32_t *__restrict__ idx, flo
 // the mask below its token.
 constexpr int BK_THREADS = 1024;
 
-__device__ inline int block_excl_scan(int v, int *tmp) {
-    // Hillis-Steele over BK_THREADS values in LDS; returns the exclusive prefix.
-    const int tid = threadIdx.x;
-    tmp[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < BK_THREADS; off <<= 1) {
-        const int a = tid >= off ? tmp[tid - off] : 0;
-        __syncthreads();
-        tmp[tid] += a;
-        __syncthreads();
+__device__ inline int block_excl_scan(int v, int *wsum) {
+    // wavefront scans with shuffles, then a scan of the per-wavefront totals;
+    // returns the exclusive prefix of v over the block.
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    constexpr int nw = BK_THREADS / kWave;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
     }
-    const int incl = tmp[tid];
+    if (lane == kWave - 1) wsum[w] = inc;
     __syncthreads();
-    return incl - v;
+    if (w == 0) {
+        int t = lane < nw ? wsum[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < nw; d <<= 1) {
+            const int o = __shfl_up(t, d, kWave);
+            if (lane >= d) t += o;
+        }
+        if (lane < nw) wsum[lane] = t;
+    }
+    __syncthreads();
+    const int res = (w > 0 ? wsum[w - 1] : 0) + inc - v;
+    __syncthreads();
+    return res;
 }
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -224,8 +290,16 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(int32_t *__restrict_
 int launch_logits(double *logits, const float *x, const float *W, int T, int in, int E, hipStream_t st) {
     if (T == 0) return K3G_OK;
     if (T <= 8) {
-        const int blocks = (E + 3) / 4;
-        logits_rows_kernel<<<blocks, 256, 0, st>>>(logits, x, W, T, in, E);
+        const bool vec = in % 4 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)W % 16) == 0;
+        const int rw = (in / 4 + kWave - 1) / kWave;
+        if (vec && rw <= 8)
+            logits_rows_kernel<8><<<E, 64, 0, st>>>(logits, x, W, T, in, E);
+        else if (vec && rw <= 16)
+            logits_rows_kernel<16><<<E, 64, 0, st>>>(logits, x, W, T, in, E);
+        else if (vec && rw <= 32)
+            logits_rows_kernel<32><<<E, 64, 0, st>>>(logits, x, W, T, in, E);
+        else
+            logits_rows_any_kernel<<<E, 64, 0, st>>>(logits, x, W, T, in, E);
     } else {
         const dim3 grid((E + LT - 1) / LT, (T + LT - 1) / LT);
         logits_tiled_kernel<<<grid, 256, 0, st>>>(logits, x, W, T, in, E);
@@ -236,8 +310,11 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
 int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K,
                 hipStream_t st) {
     if (T == 0) return K3G_OK;
+    int n_pow2 = 1;
+    while (n_pow2 < E) n_pow2 <<= 1;
     const int blocks = T < 8192 ? T : 8192;
-    topk_kernel<<<blocks, 64, sizeof(double) * 2 * E + sizeof(int) * 64, st>>>(idx, wts, logits, bias, T, E, K);
+    const size_t lds = sizeof(double) * (size_t)(n_pow2 + E) + sizeof(int) * (size_t)n_pow2;
+    topk_kernel<<<blocks, TK_THREADS, lds, st>>>(idx, wts, logits, bias, T, E, K, n_pow2);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

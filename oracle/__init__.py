@@ -38,6 +38,8 @@ def lib():
         L = C.CDLL(_LIB_PATH)
         P = C.c_void_p
         i = C.c_int
+        L.k3o_threads.restype = i
+        L.k3o_threads.argtypes = []
         L.k3o_e2m1.restype = C.c_double
         L.k3o_e2m1.argtypes = [i]
         L.k3o_e2m1_doubled.restype = i
@@ -77,6 +79,11 @@ def _c(a, dtype):
 def _chk(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().k3o_threads())
 
 
 # -- format ----------------------------------------------------------------

@@ -31,6 +31,20 @@
 
 #define K3O_GROUP 32
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads an OpenMP region of the oracle uses (1 without OpenMP). */
+int k3o_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Format tables, built from the bit-field definitions (never copied).        */
 /* ------------------------------------------------------------------------ */

@@ -26,10 +26,17 @@ def assert_norm_close(got, ref, nrm, rel=REL, what="output"):
     return float((err / np.where(nrm > 0, nrm, 1)).max())
 
 
+def sigmoid64(g):
+    """The logistic function, accurate in both tails and free of overflow."""
+    g = np.asarray(g, np.float64)
+    e = np.exp(-np.abs(g))
+    return np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
 def situ64(g, u):
     g = np.asarray(g, np.float64)
     u = np.asarray(u, np.float64)
-    return 4 * np.tanh(g / 4) * (0.5 * (1 + np.tanh(0.5 * g))) * 25 * np.tanh(u / 25)
+    return 4 * np.tanh(g / 4) * sigmoid64(g) * 25 * np.tanh(u / 25)
 
 
 def situ_tolerance(g, u, ng, nu, rel=REL):
@@ -42,7 +49,7 @@ def situ_tolerance(g, u, ng, nu, rel=REL):
     du = rel * np.asarray(nu, np.float64)
 
     def parts(gg, uu):
-        sig = 0.5 * (1 + np.tanh(0.5 * gg))  # the logistic function, overflow-free
+        sig = sigmoid64(gg)
         a = 4 * np.tanh(gg / 4) * sig
         da = (1 - np.tanh(gg / 4) ** 2) * sig + 4 * np.tanh(gg / 4) * sig * (1 - sig)
         b = 25 * np.tanh(uu / 25)
