@@ -102,11 +102,11 @@ def main():
         stages.append(("quant_h", k3g.STAGE_QUANT_H))
     stages += [("down", k3g.STAGE_DOWN), ("combine", k3g.STAGE_COMBINE)]
 
-    def stage(r, st):
+    def stage(r, st, m=mode):
         if st is None:
             k3g.k3g_moe_route(idx[r], wts[r], xs[r], Wd, bd, K, ws_r[r])
         else:
-            k3g.k3g_moe_layer_stage(st, ys[r], xs[r], idx[r], wts[r], bank, mode, ws[r])
+            k3g.k3g_moe_layer_stage(st, ys[r], xs[r], idx[r], wts[r], bank, m, ws[r])
 
     def step(r):
         for _, st in stages:
@@ -149,13 +149,13 @@ def main():
     # graph, bracketed by HIP events on the stream it runs on; the average
     # launch time is the elapsed time over the number of launches
     stream = torch.cuda.current_stream()
-    stage_ms = {}
     reps = 3
-    for name, st in stages:
+
+    def time_stage(st, m):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for r in range(n_rot):
-                stage(r, st)
+                stage(r, st, m)
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -164,8 +164,13 @@ def main():
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        stage_ms[name] = e0.elapsed_time(e1) / (reps * n_rot)
-        del g
+        return e0.elapsed_time(e1) / (reps * n_rot)
+
+    stage_ms = {name: time_stage(st, mode) for name, st in stages}
+    # the same expert kernels with the nibbles decoded through the LDS byte-pair table
+    lut_ms = {}
+    if mode == k3g.EXACT:
+        lut_ms = {name: time_stage(st, mode | k3g.DECODE_LUT) for name, st in stages if name in ("up", "down")}
     timing = (f"step: {len(graphs) and 'HIP graph per step' or 'eager'} replay; stages: HIP events around a graph "
               f"of {n_rot} launches of the stage, {reps} replays")
 
@@ -213,6 +218,8 @@ def main():
         },
         "tokens_per_s": round(tok_s, 1),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "decode": "gfx950 FP4->FP32 convert" if mode == k3g.EXACT else "int8 MFMA",
+        "stage_us_lds_lut_decode": {k: round(v * 1e3, 2) for k, v in lut_ms.items()},
         "timing": timing,
         "roofline": {
             "kernel": "moe_up (w1, w3 and SiTU for every selected expert)",

@@ -60,6 +60,12 @@ typedef enum {
  *        matrix cores ([COLIBRI-K3] "Streaming design", K3_IDOT). */
 typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
 
+/* OR-ed into `mode` of the EXACT calls: decode the nibbles through the
+ * byte-pair table held in LDS, the pages' decode ([KIC-ARTICLE] "Reduction
+ * one", K3_E2M1_PAIR), instead of gfx950's FP4 -> FP32 convert instruction
+ * (the default). Both give the same values: e2m1 codes are exact in either. */
+#define K3G_DECODE_LUT 0x100
+
 typedef struct {
     const uint8_t *packed; /* [rows][in/2], 16-byte aligned */
     const uint8_t *scales; /* [rows][in/32]                 */
@@ -165,6 +171,11 @@ int k3g_workspace_layout(k3g_ws_layout *out, int op, const k3g_shape *shape);
  * accumulation. */
 int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed,
                    const uint8_t *scales, int in, int rows, int group, void *stream);
+
+/* The same product with the nibbles decoded through the LDS byte-pair table
+ * (see K3G_DECODE_LUT); same arguments, same results. */
+int k3g_mxfp4_gemv_lut(float *y, const float *x, const uint8_t *packed,
+                       const uint8_t *scales, int in, int rows, int group, void *stream);
 
 /* One expert on one token: g = w1 x, u = w3 x, h = 4 tanh(g/4) sigmoid(g)
  * 25 tanh(u/25) (SiTU-GLU, [COLIBRI-K3] "Architecture notes"), y = w2 h.

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libk3g.so")
 
 EXACT = 0
 IDOT = 1
+DECODE_LUT = 0x100  # OR into the EXACT mode: decode through the LDS byte-pair table
 OP_EXPERT_GLU = 1
 OP_MOE_ROUTE = 2
 OP_MOE_LAYER = 3
@@ -91,6 +92,7 @@ def lib():
         L.k3g_workspace_bytes.argtypes = [i, P]
         L.k3g_workspace_layout.argtypes = [P, i, P]
         L.k3g_mxfp4_gemv.argtypes = [P, P, P, P, i, i, i, P]
+        L.k3g_mxfp4_gemv_lut.argtypes = [P, P, P, P, i, i, i, P]
         L.k3g_expert_glu.argtypes = [P, P, P, i, P, sz, P]
         L.k3g_moe_route.argtypes = [P, P, P, P, P, i, i, i, i, P, sz, P]
         L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
@@ -187,7 +189,8 @@ def bank_struct(base: torch.Tensor, n_experts: int, latent: int, inter: int, off
 # ---- entry points ----------------------------------------------------------
 
 def k3g_mxfp4_gemv(y: torch.Tensor, x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
-                   group: int = GROUP, stream=None) -> torch.Tensor:
+                   group: int = GROUP, stream=None, lut: bool = False) -> torch.Tensor:
+    """y = W x on packed MXFP4 (batch 1). lut=True calls k3g_mxfp4_gemv_lut."""
     _dev(y, torch.float32, "y")
     _dev(x, torch.float32, "x")
     _dev(packed, torch.uint8, "packed")
@@ -195,8 +198,9 @@ def k3g_mxfp4_gemv(y: torch.Tensor, x: torch.Tensor, packed: torch.Tensor, scale
     rows, half = packed.shape
     if x.numel() != half * 2 or y.numel() != rows:
         raise ValueError("shape mismatch")
-    _check("k3g_mxfp4_gemv", lib().k3g_mxfp4_gemv(_ptr(y), _ptr(x), _ptr(packed), _ptr(scales),
-                                                   half * 2, rows, group, _stream(stream)))
+    fn = lib().k3g_mxfp4_gemv_lut if lut else lib().k3g_mxfp4_gemv
+    _check("k3g_mxfp4_gemv_lut" if lut else "k3g_mxfp4_gemv",
+           fn(_ptr(y), _ptr(x), _ptr(packed), _ptr(scales), half * 2, rows, group, _stream(stream)))
     return y
 
 

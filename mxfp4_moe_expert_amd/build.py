@@ -20,9 +20,11 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, defines=(), out: str = LIB) -> str:
+    """Compile every csrc/*.hip and link `out`. `defines` are extra -D flags
+    (build-time kernel variants)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    flags = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
+    flags = [*[f"-D{d}" for d in defines], "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
     objs = []
     with tempfile.TemporaryDirectory(prefix="k3g_build_") as tmp:
@@ -38,8 +40,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 procs[0][1].wait()
         failed = False
         for src, p in procs:
-            out = p.communicate()[0].decode(errors="replace")
-            lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            log = p.communicate()[0].decode(errors="replace")
+            lines = [ln for ln in log.splitlines() if "packed-fp32-ops" not in ln]
             if lines and (verbose or p.returncode):
                 print("\n".join(lines), flush=True)
             if p.returncode:
@@ -47,13 +49,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 failed = True
         if failed:
             raise RuntimeError("hipcc failed")
-        out_tmp = LIB + f".tmp{os.getpid()}"
+        out_tmp = out + f".tmp{os.getpid()}"
         cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        os.replace(out_tmp, LIB)
-    return LIB
+        os.replace(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":

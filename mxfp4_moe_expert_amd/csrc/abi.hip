@@ -8,11 +8,13 @@
 
 namespace k3g {
 // launchers (gemv.hip, route.hip, idot.hip)
-int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows, hipStream_t st);
+int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows, bool lut,
+                hipStream_t st);
 int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
-                        const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, hipStream_t st);
+                        const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
+                        hipStream_t st);
 int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
-                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots, bool lut,
                           hipStream_t st);
 int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
                    int latent, hipStream_t st);
@@ -72,10 +74,16 @@ struct Carver {
     }
 };
 
+inline int base_mode(int mode) { return mode & ~K3G_DECODE_LUT; }
+inline bool mode_ok(int mode) {
+    return (mode & ~(K3G_DECODE_LUT | 0xFF)) == 0 && (base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT);
+}
+inline bool lut_of(int mode) { return (mode & K3G_DECODE_LUT) != 0; }
+
 bool shape_ok_layer(const k3g_shape &s) {
     return s.n_tokens >= 0 && s.top_k >= 1 && s.top_k <= kMaxTopK && s.n_experts >= 1 &&
            s.n_experts <= kMaxExperts && s.top_k <= s.n_experts && s.latent > 0 && s.inter > 0 &&
-           s.latent % kGroup == 0 && s.inter % kGroup == 0 && (s.mode == K3G_EXACT || s.mode == K3G_IDOT);
+           s.latent % kGroup == 0 && s.inter % kGroup == 0 && mode_ok(s.mode);
 }
 
 // Regions are laid out from offset 256 so that 0 can mean "absent".
@@ -86,11 +94,10 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
     const size_t T = (size_t)(s.n_tokens > 0 ? s.n_tokens : 0);
     switch (op) {
         case K3G_OP_EXPERT_GLU: {
-            if (s.latent <= 0 || s.inter <= 0 || s.latent % kGroup || s.inter % kGroup ||
-                (s.mode != K3G_EXACT && s.mode != K3G_IDOT))
+            if (s.latent <= 0 || s.inter <= 0 || s.latent % kGroup || s.inter % kGroup || !mode_ok(s.mode))
                 return K3G_EINVAL;
             o->h = c.take(sizeof(float) * s.inter);
-            if (s.mode == K3G_IDOT) {
+            if (base_mode(s.mode) == K3G_IDOT) {
                 o->xq = c.take((size_t)s.latent);
                 o->xs = c.take(sizeof(float) * (s.latent / kGroup));
                 o->hq = c.take((size_t)s.inter);
@@ -124,7 +131,7 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
             o->active = c.take(sizeof(int32_t) * (E + 1));
             o->h = c.take(sizeof(float) * (P ? P : 1) * s.inter);
             o->ypair = c.take(sizeof(float) * (P ? P : 1) * s.latent);
-            if (s.mode == K3G_IDOT) {
+            if (base_mode(s.mode) == K3G_IDOT) {
                 o->xq = c.take((T ? T : 1) * (size_t)s.latent);
                 o->xs = c.take(sizeof(float) * (T ? T : 1) * (s.latent / kGroup));
                 o->hq = c.take((P ? P : 1) * (size_t)s.inter);
@@ -207,14 +214,25 @@ int k3g_workspace_layout(k3g_ws_layout *out, int op, const k3g_shape *shape) {
     return layout(out, op, *shape);
 }
 
-int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
-                   int group, void *stream) {
+static int gemv_entry(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
+                      int group, bool lut, void *stream) {
     if (!y || !x || group != kGroup) return K3G_EINVAL;
     K3G_TRY(mxfp4_ok(packed, scales, in, rows));
     if (!aligned(x, 16) || !aligned(y, 4)) return K3G_EALIGN;
     if (overlap(y, sizeof(float) * rows, x, sizeof(float) * in)) return K3G_EINVAL;
+    if ((int64_t)rows * (in / 2) >= ((int64_t)1 << 31)) return K3G_EUNSUPPORTED;  // 32-bit buffer offsets
     K3G_TRY(check_device());
-    return launch_gemv(y, x, packed, scales, in, rows, S(stream));
+    return launch_gemv(y, x, packed, scales, in, rows, lut, S(stream));
+}
+
+int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
+                   int group, void *stream) {
+    return gemv_entry(y, x, packed, scales, in, rows, group, false, stream);
+}
+
+int k3g_mxfp4_gemv_lut(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
+                       int group, void *stream) {
+    return gemv_entry(y, x, packed, scales, in, rows, group, true, stream);
 }
 
 int k3g_quantize_i8_groups(int8_t *q, float *s, const float *x, int n_rows, int in, void *stream) {
@@ -260,9 +278,9 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
     char *w = (char *)ws;
     float *h = (float *)(w + L.h);
     hipStream_t st = S(stream);
-    if (mode == K3G_EXACT) {
-        K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, st));
-        return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, st);
+    if (base_mode(mode) == K3G_EXACT) {
+        K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut_of(mode), st));
+        return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, lut_of(mode), st);
     }
     int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
     float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
@@ -328,17 +346,19 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
         case K3G_STAGE_BUCKET:
             return launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
         case K3G_STAGE_QUANT_X:
-            return mode == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, st) : K3G_OK;
+            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, st) : K3G_OK;
         case K3G_STAGE_UP:
-            return mode == K3G_IDOT
+            return base_mode(mode) == K3G_IDOT
                        ? launch_moe_up_idot(h, xq, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
-                       : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P, st);
+                       : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P,
+                                             lut_of(mode), st);
         case K3G_STAGE_QUANT_H:
-            return mode == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, st) : K3G_OK;
+            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, st) : K3G_OK;
         case K3G_STAGE_DOWN:
-            return mode == K3G_IDOT
+            return base_mode(mode) == K3G_IDOT
                        ? launch_moe_down_idot(ypair, hq, hs, b, active, offsets, perm, latent, inter, max_slots, st)
-                       : launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots, st);
+                       : launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots,
+                                               lut_of(mode), st);
         case K3G_STAGE_COMBINE:
             return launch_combine(y, ypair, wts, inv, n_tokens, top_k, latent, st);
         default:

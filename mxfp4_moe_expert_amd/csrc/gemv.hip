@@ -14,6 +14,25 @@
 // kernels, one expert), so x is fetched once per item.
 #include "k3g_common.h"
 
+// Build-time knobs (defaults are the shipped configuration).
+#ifndef K3G_GEMV_THREADS
+#define K3G_GEMV_THREADS 256
+#endif
+#ifndef K3G_WAVES_PER_EU
+#define K3G_WAVES_PER_EU 0  // 0: let the compiler choose the register budget
+#endif
+#if K3G_WAVES_PER_EU
+#define K3G_OCC __attribute__((amdgpu_waves_per_eu(K3G_WAVES_PER_EU)))
+#else
+#define K3G_OCC
+#endif
+#ifndef K3G_PIPE
+#define K3G_PIPE 3  // rows (per matrix) a wavefront keeps in flight
+#endif
+#ifndef K3G_ITEMS_TARGET
+#define K3G_ITEMS_TARGET 2048  // work items a decode launch is cut into
+#endif
+
 namespace k3g {
 
 template <int NG>
@@ -24,25 +43,68 @@ struct RowData {
 
 // Loads are unconditional so that the compiler can count them: a lane past
 // the last group reads group ngrp-1 again, and row_partial drops it (the
-// lane's `valid` bits).
+// lane's `valid` bits). The row pointers are wave-uniform (SGPRs); each lane
+// adds its own constant byte offset, so no per-lane address arithmetic is
+// repeated per row.
 template <int NG>
-__device__ inline void load_row(RowData<NG> &d, const uint8_t *prow, const uint8_t *srow, int lane, int ngrp) {
+struct LaneCols {
+    uint32_t pk[NG];  // byte offset of the lane's group i in a packed row
+    uint32_t sc[NG];  // its index in a row of scale bytes
+};
+
+template <int NG>
+__device__ inline LaneCols<NG> lane_cols(int lane, int ngrp) {
+    LaneCols<NG> c;
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int g = lane * NG + i;
         const int gc = g < ngrp ? g : ngrp - 1;
-        d.w[i] = load16(prow + (size_t)gc * 16);
-        d.s[i] = srow[gc];
+        c.pk[i] = (uint32_t)gc * 16u;
+        c.sc[i] = (uint32_t)gc;
     }
+    return c;
+}
+
+// One MXFP4 matrix as two buffer resources plus its row pitches.
+struct MatRef {
+    rsrc_t p, s;
+    uint32_t pitch_p, pitch_s;
+};
+
+__device__ inline MatRef mat_ref(const uint8_t *packed, const uint8_t *scales, int rows, int in) {
+    MatRef m;
+    m.pitch_p = (uint32_t)in / 2;
+    m.pitch_s = (uint32_t)in / kGroup;
+    m.p = make_rsrc(packed, m.pitch_p * (uint32_t)rows);
+    m.s = make_rsrc(scales, m.pitch_s * (uint32_t)rows);
+    return m;
 }
 
 template <int NG>
+__device__ inline void load_row(RowData<NG> &d, const MatRef &m, int r, const LaneCols<NG> &c) {
+    const uint32_t op = (uint32_t)r * m.pitch_p, os = (uint32_t)r * m.pitch_s;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        d.w[i] = buf_load16(m.p, c.pk[i], op);
+        d.s[i] = buf_load8(m.s, c.sc[i], os);
+    }
+}
+
+// Decode: LUT = the byte-pair table in LDS; otherwise gfx950's FP4 convert.
+template <int NG, bool LUT>
 __device__ inline float row_partial(const RowData<NG> &d, const uint32_t *lut, uint32_t lane_off, const float *xr,
                                    uint32_t valid) {
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-        const float sub = group_dot(lut, lane_off, d.w[i], xr + i * kGroup);
+        float sub;
+        if constexpr (LUT) {
+            sub = group_dot(lut, lane_off, d.w[i], xr + i * kGroup);
+        } else {
+            sub = group_dot_cvt(d.w[i], xr + i * kGroup);
+            (void)lut;
+            (void)lane_off;
+        }
         p += ((valid >> i) & 1u) ? apply_scale(sub, d.s[i]) : 0.0f;
     }
     return p;
@@ -78,40 +140,50 @@ __device__ inline void load_x(float *xr, const float *x, int lane, int ngrp) {
 }
 
 // y[r] for r in [0, rows): one matrix, one x. Items of rpi rows.
-template <int NG>
-__global__ __launch_bounds__(256) void gemv_kernel(float *__restrict__ y, const float *__restrict__ x,
+template <int NG, bool LUT>
+__global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *__restrict__ y, const float *__restrict__ x,
                                                    const uint8_t *__restrict__ packed,
                                                    const uint8_t *__restrict__ scales, int in, int rows, int rpi) {
-    __shared__ uint32_t lut[kLutWords];
-    build_pair_lut(lut);
-    __syncthreads();
+    uint32_t *lut = nullptr;
+    if constexpr (LUT) {
+        __shared__ uint32_t lut_lds[kLutWords];
+        build_pair_lut(lut_lds);
+        __syncthreads();
+        lut = lut_lds;
+    }
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int waves = blockDim.x / kWave;
     const uint32_t lane_off = uint32_t(lane) << 2;
     const int ngrp = in / kGroup;
-    const size_t rowbytes = (size_t)in / 2;
     const uint32_t valid = valid_groups<NG>(lane, ngrp);
+    const LaneCols<NG> cols = lane_cols<NG>(lane, ngrp);
+    const MatRef mat = mat_ref(packed, scales, rows, in);
     float xr[NG * kGroup];
     load_x<NG>(xr, x, lane, ngrp);
     const int n_items = (rows + rpi - 1) / rpi;
     for (int item = blockIdx.x * waves + wave; item < n_items; item += gridDim.x * waves) {
         const int r0 = item * rpi;
         const int r1 = min(rows, r0 + rpi);
-        auto P = [&](int r) { return packed + (size_t)min(r, r1 - 1) * rowbytes; };
-        auto Q = [&](int r) { return scales + (size_t)min(r, r1 - 1) * ngrp; };
-        RowData<NG> a, b;
-        load_row<NG>(a, P(r0), Q(r0), lane, ngrp);
-        load_row<NG>(b, P(r0 + 1), Q(r0 + 1), lane, ngrp);
-        for (int r = r0; r < r1; r += 2) {
-            const float sa = wave_sum(row_partial<NG>(a, lut, lane_off, xr, valid));
-            load_row<NG>(a, P(r + 2), Q(r + 2), lane, ngrp);
-            if (lane == 0) y[r] = sa;
-            if (r + 1 < r1) {
-                const float sb = wave_sum(row_partial<NG>(b, lut, lane_off, xr, valid));
-                if (lane == 0) y[r + 1] = sb;
+        auto R = [&](int r) { return min(r, r1 - 1); };
+        RowData<NG> buf[K3G_PIPE];
+#pragma unroll
+        for (int st = 0; st < K3G_PIPE; ++st) load_row<NG>(buf[st], mat, R(r0 + st), cols);
+        float acc = 0.f;  // lane k holds row (r - r0) % 64 == k until its block of 64 is stored
+        for (int r = r0; r < r1; r += K3G_PIPE) {
+#pragma unroll
+            for (int st = 0; st < K3G_PIPE; ++st) {
+                const int rr = r + st;
+                if (rr < r1) {
+                    const float sa = wave_sum(row_partial<NG, LUT>(buf[st], lut, lane_off, xr, valid));
+                    const int k = (rr - r0) & (kWave - 1);
+                    acc = lane == k ? sa : acc;
+                    if (k == kWave - 1 || rr == r1 - 1) {
+                        if (lane <= k) y[rr - k + lane] = acc;
+                    }
+                }
+                load_row<NG>(buf[st], mat, R(rr + K3G_PIPE), cols);
             }
-            load_row<NG>(b, P(r + 3), Q(r + 3), lane, ngrp);
         }
     }
 }
@@ -121,21 +193,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(float *__restrict__ y, const 
 // positions [offsets[e], offsets[e+1]), token = perm[pos] / top_k. For each
 // pair and row r: g = w1[r].x, u = w3[r].x, h[pos][r] = SiTU(g, u).
 // With perm == nullptr the call is one expert (bank expert 0) on token 0.
-template <int NG>
-__global__ __launch_bounds__(256) void moe_up_exact_kernel(
+template <int NG, bool LUT>
+__global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
     float *__restrict__ h, const float *__restrict__ x, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int latent, int inter,
     int max_slots, int rpi) {
-    __shared__ uint32_t lut[kLutWords];
-    build_pair_lut(lut);
-    __syncthreads();
+    uint32_t *lut = nullptr;
+    if constexpr (LUT) {
+        __shared__ uint32_t lut_lds[kLutWords];
+        build_pair_lut(lut_lds);
+        __syncthreads();
+        lut = lut_lds;
+    }
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int waves = blockDim.x / kWave;
     const uint32_t lane_off = uint32_t(lane) << 2;
     const int ngrp = latent / kGroup;
-    const size_t rowbytes = (size_t)latent / 2;
     const uint32_t valid = valid_groups<NG>(lane, ngrp);
+    const LaneCols<NG> cols = lane_cols<NG>(lane, ngrp);
     const int chunks = (inter + rpi - 1) / rpi;
     const int n_act = perm ? active[0] : 1;
     const int n_items = max_slots * chunks;
@@ -148,35 +224,39 @@ __global__ __launch_bounds__(256) void moe_up_exact_kernel(
         const int p0 = perm ? offsets[e] : 0;
         const int p1 = perm ? offsets[e + 1] : 1;
         const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
-        const uint8_t *w1p = eb + bank.off[W1P], *w1s = eb + bank.off[W1S];
-        const uint8_t *w3p = eb + bank.off[W3P], *w3s = eb + bank.off[W3S];
+        const MatRef m1 = mat_ref(eb + bank.off[W1P], eb + bank.off[W1S], inter, latent);
+        const MatRef m3 = mat_ref(eb + bank.off[W3P], eb + bank.off[W3S], inter, latent);
         const int r0 = chunk * rpi;
         const int r1 = min(inter, r0 + rpi);
-        auto P1 = [&](int r) { return w1p + (size_t)min(r, r1 - 1) * rowbytes; };
-        auto S1 = [&](int r) { return w1s + (size_t)min(r, r1 - 1) * ngrp; };
-        auto P3 = [&](int r) { return w3p + (size_t)min(r, r1 - 1) * rowbytes; };
-        auto S3 = [&](int r) { return w3s + (size_t)min(r, r1 - 1) * ngrp; };
+        auto R = [&](int r) { return min(r, r1 - 1); };
         for (int pos = p0; pos < p1; ++pos) {
             const int t = perm ? perm[pos] / top_k : 0;
             load_x<NG>(xr, x + (size_t)t * latent, lane, ngrp);
-            RowData<NG> a1, a3, b1, b3;
-            load_row<NG>(a1, P1(r0), S1(r0), lane, ngrp);
-            load_row<NG>(a3, P3(r0), S3(r0), lane, ngrp);
-            load_row<NG>(b1, P1(r0 + 1), S1(r0 + 1), lane, ngrp);
-            load_row<NG>(b3, P3(r0 + 1), S3(r0 + 1), lane, ngrp);
-            for (int r = r0; r < r1; r += 2) {
-                const float ga = wave_sum(row_partial<NG>(a1, lut, lane_off, xr, valid));
-                const float ua = wave_sum(row_partial<NG>(a3, lut, lane_off, xr, valid));
-                load_row<NG>(a1, P1(r + 2), S1(r + 2), lane, ngrp);
-                load_row<NG>(a3, P3(r + 2), S3(r + 2), lane, ngrp);
-                if (lane == 0) h[(size_t)pos * inter + r] = situ(ga, ua);
-                if (r + 1 < r1) {
-                    const float gb = wave_sum(row_partial<NG>(b1, lut, lane_off, xr, valid));
-                    const float ub = wave_sum(row_partial<NG>(b3, lut, lane_off, xr, valid));
-                    if (lane == 0) h[(size_t)pos * inter + r + 1] = situ(gb, ub);
+            RowData<NG> b1[K3G_PIPE], b3[K3G_PIPE];
+#pragma unroll
+            for (int st = 0; st < K3G_PIPE; ++st) {
+                load_row<NG>(b1[st], m1, R(r0 + st), cols);
+                load_row<NG>(b3[st], m3, R(r0 + st), cols);
+            }
+            float gv = 0.f, uv = 0.f;  // lane k holds row k of the current block of 64
+            for (int r = r0; r < r1; r += K3G_PIPE) {
+#pragma unroll
+                for (int st = 0; st < K3G_PIPE; ++st) {
+                    const int rr = r + st;
+                    if (rr < r1) {
+                        const float g = wave_sum(row_partial<NG, LUT>(b1[st], lut, lane_off, xr, valid));
+                        const float u = wave_sum(row_partial<NG, LUT>(b3[st], lut, lane_off, xr, valid));
+                        const int k = (rr - r0) & (kWave - 1);
+                        gv = lane == k ? g : gv;
+                        uv = lane == k ? u : uv;
+                        if (k == kWave - 1 || rr == r1 - 1) {
+                            // SiTU once per block, one row per lane
+                            if (lane <= k) h[(size_t)pos * inter + rr - k + lane] = situ(gv, uv);
+                        }
+                    }
+                    load_row<NG>(b1[st], m1, R(r + st + K3G_PIPE), cols);
+                    load_row<NG>(b3[st], m3, R(r + st + K3G_PIPE), cols);
                 }
-                load_row<NG>(b1, P1(r + 3), S1(r + 3), lane, ngrp);
-                load_row<NG>(b3, P3(r + 3), S3(r + 3), lane, ngrp);
             }
         }
     }
@@ -184,21 +264,25 @@ __global__ __launch_bounds__(256) void moe_up_exact_kernel(
 
 // Grouped down-projection: ypair[pos][r] = w2[r] . h[pos] for every pair of
 // the slot's expert. Same items as the up kernel, over latent rows.
-template <int NG>
-__global__ __launch_bounds__(256) void moe_down_exact_kernel(
+template <int NG, bool LUT>
+__global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kernel(
     float *__restrict__ ypair, const float *__restrict__ h, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int latent, int inter,
     int max_slots, int rpi) {
-    __shared__ uint32_t lut[kLutWords];
-    build_pair_lut(lut);
-    __syncthreads();
+    uint32_t *lut = nullptr;
+    if constexpr (LUT) {
+        __shared__ uint32_t lut_lds[kLutWords];
+        build_pair_lut(lut_lds);
+        __syncthreads();
+        lut = lut_lds;
+    }
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int waves = blockDim.x / kWave;
     const uint32_t lane_off = uint32_t(lane) << 2;
     const int ngrp = inter / kGroup;
-    const size_t rowbytes = (size_t)inter / 2;
     const uint32_t valid = valid_groups<NG>(lane, ngrp);
+    const LaneCols<NG> cols = lane_cols<NG>(lane, ngrp);
     const int chunks = (latent + rpi - 1) / rpi;
     const int n_act = perm ? active[0] : 1;
     const int n_items = max_slots * chunks;
@@ -211,25 +295,30 @@ __global__ __launch_bounds__(256) void moe_down_exact_kernel(
         const int p0 = perm ? offsets[e] : 0;
         const int p1 = perm ? offsets[e + 1] : 1;
         const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
-        const uint8_t *w2p = eb + bank.off[W2P], *w2s = eb + bank.off[W2S];
+        const MatRef m2 = mat_ref(eb + bank.off[W2P], eb + bank.off[W2S], latent, inter);
         const int r0 = chunk * rpi;
         const int r1 = min(latent, r0 + rpi);
-        auto P2 = [&](int r) { return w2p + (size_t)min(r, r1 - 1) * rowbytes; };
-        auto S2 = [&](int r) { return w2s + (size_t)min(r, r1 - 1) * ngrp; };
+        auto R = [&](int r) { return min(r, r1 - 1); };
         for (int pos = p0; pos < p1; ++pos) {
             load_x<NG>(xr, h + (size_t)pos * inter, lane, ngrp);
-            RowData<NG> a, b;
-            load_row<NG>(a, P2(r0), S2(r0), lane, ngrp);
-            load_row<NG>(b, P2(r0 + 1), S2(r0 + 1), lane, ngrp);
-            for (int r = r0; r < r1; r += 2) {
-                const float sa = wave_sum(row_partial<NG>(a, lut, lane_off, xr, valid));
-                load_row<NG>(a, P2(r + 2), S2(r + 2), lane, ngrp);
-                if (lane == 0) ypair[(size_t)pos * latent + r] = sa;
-                if (r + 1 < r1) {
-                    const float sb = wave_sum(row_partial<NG>(b, lut, lane_off, xr, valid));
-                    if (lane == 0) ypair[(size_t)pos * latent + r + 1] = sb;
+            RowData<NG> buf[K3G_PIPE];
+#pragma unroll
+            for (int st = 0; st < K3G_PIPE; ++st) load_row<NG>(buf[st], m2, R(r0 + st), cols);
+            float acc = 0.f;  // lane k holds row k of the current block of 64
+            for (int r = r0; r < r1; r += K3G_PIPE) {
+#pragma unroll
+                for (int st = 0; st < K3G_PIPE; ++st) {
+                    const int rr = r + st;
+                    if (rr < r1) {
+                        const float sa = wave_sum(row_partial<NG, LUT>(buf[st], lut, lane_off, xr, valid));
+                        const int k = (rr - r0) & (kWave - 1);
+                        acc = lane == k ? sa : acc;
+                        if (k == kWave - 1 || rr == r1 - 1) {
+                            if (lane <= k) ypair[(size_t)pos * latent + rr - k + lane] = acc;
+                        }
+                    }
+                    load_row<NG>(buf[st], m2, R(r + st + K3G_PIPE), cols);
                 }
-                load_row<NG>(b, P2(r + 3), S2(r + 3), lane, ngrp);
             }
         }
     }
@@ -284,7 +373,7 @@ static int grid_for(int items, int waves_per_block) {
     return need < 1024 ? (need < 1 ? 1 : need) : 1024;
 }
 
-int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
+int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows, bool lut,
                 hipStream_t st) {
     const int ngrp = in / kGroup;
     const int ng = pick_ng(ngrp);
@@ -292,49 +381,49 @@ int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *
     int rpi = rows / 2048;
     if (rpi < 2) rpi = 2;
     const int items = (rows + rpi - 1) / rpi;
-    const dim3 grid(grid_for(items, 4)), block(256);
+    const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
     switch (ng) {
-        case 1: gemv_kernel<1><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
-        case 2: gemv_kernel<2><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
-        case 4: gemv_kernel<4><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        case 1: if (lut) gemv_kernel<1, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<1, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        case 2: if (lut) gemv_kernel<2, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<2, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        case 4: if (lut) gemv_kernel<4, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<4, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
         default: return K3G_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
 int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
-                        const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs,
+                        const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
                         hipStream_t st) {
     const int ng = pick_ng(latent / kGroup);
     // rows per item: about 2048 items in all when each expert has one pair
-    int rpi = (int)(((int64_t)max_slots * inter + 2047) / 2048);
+    int rpi = (int)(((int64_t)max_slots * inter + K3G_ITEMS_TARGET - 1) / K3G_ITEMS_TARGET);
     if (rpi < 8) rpi = 8;
     if (rpi > inter) rpi = inter;
     (void)n_pairs;
     const int items = max_slots * ((inter + rpi - 1) / rpi);
-    const dim3 grid(grid_for(items, 4)), block(256);
+    const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
     switch (ng) {
-        case 1: moe_up_exact_kernel<1><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
-        case 2: moe_up_exact_kernel<2><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
-        case 4: moe_up_exact_kernel<4><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
+        case 1: if (lut) moe_up_exact_kernel<1, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); else moe_up_exact_kernel<1, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
+        case 2: if (lut) moe_up_exact_kernel<2, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); else moe_up_exact_kernel<2, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
+        case 4: if (lut) moe_up_exact_kernel<4, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); else moe_up_exact_kernel<4, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
         default: return K3G_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
 int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
-                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots, bool lut,
                           hipStream_t st) {
     const int ng = pick_ng(inter / kGroup);
-    int rpi = (int)(((int64_t)max_slots * latent + 2047) / 2048);
+    int rpi = (int)(((int64_t)max_slots * latent + K3G_ITEMS_TARGET - 1) / K3G_ITEMS_TARGET);
     if (rpi < 8) rpi = 8;
     if (rpi > latent) rpi = latent;
     const int items = max_slots * ((latent + rpi - 1) / rpi);
-    const dim3 grid(grid_for(items, 4)), block(256);
+    const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
     switch (ng) {
-        case 1: moe_down_exact_kernel<1><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
-        case 2: moe_down_exact_kernel<2><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
-        case 4: moe_down_exact_kernel<4><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
+        case 1: if (lut) moe_down_exact_kernel<1, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); else moe_down_exact_kernel<1, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
+        case 2: if (lut) moe_down_exact_kernel<2, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); else moe_down_exact_kernel<2, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
+        case 4: if (lut) moe_down_exact_kernel<4, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); else moe_down_exact_kernel<4, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
         default: return K3G_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;

@@ -84,6 +84,29 @@ __device__ inline float group_dot(const uint32_t *lut, uint32_t lane_off, uint4 
     return a0 + a1;
 }
 
+// The same group sum with gfx950's scaled FP4 -> FP32 conversion instead of
+// the LDS table: one v_cvt_scalef32_pk_f32_fp4 decodes the two nibbles of a
+// byte (scale 1.0, so the values are the raw e2m1 ones).
+template <int B>
+__device__ inline void cvt_byte(uint32_t w, const float *xq, float &a0, float &a1) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+    a0 = __builtin_fmaf(v[0], xq[2 * B], a0);
+    a1 = __builtin_fmaf(v[1], xq[2 * B + 1], a1);
+}
+
+__device__ inline float group_dot_cvt(uint4 w, const float *xg) {
+    float a0 = 0.f, a1 = 0.f;
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        cvt_byte<0>(d[q], xg + q * 8, a0, a1);
+        cvt_byte<1>(d[q], xg + q * 8, a0, a1);
+        cvt_byte<2>(d[q], xg + q * 8, a0, a1);
+        cvt_byte<3>(d[q], xg + q * 8, a0, a1);
+    }
+    return a0 + a1;
+}
+
 // Apply one group's ue8m0 scale: 2^(s-127) * sub, or nothing for s = 255.
 __device__ inline float apply_scale(float sub, uint32_t s) {
     return s == 255u ? 0.0f : __builtin_ldexpf(sub, int(s) - 127);
@@ -121,5 +144,25 @@ __device__ inline float situ(float g, float u) {
 }
 
 __device__ inline uint4 load16(const uint8_t *p) { return *(const uint4 *)p; }
+
+// Buffer resources: a wave-uniform base and byte range in SGPRs. A buffer load
+// adds a per-lane VGPR offset and a wave-uniform SGPR offset, so per-row address
+// arithmetic stays on the scalar unit, and any byte past the range reads as 0.
+// 0x00020000 is the resource word-3 value for raw (untyped) access on gfx9-class
+// parts.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ inline uint32_t buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
 
 }  // namespace k3g

@@ -118,70 +118,126 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(double *__restrict__ 
         }
 }
 
-// ---- top-k: one workgroup per token, bitonic sort in LDS ----------------------
-// Keys are (biased score, expert id) with "larger score first, equal scores to
-// the lower id" as the order; the sort is a bitonic network over the next
-// power of two >= E (padding sorts last), so the first top_k entries are the
-// selection in output order.
-constexpr int TK_THREADS = 1024;
-
+// ---- top-k: one wavefront per token, candidates in registers ---------------------
+// The order is "larger biased score first, equal scores to the lower expert
+// id". Round k picks, over all lanes, the best candidate that comes strictly
+// after round k-1's winner, so nothing has to be marked as taken. The
+// cross-lane arg-max uses DPP within each row of 16 lanes and readlane across
+// the four rows: no LDS and no barriers.
 __device__ inline bool before(double va, int ia, double vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+    // bitwise, not short-circuit: straight-line compares and selects, no branches
+    return (va > vb) | ((va == vb) & (ia < ib));
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(int32_t *__restrict__ idx, float *__restrict__ wts,
-                                                          const double *__restrict__ logits,
-                                                          const float *__restrict__ bias, int T, int E, int K,
-                                                          int n_pow2) {
-    extern __shared__ double smem[];
-    double *key = smem;                       // [n_pow2] biased score
-    double *sc = smem + n_pow2;               // [E] raw sigmoid score by expert id
-    int *id = (int *)(smem + n_pow2 + E);     // [n_pow2] expert id
-    const int tid = threadIdx.x;
-    for (int t = blockIdx.x; t < T; t += gridDim.x) {
-        for (int e = tid; e < n_pow2; e += TK_THREADS) {
-            if (e < E) {
-                const double s = 1.0 / (1.0 + exp(-logits[(size_t)t * E + e]));
-                sc[e] = s;
-                key[e] = s + (double)bias[e];
-                id[e] = e;
-            } else {
-                key[e] = -__builtin_inf();
-                id[e] = 0x7fffffff;
-            }
+template <int CTRL>
+__device__ inline void dpp_best(double &v, int &i) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+    const double ov = __hiloint2double(hi, lo);
+    const bool take = before(ov, oi, v, i);
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+
+__device__ inline void wave_best(double &v, int &i) {
+    dpp_best<0xB1>(v, i);   // quad_perm [1,0,3,2]
+    dpp_best<0x4E>(v, i);   // quad_perm [2,3,0,1]
+    dpp_best<0x141>(v, i);  // row_half_mirror
+    dpp_best<0x140>(v, i);  // row_mirror: every lane of a row holds the row's best
+    double bv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 0),
+                                 __builtin_amdgcn_readlane(__double2loint(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+        const double rv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), r),
+                                           __builtin_amdgcn_readlane(__double2loint(v), r));
+        const int ri = __builtin_amdgcn_readlane(i, r);
+        if (before(rv, ri, bv, bi)) {
+            bv = rv;
+            bi = ri;
         }
-        __syncthreads();
-        for (int k = 2; k <= n_pow2; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = tid; i < n_pow2; i += TK_THREADS) {
-                    const int l = i ^ j;
+    }
+    v = bv;
+    i = bi;
+}
+
+__device__ inline double sigmoid64(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+// Compare-exchange of register slots a < b so that slot a holds the one that
+// comes first in the selection order.
+template <int NV>
+__device__ inline void cex(double (&v)[NV], int (&id)[NV], int a, int b) {
+    const bool sw = before(v[b], id[b], v[a], id[a]);
+    const double va = v[a], vb = v[b];
+    const int ia = id[a], ib = id[b];
+    v[a] = sw ? vb : va;
+    v[b] = sw ? va : vb;
+    id[a] = sw ? ib : ia;
+    id[b] = sw ? ia : ib;
+}
+
+// Each lane first sorts its NV candidates (a bitonic network over register
+// slots, all indices compile-time); then every round the lanes' heads compete
+// and the winning lane shifts its list by one. No per-round scan, no LDS.
+template <int NV>
+__global__ __launch_bounds__(64) void topk_kernel(int32_t *__restrict__ idx, float *__restrict__ wts,
+                                                  const double *__restrict__ logits, const float *__restrict__ bias,
+                                                  int T, int E, int K) {
+    const int lane = threadIdx.x;
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+        const double *lg = logits + (size_t)t * E;
+        double v[NV];
+        int id[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = lane + j * kWave;
+            const int ec = e < E ? e : E - 1;
+            const double b = sigmoid64(lg[ec]) + (double)bias[ec];
+            v[j] = e < E ? b : -__builtin_inf();
+            id[j] = e < E ? e : 0x7fffffff;
+        }
+#pragma unroll
+        for (int k = 2; k <= NV; k <<= 1)
+#pragma unroll
+            for (int jj = k >> 1; jj > 0; jj >>= 1)
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int l = i ^ jj;
                     if (l > i) {
-                        const double a = key[i], b = key[l];
-                        const int ia = id[i], ib = id[l];
-                        // blocks with (i & k) == 0 end up in output order, the others reversed
-                        const bool want_first = (i & k) == 0;
-                        const bool l_first = before(b, ib, a, ia);
-                        if (want_first == l_first) {
-                            key[i] = b; key[l] = a;
-                            id[i] = ib; id[l] = ia;
-                        }
+                        if ((i & k) == 0)
+                            cex<NV>(v, id, i, l);
+                        else
+                            cex<NV>(v, id, l, i);
                     }
                 }
-                __syncthreads();
+        int my_id = 0;  // lane k keeps the k-th winner
+        for (int k = 0; k < K; ++k) {
+            double bv = v[0];
+            int bi = id[0];
+            wave_best(bv, bi);
+            if (bi >= E) bi = 0;  // only with non-finite scores, outside the contract
+            my_id = lane == k ? bi : my_id;
+            const bool me = id[0] == bi;  // the winner sits at the head of its lane's list
+#pragma unroll
+            for (int j = 0; j < NV - 1; ++j) {
+                v[j] = me ? v[j + 1] : v[j];
+                id[j] = me ? id[j + 1] : id[j];
             }
+            v[NV - 1] = me ? -__builtin_inf() : v[NV - 1];
+            id[NV - 1] = me ? 0x7fffffff : id[NV - 1];
         }
-        if (tid == 0) {
-            double sum = 0.0;
-            for (int k = 0; k < K; ++k) sum += sc[id[k]];
-            key[0] = sum;  // the sorted key is not needed any more
+        // weights: each lane's raw score (the value its key was built from),
+        // summed in selection order, then renormalised
+        const double my_sc = lane < K ? sigmoid64(lg[my_id]) : 0.0;
+        double sum = 0.0;
+        for (int k = 0; k < K; ++k)
+            sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_sc), k),
+                                    __builtin_amdgcn_readlane(__double2loint(my_sc), k));
+        if (lane < K) {
+            idx[(size_t)t * K + lane] = my_id;
+            wts[(size_t)t * K + lane] = (float)(my_sc / sum);
         }
-        __syncthreads();
-        if (tid < K) {
-            const int e = id[tid];
-            idx[(size_t)t * K + tid] = e;
-            wts[(size_t)t * K + tid] = (float)(sc[e] / key[0]);
-        }
-        __syncthreads();
     }
 }
 
@@ -310,11 +366,12 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
 int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K,
                 hipStream_t st) {
     if (T == 0) return K3G_OK;
-    int n_pow2 = 1;
-    while (n_pow2 < E) n_pow2 <<= 1;
-    const int blocks = T < 8192 ? T : 8192;
-    const size_t lds = sizeof(double) * (size_t)(n_pow2 + E) + sizeof(int) * (size_t)n_pow2;
-    topk_kernel<<<blocks, TK_THREADS, lds, st>>>(idx, wts, logits, bias, T, E, K, n_pow2);
+    const int blocks = T < 65536 ? T : 65536;
+    const int nv = (E + kWave - 1) / kWave;
+    if (nv <= 16)
+        topk_kernel<16><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K);
+    else
+        topk_kernel<32><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

@@ -58,18 +58,23 @@ GEMV_CASES = [
 ]
 
 
+DECODES = [False, True]  # hardware FP4 convert, LDS byte-pair table
+
+
+@pytest.mark.parametrize("lut", DECODES, ids=["cvt", "lut"])
 @pytest.mark.parametrize("rows,n_in,lo,hi,p", GEMV_CASES)
-def test_gemv_matches_oracle(k3g, rows, n_in, lo, hi, p):
-    print(f"gemv rows={rows} in={n_in}", flush=True)
+def test_gemv_matches_oracle(k3g, rows, n_in, lo, hi, p, lut):
+    print(f"gemv rows={rows} in={n_in} lut={lut}", flush=True)
     pk, sc = synth.mxfp4_matrix(1000 + rows, 1, 0, rows, n_in, lo, hi, p)
     x = synth.activations(1000 + rows, 1, n_in)[0]
     y = torch.empty(rows, dtype=torch.float32, device="cuda")
-    k3g.k3g_mxfp4_gemv(y, dev(x), dev(pk), dev(sc))
+    k3g.k3g_mxfp4_gemv(y, dev(x), dev(pk), dev(sc), lut=lut)
     yo, _, nrm = oracle.mxfp4_gemv(x, pk, sc, full=True)
     assert_norm_close(host(y), yo, nrm, what=f"gemv {rows}x{n_in}")
 
 
-def test_gemv_edge_cases(k3g):
+@pytest.mark.parametrize("lut", DECODES, ids=["cvt", "lut"])
+def test_gemv_edge_cases(k3g, lut):
     rows, n_in = 70, 256
     pk, sc = synth.mxfp4_matrix(77, 1, 0, rows, n_in, 118, 132, 0.0)
     x = synth.activations(77, 1, n_in)[0]
@@ -80,20 +85,20 @@ def test_gemv_edge_cases(k3g):
     x_bad[32:64] = np.inf                 # non-finite x inside a skipped group of row 7 only
     pk[8, :] = 0x88                       # -0 everywhere: exactly 0
     y = torch.empty(rows, dtype=torch.float32, device="cuda")
-    k3g.k3g_mxfp4_gemv(y, dev(x), dev(pk), dev(sc))
+    k3g.k3g_mxfp4_gemv(y, dev(x), dev(pk), dev(sc), lut=lut)
     yo, _, nrm = oracle.mxfp4_gemv(x, pk, sc, full=True)
     yg = host(y)
     assert yg[5] == 0.0 and yg[8] == 0.0
     assert_norm_close(yg, yo, nrm)
     # the scale-255 group is dropped, not multiplied by zero
     y2 = torch.empty(1, dtype=torch.float32, device="cuda")
-    k3g.k3g_mxfp4_gemv(y2, dev(x_bad), dev(pk[7:8].copy()), dev(sc[7:8].copy()))
+    k3g.k3g_mxfp4_gemv(y2, dev(x_bad), dev(pk[7:8].copy()), dev(sc[7:8].copy()), lut=lut)
     yo2, _, n2 = oracle.mxfp4_gemv(x_bad, pk[7:8], sc[7:8], full=True)
     assert np.isfinite(host(y2)).all()
     assert_norm_close(host(y2), yo2, n2)
     # flipping every sign bit negates exactly
     yn = torch.empty(rows, dtype=torch.float32, device="cuda")
-    k3g.k3g_mxfp4_gemv(yn, dev(x), dev(pk ^ np.uint8(0x88)), dev(sc))
+    k3g.k3g_mxfp4_gemv(yn, dev(x), dev(pk ^ np.uint8(0x88)), dev(sc), lut=lut)
     assert np.array_equal(host(yn), -yg)
 
 
@@ -110,14 +115,14 @@ def test_gemv_deterministic(k3g):
 
 # ---- one expert -----------------------------------------------------------------
 
-def check_glu(k3g, ex, x, latent, inter, ws=None):
+def check_glu(k3g, ex, x, latent, inter, ws=None, decode=0):
     exd = {k: dev(v) for k, v in ex.items()}
     y = torch.empty(latent, dtype=torch.float32, device="cuda")
     sh = k3g.shape(latent=latent, inter=inter, mode=k3g.EXACT)
     if ws is None:
         ws = k3g.workspace(k3g.OP_EXPERT_GLU, sh)
     L = k3g.workspace_layout(k3g.OP_EXPERT_GLU, sh)
-    k3g.k3g_expert_glu(y, dev(x), exd, k3g.EXACT, ws)
+    k3g.k3g_expert_glu(y, dev(x), exd, k3g.EXACT | decode, ws)
     yg = host(y)
     hg = host(ws[L["h"]:L["h"] + 4 * inter].view(torch.float32))
     # stage 1: h against SiTU of the oracle's g, u, within the propagated bound
@@ -137,12 +142,13 @@ def check_glu(k3g, ex, x, latent, inter, ws=None):
     return yg
 
 
+@pytest.mark.parametrize("decode", [0, 0x100], ids=["cvt", "lut"])
 @pytest.mark.parametrize("lo,hi", [(118, 132), (120, 122)])
-def test_expert_glu_full_size(k3g, lo, hi):
-    print(f"expert glu scales {lo}..{hi}", flush=True)
+def test_expert_glu_full_size(k3g, lo, hi, decode):
+    print(f"expert glu scales {lo}..{hi} decode {decode:#x}", flush=True)
     ex = synth.expert(synth.SEED_BASE, 0, lo=lo, hi=hi)
     x = synth.activations(synth.SEED_BASE, 1)[0]
-    check_glu(k3g, ex, x, 3584, 3072)
+    check_glu(k3g, ex, x, 3584, 3072, decode=decode)
 
 
 def test_expert_glu_small_ragged(k3g):
@@ -179,6 +185,7 @@ def test_route_matches_oracle(k3g, T, n_in, E, K, bias):
 # ---- the MoE layer --------------------------------------------------------------------
 
 def run_layer(k3g, x, idx, wts, bank, mode):
+    """Run the layer; `mode` may carry the decode flag."""
     T = x.shape[0]
     K = idx.shape[1]
     y = torch.empty((T, bank.latent), dtype=torch.float32, device="cuda")
@@ -194,10 +201,10 @@ def ws_view(ws, L, name, count, dtype):
     return host(ws[L[name]:L[name] + nbytes]).view(dtype)
 
 
-def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None):
+def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0):
     T, K = idx.shape
     latent, inter = bank.latent, bank.inter
-    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT)
+    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | decode)
     P = T * K
     E = bank.n_experts
     perm = ws_view(ws, L, "perm", P, np.int32)
@@ -243,13 +250,14 @@ def make_bank(k3g, seed, E, latent, inter, lo=118, hi=132, p255=0.001):
     return src, bankt, bank
 
 
-def test_layer_small_ragged(k3g):
+@pytest.mark.parametrize("decode", [0, 0x100], ids=["cvt", "lut"])
+def test_layer_small_ragged(k3g, decode):
     E, latent, inter, T, K = 12, 128, 96, 9, 3
     src, bankt, bank = make_bank(k3g, 51, E, latent, inter, 120, 123, 0.01)
     x = synth.activations(51, T, latent)
     W, b = synth.router(51, E, latent, 0.2)
     idx, wts, _ = oracle.route(x, W, b, K)
-    y = check_layer_exact(k3g, src, bankt, bank, x, idx, wts)
+    y = check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=decode)
     # and end to end against the oracle's layer
     yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.EXACT)
     assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
@@ -276,7 +284,8 @@ def full_bank(k3g):
     torch.cuda.empty_cache()
 
 
-def test_layer_decode_b1_full(k3g, full_bank):
+@pytest.mark.parametrize("decode", [0, 0x100], ids=["cvt", "lut"])
+def test_layer_decode_b1_full(k3g, full_bank, decode):
     src, bankt, bank = full_bank
     W, b = synth.router(synth.SEED_BASE + 1, 896, 3584, 0.1)
     x = synth.activations(synth.SEED_BASE + 1, 1, 3584)
@@ -286,7 +295,7 @@ def test_layer_decode_b1_full(k3g, full_bank):
     k3g.k3g_moe_route(idx, wts, dev(x), dev(W), dev(b), 16, ws)
     io, wo, _ = oracle.route(x, W, b, 16)
     assert np.array_equal(host(idx), io)
-    check_layer_exact(k3g, src, None, bank, x, io, host(wts))
+    check_layer_exact(k3g, src, None, bank, x, io, host(wts), decode=decode)
 
 
 def test_layer_decode_b64_full_sampled(k3g, full_bank):
