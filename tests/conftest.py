@@ -26,3 +26,20 @@ def read_table(name):
 @pytest.fixture(scope="session")
 def golden():
     return read_table
+
+
+@pytest.fixture(scope="session")
+def full_bank():
+    """The 896-expert bank of the layer workloads (15.7 GB of HBM), shared by the GPU tests."""
+    import torch
+
+    import mxfp4_moe_expert_amd as k3g
+    import synth
+    from tests.helpers import make_bank
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    print("generating the 896-expert bank", flush=True)
+    src, bankt, bank = make_bank(k3g, synth.SEED_BASE + 1, 896, 3584, 3072)
+    yield src, bankt, bank
+    del bankt
+    torch.cuda.empty_cache()

@@ -82,3 +82,10 @@ class ExpertSource:
                 self.cache[e] = ex
             return ex
         return self.cache[e]
+
+
+def make_bank(k3g, seed, E, latent, inter, lo=118, hi=132, p255=0.001):
+    """A device bank of E seeded experts, and the host-side source of their bytes."""
+    src = ExpertSource(seed, latent, inter, lo, hi, p255)
+    bankt, bank = k3g.pack_bank(src, E, latent, inter)
+    return src, bankt, bank

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from tests.helpers import REL, ExpertSource, assert_norm_close, situ_tolerance
+from tests.helpers import REL, ExpertSource, assert_norm_close, situ_tolerance, make_bank
 
 pytestmark = pytest.mark.gpu
 
@@ -244,12 +244,6 @@ def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0)
     return y
 
 
-def make_bank(k3g, seed, E, latent, inter, lo=118, hi=132, p255=0.001):
-    src = ExpertSource(seed, latent, inter, lo, hi, p255)
-    bankt, bank = k3g.pack_bank(src, E, latent, inter)
-    return src, bankt, bank
-
-
 @pytest.mark.parametrize("decode", [0, 0x100], ids=["cvt", "lut"])
 def test_layer_small_ragged(k3g, decode):
     E, latent, inter, T, K = 12, 128, 96, 9, 3
@@ -271,17 +265,6 @@ def test_layer_skewed_routing(k3g):
     idx = np.stack([np.zeros(T, np.int32), (np.arange(T) % 5 + 1).astype(np.int32)], 1)
     wts = np.full((T, K), 0.5, np.float32)
     check_layer_exact(k3g, src, bankt, bank, x, idx, wts)
-
-
-@pytest.fixture(scope="module")
-def full_bank(k3g):
-    """The 896-expert bank of the decode workloads (15.7 GB of HBM)."""
-    seed = synth.SEED_BASE + 1
-    print("generating the 896-expert bank", flush=True)
-    src, bankt, bank = make_bank(k3g, seed, 896, 3584, 3072)
-    yield src, bankt, bank
-    del bankt
-    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("decode", [0, 0x100], ids=["cvt", "lut"])

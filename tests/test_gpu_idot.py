@@ -1,0 +1,186 @@
+"""GPU parity of the IDOT path (int8 activations, int8 matrix cores).
+
+Bit-exact: the quantised activations (q, s) and the int32 group sums. fp32
+outputs: within 1e-5 * sum_j |W_ij||a_j| of the oracle's IDOT result for the
+same quantised input, stage by stage ("Kimi K3 engine (c/kimi_k3.c)",
+"Streaming design", K3_IDOT).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import assert_norm_close, make_bank, situ_tolerance
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def k3g():
+    import mxfp4_moe_expert_amd as k
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    k.lib()
+    return k
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ws_view(ws, L, name, count, dtype):
+    nbytes = count * np.dtype(dtype).itemsize
+    return host(ws[L[name]:L[name] + nbytes]).view(dtype)
+
+
+@pytest.mark.parametrize("n,n_in,scale", [(1, 32, 1.0), (7, 96, 3.0), (64, 3584, 1.0), (300, 3072, 40.0)])
+def test_quantize_bit_exact(k3g, n, n_in, scale):
+    x = synth.activations(500 + n, n, n_in) * np.float32(scale)
+    if n > 2:
+        x[1, 32:64] = 0.0          # an all-zero group
+        x[2, :32] = np.float32(1e-30)
+        x[2, 5] = np.float32(-3e-30)
+    q = torch.empty((n, n_in), dtype=torch.int8, device="cuda")
+    s = torch.empty((n, n_in // 32), dtype=torch.float32, device="cuda")
+    k3g.k3g_quantize_i8_groups(q, s, dev(x))
+    qo, so = oracle.quant_i8_groups(x)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+def test_quantize_ties_to_even(k3g):
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 127.0
+    x[0, 1:9] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -3.5]
+    q = torch.empty((1, 32), dtype=torch.int8, device="cuda")
+    s = torch.empty((1, 1), dtype=torch.float32, device="cuda")
+    k3g.k3g_quantize_i8_groups(q, s, dev(x))
+    assert list(host(q)[0, :9]) == [127, 0, 2, 2, 0, -2, -2, 126, -4]
+
+
+@pytest.mark.parametrize("T,rows,n_in", [(1, 1, 32), (5, 37, 96), (33, 70, 256), (40, 96, 3584)])
+def test_groupsums_bit_exact(k3g, T, rows, n_in):
+    pk, _ = synth.mxfp4_matrix(600 + rows, 1, 0, rows, n_in)
+    q = synth.integers(600 + rows, 3, (T, n_in), -127, 127, np.int8)
+    q[0, :32] = 127
+    q[-1, -32:] = -127
+    sums = torch.empty((T, rows, n_in // 32), dtype=torch.int32, device="cuda")
+    k3g.k3g_mxfp4_idot_groupsums(sums, dev(q), dev(pk))
+    assert np.array_equal(host(sums), oracle.idot_groupsums(q, pk))
+
+
+def check_expert_idot(k3g, ex, x, latent, inter):
+    exd = {k: dev(v) for k, v in ex.items()}
+    y = torch.empty(latent, dtype=torch.float32, device="cuda")
+    sh = k3g.shape(latent=latent, inter=inter, mode=k3g.IDOT)
+    ws = k3g.workspace(k3g.OP_EXPERT_GLU, sh)
+    L = k3g.workspace_layout(k3g.OP_EXPERT_GLU, sh)
+    k3g.k3g_expert_glu(y, dev(x), exd, k3g.IDOT, ws)
+    yg = host(y)
+    xq = ws_view(ws, L, "xq", latent, np.int8)
+    xs = ws_view(ws, L, "xs", latent // 32, np.float32)
+    qo, so = oracle.quant_i8_groups(x)
+    assert np.array_equal(xq, qo[0]) and np.array_equal(xs, so[0])
+    g, _, ng = oracle.mxfp4_gemv_idot(qo, so, ex["w1p"], ex["w1s"], full=True)
+    u, _, nu = oracle.mxfp4_gemv_idot(qo, so, ex["w3p"], ex["w3s"], full=True)
+    hg = ws_view(ws, L, "h", inter, np.float32)
+    ho = oracle.situ_vec(g, u)
+    bad = np.abs(hg.astype(np.float64) - ho) > situ_tolerance(g, u, ng, nu)
+    assert not bad.any(), f"h: {bad.sum()} outside the bound, first {np.flatnonzero(bad)[:5]}"
+    hq = ws_view(ws, L, "hq", inter, np.int8)
+    hs = ws_view(ws, L, "hs", inter // 32, np.float32)
+    qh, sh_ = oracle.quant_i8_groups(hg)
+    assert np.array_equal(hq, qh[0]) and np.array_equal(hs, sh_[0])
+    y2, _, n2 = oracle.mxfp4_gemv_idot(qh, sh_, ex["w2p"], ex["w2s"], full=True)
+    assert_norm_close(yg, y2, n2, what="idot glu down")
+    return yg
+
+
+@pytest.mark.parametrize("lo,hi", [(118, 132), (120, 122)])
+def test_expert_glu_idot_full_size(k3g, lo, hi):
+    print(f"idot expert glu {lo}..{hi}", flush=True)
+    ex = synth.expert(synth.SEED_BASE, 0, lo=lo, hi=hi)
+    x = synth.activations(synth.SEED_BASE, 1)[0]
+    check_expert_idot(k3g, ex, x, 3584, 3072)
+
+
+def test_expert_glu_idot_small(k3g):
+    ex = synth.expert(43, 1, latent=96, inter=160, lo=121, hi=123, p255=0.03)
+    x = synth.activations(43, 1, 96)[0]
+    check_expert_idot(k3g, ex, x, 96, 160)
+
+
+def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
+    T, K = idx.shape
+    latent, inter, E = bank.latent, bank.inter, bank.n_experts
+    y = torch.empty((T, latent), dtype=torch.float32, device="cuda")
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=latent, inter=inter, mode=k3g.IDOT)
+    ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
+    k3g.k3g_moe_layer(y, dev(x), dev(idx), dev(wts), bank, k3g.IDOT, ws)
+    yg = host(y)
+    P = T * K
+    inv = ws_view(ws, L, "inv", P, np.int32)
+    xq = ws_view(ws, L, "xq", T * latent, np.int8).reshape(T, latent)
+    xs = ws_view(ws, L, "xs", T * latent // 32, np.float32).reshape(T, latent // 32)
+    qo, so = oracle.quant_i8_groups(x)
+    assert np.array_equal(xq, qo) and np.array_equal(xs.view(np.uint32), so.view(np.uint32))
+
+    def rows_of(name, count, dtype, width):
+        return lambda pos: ws_view_rows(ws, L, name, pos, width, dtype)
+
+    for t in tokens:
+        acc = np.zeros(latent)
+        nrm = np.zeros(latent)
+        for k in range(K):
+            e = int(idx[t, k])
+            ex = src(e)
+            pos = int(inv[t * K + k])
+            g, _, ng = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w1p"], ex["w1s"], full=True)
+            u, _, nu = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w3p"], ex["w3s"], full=True)
+            hg = ws_view_rows(ws, L, "h", pos, inter, np.float32)
+            bad = np.abs(hg.astype(np.float64) - oracle.situ_vec(g, u)) > situ_tolerance(g, u, ng, nu)
+            assert not bad.any(), (t, k, np.flatnonzero(bad)[:5])
+            hq = ws_view_rows(ws, L, "hq", pos, inter, np.int8)
+            hs = ws_view_rows(ws, L, "hs", pos, inter // 32, np.float32)
+            qh, sh_ = oracle.quant_i8_groups(hg)
+            assert np.array_equal(hq, qh[0]) and np.array_equal(hs, sh_[0])
+            y2, _, n2 = oracle.mxfp4_gemv_idot(qh, sh_, ex["w2p"], ex["w2s"], full=True)
+            yp = ws_view_rows(ws, L, "ypair", pos, latent, np.float32)
+            assert_norm_close(yp, y2, n2, what=f"idot down t={t} k={k}")
+            acc += float(wts[t, k]) * yp.astype(np.float64)
+            nrm += abs(float(wts[t, k])) * np.abs(yp.astype(np.float64))
+        assert_norm_close(yg[t], acc, nrm, what=f"idot combine t={t}")
+    return yg
+
+
+def ws_view_rows(ws, L, name, row, width, dtype):
+    it = np.dtype(dtype).itemsize
+    off = L[name] + row * width * it
+    return host(ws[off:off + width * it]).view(dtype)
+
+
+def test_layer_idot_small_many_tokens(k3g):
+    # 300 tokens on 8 experts, top 3: ~112 pairs per expert -> several token tiles and a second chunk
+    E, latent, inter, T, K = 8, 128, 96, 300, 3
+    src, bankt, bank = make_bank(k3g, 71, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(71, T, latent)
+    W, b = synth.router(71, E, latent, 0.1)
+    idx, wts, _ = oracle.route(x, W, b, K)
+    check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 1, 137, 299])
+
+
+def test_layer_idot_prefill_4096_sampled(k3g, full_bank):
+    src, bankt, bank = full_bank
+    seed = synth.SEED_BASE + 3
+    W, b = synth.router(seed, 896, 3584, 0.01)
+    x = synth.activations(seed, 4096, 3584)
+    print("routing 4096 tokens on the oracle", flush=True)
+    idx, wts, _ = oracle.route(x, W, b, 16)
+    check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 2047, 4095])
