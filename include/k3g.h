@@ -232,8 +232,13 @@ int k3g_moe_layer_stage(int stage, float *y, const float *x, const int32_t *idx,
                         void *ws, size_t ws_bytes, void *stream);
 
 /* The full LatentMoE block ([COLIBRI-K3] "Architecture notes"): route on x,
- * lat = W_down x, agg = layer(lat), n = RMSNorm(agg) * gamma, out = W_up n +
- * sum_s W2_s SiTU(W1_s x, W3_s x). out, x fp32 [T][hidden]. top_k as above. */
+ * lat = W_down x, agg = layer(lat), n = RMSNorm(agg) * gamma (eps =
+ * w->rms_eps, 1e-5 in [KIC-README]'s config), out = W_up n +
+ * sum_s W2_s SiTU(W1_s x, W3_s x) for the n_shared (0..2) shared experts,
+ * added unweighted. out, x fp32 [T][hidden]; x 16-byte aligned. bf16 weights
+ * are widened exactly and multiplied in fp32. top_k and the bank as for
+ * k3g_moe_layer; ws: k3g_workspace_bytes(K3G_OP_LATENT_BLOCK, ...) with
+ * hidden and sh_inter set. */
 int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w,
                          int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes,
                          void *stream);

@@ -174,7 +174,9 @@ def mxfp4(packed: torch.Tensor, scales: torch.Tensor) -> Mxfp4:
 
 
 def expert_struct(ex: dict) -> Expert:
-    return Expert(mxfp4(ex["w1p"], ex["w1s"]), mxfp4(ex["w3p"], ex["w3s"]), mxfp4(ex["w2p"], ex["w2s"]))
+    e = Expert(mxfp4(ex["w1p"], ex["w1s"]), mxfp4(ex["w3p"], ex["w3s"]), mxfp4(ex["w2p"], ex["w2s"]))
+    e._keep = dict(ex)  # the struct holds raw device pointers: keep the tensors alive with it
+    return e
 
 
 def bank_struct(base: torch.Tensor, n_experts: int, latent: int, inter: int, off=None, stride=None) -> ExpertBank:
@@ -183,7 +185,9 @@ def bank_struct(base: torch.Tensor, n_experts: int, latent: int, inter: int, off
         off, stride = bank_layout(latent, inter)
     if base.numel() < stride * n_experts:
         raise ValueError("bank tensor too small")
-    return ExpertBank(base.data_ptr(), stride, n_experts, latent, inter, (C.c_int64 * 6)(*off))
+    b = ExpertBank(base.data_ptr(), stride, n_experts, latent, inter, (C.c_int64 * 6)(*off))
+    b._keep = base  # the struct holds a raw device pointer: keep the tensor alive with it
+    return b
 
 
 # ---- entry points ----------------------------------------------------------
@@ -267,6 +271,28 @@ def k3g_moe_layer_stage(stage: int, y: torch.Tensor, x: torch.Tensor, idx: torch
                                                              C.byref(bank), T, K, mode, _ptr(ws), ws.numel(),
                                                              _stream(stream)))
     return y
+
+
+def block_struct(w_router, bias, w_down, w_up, gamma, sh_w1, sh_w3, sh_w2, bank: ExpertBank,
+                 rms_eps: float = 1e-5) -> BlockWeights:
+    """The dense weights of a LatentMoE block (device tensors; bf16 as int16/uint16 bits)."""
+    _dev(w_router, torch.float32, "w_router")
+    _dev(bias, torch.float32, "bias")
+    _dev(gamma, torch.float32, "gamma")
+    for name, t in (("w_down", w_down), ("w_up", w_up), *[(f"sh{i}", t) for i, t in enumerate(sh_w1 + sh_w3 + sh_w2)]):
+        if t.dtype not in (torch.int16, torch.uint16) or t.device.type != "cuda" or not t.is_contiguous():
+            raise TypeError(f"{name} must be contiguous bf16 bits (int16/uint16) on the GPU")
+    n_sh = len(sh_w1)
+    if not (len(sh_w3) == len(sh_w2) == n_sh) or n_sh > 2:
+        raise ValueError("up to two shared experts, each with w1, w3, w2")
+    p = lambda lst: (C.c_void_p * 2)(*[t.data_ptr() for t in lst] + [None] * (2 - len(lst)))  # noqa: E731
+    w = BlockWeights(w_router.data_ptr(), bias.data_ptr(), w_down.data_ptr(), w_up.data_ptr(), gamma.data_ptr(),
+                     p(sh_w1), p(sh_w3), p(sh_w2), n_sh, w_down.shape[1],
+                     sh_w1[0].shape[0] if n_sh else 0, rms_eps, bank)
+    # the struct holds raw device pointers: keep the tensors alive with it
+    w._keep = (w_router, bias, w_down, w_up, gamma, list(sh_w1), list(sh_w3), list(sh_w2),
+               getattr(bank, "_keep", None))
+    return w
 
 
 def k3g_latent_moe_block(out: torch.Tensor, x: torch.Tensor, w: BlockWeights, top_k: int, mode: int,

@@ -31,6 +31,15 @@ int launch_moe_up_idot(float *h, const int8_t *xq, const float *xs, const BankDe
 int launch_moe_down_idot(float *ypair, const int8_t *hq, const float *hs, const BankDev &bank, const int32_t *active,
                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
                          hipStream_t st);
+struct DenseSeg {
+    const uint16_t *w;
+    const float *x;
+    int K;
+};
+int launch_dense(float *out, const DenseSeg *segs, int n_seg, int T, int N, hipStream_t st);
+int launch_dense_glu(float *h, const uint16_t *w1, const uint16_t *w3, const float *x, int T, int K, int N,
+                     hipStream_t st);
+int launch_rmsnorm(float *n, const float *a, const float *gamma, int T, int len, float eps, hipStream_t st);
 }  // namespace k3g
 
 using namespace k3g;
@@ -115,14 +124,14 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
             if (!shape_ok_layer(s)) return K3G_EINVAL;
             const size_t P = T * s.top_k, E = s.n_experts;
             if (op == K3G_OP_LATENT_BLOCK) {
-                if (s.hidden <= 0 || s.sh_inter <= 0 || s.hidden % kGroup || s.sh_inter % kGroup) return K3G_EINVAL;
+                if (s.hidden <= 0 || s.sh_inter <= 0) return K3G_EINVAL;
                 o->logits = c.take(sizeof(double) * T * E);
                 o->idx = c.take(sizeof(int32_t) * P);
                 o->wts = c.take(sizeof(float) * P);
                 o->lat = c.take(sizeof(float) * T * s.latent);
                 o->agg = c.take(sizeof(float) * T * s.latent);
                 o->nrm = c.take(sizeof(float) * T * s.latent);
-                o->shh = c.take(sizeof(float) * T * s.sh_inter);
+                o->shh = c.take(sizeof(float) * 2 * (T ? T : 1) * s.sh_inter);  // [2][T][sh_inter]
             }
             o->counts = c.take(sizeof(int32_t) * E);
             o->offsets = c.take(sizeof(int32_t) * (E + 1));
@@ -388,6 +397,48 @@ int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts
 
 extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w, int n_tokens, int top_k,
                                     int mode, void *ws, size_t ws_bytes, void *stream) {
-    (void)out; (void)x; (void)w; (void)n_tokens; (void)top_k; (void)mode; (void)ws; (void)ws_bytes; (void)stream;
-    return K3G_EUNSUPPORTED;
+    if (!out || !x || !w || !ws || !w->w_router || !w->bias || !w->w_down || !w->w_up || !w->gamma || !w->bank.base)
+        return K3G_EINVAL;
+    if (w->n_shared < 0 || w->n_shared > 2 || !(w->rms_eps >= 0.0f)) return K3G_EINVAL;
+    for (int i = 0; i < w->n_shared; ++i)
+        if (!w->sh_w1[i] || !w->sh_w3[i] || !w->sh_w2[i]) return K3G_EINVAL;
+    const k3g_expert_bank *bank = &w->bank;
+    const int T = n_tokens, E = bank->n_experts, latent = bank->latent, inter = bank->inter;
+    const int hidden = w->hidden, sh_inter = w->n_shared ? w->sh_inter : 32;
+    k3g_shape s = {T, top_k, E, latent, inter, hidden, sh_inter, mode};
+    k3g_ws_layout L;
+    K3G_TRY(layout(&L, K3G_OP_LATENT_BLOCK, s));
+    if (ws_bytes < L.total) return K3G_ENOSPACE;
+    if (!aligned(x, 16) || !aligned(out, 4) || !aligned(ws, 256) || !aligned(w->w_router, 16)) return K3G_EALIGN;
+    if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
+    for (int i = 0; i < 6; i += 2)
+        if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
+    if (T > 0 && overlap(out, sizeof(float) * T * hidden, x, sizeof(float) * T * hidden)) return K3G_EINVAL;
+    K3G_TRY(check_device());
+    if (T == 0) return K3G_OK;
+    char *b = (char *)ws;
+    double *logits = (double *)(b + L.logits);
+    int32_t *idx = (int32_t *)(b + L.idx);
+    float *wts = (float *)(b + L.wts);
+    float *lat = (float *)(b + L.lat), *agg = (float *)(b + L.agg), *nrm = (float *)(b + L.nrm);
+    float *shh = (float *)(b + L.shh);
+    hipStream_t st = S(stream);
+    // routing on the hidden state
+    K3G_TRY(launch_logits(logits, x, w->w_router, T, hidden, E, st));
+    K3G_TRY(launch_topk(idx, wts, logits, w->bias, T, E, top_k, st));
+    // down-projection into the latent space
+    const DenseSeg down = {w->w_down, x, hidden};
+    K3G_TRY(launch_dense(lat, &down, 1, T, latent, st));
+    // the routed experts on the latent tokens
+    for (int stage = K3G_STAGE_BUCKET; stage <= K3G_STAGE_COMBINE; ++stage)
+        K3G_TRY(layer_stage(stage, L, agg, lat, idx, wts, bank, T, top_k, mode, ws, st));
+    // RMSNorm of the aggregate, the shared experts, and the up-projection
+    K3G_TRY(launch_rmsnorm(nrm, agg, w->gamma, T, latent, w->rms_eps, st));
+    DenseSeg segs[3] = {{w->w_up, nrm, latent}, {nullptr, nullptr, 0}, {nullptr, nullptr, 0}};
+    for (int i = 0; i < w->n_shared; ++i) {
+        float *h = shh + (size_t)i * T * sh_inter;
+        K3G_TRY(launch_dense_glu(h, w->sh_w1[i], w->sh_w3[i], x, T, hidden, sh_inter, st));
+        segs[1 + i] = {w->sh_w2[i], h, sh_inter};
+    }
+    return launch_dense(out, segs, 1 + w->n_shared, T, hidden, st);
 }

@@ -1,0 +1,132 @@
+"""GPU parity of the full LatentMoE block ("Kimi K3 engine (c/kimi_k3.c)",
+"Architecture notes", Stable LatentMoE), stage by stage against the oracle:
+routing on the hidden state, the bf16 down-projection, the routed layer, the
+RMSNorm of the aggregate, the shared SiTU-GLU experts and the up-projection.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import assert_norm_close, make_bank, situ_tolerance
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def k3g():
+    import mxfp4_moe_expert_amd as k
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    k.lib()
+    return k
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ws_view(ws, L, name, count, dtype, first=0):
+    it = np.dtype(dtype).itemsize
+    off = L[name] + first * it
+    return host(ws[off:off + count * it]).view(dtype)
+
+
+def run_block(k3g, x, Wr, b, dense, bank, K, mode, n_sh=2):
+    T, H = x.shape
+    sh_inter = dense["sh_w1_0"].shape[0]
+    d = {k: dev(v) for k, v in dense.items()}
+    w = k3g.block_struct(dev(Wr), dev(b), d["w_down"], d["w_up"], d["gamma"],
+                         [d[f"sh_w1_{s}"] for s in range(n_sh)], [d[f"sh_w3_{s}"] for s in range(n_sh)],
+                         [d[f"sh_w2_{s}"] for s in range(n_sh)], bank)
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=bank.n_experts, latent=bank.latent, inter=bank.inter,
+                   hidden=H, sh_inter=sh_inter, mode=mode)
+    ws = k3g.workspace(k3g.OP_LATENT_BLOCK, sh)
+    L = k3g.workspace_layout(k3g.OP_LATENT_BLOCK, sh)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    k3g.k3g_latent_moe_block(out, dev(x), w, K, mode, ws)
+    return host(out), ws, L
+
+
+def check_block(k3g, src, bank, x, Wr, b, dense, K, tokens, mode=0):
+    T, H = x.shape
+    latent, inter, E = bank.latent, bank.inter, bank.n_experts
+    SI = dense["sh_w1_0"].shape[0]
+    out, ws, L = run_block(k3g, x, Wr, b, dense, bank, K, mode)
+    idx = ws_view(ws, L, "idx", T * K, np.int32).reshape(T, K)
+    wts = ws_view(ws, L, "wts", T * K, np.float32).reshape(T, K)
+    lat = ws_view(ws, L, "lat", T * latent, np.float32).reshape(T, latent)
+    agg = ws_view(ws, L, "agg", T * latent, np.float32).reshape(T, latent)
+    nrm = ws_view(ws, L, "nrm", T * latent, np.float32).reshape(T, latent)
+    io, wo, lg = oracle.route(x, Wr, b, K)
+    if not np.array_equal(idx, io):
+        bad = np.flatnonzero((idx != io).any(1))
+        t = int(bad[0])
+        sc = 1 / (1 + np.exp(-lg[t])) + b.astype(np.float64)
+        lgg = ws_view(ws, L, "logits", T * E, np.float64).reshape(T, E)
+        raise AssertionError(f"{bad.size} tokens route differently; t={t} gpu {idx[t]} oracle {io[t]}; "
+                             f"oracle biased of gpu picks {sc[idx[t]]}, of oracle picks {sc[io[t]]}; "
+                             f"max |logit diff| {np.abs(lgg - lg).max():.3e}")
+    assert np.allclose(wts, wo, rtol=1e-6, atol=0)
+    for t in tokens:
+        # down-projection
+        lo, ln = oracle.matmul_bf16(x[t], dense["w_down"], full=True)
+        assert_norm_close(lat[t], lo, ln, what=f"block lat t={t}")
+        # the routed layer on the GPU's lat: the weighted sum of oracle expert outputs; the
+        # layer's own stages are checked one by one in test_gpu_exact/test_gpu_idot
+        ref = np.zeros(latent)
+        nrm_l = np.zeros(latent)
+        for k in range(K):
+            ex = src(int(idx[t, k]))
+            r = oracle.expert_glu(lat[t], ex, oracle.EXACT if mode == 0 else oracle.IDOT)
+            W2 = np.abs(oracle.mxfp4_dequant(ex["w2p"], ex["w2s"]))
+            ref += float(wts[t, k]) * r["y"].astype(np.float64)
+            nrm_l += float(wts[t, k]) * (W2 @ np.abs(r["h"].astype(np.float64)))
+        # composite bound: per-stage 1e-5 plus the propagation through SiTU (measured <= 1e-6 in the layer tests)
+        assert_norm_close(agg[t], ref, nrm_l, rel=1e-4, what=f"block agg t={t}")
+        # RMSNorm of the GPU's aggregate
+        n_ref = oracle.rmsnorm(agg[t], dense["gamma"])
+        assert np.allclose(nrm[t], n_ref, rtol=4e-6, atol=1e-30), f"rmsnorm t={t}"
+        # shared experts: h_s against SiTU of the oracle's bf16 products
+        acc, accn = oracle.matmul_bf16(nrm[t], dense["w_up"], full=True)
+        for s in range(2):
+            g, ng = oracle.matmul_bf16(x[t], dense[f"sh_w1_{s}"], full=True)
+            u, nu = oracle.matmul_bf16(x[t], dense[f"sh_w3_{s}"], full=True)
+            g32, u32 = g.astype(np.float32), u.astype(np.float32)
+            hs = ws_view(ws, L, "shh", SI, np.float32, first=(s * T + t) * SI)
+            ho = oracle.situ_vec(g32, u32)
+            bad = np.abs(hs.astype(np.float64) - ho) > situ_tolerance(g, u, ng, nu)
+            assert not bad.any(), f"shared h s={s} t={t}: {np.flatnonzero(bad)[:5]}"
+            y2, n2 = oracle.matmul_bf16(hs, dense[f"sh_w2_{s}"], full=True)
+            acc += y2
+            accn += n2
+        assert_norm_close(out[t], acc, accn, what=f"block out t={t}")
+    return out
+
+
+def test_block_small(k3g):
+    H, L_, I, SI, E, K, T = 256, 128, 96, 64, 8, 2, 37
+    src, bankt, bank = make_bank(k3g, 81, E, L_, I, 120, 123, 0.01)
+    Wr, b = synth.router(81, E, H, 0.1)
+    dense = synth.block_dense(81, hidden=H, latent=L_, shared_inter=SI, n_shared=2)
+    x = synth.activations(81, T, H)
+    out = check_block(k3g, src, bank, x, Wr, b, dense, K, tokens=range(T))
+    # and against the oracle's whole block
+    r = oracle.latent_block(x, Wr, b, dense, {e: src(e) for e in range(E)}, E, K, oracle.EXACT)
+    assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
+
+
+def test_block_full_size_sampled(k3g, full_bank):
+    src, bankt, bank = full_bank
+    seed = synth.SEED_BASE + 4
+    print("generating the block's dense weights", flush=True)
+    Wr, b = synth.router(seed, 896, 7168, 0.1)
+    dense = synth.block_dense(seed)
+    x = synth.activations(seed, 256, 7168)
+    check_block(k3g, src, bank, x, Wr, b, dense, 16, tokens=[0, 255])
