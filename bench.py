@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only copy a GIB-sized buffer 5 times (a plain copy of known size, for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     return ap.parse_args()
 
@@ -60,6 +63,9 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration > 0:
+        return copy_calibration(torch, args.copy_calibration)
 
     import mxfp4_moe_expert_amd as k3g
     import synth
@@ -228,13 +234,48 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(up_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, "moe_up"),
             "algorithmic_bytes_per_launch": int(up_alg),
         },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch (read + write) of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, scaled by the copy calibration; None when no
+    summary exists for this workload or the kernel sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
+    sha = hashlib.sha256(open(os.path.join(csrc, "gemv.hip"), "rb").read() +
+                         open(os.path.join(csrc, "k3g_common.h"), "rb").read()).hexdigest()
+    if sha != doc.get("source_sha256") or kernel not in doc.get("kernels", {}):
+        return None
+    k = doc["kernels"][kernel]
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def copy_calibration(torch, gib):
+    """A plain device copy of a known size: each of 5 launches reads and writes n bytes."""
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5,
+                      "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode):
