@@ -13,6 +13,12 @@
 // deterministic: no atomics decide an order.
 #include "k3g_common.h"
 
+// Up to this many tokens, top-k runs one workgroup per token; above it, one
+// wavefront per token.
+#ifndef K3G_TOPK_BLOCK_MAX_T
+#define K3G_TOPK_BLOCK_MAX_T 256
+#endif
+
 namespace k3g {
 
 // ---- logits, few tokens: one wavefront per expert row ------------------------
@@ -241,6 +247,167 @@ __global__ __launch_bounds__(64) void topk_kernel(int32_t *__restrict__ idx, flo
     }
 }
 
+// ---- top-k, few tokens: one workgroup per token ---------------------------------
+// One candidate per thread. Each wavefront sorts its four rows of 16 lanes
+// (a bitonic sort in the "flip" form: every compare-exchange leaves the better
+// candidate in the lower lane, so all rows end sorted the same way), then
+// merges rows 0+1 and 2+3 and the two results: its best 16, in order. The
+// wavefronts' lists meet in LDS and are merged four at a time, twice. Almost
+// every exchange is a DPP move; only the merges across 32 lanes go through the
+// LDS crossbar. Needs top_k <= 16 and E <= 1024.
+constexpr int TB_LIST = 16;         // candidates kept per list
+constexpr int TB_MAX_WAVES = 16;    // E <= 1024
+
+struct Cand {
+    double v;
+    int id;
+};
+
+template <int CTRL>
+__device__ inline Cand dpp_cand(const Cand &c) {
+    Cand o;
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(c.v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(c.v), CTRL, 0xF, 0xF, false);
+    o.v = __hiloint2double(hi, lo);
+    o.id = __builtin_amdgcn_update_dpp(0, c.id, CTRL, 0xF, 0xF, false);
+    return o;
+}
+
+template <int PATTERN>
+__device__ inline Cand swz_cand(const Cand &c) {
+    Cand o;
+    const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(c.v), PATTERN);
+    const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(c.v), PATTERN);
+    o.v = __hiloint2double(hi, lo);
+    o.id = __builtin_amdgcn_ds_swizzle(c.id, PATTERN);
+    return o;
+}
+
+__device__ inline Cand shfl_cand(const Cand &c, int src) {
+    Cand o;
+    const int lo = __shfl(__double2loint(c.v), src, kWave);
+    const int hi = __shfl(__double2hiint(c.v), src, kWave);
+    o.v = __hiloint2double(hi, lo);
+    o.id = __shfl(c.id, src, kWave);
+    return o;
+}
+
+// The lower lane of a pair keeps the candidate that comes first.
+__device__ inline void cx(Cand &c, const Cand &p, bool lower) {
+    const bool p_first = before(p.v, p.id, c.v, c.id);
+    const bool c_first = before(c.v, c.id, p.v, p.id);
+    const bool take = lower ? p_first : c_first;
+    c.v = take ? p.v : c.v;
+    c.id = take ? p.id : c.id;
+}
+
+// Partner lane ^ 4 inside a row of 16: one of the two row rotations by 4 and
+// by 12 supplies it, depending on the lane; `use4` says which (found once at
+// start-up from the rotated lane ids, so the rotation direction is not assumed).
+__device__ inline Cand xor4_cand(const Cand &c, bool use4) {
+    const Cand a = dpp_cand<0x124>(c);  // row_ror:4
+    const Cand b = dpp_cand<0x12C>(c);  // row_ror:12
+    return use4 ? a : b;
+}
+
+// Half-cleaners 8, 4, 2, 1 inside each row of 16.
+__device__ inline void clean16(Cand &c, int lane, bool use4) {
+    cx(c, dpp_cand<0x128>(c), (lane & 8) == 0);  // row_ror:8 = lane ^ 8
+    cx(c, xor4_cand(c, use4), (lane & 4) == 0);
+    cx(c, dpp_cand<0x4E>(c), (lane & 2) == 0);   // quad_perm [2,3,0,1]
+    cx(c, dpp_cand<0xB1>(c), (lane & 1) == 0);   // quad_perm [1,0,3,2]
+}
+
+// Sort every row of 16 lanes, best first.
+__device__ inline void sort16(Cand &c, int lane, bool use4) {
+    cx(c, dpp_cand<0xB1>(c), (lane & 1) == 0);   // k = 2
+    cx(c, dpp_cand<0x1B>(c), (lane & 2) == 0);   // k = 4: mirror in 4 (quad_perm [3,2,1,0])
+    cx(c, dpp_cand<0xB1>(c), (lane & 1) == 0);
+    cx(c, dpp_cand<0x141>(c), (lane & 4) == 0);  // k = 8: row_half_mirror
+    cx(c, dpp_cand<0x4E>(c), (lane & 2) == 0);
+    cx(c, dpp_cand<0xB1>(c), (lane & 1) == 0);
+    cx(c, dpp_cand<0x140>(c), (lane & 8) == 0);  // k = 16: row_mirror
+    cx(c, xor4_cand(c, use4), (lane & 4) == 0);
+    cx(c, dpp_cand<0x4E>(c), (lane & 2) == 0);
+    cx(c, dpp_cand<0xB1>(c), (lane & 1) == 0);
+}
+
+// Rows 0..3 hold sorted lists; afterwards row 0 holds the best 16 of the four,
+// sorted. Rows 0+1 and 2+3 merge by mirroring inside 32 lanes (swizzle with
+// xor mask 31), then row 0 meets row 2 reversed.
+__device__ inline void merge4(Cand &c, int lane, bool use4) {
+    cx(c, swz_cand<0x7C1F>(c), (lane & 16) == 0);  // and 0x1F, or 0, xor 0x1F
+    clean16(c, lane, use4);
+    const Cand p = shfl_cand(c, 47 - (lane & 15));   // row 2, last to first
+    cx(c, p, true);                                  // only row 0 is kept
+    clean16(c, lane, use4);
+}
+
+__global__ __launch_bounds__(TB_MAX_WAVES * 64) void topk_block_kernel(int32_t *__restrict__ idx,
+                                                                       float *__restrict__ wts,
+                                                                       const double *__restrict__ logits,
+                                                                       const float *__restrict__ bias, int T, int E,
+                                                                       int K) {
+    __shared__ double sc_lds[TB_MAX_WAVES * 64];
+    __shared__ double l1v[TB_MAX_WAVES * TB_LIST];
+    __shared__ int l1i[TB_MAX_WAVES * TB_LIST];
+    __shared__ double l2v[4 * TB_LIST];
+    __shared__ int l2i[4 * TB_LIST];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int n_lists = (E + kWave - 1) / kWave;
+    const bool use4 = __builtin_amdgcn_update_dpp(0, lane, 0x124, 0xF, 0xF, false) == (lane ^ 4);
+    const Cand none = {-__builtin_inf(), 0x7fffffff};
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+        const double *lg = logits + (size_t)t * E;
+        Cand c = none;
+        if (tid < E) {
+            const double sc = sigmoid64(lg[tid]);
+            sc_lds[tid] = sc;
+            c.v = sc + (double)bias[tid];
+            c.id = tid;
+        }
+        sort16(c, lane, use4);
+        merge4(c, lane, use4);
+        if (wave < n_lists && lane < TB_LIST) {
+            l1v[wave * TB_LIST + lane] = c.v;
+            l1i[wave * TB_LIST + lane] = c.id;
+        }
+        __syncthreads();
+        if (wave < 4) {
+            const int l = wave * 4 + lane / TB_LIST;
+            Cand d = none;
+            if (l < n_lists) {
+                d.v = l1v[l * TB_LIST + (lane & 15)];
+                d.id = l1i[l * TB_LIST + (lane & 15)];
+            }
+            merge4(d, lane, use4);
+            if (lane < TB_LIST) {
+                l2v[wave * TB_LIST + lane] = d.v;
+                l2i[wave * TB_LIST + lane] = d.id;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            Cand d;
+            d.v = l2v[lane];
+            d.id = l2i[lane];
+            merge4(d, lane, use4);
+            const int my_id = d.id < E ? d.id : 0;  // not a real id only with non-finite scores
+            // weights: the raw scores of the winners, summed in selection order
+            const double my_sc = lane < K ? sc_lds[my_id] : 0.0;
+            double sum = 0.0;
+            for (int k = 0; k < K; ++k)
+                sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_sc), k),
+                                        __builtin_amdgcn_readlane(__double2loint(my_sc), k));
+            if (lane < K) {
+                idx[(size_t)t * K + lane] = my_id;
+                wts[(size_t)t * K + lane] = (float)(my_sc / sum);
+            }
+        }
+        __syncthreads();  // the LDS lists are reused by the next token
+    }
+}
+
 // ---- bucket: stable counting sort of the T*K pairs by expert ---------------------
 // One workgroup. counts/offsets by an LDS histogram and scan; positions within
 // an expert follow token order: tokens are taken 64 at a time, a 64-bit mask
@@ -368,7 +535,10 @@ int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bia
     if (T == 0) return K3G_OK;
     const int blocks = T < 65536 ? T : 65536;
     const int nv = (E + kWave - 1) / kWave;
-    if (nv <= 16)
+    if (K <= TB_LIST && nv <= TB_MAX_WAVES && T <= K3G_TOPK_BLOCK_MAX_T) {
+        const int waves = nv < 4 ? 4 : nv;
+        topk_block_kernel<<<blocks, waves * kWave, 0, st>>>(idx, wts, logits, bias, T, E, K);
+    } else if (nv <= 16)
         topk_kernel<16><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K);
     else
         topk_kernel<32><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K);
