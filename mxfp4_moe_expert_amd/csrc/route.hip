@@ -78,50 +78,86 @@ __global__ __launch_bounds__(64) void logits_rows_any_kernel(double *__restrict_
     }
 }
 
-// ---- logits, many tokens: 64x64 register-tiled fp64 product -------------------
-constexpr int LT = 64, LK = 16;
-__global__ __launch_bounds__(256) void logits_tiled_kernel(double *__restrict__ logits, const float *__restrict__ x,
-                                                           const float *__restrict__ W, int T, int in, int E) {
-    __shared__ double xs[LK][LT + 1];
-    __shared__ double ws[LK][LT + 1];
-    const int t0 = blockIdx.y * LT, e0 = blockIdx.x * LT;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4];
+// ---- logits, more tokens: fp64 matrix cores ------------------------------------
+// v_mfma_f64_16x16x4_f64 on the exact fp64 widenings of x and W. A workgroup
+// owns a tile of 16*BM tokens x 16*BN experts; its SPLIT wavefronts each take
+// a slice of the columns and the partial tiles are added in wavefront order
+// through LDS, so the result does not depend on timing. Within a step of 16
+// columns, lane quarter q supplies columns 4q..4q+3, one per MFMA (A and B use
+// the same assignment, so every product meets its partner).
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+template <int BM, int BN, int SPLIT, bool VEC>
+__global__ __launch_bounds__(SPLIT * 64) void logits_mfma_kernel(double *__restrict__ logits,
+                                                                 const float *__restrict__ x,
+                                                                 const float *__restrict__ W, int T, int in, int E) {
+    __shared__ double red[SPLIT][BM * BN][4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r = lane & 15;
+    const int t0 = blockIdx.y * 16 * BM, e0 = blockIdx.x * 16 * BN;
+    const int nk = (in + 15) / 16;
+    const int per = (nk + SPLIT - 1) / SPLIT;
+    const int ka = wave * per, kb = min(nk, ka + per);
+    const float *xr[BM], *wr[BN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BM; ++i) xr[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * in;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int k0 = 0; k0 < in; k0 += LK) {
+    for (int j = 0; j < BN; ++j) wr[j] = W + (size_t)min(e0 + 16 * j + r, E - 1) * in;
+    v4d acc[BM][BN];
 #pragma unroll
-        for (int l = 0; l < 4; ++l) {
-            const int id = threadIdx.x + l * 256;
-            const int r = id / LK, kk = id % LK;
-            const int k = k0 + kk;
-            xs[kk][r] = (t0 + r < T && k < in) ? (double)x[(size_t)(t0 + r) * in + k] : 0.0;
-            ws[kk][r] = (e0 + r < E && k < in) ? (double)W[(size_t)(e0 + r) * in + k] : 0.0;
+    for (int i = 0; i < BM; ++i)
+#pragma unroll
+        for (int j = 0; j < BN; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int kk = ka; kk < kb; ++kk) {
+        const int k = kk * 16 + 4 * q;
+        float a[BM][4], b[BN][4];
+        if (VEC && k + 4 <= in) {
+#pragma unroll
+            for (int i = 0; i < BM; ++i) {
+                const float4 v = *(const float4 *)(xr[i] + k);
+                a[i][0] = v.x; a[i][1] = v.y; a[i][2] = v.z; a[i][3] = v.w;
+            }
+#pragma unroll
+            for (int j = 0; j < BN; ++j) {
+                const float4 v = *(const float4 *)(wr[j] + k);
+                b[j][0] = v.x; b[j][1] = v.y; b[j][2] = v.z; b[j][3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bool in_k = k + s < in;
+#pragma unroll
+                for (int i = 0; i < BM; ++i) a[i][s] = in_k ? xr[i][k + s] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < BN; ++j) b[j][s] = in_k ? wr[j][k + s] : 0.0f;
+            }
         }
-        __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < LK; ++kk) {
-            double a[4], b[4];
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
+            for (int i = 0; i < BM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
+                for (int j = 0; j < BN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[i][s], (double)b[j][s], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
-            if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j];
-        }
+        for (int j = 0; j < BN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wave][i * BN + j][v][lane] = acc[i][j][v];
+    __syncthreads();
+    // output element (block, v, lane): token 16*bi + lane/16 + 4*v, expert 16*bj + lane%16
+    // (the fp64 16x16x4 result layout: item v of lane l is row l/16 + 4v, column l%16)
+    for (int o = threadIdx.x; o < BM * BN * 256; o += SPLIT * 64) {
+        const int blk = o >> 8, v = (o >> 6) & 3, ln = o & 63;
+        double sum = red[0][blk][v][ln];
+#pragma unroll
+        for (int w = 1; w < SPLIT; ++w) sum += red[w][blk][v][ln];
+        const int t = t0 + 16 * (blk / BN) + (ln >> 4) + 4 * v;
+        const int e = e0 + 16 * (blk % BN) + (ln & 15);
+        if (t < T && e < E) logits[(size_t)t * E + e] = sum;
+    }
 }
 
 // ---- top-k: one wavefront per token, candidates in registers ---------------------
@@ -524,8 +560,17 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
         else
             logits_rows_any_kernel<<<E, 64, 0, st>>>(logits, x, W, T, in, E);
     } else {
-        const dim3 grid((E + LT - 1) / LT, (T + LT - 1) / LT);
-        logits_tiled_kernel<<<grid, 256, 0, st>>>(logits, x, W, T, in, E);
+        const bool vec = in % 4 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)W % 16) == 0;
+        if (T <= 256) {
+            // few token tiles: eight wavefronts share each tile's columns
+            const dim3 grid((E + 31) / 32, (T + 15) / 16);
+            if (vec) logits_mfma_kernel<1, 2, 8, true><<<grid, 512, 0, st>>>(logits, x, W, T, in, E);
+            else logits_mfma_kernel<1, 2, 8, false><<<grid, 512, 0, st>>>(logits, x, W, T, in, E);
+        } else {
+            const dim3 grid((E + 31) / 32, (T + 31) / 32);
+            if (vec) logits_mfma_kernel<2, 2, 4, true><<<grid, 256, 0, st>>>(logits, x, W, T, in, E);
+            else logits_mfma_kernel<2, 2, 4, false><<<grid, 256, 0, st>>>(logits, x, W, T, in, E);
+        }
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }

@@ -163,7 +163,9 @@ def test_expert_glu_small_ragged(k3g):
                                              (100, 3584, 896, 16, 0.01), (7, 200, 40, 5, 0.3),
                                              (33, 7168, 896, 16, 0.1), (3, 64, 64, 64, 0.0),
                                              (300, 3584, 896, 16, 0.01), (5, 128, 1000, 16, 0.05),
-                                             (2, 96, 1024, 16, 0.05), (4, 64, 130, 16, 0.05)])
+                                             (2, 96, 1024, 16, 0.05), (4, 64, 130, 16, 0.05),
+                                             (20, 200, 40, 5, 0.3), (9, 130, 70, 8, 0.2),
+                                             (600, 256, 896, 16, 0.01)])
 def test_route_matches_oracle(k3g, T, n_in, E, K, bias):
     print(f"route T={T} in={n_in} E={E} K={K}", flush=True)
     seed = 3000 + T
