@@ -29,7 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
-I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published (TOP/s)
+MFMA_PEAK_I8_TOPS = 5000.0      # MI355X dense int8 matrix, published (tera-ops)
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 N_ROT = 64                 # distinct tokens the decode steps cycle through
 
 
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot"])
+    ap.add_argument("--idot-bf16", action="store_true",
+                    help="IDOT workloads: run the group dots on the bf16 matrix cores (same results)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -79,6 +82,7 @@ def main():
     seed_bank = synth.SEED_BASE + 1
     wl_seed, T, bias_range, mode_name = synth.WORKLOADS[args.workload]
     mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
+    form = k3g.IDOT_BF16 if (mode == k3g.IDOT and args.idot_bf16) else 0
 
     t0 = time.time()
     src = lambda e: synth.expert(seed_bank, e)  # noqa: E731
@@ -97,7 +101,7 @@ def main():
     wts = [torch.empty((T, K), dtype=torch.float32, device=dev) for _ in range(n_rot)]
     ys = [torch.empty((T, L), dtype=torch.float32, device=dev) for _ in range(n_rot)]
     ws_r = [k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=T, n_experts=E)) for _ in range(n_rot)]
-    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=mode)
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=mode | form)
     ws = [k3g.workspace(k3g.OP_MOE_LAYER, sh) for _ in range(n_rot)]
 
     stages = [("route", None), ("bucket", k3g.STAGE_BUCKET)]
@@ -108,7 +112,7 @@ def main():
         stages.append(("quant_h", k3g.STAGE_QUANT_H))
     stages += [("down", k3g.STAGE_DOWN), ("combine", k3g.STAGE_COMBINE)]
 
-    def stage(r, st, m=mode):
+    def stage(r, st, m=mode | form):
         if st is None:
             k3g.k3g_moe_route(idx[r], wts[r], xs[r], Wd, bd, K, ws_r[r])
         else:
@@ -172,7 +176,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * n_rot)
 
-    stage_ms = {name: time_stage(st, mode) for name, st in stages}
+    stage_ms = {name: time_stage(st, mode | form) for name, st in stages}
     # the same expert kernels with the nibbles decoded through the LDS byte-pair table
     lut_ms = {}
     if mode == k3g.EXACT:
@@ -199,6 +203,34 @@ def main():
     gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     tok_s = T / (ms_per_step * 1e-3)
     up_gbs = up_alg / (stage_ms["up"] * 1e-3) / 1e9
+    roof = {
+        "kernel": "moe_up (w1, w3 and SiTU for every selected expert)",
+        "bound": "hbm",
+        "achieved": round(up_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(up_gbs / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(args.workload, "moe_up"),
+        "algorithmic_bytes_per_launch": int(up_alg),
+    }
+    if mode == k3g.IDOT:
+        # matrix-core work of the up kernel: 2 ops per multiply-add, w1 and w3 rows, every pair
+        up_ops = 2.0 * P * 2 * I * L
+        peak = MFMA_PEAK_BF16_TFLOPS if form else MFMA_PEAK_I8_TOPS
+        tops = up_ops / (stage_ms["up"] * 1e-3) / 1e12
+        roof = {
+            "kernel": "moe_up (IDOT group dots of w1 and w3 for every pair, SiTU)",
+            "bound": "mfma",
+            "achieved": round(tops, 1),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "ops": "int8 multiply-adds x 2" if not form else "bf16 multiply-adds x 2 (exact int8 values)",
+            "frac": round(tops / peak, 4),
+            "traffic": measured_traffic(args.workload, "moe_up"),
+            "algorithmic_ops_per_launch": up_ops,
+            "hbm_achieved_GBps": round(up_gbs, 1),
+            "hbm_frac": round(up_gbs / HBM_PEAK_GBS, 4),
+        }
 
     result = {
         "metric": "MXFP4 expert GEMV HBM GB/s (batch 1); MoE-layer tokens/s at 4096 tokens",
@@ -224,19 +256,11 @@ def main():
         },
         "tokens_per_s": round(tok_s, 1),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-        "decode": "gfx950 FP4->FP32 convert" if mode == k3g.EXACT else "int8 MFMA",
+        "decode": ("gfx950 FP4->FP32 convert" if mode == k3g.EXACT else
+                   "bf16 MFMA on exact int8 values" if form else "int8 MFMA"),
         "stage_us_lds_lut_decode": {k: round(v * 1e3, 2) for k, v in lut_ms.items()},
         "timing": timing,
-        "roofline": {
-            "kernel": "moe_up (w1, w3 and SiTU for every selected expert)",
-            "bound": "hbm",
-            "achieved": round(up_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(up_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, "moe_up"),
-            "algorithmic_bytes_per_launch": int(up_alg),
-        },
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode)

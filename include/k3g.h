@@ -57,7 +57,9 @@ typedef enum {
 
 /* EXACT: fp32 activations, exact e2m1 products, fp32 accumulation.
  * IDOT:  activations quantised per 32-group to int8, int32 group dots on the
- *        matrix cores ([COLIBRI-K3] "Streaming design", K3_IDOT). */
+ *        matrix cores ([COLIBRI-K3] "Streaming design", K3_IDOT). The IDOT
+ *        kernels need latent and inter to be multiples of 128 and the scale
+ *        tensors 4-byte aligned (K3G_EUNSUPPORTED / K3G_EALIGN otherwise). */
 typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
 
 /* OR-ed into `mode` of the EXACT calls: decode the nibbles through the
@@ -65,6 +67,14 @@ typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
  * one", K3_E2M1_PAIR), instead of gfx950's FP4 -> FP32 convert instruction
  * (the default). Both give the same values: e2m1 codes are exact in either. */
 #define K3G_DECODE_LUT 0x100
+
+/* OR-ed into K3G_IDOT: compute the same group dots on the bf16 matrix cores
+ * instead of the int8 ones. The int8 activations are widened to bf16 and the
+ * e2m1 values carry their group's power-of-two scale (both exact), so each
+ * group's fp32 result is exactly I * 2^(s-128) and the per-group epilogue is
+ * one fma instead of a convert, a multiply and an fma. Results are identical
+ * to the int8 form bit for bit; the workspace gains bf16 copies of xq and hq. */
+#define K3G_IDOT_BF16 0x200
 
 typedef struct {
     const uint8_t *packed; /* [rows][in/2], 16-byte aligned */
@@ -137,12 +147,14 @@ typedef struct {
  *   idx, wts int32/float [T][top_k]      block routing
  *   lat, agg, nrm  float [T][latent]     block stages
  *   shh     float [T][sh_inter]          block shared-expert SiTU output
- *   layer   the MoE layer's own workspace inside the block's */
+ *   layer   the MoE layer's own workspace inside the block's
+ *   xqb, hqb  uint16 (bf16) copies of xq and hq (K3G_IDOT_BF16 only) */
 typedef struct {
     size_t total;
     size_t logits, counts, offsets, perm, inv, active;
     size_t xq, xs, h, hq, hs, ypair;
     size_t idx, wts, lat, agg, nrm, shh, layer;
+    size_t xqb, hqb;
 } k3g_ws_layout;
 
 /* Human-readable name of a status code (static storage). */

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libk3g.so")
 EXACT = 0
 IDOT = 1
 DECODE_LUT = 0x100  # OR into the EXACT mode: decode through the LDS byte-pair table
+IDOT_BF16 = 0x200  # OR into the IDOT mode: the same group dots on the bf16 matrix cores
 OP_EXPERT_GLU = 1
 OP_MOE_ROUTE = 2
 OP_MOE_LAYER = 3
@@ -64,7 +65,7 @@ class Shape(C.Structure):
 
 
 _WS_FIELDS = ("total", "logits", "counts", "offsets", "perm", "inv", "active", "xq", "xs", "h", "hq",
-              "hs", "ypair", "idx", "wts", "lat", "agg", "nrm", "shh", "layer")
+              "hs", "ypair", "idx", "wts", "lat", "agg", "nrm", "shh", "layer", "xqb", "hqb")
 
 
 class WsLayout(C.Structure):

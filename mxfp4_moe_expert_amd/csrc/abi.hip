@@ -22,13 +22,13 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
 int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K, hipStream_t st);
 int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
                   int T, int K, int E, hipStream_t st);
-int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, hipStream_t st);
+int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, uint16_t *qb, hipStream_t st);
 int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed, int in, int rows, int n_tokens,
                           hipStream_t st);
-int launch_moe_up_idot(float *h, const int8_t *xq, const float *xs, const BankDev &bank, const int32_t *active,
+int launch_moe_up_idot(float *h, const int8_t *xq, const uint16_t *xqb, const float *xs, const BankDev &bank, const int32_t *active,
                        const int32_t *offsets, const int32_t *perm, int top_k, int latent, int inter, int max_slots,
                        hipStream_t st);
-int launch_moe_down_idot(float *ypair, const int8_t *hq, const float *hs, const BankDev &bank, const int32_t *active,
+int launch_moe_down_idot(float *ypair, const int8_t *hq, const uint16_t *hqb, const float *hs, const BankDev &bank, const int32_t *active,
                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
                          hipStream_t st);
 struct DenseSeg {
@@ -83,11 +83,19 @@ struct Carver {
     }
 };
 
-inline int base_mode(int mode) { return mode & ~K3G_DECODE_LUT; }
+inline int base_mode(int mode) { return mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16); }
 inline bool mode_ok(int mode) {
-    return (mode & ~(K3G_DECODE_LUT | 0xFF)) == 0 && (base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT);
+    if (mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16 | 0xFF)) return false;
+    if ((mode & K3G_IDOT_BF16) && base_mode(mode) != K3G_IDOT) return false;
+    return base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT;
 }
 inline bool lut_of(int mode) { return (mode & K3G_DECODE_LUT) != 0; }
+// The IDOT kernels stage a row's scale bytes four groups at a time as aligned
+// dwords: both widths must be multiples of 128 columns.
+inline int idot_shape_ok(int mode, int latent, int inter) {
+    return (mode & 0xFF) != K3G_IDOT || (latent % 128 == 0 && inter % 128 == 0) ? K3G_OK : K3G_EUNSUPPORTED;
+}
+inline bool bf16_of(int mode) { return (mode & K3G_IDOT_BF16) != 0; }
 
 bool shape_ok_layer(const k3g_shape &s) {
     return s.n_tokens >= 0 && s.top_k >= 1 && s.top_k <= kMaxTopK && s.n_experts >= 1 &&
@@ -111,6 +119,10 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
                 o->xs = c.take(sizeof(float) * (s.latent / kGroup));
                 o->hq = c.take((size_t)s.inter);
                 o->hs = c.take(sizeof(float) * (s.inter / kGroup));
+                if (bf16_of(s.mode)) {
+                    o->xqb = c.take(sizeof(uint16_t) * s.latent);
+                    o->hqb = c.take(sizeof(uint16_t) * s.inter);
+                }
             }
             break;
         }
@@ -145,6 +157,10 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
                 o->xs = c.take(sizeof(float) * (T ? T : 1) * (s.latent / kGroup));
                 o->hq = c.take((P ? P : 1) * (size_t)s.inter);
                 o->hs = c.take(sizeof(float) * (P ? P : 1) * (s.inter / kGroup));
+                if (bf16_of(s.mode)) {
+                    o->xqb = c.take(sizeof(uint16_t) * (T ? T : 1) * s.latent);
+                    o->hqb = c.take(sizeof(uint16_t) * (P ? P : 1) * s.inter);
+                }
             }
             o->layer = 0;
             break;
@@ -248,7 +264,7 @@ int k3g_quantize_i8_groups(int8_t *q, float *s, const float *x, int n_rows, int 
     if (!q || !s || !x || n_rows < 0 || in <= 0 || in % kGroup) return K3G_EINVAL;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return K3G_EALIGN;
     K3G_TRY(check_device());
-    return launch_quant_i8(q, s, x, n_rows, in, S(stream));
+    return launch_quant_i8(q, s, x, n_rows, in, nullptr, S(stream));
 }
 
 int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed, int in, int rows, int n_tokens,
@@ -272,6 +288,10 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
     k3g_shape s = {1, 1, 1, latent, inter, 0, 0, mode};
     k3g_ws_layout L;
     K3G_TRY(layout(&L, K3G_OP_EXPERT_GLU, s));
+    K3G_TRY(idot_shape_ok(mode, latent, inter));
+    if ((mode & 0xFF) == K3G_IDOT &&
+        (!aligned(e->w1.scales, 4) || !aligned(e->w3.scales, 4) || !aligned(e->w2.scales, 4)))
+        return K3G_EALIGN;
     if (ws_bytes < L.total) return K3G_ENOSPACE;
     K3G_TRY(check_device());
     // the expert as a one-expert bank: offsets relative to w1's packed bytes
@@ -293,10 +313,11 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
     }
     int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
     float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
-    K3G_TRY(launch_quant_i8(xq, xs, x, 1, latent, st));
-    K3G_TRY(launch_moe_up_idot(h, xq, xs, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, st));
-    K3G_TRY(launch_quant_i8(hq, hs, h, 1, inter, st));
-    return launch_moe_down_idot(y, hq, hs, b, nullptr, nullptr, nullptr, latent, inter, 1, st);
+    uint16_t *xqb = L.xqb ? (uint16_t *)(w + L.xqb) : nullptr, *hqb = L.hqb ? (uint16_t *)(w + L.hqb) : nullptr;
+    K3G_TRY(launch_quant_i8(xq, xs, x, 1, latent, xqb, st));
+    K3G_TRY(launch_moe_up_idot(h, xq, xqb, xs, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, st));
+    K3G_TRY(launch_quant_i8(hq, hs, h, 1, inter, hqb, st));
+    return launch_moe_down_idot(y, hq, hqb, hs, b, nullptr, nullptr, nullptr, latent, inter, 1, st);
 }
 
 int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_router, const float *bias, int n_tokens,
@@ -328,8 +349,11 @@ static int layer_prepare(k3g_ws_layout *L, const float *y, const float *x, const
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
         return K3G_EALIGN;
     if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
+    K3G_TRY(idot_shape_ok(mode, latent, inter));
     for (int i = 0; i < 6; i += 2)
         if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
+    for (int i = 1; i < 6; i += 2)
+        if (!aligned(bank->base + bank->off[i], 4)) return K3G_EALIGN;
     if (n_tokens > 0 && overlap(y, sizeof(float) * n_tokens * latent, x, sizeof(float) * n_tokens * latent))
         return K3G_EINVAL;
     return check_device();
@@ -348,6 +372,7 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
     float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
     int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
     float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
+    uint16_t *xqb = L.xqb ? (uint16_t *)(w + L.xqb) : nullptr, *hqb = L.hqb ? (uint16_t *)(w + L.hqb) : nullptr;
     const int P = n_tokens * top_k;
     const int max_slots = P < E ? P : E;
     const BankDev b = bank_dev(*bank);
@@ -355,17 +380,17 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
         case K3G_STAGE_BUCKET:
             return launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
         case K3G_STAGE_QUANT_X:
-            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, st) : K3G_OK;
+            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, xqb, st) : K3G_OK;
         case K3G_STAGE_UP:
             return base_mode(mode) == K3G_IDOT
-                       ? launch_moe_up_idot(h, xq, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
+                       ? launch_moe_up_idot(h, xq, xqb, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
                        : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P,
                                              lut_of(mode), st);
         case K3G_STAGE_QUANT_H:
-            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, st) : K3G_OK;
+            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, hqb, st) : K3G_OK;
         case K3G_STAGE_DOWN:
             return base_mode(mode) == K3G_IDOT
-                       ? launch_moe_down_idot(ypair, hq, hs, b, active, offsets, perm, latent, inter, max_slots, st)
+                       ? launch_moe_down_idot(ypair, hq, hqb, hs, b, active, offsets, perm, latent, inter, max_slots, st)
                        : launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots,
                                                lut_of(mode), st);
         case K3G_STAGE_COMBINE:
@@ -411,8 +436,11 @@ extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_
     if (ws_bytes < L.total) return K3G_ENOSPACE;
     if (!aligned(x, 16) || !aligned(out, 4) || !aligned(ws, 256) || !aligned(w->w_router, 16)) return K3G_EALIGN;
     if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
+    K3G_TRY(idot_shape_ok(mode, latent, inter));
     for (int i = 0; i < 6; i += 2)
         if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
+    for (int i = 1; i < 6; i += 2)
+        if (!aligned(bank->base + bank->off[i], 4)) return K3G_EALIGN;
     if (T > 0 && overlap(out, sizeof(float) * T * hidden, x, sizeof(float) * T * hidden)) return K3G_EINVAL;
     K3G_TRY(check_device());
     if (T == 0) return K3G_OK;

@@ -7,6 +7,8 @@
 // group dot is an exact int32; the float scales come after:
 //   y[r] = sum_g [s_rg != 255] I_rg * s_x[g] * 2^(s_rg - 128),
 // where 2^(s-128) = 2^(s-127)/2 undoes the doubling.
+#include <type_traits>
+
 #include "k3g_common.h"
 
 namespace k3g {
@@ -14,8 +16,10 @@ namespace k3g {
 // ---- activation quantisation: one thread per (row, group) --------------------
 // s = max|x|/127 in fp32 (correctly rounded division), q = rint(x/s) clamped
 // to +-127 (ties to even); an all-zero group gives s = 0 and q = 0.
+// qb (optional): the same q as bf16 bit patterns (exact), for the bf16 MFMA form.
 __global__ __launch_bounds__(256) void quant_i8_kernel(int8_t *__restrict__ q, float *__restrict__ s,
-                                                       const float *__restrict__ x, int n_rows, int in) {
+                                                       const float *__restrict__ x, int n_rows, int in,
+                                                       uint16_t *__restrict__ qb) {
     const int ngrp = in / kGroup;
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= (int64_t)n_rows * ngrp) return;
@@ -51,13 +55,26 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(int8_t *__restrict__ q, f
     uint4 *dst = (uint4 *)(q + id * kGroup);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    if (qb) {
+        // an int8 value has at most 8 significant bits: its fp32 form truncated to bf16 is exact
+        uint32_t hb[kGroup / 2];
+#pragma unroll
+        for (int j = 0; j < kGroup / 2; ++j) {
+            const int b0 = (int8_t)(packed[j / 2] >> (16 * (j & 1)));
+            const int b1 = (int8_t)(packed[j / 2] >> (16 * (j & 1) + 8));
+            hb[j] = (__builtin_bit_cast(uint32_t, (float)b0) >> 16) | (__builtin_bit_cast(uint32_t, (float)b1) & 0xFFFF0000u);
+        }
+        uint4 *db = (uint4 *)(qb + id * kGroup);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) db[j] = make_uint4(hb[4 * j], hb[4 * j + 1], hb[4 * j + 2], hb[4 * j + 3]);
+    }
 }
 
-int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, hipStream_t st) {
+int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, uint16_t *qb, hipStream_t st) {
     const int64_t n = (int64_t)n_rows * (in / kGroup);
     if (n == 0) return K3G_OK;
     const int blocks = (int)((n + 255) / 256);
-    quant_i8_kernel<<<blocks, 256, 0, st>>>(q, s, x, n_rows, in);
+    quant_i8_kernel<<<blocks, 256, 0, st>>>(q, s, x, n_rows, in, qb);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
@@ -151,161 +168,333 @@ int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed,
 }
 
 // ---- the grouped IDOT expert kernels ---------------------------------------------
-// Work item = (slot, block of weight rows); the wavefront loops over its
-// expert's pairs in chunks of up to 32*IT_NT tokens. Per group and token tile
-// one MFMA gives the int32 group dots I for 32 weight rows; the epilogue adds
-// float(I) * (s_x[token][g] * 2^(s_rg - 128)) in fp32 (nothing for s_rg = 255).
-// UP: the 32 MFMA columns are 16 rows of w1 and the same 16 rows of w3, so one
-//     product yields g and u; h = SiTU(g, u) is written to h[pos][row].
-// DOWN: 32 rows of w2 on the quantised h of each pair -> ypair[pos][row].
-// Each lane keeps pointers to its own weight row (w1 or w3 for UP). Token
-// scales of 8 groups at a time are staged in LDS.
-constexpr int IT_NT = 4;  // token tiles (of 32) per chunk
-constexpr int IT_KC = 8;  // groups whose token scales are staged together
+// Work item = (slot, block of weight rows), one per workgroup of IX_WAVES
+// wavefronts; the workgroup loops over its expert's pairs in chunks of up to
+// 32*IX_NT tokens. Each wavefront owns 32 weight rows (operand A) and meets
+// every token tile of the chunk (operand B, 32 tokens); lane l of a result
+// holds token l%32 and rows 8*(v/4) + 4*(l/32) + v%4.
+//  - int8 form: one v_mfma_i32_32x32x32_i8 per group and tile on the int8
+//    activations and the doubled e2m1 values gives the int32 group dots I;
+//    the epilogue adds float(I) * (s_x[token][g] * 2^(s_rg - 128)).
+//  - bf16 form: two v_mfma_f32_32x32x16_bf16 on the same int8 values widened
+//    to bf16 and the e2m1 values with 2^(s_rg-127) folded in by the FP4
+//    convert. Every product and partial sum is an integer (< 2^16) times
+//    2^(s_rg-128), exact in fp32, so the result is I * 2^(s_rg-128) exactly
+//    and the epilogue is one fma with s_x; the sums equal the int8 form's bit
+//    for bit.
+// A scale byte of 255 contributes nothing.
+// UP: a wavefront's 32 rows are 16 rows of w1 (result slots 0..7) and the same
+//     16 rows of w3 (slots 8..15): g and u of a row meet in one lane and
+//     h = SiTU(g, u) goes to h[pos][row].
+// DOWN: 32 rows of w2 per wavefront on the quantised h of each pair.
+//
+// Operands reach LDS without passing through registers (global_load_lds:
+// lane l's 16 or 4 bytes land at the instruction's LDS base + 16*l or 4*l),
+// in blocks of GB groups, double-buffered: the next block is requested before
+// the current one is computed. Every load instruction reads rows of a block
+// whole (a run of lanes per row), and each row in LDS is padded by one 16-byte
+// chunk, so that the 16 rows a fragment read touches in one cycle start in
+// distinct banks and every fragment address is a per-lane base plus a constant:
+//   tokens  [token m][chunks of the block + 1]
+//   weights [row r][GB + 1 chunks] per wavefront
+//   s_x     [group j][token m]
+//   2^(s-128) (int8 form) [wavefront][group][row], written from registers.
+constexpr int IX_WAVES = 8;
+constexpr int IX_NT = 3;     // token tiles (of 32) per chunk
 
-template <bool UP>
-__global__ __launch_bounds__(256) void moe_idot_kernel(float *__restrict__ out, const int8_t *__restrict__ aq,
-                                                      const float *__restrict__ as, BankDev bank,
-                                                      const int32_t *__restrict__ active,
-                                                      const int32_t *__restrict__ offsets,
-                                                      const int32_t *__restrict__ perm, int top_k, int n_in, int n_out,
-                                                      int max_slots) {
-    __shared__ float ts_lds[4][IT_KC][IT_NT * 32];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wl = threadIdx.x / kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) + wl);
-    const int n_waves = gridDim.x * blockDim.x / kWave;
-    const int half = lane >> 5;
-    const int col = lane & 31;                 // MFMA column of this lane
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 4 packed bytes (8 e2m1 codes, column order) -> 8 bf16 scaled by 2^(e-127),
+// e = the exponent field of `scale`.
+__device__ inline bf16x8_t fp4x8_bf16(uint32_t w, float scale) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Written as inline assembly on purpose: the compiler would otherwise wait for
+// every outstanding global-to-LDS load before the next LDS read, whatever its
+// address, and the next block's loads could never overlap the current block's
+// products. The kernel waits for them itself (s_waitcnt vmcnt(0)) before the
+// barrier that hands the buffer over. M0 holds the wavefront's LDS base.
+__device__ inline uint32_t lds_base(void *lds) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
+}
+__device__ inline void lds_load16(const void *src, void *lds) {
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base(lds))
+                     : "m0", "memory");
+}
+__device__ inline void lds_load4(const void *src, void *lds) {
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds_base(lds))
+                     : "m0", "memory");
+}
+
+template <bool UP, bool BF16>
+__global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
+    float *__restrict__ out, const int8_t *__restrict__ aq, const uint16_t *__restrict__ aqb,
+    const float *__restrict__ as, BankDev bank, const int32_t *__restrict__ active,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int n_in, int n_out,
+    int max_slots) {
+    constexpr int GB = 4;                     // groups per block
+    constexpr int GBYTES = BF16 ? 64 : 32;    // token bytes per group
+    constexpr int TCHD = GB * GBYTES / 16;    // token chunks of a block: 8 (int8) or 16 (bf16)
+    constexpr int TCH = TCHD + 1;             // token row in LDS: the chunks + pad
+    constexpr int TPITCH = 16 * TCH;
+    constexpr int WCH = GB + 1;               // weight row in LDS: GB chunks + pad
+    constexpr int WPITCH = 16 * WCH;
+    constexpr int NTOK = IX_NT * 32;
+    constexpr int TLD = (NTOK * TCH + 64 * IX_WAVES - 1) / (64 * IX_WAVES);  // token loads per wavefront
+    constexpr int WLD = (32 * WCH + 63) / 64;                                 // weight loads per wavefront
+    constexpr int SXI = NTOK * GB / 64;                                       // scale load instructions
+    static_assert(SXI <= IX_WAVES && NTOK * GB % 64 == 0, "one scale load per wavefront at most");
+    __shared__ __attribute__((aligned(16))) char tok_lds[2][NTOK * TPITCH];
+    __shared__ __attribute__((aligned(16))) char w_lds[2][IX_WAVES][WLD * 1024];
+    __shared__ __attribute__((aligned(16))) float sx_lds[2][GB][NTOK];
+    __shared__ __attribute__((aligned(16))) uint32_t sc_lds[2][IX_WAVES][64];   // a row's 4 scale bytes (x2)
+    __shared__ __attribute__((aligned(16))) float ws_lds[BF16 ? 1 : IX_WAVES][GB][32];
+    __shared__ int row_lds[NTOK];
+    const int tid = threadIdx.x, lane = tid & 63, wl = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
     const int ngrp = n_in / kGroup;
-    constexpr int ROWS = UP ? 16 : 32;        // weight rows per item
-    const int row_tiles = (n_out + ROWS - 1) / ROWS;
+    const int n_blocks = ngrp / GB;  // the launchers require in % 128 == 0
+    constexpr int ROWS = UP ? 16 : 32;  // weight rows per wavefront (UP: of w1 and of w3 each)
+    constexpr int WG_ROWS = ROWS * IX_WAVES;
+    const int row_blocks = (n_out + WG_ROWS - 1) / WG_ROWS;
     const int n_act = perm ? active[0] : 1;
-    const int n_items = max_slots * row_tiles;
-    float(*ts)[IT_NT * 32] = ts_lds[wl];
-    // which matrix and row this lane's column is
-    const int mat_p = UP ? (col < 16 ? W1P : W3P) : W2P;
-    const int mat_s = UP ? (col < 16 ? W1S : W3S) : W2S;
-    for (int item = wave; item < n_items; item += n_waves) {
-        const int slot = item / row_tiles;
+    const int n_items = max_slots * row_blocks;
+    const uint32_t pitch = (uint32_t)(n_in / 2);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int slot = item / row_blocks;
         if (slot >= n_act) continue;
-        const int rt = item - slot * row_tiles;
+        const int rb = item - slot * row_blocks;
         const int e = perm ? active[1 + slot] : 0;
         const int p0 = perm ? offsets[e] : 0;
         const int p1 = perm ? offsets[e + 1] : 1;
         const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
-        const int rr = rt * ROWS + (UP ? (col & 15) : col);
-        const int row = min(rr, n_out - 1);
-        const uint8_t *wrow = eb + bank.off[mat_p] + (size_t)row * (n_in / 2) + half * 8;
-        const uint8_t *srow = eb + bank.off[mat_s] + (size_t)row * ngrp;
-        for (int c0 = p0; c0 < p1; c0 += IT_NT * 32) {
-            const int n_tok = min(p1 - c0, IT_NT * 32);
-            const int n_tiles = (n_tok + 31) / 32;
-            const int8_t *arow[IT_NT];
+        const int rbase = rb * WG_ROWS + wl * ROWS;  // first row of this wavefront
+        // the two matrices of this kernel's operand A (UP: w1 and w3; DOWN: w2 twice),
+        // as wave-uniform pointers; a lane's row is an offset below 2^31 plus bit 31
+        // for the second matrix
+        const uint8_t *pa0 = eb + bank.off[UP ? W1P : W2P], *pa1 = eb + bank.off[UP ? W3P : W2P];
+        const uint8_t *ps0 = eb + bank.off[UP ? W1S : W2S], *ps1 = eb + bank.off[UP ? W3S : W2S];
+        auto row_of = [&](int r) {  // operand-A row r (0..31) of this wavefront
+            return min(rbase + (UP ? (r & 15) : r), n_out - 1);
+        };
+        auto sel = [](uint32_t o, const uint8_t *p0, const uint8_t *p1) {
+            return ((o >> 31) ? p1 : p0) + (o & 0x7FFFFFFFu);
+        };
+        // scale loads: lane l fetches the 4 scale bytes of a block of row l%32 (a dword:
+        // rows are ngrp bytes apart and ngrp is a multiple of 4)
+        const uint32_t ssrc = (uint32_t)row_of(col) * (uint32_t)ngrp | ((UP && col >= 16) ? 0x80000000u : 0u);
+        // weight loads of this lane: LDS slot idx = 64*i + lane -> (row, chunk)
+        uint32_t wsrc[WLD];
+        int wch[WLD];
 #pragma unroll
-            for (int tt = 0; tt < IT_NT; ++tt) {
-                const int pos = c0 + min(tt * 32 + col, n_tok - 1);
-                const int ar = UP ? (perm ? perm[pos] / top_k : 0) : pos;
-                arow[tt] = aq + (size_t)ar * n_in + half * 16;
+        for (int i = 0; i < WLD; ++i) {
+            const int idx = 64 * i + lane;
+            const int r = min(idx / WCH, 31);
+            wch[i] = idx < 32 * WCH ? min(idx % WCH, GB - 1) : -1;  // the pad chunk repeats the last one
+            wsrc[i] = (uint32_t)row_of(r) * pitch | ((UP && r >= 16) ? 0x80000000u : 0u);
+        }
+        for (int c0 = p0; c0 < p1; c0 += NTOK) {
+            const int n_tok = min(p1 - c0, NTOK);
+            const int n_tiles = __builtin_amdgcn_readfirstlane((n_tok + 31) / 32);
+            __syncthreads();  // the previous chunk is done with the LDS
+            if (tid < NTOK) {
+                const int pos = c0 + min(tid, n_tok - 1);
+                row_lds[tid] = UP ? (perm ? perm[pos] / top_k : 0) : pos;
             }
-            int srow_a[2];
+            __syncthreads();
+            // token loads of this lane: slot idx = 64*(wl + 8i) + lane -> (token, chunk)
+            const char *tbase = BF16 ? (const char *)aqb : (const char *)aq;
+            const uint32_t trow = (uint32_t)n_in * (BF16 ? 2u : 1u);
+            uint32_t tsrc[TLD];
+            int tch[TLD];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int pos = c0 + min(2 * lane + k, n_tok - 1);
-                srow_a[k] = (UP ? (perm ? perm[pos] / top_k : 0) : pos) * ngrp;
+            for (int i = 0; i < TLD; ++i) {
+                const int idx = 64 * (wl + IX_WAVES * i) + lane;
+                const int m = min(idx / TCH, NTOK - 1);
+                tch[i] = idx < NTOK * TCH ? min(idx % TCH, TCHD - 1) : -1;
+                tsrc[i] = (uint32_t)row_lds[m] * trow;
             }
-            float acc[IT_NT][16];
+            // scale load of wavefront wl (if wl < SXI): slot idx -> (group j = idx / NTOK, token idx % NTOK)
+            const int sx_idx = 64 * wl + lane;
+            const int sx_j = min(sx_idx / NTOK, GB - 1);
+            const uint32_t xsrc = (uint32_t)row_lds[sx_idx % NTOK] * (uint32_t)ngrp;
+            auto fetch = [&](int blk, int buf) {
+                const int g0 = blk * GB;
+                lds_load4(sel(ssrc, ps0, ps1) + g0, &sc_lds[buf][wl][0]);
 #pragma unroll
-            for (int tt = 0; tt < IT_NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[tt][v] = 0.f;
-            // group 0's operands
-            auto ld_b = [&](int g, uint2 &pk, uint32_t &sc) {
-                pk = *(const uint2 *)(wrow + g * 16);
-                sc = srow[g];
-            };
-            uint2 pk_n;
-            uint32_t sc_n;
-            int4_t a_n[IT_NT];
-            ld_b(0, pk_n, sc_n);
-#pragma unroll
-            for (int tt = 0; tt < IT_NT; ++tt) a_n[tt] = *(const int4_t *)(arow[tt]);
-            for (int g0 = 0; g0 < ngrp; g0 += IT_KC) {
-                const int kc = min(IT_KC, ngrp - g0);
-                // stage the token scales of groups g0..g0+kc-1
-                __builtin_amdgcn_wave_barrier();
-                for (int j = 0; j < kc; ++j) {
-                    ts[j][2 * lane] = as[srow_a[0] + g0 + j];
-                    ts[j][2 * lane + 1] = as[srow_a[1] + g0 + j];
+                for (int i = 0; i < WLD; ++i) {
+                    if (64 * i < 32 * WCH) {
+                        if (wch[i] >= 0) lds_load16(sel(wsrc[i], pa0, pa1) + (uint32_t)(g0 + wch[i]) * 16u, &w_lds[buf][wl][i * 1024]);
+                    }
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                for (int j = 0; j < kc; ++j) {
-                    const int g = g0 + j;
-                    const uint2 pk = pk_n;
-                    const uint32_t sc = sc_n;
-                    int4_t a[IT_NT];
 #pragma unroll
-                    for (int tt = 0; tt < IT_NT; ++tt) a[tt] = a_n[tt];
-                    // prefetch group g+1 (the last group reloads itself)
-                    const int gn = g + 1 < ngrp ? g + 1 : g;
-                    ld_b(gn, pk_n, sc_n);
+                for (int i = 0; i < TLD; ++i) {
+                    const int d = wl + IX_WAVES * i;       // instruction: LDS bytes [1024 d, 1024 d + 1024)
+                    if (64 * d < n_tiles * 32 * TCH) {     // tokens the chunk uses (whole rows or more)
+                        const int c = tch[i];
+                        if (c >= 0) lds_load16(tbase + tsrc[i] + (uint32_t)g0 * GBYTES + c * 16, &tok_lds[buf][d * 1024]);
+                    }
+                }
+                if (wl < SXI) lds_load4(as + xsrc + g0 + sx_j, &sx_lds[buf][0][0] + 64 * wl);
+            };
+            // int8 form: 2^(s-128) of the block's groups for the rows' epilogues, from the
+            // staged scale bytes into this wavefront's own table (so no workgroup barrier)
+            auto row_scales = [&](int buf) {
+                if constexpr (!BF16) {
+                    if (half == 0) {
+                        const uint32_t sw = sc_lds[buf][wl][col];
 #pragma unroll
-                    for (int tt = 0; tt < IT_NT; ++tt) a_n[tt] = *(const int4_t *)(arow[tt] + gn * kGroup);
-                    const int4_t b = decode_b(pk);
-                    const float ws = sc == 255u ? 0.0f : __builtin_ldexpf(1.0f, (int)sc - 128);
+                        for (int j = 0; j < GB; ++j) {
+                            const uint32_t sb = (sw >> (8 * j)) & 0xFFu;
+                            ws_lds[wl][j][col] = sb == 255u ? 0.0f : __builtin_ldexpf(1.0f, (int)sb - 128);
+                        }
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
+            };
+            auto lds_loads_done = [] { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+            auto run_chunk = [&](auto ntl_c) {
+                constexpr int NTL = decltype(ntl_c)::value;
+                float acc[NTL][16];
 #pragma unroll
-                    for (int tt = 0; tt < IT_NT; ++tt) {
-                        if (tt < n_tiles) {
-                            const int16_t_v I = mfma_group(a[tt], b);
+                for (int tt = 0; tt < NTL; ++tt)
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const float sx = ts[j][tt * 32 + out_row(lane, v)];
-                                acc[tt][v] = __builtin_fmaf((float)I[v], sx * ws, acc[tt][v]);
+                    for (int v = 0; v < 16; ++v) acc[tt][v] = 0.f;
+                // one group j of the block in buffer buf
+                auto group = [&](int buf, int j) {
+                    // this lane's half of group j of its row (the whole 16 bytes are read)
+                    const int4_t wq = *(const int4_t *)&w_lds[buf][wl][col * WPITCH + 16 * j];
+                    const uint32_t wlo = (uint32_t)(half ? wq[2] : wq[0]), whi = (uint32_t)(half ? wq[3] : wq[1]);
+                    auto tok_frag = [&](int tt, int c) {
+                        return *(const int4_t *)&tok_lds[buf][(32 * tt + col) * TPITCH + 16 * c];
+                    };
+                    auto sx_of = [&](int tt) { return sx_lds[buf][j][32 * tt + col]; };
+                    if constexpr (BF16) {
+                        const uint32_t sbyte = (sc_lds[buf][wl][col] >> (8 * j)) & 0xFFu;
+                        const bool skip = sbyte == 255u;
+                        const float scale = __builtin_bit_cast(float, (skip ? 127u : sbyte) << 23);
+                        const bf16x8_t a0 = fp4x8_bf16(skip ? 0u : wlo, scale);
+                        const bf16x8_t a1 = fp4x8_bf16(skip ? 0u : whi, scale);
+                        auto mm = [&](int tt) {
+                            const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, tok_frag(tt, 4 * j + 2 * half));
+                            const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, tok_frag(tt, 4 * j + 2 * half + 1));
+                            const f32x16_t z = {};
+                            const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, z, 0, 0, 0);
+                            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, d, 0, 0, 0);
+                        };
+                        f32x16_t cur = mm(0);
+#pragma unroll
+                        for (int tt = 0; tt < NTL; ++tt) {
+                            f32x16_t nxt;
+                            if (tt + 1 < NTL) nxt = mm(tt + 1);
+                            const float sx = sx_of(tt);
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) acc[tt][v] = __builtin_fmaf(cur[v], sx, acc[tt][v]);
+                            if (tt + 1 < NTL) cur = nxt;
+                        }
+                    } else {
+                        const int4_t a = decode_b(make_uint2(wlo, whi));
+                        int16_t_v cur = mfma_group(a, tok_frag(0, 2 * j + half));
+                        // row scales of result slots 4q..4q+3: rows 8q + 4*half + 0..3
+                        float ws[16];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 w4 = *(const float4 *)&ws_lds[wl][j][8 * q + 4 * half];
+                            ws[4 * q + 0] = w4.x; ws[4 * q + 1] = w4.y; ws[4 * q + 2] = w4.z; ws[4 * q + 3] = w4.w;
+                        }
+#pragma unroll
+                        for (int tt = 0; tt < NTL; ++tt) {
+                            int16_t_v nxt;
+                            if (tt + 1 < NTL) nxt = mfma_group(a, tok_frag(tt + 1, 2 * j + half));
+                            const float sx = sx_of(tt);
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                acc[tt][v] = __builtin_fmaf((float)cur[v], sx * ws[v], acc[tt][v]);
+                            if (tt + 1 < NTL) cur = nxt;
+                        }
+                    }
+                };
+                fetch(0, 0);
+                lds_loads_done();
+                __syncthreads();
+                for (int blk = 0; blk < n_blocks; ++blk) {
+                    const int buf = blk & 1;
+                    if (blk + 1 < n_blocks) fetch(blk + 1, buf ^ 1);
+                    row_scales(buf);
+#pragma unroll 1
+                    for (int j = 0; j < GB; ++j) group(buf, j);
+                    lds_loads_done();
+                    __syncthreads();
+                }
+                // results: lane holds token col of each tile, rows 8q + 4*half + 0..3 in slots 4q..4q+3
+#pragma unroll
+                for (int tt = 0; tt < NTL; ++tt) {
+                    const int i = tt * 32 + col;
+                    if (i < n_tok) {
+                        float *dst = out + (size_t)(c0 + i) * n_out + rbase + 4 * half;
+#pragma unroll
+                        for (int q = 0; q < (UP ? 2 : 4); ++q) {
+                            float r4[4];
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                r4[b] = UP ? situ(acc[tt][4 * q + b], acc[tt][8 + 4 * q + b]) : acc[tt][4 * q + b];
+                            const int r0 = rbase + 8 * q + 4 * half;
+                            if (r0 + 3 < n_out && ((uintptr_t)(dst + 8 * q) & 15) == 0) {
+                                *(float4 *)(dst + 8 * q) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+                            } else {
+#pragma unroll
+                                for (int b = 0; b < 4; ++b)
+                                    if (r0 + b < n_out) dst[8 * q + b] = r4[b];
                             }
                         }
                     }
                 }
-            }
-#pragma unroll
-            for (int tt = 0; tt < IT_NT; ++tt) {
-                if (tt < n_tiles) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int i = tt * 32 + out_row(lane, v);
-                        float val = acc[tt][v];
-                        if (UP) {
-                            // lane col (< 16) holds g of row rr, lane col+16 holds u of the same row
-                            const float other = __shfl_xor(val, 16, kWave);
-                            val = situ(val, other);
-                        }
-                        const bool mine = UP ? (col < 16) : true;
-                        if (mine && i < n_tok && rr < n_out) out[(size_t)(c0 + i) * n_out + rr] = val;
-                    }
-                }
+            };
+            static_assert(IX_NT == 3, "one instantiation per tile count");
+            switch (n_tiles) {
+                case 1: run_chunk(std::integral_constant<int, 1>{}); break;
+                case 2: run_chunk(std::integral_constant<int, 2>{}); break;
+                default: run_chunk(std::integral_constant<int, 3>{}); break;
             }
         }
     }
 }
 
-int launch_moe_up_idot(float *h, const int8_t *xq, const float *xs, const BankDev &bank, const int32_t *active,
-                       const int32_t *offsets, const int32_t *perm, int top_k, int latent, int inter, int max_slots,
-                       hipStream_t st) {
-    const int items = max_slots * ((inter + 15) / 16);
-    const int blocks = (items + 3) / 4 < 8192 ? (items + 3) / 4 : 8192;
-    moe_idot_kernel<true><<<blocks, 256, 0, st>>>(h, xq, xs, bank, active, offsets, perm, top_k, latent, inter,
-                                                  max_slots);
+int launch_moe_up_idot(float *h, const int8_t *xq, const uint16_t *xqb, const float *xs, const BankDev &bank,
+                       const int32_t *active, const int32_t *offsets, const int32_t *perm, int top_k, int latent,
+                       int inter, int max_slots, hipStream_t st) {
+    const int items = max_slots * ((inter + 16 * IX_WAVES - 1) / (16 * IX_WAVES));
+    const int blocks = items < 16384 ? items : 16384;
+    if (xqb)
+        moe_idot_kernel<true, true><<<blocks, IX_WAVES * 64, 0, st>>>(h, xq, xqb, xs, bank, active, offsets, perm,
+                                                                      top_k, latent, inter, max_slots);
+    else
+        moe_idot_kernel<true, false><<<blocks, IX_WAVES * 64, 0, st>>>(h, xq, xqb, xs, bank, active, offsets, perm,
+                                                                       top_k, latent, inter, max_slots);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
-int launch_moe_down_idot(float *ypair, const int8_t *hq, const float *hs, const BankDev &bank, const int32_t *active,
-                         const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
-                         hipStream_t st) {
-    const int items = max_slots * ((latent + 31) / 32);
-    const int blocks = (items + 3) / 4 < 8192 ? (items + 3) / 4 : 8192;
-    moe_idot_kernel<false><<<blocks, 256, 0, st>>>(ypair, hq, hs, bank, active, offsets, perm, 1, inter, latent,
-                                                   max_slots);
+int launch_moe_down_idot(float *ypair, const int8_t *hq, const uint16_t *hqb, const float *hs, const BankDev &bank,
+                         const int32_t *active, const int32_t *offsets, const int32_t *perm, int latent, int inter,
+                         int max_slots, hipStream_t st) {
+    const int items = max_slots * ((latent + 32 * IX_WAVES - 1) / (32 * IX_WAVES));
+    const int blocks = items < 16384 ? items : 16384;
+    if (hqb)
+        moe_idot_kernel<false, true><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, hq, hqb, hs, bank, active, offsets,
+                                                                       perm, 1, inter, latent, max_slots);
+    else
+        moe_idot_kernel<false, false><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, hq, hqb, hs, bank, active, offsets,
+                                                                        perm, 1, inter, latent, max_slots);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

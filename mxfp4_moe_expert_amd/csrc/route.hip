@@ -108,37 +108,47 @@ __global__ __launch_bounds__(SPLIT * 64) void logits_mfma_kernel(double *__restr
     for (int i = 0; i < BM; ++i)
 #pragma unroll
         for (int j = 0; j < BN; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
-    for (int kk = ka; kk < kb; ++kk) {
-        const int k = kk * 16 + 4 * q;
-        float a[BM][4], b[BN][4];
-        if (VEC && k + 4 <= in) {
+    // NS steps of operands are loaded back to back, then consumed: one memory
+    // latency per NS steps (steps past the slice read zeros)
+    constexpr int NS = 8;
+    for (int k0 = ka; k0 < kb; k0 += NS) {
+        float a[NS][BM][4], b[NS][BN][4];
 #pragma unroll
-            for (int i = 0; i < BM; ++i) {
-                const float4 v = *(const float4 *)(xr[i] + k);
-                a[i][0] = v.x; a[i][1] = v.y; a[i][2] = v.z; a[i][3] = v.w;
-            }
+        for (int st = 0; st < NS; ++st) {
+            const int k = (k0 + st) * 16 + 4 * q;
+            const bool live = k0 + st < kb;
+            if (VEC && live && k + 4 <= in) {
 #pragma unroll
-            for (int j = 0; j < BN; ++j) {
-                const float4 v = *(const float4 *)(wr[j] + k);
-                b[j][0] = v.x; b[j][1] = v.y; b[j][2] = v.z; b[j][3] = v.w;
-            }
-        } else {
+                for (int i = 0; i < BM; ++i) {
+                    const float4 v = *(const float4 *)(xr[i] + k);
+                    a[st][i][0] = v.x; a[st][i][1] = v.y; a[st][i][2] = v.z; a[st][i][3] = v.w;
+                }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bool in_k = k + s < in;
+                for (int j = 0; j < BN; ++j) {
+                    const float4 v = *(const float4 *)(wr[j] + k);
+                    b[st][j][0] = v.x; b[st][j][1] = v.y; b[st][j][2] = v.z; b[st][j][3] = v.w;
+                }
+            } else {
 #pragma unroll
-                for (int i = 0; i < BM; ++i) a[i][s] = in_k ? xr[i][k + s] : 0.0f;
+                for (int s = 0; s < 4; ++s) {
+                    const bool in_k = live && k + s < in;
 #pragma unroll
-                for (int j = 0; j < BN; ++j) b[j][s] = in_k ? wr[j][k + s] : 0.0f;
+                    for (int i = 0; i < BM; ++i) a[st][i][s] = in_k ? xr[i][k + s] : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < BN; ++j) b[st][j][s] = in_k ? wr[j][k + s] : 0.0f;
+                }
             }
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int st = 0; st < NS; ++st)
 #pragma unroll
-            for (int i = 0; i < BM; ++i)
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int j = 0; j < BN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[i][s], (double)b[j][s], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < BM; ++i)
+#pragma unroll
+                    for (int j = 0; j < BN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[st][i][s], (double)b[st][j][s],
+                                                                        acc[i][j], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < BM; ++i)

@@ -77,4 +77,13 @@ def test_rejects_bad_arguments_before_any_launch(k3g):
     bank = k3g.ExpertBank(4096, 4096, 8, 64, 64, (C.c_int64 * 6)(0, 2048, 2304, 4352, 4608, 6656))
     assert L.k3g_moe_layer(fake, fake, fake, fake, C.byref(bank), 2, 2, 0, fake, 16, None) == -3
     assert L.k3g_moe_layer(fake, fake, fake, fake, C.byref(bank), 2, 2, 7, fake, 1 << 24, None) == -1
+    # IDOT needs widths that are multiples of 128 (bank of 64-wide experts: unsupported),
+    # and the bf16 form only as a modifier of IDOT
+    assert L.k3g_moe_layer(P(1 << 20), P(2 << 20), P(3 << 20), P(4 << 20), C.byref(bank), 2, 2, 1, P(1 << 24),
+                           1 << 24, None) == -5
+    assert L.k3g_moe_layer(fake, fake, fake, fake, C.byref(bank), 2, 2, 0x200, fake, 1 << 24, None) == -1
+    bank128 = k3g.ExpertBank(4096, 1 << 16, 8, 128, 128, (C.c_int64 * 6)(0, 8192, 8704, 16896, 17408, 25602))
+    # a scale tensor off its 4-byte alignment
+    assert L.k3g_moe_layer(P(1 << 20), P(2 << 20), P(3 << 20), P(4 << 20), C.byref(bank128), 2, 2, 1, P(1 << 24),
+                           1 << 24, None) == -2
     assert L.k3g_status_string(-3) == b"workspace too small"

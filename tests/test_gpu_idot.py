@@ -1,9 +1,10 @@
-"""GPU parity of the IDOT path (int8 activations, int8 matrix cores).
+"""GPU parity of the IDOT path (int8 activations; int8 matrix cores, or the
+bf16 matrix cores on the same exact values with K3G_IDOT_BF16).
 
-Bit-exact: the quantised activations (q, s) and the int32 group sums. fp32
-outputs: within 1e-5 * sum_j |W_ij||a_j| of the oracle's IDOT result for the
-same quantised input, stage by stage ("Kimi K3 engine (c/kimi_k3.c)",
-"Streaming design", K3_IDOT).
+Bit-exact: the quantised activations (q, s), the int32 group sums, and the
+two forms' outputs against each other. fp32 outputs: within 1e-5 *
+sum_j |W_ij||a_j| of the oracle's IDOT result for the same quantised input,
+stage by stage ("Kimi K3 engine (c/kimi_k3.c)", "Streaming design", K3_IDOT).
 """
 import numpy as np
 import pytest
@@ -75,13 +76,14 @@ def test_groupsums_bit_exact(k3g, T, rows, n_in):
     assert np.array_equal(host(sums), oracle.idot_groupsums(q, pk))
 
 
-def check_expert_idot(k3g, ex, x, latent, inter):
+def check_expert_idot(k3g, ex, x, latent, inter, form=0):
+    mode = k3g.IDOT | form
     exd = {k: dev(v) for k, v in ex.items()}
     y = torch.empty(latent, dtype=torch.float32, device="cuda")
-    sh = k3g.shape(latent=latent, inter=inter, mode=k3g.IDOT)
+    sh = k3g.shape(latent=latent, inter=inter, mode=mode)
     ws = k3g.workspace(k3g.OP_EXPERT_GLU, sh)
     L = k3g.workspace_layout(k3g.OP_EXPERT_GLU, sh)
-    k3g.k3g_expert_glu(y, dev(x), exd, k3g.IDOT, ws)
+    k3g.k3g_expert_glu(y, dev(x), exd, mode, ws)
     yg = host(y)
     xq = ws_view(ws, L, "xq", latent, np.int8)
     xs = ws_view(ws, L, "xs", latent // 32, np.float32)
@@ -102,29 +104,40 @@ def check_expert_idot(k3g, ex, x, latent, inter):
     return yg
 
 
+FORMS = [0, 0x200]  # int8 matrix cores; K3G_IDOT_BF16
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("lo,hi", [(118, 132), (120, 122)])
-def test_expert_glu_idot_full_size(k3g, lo, hi):
-    print(f"idot expert glu {lo}..{hi}", flush=True)
+def test_expert_glu_idot_full_size(k3g, lo, hi, form):
+    print(f"idot expert glu {lo}..{hi} form {form:#x}", flush=True)
     ex = synth.expert(synth.SEED_BASE, 0, lo=lo, hi=hi)
     x = synth.activations(synth.SEED_BASE, 1)[0]
-    check_expert_idot(k3g, ex, x, 3584, 3072)
+    check_expert_idot(k3g, ex, x, 3584, 3072, form)
 
 
-def test_expert_glu_idot_small(k3g):
-    ex = synth.expert(43, 1, latent=96, inter=160, lo=121, hi=123, p255=0.03)
-    x = synth.activations(43, 1, 96)[0]
-    check_expert_idot(k3g, ex, x, 96, 160)
+@pytest.mark.parametrize("form", FORMS)
+def test_expert_glu_idot_small(k3g, form):
+    ex = synth.expert(43, 1, latent=128, inter=256, lo=121, hi=123, p255=0.03)
+    x = synth.activations(43, 1, 128)[0]
+    check_expert_idot(k3g, ex, x, 128, 256, form)
+
+
+def run_layer_idot(k3g, bank, x, idx, wts, form):
+    T, K = idx.shape
+    mode = k3g.IDOT | form
+    y = torch.empty((T, bank.latent), dtype=torch.float32, device="cuda")
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=bank.n_experts, latent=bank.latent, inter=bank.inter, mode=mode)
+    ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
+    k3g.k3g_moe_layer(y, dev(x), dev(idx), dev(wts), bank, mode, ws)
+    return host(y), ws, L
 
 
 def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
     T, K = idx.shape
     latent, inter, E = bank.latent, bank.inter, bank.n_experts
-    y = torch.empty((T, latent), dtype=torch.float32, device="cuda")
-    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=latent, inter=inter, mode=k3g.IDOT)
-    ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
-    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
-    k3g.k3g_moe_layer(y, dev(x), dev(idx), dev(wts), bank, k3g.IDOT, ws)
-    yg = host(y)
+    yg, ws, L = run_layer_idot(k3g, bank, x, idx, wts, 0)
     P = T * K
     inv = ws_view(ws, L, "inv", P, np.int32)
     xq = ws_view(ws, L, "xq", T * latent, np.int8).reshape(T, latent)
@@ -157,6 +170,14 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
             acc += float(wts[t, k]) * yp.astype(np.float64)
             nrm += abs(float(wts[t, k])) * np.abs(yp.astype(np.float64))
         assert_norm_close(yg[t], acc, nrm, what=f"idot combine t={t}")
+    # the bf16 form computes the same numbers bit for bit
+    yb, wsb, Lb = run_layer_idot(k3g, bank, x, idx, wts, 0x200)
+    P = T * K
+    for name, width, dt in (("h", inter, np.float32), ("hq", inter, np.int8), ("ypair", latent, np.float32)):
+        a = ws_view(ws, L, name, P * width, dt)
+        b = ws_view(wsb, Lb, name, P * width, dt)
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"bf16 form differs in {name}"
+    assert np.array_equal(yg.view(np.uint32), yb.view(np.uint32)), "bf16 form differs in y"
     return yg
 
 
@@ -168,7 +189,7 @@ def ws_view_rows(ws, L, name, row, width, dtype):
 
 def test_layer_idot_small_many_tokens(k3g):
     # 300 tokens on 8 experts, top 3: ~112 pairs per expert -> several token tiles and a second chunk
-    E, latent, inter, T, K = 8, 128, 96, 300, 3
+    E, latent, inter, T, K = 8, 128, 256, 300, 3
     src, bankt, bank = make_bank(k3g, 71, E, latent, inter, 120, 123, 0.01)
     x = synth.activations(71, T, latent)
     W, b = synth.router(71, E, latent, 0.1)
