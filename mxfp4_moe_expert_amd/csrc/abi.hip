@@ -14,8 +14,8 @@ int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int
                         const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
                         hipStream_t st);
 int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
-                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots, bool lut,
-                          hipStream_t st);
+                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                          bool multi_pairs, bool lut, hipStream_t st);
 int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
                    int latent, hipStream_t st);
 int launch_logits(double *logits, const float *x, const float *W, int T, int in, int E, hipStream_t st);
@@ -309,7 +309,7 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
     hipStream_t st = S(stream);
     if (base_mode(mode) == K3G_EXACT) {
         K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut_of(mode), st));
-        return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, lut_of(mode), st);
+        return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, false, lut_of(mode), st);
     }
     int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
     float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
@@ -392,7 +392,7 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_down_idot(ypair, hq, hqb, hs, b, active, offsets, perm, latent, inter, max_slots, st)
                        : launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots,
-                                               lut_of(mode), st);
+                                               n_tokens > 1, lut_of(mode), st);
         case K3G_STAGE_COMBINE:
             return launch_combine(y, ypair, wts, inv, n_tokens, top_k, latent, st);
         default:

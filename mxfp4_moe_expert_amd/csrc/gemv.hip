@@ -192,12 +192,15 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
 // is the i-th expert that has pairs (active[1+i]); its pairs are the sorted
 // positions [offsets[e], offsets[e+1]), token = perm[pos] / top_k. For each
 // pair and row r: g = w1[r].x, u = w3[r].x, h[pos][r] = SiTU(g, u).
+// NP pairs share each pass over the rows (their x in registers), so an expert
+// chosen by several tokens is streamed ceil(pairs / NP) times.
 // With perm == nullptr the call is one expert (bank expert 0) on token 0.
-template <int NG, bool LUT>
+template <int NG, bool LUT, int NP>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
     float *__restrict__ h, const float *__restrict__ x, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int latent, int inter,
     int max_slots, int rpi) {
+    constexpr int PIPE = NP > 1 ? 2 : K3G_PIPE;  // rows in flight: two pairs need the registers
     uint32_t *lut = nullptr;
     if constexpr (LUT) {
         __shared__ uint32_t lut_lds[kLutWords];
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
     const int chunks = (inter + rpi - 1) / rpi;
     const int n_act = perm ? active[0] : 1;
     const int n_items = max_slots * chunks;
-    float xr[NG * kGroup];
+    float xr[NP][NG * kGroup];
     for (int item = blockIdx.x * waves + wave; item < n_items; item += gridDim.x * waves) {
         const int slot = item / chunks;
         if (slot >= n_act) continue;
@@ -229,33 +232,46 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
         const int r0 = chunk * rpi;
         const int r1 = min(inter, r0 + rpi);
         auto R = [&](int r) { return min(r, r1 - 1); };
-        for (int pos = p0; pos < p1; ++pos) {
-            const int t = perm ? perm[pos] / top_k : 0;
-            load_x<NG>(xr, x + (size_t)t * latent, lane, ngrp);
-            RowData<NG> b1[K3G_PIPE], b3[K3G_PIPE];
+        for (int pos = p0; pos < p1; pos += NP) {
+            // a pass of NP pairs; a missing last pair repeats the one before and is not stored
+            int ps[NP];
 #pragma unroll
-            for (int st = 0; st < K3G_PIPE; ++st) {
+            for (int q = 0; q < NP; ++q) {
+                ps[q] = min(pos + q, p1 - 1);
+                const int t = perm ? perm[ps[q]] / top_k : 0;
+                load_x<NG>(xr[q], x + (size_t)t * latent, lane, ngrp);
+            }
+            RowData<NG> b1[PIPE], b3[PIPE];
+#pragma unroll
+            for (int st = 0; st < PIPE; ++st) {
                 load_row<NG>(b1[st], m1, R(r0 + st), cols);
                 load_row<NG>(b3[st], m3, R(r0 + st), cols);
             }
-            float gv = 0.f, uv = 0.f;  // lane k holds row k of the current block of 64
-            for (int r = r0; r < r1; r += K3G_PIPE) {
+            float gv[NP], uv[NP];  // lane k holds row k of the current block of 64
 #pragma unroll
-                for (int st = 0; st < K3G_PIPE; ++st) {
+            for (int q = 0; q < NP; ++q) gv[q] = uv[q] = 0.f;
+            for (int r = r0; r < r1; r += PIPE) {
+#pragma unroll
+                for (int st = 0; st < PIPE; ++st) {
                     const int rr = r + st;
                     if (rr < r1) {
-                        const float g = wave_sum(row_partial<NG, LUT>(b1[st], lut, lane_off, xr, valid));
-                        const float u = wave_sum(row_partial<NG, LUT>(b3[st], lut, lane_off, xr, valid));
                         const int k = (rr - r0) & (kWave - 1);
-                        gv = lane == k ? g : gv;
-                        uv = lane == k ? u : uv;
+#pragma unroll
+                        for (int q = 0; q < NP; ++q) {
+                            const float g = wave_sum(row_partial<NG, LUT>(b1[st], lut, lane_off, xr[q], valid));
+                            const float u = wave_sum(row_partial<NG, LUT>(b3[st], lut, lane_off, xr[q], valid));
+                            gv[q] = lane == k ? g : gv[q];
+                            uv[q] = lane == k ? u : uv[q];
+                        }
                         if (k == kWave - 1 || rr == r1 - 1) {
                             // SiTU once per block, one row per lane
-                            if (lane <= k) h[(size_t)pos * inter + rr - k + lane] = situ(gv, uv);
+#pragma unroll
+                            for (int q = 0; q < NP; ++q)
+                                if (lane <= k && pos + q < p1) h[(size_t)ps[q] * inter + rr - k + lane] = situ(gv[q], uv[q]);
                         }
                     }
-                    load_row<NG>(b1[st], m1, R(r + st + K3G_PIPE), cols);
-                    load_row<NG>(b3[st], m3, R(r + st + K3G_PIPE), cols);
+                    load_row<NG>(b1[st], m1, R(r + st + PIPE), cols);
+                    load_row<NG>(b3[st], m3, R(r + st + PIPE), cols);
                 }
             }
         }
@@ -263,12 +279,14 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
 }
 
 // Grouped down-projection: ypair[pos][r] = w2[r] . h[pos] for every pair of
-// the slot's expert. Same items as the up kernel, over latent rows.
-template <int NG, bool LUT>
+// the slot's expert. Same items as the up kernel, over latent rows; NP pairs
+// share each pass over the rows.
+template <int NG, bool LUT, int NP>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kernel(
     float *__restrict__ ypair, const float *__restrict__ h, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int latent, int inter,
     int max_slots, int rpi) {
+    constexpr int PIPE = NP > 1 ? 2 : K3G_PIPE;  // rows in flight: two pairs need the registers
     uint32_t *lut = nullptr;
     if constexpr (LUT) {
         __shared__ uint32_t lut_lds[kLutWords];
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kerne
     const int chunks = (latent + rpi - 1) / rpi;
     const int n_act = perm ? active[0] : 1;
     const int n_items = max_slots * chunks;
-    float xr[NG * kGroup];
+    float xr[NP][NG * kGroup];
     for (int item = blockIdx.x * waves + wave; item < n_items; item += gridDim.x * waves) {
         const int slot = item / chunks;
         if (slot >= n_act) continue;
@@ -299,25 +317,37 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kerne
         const int r0 = chunk * rpi;
         const int r1 = min(latent, r0 + rpi);
         auto R = [&](int r) { return min(r, r1 - 1); };
-        for (int pos = p0; pos < p1; ++pos) {
-            load_x<NG>(xr, h + (size_t)pos * inter, lane, ngrp);
-            RowData<NG> buf[K3G_PIPE];
+        for (int pos = p0; pos < p1; pos += NP) {
+            int ps[NP];
 #pragma unroll
-            for (int st = 0; st < K3G_PIPE; ++st) load_row<NG>(buf[st], m2, R(r0 + st), cols);
-            float acc = 0.f;  // lane k holds row k of the current block of 64
-            for (int r = r0; r < r1; r += K3G_PIPE) {
+            for (int q = 0; q < NP; ++q) {
+                ps[q] = min(pos + q, p1 - 1);
+                load_x<NG>(xr[q], h + (size_t)ps[q] * inter, lane, ngrp);
+            }
+            RowData<NG> buf[PIPE];
 #pragma unroll
-                for (int st = 0; st < K3G_PIPE; ++st) {
+            for (int st = 0; st < PIPE; ++st) load_row<NG>(buf[st], m2, R(r0 + st), cols);
+            float acc[NP];  // lane k holds row k of the current block of 64
+#pragma unroll
+            for (int q = 0; q < NP; ++q) acc[q] = 0.f;
+            for (int r = r0; r < r1; r += PIPE) {
+#pragma unroll
+                for (int st = 0; st < PIPE; ++st) {
                     const int rr = r + st;
                     if (rr < r1) {
-                        const float sa = wave_sum(row_partial<NG, LUT>(buf[st], lut, lane_off, xr, valid));
                         const int k = (rr - r0) & (kWave - 1);
-                        acc = lane == k ? sa : acc;
+#pragma unroll
+                        for (int q = 0; q < NP; ++q) {
+                            const float sa = wave_sum(row_partial<NG, LUT>(buf[st], lut, lane_off, xr[q], valid));
+                            acc[q] = lane == k ? sa : acc[q];
+                        }
                         if (k == kWave - 1 || rr == r1 - 1) {
-                            if (lane <= k) ypair[(size_t)pos * latent + rr - k + lane] = acc;
+#pragma unroll
+                            for (int q = 0; q < NP; ++q)
+                                if (lane <= k && pos + q < p1) ypair[(size_t)ps[q] * latent + rr - k + lane] = acc[q];
                         }
                     }
-                    load_row<NG>(buf[st], m2, R(r + st + K3G_PIPE), cols);
+                    load_row<NG>(buf[st], m2, R(r + st + PIPE), cols);
                 }
             }
         }
@@ -391,41 +421,67 @@ int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
+// Rows per work item: about `target` items in all, at least 8 rows each.
+static int rows_per_item(int max_slots, int rows, int target) {
+    int rpi = (int)(((int64_t)max_slots * rows + target - 1) / target);
+    if (rpi < 8) rpi = 8;
+    return rpi > rows ? rows : rpi;
+}
+
+// One token: every slot has exactly one pair (top-k picks distinct experts), and
+// ~2048 items. More tokens: pairs go two to a pass and the rows are cut finer
+// (more slots share the chip).
 int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
                         const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
                         hipStream_t st) {
     const int ng = pick_ng(latent / kGroup);
-    // rows per item: about 2048 items in all when each expert has one pair
-    int rpi = (int)(((int64_t)max_slots * inter + K3G_ITEMS_TARGET - 1) / K3G_ITEMS_TARGET);
-    if (rpi < 8) rpi = 8;
-    if (rpi > inter) rpi = inter;
-    (void)n_pairs;
+    const bool multi = n_pairs > top_k && ng <= 2;
+    const int rpi = rows_per_item(max_slots, inter, multi ? 4 * K3G_ITEMS_TARGET : K3G_ITEMS_TARGET);
     const int items = max_slots * ((inter + rpi - 1) / rpi);
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
-    switch (ng) {
-        case 1: if (lut) moe_up_exact_kernel<1, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); else moe_up_exact_kernel<1, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
-        case 2: if (lut) moe_up_exact_kernel<2, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); else moe_up_exact_kernel<2, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
-        case 4: if (lut) moe_up_exact_kernel<4, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); else moe_up_exact_kernel<4, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi); break;
+#define K3G_UP(NG_, LUT_, NP_) \
+    moe_up_exact_kernel<NG_, LUT_, NP_><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi)
+    switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
+        case 4: K3G_UP(1, false, 1); break;
+        case 5: K3G_UP(1, true, 1); break;
+        case 6: K3G_UP(1, false, 2); break;
+        case 7: K3G_UP(1, true, 2); break;
+        case 8: K3G_UP(2, false, 1); break;
+        case 9: K3G_UP(2, true, 1); break;
+        case 10: K3G_UP(2, false, 2); break;
+        case 11: K3G_UP(2, true, 2); break;
+        case 16: K3G_UP(4, false, 1); break;
+        case 17: K3G_UP(4, true, 1); break;
         default: return K3G_EUNSUPPORTED;
     }
+#undef K3G_UP
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
 int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
-                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots, bool lut,
-                          hipStream_t st) {
+                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                          bool multi_pairs, bool lut, hipStream_t st) {
     const int ng = pick_ng(inter / kGroup);
-    int rpi = (int)(((int64_t)max_slots * latent + K3G_ITEMS_TARGET - 1) / K3G_ITEMS_TARGET);
-    if (rpi < 8) rpi = 8;
-    if (rpi > latent) rpi = latent;
+    const bool multi = multi_pairs && ng <= 2;
+    const int rpi = rows_per_item(max_slots, latent, multi ? 4 * K3G_ITEMS_TARGET : K3G_ITEMS_TARGET);
     const int items = max_slots * ((latent + rpi - 1) / rpi);
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
-    switch (ng) {
-        case 1: if (lut) moe_down_exact_kernel<1, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); else moe_down_exact_kernel<1, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
-        case 2: if (lut) moe_down_exact_kernel<2, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); else moe_down_exact_kernel<2, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
-        case 4: if (lut) moe_down_exact_kernel<4, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); else moe_down_exact_kernel<4, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi); break;
+#define K3G_DN(NG_, LUT_, NP_) \
+    moe_down_exact_kernel<NG_, LUT_, NP_><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi)
+    switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
+        case 4: K3G_DN(1, false, 1); break;
+        case 5: K3G_DN(1, true, 1); break;
+        case 6: K3G_DN(1, false, 2); break;
+        case 7: K3G_DN(1, true, 2); break;
+        case 8: K3G_DN(2, false, 1); break;
+        case 9: K3G_DN(2, true, 1); break;
+        case 10: K3G_DN(2, false, 2); break;
+        case 11: K3G_DN(2, true, 2); break;
+        case 16: K3G_DN(4, false, 1); break;
+        case 17: K3G_DN(4, true, 1); break;
         default: return K3G_EUNSUPPORTED;
     }
+#undef K3G_DN
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
