@@ -32,6 +32,15 @@
 #ifndef K3G_ITEMS_TARGET
 #define K3G_ITEMS_TARGET 2048  // work items a decode launch is cut into
 #endif
+// Several tokens: the pairs of an expert take turns over short runs of rows, so
+// that the later passes find the rows in L2 (one pair per pass keeps the
+// kernel at two wavefronts per SIMD; two per pass needs all 256 VGPRs).
+#ifndef K3G_MULTI_ITEMS
+#define K3G_MULTI_ITEMS 131072  // work items when several tokens share experts
+#endif
+#ifndef K3G_MULTI_NP
+#define K3G_MULTI_NP 1          // pairs per pass over the rows when several tokens share experts
+#endif
 
 namespace k3g {
 
@@ -436,7 +445,7 @@ int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int
                         hipStream_t st) {
     const int ng = pick_ng(latent / kGroup);
     const bool multi = n_pairs > top_k && ng <= 2;
-    const int rpi = rows_per_item(max_slots, inter, multi ? 4 * K3G_ITEMS_TARGET : K3G_ITEMS_TARGET);
+    const int rpi = rows_per_item(max_slots, inter, multi ? K3G_MULTI_ITEMS : K3G_ITEMS_TARGET);
     const int items = max_slots * ((inter + rpi - 1) / rpi);
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
 #define K3G_UP(NG_, LUT_, NP_) \
@@ -444,12 +453,12 @@ int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int
     switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
         case 4: K3G_UP(1, false, 1); break;
         case 5: K3G_UP(1, true, 1); break;
-        case 6: K3G_UP(1, false, 2); break;
-        case 7: K3G_UP(1, true, 2); break;
+        case 6: K3G_UP(1, false, K3G_MULTI_NP); break;
+        case 7: K3G_UP(1, true, K3G_MULTI_NP); break;
         case 8: K3G_UP(2, false, 1); break;
         case 9: K3G_UP(2, true, 1); break;
-        case 10: K3G_UP(2, false, 2); break;
-        case 11: K3G_UP(2, true, 2); break;
+        case 10: K3G_UP(2, false, K3G_MULTI_NP); break;
+        case 11: K3G_UP(2, true, K3G_MULTI_NP); break;
         case 16: K3G_UP(4, false, 1); break;
         case 17: K3G_UP(4, true, 1); break;
         default: return K3G_EUNSUPPORTED;
@@ -463,7 +472,7 @@ int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, con
                           bool multi_pairs, bool lut, hipStream_t st) {
     const int ng = pick_ng(inter / kGroup);
     const bool multi = multi_pairs && ng <= 2;
-    const int rpi = rows_per_item(max_slots, latent, multi ? 4 * K3G_ITEMS_TARGET : K3G_ITEMS_TARGET);
+    const int rpi = rows_per_item(max_slots, latent, multi ? K3G_MULTI_ITEMS : K3G_ITEMS_TARGET);
     const int items = max_slots * ((latent + rpi - 1) / rpi);
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
 #define K3G_DN(NG_, LUT_, NP_) \
@@ -471,12 +480,12 @@ int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, con
     switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
         case 4: K3G_DN(1, false, 1); break;
         case 5: K3G_DN(1, true, 1); break;
-        case 6: K3G_DN(1, false, 2); break;
-        case 7: K3G_DN(1, true, 2); break;
+        case 6: K3G_DN(1, false, K3G_MULTI_NP); break;
+        case 7: K3G_DN(1, true, K3G_MULTI_NP); break;
         case 8: K3G_DN(2, false, 1); break;
         case 9: K3G_DN(2, true, 1); break;
-        case 10: K3G_DN(2, false, 2); break;
-        case 11: K3G_DN(2, true, 2); break;
+        case 10: K3G_DN(2, false, K3G_MULTI_NP); break;
+        case 11: K3G_DN(2, true, K3G_MULTI_NP); break;
         case 16: K3G_DN(4, false, 1); break;
         case 17: K3G_DN(4, true, 1); break;
         default: return K3G_EUNSUPPORTED;

@@ -455,23 +455,23 @@ __global__ __launch_bounds__(TB_MAX_WAVES * 64) void topk_block_kernel(int32_t *
 }
 
 // ---- bucket: stable counting sort of the T*K pairs by expert ---------------------
-// One workgroup. counts/offsets by an LDS histogram and scan; positions within
-// an expert follow token order: tokens are taken 64 at a time, a 64-bit mask
-// per expert marks which of them chose it, and a pair's rank is the popcount of
-// the mask below its token.
-constexpr int BK_THREADS = 1024;
-
+// One workgroup of NT threads. counts/offsets by an LDS histogram and scan;
+// positions within an expert follow token order: tokens are taken up to 64 at
+// a time, a 64-bit mask per expert marks which of them chose it, and a pair's
+// rank is the popcount of the mask below its token.
+template <int NT>
 __device__ inline int block_excl_scan(int v, int *wsum) {
     // wavefront scans with shuffles, then a scan of the per-wavefront totals;
     // returns the exclusive prefix of v over the block.
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-    constexpr int nw = BK_THREADS / kWave;
+    constexpr int nw = NT / kWave;
     int inc = v;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
         const int o = __shfl_up(inc, d, kWave);
         if (lane >= d) inc += o;
     }
+    if (nw == 1) return inc - v;
     if (lane == kWave - 1) wsum[w] = inc;
     __syncthreads();
     if (w == 0) {
@@ -489,35 +489,36 @@ __device__ inline int block_excl_scan(int v, int *wsum) {
     return res;
 }
 
-__global__ __launch_bounds__(BK_THREADS) void bucket_kernel(int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                            int32_t *__restrict__ perm, int32_t *__restrict__ inv,
-                                                            int32_t *__restrict__ active, const int32_t *__restrict__ idx,
-                                                            int T, int K, int E) {
+template <int NT>
+__global__ __launch_bounds__(NT) void bucket_kernel(int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                    int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                                                    int32_t *__restrict__ active, const int32_t *__restrict__ idx,
+                                                    int T, int K, int E) {
     extern __shared__ int sm[];
     int *cnt = sm;                                        // [E]
     int *run = sm + E;                                    // [E]
-    int *tmp = sm + 2 * E;                                // [BK_THREADS]
-    unsigned long long *mask = (unsigned long long *)(sm + 2 * E + BK_THREADS + ((2 * E + BK_THREADS) & 1));  // [E]
+    int *tmp = sm + 2 * E;                                // [NT / 64]
+    unsigned long long *mask = (unsigned long long *)(sm + 2 * E + 16 + ((2 * E) & 1));  // [E]
     const int tid = threadIdx.x;
     const int P = T * K;
-    for (int e = tid; e < E; e += BK_THREADS) { cnt[e] = 0; mask[e] = 0ull; }
+    for (int e = tid; e < E; e += NT) { cnt[e] = 0; mask[e] = 0ull; }
     __syncthreads();
     // ids outside [0, E) break the caller's precondition; they are dropped here
     // (their pair gets inv = -1 and contributes nothing) rather than written
     // out of bounds.
-    for (int p = tid; p < P; p += BK_THREADS) {
+    for (int p = tid; p < P; p += NT) {
         const int e = idx[p];
         if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
         else inv[p] = -1;
     }
     __syncthreads();
-    // each thread owns a run of ceil(E/BK_THREADS) experts
-    const int per = (E + BK_THREADS - 1) / BK_THREADS;
+    // each thread owns a run of ceil(E/NT) experts
+    const int per = (E + NT - 1) / NT;
     const int e0 = tid * per;
     int local = 0, nz = 0;
     for (int e = e0; e < e0 + per && e < E; ++e) { local += cnt[e]; nz += cnt[e] > 0; }
-    const int base = block_excl_scan(local, tmp);
-    const int nzbase = block_excl_scan(nz, tmp);
+    const int base = block_excl_scan<NT>(local, tmp);
+    const int nzbase = block_excl_scan<NT>(nz, tmp);
     int acc = base, nacc = nzbase;
     for (int e = e0; e < e0 + per && e < E; ++e) {
         counts[e] = cnt[e];
@@ -526,12 +527,12 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(int32_t *__restrict_
         if (cnt[e] > 0) active[1 + nacc++] = e;
         acc += cnt[e];
     }
-    if (tid == BK_THREADS - 1) {
+    if (tid == NT - 1) {
         offsets[E] = acc;  // the last thread's prefix + its own is the total
         active[0] = nacc;
     }
     __syncthreads();
-    const int tpc = (BK_THREADS / K) < 64 ? (BK_THREADS / K) : 64;  // tokens per chunk
+    const int tpc = (NT / K) < 64 ? (NT / K) : 64;  // tokens per chunk
     for (int c0 = 0; c0 < T; c0 += tpc) {
         const int lt = tid / K, k = tid - lt * K;
         const int t = c0 + lt;
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(int32_t *__restrict_
             inv[t * K + k] = pos;
         }
         __syncthreads();
-        for (int ee = tid; ee < E; ee += BK_THREADS) {
+        for (int ee = tid; ee < E; ee += NT) {
             run[ee] += __popcll(mask[ee]);
             mask[ee] = 0ull;
         }
@@ -601,12 +602,13 @@ int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bia
 }
 
 size_t bucket_lds_bytes(int E) {
-    return sizeof(int) * (size_t)(2 * E + BK_THREADS + 2) + sizeof(unsigned long long) * (size_t)E;
+    return sizeof(int) * (size_t)(2 * E + 16 + 2) + sizeof(unsigned long long) * (size_t)E;
 }
 
 int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
                   int T, int K, int E, hipStream_t st) {
-    bucket_kernel<<<1, BK_THREADS, bucket_lds_bytes(E), st>>>(counts, offsets, perm, inv, active, idx, T, K, E);
+    // one wavefront was measured slower for 16 pairs: its per-expert loops run 16x longer
+    bucket_kernel<1024><<<1, 1024, bucket_lds_bytes(E), st>>>(counts, offsets, perm, inv, active, idx, T, K, E);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
