@@ -12,7 +12,11 @@ Output: one JSON line (rank 0) with the whole-job throughput, the roofline of
 the dominant kernel (its HIP-event time on the stream it runs on) and the CPU
 oracle timed on a bounded sample on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_b1|prefill_4096_idot]
+    python bench.py [--steps K] [--warmup W] [--workload decode_b1|decode_b64|prefill_4096_idot]
+
+The default run (decode_b1) also measures, on the same resident bank, short
+runs of the 64-token EXACT layer and the 4096-token IDOT layer (int8 and bf16
+matrix-core forms) and reports them under "other_workloads".
 """
 from __future__ import annotations
 
@@ -43,6 +47,8 @@ def parse():
     ap.add_argument("--idot-bf16", action="store_true",
                     help="IDOT workloads: run the group dots on the bf16 matrix cores (same results)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="decode_b1 only: skip the short runs of the 64-token and 4096-token workloads")
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only copy a GIB-sized buffer 5 times (a plain copy of known size, for scaling the "
@@ -78,22 +84,44 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    L, I, E, K = synth.LATENT, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    L, I, E = synth.LATENT, synth.INTER, synth.N_EXPERTS
     seed_bank = synth.SEED_BASE + 1
-    wl_seed, T, bias_range, mode_name = synth.WORKLOADS[args.workload]
-    mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
-    form = k3g.IDOT_BF16 if (mode == k3g.IDOT and args.idot_bf16) else 0
-
     t0 = time.time()
     src = lambda e: synth.expert(seed_bank, e)  # noqa: E731
     bankt, bank = k3g.pack_bank(src, E, L, I)
+    print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
+
+    ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager)
+    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, src, *host)
+    if args.workload == "decode_b1" and not args.no_secondary:
+        # the other configurations on the same resident bank, shorter runs (not the headline)
+        others = []
+        for wl, steps, warm, bf16 in (("decode_b64", 20, 3, False), ("prefill_4096_idot", 10, 2, False),
+                                      ("prefill_4096_idot", 10, 2, True)):
+            r, _ = run_workload(ctx, wl, steps, warm, bf16)
+            others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
+                                             "decode", "roofline", "steps", "warmup")})
+        result["other_workloads"] = others
+    print(json.dumps(result), flush=True)
+
+
+def run_workload(ctx, workload, steps, warmup, idot_bf16):
+    """Measure one workload on the resident bank. Returns the result record and
+    what the CPU baseline needs (the same inputs)."""
+    torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
+    L, I, E, K = synth.LATENT, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    wl_seed, T, bias_range, mode_name = synth.WORKLOADS[workload]
+    mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
+    form = k3g.IDOT_BF16 if (mode == k3g.IDOT and idot_bf16) else 0
+
     W, b = synth.router(wl_seed, E, L, bias_range)
     Wd = torch.from_numpy(W).to(dev)
     bd = torch.from_numpy(b).to(dev)
     n_rot = N_ROT if T == 1 else 4
     xs_host = [synth.activations(wl_seed, T, L, key=r) for r in range(n_rot)]
     xs = [torch.from_numpy(x).to(dev) for x in xs_host]
-    print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
 
     # per input batch r: its own routing, workspaces and output, so that any
     # stage can be replayed over all batches
@@ -129,7 +157,7 @@ def main():
 
     # one HIP graph per input batch holding the whole step
     graphs = []
-    if not args.eager:
+    if not ctx["eager"]:
         for r in range(n_rot):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -143,17 +171,17 @@ def main():
         else:
             step(i % n_rot)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, host clock between two device syncs
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        run(args.warmup + i)
+    for i in range(steps):
+        run(warmup + i)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    ms_per_step = 1e3 * t_total / args.steps
+    ms_per_step = 1e3 * t_total / steps
 
     # per-kernel times: each stage replayed over every input batch inside one
     # graph, bracketed by HIP events on the stream it runs on; the average
@@ -179,12 +207,12 @@ def main():
     stage_ms = {name: time_stage(st, mode | form) for name, st in stages}
     # the same expert kernels with the nibbles decoded through the LDS byte-pair table
     lut_ms = {}
-    if mode == k3g.EXACT:
+    if mode == k3g.EXACT and T == 1:
         lut_ms = {name: time_stage(st, mode | k3g.DECODE_LUT) for name, st in stages if name in ("up", "down")}
     timing = (f"step: {len(graphs) and 'HIP graph per step' or 'eager'} replay; stages: HIP events around a graph "
               f"of {n_rot} launches of the stage, {reps} replays")
 
-    # distinct experts per step (decode: always top_k; prefill: counted from the routing)
+    # distinct experts per step (decode: always top_k; more tokens: counted from the routing)
     counts = None
     if T > 1:
         cnt = []
@@ -210,7 +238,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(up_gbs / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(args.workload, "moe_up"),
+        "traffic": measured_traffic(workload, "moe_up"),
         "algorithmic_bytes_per_launch": int(up_alg),
     }
     if mode == k3g.IDOT:
@@ -226,7 +254,7 @@ def main():
             "unit": "TFLOP/s",
             "ops": "int8 multiply-adds x 2" if not form else "bf16 multiply-adds x 2 (exact int8 values)",
             "frac": round(tops / peak, 4),
-            "traffic": measured_traffic(args.workload, "moe_up"),
+            "traffic": measured_traffic(workload, "moe_up"),
             "algorithmic_ops_per_launch": up_ops,
             "hbm_achieved_GBps": round(up_gbs, 1),
             "hbm_frac": round(up_gbs / HBM_PEAK_GBS, 4),
@@ -237,8 +265,8 @@ def main():
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -246,13 +274,13 @@ def main():
         "dtype": "f32" if mode == k3g.EXACT else "i8",
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": workload,
             "tokens_per_step": T,
             "experts": E, "top_k": K, "latent": L, "inter": I,
-            "mode": mode_name,
+            "mode": mode_name + ("+bf16-mfma" if form else ""),
             "distinct_experts_per_step": n_exp,
             "algorithmic_bytes_per_step": int(alg_bytes),
-            "seed_bank": seed_bank, "seed_workload": wl_seed,
+            "seed_bank": ctx["seed_bank"], "seed_workload": wl_seed,
         },
         "tokens_per_s": round(tok_s, 1),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
@@ -262,9 +290,11 @@ def main():
         "timing": timing,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode)
-    print(json.dumps(result), flush=True)
+    # release this workload's device memory before the next one
+    del graphs, ws, ws_r, idx, wts, ys, xs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result, (xs_host, W, b, alg_bytes, T, mode)
 
 
 def measured_traffic(workload, kernel):
@@ -312,8 +342,9 @@ def cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode):
     spent = 0.0
     tokens = 0
     xs_flat = np.concatenate(xs_host, 0)
-    while spent < args.cpu_seconds and done < xs_flat.shape[0]:
-        x = xs_flat[done:done + 1]
+    while spent < args.cpu_seconds:
+        i = done % xs_flat.shape[0]  # the bench's tokens, cycled until the budget is spent
+        x = xs_flat[i:i + 1]
         io, wo, _ = oracle.route(x, W, b, K)  # noqa: F841 (timed below with the layer)
         experts = {int(e): src(int(e)) for e in io.ravel()}   # generation is not timed
         t = time.perf_counter()
