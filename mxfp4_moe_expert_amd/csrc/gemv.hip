@@ -59,6 +59,7 @@ template <int NG>
 struct LaneCols {
     uint32_t pk[NG];  // byte offset of the lane's group i in a packed row
     uint32_t sc[NG];  // its index in a row of scale bytes
+    uint32_t sc2;     // NG = 2: even index of the lane's two scale bytes (one 16-bit load)
 };
 
 template <int NG>
@@ -71,6 +72,8 @@ __device__ inline LaneCols<NG> lane_cols(int lane, int ngrp) {
         c.pk[i] = (uint32_t)gc * 16u;
         c.sc[i] = (uint32_t)gc;
     }
+    const int g2 = lane * NG;
+    c.sc2 = (uint32_t)(g2 + 1 < ngrp ? g2 : (ngrp >= 2 ? ((ngrp - 2) & ~1) : 0));
     return c;
 }
 
@@ -89,13 +92,18 @@ __device__ inline MatRef mat_ref(const uint8_t *packed, const uint8_t *scales, i
     return m;
 }
 
-template <int NG>
+template <int NG, bool SC2 = false>
 __device__ inline void load_row(RowData<NG> &d, const MatRef &m, int r, const LaneCols<NG> &c) {
     const uint32_t op = (uint32_t)r * m.pitch_p, os = (uint32_t)r * m.pitch_s;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-        d.w[i] = buf_load16(m.p, c.pk[i], op);
-        d.s[i] = buf_load8(m.s, c.sc[i], os);
+    for (int i = 0; i < NG; ++i) d.w[i] = buf_load16(m.p, c.pk[i], op);
+    if constexpr (NG == 2 && SC2) {
+        const uint32_t v = buf_load_u16(m.s, c.sc2, os);
+        d.s[0] = v & 0xFFu;
+        d.s[NG - 1] = v >> 8;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) d.s[i] = buf_load8(m.s, c.sc[i], os);
     }
 }
 
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
 // NP pairs share each pass over the rows (their x in registers), so an expert
 // chosen by several tokens is streamed ceil(pairs / NP) times.
 // With perm == nullptr the call is one expert (bank expert 0) on token 0.
-template <int NG, bool LUT, int NP>
+template <int NG, bool LUT, int NP, bool SC2>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
     float *__restrict__ h, const float *__restrict__ x, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int latent, int inter,
@@ -253,8 +261,8 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
             RowData<NG> b1[PIPE], b3[PIPE];
 #pragma unroll
             for (int st = 0; st < PIPE; ++st) {
-                load_row<NG>(b1[st], m1, R(r0 + st), cols);
-                load_row<NG>(b3[st], m3, R(r0 + st), cols);
+                load_row<NG, SC2>(b1[st], m1, R(r0 + st), cols);
+                load_row<NG, SC2>(b3[st], m3, R(r0 + st), cols);
             }
             float gv[NP], uv[NP];  // lane k holds row k of the current block of 64
 #pragma unroll
@@ -279,8 +287,8 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
                                 if (lane <= k && pos + q < p1) h[(size_t)ps[q] * inter + rr - k + lane] = situ(gv[q], uv[q]);
                         }
                     }
-                    load_row<NG>(b1[st], m1, R(r + st + PIPE), cols);
-                    load_row<NG>(b3[st], m3, R(r + st + PIPE), cols);
+                    load_row<NG, SC2>(b1[st], m1, R(r + st + PIPE), cols);
+                    load_row<NG, SC2>(b3[st], m3, R(r + st + PIPE), cols);
                 }
             }
         }
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
 // Grouped down-projection: ypair[pos][r] = w2[r] . h[pos] for every pair of
 // the slot's expert. Same items as the up kernel, over latent rows; NP pairs
 // share each pass over the rows.
-template <int NG, bool LUT, int NP>
+template <int NG, bool LUT, int NP, bool SC2>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kernel(
     float *__restrict__ ypair, const float *__restrict__ h, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int latent, int inter,
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kerne
             }
             RowData<NG> buf[PIPE];
 #pragma unroll
-            for (int st = 0; st < PIPE; ++st) load_row<NG>(buf[st], m2, R(r0 + st), cols);
+            for (int st = 0; st < PIPE; ++st) load_row<NG, SC2>(buf[st], m2, R(r0 + st), cols);
             float acc[NP];  // lane k holds row k of the current block of 64
 #pragma unroll
             for (int q = 0; q < NP; ++q) acc[q] = 0.f;
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kerne
                                 if (lane <= k && pos + q < p1) ypair[(size_t)ps[q] * latent + rr - k + lane] = acc[q];
                         }
                     }
-                    load_row<NG>(buf[st], m2, R(r + st + PIPE), cols);
+                    load_row<NG, SC2>(buf[st], m2, R(r + st + PIPE), cols);
                 }
             }
         }
@@ -448,8 +456,18 @@ int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int
     const int rpi = rows_per_item(max_slots, inter, multi ? K3G_MULTI_ITEMS : K3G_ITEMS_TARGET);
     const int items = max_slots * ((inter + rpi - 1) / rpi);
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
-#define K3G_UP(NG_, LUT_, NP_) \
-    moe_up_exact_kernel<NG_, LUT_, NP_><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm, top_k, latent, inter, max_slots, rpi)
+    // a lane's two scale bytes as one 16-bit load when every scale row starts at an even address
+    const bool sc2 = ng == 2 && (latent / kGroup) % 2 == 0 && bank.stride % 2 == 0 &&
+                     ((uintptr_t)bank.base + bank.off[W1S]) % 2 == 0 && ((uintptr_t)bank.base + bank.off[W3S]) % 2 == 0;
+#define K3G_UP(NG_, LUT_, NP_)                                                                                     \
+    do {                                                                                                           \
+        if (NG_ == 2 && sc2)                                                                                       \
+            moe_up_exact_kernel<NG_, LUT_, NP_, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm,   \
+                                                                             top_k, latent, inter, max_slots, rpi); \
+        else                                                                                                       \
+            moe_up_exact_kernel<NG_, LUT_, NP_, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm,  \
+                                                                              top_k, latent, inter, max_slots, rpi); \
+    } while (0)
     switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
         case 4: K3G_UP(1, false, 1); break;
         case 5: K3G_UP(1, true, 1); break;
@@ -475,8 +493,17 @@ int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, con
     const int rpi = rows_per_item(max_slots, latent, multi ? K3G_MULTI_ITEMS : K3G_ITEMS_TARGET);
     const int items = max_slots * ((latent + rpi - 1) / rpi);
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
-#define K3G_DN(NG_, LUT_, NP_) \
-    moe_down_exact_kernel<NG_, LUT_, NP_><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets, perm, latent, inter, max_slots, rpi)
+    const bool sc2 = ng == 2 && (inter / kGroup) % 2 == 0 && bank.stride % 2 == 0 &&
+                     ((uintptr_t)bank.base + bank.off[W2S]) % 2 == 0;
+#define K3G_DN(NG_, LUT_, NP_)                                                                                      \
+    do {                                                                                                            \
+        if (NG_ == 2 && sc2)                                                                                        \
+            moe_down_exact_kernel<NG_, LUT_, NP_, true><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets,    \
+                                                                               perm, latent, inter, max_slots, rpi); \
+        else                                                                                                        \
+            moe_down_exact_kernel<NG_, LUT_, NP_, false><<<grid, block, 0, st>>>(ypair, h, bank, active, offsets,   \
+                                                                                perm, latent, inter, max_slots, rpi); \
+    } while (0)
     switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
         case 4: K3G_DN(1, false, 1); break;
         case 5: K3G_DN(1, true, 1); break;

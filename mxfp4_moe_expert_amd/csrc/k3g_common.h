@@ -165,4 +165,8 @@ __device__ inline uint32_t buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 
+__device__ inline uint32_t buf_load_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
 }  // namespace k3g
