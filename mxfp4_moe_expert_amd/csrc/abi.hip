@@ -91,9 +91,16 @@ inline bool mode_ok(int mode) {
 }
 inline bool lut_of(int mode) { return (mode & K3G_DECODE_LUT) != 0; }
 // The IDOT kernels stage a row's scale bytes four groups at a time as aligned
-// dwords: both widths must be multiples of 128 columns.
-inline int idot_shape_ok(int mode, int latent, int inter) {
-    return (mode & 0xFF) != K3G_IDOT || (latent % 128 == 0 && inter % 128 == 0) ? K3G_OK : K3G_EUNSUPPORTED;
+// dwords: both widths must be multiples of 128 columns. The bf16 form addresses
+// a row of its activations by a 32-bit byte offset: T rows of x and T*top_k
+// rows of h, 2 bytes per element.
+inline int idot_shape_ok(int mode, int latent, int inter, int n_tokens = 1, int top_k = 1) {
+    if ((mode & 0xFF) != K3G_IDOT) return K3G_OK;
+    if (latent % 128 || inter % 128) return K3G_EUNSUPPORTED;
+    const int64_t P = (int64_t)n_tokens * top_k;
+    if (P * inter * 2 >= ((int64_t)1 << 32) || (int64_t)n_tokens * latent * 2 >= ((int64_t)1 << 32))
+        return K3G_EUNSUPPORTED;
+    return K3G_OK;
 }
 inline bool bf16_of(int mode) { return (mode & K3G_IDOT_BF16) != 0; }
 
@@ -349,7 +356,7 @@ static int layer_prepare(k3g_ws_layout *L, const float *y, const float *x, const
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
         return K3G_EALIGN;
     if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
-    K3G_TRY(idot_shape_ok(mode, latent, inter));
+    K3G_TRY(idot_shape_ok(mode, latent, inter, n_tokens, top_k));
     for (int i = 0; i < 6; i += 2)
         if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
     for (int i = 1; i < 6; i += 2)
@@ -436,7 +443,7 @@ extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_
     if (ws_bytes < L.total) return K3G_ENOSPACE;
     if (!aligned(x, 16) || !aligned(out, 4) || !aligned(ws, 256) || !aligned(w->w_router, 16)) return K3G_EALIGN;
     if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
-    K3G_TRY(idot_shape_ok(mode, latent, inter));
+    K3G_TRY(idot_shape_ok(mode, latent, inter, T, top_k));
     for (int i = 0; i < 6; i += 2)
         if (!aligned(bank->base + bank->off[i], 16) || bank->stride % 16) return K3G_EALIGN;
     for (int i = 1; i < 6; i += 2)

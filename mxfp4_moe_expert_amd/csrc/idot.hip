@@ -173,16 +173,11 @@ int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed,
 // 32*IX_NT tokens. Each wavefront owns 32 weight rows (operand A) and meets
 // every token tile of the chunk (operand B, 32 tokens); lane l of a result
 // holds token l%32 and rows 8*(v/4) + 4*(l/32) + v%4.
-//  - int8 form: one v_mfma_i32_32x32x32_i8 per group and tile on the int8
-//    activations and the doubled e2m1 values gives the int32 group dots I;
-//    the epilogue adds float(I) * (s_x[token][g] * 2^(s_rg - 128)).
-//  - bf16 form: two v_mfma_f32_32x32x16_bf16 on the same int8 values widened
-//    to bf16 and the e2m1 values with 2^(s_rg-127) folded in by the FP4
-//    convert. Every product and partial sum is an integer (< 2^16) times
-//    2^(s_rg-128), exact in fp32, so the result is I * 2^(s_rg-128) exactly
-//    and the epilogue is one fma with s_x; the sums equal the int8 form's bit
-//    for bit.
-// A scale byte of 255 contributes nothing.
+// One v_mfma_i32_32x32x32_i8 per group and tile on the int8 activations and
+// the doubled e2m1 values gives the int32 group dots I; the epilogue adds
+// float(I) * (s_x[token][g] * 2^(s_rg - 128)). A scale byte of 255 contributes
+// nothing. (The bf16 matrix-core form of the same products, whose epilogue is
+// one fma per result, lives in idot_bf16.hip.)
 // UP: a wavefront's 32 rows are 16 rows of w1 (result slots 0..7) and the same
 //     16 rows of w3 (slots 8..15): g and u of a row meet in one lane and
 //     h = SiTU(g, u) goes to h[pos][row].
@@ -202,19 +197,7 @@ int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed,
 constexpr int IX_WAVES = 8;
 constexpr int IX_NT = 3;     // token tiles (of 32) per chunk
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// 4 packed bytes (8 e2m1 codes, column order) -> 8 bf16 scaled by 2^(e-127),
-// e = the exponent field of `scale`.
-__device__ inline bf16x8_t fp4x8_bf16(uint32_t w, float scale) {
-    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
 
 // Written as inline assembly on purpose: the compiler would otherwise wait for
 // every outstanding global-to-LDS load before the next LDS read, whatever its
@@ -233,15 +216,14 @@ __device__ inline void lds_load4(const void *src, void *lds) {
                      : "m0", "memory");
 }
 
-template <bool UP, bool BF16>
+template <bool UP>
 __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
-    float *__restrict__ out, const int8_t *__restrict__ aq, const uint16_t *__restrict__ aqb,
-    const float *__restrict__ as, BankDev bank, const int32_t *__restrict__ active,
+    float *__restrict__ out, const int8_t *__restrict__ aq, const float *__restrict__ as, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int n_in, int n_out,
     int max_slots) {
     constexpr int GB = 4;                     // groups per block
-    constexpr int GBYTES = BF16 ? 64 : 32;    // token bytes per group
-    constexpr int TCHD = GB * GBYTES / 16;    // token chunks of a block: 8 (int8) or 16 (bf16)
+    constexpr int GBYTES = 32;                // token bytes per group
+    constexpr int TCHD = GB * GBYTES / 16;    // token chunks of a block: 8
     constexpr int TCH = TCHD + 1;             // token row in LDS: the chunks + pad
     constexpr int TPITCH = 16 * TCH;
     constexpr int WCH = GB + 1;               // weight row in LDS: GB chunks + pad
@@ -255,7 +237,7 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
     __shared__ __attribute__((aligned(16))) char w_lds[2][IX_WAVES][WLD * 1024];
     __shared__ __attribute__((aligned(16))) float sx_lds[2][GB][NTOK];
     __shared__ __attribute__((aligned(16))) uint32_t sc_lds[2][IX_WAVES][64];   // a row's 4 scale bytes (x2)
-    __shared__ __attribute__((aligned(16))) float ws_lds[BF16 ? 1 : IX_WAVES][GB][32];
+    __shared__ __attribute__((aligned(16))) float ws_lds[IX_WAVES][GB][32];
     __shared__ int row_lds[NTOK];
     const int tid = threadIdx.x, lane = tid & 63, wl = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -310,8 +292,8 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
             }
             __syncthreads();
             // token loads of this lane: slot idx = 64*(wl + 8i) + lane -> (token, chunk)
-            const char *tbase = BF16 ? (const char *)aqb : (const char *)aq;
-            const uint32_t trow = (uint32_t)n_in * (BF16 ? 2u : 1u);
+            const char *tbase = (const char *)aq;
+            const uint32_t trow = (uint32_t)n_in;
             uint32_t tsrc[TLD];
             int tch[TLD];
 #pragma unroll
@@ -347,7 +329,7 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
             // int8 form: 2^(s-128) of the block's groups for the rows' epilogues, from the
             // staged scale bytes into this wavefront's own table (so no workgroup barrier)
             auto row_scales = [&](int buf) {
-                if constexpr (!BF16) {
+                {
                     if (half == 0) {
                         const uint32_t sw = sc_lds[buf][wl][col];
 #pragma unroll
@@ -379,30 +361,7 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
                         return *(const int4_t *)&tok_lds[buf][(32 * tt + col) * TPITCH + 16 * c];
                     };
                     auto sx_of = [&](int tt) { return sx_lds[buf][j][32 * tt + col]; };
-                    if constexpr (BF16) {
-                        const uint32_t sbyte = (sc_lds[buf][wl][col] >> (8 * j)) & 0xFFu;
-                        const bool skip = sbyte == 255u;
-                        const float scale = __builtin_bit_cast(float, (skip ? 127u : sbyte) << 23);
-                        const bf16x8_t a0 = fp4x8_bf16(skip ? 0u : wlo, scale);
-                        const bf16x8_t a1 = fp4x8_bf16(skip ? 0u : whi, scale);
-                        auto mm = [&](int tt) {
-                            const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, tok_frag(tt, 4 * j + 2 * half));
-                            const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, tok_frag(tt, 4 * j + 2 * half + 1));
-                            const f32x16_t z = {};
-                            const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, z, 0, 0, 0);
-                            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, d, 0, 0, 0);
-                        };
-                        f32x16_t cur = mm(0);
-#pragma unroll
-                        for (int tt = 0; tt < NTL; ++tt) {
-                            f32x16_t nxt;
-                            if (tt + 1 < NTL) nxt = mm(tt + 1);
-                            const float sx = sx_of(tt);
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) acc[tt][v] = __builtin_fmaf(cur[v], sx, acc[tt][v]);
-                            if (tt + 1 < NTL) cur = nxt;
-                        }
-                    } else {
+                    {
                         const int4_t a = decode_b(make_uint2(wlo, whi));
                         int16_t_v cur = mfma_group(a, tok_frag(0, 2 * j + half));
                         // row scales of result slots 4q..4q+3: rows 8q + 4*half + 0..3
@@ -470,31 +429,29 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
     }
 }
 
+int launch_idot_bf16(bool up, float *out, const uint16_t *aqb, const float *as, const BankDev &bank,
+                     const int32_t *active, const int32_t *offsets, const int32_t *perm, int top_k, int n_in,
+                     int n_out, int max_slots, hipStream_t st);
+
 int launch_moe_up_idot(float *h, const int8_t *xq, const uint16_t *xqb, const float *xs, const BankDev &bank,
                        const int32_t *active, const int32_t *offsets, const int32_t *perm, int top_k, int latent,
                        int inter, int max_slots, hipStream_t st) {
+    if (xqb) return launch_idot_bf16(true, h, xqb, xs, bank, active, offsets, perm, top_k, latent, inter, max_slots, st);
     const int items = max_slots * ((inter + 16 * IX_WAVES - 1) / (16 * IX_WAVES));
     const int blocks = items < 16384 ? items : 16384;
-    if (xqb)
-        moe_idot_kernel<true, true><<<blocks, IX_WAVES * 64, 0, st>>>(h, xq, xqb, xs, bank, active, offsets, perm,
-                                                                      top_k, latent, inter, max_slots);
-    else
-        moe_idot_kernel<true, false><<<blocks, IX_WAVES * 64, 0, st>>>(h, xq, xqb, xs, bank, active, offsets, perm,
-                                                                       top_k, latent, inter, max_slots);
+    moe_idot_kernel<true><<<blocks, IX_WAVES * 64, 0, st>>>(h, xq, xs, bank, active, offsets, perm, top_k, latent,
+                                                            inter, max_slots);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
 int launch_moe_down_idot(float *ypair, const int8_t *hq, const uint16_t *hqb, const float *hs, const BankDev &bank,
                          const int32_t *active, const int32_t *offsets, const int32_t *perm, int latent, int inter,
                          int max_slots, hipStream_t st) {
+    if (hqb) return launch_idot_bf16(false, ypair, hqb, hs, bank, active, offsets, perm, 1, inter, latent, max_slots, st);
     const int items = max_slots * ((latent + 32 * IX_WAVES - 1) / (32 * IX_WAVES));
     const int blocks = items < 16384 ? items : 16384;
-    if (hqb)
-        moe_idot_kernel<false, true><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, hq, hqb, hs, bank, active, offsets,
-                                                                       perm, 1, inter, latent, max_slots);
-    else
-        moe_idot_kernel<false, false><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, hq, hqb, hs, bank, active, offsets,
-                                                                        perm, 1, inter, latent, max_slots);
+    moe_idot_kernel<false><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, hq, hs, bank, active, offsets, perm, 1, inter,
+                                                             latent, max_slots);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
