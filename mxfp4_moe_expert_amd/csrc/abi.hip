@@ -12,7 +12,7 @@ int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *
                 hipStream_t st);
 int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
                         const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
-                        hipStream_t st);
+                        const Route1 &rt, hipStream_t st);
 int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
                           const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
                           bool multi_pairs, bool lut, hipStream_t st);
@@ -315,7 +315,8 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
     float *h = (float *)(w + L.h);
     hipStream_t st = S(stream);
     if (base_mode(mode) == K3G_EXACT) {
-        K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut_of(mode), st));
+        K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut_of(mode), Route1{},
+                                    st));
         return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, false, lut_of(mode), st);
     }
     int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
@@ -383,16 +384,20 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
     const int P = n_tokens * top_k;
     const int max_slots = P < E ? P : E;
     const BankDev b = bank_dev(*bank);
+    // One token in EXACT mode: the up-projection ranks the route entries itself
+    // and writes the bucket, so the bucket stage launches nothing.
+    const bool route1 = n_tokens == 1 && base_mode(mode) == K3G_EXACT;
+    const Route1 r1 = route1 ? Route1{idx, counts, offsets, perm, inv, active, E} : Route1{};
     switch (stage) {
         case K3G_STAGE_BUCKET:
-            return launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
+            return route1 ? K3G_OK : launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
         case K3G_STAGE_QUANT_X:
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, xqb, st) : K3G_OK;
         case K3G_STAGE_UP:
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_up_idot(h, xq, xqb, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
                        : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P,
-                                             lut_of(mode), st);
+                                             lut_of(mode), r1, st);
         case K3G_STAGE_QUANT_H:
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, hqb, st) : K3G_OK;
         case K3G_STAGE_DOWN:

@@ -122,7 +122,11 @@ __device__ inline float row_partial(const RowData<NG> &d, const uint32_t *lut, u
             (void)lut;
             (void)lane_off;
         }
-        p += ((valid >> i) & 1u) ? apply_scale(sub, d.s[i]) : 0.0f;
+        // a group past the row's end is dropped by masking its bits (+0.0): a
+        // select here would be turned into a branch around the whole group,
+        // and the branches would cost the loads of the rows in flight
+        const uint32_t keep = 0u - ((valid >> i) & 1u);
+        p += __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, apply_scale(sub, d.s[i])) & keep);
     }
     return p;
 }
@@ -185,9 +189,15 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
         auto R = [&](int r) { return min(r, r1 - 1); };
         RowData<NG> buf[K3G_PIPE];
 #pragma unroll
-        for (int st = 0; st < K3G_PIPE; ++st) load_row<NG>(buf[st], mat, R(r0 + st), cols);
+        for (int st = 0; st < K3G_PIPE; ++st) {
+            load_row<NG>(buf[st], mat, R(r0 + st), cols);
+            __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (see below)
+        }
         float acc = 0.f;  // lane k holds row (r - r0) % 64 == k until its block of 64 is stored
-        for (int r = r0; r < r1; r += K3G_PIPE) {
+        // every work item has at least one row: a do-while keeps the loads of x
+        // and of the first rows in one block (no preheader to sink x into)
+        int r = r0;
+        do {
 #pragma unroll
             for (int st = 0; st < K3G_PIPE; ++st) {
                 const int rr = r + st;
@@ -201,8 +211,69 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
                 }
                 load_row<NG>(buf[st], mat, R(rr + K3G_PIPE), cols);
             }
+            r += K3G_PIPE;
+        } while (r < r1);
+    }
+}
+
+// ---- one token: its route entries in the bucket's order -------------------------
+// With a single token the bucket (pairs sorted by expert, then token) is a
+// small permutation of the K route entries, which a wavefront can rank on its
+// own; the decode up-projection does that instead of waiting for a separate
+// bucket launch. Lane k holds entry k: its expert, whether the id is in range,
+// its position among the sorted pairs, whether it is the first entry of its
+// expert (duplicates share one slot), the slot of its expert (rank among the
+// distinct experts) and the number of entries of its expert.
+struct Route1Lane {
+    int e, pos, slot, cnt;
+    bool valid, first;
+    uint64_t firsts;  // ballot of `first`: popcount = number of slots
+};
+
+__device__ inline Route1Lane route1_lane(const int32_t *idx, int K, int E, int lane) {
+    Route1Lane r;
+    r.e = lane < K ? idx[lane] : -1;
+    r.valid = lane < K && (unsigned)r.e < (unsigned)E;
+    r.pos = 0;
+    r.cnt = 0;
+    r.first = r.valid;
+    for (int j = 0; j < K; ++j) {  // uniform loop: entry j's expert read from lane j
+        const int ej = __builtin_amdgcn_readlane(r.e, j);
+        if ((unsigned)ej < (unsigned)E) {
+            r.pos += (ej < r.e || (ej == r.e && j < lane)) ? 1 : 0;
+            r.cnt += ej == r.e ? 1 : 0;
+            r.first = r.first && !(ej == r.e && j < lane);
         }
     }
+    r.firsts = __ballot(r.first);
+    r.slot = 0;
+    for (int j = 0; j < K; ++j) {
+        const int ej = __builtin_amdgcn_readlane(r.e, j);
+        if ((r.firsts >> j) & 1ull) r.slot += ej < r.e ? 1 : 0;
+    }
+    return r;
+}
+
+// Workgroup 0's wavefront 0 writes the bucket as the bucket kernel would.
+__device__ inline void route1_write_bucket(const Route1 &rt, const Route1Lane &r, int K, int lane) {
+    const int E = rt.n_experts;
+    for (int e0 = 0; e0 <= E; e0 += kWave) {
+        const int e = e0 + lane;
+        int below = 0, c = 0;
+        for (int j = 0; j < K; ++j) {
+            const int ej = __builtin_amdgcn_readlane(r.e, j);
+            if ((unsigned)ej < (unsigned)E) {
+                below += ej < e ? 1 : 0;
+                c += ej == e ? 1 : 0;
+            }
+        }
+        if (e < E) rt.counts[e] = c;
+        if (e <= E) rt.offsets[e] = below;
+    }
+    if (r.valid) rt.perm[r.pos] = lane;
+    if (lane < K) rt.inv[lane] = r.valid ? r.pos : -1;
+    if (r.first) rt.active[1 + r.slot] = r.e;
+    if (lane == 0) rt.active[0] = __popcll(r.firsts);
 }
 
 // Grouped SiTU-GLU up-projection. Work item = (slot, run of rpi rows); slot i
@@ -216,7 +287,7 @@ template <int NG, bool LUT, int NP, bool SC2>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
     float *__restrict__ h, const float *__restrict__ x, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int latent, int inter,
-    int max_slots, int rpi) {
+    int max_slots, int rpi, Route1 rt) {
     constexpr int PIPE = NP > 1 ? 2 : K3G_PIPE;  // rows in flight: two pairs need the registers
     uint32_t *lut = nullptr;
     if constexpr (LUT) {
@@ -233,16 +304,31 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
     const uint32_t valid = valid_groups<NG>(lane, ngrp);
     const LaneCols<NG> cols = lane_cols<NG>(lane, ngrp);
     const int chunks = (inter + rpi - 1) / rpi;
-    const int n_act = perm ? active[0] : 1;
+    // one token without a bucket: rank the route entries here (rt.idx set)
+    Route1Lane r1 = {};
+    if (rt.idx) {
+        r1 = route1_lane(rt.idx, top_k, rt.n_experts, lane);
+        if (blockIdx.x == 0 && wave == 0) route1_write_bucket(rt, r1, top_k, lane);
+    }
+    const int n_act = rt.idx ? __popcll(r1.firsts) : (perm ? active[0] : 1);
     const int n_items = max_slots * chunks;
     float xr[NP][NG * kGroup];
     for (int item = blockIdx.x * waves + wave; item < n_items; item += gridDim.x * waves) {
         const int slot = item / chunks;
         if (slot >= n_act) continue;
         const int chunk = item - slot * chunks;
-        const int e = perm ? active[1 + slot] : 0;
-        const int p0 = perm ? offsets[e] : 0;
-        const int p1 = perm ? offsets[e + 1] : 1;
+        int e, p0, p1;
+        if (rt.idx) {  // the lane holding the first entry of this slot's expert
+            const uint64_t m = __ballot(r1.first && r1.slot == slot);
+            const int L = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+            e = __builtin_amdgcn_readlane(r1.e, L);
+            p0 = __builtin_amdgcn_readlane(r1.pos, L);
+            p1 = p0 + __builtin_amdgcn_readlane(r1.cnt, L);
+        } else {
+            e = perm ? active[1 + slot] : 0;
+            p0 = perm ? offsets[e] : 0;
+            p1 = perm ? offsets[e + 1] : 1;
+        }
         const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
         const MatRef m1 = mat_ref(eb + bank.off[W1P], eb + bank.off[W1S], inter, latent);
         const MatRef m3 = mat_ref(eb + bank.off[W3P], eb + bank.off[W3S], inter, latent);
@@ -255,19 +341,27 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
                 ps[q] = min(pos + q, p1 - 1);
-                const int t = perm ? perm[ps[q]] / top_k : 0;
+                const int t = (perm && !rt.idx) ? perm[ps[q]] / top_k : 0;  // one token: token 0
                 load_x<NG>(xr[q], x + (size_t)t * latent, lane, ngrp);
             }
+            __builtin_amdgcn_sched_barrier(0);  // x before the rows: the oldest loads
             RowData<NG> b1[PIPE], b3[PIPE];
 #pragma unroll
             for (int st = 0; st < PIPE; ++st) {
                 load_row<NG, SC2>(b1[st], m1, R(r0 + st), cols);
                 load_row<NG, SC2>(b3[st], m3, R(r0 + st), cols);
+                // The rows go out in the order the loop below will refill them,
+                // so that on every pass the row being summed is the oldest load
+                // and the compiler's wait leaves the later rows in flight.
+                __builtin_amdgcn_sched_barrier(0);
             }
             float gv[NP], uv[NP];  // lane k holds row k of the current block of 64
 #pragma unroll
             for (int q = 0; q < NP; ++q) gv[q] = uv[q] = 0.f;
-            for (int r = r0; r < r1; r += PIPE) {
+            // every work item has at least one row: a do-while keeps the loads of x
+            // and of the first rows in one block (no preheader to sink x into)
+            int r = r0;
+            do {
 #pragma unroll
                 for (int st = 0; st < PIPE; ++st) {
                     const int rr = r + st;
@@ -290,7 +384,8 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_up_exact_kernel(
                     load_row<NG, SC2>(b1[st], m1, R(r + st + PIPE), cols);
                     load_row<NG, SC2>(b3[st], m3, R(r + st + PIPE), cols);
                 }
-            }
+                r += PIPE;
+            } while (r < r1);
         }
     }
 }
@@ -341,13 +436,20 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kerne
                 ps[q] = min(pos + q, p1 - 1);
                 load_x<NG>(xr[q], h + (size_t)ps[q] * inter, lane, ngrp);
             }
+            __builtin_amdgcn_sched_barrier(0);  // h before the rows: the oldest loads
             RowData<NG> buf[PIPE];
 #pragma unroll
-            for (int st = 0; st < PIPE; ++st) load_row<NG, SC2>(buf[st], m2, R(r0 + st), cols);
+            for (int st = 0; st < PIPE; ++st) {
+                load_row<NG, SC2>(buf[st], m2, R(r0 + st), cols);
+                __builtin_amdgcn_sched_barrier(0);  // the loop's load order
+            }
             float acc[NP];  // lane k holds row k of the current block of 64
 #pragma unroll
             for (int q = 0; q < NP; ++q) acc[q] = 0.f;
-            for (int r = r0; r < r1; r += PIPE) {
+            // every work item has at least one row: a do-while keeps the loads of x
+            // and of the first rows in one block (no preheader to sink x into)
+            int r = r0;
+            do {
 #pragma unroll
                 for (int st = 0; st < PIPE; ++st) {
                     const int rr = r + st;
@@ -366,7 +468,8 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void moe_down_exact_kerne
                     }
                     load_row<NG, SC2>(buf[st], m2, R(r + st + PIPE), cols);
                 }
-            }
+                r += PIPE;
+            } while (r < r1);
         }
     }
 }
@@ -450,7 +553,7 @@ static int rows_per_item(int max_slots, int rows, int target) {
 // (more slots share the chip).
 int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
                         const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
-                        hipStream_t st) {
+                        const Route1 &rt, hipStream_t st) {
     const int ng = pick_ng(latent / kGroup);
     const bool multi = n_pairs > top_k && ng <= 2;
     const int rpi = rows_per_item(max_slots, inter, multi ? K3G_MULTI_ITEMS : K3G_ITEMS_TARGET);
@@ -463,10 +566,10 @@ int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int
     do {                                                                                                           \
         if (NG_ == 2 && sc2)                                                                                       \
             moe_up_exact_kernel<NG_, LUT_, NP_, true><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm,   \
-                                                                             top_k, latent, inter, max_slots, rpi); \
+                                                                             top_k, latent, inter, max_slots, rpi, rt); \
         else                                                                                                       \
             moe_up_exact_kernel<NG_, LUT_, NP_, false><<<grid, block, 0, st>>>(h, x, bank, active, offsets, perm,  \
-                                                                              top_k, latent, inter, max_slots, rpi); \
+                                                                              top_k, latent, inter, max_slots, rpi, rt); \
     } while (0)
     switch (ng * 4 + (multi ? 2 : 0) + (lut ? 1 : 0)) {
         case 4: K3G_UP(1, false, 1); break;

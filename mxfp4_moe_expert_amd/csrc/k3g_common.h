@@ -33,6 +33,15 @@ struct BankDev {
 
 enum { W1P = 0, W1S = 1, W3P = 2, W3S = 3, W2P = 4, W2S = 5 };
 
+// One token's route entries handed to the decode up-projection, which ranks
+// them in the bucket's order itself and writes the bucket from workgroup 0
+// (idx null: the bucket was built by its own kernel).
+struct Route1 {
+    const int32_t *idx;                                // the token's K route entries
+    int32_t *counts, *offsets, *perm, *inv, *active;  // the bucket's arrays
+    int n_experts;
+};
+
 // Value of an e2m1 code from its bit fields: sign bit 3, exponent bits 2..1
 // (bias 1), mantissa bit 0; exponent 0 is subnormal (0 or 0.5).
 __host__ __device__ constexpr float e2m1_value(unsigned c) {
