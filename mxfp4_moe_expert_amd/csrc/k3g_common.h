@@ -145,11 +145,37 @@ __device__ inline double wave_sum_f64(double v) {
     return v;
 }
 
+// e^x to about 2 ulp: v_exp_f32 (2^t, 1 ulp) at t = x*log2(e) rounded, times
+// 1 + r*ln(2) for the part r of x*log2(e) that the rounding dropped (|r| is
+// at most 2^-17 where the result is finite, so the factor is exact enough).
+__device__ inline float exp_fast(float x) {
+    constexpr float kL2E = 1.44269502f;        // log2(e) rounded to fp32
+    constexpr float kL2E_LO = 1.92596299e-8f;  // log2(e) - kL2E
+    const float t = x * kL2E;
+    const float r = __builtin_fmaf(x, kL2E_LO, __builtin_fmaf(x, kL2E, -t));
+    return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(r, 0.693147182f, 1.0f);
+}
+
+// tanh(y): below |y| = 0.3 the odd Taylor series through y^9 (the next term
+// is under 6e-8 of the value); above, 1 - 2/(e^{2|y|} + 1) with y's sign
+// (v_rcp_f32, 1 ulp; the subtraction loses under 2 bits at |y| = 0.3).
+__device__ inline float tanh_fast(float y) {
+    const float a = __builtin_fabsf(y);
+    const float s = y * y;
+    float p = __builtin_fmaf(s, 62.0f / 2835.0f, -17.0f / 315.0f);
+    p = __builtin_fmaf(s, p, 2.0f / 15.0f);
+    p = __builtin_fmaf(s, p, -1.0f / 3.0f);
+    const float small = __builtin_fmaf(y * s, p, y);
+    const float big = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(exp_fast(2.0f * a) + 1.0f), 1.0f);
+    return a < 0.3f ? small : __builtin_copysignf(big, y);
+}
+
 // SiTU-GLU ("Kimi K3 engine (c/kimi_k3.c)", "Architecture notes"):
-// 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25), in fp32.
+// 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25), in fp32 (a few ulp: exp and the
+// reciprocal through the hardware approximations above; u/25 as u * 0.04).
 __device__ inline float situ(float g, float u) {
-    const float sig = 1.0f / (1.0f + expf(-g));
-    return 4.0f * tanhf(g * 0.25f) * sig * (25.0f * tanhf(u / 25.0f));
+    const float sig = __builtin_amdgcn_rcpf(1.0f + exp_fast(-g));
+    return 4.0f * tanh_fast(g * 0.25f) * sig * (25.0f * tanh_fast(u * 0.04f));
 }
 
 __device__ inline uint4 load16(const uint8_t *p) { return *(const uint4 *)p; }
