@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot"])
     ap.add_argument("--idot-bf16", action="store_true",
                     help="IDOT workloads: run the group dots on the bf16 matrix cores (same results)")
+    ap.add_argument("--mfma-decode", action="store_true",
+                    help="one-token EXACT workloads: the expert products on the FP4 matrix cores (x and h as e2m1 "
+                         "pieces) instead of the vector kernels (same bound)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="decode_b1 only: skip the short runs of the 64-token and 4096-token workloads")
@@ -92,7 +95,7 @@ def main():
     print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
 
     ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager)
-    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16)
+    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16, args.mfma_decode)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, src, *host)
     if args.workload == "decode_b1" and not args.no_secondary:
@@ -107,7 +110,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_workload(ctx, workload, steps, warmup, idot_bf16):
+def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False):
     """Measure one workload on the resident bank. Returns the result record and
     what the CPU baseline needs (the same inputs)."""
     torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
@@ -115,6 +118,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16):
     wl_seed, T, bias_range, mode_name = synth.WORKLOADS[workload]
     mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
     form = k3g.IDOT_BF16 if (mode == k3g.IDOT and idot_bf16) else 0
+    if mode == k3g.EXACT and T == 1 and mfma_decode:
+        form = k3g.DECODE_MFMA
 
     W, b = synth.router(wl_seed, E, L, bias_range)
     Wd = torch.from_numpy(W).to(dev)
@@ -132,19 +137,26 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16):
     sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=mode | form)
     ws = [k3g.workspace(k3g.OP_MOE_LAYER, sh) for _ in range(n_rot)]
 
+    # one token in EXACT mode on the FP4 matrix cores: QUANT_X splits x into pieces
+    f4 = form == k3g.DECODE_MFMA
     stages = [("route", None), ("bucket", k3g.STAGE_BUCKET)]
-    if mode == k3g.IDOT:
+    if mode == k3g.IDOT or f4:
         stages.append(("quant_x", k3g.STAGE_QUANT_X))
     stages.append(("up", k3g.STAGE_UP))
-    if mode == k3g.IDOT:
+    if mode == k3g.IDOT or f4:
         stages.append(("quant_h", k3g.STAGE_QUANT_H))
     stages += [("down", k3g.STAGE_DOWN), ("combine", k3g.STAGE_COMBINE)]
+
+    ws_by_mode = {mode | form: ws}
 
     def stage(r, st, m=mode | form):
         if st is None:
             k3g.k3g_moe_route(idx[r], wts[r], xs[r], Wd, bd, K, ws_r[r])
         else:
-            k3g.k3g_moe_layer_stage(st, ys[r], xs[r], idx[r], wts[r], bank, m, ws[r])
+            if m not in ws_by_mode:  # another decode form: a workspace of its own size
+                shm = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=m)
+                ws_by_mode[m] = [k3g.workspace(k3g.OP_MOE_LAYER, shm) for _ in range(n_rot)]
+            k3g.k3g_moe_layer_stage(st, ys[r], xs[r], idx[r], wts[r], bank, m, ws_by_mode[m][r])
 
     def step(r):
         for _, st in stages:
@@ -190,6 +202,12 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16):
     reps = 3
 
     def time_stage(st, m):
+        for r in range(n_rot):  # eager once first: earlier stages' results, and workspaces allocated outside capture
+            for _, s0 in stages:
+                if st is not None and s0 is not None and s0 < st:
+                    stage(r, s0, m)
+            stage(r, st, m)
+        torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for r in range(n_rot):
@@ -205,10 +223,15 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16):
         return e0.elapsed_time(e1) / (reps * n_rot)
 
     stage_ms = {name: time_stage(st, mode | form) for name, st in stages}
-    # the same expert kernels with the nibbles decoded through the LDS byte-pair table
-    lut_ms = {}
+    # the same products in the other decode forms: the LDS byte-pair table, and the
+    # FP4 matrix cores (x split into pieces first) or the vector convert
+    lut_ms, alt_ms = {}, {}
     if mode == k3g.EXACT and T == 1:
         lut_ms = {name: time_stage(st, mode | k3g.DECODE_LUT) for name, st in stages if name in ("up", "down")}
+        alt = mode if f4 else mode | k3g.DECODE_MFMA
+        alt_ms = {name: time_stage(st, alt) for name, st in
+                  [("quant_x", k3g.STAGE_QUANT_X), ("up", k3g.STAGE_UP), ("down", k3g.STAGE_DOWN)]
+                  if f4 is False or name != "quant_x"}
     timing = (f"step: {len(graphs) and 'HIP graph per step' or 'eager'} replay; stages: HIP events around a graph "
               f"of {n_rot} launches of the stage, {reps} replays")
 
@@ -277,30 +300,38 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16):
             "workload": workload,
             "tokens_per_step": T,
             "experts": E, "top_k": K, "latent": L, "inter": I,
-            "mode": mode_name + ("+bf16-mfma" if form else ""),
+            "mode": mode_name + ("+bf16-mfma" if form == k3g.IDOT_BF16 else "+fp4-mfma" if form else ""),
             "distinct_experts_per_step": n_exp,
             "algorithmic_bytes_per_step": int(alg_bytes),
             "seed_bank": ctx["seed_bank"], "seed_workload": wl_seed,
         },
         "tokens_per_s": round(tok_s, 1),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-        "decode": ("gfx950 FP4->FP32 convert" if mode == k3g.EXACT else
+        "decode": ("gfx950 FP4 MFMA on the stored nibbles, x and h as 16 e2m1 pieces" if f4 else
+                   "gfx950 FP4->FP32 convert" if mode == k3g.EXACT else
                    "bf16 MFMA on exact int8 values" if form else "int8 MFMA"),
+        ("stage_us_vector_cvt_decode" if f4 else "stage_us_fp4_mfma_decode"):
+            {k: round(v * 1e3, 2) for k, v in alt_ms.items()},
         "stage_us_lds_lut_decode": {k: round(v * 1e3, 2) for k, v in lut_ms.items()},
         "timing": timing,
         "roofline": roof,
     }
     # release this workload's device memory before the next one
-    del graphs, ws, ws_r, idx, wts, ys, xs
+    del graphs, ws, ws_r, ws_by_mode, idx, wts, ys, xs
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return result, (xs_host, W, b, alg_bytes, T, mode)
 
 
+# the sources of the decode expert kernels whose counters profiles/ holds
+TRAFFIC_SOURCES = ("f4mma.hip", "gemv.hip", "k3g_common.h")
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch (read + write) of `kernel` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary, scaled by the copy calibration; None when no
-    summary exists for this workload or the kernel sources changed since."""
+    summary exists for this workload or the kernel sources (TRAFFIC_SOURCES)
+    changed since."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
@@ -308,8 +339,7 @@ def measured_traffic(workload, kernel):
         return None
     doc = json.load(open(path))
     csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
-    sha = hashlib.sha256(open(os.path.join(csrc, "gemv.hip"), "rb").read() +
-                         open(os.path.join(csrc, "k3g_common.h"), "rb").read()).hexdigest()
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in TRAFFIC_SOURCES)).hexdigest()
     if sha != doc.get("source_sha256") or kernel not in doc.get("kernels", {}):
         return None
     k = doc["kernels"][kernel]

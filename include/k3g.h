@@ -76,6 +76,16 @@ typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
  * to the int8 form bit for bit; the workspace gains bf16 copies of xq and hq. */
 #define K3G_IDOT_BF16 0x200
 
+/* OR-ed into K3G_EXACT: run a one-token layer on the FP4 matrix cores instead
+ * of the vector kernels. The products use v_mfma_scale_f32_16x16x128_f8f6f4
+ * on the stored nibbles and scales, with x and h written as sums of 16 e2m1
+ * vectors (one ue8m0 scale per 32 entries each, entries below 2^-127
+ * dropped); every product is exact and sums are fp32, as in the vector form,
+ * so both meet the same bound. Needs latent and inter multiples of 512 (at
+ * most 4096) and a bank with 16-byte aligned scale tensors and stride;
+ * otherwise, and with more than one token, the vector kernels run. */
+#define K3G_DECODE_MFMA 0x400
+
 typedef struct {
     const uint8_t *packed; /* [rows][in/2], 16-byte aligned */
     const uint8_t *scales; /* [rows][in/32]                 */
@@ -148,13 +158,17 @@ typedef struct {
  *   lat, agg, nrm  float [T][latent]     block stages
  *   shh     float [T][sh_inter]          block shared-expert SiTU output
  *   layer   the MoE layer's own workspace inside the block's
- *   xqb, hqb  uint16 (bf16) copies of xq and hq (K3G_IDOT_BF16 only) */
+ *   xqb, hqb  uint16 (bf16) copies of xq and hq (K3G_IDOT_BF16 only)
+ *   xp, hp    one-token layer with K3G_DECODE_MFMA: x and each pair's h as 16
+ *             e2m1 pieces, 1280 bytes per 128 entries (operand B of the
+ *             instruction and its block scales) */
 typedef struct {
     size_t total;
     size_t logits, counts, offsets, perm, inv, active;
     size_t xq, xs, h, hq, hs, ypair;
     size_t idx, wts, lat, agg, nrm, shh, layer;
     size_t xqb, hqb;
+    size_t xp, hp;
 } k3g_ws_layout;
 
 /* Human-readable name of a status code (static storage). */
@@ -223,9 +237,10 @@ int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts
  * one kernel launch (stages a mode does not have enqueue nothing), so a
  * caller can place events between them to time each kernel:
  *   BUCKET   stable sort of the pairs by expert (counts, offsets, perm, inv, active)
- *   QUANT_X  IDOT only: x -> xq, xs
+ *   QUANT_X  IDOT: x -> xq, xs; one token with K3G_DECODE_MFMA: x -> xp
  *   UP       per expert and row: g = w1 a, u = w3 a, h = SiTU(g, u)
- *   QUANT_H  IDOT only: h -> hq, hs
+ *   QUANT_H  IDOT: h -> hq, hs (with K3G_DECODE_MFMA, UP writes hp itself
+ *            and this stage enqueues nothing)
  *   DOWN     per expert and row: ypair = w2 h
  *   COMBINE  y[t] = sum_k wts[t][k] * ypair[inv[t*top_k+k]]
  * Arguments as k3g_moe_layer; every stage validates them the same way and

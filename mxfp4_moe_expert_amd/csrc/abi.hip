@@ -37,6 +37,13 @@ struct DenseSeg {
     int K;
 };
 int launch_dense(float *out, const DenseSeg *segs, int n_seg, int T, int N, hipStream_t st);
+int launch_split(uint8_t *dst, const float *src, int n_vec, int len, int src_stride, hipStream_t st);
+int launch_moe_up_f4(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const Route1 &rt, int top_k,
+                     int latent, int inter, int max_slots, hipStream_t st);
+int launch_moe_down_f4(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
+                       const int32_t *offsets, int latent, int inter, int max_slots, hipStream_t st);
+bool f4_shape_ok(int latent, int inter);
+bool f4_bank_ok(const BankDev &b);
 int launch_dense_glu(float *h, const uint16_t *w1, const uint16_t *w3, const float *x, int T, int K, int N,
                      hipStream_t st);
 int launch_rmsnorm(float *n, const float *a, const float *gamma, int T, int len, float eps, hipStream_t st);
@@ -83,13 +90,20 @@ struct Carver {
     }
 };
 
-inline int base_mode(int mode) { return mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16); }
+inline int base_mode(int mode) { return mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_DECODE_MFMA); }
 inline bool mode_ok(int mode) {
-    if (mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16 | 0xFF)) return false;
+    if (mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_DECODE_MFMA | 0xFF)) return false;
     if ((mode & K3G_IDOT_BF16) && base_mode(mode) != K3G_IDOT) return false;
+    if ((mode & (K3G_DECODE_LUT | K3G_DECODE_MFMA)) && base_mode(mode) != K3G_EXACT) return false;
     return base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT;
 }
 inline bool lut_of(int mode) { return (mode & K3G_DECODE_LUT) != 0; }
+// One token in EXACT mode with K3G_DECODE_MFMA runs on the FP4 matrix cores
+// when the shape fits them (the bank's alignment is checked where the bank is
+// known).
+inline bool f4_layer(int mode, int n_tokens, int latent, int inter) {
+    return n_tokens == 1 && mode == (K3G_EXACT | K3G_DECODE_MFMA) && f4_shape_ok(latent, inter);
+}
 // The IDOT kernels stage a row's scale bytes four groups at a time as aligned
 // dwords: both widths must be multiples of 128 columns. The bf16 form addresses
 // a row of its activations by a 32-bit byte offset: T rows of x and T*top_k
@@ -168,6 +182,10 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
                     o->xqb = c.take(sizeof(uint16_t) * (T ? T : 1) * s.latent);
                     o->hqb = c.take(sizeof(uint16_t) * (P ? P : 1) * s.inter);
                 }
+            }
+            if (f4_layer(s.mode, s.n_tokens, s.latent, s.inter)) {  // 40 bytes per entry
+                o->xp = c.take((size_t)s.latent / 128 * 1280);
+                o->hp = c.take(P * (size_t)s.inter / 128 * 1280);
             }
             o->layer = 0;
             break;
@@ -388,19 +406,26 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
     // and writes the bucket, so the bucket stage launches nothing.
     const bool route1 = n_tokens == 1 && base_mode(mode) == K3G_EXACT;
     const Route1 r1 = route1 ? Route1{idx, counts, offsets, perm, inv, active, E} : Route1{};
+    // one token on the FP4 matrix cores: x and h split into e2m1 pieces first
+    const bool f4 = f4_layer(mode, n_tokens, latent, inter) && f4_bank_ok(b) && L.xp && L.hp;
+    uint8_t *xp = (uint8_t *)(w + L.xp), *hp = (uint8_t *)(w + L.hp);
     switch (stage) {
         case K3G_STAGE_BUCKET:
             return route1 ? K3G_OK : launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
         case K3G_STAGE_QUANT_X:
+            if (f4) return launch_split(xp, x, 1, latent, latent, st);
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, xqb, st) : K3G_OK;
         case K3G_STAGE_UP:
+            if (f4) return launch_moe_up_f4(h, hp, xp, b, r1, top_k, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_up_idot(h, xq, xqb, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
                        : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P,
                                              lut_of(mode), r1, st);
         case K3G_STAGE_QUANT_H:
+            if (f4) return K3G_OK;  // the up-projection wrote hp
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, hqb, st) : K3G_OK;
         case K3G_STAGE_DOWN:
+            if (f4) return launch_moe_down_f4(ypair, hp, b, active, offsets, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_down_idot(ypair, hq, hqb, hs, b, active, offsets, perm, latent, inter, max_slots, st)
                        : launch_moe_down_exact(ypair, h, b, active, offsets, perm, latent, inter, max_slots,

@@ -1,0 +1,384 @@
+// f4mma.hip -- the one-token expert products on gfx950's block-scaled FP4
+// matrix cores.
+//
+// The product is the pages' exact one ("kimi-k3-in-c: 2.78 trillion
+// parameters, one CPU, 8 GB of RAM", section "Reduction one"): per row, every
+// 32-group's e2m1 values dotted with fp32 x, times 2^(s-127), groups with
+// s = 255 left out, fp32 accumulation. The convert-and-FMA form of it spends
+// about 1.5 vector instructions per weight, which on this chip takes longer
+// than streaming the weights from HBM. Here the weights go to
+// v_mfma_scale_f32_16x16x128_f8f6f4 as they are stored: the nibbles are
+// operand A and the group's ue8m0 byte is A's block scale, so decoding costs
+// nothing. The matrix cores take no fp32 operand, so x is first written as a
+// sum of 16 e2m1 vectors ("pieces") with one ue8m0 scale per 32 entries each.
+// Piece 0 rounds x to e2m1 on the power-of-two grid that puts the group's
+// largest |x| in (3, 6]; every later piece rounds what is left on a grid four
+// times finer than the one before. Each step is exact in fp32, and what is
+// left never exceeds half a grid unit of the step before, so it always fits
+// the next grid (at most 4 of its units) and shrinks at least four-fold per
+// piece: after 16 pieces it is below 2^-30 of the group's largest entry (in
+// practice zero: an fp32 entry has 24 bits). Grids stop at 2^-126, so entries
+// below 2^-127 are dropped. The 16 pieces are the 16
+// columns of operand B; every product e2m1 * e2m1 * 2^a * 2^b is exact, the
+// matrix cores add in fp32, and the 16 column sums are added at the end
+// (fp32, by DPP).
+//
+// Layout of one vector's pieces (n = 32 * ngrp entries, ngrp a multiple of 4),
+// in chunks of 128 entries (one k-step of the instruction), 1280 bytes each:
+//   bytes [0, 1024):    lane l = p + 16*q holds, at 16*l, the 32 nibbles of
+//                       piece p for group 4*i + q (entry 2b in the low nibble
+//                       of byte b) -- exactly operand B of the instruction;
+//   bytes [1024, 1280): lane l's uint32 at 1024 + 4*l, low byte the ue8m0
+//                       scale of that piece and group -- B's block scale.
+// Operand A uses the same k order: lane l = r + 16*q of a 16-row tile loads
+// the 16 bytes of group 4*i + q of row r, so one instruction reads 64
+// contiguous bytes of each of 16 rows.
+#include "k3g_common.h"
+
+// Build-time knob (the default is the shipped configuration): blocks of four
+// chunks in the product kernels' load ring; all but one are in flight while
+// the oldest is multiplied.
+#ifndef K3G_F4_NBUF
+#define K3G_F4_NBUF 6
+#endif
+
+namespace k3g {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+namespace f4 {
+constexpr int kChunkBytes = 1280;  // pieces + scales of 128 entries
+constexpr int kWaves = 4;          // wavefronts per workgroup
+constexpr int kRows = 32;          // rows a wavefront owns (two 16-row tiles)
+constexpr int kPieces = 16;
+}  // namespace f4
+
+// ---- pieces -----------------------------------------------------------------
+
+// The 16 pieces of one 32-entry group whose entry e = lane & 31 is r (both
+// halves of the wavefront may hold groups): written at `out` (the group's
+// chunk) as column group q when `store`. The rounding to e2m1 is gfx950's
+// scaled convert (to nearest, ties to the even code, r / 2^x with a
+// power-of-two scale; the way back gives the value times 2^x exactly).
+__device__ inline void split_group(float r, uint8_t *out, int q, bool store) {
+    const int e = threadIdx.x & 31;
+    float m = __builtin_fabsf(r);
+#pragma unroll
+    for (int s = 1; s < 32; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 32));
+    // piece 0's grid: the smallest x with m <= 6 * 2^x. With m = M * 2^E, M in
+    // [1, 2): E - 2 when M <= 1.5, else E - 1 (m / 2^x then lies in (3, 6]).
+    // Grids stop at 2^-126 (a normal fp32 scale): entries below 2^-127 are
+    // dropped.
+    const uint32_t mb = __builtin_bit_cast(uint32_t, m);
+    const int x0 = int(mb >> 23) - 129 + ((mb & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+#pragma unroll
+    for (int p = 0; p < f4::kPieces; ++p) {
+        const int x = max(x0 - 2 * p, -126);
+        const float sc = __builtin_bit_cast(float, (uint32_t)(x + 127) << 23);
+        const uint32_t nib = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r, 0.0f, sc, 0) & 15u;
+        r -= __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, sc, 0)[0];  // exact: both are multiples of r's last bit
+        // eight nibbles per dword: every lane of an aligned group of 8 collects
+        // entries 8d..8d+7 (quad swaps, then the half-row mirror)
+        uint32_t w = nib << (4 * (e & 7));
+        w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0xB1, 0xF, 0xF, false);
+        w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x4E, 0xF, 0xF, false);
+        w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x141, 0xF, 0xF, false);
+        const int lane = p + 16 * q;
+        if (store && (e & 7) == 0) *(uint32_t *)(out + 16 * lane + 4 * (e >> 3)) = w;
+        if (store && e == 0) *(uint32_t *)(out + 1024 + 4 * lane) = (uint32_t)(x + 127);
+    }
+}
+
+// Pieces of n_vec vectors of ngrp groups each: src fp32 rows of src_stride
+// floats, dst rows of (ngrp/4)*1280 bytes. One half-wavefront per group.
+__global__ __launch_bounds__(256) void split_kernel(uint8_t *__restrict__ dst, const float *__restrict__ src,
+                                                    int n_vec, int ngrp, int src_stride) {
+    const int G = blockIdx.x * 8 + (threadIdx.x >> 5);
+    const bool live = G < n_vec * ngrp;
+    const int Gc = live ? G : 0;
+    const int v = Gc / ngrp, g = Gc - v * ngrp;
+    const float r = src[(size_t)v * src_stride + g * kGroup + (threadIdx.x & 31)];
+    split_group(r, dst + (size_t)v * (ngrp / 4) * f4::kChunkBytes + (g >> 2) * f4::kChunkBytes, g & 3, live);
+}
+
+int launch_split(uint8_t *dst, const float *src, int n_vec, int len, int src_stride, hipStream_t st) {
+    const int ngrp = len / kGroup;
+    const int groups = n_vec * ngrp;
+    if (groups == 0) return K3G_OK;
+    split_kernel<<<(groups + 7) / 8, 256, 0, st>>>(dst, src, n_vec, ngrp, src_stride);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
+// ---- the products -------------------------------------------------------------
+
+// Out-of-range soffset: a buffer load past the resource's range returns 0
+// without touching memory, so a wavefront with no rows still runs the same
+// straight-line code (and the barrier) without reading anything.
+constexpr uint32_t kOffRange = 0x80000000u;
+
+// UP:   tiles (w1, rows r0..r0+15), (w3, r0..r0+15), (w1, r0+16..), (w3, r0+16..);
+//       h[pos][r] = SiTU(g, u) for the 32 rows, and the 16 pieces of this
+//       32-entry group of h (the down-projection's operand B) into hp[pos].
+// DOWN: tiles (w2, rows r0..r0+15), (w2, r0+16..); ypair[pos][r] for the 32 rows.
+// A wavefront walks its tiles one after another (a tile's 16 rows are
+// contiguous in memory) in blocks of four chunks: a block's loads (four
+// 16-byte loads of nibbles a lane and one 16-byte load of the rows' scale
+// dwords) go out together into a ring of NBUF blocks, and NBUF - 1 blocks are
+// in flight while the oldest is multiplied.
+// A workgroup's wavefronts own consecutive 32-row blocks of one slot (DOWN) or
+// of any slots (UP: B is x for all of them). One token: every slot has one
+// pair, or several equal ones when the route repeats an expert.
+template <bool UP, int NCK>
+__global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4_kernel(
+    float *__restrict__ out, const uint8_t *__restrict__ pieces, uint8_t *__restrict__ hp, BankDev bank, Route1 rt,
+    const int32_t *__restrict__ active, const int32_t *__restrict__ offsets, int top_k, int latent, int inter,
+    int max_slots) {
+    constexpr int TILES = UP ? 4 : 2;
+    constexpr int NS = TILES * NCK;  // steps: (tile, chunk)
+    constexpr int CPB = 4;                // chunks per block
+    constexpr int NB = TILES * NCK / CPB;  // blocks
+    constexpr int NBUF = K3G_F4_NBUF;      // ring of blocks
+    constexpr int ngrp = 4 * NCK;
+    extern __shared__ uint4 lds_b[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n_out = UP ? inter : latent;
+    const int blocks_per_slot = n_out / f4::kRows;
+
+    // which slot and rows this wavefront owns
+    int slot, blk32;
+    if (UP) {
+        const int item = blockIdx.x * f4::kWaves + wave;
+        slot = item / blocks_per_slot;
+        blk32 = item - slot * blocks_per_slot;
+    } else {
+        const int wgs = (blocks_per_slot + f4::kWaves - 1) / f4::kWaves;
+        slot = blockIdx.x / wgs;
+        blk32 = (blockIdx.x - slot * wgs) * f4::kWaves + wave;
+    }
+    int e = 0, p0 = 0, p1 = 0, n_act;
+    Route1Lane r1 = {};
+    if (UP) {
+        r1 = route1_lane(rt.idx, top_k, rt.n_experts, lane);
+        n_act = __popcll(r1.firsts);
+        const uint64_t m = __ballot(r1.first && r1.slot == slot);
+        if (m) {
+            const int L = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+            e = __builtin_amdgcn_readlane(r1.e, L);
+            p0 = __builtin_amdgcn_readlane(r1.pos, L);
+            p1 = p0 + __builtin_amdgcn_readlane(r1.cnt, L);
+        }
+    } else {
+        n_act = active[0];
+        if (slot < n_act) {
+            e = active[1 + slot];
+            p0 = offsets[e];
+            p1 = offsets[e + 1];
+        }
+    }
+    if (!UP && slot >= n_act) return;  // whole workgroup: DOWN's workgroups hold one slot
+    const bool live = slot < n_act && slot < max_slots && blk32 < blocks_per_slot && p1 > p0;
+
+    // the wavefront's tiles: buffer resources, and this lane's row offsets
+    const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
+    constexpr uint32_t pitch_p = 16u * ngrp, pitch_s = ngrp;
+    const int r0 = (live ? blk32 : 0) * f4::kRows;
+    rsrc_t rp[TILES], rs[TILES];
+    uint32_t vp[TILES], vs[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
+        const uint32_t row = (uint32_t)(r0 + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
+        rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
+        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vs[t] = row * pitch_s;
+    }
+    // block k: tile k / (NCK/4), chunks 4*(k % (NCK/4)) .. +3 (a dead wavefront's
+    // loads are all past the range: zeros, no memory traffic)
+    const uint32_t dead = live ? 0u : kOffRange;
+    uint4 A[NBUF][CPB], S[NBUF];
+    auto load_block = [&](int k) {
+        const int t = k / (NCK / CPB), c0 = CPB * (k % (NCK / CPB)), b = k % NBUF;
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u + dead);
+        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u + dead);
+    };
+    // the bucket: wavefront 0 of workgroup b writes counts and offsets
+    // [64b, 64b + 64) (workgroup 0 also perm, inv, active)
+    if (UP && wave == 0)
+        for (int part = blockIdx.x; part * kWave <= rt.n_experts; part += gridDim.x)
+            route1_write_bucket_part(rt, r1, top_k, lane, part);
+    // B: this workgroup's vector of pieces into LDS (no registers); then the
+    // first NBUF - 1 blocks of weights. The wait before the barrier leaves
+    // exactly those in flight (vmcnt counts the bucket's stores, the DMA and
+    // the weight loads in the order they were issued).
+    {
+        const int pos_b = UP ? 0 : p0;
+        const uint8_t *src = pieces + (size_t)pos_b * NCK * f4::kChunkBytes;
+        const uint32_t lb = lds_addr(lds_b);
+        constexpr int units = NCK * f4::kChunkBytes / 1024;  // 1 KB per wavefront instruction
+        for (int u = wave; u < units; u += f4::kWaves) dma16(src, 1024u * u + 16u * lane, lb + 1024u * u);
+    }
+    __asm__ volatile("" ::: "memory");  // the weight loads stay after the DMA
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int PRO = NBUF - 1 < NB ? NBUF - 1 : NB;  // blocks loaded ahead
+#pragma unroll
+    for (int k = 0; k < PRO; ++k) load_block(k);
+    wait_vm<PRO * (CPB + 1)>();
+    __syncthreads();
+
+    const uint32_t qsh = 8u * (uint32_t)(lane >> 4);
+    // two accumulators per tile (even and odd chunks), so that consecutive
+    // products do not wait for each other
+    float4_t acc[TILES][2];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) acc[t][0] = acc[t][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // B of block k, read from LDS one block ahead
+    uint4 Bv[2][CPB];
+    uint32_t Bs[2][CPB];
+    auto read_b = [&](int k) {
+        const int c0 = CPB * (k % (NCK / CPB));
+        // every tile reads B again from LDS: without this the compiler keeps the
+        // first tile's reads of all chunks in registers for the later tiles
+        if (c0 == 0) __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+            const int i = c0 + c;
+            Bv[k & 1][c] = lds_b[i * (f4::kChunkBytes / 16) + lane];
+            Bs[k & 1][c] = ((const uint32_t *)lds_b)[(i * f4::kChunkBytes + 1024) / 4 + lane];
+        }
+    };
+    auto compute = [&](int k) {
+        const int t = k / (NCK / CPB), b = k % NBUF;
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+            const uint4 bv = Bv[k & 1][c];
+            const v8i_t B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
+            const uint32_t sd = c == 0 ? S[b].x : c == 1 ? S[b].y : c == 2 ? S[b].z : S[b].w;
+            const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
+            // scale 255: the group is left out (its data zeroed, its scale made finite)
+            const uint32_t keep = sa == 255u ? 0u : ~0u;
+            const uint4 a = A[b][c];
+            const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
+            float4_t &ac = acc[t][c & 1];
+            ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av, B, ac, 4, 4, 0, (int)(sa & keep), 0,
+                                                                  (int)Bs[k & 1][c]);
+        }
+    };
+    read_b(0);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        if (k + NBUF - 1 < NB) load_block(k + NBUF - 1);
+        if (k + 1 < NB) read_b(k + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) acc[t][0] += acc[t][1];
+    // (no early exit for a dead wavefront here: a branch around the epilogue
+    // would let the compiler sink every product into it, after all the loads)
+
+    // sum the 16 piece columns: lanes 16w..16w+15 hold one row block's columns
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sm = acc[t][0][v];
+            sm += dpp<0xB1>(sm);
+            sm += dpp<0x4E>(sm);
+            sm += dpp<0x141>(sm);
+            sm += dpp<0x140>(sm);
+            acc[t][0][v] = sm;
+        }
+    // lane (q = lane & 15) < 8 holds row 16*ts + 4*(lane >> 4) + v, ts = q >> 2, v = q & 3
+    const int q = lane & 15, ts = (q >> 2) & 1, v = q & 3;
+    auto sel = [&](const float4_t &x0, const float4_t &x1) {
+        const float4_t &x = ts ? x1 : x0;
+        return v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
+    };
+    const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+    if constexpr (UP) {
+        const float g = sel(acc[0][0], acc[2][0]);
+        const float u = sel(acc[1][0], acc[3][0]);
+        const float hv = situ(g, u);
+        if (live && q < 8)
+            for (int p = p0; p < p1; ++p) out[(size_t)p * n_out + row] = hv;
+        // the pieces of this group of h: entry j (row r0 + j) from lane
+        // 16*((j%16)/4) + 4*(j/16) + j%4 into lanes j and 32 + j
+        const int j = lane & 31;
+        const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
+        const int g32 = r0 / kGroup;  // the group's index in a row of h
+        const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+        uint8_t *dst = hp + (size_t)p0 * hstride + (g32 >> 2) * f4::kChunkBytes;
+        split_group(hj, dst, g32 & 3, live && lane < 32);
+        for (int p = p0 + 1; p < p1; ++p)  // a repeated expert: equal pairs, equal pieces
+            split_group(hj, dst + (size_t)(p - p0) * hstride, g32 & 3, live && lane < 32);
+    } else {
+        const float y = sel(acc[0][0], acc[1][0]);
+        if (live && q < 8)
+            for (int p = p0; p < p1; ++p) out[(size_t)p * n_out + row] = y;
+    }
+}
+
+// The matrix-core path takes whole 4-chunk blocks (512 entries; a row's
+// scale bytes in 16-byte loads), whole 32-row blocks and whole 4-chunk groups
+// of h's pieces: in and out sizes multiples of 512, at most 4096 (B -- a
+// vector's pieces, 40 bytes per entry -- in LDS); scale tensors and bank
+// stride 16-byte aligned. (Other shapes and banks use the vector kernels.)
+bool f4_shape_ok(int latent, int inter) {
+    auto ok = [](int n) { return n % 512 == 0 && n >= 512 && n <= 4096; };
+    return ok(latent) && ok(inter);
+}
+
+bool f4_bank_ok(const BankDev &b) {
+    if (b.stride % 16) return false;
+    for (int i = 1; i < 6; i += 2)
+        if (((uintptr_t)b.base + b.off[i]) % 16) return false;
+    return true;
+}
+
+template <bool UP, int NCK>
+static int launch_f4(float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank, const Route1 &rt,
+                     const int32_t *active, const int32_t *offsets, int top_k, int latent, int inter, int max_slots,
+                     hipStream_t st) {
+    const int n_out = UP ? inter : latent;
+    const int bps = n_out / f4::kRows;
+    const int grid = UP ? (max_slots * bps + f4::kWaves - 1) / f4::kWaves
+                        : max_slots * ((bps + f4::kWaves - 1) / f4::kWaves);
+    if (grid == 0) return K3G_OK;
+    const size_t lds = (size_t)NCK * f4::kChunkBytes;
+    moe_f4_kernel<UP, NCK><<<grid, f4::kWaves * kWave, lds, st>>>(out, pieces, hp, bank, rt, active, offsets, top_k,
+                                                                  latent, inter, max_slots);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
+// NCK = a row's chunks of 128 entries (n/128: 4, 8, ..., 32).
+template <bool UP>
+static int launch_f4_n(int n_in, float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank,
+                       const Route1 &rt, const int32_t *active, const int32_t *offsets, int top_k, int latent,
+                       int inter, int max_slots, hipStream_t st) {
+    switch (n_in / 128) {
+#define K3G_F4(C)                                                                                              \
+    case C:                                                                                                    \
+        return launch_f4<UP, C>(out, pieces, hp, bank, rt, active, offsets, top_k, latent, inter, max_slots, st);
+        K3G_F4(4) K3G_F4(8) K3G_F4(12) K3G_F4(16) K3G_F4(20) K3G_F4(24) K3G_F4(28) K3G_F4(32)
+#undef K3G_F4
+        default: return K3G_EUNSUPPORTED;
+    }
+}
+
+// The up-projection also writes the pieces of h (hp) for the down-projection.
+int launch_moe_up_f4(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const Route1 &rt, int top_k,
+                     int latent, int inter, int max_slots, hipStream_t st) {
+    return launch_f4_n<true>(latent, h, xp, hp, bank, rt, nullptr, nullptr, top_k, latent, inter, max_slots, st);
+}
+
+int launch_moe_down_f4(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
+                       const int32_t *offsets, int latent, int inter, int max_slots, hipStream_t st) {
+    return launch_f4_n<false>(inter, ypair, hp, nullptr, bank, Route1{}, active, offsets, 1, latent, inter,
+                              max_slots, st);
+}
+
+}  // namespace k3g

@@ -216,66 +216,6 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
     }
 }
 
-// ---- one token: its route entries in the bucket's order -------------------------
-// With a single token the bucket (pairs sorted by expert, then token) is a
-// small permutation of the K route entries, which a wavefront can rank on its
-// own; the decode up-projection does that instead of waiting for a separate
-// bucket launch. Lane k holds entry k: its expert, whether the id is in range,
-// its position among the sorted pairs, whether it is the first entry of its
-// expert (duplicates share one slot), the slot of its expert (rank among the
-// distinct experts) and the number of entries of its expert.
-struct Route1Lane {
-    int e, pos, slot, cnt;
-    bool valid, first;
-    uint64_t firsts;  // ballot of `first`: popcount = number of slots
-};
-
-__device__ inline Route1Lane route1_lane(const int32_t *idx, int K, int E, int lane) {
-    Route1Lane r;
-    r.e = lane < K ? idx[lane] : -1;
-    r.valid = lane < K && (unsigned)r.e < (unsigned)E;
-    r.pos = 0;
-    r.cnt = 0;
-    r.first = r.valid;
-    for (int j = 0; j < K; ++j) {  // uniform loop: entry j's expert read from lane j
-        const int ej = __builtin_amdgcn_readlane(r.e, j);
-        if ((unsigned)ej < (unsigned)E) {
-            r.pos += (ej < r.e || (ej == r.e && j < lane)) ? 1 : 0;
-            r.cnt += ej == r.e ? 1 : 0;
-            r.first = r.first && !(ej == r.e && j < lane);
-        }
-    }
-    r.firsts = __ballot(r.first);
-    r.slot = 0;
-    for (int j = 0; j < K; ++j) {
-        const int ej = __builtin_amdgcn_readlane(r.e, j);
-        if ((r.firsts >> j) & 1ull) r.slot += ej < r.e ? 1 : 0;
-    }
-    return r;
-}
-
-// Workgroup 0's wavefront 0 writes the bucket as the bucket kernel would.
-__device__ inline void route1_write_bucket(const Route1 &rt, const Route1Lane &r, int K, int lane) {
-    const int E = rt.n_experts;
-    for (int e0 = 0; e0 <= E; e0 += kWave) {
-        const int e = e0 + lane;
-        int below = 0, c = 0;
-        for (int j = 0; j < K; ++j) {
-            const int ej = __builtin_amdgcn_readlane(r.e, j);
-            if ((unsigned)ej < (unsigned)E) {
-                below += ej < e ? 1 : 0;
-                c += ej == e ? 1 : 0;
-            }
-        }
-        if (e < E) rt.counts[e] = c;
-        if (e <= E) rt.offsets[e] = below;
-    }
-    if (r.valid) rt.perm[r.pos] = lane;
-    if (lane < K) rt.inv[lane] = r.valid ? r.pos : -1;
-    if (r.first) rt.active[1 + r.slot] = r.e;
-    if (lane == 0) rt.active[0] = __popcll(r.firsts);
-}
-
 // Grouped SiTU-GLU up-projection. Work item = (slot, run of rpi rows); slot i
 // is the i-th expert that has pairs (active[1+i]); its pairs are the sorted
 // positions [offsets[e], offsets[e+1]), token = perm[pos] / top_k. For each

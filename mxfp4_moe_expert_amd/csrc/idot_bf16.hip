@@ -80,31 +80,6 @@ __device__ inline bf16x8_t fp4x8_bf16(uint32_t w, float scale) {
     return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ inline uint32_t lds_addr(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p);
-}
-
-// Global -> LDS without registers: lane l's 16 (or 4) bytes from base + voff
-// land at `lds` + 16*l (or 4*l). `base` is wave-uniform (SGPRs). The loads are
-// inline assembly so that the compiler does not wait for them before every
-// LDS read; the kernel waits with s_waitcnt vmcnt itself.
-__device__ inline void dma16(const void *base, uint32_t voff, uint32_t lds) {
-    lds = __builtin_amdgcn_readfirstlane(lds);
-    __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
-                     : "m0");
-}
-__device__ inline void dma4(const void *base, uint32_t voff, uint32_t lds) {
-    lds = __builtin_amdgcn_readfirstlane(lds);
-    __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "s"(lds)
-                     : "m0");
-}
-
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __asm__ volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 // Number of token-load instructions of a pass with NT tiles, and how many of
 // them fall on wavefront wl (instruction n goes to wavefront n % NW).
 constexpr int tok_instr(int nt) { return (nt * 16 * TCH + 63) / 64; }

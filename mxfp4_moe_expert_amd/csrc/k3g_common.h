@@ -178,6 +178,90 @@ __device__ inline float situ(float g, float u) {
     return 4.0f * tanh_fast(g * 0.25f) * sig * (25.0f * tanh_fast(u * 0.04f));
 }
 
+// ---- one token: its route entries in the bucket's order -------------------------
+// With a single token the bucket (pairs sorted by expert, then token) is a
+// small permutation of the K route entries, which a wavefront can rank on its
+// own; the decode up-projection does that instead of waiting for a separate
+// bucket launch. Lane k holds entry k: its expert, whether the id is in range,
+// its position among the sorted pairs, whether it is the first entry of its
+// expert (duplicates share one slot), the slot of its expert (rank among the
+// distinct experts) and the number of entries of its expert.
+struct Route1Lane {
+    int e, pos, slot, cnt;
+    bool valid, first;
+    uint64_t firsts;  // ballot of `first`: popcount = number of slots
+};
+
+__device__ inline Route1Lane route1_lane(const int32_t *idx, int K, int E, int lane) {
+    Route1Lane r;
+    r.e = lane < K ? idx[lane] : -1;
+    r.valid = lane < K && (unsigned)r.e < (unsigned)E;
+    r.pos = 0;
+    r.cnt = 0;
+    r.first = r.valid;
+    for (int j = 0; j < K; ++j) {  // uniform loop: entry j's expert read from lane j
+        const int ej = __builtin_amdgcn_readlane(r.e, j);
+        if ((unsigned)ej < (unsigned)E) {
+            r.pos += (ej < r.e || (ej == r.e && j < lane)) ? 1 : 0;
+            r.cnt += ej == r.e ? 1 : 0;
+            r.first = r.first && !(ej == r.e && j < lane);
+        }
+    }
+    r.firsts = __ballot(r.first);
+    r.slot = 0;
+    for (int j = 0; j < K; ++j) {
+        const int ej = __builtin_amdgcn_readlane(r.e, j);
+        if ((r.firsts >> j) & 1ull) r.slot += ej < r.e ? 1 : 0;
+    }
+    return r;
+}
+
+// One slice of the bucket as the bucket kernel would write it: counts and
+// offsets of experts [64*part, 64*part + 64), and for part 0 also perm, inv
+// and active.
+__device__ inline void route1_write_bucket_part(const Route1 &rt, const Route1Lane &r, int K, int lane, int part) {
+    const int E = rt.n_experts;
+    const int e = part * kWave + lane;
+    int below = 0, c = 0;
+    for (int j = 0; j < K; ++j) {
+        const int ej = __builtin_amdgcn_readlane(r.e, j);
+        if ((unsigned)ej < (unsigned)E) {
+            below += ej < e ? 1 : 0;
+            c += ej == e ? 1 : 0;
+        }
+    }
+    if (e < E) rt.counts[e] = c;
+    if (e <= E) rt.offsets[e] = below;
+    if (part == 0) {
+        if (r.valid) rt.perm[r.pos] = lane;
+        if (lane < K) rt.inv[lane] = r.valid ? r.pos : -1;
+        if (r.first) rt.active[1 + r.slot] = r.e;
+        if (lane == 0) rt.active[0] = __popcll(r.firsts);
+    }
+}
+
+// Workgroup 0's wavefront 0 writes the bucket as the bucket kernel would.
+__device__ inline void route1_write_bucket(const Route1 &rt, const Route1Lane &r, int K, int lane) {
+    const int E = rt.n_experts;
+    for (int e0 = 0; e0 <= E; e0 += kWave) {
+        const int e = e0 + lane;
+        int below = 0, c = 0;
+        for (int j = 0; j < K; ++j) {
+            const int ej = __builtin_amdgcn_readlane(r.e, j);
+            if ((unsigned)ej < (unsigned)E) {
+                below += ej < e ? 1 : 0;
+                c += ej == e ? 1 : 0;
+            }
+        }
+        if (e < E) rt.counts[e] = c;
+        if (e <= E) rt.offsets[e] = below;
+    }
+    if (r.valid) rt.perm[r.pos] = lane;
+    if (lane < K) rt.inv[lane] = r.valid ? r.pos : -1;
+    if (r.first) rt.active[1 + r.slot] = r.e;
+    if (lane == 0) rt.active[0] = __popcll(r.firsts);
+}
+
 __device__ inline uint4 load16(const uint8_t *p) { return *(const uint4 *)p; }
 
 // Buffer resources: a wave-uniform base and byte range in SGPRs. A buffer load
@@ -202,6 +286,33 @@ __device__ inline uint32_t buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
 
 __device__ inline uint32_t buf_load_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
+// ---- LDS DMA ----------------------------------------------------------------------
+
+__device__ inline uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p);
+}
+
+// Global -> LDS without registers: lane l's 16 (or 4) bytes from base + voff
+// land at `lds` + 16*l (or 4*l). `base` is wave-uniform (SGPRs). The loads are
+// inline assembly so that the compiler does not wait for them before every
+// LDS read; the kernel waits with s_waitcnt vmcnt itself.
+__device__ inline void dma16(const void *base, uint32_t voff, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
+                     : "m0");
+}
+__device__ inline void dma4(const void *base, uint32_t voff, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "s"(lds)
+                     : "m0");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __asm__ volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 }  // namespace k3g

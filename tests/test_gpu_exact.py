@@ -271,7 +271,7 @@ def test_layer_skewed_routing(k3g):
     check_layer_exact(k3g, src, bankt, bank, x, idx, wts)
 
 
-@pytest.mark.parametrize("decode", [0, 0x100], ids=["cvt", "lut"])
+@pytest.mark.parametrize("decode", [0, 0x100, 0x400], ids=["cvt", "lut", "f4mma"])
 def test_layer_decode_b1_full(k3g, full_bank, decode):
     src, bankt, bank = full_bank
     W, b = synth.router(synth.SEED_BASE + 1, 896, 3584, 0.1)
@@ -283,6 +283,58 @@ def test_layer_decode_b1_full(k3g, full_bank, decode):
     io, wo, _ = oracle.route(x, W, b, 16)
     assert np.array_equal(host(idx), io)
     check_layer_exact(k3g, src, None, bank, x, io, host(wts), decode=decode)
+
+
+# ---- one token on the FP4 matrix cores -------------------------------------------------
+
+E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def decode_pieces(raw, n):
+    """The 16 e2m1 pieces of an n-vector from the matrix-core layout: chunks of
+    128 entries, 1280 bytes each; lane l = p + 16q holds 16 bytes of piece p,
+    group 4i + q (entry 2b in the low nibble of byte b), and its ue8m0 scale as
+    the low byte of the uint32 at 1024 + 4l. Returns pieces [16][n] (fp64)."""
+    out = np.zeros((16, n))
+    for i in range(n // 128):
+        blk = raw[i * 1280:(i + 1) * 1280]
+        data = blk[:1024].reshape(64, 16)
+        sc = blk[1024:].view(np.uint32)
+        for lane in range(64):
+            p, q = lane % 16, lane // 16
+            nib = np.stack([data[lane] & 15, data[lane] >> 4], 1).ravel()
+            g = 4 * i + q
+            out[p, 32 * g:32 * g + 32] = E2M1[nib] * 2.0 ** (int(sc[lane] & 0xFF) - 127)
+    return out
+
+
+def check_pieces(raw, v):
+    """The pieces add up to v: to 2^-30 of each 32-group's largest entry."""
+    v = np.asarray(v, np.float64)
+    rec = decode_pieces(raw, v.size).sum(0)
+    gmax = np.abs(v).reshape(-1, 32).max(1).repeat(32)
+    assert np.all(np.abs(rec - v) <= 2.0 ** -30 * gmax), np.abs(rec - v).max()
+
+
+@pytest.mark.parametrize("case", ["several_tiles", "repeated_expert", "wide_range"])
+def test_layer_one_token_f4mma(k3g, case):
+    E, latent, inter, K = 24, 1024, 512, 6
+    src, bankt, bank = make_bank(k3g, 61, E, latent, inter, 110, 140, 0.02)
+    x = synth.activations(61, 1, latent)
+    if case == "wide_range":  # entries over 40 decades: the split's grids follow each group
+        x = (x * 10.0 ** np.random.default_rng(61).uniform(-20, 20, x.shape)).astype(np.float32)
+    W, b = synth.router(61, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K)
+    if case == "repeated_expert":  # the same expert twice: equal pairs, one slot
+        idx[0, 3] = idx[0, 1]
+    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | k3g.DECODE_MFMA)
+    assert L["xp"] and L["hp"]  # the matrix-core path's regions exist for this shape
+    check_pieces(ws_view(ws, L, "xp", latent // 128 * 1280, np.uint8), x[0])
+    h = ws_view(ws, L, "h", K * inter, np.float32).reshape(K, inter)
+    hp = ws_view(ws, L, "hp", K * inter // 128 * 1280, np.uint8).reshape(K, -1)
+    for k in range(K):
+        check_pieces(hp[k], h[k])
+    check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=k3g.DECODE_MFMA)
 
 
 def test_layer_decode_b64_full_sampled(k3g, full_bank):
