@@ -324,7 +324,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False):
 
 
 # the sources of the decode expert kernels whose counters profiles/ holds
-TRAFFIC_SOURCES = ("f4mma.hip", "gemv.hip", "k3g_common.h")
+TRAFFIC_SOURCES = ("gemv.hip", "k3g_common.h")
 
 
 def measured_traffic(workload, kernel):

@@ -60,6 +60,7 @@ def lib():
         L.k3o_expert_glu.argtypes = [P] * 11 + [i, i, i]
         L.k3o_route_logits.argtypes = [P, P, P, i, i, i]
         L.k3o_route_select.argtypes = [P, P, P, P, P, i, i, i]
+        L.k3o_route_topp.argtypes = [P, P, P, i, i, i, C.c_double]
         L.k3o_moe_layer.argtypes = [P] * 12 + [i] * 6
         L.k3o_rmsnorm.argtypes = [P, P, P, i, C.c_double]
         L.k3o_latent_block.argtypes = [P] * 16 + [i] + [P] * 6 + [i] * 8 + [C.c_double]
@@ -237,10 +238,24 @@ def route_select(logits, bias, top_k: int):
     return idx, wts, b
 
 
-def route(x, W, bias, top_k: int):
+def route(x, W, bias, top_k: int, top_p: float = 0.0):
+    """Routing of the tokens x: logits, top-k selection, and with top_p > 0 the
+    K3_TOPP cut of the low-weight tail (dropped entries idx -1, wts 0)."""
     lg = route_logits(x, W)
     idx, wts, _ = route_select(lg, bias, top_k)
+    if top_p:
+        idx, wts = route_topp(idx, wts, lg, top_p)
     return idx, wts, lg
+
+
+def route_topp(idx, wts, logits, top_p: float):
+    """K3_TOPP applied to a top-k routing (copies; see k3o_route_topp)."""
+    idx = np.array(np.atleast_2d(idx), np.int32, order="C")
+    wts = np.array(np.atleast_2d(wts), np.float32, order="C")
+    logits = _c(np.atleast_2d(logits), np.float64)
+    T, K = idx.shape
+    _chk(lib().k3o_route_topp(_p(idx), _p(wts), _p(logits), T, logits.shape[1], K, float(top_p)), "route_topp")
+    return idx, wts
 
 
 def _expert_ptr_arrays(experts: dict, n_experts: int):

@@ -508,13 +508,84 @@ int k3o_route_select(int32_t *idx, float *wts, double *biased, const double *log
     return 0;
 }
 
+/* K3_TOPP on the output of k3o_route_select ([COLIBRI-K3] "Streaming design",
+ * and its table of environment variables: keep the routed experts up to a
+ * cumulative weight p, drop the low-weight tail of the top-k, renormalise;
+ * p = 0 is off). The pages leave the order and the boundary open; this
+ * library's reading:
+ *   - the weights are the renormalised raw scores w_k = sc_k / sum, sum over
+ *     the selected experts in selection order (double, as k3o_route_select);
+ *   - the selected experts are taken largest weight first, equal weights in
+ *     selection order;
+ *   - an expert is kept when the weight taken before it (summed in that
+ *     order, double) is still below p: the expert that reaches p is kept;
+ *   - a dropped entry becomes idx -1, wts 0, in place (route order kept);
+ *     kept entries get wts sc_k / (sum of the kept sc, selection order).
+ * p <= 0 leaves the routing as it is. In place on idx and wts; the raw
+ * scores are recomputed from the logits as k3o_route_select computes them. */
+int k3o_route_topp(int32_t *idx, float *wts, const double *logits, int n_tokens, int n_experts,
+                   int top_k, double p)
+{
+    if (n_tokens < 0 || n_experts <= 0 || top_k < 1 || top_k > n_experts || !(p >= 0.0))
+        return -1;
+    if (p == 0.0)
+        return 0;
+    for (int t = 0; t < n_tokens; ++t) {
+        int32_t *id = idx + (size_t)t * top_k;
+        float *w = wts + (size_t)t * top_k;
+        double sc[64];
+        int order[64];
+        char keep[64];
+        if (top_k > 64)
+            return -1;
+        double sum = 0.0;
+        for (int k = 0; k < top_k; ++k) {
+            if (id[k] < 0 || id[k] >= n_experts)
+                return -1;
+            sc[k] = 1.0 / (1.0 + exp(-logits[(size_t)t * n_experts + id[k]]));
+            sum += sc[k];
+            order[k] = k;
+        }
+        /* insertion sort by weight, largest first; equal weights keep
+         * selection order (a later entry moves only past a smaller weight) */
+        for (int a = 1; a < top_k; ++a) {
+            const int o = order[a];
+            int b = a;
+            while (b > 0 && sc[order[b - 1]] / sum < sc[o] / sum) {
+                order[b] = order[b - 1];
+                --b;
+            }
+            order[b] = o;
+        }
+        double before = 0.0;
+        for (int r = 0; r < top_k; ++r) {
+            keep[order[r]] = before < p;
+            before += sc[order[r]] / sum;
+        }
+        double kept = 0.0;
+        for (int k = 0; k < top_k; ++k)
+            if (keep[k])
+                kept += sc[k];
+        for (int k = 0; k < top_k; ++k) {
+            if (keep[k]) {
+                w[k] = (float)(sc[k] / kept);
+            } else {
+                id[k] = -1;
+                w[k] = 0.0f;
+            }
+        }
+    }
+    return 0;
+}
+
 /* The MoE layer for given routing: y[t] = sum_k w[t][k] * E_{idx[t][k]}(x_t),
  * each expert output rounded to float, the weighted sum in double over k in
  * route order, rounded to float ([COLIBRI-K3] "Architecture notes": weights
  * are the renormalised raw scores; routed_scale 1.0 in [KIC-README]'s config).
  * The experts are passed as six pointer arrays indexed by expert id (entries
- * that no token selects may be NULL). Optional per-pair outputs
- * ypair[t][k][latent] and hpair[t][k][inter]. */
+ * that no token selects may be NULL). An entry with idx -1 is a pair that
+ * K3_TOPP dropped: it adds nothing (its ypair and hpair rows are zero).
+ * Optional per-pair outputs ypair[t][k][latent] and hpair[t][k][inter]. */
 int k3o_moe_layer(float *y, float *ypair, float *hpair, const float *x,
                   const int32_t *idx, const float *wts,
                   const uint8_t *const *w1p, const uint8_t *const *w1s,
@@ -528,6 +599,8 @@ int k3o_moe_layer(float *y, float *ypair, float *hpair, const float *x,
         return -1;
     for (int i = 0; i < n_tokens * top_k; ++i) {
         const int e = idx[i];
+        if (e == -1)
+            continue;
         if (e < 0 || e >= n_experts || !w1p[e] || !w1s[e] || !w3p[e] || !w3s[e] || !w2p[e] || !w2s[e])
             return -2;
     }
@@ -541,6 +614,11 @@ int k3o_moe_layer(float *y, float *ypair, float *hpair, const float *x,
     for (int p = 0; p < P; ++p) {
         const int e = idx[p];
         const int t = p / top_k;
+        if (e == -1) {
+            memset(ye_all + (size_t)p * latent, 0, sizeof(float) * latent);
+            memset(h_all + (size_t)p * inter, 0, sizeof(float) * inter);
+            continue;
+        }
         const k3o_expert ex = {w1p[e], w1s[e], w3p[e], w3s[e], w2p[e], w2s[e]};
         float *g = malloc(sizeof(float) * inter);
         float *u = malloc(sizeof(float) * inter);
@@ -557,8 +635,9 @@ int k3o_moe_layer(float *y, float *ypair, float *hpair, const float *x,
         for (int i = 0; i < latent; ++i) {
             double acc = 0.0;
             for (int k = 0; k < top_k; ++k)
-                acc += (double)wts[(size_t)t * top_k + k] *
-                       (double)ye_all[((size_t)t * top_k + k) * latent + i];
+                if (idx[(size_t)t * top_k + k] != -1)
+                    acc += (double)wts[(size_t)t * top_k + k] *
+                           (double)ye_all[((size_t)t * top_k + k) * latent + i];
             y[(size_t)t * latent + i] = (float)acc;
         }
     if (ypair)

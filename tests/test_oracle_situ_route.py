@@ -109,3 +109,98 @@ def test_logits_fixed_order_and_exactness():
     got = oracle.route_logits(xv, w[None, :])[0, 0]
     a0, a1, a2, a3 = float(np.float32(1e16)), 1.0, -float(np.float32(1e16)), 1.0
     assert got == ((a0 + a1) + (a2 + a3)) + 1.0
+
+
+# ---- K3_TOPP ("Kimi K3 engine (c/kimi_k3.c)", "Streaming design" and its table of
+# environment variables): keep the routed experts up to cumulative weight p,
+# drop the low-weight tail of the top-k, renormalise; p = 0 is off.
+
+def _logits_for(scores):
+    """Logits whose sigmoid is the given scores."""
+    s = np.asarray(scores, np.float64)
+    return np.log(s / (1.0 - s))[None, :]
+
+
+def _topp(logits, top_k, p, bias=None):
+    bias = np.zeros(logits.shape[1], np.float32) if bias is None else bias
+    idx, wts, _ = oracle.route_select(logits, bias, top_k)
+    return oracle.route_topp(idx, wts, logits, p)
+
+
+def test_topp_hand_example():
+    # scores 0.8, 0.6, 0.4, 0.2 selected (top 4 of 6): weights 0.4, 0.3, 0.2, 0.1
+    lg = _logits_for([0.8, 0.6, 0.4, 0.2, 0.1, 0.05])
+    idx, wts = _topp(lg, 4, 0.5)  # 0.4 taken; 0.3 taken (0.4 < 0.5); 0.2 not (0.7 >= 0.5)
+    assert np.array_equal(idx[0], [0, 1, -1, -1])
+    assert np.allclose(wts[0], [4 / 7, 3 / 7, 0, 0], rtol=0, atol=1e-7)
+    idx, wts = _topp(lg, 4, 0.85)  # 0.9 before the last weight: it is dropped
+    assert np.array_equal(idx[0], [0, 1, 2, -1])
+    assert np.allclose(wts[0], [0.8 / 1.8, 0.6 / 1.8, 0.4 / 1.8, 0], rtol=0, atol=1e-7)
+    for p in (0.95, 1.0, 0.0):  # everything kept: the weights are the top-k ones
+        idx, wts = _topp(lg, 4, p)
+        assert np.array_equal(idx[0], [0, 1, 2, 3])
+        assert np.allclose(wts[0], [0.4, 0.3, 0.2, 0.1], rtol=0, atol=1e-7)
+
+
+def test_topp_boundary_keeps_the_expert_that_reaches_p():
+    lg = _logits_for([0.8, 0.6, 0.4, 0.2, 0.1, 0.05])
+    w0 = 0.8 / (0.8 + 0.6 + 0.4 + 0.2)
+    idx, _ = _topp(lg, 4, w0 - 1e-9)  # p reached by the first expert alone
+    assert np.array_equal(idx[0], [0, -1, -1, -1])
+    idx, _ = _topp(lg, 4, w0 + 1e-9)  # the second expert is needed to reach p
+    assert np.array_equal(idx[0], [0, 1, -1, -1])
+
+
+def test_topp_order_is_by_weight_with_ties_in_route_order():
+    # experts 0 and 1 have equal scores (equal weights); the bias puts expert 1
+    # ahead of expert 0 in the route, and expert 2 (largest weight) behind both
+    lg = _logits_for([0.3, 0.3, 0.4, 0.01])
+    bias = np.array([0.0, 0.05, -0.2, 0.0], np.float32)
+    idx, wts, _ = oracle.route_select(lg, bias, 3)
+    assert np.array_equal(idx[0], [1, 0, 2])  # route order: biased score
+    t_idx, t_wts = oracle.route_topp(idx, wts, lg, 0.4 + 1e-9)
+    # by weight: expert 2 (0.4) first; then the tie 1, 0 in route order: 1 is taken
+    assert np.array_equal(t_idx[0], [1, -1, 2])
+    assert np.allclose(t_wts[0], [0.3 / 0.7, 0, 0.4 / 0.7], rtol=0, atol=1e-7)
+
+
+def test_topp_invariants_on_random_routings():
+    W, b = synth.router(33, 896, 512, 0.1)
+    x = synth.activations(33, 40, 512)
+    lg = oracle.route_logits(x, W)
+    idx, wts, _ = oracle.route_select(lg, b, 16)
+    sig = 1.0 / (1.0 + np.exp(-lg))
+    rng = np.random.default_rng(33)
+    for p in rng.uniform(0.05, 0.99, 6):
+        t_idx, t_wts = oracle.route_topp(idx, wts, lg, p)
+        for t in range(x.shape[0]):
+            w = sig[t, idx[t]] / sig[t, idx[t]].sum()
+            kept = t_idx[t] >= 0
+            assert np.all(t_idx[t][kept] == idx[t][kept])  # kept entries stay in place
+            assert np.all(t_wts[t][~kept] == 0)
+            # the kept set is a prefix of the weight order (ties: route order) ...
+            order = np.lexsort((np.arange(16), -w))
+            n = kept.sum()
+            assert set(order[:n]) == set(np.flatnonzero(kept))
+            # ... the shortest one that reaches p
+            cum = np.cumsum(w[order])
+            assert n == 16 or cum[n - 1] >= p - 1e-12
+            assert n == 1 or cum[n - 2] < p + 1e-12
+            # renormalised over the kept experts
+            assert abs(t_wts[t][kept].sum() - 1.0) < 1e-6
+            assert np.allclose(t_wts[t][kept], w[kept] / w[kept].sum(), rtol=2e-7, atol=0)
+
+
+def test_layer_skips_dropped_pairs():
+    # a dropped pair (idx -1) adds nothing: the same as a kept expert with weight 0
+    from tests.helpers import ExpertSource
+    E, latent, inter = 5, 64, 64
+    src = ExpertSource(35, latent, inter, 120, 123, 0.0)
+    ex = {e: src(e) for e in range(E)}
+    x = synth.activations(35, 3, latent)
+    idx = np.array([[0, -1, 2], [-1, -1, 4], [1, 3, -1]], np.int32)
+    wts = np.array([[0.6, 0.0, 0.4], [0.0, 0.0, 1.0], [0.5, 0.5, 0.0]], np.float32)
+    y = oracle.moe_layer(x, idx, wts, ex, E)
+    idx0 = np.where(idx < 0, 0, idx).astype(np.int32)
+    y0 = oracle.moe_layer(x, idx0, wts, ex, E)
+    assert np.array_equal(y, y0)
