@@ -222,13 +222,30 @@ int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_route
                   const float *bias, int n_tokens, int in, int n_experts, int top_k,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* The same routing with K3_TOPP ([COLIBRI-K3] "Streaming design" and its table
+ * of environment variables: keep routed experts up to cumulative weight p,
+ * drop the low-weight tail of the top-k, renormalise). This library's reading
+ * of the steps the pages leave open: the top_k entries are ranked by weight,
+ * largest first, equal weights in selection order; an entry is kept while the
+ * weight ranked before it (summed in rank order, double) is below top_p, so
+ * the entry that reaches top_p is kept; kept weights are the kept raw scores
+ * renormalised over the kept set. idx and wts keep their [T][top_k] shape and
+ * route order: a dropped entry is idx -1, wts 0 (k3g_moe_layer skips it, so
+ * its expert is never read). top_p = 0 is k3g_moe_route; top_p outside
+ * [0, 1] or NaN -> K3G_EINVAL. Same workspace as k3g_moe_route. */
+int k3g_moe_route_topp(int32_t *idx, float *wts, const float *x, const float *w_router,
+                       const float *bias, int n_tokens, int in, int n_experts, int top_k,
+                       float top_p, void *ws, size_t ws_bytes, void *stream);
+
 /* The MoE layer for given routing: y[t] = sum_k wts[t][k] * E_{idx[t][k]}(x_t)
  * with each expert a SiTU-GLU. Pairs are sorted by expert id so each selected
  * expert's weights stream from HBM once for all of its tokens ([COLIBRI-K3]
  * "Chunked prefill": each unique expert of a chunk is loaded once); the
  * weighted combine runs in k order per token. y, x fp32 [T][latent]; idx,
- * wts [T][top_k] as k3g_moe_route writes them. Precondition: idx values in
- * [0, bank->n_experts) (not checked on the device). */
+ * wts [T][top_k] as k3g_moe_route or k3g_moe_route_topp writes them: an idx
+ * of -1 is a dropped entry and adds nothing (its expert is not read).
+ * Precondition: every other idx value in [0, bank->n_experts) (not checked on
+ * the device; the kernels drop any id outside it as they drop -1). */
 int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts,
                   const k3g_expert_bank *bank, int n_tokens, int top_k, int mode,
                   void *ws, size_t ws_bytes, void *stream);

@@ -97,6 +97,7 @@ def lib():
         L.k3g_mxfp4_gemv_lut.argtypes = [P, P, P, P, i, i, i, P]
         L.k3g_expert_glu.argtypes = [P, P, P, i, P, sz, P]
         L.k3g_moe_route.argtypes = [P, P, P, P, P, i, i, i, i, P, sz, P]
+        L.k3g_moe_route_topp.argtypes = [P, P, P, P, P, i, i, i, i, C.c_float, P, sz, P]
         L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
         L.k3g_moe_layer_stage.argtypes = [i, P, P, P, P, P, i, i, i, P, sz, P]
         L.k3g_latent_moe_block.argtypes = [P, P, P, i, i, i, P, sz, P]
@@ -235,6 +236,25 @@ def k3g_moe_route(idx: torch.Tensor, wts: torch.Tensor, x: torch.Tensor, w_route
         raise ValueError("shape mismatch")
     _check("k3g_moe_route", lib().k3g_moe_route(_ptr(idx), _ptr(wts), _ptr(x), _ptr(w_router), _ptr(bias),
                                                  T, n_in, E, top_k, _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, wts
+
+
+def k3g_moe_route_topp(idx: torch.Tensor, wts: torch.Tensor, x: torch.Tensor, w_router: torch.Tensor,
+                       bias: torch.Tensor, top_k: int, top_p: float, ws: torch.Tensor, stream=None):
+    """k3g_moe_route with the K3_TOPP cut (dropped entries idx -1, wts 0)."""
+    _dev(idx, torch.int32, "idx")
+    _dev(wts, torch.float32, "wts")
+    _dev(x, torch.float32, "x")
+    _dev(w_router, torch.float32, "w_router")
+    _dev(bias, torch.float32, "bias")
+    _dev(ws, torch.uint8, "ws")
+    T, n_in = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != n_in or bias.numel() != E or idx.shape != (T, top_k) or wts.shape != (T, top_k):
+        raise ValueError("shape mismatch")
+    _check("k3g_moe_route_topp",
+           lib().k3g_moe_route_topp(_ptr(idx), _ptr(wts), _ptr(x), _ptr(w_router), _ptr(bias), T, n_in, E, top_k,
+                                    C.c_float(top_p), _ptr(ws), ws.numel(), _stream(stream)))
     return idx, wts
 
 

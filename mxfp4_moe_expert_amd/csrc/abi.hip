@@ -19,7 +19,8 @@ int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, con
 int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
                    int latent, hipStream_t st);
 int launch_logits(double *logits, const float *x, const float *W, int T, int in, int E, hipStream_t st);
-int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K, hipStream_t st);
+int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K,
+                double top_p, hipStream_t st);
 int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
                   int T, int K, int E, hipStream_t st);
 int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, uint16_t *qb, hipStream_t st);
@@ -348,7 +349,15 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
 
 int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_router, const float *bias, int n_tokens,
                   int in, int n_experts, int top_k, void *ws, size_t ws_bytes, void *stream) {
+    return k3g_moe_route_topp(idx, wts, x, w_router, bias, n_tokens, in, n_experts, top_k, 0.0f, ws, ws_bytes,
+                              stream);
+}
+
+int k3g_moe_route_topp(int32_t *idx, float *wts, const float *x, const float *w_router, const float *bias,
+                       int n_tokens, int in, int n_experts, int top_k, float top_p, void *ws, size_t ws_bytes,
+                       void *stream) {
     if (!idx || !wts || !x || !w_router || !bias || !ws) return K3G_EINVAL;
+    if (!(top_p >= 0.0f && top_p <= 1.0f)) return K3G_EINVAL;  // NaN too
     if (n_tokens < 0 || in <= 0 || n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > kMaxTopK ||
         top_k > n_experts)
         return K3G_EINVAL;
@@ -362,7 +371,7 @@ int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_route
     double *logits = (double *)((char *)ws + L.logits);
     hipStream_t st = S(stream);
     K3G_TRY(launch_logits(logits, x, w_router, n_tokens, in, n_experts, st));
-    return launch_topk(idx, wts, logits, bias, n_tokens, n_experts, top_k, st);
+    return launch_topk(idx, wts, logits, bias, n_tokens, n_experts, top_k, (double)top_p, st);
 }
 
 static int layer_prepare(k3g_ws_layout *L, const float *y, const float *x, const int32_t *idx, const float *wts,
@@ -490,7 +499,7 @@ extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_
     hipStream_t st = S(stream);
     // routing on the hidden state
     K3G_TRY(launch_logits(logits, x, w->w_router, T, hidden, E, st));
-    K3G_TRY(launch_topk(idx, wts, logits, w->bias, T, E, top_k, st));
+    K3G_TRY(launch_topk(idx, wts, logits, w->bias, T, E, top_k, 0.0, st));
     // down-projection into the latent space
     const DenseSeg down = {w->w_down, x, hidden};
     K3G_TRY(launch_dense(lat, &down, 1, T, latent, st));

@@ -229,13 +229,56 @@ __device__ inline void cex(double (&v)[NV], int (&id)[NV], int a, int b) {
     id[b] = sw ? ia : ib;
 }
 
+__device__ inline double readlane_f64(double v, int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+// One token's routing from its winners: lane k < K holds entry k (selection
+// order) with its expert id and raw score. The weights are the raw scores
+// renormalised over the selection (summed in selection order). With top_p > 0,
+// K3_TOPP ("Kimi K3 engine (c/kimi_k3.c)", "Streaming design" and its table of
+// environment variables): the entries are ranked by weight, largest first,
+// equal weights in selection order; an entry is kept while the weight ranked
+// before it (summed in rank order, double) is below top_p, so the entry that
+// reaches top_p is kept; a dropped entry is written as idx -1, wts 0 and the
+// kept weights are renormalised over the kept raw scores.
+__device__ inline void write_routing(int32_t *idx, float *wts, int my_id, double my_sc, int K, int lane,
+                                     double top_p) {
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += readlane_f64(my_sc, k);
+    bool keep = true;
+    if (top_p > 0.0) {
+        const double w = my_sc / sum;
+        int rank = 0;
+        for (int j = 0; j < K; ++j) {
+            const double wj = readlane_f64(w, j);
+            rank += (wj > w || (wj == w && j < lane)) ? 1 : 0;
+        }
+        double before = 0.0, mine = 0.0;
+        for (int r = 0; r < K; ++r) {
+            const uint64_t m = __ballot(lane < K && rank == r);
+            const int L = __builtin_amdgcn_readfirstlane(m ? __builtin_ctzll(m) : 0);
+            mine = lane == L ? before : mine;
+            before += readlane_f64(w, L);
+        }
+        keep = mine < top_p;
+    }
+    double kept = 0.0;
+    for (int k = 0; k < K; ++k) kept += readlane_f64(keep ? my_sc : 0.0, k);
+    if (lane < K) {
+        idx[lane] = keep ? my_id : -1;
+        wts[lane] = keep ? (float)(my_sc / kept) : 0.0f;
+    }
+}
+
 // Each lane first sorts its NV candidates (a bitonic network over register
 // slots, all indices compile-time); then every round the lanes' heads compete
 // and the winning lane shifts its list by one. No per-round scan, no LDS.
 template <int NV>
 __global__ __launch_bounds__(64) void topk_kernel(int32_t *__restrict__ idx, float *__restrict__ wts,
                                                   const double *__restrict__ logits, const float *__restrict__ bias,
-                                                  int T, int E, int K) {
+                                                  int T, int E, int K, double top_p) {
     const int lane = threadIdx.x;
     for (int t = blockIdx.x; t < T; t += gridDim.x) {
         const double *lg = logits + (size_t)t * E;
@@ -279,17 +322,9 @@ __global__ __launch_bounds__(64) void topk_kernel(int32_t *__restrict__ idx, flo
             v[NV - 1] = me ? -__builtin_inf() : v[NV - 1];
             id[NV - 1] = me ? 0x7fffffff : id[NV - 1];
         }
-        // weights: each lane's raw score (the value its key was built from),
-        // summed in selection order, then renormalised
+        // weights: each lane's raw score (the value its key was built from)
         const double my_sc = lane < K ? sigmoid64(lg[my_id]) : 0.0;
-        double sum = 0.0;
-        for (int k = 0; k < K; ++k)
-            sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_sc), k),
-                                    __builtin_amdgcn_readlane(__double2loint(my_sc), k));
-        if (lane < K) {
-            idx[(size_t)t * K + lane] = my_id;
-            wts[(size_t)t * K + lane] = (float)(my_sc / sum);
-        }
+        write_routing(idx + (size_t)t * K, wts + (size_t)t * K, my_id, my_sc, K, lane, top_p);
     }
 }
 
@@ -393,7 +428,7 @@ __global__ __launch_bounds__(TB_MAX_WAVES * 64) void topk_block_kernel(int32_t *
                                                                        float *__restrict__ wts,
                                                                        const double *__restrict__ logits,
                                                                        const float *__restrict__ bias, int T, int E,
-                                                                       int K) {
+                                                                       int K, double top_p) {
     __shared__ double sc_lds[TB_MAX_WAVES * 64];
     __shared__ double l1v[TB_MAX_WAVES * TB_LIST];
     __shared__ int l1i[TB_MAX_WAVES * TB_LIST];
@@ -439,16 +474,9 @@ __global__ __launch_bounds__(TB_MAX_WAVES * 64) void topk_block_kernel(int32_t *
             d.id = l2i[lane];
             merge4(d, lane, use4);
             const int my_id = d.id < E ? d.id : 0;  // not a real id only with non-finite scores
-            // weights: the raw scores of the winners, summed in selection order
+            // weights: the raw scores of the winners
             const double my_sc = lane < K ? sc_lds[my_id] : 0.0;
-            double sum = 0.0;
-            for (int k = 0; k < K; ++k)
-                sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_sc), k),
-                                        __builtin_amdgcn_readlane(__double2loint(my_sc), k));
-            if (lane < K) {
-                idx[(size_t)t * K + lane] = my_id;
-                wts[(size_t)t * K + lane] = (float)(my_sc / sum);
-            }
+            write_routing(idx + (size_t)t * K, wts + (size_t)t * K, my_id, my_sc, K, lane, top_p);
         }
         __syncthreads();  // the LDS lists are reused by the next token
     }
@@ -587,17 +615,17 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
 }
 
 int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K,
-                hipStream_t st) {
+                double top_p, hipStream_t st) {
     if (T == 0) return K3G_OK;
     const int blocks = T < 65536 ? T : 65536;
     const int nv = (E + kWave - 1) / kWave;
     if (K <= TB_LIST && nv <= TB_MAX_WAVES && T <= K3G_TOPK_BLOCK_MAX_T) {
         const int waves = nv < 4 ? 4 : nv;
-        topk_block_kernel<<<blocks, waves * kWave, 0, st>>>(idx, wts, logits, bias, T, E, K);
+        topk_block_kernel<<<blocks, waves * kWave, 0, st>>>(idx, wts, logits, bias, T, E, K, top_p);
     } else if (nv <= 16)
-        topk_kernel<16><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K);
+        topk_kernel<16><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K, top_p);
     else
-        topk_kernel<32><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K);
+        topk_kernel<32><<<blocks, 64, 0, st>>>(idx, wts, logits, bias, T, E, K, top_p);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

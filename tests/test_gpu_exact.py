@@ -216,12 +216,15 @@ def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0)
     offsets = ws_view(ws, L, "offsets", E + 1, np.int32)
     counts = ws_view(ws, L, "counts", E, np.int32)
     active = ws_view(ws, L, "active", E + 1, np.int32)
-    # bucket: exact, stable by token
-    pid = np.arange(P)
-    key = idx.ravel().astype(np.int64) * T + pid // K
-    assert np.array_equal(perm, pid[np.argsort(key, kind="stable")].astype(np.int32))
-    assert np.array_equal(inv[perm], pid.astype(np.int32))
-    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    # bucket: exact, stable by token; entries with idx -1 (dropped by K3_TOPP) are not pairs
+    flat = idx.ravel()
+    pid = np.flatnonzero(flat >= 0)
+    key = flat[pid].astype(np.int64) * T + pid // K
+    Pv = pid.size
+    assert np.array_equal(perm[:Pv], pid[np.argsort(key, kind="stable")].astype(np.int32))
+    assert np.array_equal(inv[perm[:Pv]], np.arange(Pv, dtype=np.int32))
+    assert np.all(inv[flat < 0] == -1)
+    assert np.array_equal(counts, np.bincount(flat[pid], minlength=E))
     assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
     assert active[0] == np.count_nonzero(counts)
     assert np.array_equal(active[1:1 + active[0]], np.flatnonzero(counts))
@@ -233,6 +236,8 @@ def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0)
         nrm_c = np.zeros(latent)
         for k in range(K):
             e = int(idx[t, k])
+            if e < 0:  # dropped: contributes nothing
+                continue
             ex = src(e)
             pos = inv[t * K + k]
             g, _, ng = oracle.mxfp4_gemv(x[t], ex["w1p"], ex["w1s"], full=True)
@@ -335,6 +340,65 @@ def test_layer_one_token_f4mma(k3g, case):
     for k in range(K):
         check_pieces(hp[k], h[k])
     check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=k3g.DECODE_MFMA)
+
+
+# ---- K3_TOPP ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,n_in,E,K", [(1, 3584, 896, 16), (8, 512, 896, 20), (3, 256, 2000, 16), (300, 512, 896, 16)],
+                         ids=["decode_block", "k20", "e2000", "t300"])
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_route_topp_matches_oracle(k3g, T, n_in, E, K, p):
+    W, b = synth.router(71, E, n_in, 0.1)
+    x = synth.activations(71, T, n_in)
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ws = k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=T, n_experts=E))
+    k3g.k3g_moe_route_topp(idx, wts, dev(x), dev(W), dev(b), K, p, ws)
+    io, wo, _ = oracle.route(x, W, b, K, top_p=p)
+    assert np.array_equal(host(idx), io)
+    assert np.allclose(host(wts), wo, rtol=1e-6, atol=0)
+    assert (io < 0).any()  # the cut dropped something
+    # p = 0: the plain routing, bit for bit
+    k3g.k3g_moe_route_topp(idx, wts, dev(x), dev(W), dev(b), K, 0.0, ws)
+    i0 = torch.empty_like(idx)
+    w0 = torch.empty_like(wts)
+    k3g.k3g_moe_route(i0, w0, dev(x), dev(W), dev(b), K, ws)
+    assert torch.equal(idx, i0) and torch.equal(wts, w0)
+
+
+def test_route_topp_rejects_bad_p(k3g):
+    idx = torch.empty((1, 4), dtype=torch.int32, device="cuda")
+    wts = torch.empty((1, 4), dtype=torch.float32, device="cuda")
+    x = torch.zeros((1, 64), dtype=torch.float32, device="cuda")
+    W = torch.zeros((16, 64), dtype=torch.float32, device="cuda")
+    b = torch.zeros(16, dtype=torch.float32, device="cuda")
+    ws = k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=1, n_experts=16))
+    for p in (-0.1, 1.5, float("nan")):
+        with pytest.raises(k3g.K3GError):
+            k3g.k3g_moe_route_topp(idx, wts, x, W, b, 4, p, ws)
+
+
+@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+def test_layer_decode_b1_topp(k3g, full_bank, decode):
+    # one token, top-16 cut at p = 0.7: only the kept experts are read and combined
+    src, bankt, bank = full_bank
+    W, b = synth.router(synth.SEED_BASE + 1, 896, 3584, 0.1)
+    x = synth.activations(synth.SEED_BASE + 1, 1, 3584)
+    io, wo, _ = oracle.route(x, W, b, 16, top_p=0.7)
+    assert 0 < (io < 0).sum() < 16
+    check_layer_exact(k3g, src, None, bank, x, io, wo, decode=decode)
+
+
+def test_layer_small_topp(k3g):
+    E, latent, inter, T, K = 12, 128, 96, 9, 4
+    src, bankt, bank = make_bank(k3g, 73, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(73, T, latent)
+    W, b = synth.router(73, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K, top_p=0.6)
+    assert (idx < 0).any()
+    y = check_layer_exact(k3g, src, bankt, bank, x, idx, wts)
+    yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.EXACT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
 def test_layer_decode_b64_full_sampled(k3g, full_bank):
