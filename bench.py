@@ -101,16 +101,17 @@ def main():
     if args.workload == "decode_b1" and not args.no_secondary:
         # the other configurations on the same resident bank, shorter runs (not the headline)
         others = []
-        for wl, steps, warm, bf16 in (("decode_b64", 20, 3, False), ("prefill_4096_idot", 10, 2, False),
-                                      ("prefill_4096_idot", 10, 2, True)):
-            r, _ = run_workload(ctx, wl, steps, warm, bf16)
+        for wl, steps, warm, bf16, p in (("decode_b1", 100, 10, False, 0.9), ("decode_b64", 20, 3, False, 0.0),
+                                         ("prefill_4096_idot", 10, 2, False, 0.0),
+                                         ("prefill_4096_idot", 10, 2, True, 0.0)):
+            r, _ = run_workload(ctx, wl, steps, warm, bf16, top_p=p)
             others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
                                              "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
     print(json.dumps(result), flush=True)
 
 
-def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False):
+def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top_p=0.0):
     """Measure one workload on the resident bank. Returns the result record and
     what the CPU baseline needs (the same inputs)."""
     torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
@@ -151,7 +152,10 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False):
 
     def stage(r, st, m=mode | form):
         if st is None:
-            k3g.k3g_moe_route(idx[r], wts[r], xs[r], Wd, bd, K, ws_r[r])
+            if top_p:
+                k3g.k3g_moe_route_topp(idx[r], wts[r], xs[r], Wd, bd, K, top_p, ws_r[r])
+            else:
+                k3g.k3g_moe_route(idx[r], wts[r], xs[r], Wd, bd, K, ws_r[r])
         else:
             if m not in ws_by_mode:  # another decode form: a workspace of its own size
                 shm = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=m)
@@ -235,18 +239,20 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False):
     timing = (f"step: {len(graphs) and 'HIP graph per step' or 'eager'} replay; stages: HIP events around a graph "
               f"of {n_rot} launches of the stage, {reps} replays")
 
-    # distinct experts per step (decode: always top_k; more tokens: counted from the routing)
+    # distinct experts per step (one token: top_k; more tokens, or a K3_TOPP cut:
+    # counted from the routing, dropped entries excluded)
     counts = None
-    if T > 1:
+    if T > 1 or top_p:
         cnt = []
         for r in range(n_rot):
-            cnt.append(len(np.unique(idx[r].cpu().numpy())))
+            ids = idx[r].cpu().numpy()
+            cnt.append(len(np.unique(ids[ids >= 0])))
         counts = float(np.mean(cnt))
-    n_exp = float(K) if T == 1 else counts
+    n_exp = float(K) if counts is None else counts
+    P = T * K if not top_p else int(sum(int((idx[r] >= 0).sum()) for r in range(n_rot)) / n_rot)
     up_b, dn_b = expert_bytes(L, I)
     router_b = E * L * 4 + E * 4
     alg_bytes = n_exp * (up_b + dn_b) + router_b + 2 * T * L * 4
-    P = T * K
     up_alg = n_exp * up_b + T * L * 4 + P * I * 4       # weights once, x in, h out
     if mode == k3g.IDOT:
         up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * 4
@@ -302,6 +308,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False):
             "experts": E, "top_k": K, "latent": L, "inter": I,
             "mode": mode_name + ("+bf16-mfma" if form == k3g.IDOT_BF16 else "+fp4-mfma" if form else ""),
             "distinct_experts_per_step": n_exp,
+            "top_p": top_p,
             "algorithmic_bytes_per_step": int(alg_bytes),
             "seed_bank": ctx["seed_bank"], "seed_workload": wl_seed,
         },
