@@ -287,6 +287,62 @@ int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w,
                          int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* ---- the routed-expert cache: host memory -> HBM (streaming tier) -------- */
+
+/* The pages stream experts from storage through an LRU of expert slots
+ * ([KIC-ARTICLE] "The cache the project exists for"; [COLIBRI-K3] "Streaming
+ * design"). Here the storage is host memory and the slots are an expert bank
+ * in HBM (`arena`, arena->n_experts slots, any layout k3g_moe_layer accepts):
+ * the cache rewrites a step's expert ids into slot ids, and k3g_moe_layer runs
+ * on the arena with them. Policy: LRU with pinning; a miss takes the first
+ * empty slot, else the least recently used slot that the step neither uses nor
+ * fills and whose expert is not pinned (linear scan, equal ages to the lower
+ * slot); slots taken by a step's prefetch are in flight (neither empty nor
+ * evictable) until their copies are issued; misses are fetched in ascending
+ * expert id (host-address) order; a request histogram per expert. All state
+ * is host-side; the object is not thread-safe. */
+typedef struct k3g_cache k3g_cache;
+
+typedef struct {
+    uint64_t steps, hits, misses, evictions, bytes_copied;
+} k3g_cache_stats;
+
+/* host_bank: host pointer (pinned memory copies fastest) holding n_total
+ * experts at host_bank + e*arena->stride, each laid out as in the arena
+ * (may be NULL for plan-only use); the arena's tensors must stay valid while
+ * the cache lives. */
+int k3g_cache_create(k3g_cache **out, const uint8_t *host_bank, int32_t n_total,
+                     const k3g_expert_bank *arena);
+void k3g_cache_destroy(k3g_cache *c);
+
+/* Pin (1) or unpin (0) an expert: a pinned expert, once loaded, is never
+ * evicted. */
+int k3g_cache_pin(k3g_cache *c, int32_t expert, int pinned);
+
+/* The policy alone (host pointers, no device work): for one step's routing
+ * idx [T][top_k] (-1 = dropped entry) writes idx_slot [T][top_k] (slot ids,
+ * -1 kept) and the copies the step needs, copy_expert/copy_slot [<= n_slots]
+ * (may be NULL), *n_copies. The new slots stay in flight until
+ * k3g_cache_complete (or the next plan). K3G_ENOSPACE, with nothing changed,
+ * when the step's experts do not fit the unpinned slots. */
+int k3g_cache_plan(k3g_cache *c, int32_t *idx_slot, int32_t *copy_expert, int32_t *copy_slot,
+                   int32_t *n_copies, const int32_t *idx, int n_tokens, int top_k);
+int k3g_cache_complete(k3g_cache *c);
+
+/* Plan one step and enqueue it: idx is the step's routing on the host,
+ * idx_slot a device int32 [T][top_k] that receives the slot ids. The copies
+ * (one hipMemcpyAsync of arena->stride bytes per missing expert, then idx_slot)
+ * go on copy_stream after everything already on `stream`; `stream` then waits
+ * for them, so a k3g_moe_layer enqueued next on `stream` with idx_slot and the
+ * arena sees the step's experts. Pinned host staging is allocated on first use
+ * and kept by the cache. */
+int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n_tokens, int top_k,
+                      void *copy_stream, void *stream);
+
+/* Counters, and optionally the expert -> slot map (int32 [n_total], -1 = not
+ * resident) and the request histogram (uint64 [n_total]). */
+int k3g_cache_query(const k3g_cache *c, k3g_cache_stats *stats, int32_t *slot_of, uint64_t *hist);
+
 /* ---- stage hooks used by the bit-exact checks ----------------------------- */
 
 /* Per row and 32-group: s = max|x|/127 (fp32), q = rint(x/s) clamped to

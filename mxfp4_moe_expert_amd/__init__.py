@@ -97,6 +97,14 @@ def lib():
         L.k3g_mxfp4_gemv_lut.argtypes = [P, P, P, P, i, i, i, P]
         L.k3g_expert_glu.argtypes = [P, P, P, i, P, sz, P]
         L.k3g_moe_route.argtypes = [P, P, P, P, P, i, i, i, i, P, sz, P]
+        L.k3g_cache_create.argtypes = [P, P, i, P]
+        L.k3g_cache_destroy.argtypes = [P]
+        L.k3g_cache_destroy.restype = None
+        L.k3g_cache_pin.argtypes = [P, i, i]
+        L.k3g_cache_plan.argtypes = [P, P, P, P, P, P, i, i]
+        L.k3g_cache_complete.argtypes = [P]
+        L.k3g_cache_prepare.argtypes = [P, P, P, i, i, P, P]
+        L.k3g_cache_query.argtypes = [P, P, P, P]
         L.k3g_moe_route_topp.argtypes = [P, P, P, P, P, i, i, i, i, C.c_float, P, sz, P]
         L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
         L.k3g_moe_layer_stage.argtypes = [i, P, P, P, P, P, i, i, i, P, sz, P]
@@ -382,3 +390,80 @@ def pack_bank(experts, n_experts: int, latent: int, inter: int, device="cuda", t
     dev = host.to(device, non_blocking=False)
     del host
     return dev, bank_struct(dev, n_experts, latent, inter, off, stride)
+
+
+# ---- the routed-expert cache (host memory -> HBM) -----------------------------------
+
+class CacheStats(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in ("steps", "hits", "misses", "evictions", "bytes_copied")]
+
+
+class ExpertCache:
+    """k3g_cache: an LRU of expert slots in HBM (`arena`, an ExpertBank of the
+    slots) fed from `host_bank` (a host uint8 tensor of n_total experts laid out
+    with the arena's stride; pinned copies fastest; None for plan-only use)."""
+
+    def __init__(self, host_bank, n_total: int, arena):
+        self._keep = (host_bank, arena)
+        ptr = C.c_void_p()
+        hp = None if host_bank is None else C.c_void_p(host_bank.data_ptr())
+        if host_bank is not None:
+            if host_bank.device.type != "cpu" or host_bank.dtype != torch.uint8 or not host_bank.is_contiguous():
+                raise ValueError("host_bank must be a contiguous host uint8 tensor")
+            if host_bank.numel() < n_total * arena.stride:
+                raise ValueError("host_bank is smaller than n_total experts")
+        _check("k3g_cache_create", lib().k3g_cache_create(C.byref(ptr), hp, n_total, C.byref(arena)))
+        self._c = ptr
+        self.n_total = n_total
+        self.n_slots = arena.n_experts
+
+    def close(self):
+        if self._c:
+            lib().k3g_cache_destroy(self._c)
+            self._c = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pin(self, expert: int, pinned: bool = True):
+        _check("k3g_cache_pin", lib().k3g_cache_pin(self._c, expert, 1 if pinned else 0))
+
+    def plan(self, idx):
+        """The policy on host int32 idx [T][top_k]: returns (idx_slot, copies [(expert, slot)])."""
+        import numpy as np
+        idx = np.ascontiguousarray(np.atleast_2d(idx), dtype=np.int32)
+        T, K = idx.shape
+        out = np.empty_like(idx)
+        ce = np.empty(self.n_slots, np.int32)
+        cs = np.empty(self.n_slots, np.int32)
+        n = C.c_int32()
+        _check("k3g_cache_plan", lib().k3g_cache_plan(self._c, out.ctypes.data, ce.ctypes.data, cs.ctypes.data,
+                                                       C.byref(n), idx.ctypes.data, T, K))
+        return out, list(zip(ce[:n.value].tolist(), cs[:n.value].tolist()))
+
+    def complete(self):
+        _check("k3g_cache_complete", lib().k3g_cache_complete(self._c))
+
+    def prepare(self, idx_slot: torch.Tensor, idx, copy_stream, stream=None):
+        """Plan one step (host idx) and enqueue its copies on copy_stream;
+        `stream` waits for them. idx_slot: device int32 [T][top_k]."""
+        import numpy as np
+        _dev(idx_slot, torch.int32, "idx_slot")
+        idx = np.ascontiguousarray(np.atleast_2d(idx), dtype=np.int32)
+        T, K = idx.shape
+        if tuple(idx_slot.shape) != (T, K):
+            raise ValueError("shape mismatch")
+        _check("k3g_cache_prepare", lib().k3g_cache_prepare(self._c, _ptr(idx_slot), idx.ctypes.data, T, K,
+                                                             C.c_void_p(copy_stream.cuda_stream), _stream(stream)))
+
+    def query(self):
+        """(stats dict, slot_of numpy int32 [n_total], histogram numpy uint64 [n_total])."""
+        import numpy as np
+        st = CacheStats()
+        so = np.empty(self.n_total, np.int32)
+        hi = np.empty(self.n_total, np.uint64)
+        _check("k3g_cache_query", lib().k3g_cache_query(self._c, C.byref(st), so.ctypes.data, hi.ctypes.data))
+        return {n: getattr(st, n) for n, _ in CacheStats._fields_}, so, hi

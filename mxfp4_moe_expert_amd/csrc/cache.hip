@@ -1,0 +1,223 @@
+// cache.hip -- the routed-expert cache in HBM, fed from host memory.
+//
+// The pages stream experts from storage through an LRU of expert slots
+// ("kimi-k3-in-c: 2.78 trillion parameters, one CPU, 8 GB of RAM", section
+// "The cache the project exists for"; "Kimi K3 engine (c/kimi_k3.c)", section
+// "Streaming design"): LRU with pinning, a victim found by a plain linear scan,
+// a slot table of three states (an expert, empty, or in flight -- reserved by
+// a batch prefetch whose read has not finished, so that one batch never hands
+// the same slot to two reads), a request histogram for choosing what to pin,
+// and a token's misses read as one batch in storage order, overlapped with
+// compute. Here the storage is host memory (ideally pinned) and the slots are
+// an expert bank in HBM: the cache rewrites a step's expert ids into slot ids,
+// so the layer runs unchanged on the slot bank. All state is host-side; the
+// copies go out on the caller's copy stream as hipMemcpyAsync, one per
+// missing expert (six tensors back to back = one copy), in host-address order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "k3g.h"
+
+namespace {
+
+constexpr int32_t kEmpty = -1;     // slot holds nothing, free to take
+constexpr int32_t kInflight = -2;  // slot reserved by this batch's prefetch
+
+}  // namespace
+
+struct k3g_cache {
+    const uint8_t *host_bank = nullptr;
+    int32_t n_total = 0;
+    k3g_expert_bank arena{};
+    int32_t n_slots = 0;
+    std::vector<int32_t> slot_key;   // per slot: expert id, kEmpty or kInflight
+    std::vector<int32_t> incoming;   // per slot in flight: the expert it receives
+    std::vector<int64_t> last_use;   // per slot: step of its last use
+    std::vector<int32_t> slot_of;    // per expert: its slot, or -1
+    std::vector<uint8_t> pinned;     // per expert
+    std::vector<uint64_t> hist;      // per expert: requests seen
+    std::vector<int32_t> step_copies_e, step_copies_s;
+    int64_t tick = 0;
+    k3g_cache_stats stats{};
+    hipEvent_t ev_prev = nullptr, ev_copy = nullptr;
+    int32_t *idx_stage = nullptr;    // pinned host staging of the rewritten ids
+    size_t idx_stage_n = 0;
+};
+
+extern "C" {
+
+int k3g_cache_create(k3g_cache **out, const uint8_t *host_bank, int32_t n_total, const k3g_expert_bank *arena) {
+    if (!out || !arena || n_total < 1 || arena->n_experts < 1 || arena->stride <= 0) return K3G_EINVAL;
+    k3g_cache *c = new (std::nothrow) k3g_cache;
+    if (!c) return K3G_ENOSPACE;
+    c->host_bank = host_bank;
+    c->n_total = n_total;
+    c->arena = *arena;
+    c->n_slots = arena->n_experts;
+    c->slot_key.assign(c->n_slots, kEmpty);
+    c->incoming.assign(c->n_slots, -1);
+    c->last_use.assign(c->n_slots, -1);
+    c->slot_of.assign(n_total, -1);
+    c->pinned.assign(n_total, 0);
+    c->hist.assign(n_total, 0);
+    *out = c;
+    return K3G_OK;
+}
+
+void k3g_cache_destroy(k3g_cache *c) {
+    if (!c) return;
+    if (c->ev_prev) (void)hipEventDestroy(c->ev_prev);
+    if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+    if (c->idx_stage) (void)hipHostFree(c->idx_stage);
+    delete c;
+}
+
+int k3g_cache_pin(k3g_cache *c, int32_t expert, int pinned) {
+    if (!c || expert < 0 || expert >= c->n_total) return K3G_EINVAL;
+    c->pinned[expert] = pinned ? 1 : 0;
+    return K3G_OK;
+}
+
+int k3g_cache_plan(k3g_cache *c, int32_t *idx_slot, int32_t *copy_expert, int32_t *copy_slot, int32_t *n_copies,
+                   const int32_t *idx, int n_tokens, int top_k) {
+    if (!c || !n_copies || n_tokens < 0 || top_k < 1 || (n_tokens > 0 && (!idx || !idx_slot))) return K3G_EINVAL;
+    // the previous batch's slots are filled by now (its copies were ordered
+    // before the work that used them)
+    (void)k3g_cache_complete(c);
+    const int64_t P = (int64_t)n_tokens * top_k;
+    for (int64_t p = 0; p < P; ++p)
+        if (idx[p] < -1 || idx[p] >= c->n_total) return K3G_EINVAL;
+    // the step's distinct experts (ids ascending = host-address order)
+    std::vector<int32_t> want;
+    want.reserve((size_t)std::min<int64_t>(P, c->n_total));
+    for (int64_t p = 0; p < P; ++p)
+        if (idx[p] >= 0) want.push_back(idx[p]);
+    std::sort(want.begin(), want.end());
+    want.erase(std::unique(want.begin(), want.end()), want.end());
+    // the step must fit before anything changes: its misses need slots that are
+    // empty or hold an unpinned expert the step does not use
+    std::vector<uint8_t> in_use(c->n_slots, 0);
+    int32_t hits = 0;
+    for (int32_t e : want)
+        if (c->slot_of[e] >= 0) {
+            in_use[c->slot_of[e]] = 1;
+            ++hits;
+        }
+    int64_t free_slots = 0;
+    for (int32_t i = 0; i < c->n_slots; ++i) {
+        const int32_t k = c->slot_key[i];
+        free_slots += !in_use[i] && (k == kEmpty || (k >= 0 && !c->pinned[k]));
+    }
+    if ((int64_t)want.size() - hits > free_slots) return K3G_ENOSPACE;
+    ++c->tick;
+    for (int64_t p = 0; p < P; ++p)
+        if (idx[p] >= 0) ++c->hist[idx[p]];
+    // hits: refresh, and keep them out of this batch's victims
+    for (int32_t e : want)
+        if (c->slot_of[e] >= 0) c->last_use[c->slot_of[e]] = c->tick;
+    // misses, in host-address order: an empty slot if there is one, else the
+    // least recently used slot that this batch neither uses nor fills and
+    // whose expert is not pinned (a linear scan; equal ages: the lower slot)
+    int32_t nc = 0;
+    for (int32_t e : want) {
+        if (c->slot_of[e] >= 0) continue;
+        int32_t s = -1;
+        for (int32_t i = 0; i < c->n_slots && s < 0; ++i)
+            if (c->slot_key[i] == kEmpty) s = i;
+        if (s < 0)
+            for (int32_t i = 0; i < c->n_slots; ++i) {
+                const int32_t k = c->slot_key[i];
+                if (in_use[i] || k == kInflight || (k >= 0 && c->pinned[k])) continue;
+                if (s < 0 || c->last_use[i] < c->last_use[s]) s = i;
+            }
+        if (c->slot_key[s] >= 0) {
+            c->slot_of[c->slot_key[s]] = -1;
+            ++c->stats.evictions;
+        }
+        c->slot_key[s] = kInflight;
+        c->incoming[s] = e;
+        c->slot_of[e] = s;
+        c->last_use[s] = c->tick;
+        in_use[s] = 1;
+        if (copy_expert) copy_expert[nc] = e;
+        if (copy_slot) copy_slot[nc] = s;
+        ++nc;
+    }
+    for (int64_t p = 0; p < P; ++p) idx_slot[p] = idx[p] >= 0 ? c->slot_of[idx[p]] : -1;
+    *n_copies = nc;
+    c->stats.steps += 1;
+    c->stats.hits += hits;
+    c->stats.misses += nc;
+    c->stats.bytes_copied += (uint64_t)nc * (uint64_t)c->arena.stride;
+    return K3G_OK;
+}
+
+int k3g_cache_complete(k3g_cache *c) {
+    if (!c) return K3G_EINVAL;
+    for (int32_t s = 0; s < c->n_slots; ++s)
+        if (c->slot_key[s] == kInflight) {
+            c->slot_key[s] = c->incoming[s];
+            c->incoming[s] = -1;
+        }
+    return K3G_OK;
+}
+
+int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n_tokens, int top_k,
+                      void *copy_stream, void *stream) {
+    if (!c || !c->host_bank || n_tokens < 0 || top_k < 1) return K3G_EINVAL;
+    const size_t P = (size_t)n_tokens * top_k;
+    if (P == 0) return K3G_OK;
+    if (!idx || !idx_slot) return K3G_EINVAL;
+    if (!c->ev_prev) {
+        if (hipEventCreateWithFlags(&c->ev_prev, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming) != hipSuccess)
+            return K3G_EHIP;
+    }
+    // the staging buffer is reused: the previous step's copy of it must be done
+    if (c->ev_copy && hipEventSynchronize(c->ev_copy) != hipSuccess) return K3G_EHIP;
+    if (c->idx_stage_n < P) {
+        if (c->idx_stage) (void)hipHostFree(c->idx_stage);
+        c->idx_stage = nullptr;
+        c->idx_stage_n = 0;
+        if (hipHostMalloc((void **)&c->idx_stage, sizeof(int32_t) * P, hipHostMallocDefault) != hipSuccess)
+            return K3G_ENOSPACE;
+        c->idx_stage_n = P;
+    }
+    c->step_copies_e.resize((size_t)c->n_slots);
+    c->step_copies_s.resize((size_t)c->n_slots);
+    int32_t nc = 0;
+    const int rc = k3g_cache_plan(c, c->idx_stage, c->step_copies_e.data(), c->step_copies_s.data(), &nc, idx,
+                                  n_tokens, top_k);
+    if (rc != K3G_OK) return rc;
+    hipStream_t cs = (hipStream_t)copy_stream, st = (hipStream_t)stream;
+    // the slots about to be overwritten may still be read by work already on
+    // `stream`: the copies start after it
+    if (hipEventRecord(c->ev_prev, st) != hipSuccess || hipStreamWaitEvent(cs, c->ev_prev, 0) != hipSuccess)
+        return K3G_EHIP;
+    const size_t stride = (size_t)c->arena.stride;
+    for (int32_t i = 0; i < nc; ++i) {
+        const uint8_t *src = c->host_bank + (size_t)c->step_copies_e[i] * stride;
+        uint8_t *dst = const_cast<uint8_t *>(c->arena.base) + (size_t)c->step_copies_s[i] * stride;
+        if (hipMemcpyAsync(dst, src, stride, hipMemcpyHostToDevice, cs) != hipSuccess) return K3G_EHIP;
+    }
+    if (hipMemcpyAsync(idx_slot, c->idx_stage, sizeof(int32_t) * P, hipMemcpyHostToDevice, cs) != hipSuccess)
+        return K3G_EHIP;
+    if (hipEventRecord(c->ev_copy, cs) != hipSuccess || hipStreamWaitEvent(st, c->ev_copy, 0) != hipSuccess)
+        return K3G_EHIP;
+    return k3g_cache_complete(c);
+}
+
+int k3g_cache_query(const k3g_cache *c, k3g_cache_stats *stats, int32_t *slot_of, uint64_t *hist) {
+    if (!c) return K3G_EINVAL;
+    if (stats) *stats = c->stats;
+    if (slot_of) memcpy(slot_of, c->slot_of.data(), sizeof(int32_t) * c->n_total);
+    if (hist) memcpy(hist, c->hist.data(), sizeof(uint64_t) * c->n_total);
+    return K3G_OK;
+}
+
+}  // extern "C"

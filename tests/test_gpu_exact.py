@@ -409,3 +409,80 @@ def test_layer_decode_b64_full_sampled(k3g, full_bank):
     io, wo, _ = oracle.route(x, W, b, 16)
     # sampled outputs: three tokens checked pair by pair
     check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=[0, 31, 63])
+
+
+# ---- the routed-expert cache: host memory -> HBM ------------------------------------------
+
+def run_cached_steps(k3g, bankt, bank, n_slots, steps, mode=0):
+    """Each step's layer on the cache arena (experts copied from pinned host
+    memory on demand) against the same layer on the resident bank: the same
+    kernels on the same bytes, so y is equal bit for bit. Returns the cache's
+    counters and the policy oracle's."""
+    from oracle.cache import LruSlots
+
+    E, latent, inter = bank.n_experts, bank.latent, bank.inter
+    off, stride = k3g.bank_layout(latent, inter)
+    host = torch.empty(E * stride, dtype=torch.uint8, pin_memory=True)
+    host.copy_(bankt[:E * stride])
+    arena_t = torch.zeros(n_slots * stride, dtype=torch.uint8, device="cuda")
+    arena = k3g.bank_struct(arena_t, n_slots, latent, inter, off, stride)
+    cache = k3g.ExpertCache(host, E, arena)
+    ref = LruSlots(n_slots, E)
+    copy_stream = torch.cuda.Stream()
+    for x, idx, wts in steps:
+        T, K = idx.shape
+        y_full, _, _ = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | mode)
+        idx_slot = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        cache.prepare(idx_slot, idx, copy_stream)
+        want_slots, _ = ref.request(idx.tolist())
+        y_c, _, _ = run_layer_dev(k3g, x, idx_slot, wts, arena, k3g.EXACT | mode)
+        assert host_arr(idx_slot).tolist() == want_slots
+        assert np.array_equal(y_c, y_full)
+    stats, _, _ = cache.query()
+    cache.close()
+    return stats, ref
+
+
+def host_arr(t):
+    return t.cpu().numpy()
+
+
+def run_layer_dev(k3g, x, idx_dev, wts, bank, mode):
+    """run_layer with the routing already on the device."""
+    T = x.shape[0]
+    K = idx_dev.shape[1]
+    y = torch.empty((T, bank.latent), dtype=torch.float32, device="cuda")
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=bank.n_experts, latent=bank.latent, inter=bank.inter, mode=mode)
+    ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
+    k3g.k3g_moe_layer(y, dev(x), idx_dev, dev(wts), bank, mode, ws)
+    return host(y), ws, L
+
+
+def test_cache_layer_small(k3g):
+    E, latent, inter, T, K = 24, 256, 128, 3, 4
+    src, bankt, bank = make_bank(k3g, 81, E, latent, inter, 120, 123, 0.01)
+    W, b = synth.router(81, E, latent, 0.3)
+    steps = []
+    for r in range(12):
+        x = synth.activations(81, T, latent, key=r)
+        idx, wts, _ = oracle.route(x, W, b, K, top_p=0.8 if r % 3 == 2 else 0.0)
+        steps.append((x, idx, wts))
+    stats, ref = run_cached_steps(k3g, bankt, bank, 10, steps)
+    assert (stats["hits"], stats["misses"], stats["evictions"]) == (ref.hits, ref.misses, ref.evictions)
+    assert stats["evictions"] > 0 and stats["hits"] > 0
+
+
+@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+def test_cache_layer_decode_full(k3g, full_bank, decode):
+    # one token per step, 896 experts in host memory, 32 slots in HBM
+    src, bankt, bank = full_bank
+    W, b = synth.router(synth.SEED_BASE + 1, 896, 3584, 0.1)
+    steps = []
+    for r in range(6):
+        x = synth.activations(synth.SEED_BASE + 1, 1, 3584, key=r)
+        idx, wts, _ = oracle.route(x, W, b, 16)
+        steps.append((x, idx, wts))
+    steps.append(steps[0])  # a repeated token: all hits if its experts are still resident
+    stats, ref = run_cached_steps(k3g, bankt, bank, 32, steps, decode)
+    assert stats["misses"] == ref.misses and stats["bytes_copied"] == ref.misses * bank.stride
