@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true",
                     help="decode_b1 only: skip the short runs of the 64-token and 4096-token workloads")
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
+    ap.add_argument("--stream-steps", type=int, default=40,
+                    help="decode steps per cache size in the streaming-tier measurement")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only copy a GIB-sized buffer 5 times (a plain copy of known size, for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -108,6 +110,9 @@ def main():
             others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
                                              "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
+        # the expert streaming tier: the bank in pinned host memory, an LRU of slots in HBM
+        result["streaming_tier"] = run_stream(ctx, bankt, configs=((64, 0.1), (256, 0.1), (256, 0.01)),
+                                              steps=args.stream_steps)
     print(json.dumps(result), flush=True)
 
 
@@ -351,6 +356,79 @@ def measured_traffic(workload, kernel):
         return None
     k = doc["kernels"][kernel]
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def run_stream(ctx, bankt, configs, steps):
+    """Decode with the 896-expert bank in pinned host memory and an LRU of n
+    slots in HBM (k3g_cache): each step routes on the GPU, brings the 16 ids to
+    the host, plans, copies the misses host -> HBM on a copy stream and runs the
+    layer on the slots. configs: (slots, router bias range): 0.1 is the decode
+    workload's router (the bias makes some experts hot), 0.01 near-flat use
+    (the pages' trained router is balanced to flat use). Host clock around
+    `steps` steps after 8 warm-up steps; also the bare pinned host -> HBM copy
+    rate of one expert (17.5 MB) at a time."""
+    torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
+    L, I, E, K = synth.LATENT, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    off, stride = k3g.bank_layout(L, I)
+    host = torch.empty(E * stride, dtype=torch.uint8, pin_memory=True)
+    host.copy_(bankt[:E * stride])
+    wl_seed = synth.WORKLOADS["decode_b1"][0]
+    n_rot = 512
+    xs = [torch.from_numpy(synth.activations(wl_seed, 1, L, key=1000 + r)).to(dev) for r in range(n_rot)]
+    idx = torch.empty((1, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, K), dtype=torch.float32, device=dev)
+    idx_slot = torch.empty((1, K), dtype=torch.int32, device=dev)
+    y = torch.empty((1, L), dtype=torch.float32, device=dev)
+    ws_r = k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=1, n_experts=E))
+    copy_stream = torch.cuda.Stream()
+    # bare copy rate: one expert per copy, 64 copies
+    dst = torch.empty(stride, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(64):
+        dst.copy_(host[(i % E) * stride:(i % E + 1) * stride], non_blocking=True)
+    torch.cuda.synchronize()
+    bare = 64 * stride / (time.perf_counter() - t0) / 1e9
+    out = {"host_bank_bytes": E * stride, "bare_copy_GBps": round(bare, 2),
+           "pages_nvme_GBps": 6.3, "note": "host clock, steps include the idx round trip to the host"}
+    runs = []
+    for n_slots, bias_range in configs:
+        W, b = synth.router(wl_seed, E, L, bias_range)
+        Wd, bd = torch.from_numpy(W).to(dev), torch.from_numpy(b).to(dev)
+        arena_t = torch.empty(n_slots * stride, dtype=torch.uint8, device=dev)
+        arena = k3g.bank_struct(arena_t, n_slots, L, I, off, stride)
+        cache = k3g.ExpertCache(host, E, arena)
+        sh = k3g.shape(n_tokens=1, top_k=K, n_experts=n_slots, latent=L, inter=I, mode=k3g.EXACT)
+        ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+
+        def step(r):
+            k3g.k3g_moe_route(idx, wts, xs[r % n_rot], Wd, bd, K, ws_r)
+            cache.prepare(idx_slot, idx.cpu().numpy(), copy_stream)
+            k3g.k3g_moe_layer(y, xs[r % n_rot], idx_slot, wts, arena, k3g.EXACT, ws)
+
+        for r in range(8):
+            step(r)
+        torch.cuda.synchronize()
+        s0, _, _ = cache.query()
+        t0 = time.perf_counter()
+        for r in range(steps):
+            step(8 + r)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        s1, _, _ = cache.query()
+        copied = s1["bytes_copied"] - s0["bytes_copied"]
+        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+        runs.append({"slots": n_slots, "arena_GB": round(n_slots * stride / 1e9, 2), "router_bias_range": bias_range,
+                     "steps": steps,
+                     "ms_per_step": round(1e3 * dt / steps, 3), "tokens_per_s": round(steps / dt, 1),
+                     "hit_rate": round(hits / max(1, hits + misses), 4),
+                     "copy_GBps": round(copied / dt / 1e9, 2)})
+        cache.close()
+        del arena_t, ws
+        torch.cuda.empty_cache()
+    out["runs"] = runs
+    del host
+    return out
 
 
 def copy_calibration(torch, gib):
