@@ -110,6 +110,8 @@ def main():
             others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
                                              "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
+        # the Vulkan-tier scale format: the same product with f32 per-group scales
+        result["scale_format"] = run_scale_format(ctx)
         # the expert streaming tier: the bank in pinned host memory, an LRU of slots in HBM
         result["streaming_tier"] = run_stream(ctx, bankt, configs=((64, 0.1), (256, 0.1), (256, 0.01)),
                                               steps=args.stream_steps)
@@ -356,6 +358,50 @@ def measured_traffic(workload, kernel):
         return None
     k = doc["kernels"][kernel]
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def run_scale_format(ctx, n_mat=8, launches=64):
+    """The batch-1 product on 16 experts' w1+w3 stacked (49,152 x 3,584), with
+    ue8m0 scales and with the scales expanded to f32 at upload (the pages'
+    Vulkan-tier format): time per launch (HIP events around `launches`
+    launches cycling over n_mat distinct matrices, so no launch finds its
+    matrix in the Infinity Cache) and algorithmic bytes per second."""
+    torch, k3g, dev = ctx["torch"], ctx["k3g"], ctx["dev"]
+    rows, n_in = 16 * 3072, 3584
+    g = torch.Generator(device=dev).manual_seed(0x4B33)
+    pk = [torch.randint(0, 256, (rows, n_in // 2), dtype=torch.uint8, device=dev, generator=g) for _ in range(n_mat)]
+    s8 = [torch.randint(118, 133, (rows, n_in // 32), dtype=torch.uint8, device=dev, generator=g)
+          for _ in range(n_mat)]
+    s32 = [torch.empty((rows, n_in // 32), dtype=torch.float32, device=dev) for _ in range(n_mat)]
+    for a, b in zip(s8, s32):
+        k3g.k3g_mxfp4_scales_to_f32(b, a)
+    x = torch.randn(n_in, dtype=torch.float32, device=dev, generator=g)
+    ys = [torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for i in range(n_mat):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            fn(i % n_mat)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / launches
+
+    us8 = timed(lambda i: k3g.k3g_mxfp4_gemv(ys[0], x, pk[i], s8[i]))
+    us32 = timed(lambda i: k3g.k3g_mxfp4_gemv_f32s(ys[1], x, pk[i], s32[i]))
+    same = bool(torch.equal(ys[0], ys[1]))
+    b8 = rows * (n_in // 2 + n_in // 32) + 4 * (n_in + rows)
+    b32 = rows * (n_in // 2 + 4 * (n_in // 32)) + 4 * (n_in + rows)
+    out = {"matrix": f"{rows}x{n_in}", "ue8m0_us": round(us8, 2), "ue8m0_GBps": round(b8 / us8 / 1e3, 1),
+           "f32_us": round(us32, 2), "f32_GBps": round(b32 / us32 / 1e3, 1),
+           "bytes_ue8m0": b8, "bytes_f32": b32, "results_identical": same}
+    del pk, s8, s32, ys
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_stream(ctx, bankt, configs, steps):

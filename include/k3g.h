@@ -203,6 +203,21 @@ int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed,
 int k3g_mxfp4_gemv_lut(float *y, const float *x, const uint8_t *packed,
                        const uint8_t *scales, int in, int rows, int group, void *stream);
 
+/* The pages' Vulkan-tier format ([COLIBRI-K3] "Vulkan tier": e2m1 nibbles
+ * uploaded as stored, ue8m0 exponents expanded to f32 per-32-group scales at
+ * upload). k3g_mxfp4_scales_to_f32 expands n scale bytes: out = 2^(s-127)
+ * exactly (s = 0 gives the subnormal 2^-127), 255 (skip) gives 0; out fp32 [n],
+ * 4-byte aligned, not overlapping scales. k3g_mxfp4_gemv_f32s is
+ * k3g_mxfp4_gemv with such scales (fp32 [rows][in/32], 4-byte aligned): each
+ * group sum times its f32 scale. With finite x the results equal
+ * k3g_mxfp4_gemv's bit for bit (both scalings are exact powers of two); a
+ * skipped group contributes 0 * its sum, so a non-finite x in it propagates,
+ * where the ue8m0 form drops the group. The f32 scales cost 3 more bytes per
+ * group (20 instead of 17). */
+int k3g_mxfp4_scales_to_f32(float *out, const uint8_t *scales, int64_t n, void *stream);
+int k3g_mxfp4_gemv_f32s(float *y, const float *x, const uint8_t *packed, const float *scales,
+                        int in, int rows, int group, void *stream);
+
 /* One expert on one token: g = w1 x, u = w3 x, h = 4 tanh(g/4) sigmoid(g)
  * 25 tanh(u/25) (SiTU-GLU, [COLIBRI-K3] "Architecture notes"), y = w2 h.
  * y, x fp32 [latent], 16-byte aligned. In IDOT mode x and h are quantised per

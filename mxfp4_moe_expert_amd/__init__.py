@@ -97,6 +97,8 @@ def lib():
         L.k3g_mxfp4_gemv_lut.argtypes = [P, P, P, P, i, i, i, P]
         L.k3g_expert_glu.argtypes = [P, P, P, i, P, sz, P]
         L.k3g_moe_route.argtypes = [P, P, P, P, P, i, i, i, i, P, sz, P]
+        L.k3g_mxfp4_scales_to_f32.argtypes = [P, P, C.c_int64, P]
+        L.k3g_mxfp4_gemv_f32s.argtypes = [P, P, P, P, i, i, i, P]
         L.k3g_cache_create.argtypes = [P, P, i, P]
         L.k3g_cache_destroy.argtypes = [P]
         L.k3g_cache_destroy.restype = None
@@ -227,6 +229,33 @@ def k3g_expert_glu(y: torch.Tensor, x: torch.Tensor, ex: dict, mode: int, ws: to
     e = expert_struct(ex)
     _check("k3g_expert_glu", lib().k3g_expert_glu(_ptr(y), _ptr(x), C.byref(e), mode, _ptr(ws),
                                                    ws.numel(), _stream(stream)))
+    return y
+
+
+def k3g_mxfp4_scales_to_f32(out: torch.Tensor, scales: torch.Tensor, stream=None) -> torch.Tensor:
+    """ue8m0 scale bytes -> fp32 scales (255 -> 0), the pages' Vulkan-tier upload."""
+    _dev(out, torch.float32, "out")
+    _dev(scales, torch.uint8, "scales")
+    if out.numel() != scales.numel():
+        raise ValueError("shape mismatch")
+    _check("k3g_mxfp4_scales_to_f32", lib().k3g_mxfp4_scales_to_f32(_ptr(out), _ptr(scales), scales.numel(),
+                                                                     _stream(stream)))
+    return out
+
+
+def k3g_mxfp4_gemv_f32s(y: torch.Tensor, x: torch.Tensor, packed: torch.Tensor, scales_f32: torch.Tensor,
+                        stream=None) -> torch.Tensor:
+    """k3g_mxfp4_gemv with fp32 per-group scales [rows][in/32]."""
+    _dev(y, torch.float32, "y")
+    _dev(x, torch.float32, "x")
+    _dev(packed, torch.uint8, "packed")
+    _dev(scales_f32, torch.float32, "scales_f32")
+    rows, half = packed.shape
+    n_in = half * 2
+    if x.numel() != n_in or y.numel() != rows or tuple(scales_f32.shape) != (rows, n_in // 32):
+        raise ValueError("shape mismatch")
+    _check("k3g_mxfp4_gemv_f32s", lib().k3g_mxfp4_gemv_f32s(_ptr(y), _ptr(x), _ptr(packed), _ptr(scales_f32),
+                                                             n_in, rows, 32, _stream(stream)))
     return y
 
 

@@ -38,6 +38,9 @@ struct DenseSeg {
     int K;
 };
 int launch_dense(float *out, const DenseSeg *segs, int n_seg, int T, int N, hipStream_t st);
+int launch_scales_f32(float *out, const uint8_t *s, int64_t n, hipStream_t st);
+int launch_gemv_f32s(float *y, const float *x, const uint8_t *packed, const float *scales, int in, int rows,
+                     hipStream_t st);
 int launch_split(uint8_t *dst, const float *src, int n_vec, int len, int src_stride, hipStream_t st);
 int launch_moe_up_f4(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const Route1 &rt, int top_k,
                      int latent, int inter, int max_slots, hipStream_t st);
@@ -284,6 +287,26 @@ int k3g_mxfp4_gemv(float *y, const float *x, const uint8_t *packed, const uint8_
 int k3g_mxfp4_gemv_lut(float *y, const float *x, const uint8_t *packed, const uint8_t *scales, int in, int rows,
                        int group, void *stream) {
     return gemv_entry(y, x, packed, scales, in, rows, group, true, stream);
+}
+
+int k3g_mxfp4_scales_to_f32(float *out, const uint8_t *scales, int64_t n, void *stream) {
+    if (!out || !scales || n < 0) return K3G_EINVAL;
+    if (!aligned(out, 4)) return K3G_EALIGN;
+    if (n > 0 && overlap(out, sizeof(float) * (size_t)n, scales, (size_t)n)) return K3G_EINVAL;
+    K3G_TRY(check_device());
+    return launch_scales_f32(out, scales, n, S(stream));
+}
+
+int k3g_mxfp4_gemv_f32s(float *y, const float *x, const uint8_t *packed, const float *scales, int in, int rows,
+                        int group, void *stream) {
+    if (!y || !x || group != kGroup) return K3G_EINVAL;
+    K3G_TRY(mxfp4_ok(packed, (const uint8_t *)scales, in, rows));
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(scales, 4)) return K3G_EALIGN;
+    if (overlap(y, sizeof(float) * rows, x, sizeof(float) * in)) return K3G_EINVAL;
+    if ((int64_t)rows * (in / 2) >= ((int64_t)1 << 31) || (int64_t)rows * (in / kGroup) * 4 >= ((int64_t)1 << 31))
+        return K3G_EUNSUPPORTED;  // 32-bit buffer offsets
+    K3G_TRY(check_device());
+    return launch_gemv_f32s(y, x, packed, scales, in, rows, S(stream));
 }
 
 int k3g_quantize_i8_groups(int8_t *q, float *s, const float *x, int n_rows, int in, void *stream) {

@@ -92,12 +92,18 @@ __device__ inline MatRef mat_ref(const uint8_t *packed, const uint8_t *scales, i
     return m;
 }
 
-template <int NG, bool SC2 = false>
+// F32S: the scales are fp32 per group (expanded at upload; m.pitch_s in bytes
+// is 4 * groups), d.s holds their bits.
+template <int NG, bool SC2 = false, bool F32S = false>
 __device__ inline void load_row(RowData<NG> &d, const MatRef &m, int r, const LaneCols<NG> &c) {
     const uint32_t op = (uint32_t)r * m.pitch_p, os = (uint32_t)r * m.pitch_s;
 #pragma unroll
     for (int i = 0; i < NG; ++i) d.w[i] = buf_load16(m.p, c.pk[i], op);
-    if constexpr (NG == 2 && SC2) {
+    if constexpr (F32S) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i)
+            d.s[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(m.s, (int)(4u * c.sc[i]), (int)os, 0);
+    } else if constexpr (NG == 2 && SC2) {
         const uint32_t v = buf_load_u16(m.s, c.sc2, os);
         d.s[0] = v & 0xFFu;
         d.s[NG - 1] = v >> 8;
@@ -108,7 +114,7 @@ __device__ inline void load_row(RowData<NG> &d, const MatRef &m, int r, const La
 }
 
 // Decode: LUT = the byte-pair table in LDS; otherwise gfx950's FP4 convert.
-template <int NG, bool LUT>
+template <int NG, bool LUT, bool F32S = false>
 __device__ inline float row_partial(const RowData<NG> &d, const uint32_t *lut, uint32_t lane_off, const float *xr,
                                    uint32_t valid) {
     float p = 0.f;
@@ -126,7 +132,8 @@ __device__ inline float row_partial(const RowData<NG> &d, const uint32_t *lut, u
         // select here would be turned into a branch around the whole group,
         // and the branches would cost the loads of the rows in flight
         const uint32_t keep = 0u - ((valid >> i) & 1u);
-        p += __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, apply_scale(sub, d.s[i])) & keep);
+        const float scaled = F32S ? sub * __builtin_bit_cast(float, d.s[i]) : apply_scale(sub, d.s[i]);
+        p += __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, scaled) & keep);
     }
     return p;
 }
@@ -160,8 +167,9 @@ __device__ inline void load_x(float *xr, const float *x, int lane, int ngrp) {
     }
 }
 
-// y[r] for r in [0, rows): one matrix, one x. Items of rpi rows.
-template <int NG, bool LUT>
+// y[r] for r in [0, rows): one matrix, one x. Items of rpi rows. F32S: the
+// scales are fp32 per group (the pages' Vulkan-tier format).
+template <int NG, bool LUT, bool F32S = false>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *__restrict__ y, const float *__restrict__ x,
                                                    const uint8_t *__restrict__ packed,
                                                    const uint8_t *__restrict__ scales, int in, int rows, int rpi) {
@@ -179,7 +187,11 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
     const int ngrp = in / kGroup;
     const uint32_t valid = valid_groups<NG>(lane, ngrp);
     const LaneCols<NG> cols = lane_cols<NG>(lane, ngrp);
-    const MatRef mat = mat_ref(packed, scales, rows, in);
+    MatRef mat = mat_ref(packed, scales, rows, in);
+    if constexpr (F32S) {
+        mat.pitch_s = 4u * (uint32_t)ngrp;
+        mat.s = make_rsrc(scales, mat.pitch_s * (uint32_t)rows);
+    }
     float xr[NG * kGroup];
     load_x<NG>(xr, x, lane, ngrp);
     const int n_items = (rows + rpi - 1) / rpi;
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
         RowData<NG> buf[K3G_PIPE];
 #pragma unroll
         for (int st = 0; st < K3G_PIPE; ++st) {
-            load_row<NG>(buf[st], mat, R(r0 + st), cols);
+            load_row<NG, false, F32S>(buf[st], mat, R(r0 + st), cols);
             __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (see below)
         }
         float acc = 0.f;  // lane k holds row (r - r0) % 64 == k until its block of 64 is stored
@@ -202,19 +214,20 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
             for (int st = 0; st < K3G_PIPE; ++st) {
                 const int rr = r + st;
                 if (rr < r1) {
-                    const float sa = wave_sum(row_partial<NG, LUT>(buf[st], lut, lane_off, xr, valid));
+                    const float sa = wave_sum(row_partial<NG, LUT, F32S>(buf[st], lut, lane_off, xr, valid));
                     const int k = (rr - r0) & (kWave - 1);
                     acc = lane == k ? sa : acc;
                     if (k == kWave - 1 || rr == r1 - 1) {
                         if (lane <= k) y[rr - k + lane] = acc;
                     }
                 }
-                load_row<NG>(buf[st], mat, R(rr + K3G_PIPE), cols);
+                load_row<NG, false, F32S>(buf[st], mat, R(rr + K3G_PIPE), cols);
             }
             r += K3G_PIPE;
         } while (r < r1);
     }
 }
+
 
 // Grouped SiTU-GLU up-projection. Work item = (slot, run of rpi rows); slot i
 // is the i-th expert that has pairs (active[1+i]); its pairs are the sorted
@@ -476,6 +489,42 @@ int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *
         case 1: if (lut) gemv_kernel<1, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<1, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
         case 2: if (lut) gemv_kernel<2, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<2, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
         case 4: if (lut) gemv_kernel<4, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<4, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        default: return K3G_EUNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
+// ue8m0 -> fp32 per group, as the pages' Vulkan tier does at upload: 2^(s-127)
+// exactly (s = 0 is the subnormal 2^-127), 255 (skip) -> 0.
+__global__ __launch_bounds__(256) void scales_f32_kernel(float *__restrict__ out, const uint8_t *__restrict__ s,
+                                                         int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t b = s[i];
+        const uint32_t bits = b == 255u ? 0u : (b == 0u ? 0x00400000u : b << 23);
+        out[i] = __builtin_bit_cast(float, bits);
+    }
+}
+
+int launch_scales_f32(float *out, const uint8_t *s, int64_t n, hipStream_t st) {
+    if (n == 0) return K3G_OK;
+    const int64_t blocks = (n + 255) / 256;
+    scales_f32_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, st>>>(out, s, n);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
+int launch_gemv_f32s(float *y, const float *x, const uint8_t *packed, const float *scales, int in, int rows,
+                     hipStream_t st) {
+    const int ngrp = in / kGroup;
+    const int ng = pick_ng(ngrp);
+    int rpi = rows / 2048;
+    if (rpi < 2) rpi = 2;
+    const int items = (rows + rpi - 1) / rpi;
+    const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
+    const uint8_t *sc = (const uint8_t *)scales;
+    switch (ng) {
+        case 1: gemv_kernel<1, false, true><<<grid, block, 0, st>>>(y, x, packed, sc, in, rows, rpi); break;
+        case 2: gemv_kernel<2, false, true><<<grid, block, 0, st>>>(y, x, packed, sc, in, rows, rpi); break;
+        case 4: gemv_kernel<4, false, true><<<grid, block, 0, st>>>(y, x, packed, sc, in, rows, rpi); break;
         default: return K3G_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;

@@ -101,6 +101,15 @@ def e8m0(s: int) -> float:
     return lib().k3o_e8m0(int(s))
 
 
+def scales_to_f32(scales):
+    """The pages' Vulkan-tier scale format ("Kimi K3 engine (c/kimi_k3.c)",
+    "Vulkan tier": ue8m0 expanded to f32 per group at upload): 2^(s-127) for
+    s < 255 (exact in fp32; s = 0 is subnormal), and 0 for the skip code 255."""
+    s = np.asarray(scales, np.uint8)
+    v = np.ldexp(1.0, s.astype(np.int64) - 127)
+    return np.where(s == 255, 0.0, v).astype(np.float32)
+
+
 def mxfp4_bytes(rows: int, cols: int) -> int:
     return int(lib().k3o_mxfp4_bytes(int(rows), int(cols)))
 

@@ -73,6 +73,31 @@ def test_gemv_matches_oracle(k3g, rows, n_in, lo, hi, p, lut):
     assert_norm_close(host(y), yo, nrm, what=f"gemv {rows}x{n_in}")
 
 
+def test_scales_to_f32_exact(k3g):
+    sc = np.concatenate([np.arange(256, dtype=np.uint8),
+                         np.random.default_rng(7).integers(0, 256, 10000, dtype=np.uint8)])
+    out = torch.empty(sc.size, dtype=torch.float32, device="cuda")
+    k3g.k3g_mxfp4_scales_to_f32(out, dev(sc))
+    assert np.array_equal(host(out).view(np.uint32), oracle.scales_to_f32(sc).view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,n_in,lo,hi,p", GEMV_CASES)
+def test_gemv_f32_scales_equal_ue8m0(k3g, rows, n_in, lo, hi, p):
+    # the Vulkan-tier format: the same products with the scales expanded at upload
+    pk, sc = synth.mxfp4_matrix(1000 + rows, 1, 0, rows, n_in, lo, hi, p)
+    x = synth.activations(1000 + rows, 1, n_in)[0]
+    y8 = torch.empty(rows, dtype=torch.float32, device="cuda")
+    y32 = torch.empty(rows, dtype=torch.float32, device="cuda")
+    scd = dev(sc)
+    s32 = torch.empty(sc.shape, dtype=torch.float32, device="cuda")
+    k3g.k3g_mxfp4_scales_to_f32(s32, scd)
+    k3g.k3g_mxfp4_gemv(y8, dev(x), dev(pk), scd)
+    k3g.k3g_mxfp4_gemv_f32s(y32, dev(x), dev(pk), s32)
+    assert torch.equal(y8, y32)
+    yo, _, nrm = oracle.mxfp4_gemv(x, pk, sc, full=True)
+    assert_norm_close(host(y32), yo, nrm, what=f"gemv f32 scales {rows}x{n_in}")
+
+
 @pytest.mark.parametrize("lut", DECODES, ids=["cvt", "lut"])
 def test_gemv_edge_cases(k3g, lut):
     rows, n_in = 70, 256

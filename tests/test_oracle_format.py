@@ -64,3 +64,25 @@ def test_e8m0():
     assert oracle.e8m0(0) == 2.0 ** -127
     assert oracle.e8m0(254) == 2.0 ** 127
     assert math.isnan(oracle.e8m0(255))
+
+
+def test_scales_to_f32_format():
+    # the Vulkan-tier scale format ("Kimi K3 engine (c/kimi_k3.c)", "Vulkan tier"):
+    # 2^(s-127) exactly, the subnormal 2^-127 for s = 0, 0 for the skip code 255
+    import math
+    s = np.arange(256, dtype=np.uint8)
+    f = oracle.scales_to_f32(s)
+    assert f.dtype == np.float32
+    assert f[127] == 1.0 and f[128] == 2.0 and f[126] == 0.5 and f[254] == 2.0 ** 127
+    assert f[0] == math.ldexp(1.0, -127) and f[0] > 0 and f[255] == 0.0
+    for b in range(255):
+        assert float(f[b]) == oracle.e8m0(b)  # the oracle's E8M0 table, exactly
+    # a product with the expanded scales is the ue8m0 product (finite x)
+    pk = np.random.default_rng(3).integers(0, 256, (5, 48), dtype=np.uint8)
+    sc = np.random.default_rng(4).integers(118, 133, (5, 3), dtype=np.uint8)
+    sc[1, 2] = 255
+    x = np.random.default_rng(5).standard_normal(96).astype(np.float32)
+    W = oracle.mxfp4_dequant(pk, sc)
+    f3 = oracle.scales_to_f32(sc)
+    Wf = oracle.mxfp4_dequant(pk, np.full_like(sc, 127)) * np.repeat(f3.astype(np.float64), 32, axis=1)
+    assert np.array_equal(W, Wf)
