@@ -43,18 +43,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot"])
+    ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot", "prefill_4096_exact"])
     ap.add_argument("--idot-bf16", action="store_true",
                     help="IDOT workloads: run the group dots on the bf16 matrix cores (same results)")
     ap.add_argument("--mfma-decode", action="store_true",
-                    help="one-token EXACT workloads: the expert products on the FP4 matrix cores (x and h as e2m1 "
-                         "pieces) instead of the vector kernels (same bound)")
+                    help="EXACT workloads and the block: the expert products on the FP4 matrix cores (x and h as "
+                         "e2m1 pieces) instead of the vector kernels (same bound)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="decode_b1 only: skip the short runs of the 64-token and 4096-token workloads")
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
     ap.add_argument("--stream-steps", type=int, default=40,
                     help="decode steps per cache size in the streaming-tier measurement")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only time the 256-token LatentMoE block (for profiling) and exit")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only copy a GIB-sized buffer 5 times (a plain copy of known size, for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -97,6 +99,9 @@ def main():
     print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
 
     ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager)
+    if args.block_only:
+        print(json.dumps({"block_256": run_block(ctx, bank, mfma_decode=args.mfma_decode)}), flush=True)
+        return
     result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16, args.mfma_decode)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, src, *host)
@@ -110,6 +115,8 @@ def main():
             others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
                                              "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
+        # the full LatentMoE block at 256 tokens
+        result["block_256"] = run_block(ctx, bank)
         # the Vulkan-tier scale format: the same product with f32 per-group scales
         result["scale_format"] = run_scale_format(ctx)
         # the expert streaming tier: the bank in pinned host memory, an LRU of slots in HBM
@@ -126,7 +133,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     wl_seed, T, bias_range, mode_name = synth.WORKLOADS[workload]
     mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
     form = k3g.IDOT_BF16 if (mode == k3g.IDOT and idot_bf16) else 0
-    if mode == k3g.EXACT and T == 1 and mfma_decode:
+    if mode == k3g.EXACT and mfma_decode:
         form = k3g.DECODE_MFMA
 
     W, b = synth.router(wl_seed, E, L, bias_range)
@@ -358,6 +365,44 @@ def measured_traffic(workload, kernel):
         return None
     k = doc["kernels"][kernel]
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def run_block(ctx, bank, reps=10, mfma_decode=False):
+    """The full LatentMoE block on 256 tokens (route on the 7168-wide hidden
+    state, bf16 down-projection, the routed layer on the resident bank, RMSNorm,
+    bf16 up-projection, two bf16 shared SiTU-GLU experts of 6144): HIP events
+    around `reps` calls, and the dense parts' matrix work as a rate."""
+    torch, k3g, synth, dev = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"]
+    seed, T, bias_range, _ = synth.WORKLOADS["block_256"]
+    mode = k3g.EXACT | (k3g.DECODE_MFMA if mfma_decode else 0)
+    H, Lt, SI, E, K = synth.HIDDEN, synth.LATENT, synth.SHARED_INTER, synth.N_EXPERTS, synth.TOP_K
+    dense = {k: torch.from_numpy(v).to(dev) for k, v in synth.block_dense(seed).items()}
+    W, b = synth.router(seed, E, H, bias_range)
+    x = torch.from_numpy(synth.activations(seed, T, H)).to(dev)
+    w = k3g.block_struct(torch.from_numpy(W).to(dev), torch.from_numpy(b).to(dev), dense["w_down"], dense["w_up"],
+                         dense["gamma"], [dense[f"sh_w1_{s}"] for s in range(2)],
+                         [dense[f"sh_w3_{s}"] for s in range(2)], [dense[f"sh_w2_{s}"] for s in range(2)], bank)
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=Lt, inter=synth.INTER, hidden=H, sh_inter=SI,
+                   mode=mode)
+    ws = k3g.workspace(k3g.OP_LATENT_BLOCK, sh)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    k3g.k3g_latent_moe_block(out, x, w, K, mode, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        k3g.k3g_latent_moe_block(out, x, w, K, mode, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # dense matrix work: down, up, and per shared expert w1, w3 and w2 (2 flops per product)
+    flops = 2.0 * T * (2 * H * Lt + 2 * 3 * H * SI)
+    out_d = {"tokens": T, "ms_per_block": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+             "dense_flops": flops, "dense_TFLOPs_if_all_time": round(flops / (ms * 1e-3) / 1e12, 1)}
+    del dense, ws, out, x
+    torch.cuda.empty_cache()
+    return out_d
 
 
 def run_scale_format(ctx, n_mat=8, launches=64):

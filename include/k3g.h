@@ -76,14 +76,15 @@ typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
  * to the int8 form bit for bit; the workspace gains bf16 copies of xq and hq. */
 #define K3G_IDOT_BF16 0x200
 
-/* OR-ed into K3G_EXACT: run a one-token layer on the FP4 matrix cores instead
- * of the vector kernels. The products use v_mfma_scale_f32_16x16x128_f8f6f4
- * on the stored nibbles and scales, with x and h written as sums of 16 e2m1
- * vectors (one ue8m0 scale per 32 entries each, entries below 2^-127
- * dropped); every product is exact and sums are fp32, as in the vector form,
- * so both meet the same bound. Needs latent and inter multiples of 512 (at
- * most 4096) and a bank with 16-byte aligned scale tensors and stride;
- * otherwise, and with more than one token, the vector kernels run. */
+/* OR-ed into K3G_EXACT: run the layer on the FP4 matrix cores instead of the
+ * vector kernels. The products use v_mfma_scale_f32_16x16x128_f8f6f4 on the
+ * stored nibbles and scales, with x and h written as sums of 16 e2m1 vectors
+ * (one ue8m0 scale per 32 entries each, entries below 2^-127 dropped); every
+ * product is exact and sums are fp32, as in the vector form, so both meet the
+ * same bound. With more than one token each workgroup takes one expert's
+ * sorted pairs two at a time, so each weight row is read once per two pairs.
+ * Needs latent and inter multiples of 512 (at most 4096) and a bank with
+ * 16-byte aligned scale tensors and stride; otherwise the vector kernels run. */
 #define K3G_DECODE_MFMA 0x400
 
 typedef struct {
@@ -159,9 +160,18 @@ typedef struct {
  *   shh     float [T][sh_inter]          block shared-expert SiTU output
  *   layer   the MoE layer's own workspace inside the block's
  *   xqb, hqb  uint16 (bf16) copies of xq and hq (K3G_IDOT_BF16 only)
- *   xp, hp    one-token layer with K3G_DECODE_MFMA: x and each pair's h as 16
- *             e2m1 pieces, 1280 bytes per 128 entries (operand B of the
- *             instruction and its block scales) */
+ *   xp, hp    layer with K3G_DECODE_MFMA: each token's x and each pair's h as
+ *             16 e2m1 pieces, 1280 bytes per 128 entries (operand B of the
+ *             instruction and its block scales)
+ *   passes  int32 [1 + 2 * n]            K3G_DECODE_MFMA with more than one
+ *             token: [0] = n, then (active slot, pass index) per pass, every
+ *             expert's sorted pairs taken a few at a time
+ *   dxh, dxl, dxs  block: the hidden state, the normalised aggregate and the
+ *             shared experts' h as three bf16 pieces each (6 bytes per entry,
+ *             tokens padded to a multiple of 64) for the dense products on the
+ *             bf16 matrix cores; 0 where a product's shape keeps it on the
+ *             fp32 fma kernels
+ *   dpart   float  block: the dense products' K-slice partial sums */
 typedef struct {
     size_t total;
     size_t logits, counts, offsets, perm, inv, active;
@@ -169,6 +179,8 @@ typedef struct {
     size_t idx, wts, lat, agg, nrm, shh, layer;
     size_t xqb, hqb;
     size_t xp, hp;
+    size_t passes;
+    size_t dxh, dxl, dxs, dpart;
 } k3g_ws_layout;
 
 /* Human-readable name of a status code (static storage). */
@@ -269,7 +281,7 @@ int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts
  * one kernel launch (stages a mode does not have enqueue nothing), so a
  * caller can place events between them to time each kernel:
  *   BUCKET   stable sort of the pairs by expert (counts, offsets, perm, inv, active)
- *   QUANT_X  IDOT: x -> xq, xs; one token with K3G_DECODE_MFMA: x -> xp
+ *   QUANT_X  IDOT: x -> xq, xs; K3G_DECODE_MFMA: x -> xp
  *   UP       per expert and row: g = w1 a, u = w3 a, h = SiTU(g, u)
  *   QUANT_H  IDOT: h -> hq, hs (with K3G_DECODE_MFMA, UP writes hp itself
  *            and this stage enqueues nothing)
@@ -294,10 +306,14 @@ int k3g_moe_layer_stage(int stage, float *y, const float *x, const int32_t *idx,
  * lat = W_down x, agg = layer(lat), n = RMSNorm(agg) * gamma (eps =
  * w->rms_eps, 1e-5 in [KIC-README]'s config), out = W_up n +
  * sum_s W2_s SiTU(W1_s x, W3_s x) for the n_shared (0..2) shared experts,
- * added unweighted. out, x fp32 [T][hidden]; x 16-byte aligned. bf16 weights
- * are widened exactly and multiplied in fp32. top_k and the bank as for
- * k3g_moe_layer; ws: k3g_workspace_bytes(K3G_OP_LATENT_BLOCK, ...) with
- * hidden and sh_inter set. */
+ * added unweighted. out, x fp32 [T][hidden]; x 16-byte aligned. Every
+ * product of a bf16 weight and an fp32 activation is exact and sums are fp32:
+ * with hidden, latent and sh_inter multiples of 64 and the dense weights
+ * 16-byte aligned the products run on the bf16 matrix cores, each activation
+ * split exactly into three bf16 pieces (sums over K slices added in a fixed
+ * order, so results do not depend on timing); otherwise on fp32 fma kernels.
+ * top_k and the bank as for k3g_moe_layer; ws:
+ * k3g_workspace_bytes(K3G_OP_LATENT_BLOCK, ...) with hidden and sh_inter set. */
 int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w,
                          int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes,
                          void *stream);

@@ -25,7 +25,7 @@ EXACT = 0
 IDOT = 1
 DECODE_LUT = 0x100  # OR into the EXACT mode: decode through the LDS byte-pair table
 IDOT_BF16 = 0x200  # OR into the IDOT mode: the same group dots on the bf16 matrix cores
-DECODE_MFMA = 0x400  # OR into the EXACT mode: one token on the FP4 matrix cores (x and h as e2m1 pieces)
+DECODE_MFMA = 0x400  # OR into the EXACT mode: the expert products on the FP4 matrix cores (x and h as e2m1 pieces)
 OP_EXPERT_GLU = 1
 OP_MOE_ROUTE = 2
 OP_MOE_LAYER = 3
@@ -66,7 +66,8 @@ class Shape(C.Structure):
 
 
 _WS_FIELDS = ("total", "logits", "counts", "offsets", "perm", "inv", "active", "xq", "xs", "h", "hq",
-              "hs", "ypair", "idx", "wts", "lat", "agg", "nrm", "shh", "layer", "xqb", "hqb", "xp", "hp")
+              "hs", "ypair", "idx", "wts", "lat", "agg", "nrm", "shh", "layer", "xqb", "hqb", "xp", "hp",
+              "passes", "dxh", "dxl", "dxs", "dpart")
 
 
 class WsLayout(C.Structure):

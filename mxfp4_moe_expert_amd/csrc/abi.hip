@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "k3g_common.h"
 
 namespace k3g {
@@ -22,7 +24,7 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
 int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K,
                 double top_p, hipStream_t st);
 int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
-                  int T, int K, int E, hipStream_t st);
+                  int T, int K, int E, hipStream_t st, int32_t *passes = nullptr, int npp = 0);
 int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, uint16_t *qb, hipStream_t st);
 int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed, int in, int rows, int n_tokens,
                           hipStream_t st);
@@ -46,11 +48,24 @@ int launch_moe_up_f4(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &ba
                      int latent, int inter, int max_slots, hipStream_t st);
 int launch_moe_down_f4(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
                        const int32_t *offsets, int latent, int inter, int max_slots, hipStream_t st);
+int f4_pairs_per_pass();
+int launch_moe_up_f4m(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const int32_t *active,
+                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int top_k, int latent,
+                      int inter, int n_pairs, int max_slots, hipStream_t st);
+int launch_moe_down_f4m(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
+                        const int32_t *offsets, const int32_t *passes, int latent, int inter, int n_pairs,
+                        int max_slots, hipStream_t st);
 bool f4_shape_ok(int latent, int inter);
 bool f4_bank_ok(const BankDev &b);
 int launch_dense_glu(float *h, const uint16_t *w1, const uint16_t *w3, const float *x, int T, int K, int N,
                      hipStream_t st);
 int launch_rmsnorm(float *n, const float *a, const float *gamma, int T, int len, float eps, hipStream_t st);
+int dense_t64(int T);
+bool dense_mfma_ok(int T, int N, const int *K, int n_seg);
+int dense_slices(int T, int N, int K_total, bool glu);
+int launch_split3(uint8_t *xb, const float *x, int T, int K, int ld, hipStream_t st);
+int launch_dense_mfma(float *out, uint8_t *xb_out, float *part, const uint16_t *const *w, const uint8_t *const *xb,
+                      const int *K, int n_seg, const uint16_t *w3, int T, int N, hipStream_t st);
 }  // namespace k3g
 
 using namespace k3g;
@@ -102,12 +117,37 @@ inline bool mode_ok(int mode) {
     return base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT;
 }
 inline bool lut_of(int mode) { return (mode & K3G_DECODE_LUT) != 0; }
-// One token in EXACT mode with K3G_DECODE_MFMA runs on the FP4 matrix cores
-// when the shape fits them (the bank's alignment is checked where the bank is
-// known).
+// EXACT mode with K3G_DECODE_MFMA runs on the FP4 matrix cores when the shape
+// fits them (the bank's alignment is checked where the bank is known).
 inline bool f4_layer(int mode, int n_tokens, int latent, int inter) {
-    return n_tokens == 1 && mode == (K3G_EXACT | K3G_DECODE_MFMA) && f4_shape_ok(latent, inter);
+    return n_tokens >= 1 && mode == (K3G_EXACT | K3G_DECODE_MFMA) && f4_shape_ok(latent, inter);
 }
+// The block's dense products on the bf16 matrix cores (x as three exact bf16
+// pieces): the down-projection and the shared GLUs read the pieces of the
+// hidden state, the up-projection those of the normalised aggregate and of
+// the shared h. Each product takes that form when its shape allows; the
+// workspace is sized for two shared experts.
+struct DensePlan {
+    bool down = false, glu = false, up = false;
+    size_t part_floats = 0;  // the largest product's slices
+};
+inline DensePlan dense_plan(int T, int hidden, int latent, int sh_inter, int n_shared) {
+    DensePlan d;
+    if (T < 1) return d;
+    const int kd[1] = {hidden};
+    d.down = dense_mfma_ok(T, latent, kd, 1);
+    d.glu = d.down && n_shared > 0 && dense_mfma_ok(T, sh_inter, kd, 1) && sh_inter % 64 == 0;
+    const int ku[3] = {latent, sh_inter, sh_inter};
+    d.up = latent % 64 == 0 && (n_shared == 0 || d.glu) && dense_mfma_ok(T, hidden, ku, 1 + n_shared);
+    const size_t Ts = (size_t)T;
+    if (d.down) d.part_floats = std::max(d.part_floats, dense_slices(T, latent, hidden, false) * Ts * latent);
+    if (d.glu) d.part_floats = std::max(d.part_floats, dense_slices(T, sh_inter, hidden, true) * 2 * Ts * sh_inter);
+    if (d.up)
+        d.part_floats = std::max(
+            d.part_floats, dense_slices(T, hidden, latent + n_shared * sh_inter, false) * Ts * hidden);
+    return d;
+}
+
 // The IDOT kernels stage a row's scale bytes four groups at a time as aligned
 // dwords: both widths must be multiples of 128 columns. The bf16 form addresses
 // a row of its activations by a 32-bit byte offset: T rows of x and T*top_k
@@ -169,6 +209,12 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
                 o->agg = c.take(sizeof(float) * T * s.latent);
                 o->nrm = c.take(sizeof(float) * T * s.latent);
                 o->shh = c.take(sizeof(float) * 2 * (T ? T : 1) * s.sh_inter);  // [2][T][sh_inter]
+                const DensePlan dp = dense_plan(s.n_tokens, s.hidden, s.latent, s.sh_inter, 2);
+                const size_t t64 = (size_t)dense_t64(s.n_tokens);
+                if (dp.down) o->dxh = c.take(t64 * s.hidden * 6);
+                if (dp.up) o->dxl = c.take(t64 * s.latent * 6);
+                if (dp.glu) o->dxs = c.take(2 * t64 * s.sh_inter * 6);
+                if (dp.part_floats) o->dpart = c.take(sizeof(float) * dp.part_floats);
             }
             o->counts = c.take(sizeof(int32_t) * E);
             o->offsets = c.take(sizeof(int32_t) * (E + 1));
@@ -187,9 +233,15 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
                     o->hqb = c.take(sizeof(uint16_t) * (P ? P : 1) * s.inter);
                 }
             }
-            if (f4_layer(s.mode, s.n_tokens, s.latent, s.inter)) {  // 40 bytes per entry
-                o->xp = c.take((size_t)s.latent / 128 * 1280);
+            if (f4_layer(s.mode, s.n_tokens, s.latent, s.inter)) {  // 10 bytes per entry
+                o->xp = c.take(T * (size_t)s.latent / 128 * 1280);
                 o->hp = c.take(P * (size_t)s.inter / 128 * 1280);
+                // the pass table: each expert with pairs takes ceil(pairs / npp)
+                // passes, fewer than P / npp + 1 per expert in all
+                if (s.n_tokens > 1) {
+                    const size_t npp = (size_t)f4_pairs_per_pass();
+                    o->passes = c.take(sizeof(int32_t) * (1 + 2 * ((P + npp - 1) / npp + std::min(P, E))));
+                }
             }
             o->layer = 0;
             break;
@@ -438,16 +490,25 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
     // and writes the bucket, so the bucket stage launches nothing.
     const bool route1 = n_tokens == 1 && base_mode(mode) == K3G_EXACT;
     const Route1 r1 = route1 ? Route1{idx, counts, offsets, perm, inv, active, E} : Route1{};
-    // one token on the FP4 matrix cores: x and h split into e2m1 pieces first
+    // on the FP4 matrix cores x and h are split into e2m1 pieces first; more
+    // than one token: the bucket also writes the table of (expert, pairs) passes
     const bool f4 = f4_layer(mode, n_tokens, latent, inter) && f4_bank_ok(b) && L.xp && L.hp;
+    const bool f4m = f4 && n_tokens > 1 && L.passes;
     uint8_t *xp = (uint8_t *)(w + L.xp), *hp = (uint8_t *)(w + L.hp);
+    int32_t *passes = f4m ? (int32_t *)(w + L.passes) : nullptr;
+    const int npp = f4_pairs_per_pass();
+    if (f4 && n_tokens > 1 && !f4m) return K3G_EINVAL;  // a layout without the pass table
     switch (stage) {
         case K3G_STAGE_BUCKET:
-            return route1 ? K3G_OK : launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st);
+            return route1 ? K3G_OK
+                          : launch_bucket(counts, offsets, perm, inv, active, idx, n_tokens, top_k, E, st, passes, npp);
         case K3G_STAGE_QUANT_X:
-            if (f4) return launch_split(xp, x, 1, latent, latent, st);
+            if (f4) return launch_split(xp, x, n_tokens, latent, latent, st);
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, xqb, st) : K3G_OK;
         case K3G_STAGE_UP:
+            if (f4m)
+                return launch_moe_up_f4m(h, hp, xp, b, active, offsets, perm, passes, top_k, latent, inter, P,
+                                         max_slots, st);
             if (f4) return launch_moe_up_f4(h, hp, xp, b, r1, top_k, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_up_idot(h, xq, xqb, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
@@ -457,6 +518,8 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
             if (f4) return K3G_OK;  // the up-projection wrote hp
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, hqb, st) : K3G_OK;
         case K3G_STAGE_DOWN:
+            if (f4m)
+                return launch_moe_down_f4m(ypair, hp, b, active, offsets, passes, latent, inter, P, max_slots, st);
             if (f4) return launch_moe_down_f4(ypair, hp, b, active, offsets, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_down_idot(ypair, hq, hqb, hs, b, active, offsets, perm, latent, inter, max_slots, st)
@@ -523,14 +586,52 @@ extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_
     // routing on the hidden state
     K3G_TRY(launch_logits(logits, x, w->w_router, T, hidden, E, st));
     K3G_TRY(launch_topk(idx, wts, logits, w->bias, T, E, top_k, 0.0, st));
+    // the dense products: bf16 matrix cores where the plan allows (and the
+    // workspace has the regions), the fp32 fma kernels otherwise
+    DensePlan dp = dense_plan(T, hidden, latent, sh_inter, w->n_shared);
+    bool al = aligned(w->w_down, 16) && aligned(w->w_up, 16);
+    for (int i = 0; i < w->n_shared; ++i)
+        al = al && aligned(w->sh_w1[i], 16) && aligned(w->sh_w3[i], 16) && aligned(w->sh_w2[i], 16);
+    dp.down = dp.down && al && L.dxh && L.dpart;
+    dp.glu = dp.glu && dp.down && L.dxs;
+    dp.up = dp.up && al && L.dxl && L.dpart && (w->n_shared == 0 || dp.glu);
+    uint8_t *dxh = (uint8_t *)(b + L.dxh), *dxl = (uint8_t *)(b + L.dxl), *dxs = (uint8_t *)(b + L.dxs);
+    float *dpart = (float *)(b + L.dpart);
+    const size_t t64 = (size_t)dense_t64(T);
     // down-projection into the latent space
-    const DenseSeg down = {w->w_down, x, hidden};
-    K3G_TRY(launch_dense(lat, &down, 1, T, latent, st));
+    if (dp.down) {
+        K3G_TRY(launch_split3(dxh, x, T, hidden, hidden, st));
+        const uint16_t *wd[1] = {w->w_down};
+        const uint8_t *xd[1] = {dxh};
+        const int kd[1] = {hidden};
+        K3G_TRY(launch_dense_mfma(lat, nullptr, dpart, wd, xd, kd, 1, nullptr, T, latent, st));
+    } else {
+        const DenseSeg down = {w->w_down, x, hidden};
+        K3G_TRY(launch_dense(lat, &down, 1, T, latent, st));
+    }
     // the routed experts on the latent tokens
     for (int stage = K3G_STAGE_BUCKET; stage <= K3G_STAGE_COMBINE; ++stage)
         K3G_TRY(layer_stage(stage, L, agg, lat, idx, wts, bank, T, top_k, mode, ws, st));
     // RMSNorm of the aggregate, the shared experts, and the up-projection
     K3G_TRY(launch_rmsnorm(nrm, agg, w->gamma, T, latent, w->rms_eps, st));
+    if (dp.up) {
+        K3G_TRY(launch_split3(dxl, nrm, T, latent, latent, st));
+        const uint16_t *wu[3] = {w->w_up, nullptr, nullptr};
+        const uint8_t *xu[3] = {dxl, nullptr, nullptr};
+        int ku[3] = {latent, 0, 0};
+        for (int i = 0; i < w->n_shared; ++i) {
+            float *h = shh + (size_t)i * T * sh_inter;
+            uint8_t *hp = dxs + (size_t)i * t64 * sh_inter * 6;
+            const uint16_t *w1[1] = {w->sh_w1[i]};
+            const uint8_t *x1[1] = {dxh};
+            const int k1[1] = {hidden};
+            K3G_TRY(launch_dense_mfma(h, hp, dpart, w1, x1, k1, 1, w->sh_w3[i], T, sh_inter, st));
+            wu[1 + i] = w->sh_w2[i];
+            xu[1 + i] = hp;
+            ku[1 + i] = sh_inter;
+        }
+        return launch_dense_mfma(out, nullptr, dpart, wu, xu, ku, 1 + w->n_shared, nullptr, T, hidden, st);
+    }
     DenseSeg segs[3] = {{w->w_up, nrm, latent}, {nullptr, nullptr, 0}, {nullptr, nullptr, 0}};
     for (int i = 0; i < w->n_shared; ++i) {
         float *h = shh + (size_t)i * T * sh_inter;

@@ -127,4 +127,364 @@ int launch_rmsnorm(float *n, const float *a, const float *gamma, int T, int len,
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
+// ---- dense products on the bf16 matrix cores ------------------------------------------
+//
+// out[t][n] = sum_s W_s[n][:] . x_s[t][:] with W bf16 and x fp32. Each entry of
+// x is written exactly as three bf16 pieces, x = x0 + x1 + x2: x0 is x cut to
+// its top 8 significant bits, x1 the top 8 bits of what is left and x2 the
+// rest (at most 8 bits, so exact while |x| >= 2^-100 keeps the pieces normal).
+// Every product w * x_i (8 x 8 bits) is exact in fp32 and
+// v_mfma_f32_16x16x32_bf16 sums them in fp32, so the result meets the same
+// bound as the fp32 fma form, with the matrix cores doing three products per
+// weight instead of the vector unit doing one.
+//
+// Pieces in HBM, in the order the products read them (operand B of
+// 16x16x32: lane l = token l%16, entries 8*(l/16)..+7 of a 32-entry step):
+//   [token tile of 16][step of 32][piece 0..2][lane 0..63][8 bf16]
+// so one step of one token tile is 3 KB, and the token count is padded to a
+// multiple of 64 with zero pieces.
+//
+// The product splits K over S slices (S chosen so that the grid fills the
+// chip): each workgroup sums one slice of 256 rows (GLU: 128 rows of both
+// W1 and W3) x 64 tokens into fp32 partials [S][G][T][N]; the reduction adds
+// the slices in order (the result does not depend on timing) and applies the
+// epilogue. Per workgroup: 4 wavefronts, each owning 64 operand-A rows as four
+// tiles of 16 (GLU: W1 rows r..r+31 and W3 rows r..r+31) loaded straight into
+// registers through a 3-deep ring of 64-entry blocks; operand B (4 token tiles
+// x 2 steps x 3 pieces, 24 KB per block) goes global -> LDS by DMA into two
+// buffers, one block ahead.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+namespace dm {
+constexpr int kWaves = 4;
+constexpr int kTok = 64;        // tokens per workgroup
+constexpr int kKB = 64;         // entries per block (two steps)
+constexpr int kStepBytes = 3 * 1024;           // one token tile, one step, three pieces
+constexpr int kBlockB = 4 * 2 * kStepBytes;    // 24 KB: one block of operand B
+constexpr int kNBUF = 3;        // operand-A ring depth (blocks)
+constexpr int kMaxSeg = 3;
+constexpr int kTargetWG = 512;  // two workgroups per CU
+}  // namespace dm
+
+struct DenseMSeg {
+    const uint16_t *w;   // bf16 [N][K]
+    const uint8_t *xb;   // pieces of x [T64 / 16][K / 32][3][64][16 B]
+    int K;               // multiple of 64
+};
+
+struct DenseMArgs {
+    DenseMSeg seg[dm::kMaxSeg];
+    const uint16_t *w3;  // GLU: the second matrix (same K and x as seg[0])
+    float *part;         // [S][G][T][N]
+    int n_seg, N, T, S, nkb;  // nkb: blocks over all segments
+    int kb_start[dm::kMaxSeg + 1];
+    int row_blocks, tok_blocks, n_items;
+};
+
+__device__ inline uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ inline float bits_f32(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+// x -> three bf16 pieces (bit patterns): cut to the top 8 significant bits
+// twice, the remainder being exact in bf16.
+__device__ inline void bf16x3(float x, uint32_t &p0, uint32_t &p1, uint32_t &p2) {
+    const uint32_t b0 = f32_bits(x) & 0xFFFF0000u;
+    const float r1 = x - bits_f32(b0);
+    const uint32_t b1 = f32_bits(r1) & 0xFFFF0000u;
+    const float r2 = r1 - bits_f32(b1);
+    p0 = b0 >> 16;
+    p1 = b1 >> 16;
+    p2 = f32_bits(r2) >> 16;
+}
+
+// Write the pieces of 8 consecutive entries (k = 8c..8c+7) of token t.
+__device__ inline void store_pieces8(uint8_t *xb, int nks, int t, int c, const float *v) {
+    uint32_t q[3][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t a0, a1, a2, b0, b1, b2;
+        bf16x3(v[2 * j], a0, a1, a2);
+        bf16x3(v[2 * j + 1], b0, b1, b2);
+        q[0][j] = a0 | (b0 << 16);
+        q[1][j] = a1 | (b1 << 16);
+        q[2][j] = a2 | (b2 << 16);
+    }
+    const int tt = t >> 4, s = c >> 2, lane = (t & 15) + 16 * (c & 3);
+    uint8_t *dst = xb + ((size_t)tt * nks + s) * dm::kStepBytes + 16 * lane;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) *(uint4 *)(dst + 1024 * p) = make_uint4(q[p][0], q[p][1], q[p][2], q[p][3]);
+}
+
+// x [T][K] (row stride ld) -> pieces for T64 tokens (zero past T).
+__global__ __launch_bounds__(256) void split3_kernel(uint8_t *__restrict__ xb, const float *__restrict__ x, int T,
+                                                     int T64, int K, int ld) {
+    const int nc = K / 8;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= (int64_t)T64 * nc) return;
+    const int t = (int)(id / nc), c = (int)(id - (int64_t)t * nc);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t < T) {
+        const float4 a = *(const float4 *)(x + (size_t)t * ld + 8 * c);
+        const float4 b = *(const float4 *)(x + (size_t)t * ld + 8 * c + 4);
+        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    }
+    store_pieces8(xb, K / 32, t, c, v);
+}
+
+template <bool GLU>
+__global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(DenseMArgs a) {
+    using namespace dm;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockB];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // XCD-aware order: consecutive workgroups go round the 8 XCDs, so item
+    // w = (XCD, position) keeps each XCD on a contiguous run of items, where
+    // the token blocks of one (row block, slice) are neighbours and share the
+    // weights through that XCD's L2
+    const int per_xcd = (int)(gridDim.x / 8);
+    const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (item >= a.n_items) return;  // whole workgroup
+    const int tb = item % a.tok_blocks;
+    const int rest = item / a.tok_blocks;
+    const int sl = rest % a.S, rb = rest / a.S;
+    const int kb0 = (int)((int64_t)a.nkb * sl / a.S), kb1 = (int)((int64_t)a.nkb * (sl + 1) / a.S);
+    constexpr int ROWS_W = GLU ? 32 : 64;  // output rows per wavefront
+    const int r0 = (rb * kWaves + wave) * ROWS_W;
+
+    // operand A: four tiles of 16 rows; lane (i = l%16, q = l/16) reads 16 B at
+    // entry 8q of a step for row i of its tile
+    rsrc_t ra[kMaxSeg], ra3;
+#pragma unroll
+    for (int s = 0; s < kMaxSeg; ++s)
+        ra[s] = make_rsrc(s < a.n_seg ? a.seg[s].w : a.seg[0].w,
+                          (uint32_t)((s < a.n_seg ? (uint64_t)a.seg[s].K : 0) * 2 * (uint64_t)a.N));
+    ra3 = make_rsrc(GLU ? a.w3 : a.seg[0].w, GLU ? (uint32_t)((uint64_t)a.seg[0].K * 2 * a.N) : 0u);
+    auto seg_of = [&](int kb) { return kb >= a.kb_start[2] ? 2 : kb >= a.kb_start[1] ? 1 : 0; };
+    uint4 A[kNBUF][4][2];
+    auto load_a = [&](int kb, int slot) {
+        const int s = seg_of(kb);
+        const uint32_t K2 = 2u * (uint32_t)a.seg[s].K;
+        const uint32_t soff = 128u * (uint32_t)(kb - a.kb_start[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + (GLU ? 16 * (i & 1) : 16 * i) + (lane & 15);
+            const uint32_t v = (uint32_t)row * K2 + 16u * (uint32_t)(lane >> 4);
+            const rsrc_t r = (GLU && i >= 2) ? ra3 : (s == 0 ? ra[0] : s == 1 ? ra[1] : ra[2]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) A[slot][i][h] = buf_load16(r, v, soff + 64u * h);
+        }
+    };
+    // operand B: wavefront w brings token tile w of the block (6 KB)
+    const uint32_t lb = lds_addr(lds);
+    auto dma_b = [&](int kb, int buf) {
+        const int s = seg_of(kb);
+        const int nks = a.seg[s].K / 32;
+        const int ttg = tb * 4 + wave;
+        const uint8_t *src = a.seg[s].xb + ((size_t)ttg * nks + 2 * (kb - a.kb_start[s])) * kStepBytes;
+#pragma unroll
+        for (int j = 0; j < 6; ++j)
+            dma16(src, 1024u * j + 16u * lane, lb + (uint32_t)(buf * kBlockB + wave * 2 * kStepBytes + 1024 * j));
+    };
+
+    float4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    int li = lane;
+    __asm__ volatile("" : "+v"(li));
+    auto compute = [&](int slot, int buf) {
+        const uint4 *bb = (const uint4 *)(lds + buf * kBlockB) + li;
+        __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                bf16x8_t B[3];
+#pragma unroll
+                for (int p = 0; p < 3; ++p) B[p] = __builtin_bit_cast(bf16x8_t, bb[((t * 2 + st) * 3 + p) * 64]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, A[slot][i][st]);
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, B[p], acc[i][t], 0, 0, 0);
+                }
+            }
+    };
+
+    // prologue: B of the first block, A of the first two
+    if (kb0 < kb1) {
+        dma_b(kb0, 0);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kNBUF - 1; ++j)
+            if (kb0 + j < kb1) load_a(kb0 + j, j);
+        wait_vm<0>();
+        __syncthreads();
+    }
+    // main loop, unrolled by the ring depth so that every ring slot is static
+    for (int kb = kb0; kb < kb1; kb += kNBUF) {
+#pragma unroll
+        for (int j = 0; j < kNBUF; ++j) {
+            const int k = kb + j;
+            if (k < kb1) {  // uniform
+                const int buf = (k - kb0) & 1;
+                const bool nb = k + 1 < kb1, na = k + kNBUF - 1 < kb1;
+                if (nb) dma_b(k + 1, buf ^ 1);
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                if (na) load_a(k + kNBUF - 1, (j + kNBUF - 1) % kNBUF);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(j, buf);
+                __builtin_amdgcn_sched_barrier(0);
+                // the next block's B is in LDS, and every wavefront is done
+                // with this buffer before it is filled again
+                if (na) wait_vm<8>();
+                else wait_vm<0>();
+                __syncthreads();
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) __asm__ volatile("" : "+v"(acc[i][t]));
+
+    // lane l holds token 16t + l%16 and rows 4(l/16)..+3 of each tile
+    const int tok0 = tb * kTok + (lane & 15);
+    const int G = GLU ? 2 : 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = GLU ? i >> 1 : 0;
+        const int n = r0 + (GLU ? 16 * (i & 1) : 16 * i) + 4 * (lane >> 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int tok = tok0 + 16 * t;
+            if (tok < a.T && n < a.N) {
+                float *dst = a.part + (((size_t)sl * G + g) * a.T + tok) * a.N + n;
+                *(float4 *)dst = make_float4(acc[i][t][0], acc[i][t][1], acc[i][t][2], acc[i][t][3]);
+            }
+        }
+    }
+}
+
+// partials [S][G][T][N] -> out [T][N] (G = 1: the sum over slices; G = 2: SiTU
+// of the two sums), slices added in order; optionally also the pieces of out
+// for the next product (T64 tokens, zero past T). Thread: 8 entries of a token.
+template <bool GLU>
+__global__ __launch_bounds__(256) void dense_reduce_kernel(float *__restrict__ out, uint8_t *__restrict__ xb,
+                                                           const float *__restrict__ part, int S, int T, int T64,
+                                                           int N) {
+    const int nc = N / 8;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= (int64_t)T64 * nc) return;
+    const int t = (int)(id / nc), c = (int)(id - (int64_t)t * nc);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t < T) {
+        const int G = GLU ? 2 : 1;
+        float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {
+            const float *pg = part + (((size_t)s * G) * T + t) * N + 8 * c;
+            const float4 a0 = *(const float4 *)pg, a1 = *(const float4 *)(pg + 4);
+            g[0] += a0.x, g[1] += a0.y, g[2] += a0.z, g[3] += a0.w;
+            g[4] += a1.x, g[5] += a1.y, g[6] += a1.z, g[7] += a1.w;
+            if (GLU) {
+                const float *pu = pg + (size_t)T * N;
+                const float4 b0 = *(const float4 *)pu, b1 = *(const float4 *)(pu + 4);
+                u[0] += b0.x, u[1] += b0.y, u[2] += b0.z, u[3] += b0.w;
+                u[4] += b1.x, u[5] += b1.y, u[6] += b1.z, u[7] += b1.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = GLU ? situ(g[j], u[j]) : g[j];
+        float *o = out + (size_t)t * N + 8 * c;
+        *(float4 *)o = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4 *)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    if (xb) store_pieces8(xb, N / 32, t, c, v);
+}
+
+// ---- host side -------------------------------------------------------------------------
+
+int dense_t64(int T) { return (T + dm::kTok - 1) / dm::kTok * dm::kTok; }
+
+// The matrix-core form takes K multiples of 64 and N multiples of 16, with
+// every 32-bit offset in range; otherwise the fp32 fma form runs.
+bool dense_mfma_ok(int T, int N, const int *K, int n_seg) {
+    if (T < 1 || N < 16 || N % 16) return false;
+    const int64_t t64 = dense_t64(T);
+    for (int s = 0; s < n_seg; ++s) {
+        if (K[s] < 64 || K[s] % 64) return false;
+        if ((int64_t)N * K[s] * 2 >= ((int64_t)1 << 31) || t64 * K[s] * 6 >= ((int64_t)1 << 31)) return false;
+    }
+    return true;
+}
+
+// Slices of K: enough workgroups to fill the chip, at least 4 blocks a slice.
+int dense_slices(int T, int N, int K_total, bool glu) {
+    const int rows_wg = dm::kWaves * (glu ? 32 : 64);
+    const int64_t tiles = (int64_t)((N + rows_wg - 1) / rows_wg) * (dense_t64(T) / dm::kTok);
+    const int nkb = K_total / dm::kKB;
+    int64_t s = (dm::kTargetWG + tiles - 1) / tiles;
+    s = s < nkb / 4 ? s : nkb / 4;
+    return s < 1 ? 1 : (int)s;
+}
+
+int launch_split3(uint8_t *xb, const float *x, int T, int K, int ld, hipStream_t st) {
+    if (K % 64 || ld % 4 || ld < K || ((uintptr_t)x & 15)) return K3G_EUNSUPPORTED;
+    const int64_t n = (int64_t)dense_t64(T) * (K / 8);
+    if (n == 0) return K3G_OK;
+    split3_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(xb, x, T, dense_t64(T), K, ld);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
+// out (+ pieces of out when xb_out) = sum over segments of W_s x_s; GLU (one
+// segment, w3 given): out = SiTU(W1 x, W3 x). part holds S * G * T * N floats.
+int launch_dense_mfma(float *out, uint8_t *xb_out, float *part, const uint16_t *const *w, const uint8_t *const *xb,
+                      const int *K, int n_seg, const uint16_t *w3, int T, int N, hipStream_t st) {
+    if (T == 0) return K3G_OK;
+    if (n_seg < 1 || n_seg > dm::kMaxSeg || (w3 && n_seg != 1) || !dense_mfma_ok(T, N, K, n_seg) ||
+        (xb_out && N % 64))  // the pieces feed a product whose K is this N
+        return K3G_EUNSUPPORTED;
+    const bool glu = w3 != nullptr;
+    DenseMArgs a{};
+    int kt = 0;
+    for (int s = 0; s < dm::kMaxSeg; ++s) {
+        a.kb_start[s] = kt / dm::kKB;
+        if (s < n_seg) {
+            a.seg[s] = DenseMSeg{w[s], xb[s], K[s]};
+            kt += K[s];
+        } else {
+            a.kb_start[s] = 0x7fffffff;
+        }
+    }
+    a.kb_start[dm::kMaxSeg] = 0x7fffffff;
+    a.w3 = w3;
+    a.part = part;
+    a.n_seg = n_seg;
+    a.N = N;
+    a.T = T;
+    a.nkb = kt / dm::kKB;
+    a.S = dense_slices(T, N, kt, glu);
+    const int rows_wg = dm::kWaves * (glu ? 32 : 64);
+    a.row_blocks = (N + rows_wg - 1) / rows_wg;
+    a.tok_blocks = dense_t64(T) / dm::kTok;
+    const int64_t items = (int64_t)a.row_blocks * a.S * a.tok_blocks;
+    if (items > (1 << 30)) return K3G_EUNSUPPORTED;
+    a.n_items = (int)items;
+    const unsigned grid = (unsigned)((items + 7) / 8 * 8);  // a whole number per XCD
+    if (glu) dense_mfma_kernel<true><<<grid, dm::kWaves * kWave, 0, st>>>(a);
+    else dense_mfma_kernel<false><<<grid, dm::kWaves * kWave, 0, st>>>(a);
+    if (hipGetLastError() != hipSuccess) return K3G_EHIP;
+    const int64_t n = (int64_t)dense_t64(T) * (N / 8);
+    if (glu) dense_reduce_kernel<true><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(out, xb_out, part, a.S, T,
+                                                                                   dense_t64(T), N);
+    else dense_reduce_kernel<false><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(out, xb_out, part, a.S, T,
+                                                                                 dense_t64(T), N);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
 }  // namespace k3g

@@ -322,6 +322,193 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4_kernel(
     }
 }
 
+// More tokens: workgroup w takes the pass k = w / row_blocks of the work
+// table the bucket wrote (passes[0] = count, then (slot, pass index) pairs):
+// the slot's sorted pairs [p0, p1), up to NPP of them, and 128 rows
+// (4 wavefronts x 32). The pairs' B operands (x's pieces per token for UP,
+// h's pieces per pair for DOWN) sit in LDS; every A fragment of the weights
+// feeds one product per pair, so the weights stream once per pass. A pass
+// with fewer than NPP pairs repeats its last pair (products not stored).
+template <bool UP, int NCK, int NPP>
+__global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
+    float *__restrict__ out, const uint8_t *__restrict__ pieces, uint8_t *__restrict__ hp, BankDev bank,
+    const int32_t *__restrict__ active, const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ passes, int top_k, int latent, int inter) {
+    constexpr int TILES = UP ? 4 : 2;
+    constexpr int CPB = 4;                 // chunks per block
+    constexpr int NB = TILES * NCK / CPB;  // blocks
+    constexpr int NBUF = 4;                // ring of blocks
+    constexpr int ngrp = 4 * NCK;
+    constexpr int VEC = NCK * f4::kChunkBytes;  // one vector's pieces
+    extern __shared__ uint4 lds_b[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n_out = UP ? inter : latent;
+    const int row_blocks = (n_out / f4::kRows + f4::kWaves - 1) / f4::kWaves;
+    const int k = blockIdx.x / row_blocks;
+    if (k >= passes[0]) return;  // whole workgroup
+    const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
+    const int e = active[1 + slot];
+    const int p0 = offsets[e] + pass * NPP;
+    const int np = min(NPP, offsets[e + 1] - p0);
+    const int blk32 = (blockIdx.x - k * row_blocks) * f4::kWaves + wave;
+    const bool live = blk32 < n_out / f4::kRows;
+
+    // the wavefront's tiles: buffer resources, and this lane's row offsets
+    const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
+    constexpr uint32_t pitch_p = 16u * ngrp, pitch_s = ngrp;
+    const int r0 = (live ? blk32 : 0) * f4::kRows;
+    rsrc_t rp[TILES], rs[TILES];
+    uint32_t vp[TILES], vs[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
+        const uint32_t row = (uint32_t)(r0 + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
+        rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
+        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vs[t] = row * pitch_s;
+    }
+    const uint32_t dead = live ? 0u : kOffRange;
+    uint4 A[NBUF][CPB], S[NBUF];
+    auto load_block = [&](int kb) {
+        const int t = kb / (NCK / CPB), c0 = CPB * (kb % (NCK / CPB)), b = kb % NBUF;
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u + dead);
+        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u + dead);
+    };
+    // B: the pass's NPP vectors of pieces into LDS, then the first weight blocks
+    {
+        const uint32_t lb = lds_addr(lds_b);
+        constexpr int units = VEC / 1024;  // 1 KB per wavefront instruction
+#pragma unroll
+        for (int q = 0; q < NPP; ++q) {
+            const int pq = p0 + min(q, np - 1);
+            const int v = UP ? perm[pq] / top_k : pq;  // UP: the pair's token; DOWN: the pair's h
+            const uint8_t *src = pieces + (size_t)v * VEC;
+            for (int u = wave; u < units; u += f4::kWaves)
+                dma16(src, 1024u * u + 16u * lane, lb + (uint32_t)(q * VEC) + 1024u * u);
+        }
+    }
+    __asm__ volatile("" ::: "memory");  // the weight loads stay after the DMA
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int PRO = NBUF - 1 < NB ? NBUF - 1 : NB;
+#pragma unroll
+    for (int kb = 0; kb < PRO; ++kb) load_block(kb);
+    wait_vm<PRO * (CPB + 1)>();
+    __syncthreads();
+
+    const uint32_t qsh = 8u * (uint32_t)(lane >> 4);
+    float4_t acc[NPP][TILES];
+#pragma unroll
+    for (int q = 0; q < NPP; ++q)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[q][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // the lane's LDS index, opaque to the compiler: every read is then one base
+    // register plus an immediate offset (known, the compiler rebuilds each
+    // address from the previous one and keeps them all live)
+    int li = lane;
+    __asm__ volatile("" : "+v"(li));
+    const uint4 *bq[NPP];
+    const uint32_t *sq[NPP];
+#pragma unroll
+    for (int q = 0; q < NPP; ++q) {
+        bq[q] = lds_b + q * (VEC / 16) + li;
+        sq[q] = (const uint32_t *)lds_b + (q * VEC + 1024) / 4 + li;
+    }
+    // B of block kb for every pair, read from LDS one block ahead
+    uint4 Bv[2][NPP][CPB];
+    uint32_t Bs[2][NPP][CPB];
+    auto read_b = [&](int kb) {
+        const int c0 = CPB * (kb % (NCK / CPB));
+        // every tile reads B again: without this the compiler keeps the first
+        // tile's reads of all chunks in registers for the later tiles
+        if (c0 == 0) __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < NPP; ++q)
+#pragma unroll
+            for (int c = 0; c < CPB; ++c) {
+                Bv[kb & 1][q][c] = bq[q][(c0 + c) * (f4::kChunkBytes / 16)];
+                Bs[kb & 1][q][c] = sq[q][(c0 + c) * (f4::kChunkBytes / 4)];
+            }
+    };
+    auto compute = [&](int kb) {
+        const int t = kb / (NCK / CPB), b = kb % NBUF;
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+            const uint32_t sd = c == 0 ? S[b].x : c == 1 ? S[b].y : c == 2 ? S[b].z : S[b].w;
+            const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
+            const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
+            const uint4 a = A[b][c];
+            const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < NPP; ++q) {
+                const uint4 bv = Bv[kb & 1][q][c];
+                const v8i_t B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
+                acc[q][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av, B, acc[q][t], 4, 4, 0,
+                                                                             (int)(sa & keep), 0, (int)Bs[kb & 1][q][c]);
+            }
+        }
+    };
+    read_b(0);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+        if (kb + NBUF - 1 < NB) load_block(kb + NBUF - 1);
+        if (kb + 1 < NB) read_b(kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // every product is done here: left free, the compiler sinks a later pair's
+    // products into the epilogue past the earlier pairs' stores, holding their
+    // operands live all the way
+#pragma unroll
+    for (int q = 0; q < NPP; ++q)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) __asm__ volatile("" : "+v"(acc[q][t]));
+    // (no early exit for a dead wavefront here: a branch around the epilogue
+    // would let the compiler sink every product into it, after all the loads)
+
+    // per pair: sum the 16 piece columns (lanes 16w..16w+15 hold one row
+    // block's columns), then lane q < 8 of each 16 holds row 16*ts + 4*(lane >> 4) + v
+    const int qd = lane & 15, ts = (qd >> 2) & 1, v = qd & 3;
+    const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+#pragma unroll
+    for (int q = 0; q < NPP; ++q) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                float sm = acc[q][t][vv];
+                sm += dpp<0xB1>(sm);
+                sm += dpp<0x4E>(sm);
+                sm += dpp<0x141>(sm);
+                sm += dpp<0x140>(sm);
+                acc[q][t][vv] = sm;
+            }
+        auto sel = [&](const float4_t &x0, const float4_t &x1) {
+            const float4_t &x = ts ? x1 : x0;
+            return v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
+        };
+        const bool store = live && q < np;
+        const int pq = p0 + q;
+        if constexpr (UP) {
+            const float hv = situ(sel(acc[q][0], acc[q][2]), sel(acc[q][1], acc[q][3]));
+            if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
+            // this pair's group of h as pieces for the down-projection
+            const int j = lane & 31;
+            const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
+            const int g32 = r0 / kGroup;
+            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+            split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
+                        store && lane < 32);
+        } else {
+            const float y = sel(acc[q][0], acc[q][1]);
+            if (store && qd < 8) out[(size_t)pq * n_out + row] = y;
+        }
+    }
+}
+
 // The matrix-core path takes whole 4-chunk blocks (512 entries; a row's
 // scale bytes in 16-byte loads), whole 32-row blocks and whole 4-chunk groups
 // of h's pieces: in and out sizes multiples of 512, at most 4096 (B -- a
@@ -367,6 +554,61 @@ static int launch_f4_n(int n_in, float *out, const uint8_t *pieces, uint8_t *hp,
 #undef K3G_F4
         default: return K3G_EUNSUPPORTED;
     }
+}
+
+// More tokens: the bucket's pass table drives the grid (an upper bound on the
+// passes: every slot's last pass may be short).
+constexpr int kF4Npp = 2;  // pairs per pass
+
+template <bool UP, int NCK>
+static int launch_f4m(float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank, const int32_t *active,
+                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int top_k, int latent,
+                      int inter, int n_pairs, int max_slots, hipStream_t st) {
+    const int n_out = UP ? inter : latent;
+    const int row_blocks = (n_out / f4::kRows + f4::kWaves - 1) / f4::kWaves;
+    const int64_t max_passes = (int64_t)(n_pairs + kF4Npp - 1) / kF4Npp + max_slots;
+    const int64_t grid = max_passes * row_blocks;
+    if (grid == 0) return K3G_OK;
+    if (grid > 0x7fffffff) return K3G_EUNSUPPORTED;
+    const size_t lds = (size_t)kF4Npp * NCK * f4::kChunkBytes;  // up to 80 KB: above the 64 KB default
+    if (lds > 65536 &&
+        hipFuncSetAttribute((const void *)moe_f4m_kernel<UP, NCK, kF4Npp>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return K3G_EHIP;
+    moe_f4m_kernel<UP, NCK, kF4Npp><<<(unsigned)grid, f4::kWaves * kWave, lds, st>>>(
+        out, pieces, hp, bank, active, offsets, perm, passes, top_k, latent, inter);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
+template <bool UP>
+static int launch_f4m_n(int n_in, float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank,
+                        const int32_t *active, const int32_t *offsets, const int32_t *perm, const int32_t *passes,
+                        int top_k, int latent, int inter, int n_pairs, int max_slots, hipStream_t st) {
+    switch (n_in / 128) {
+#define K3G_F4M(C)                                                                                                  \
+    case C:                                                                                                         \
+        return launch_f4m<UP, C>(out, pieces, hp, bank, active, offsets, perm, passes, top_k, latent, inter, n_pairs, \
+                                 max_slots, st);
+        K3G_F4M(4) K3G_F4M(8) K3G_F4M(12) K3G_F4M(16) K3G_F4M(20) K3G_F4M(24) K3G_F4M(28) K3G_F4M(32)
+#undef K3G_F4M
+        default: return K3G_EUNSUPPORTED;
+    }
+}
+
+int f4_pairs_per_pass() { return kF4Npp; }
+
+int launch_moe_up_f4m(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const int32_t *active,
+                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int top_k, int latent,
+                      int inter, int n_pairs, int max_slots, hipStream_t st) {
+    return launch_f4m_n<true>(latent, h, xp, hp, bank, active, offsets, perm, passes, top_k, latent, inter, n_pairs,
+                              max_slots, st);
+}
+
+int launch_moe_down_f4m(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
+                        const int32_t *offsets, const int32_t *passes, int latent, int inter, int n_pairs,
+                        int max_slots, hipStream_t st) {
+    return launch_f4m_n<false>(inter, ypair, hp, nullptr, bank, active, offsets, nullptr, passes, 1, latent, inter,
+                               n_pairs, max_slots, st);
 }
 
 // The up-projection also writes the pieces of h (hp) for the down-projection.

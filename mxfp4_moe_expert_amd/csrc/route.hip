@@ -517,11 +517,14 @@ __device__ inline int block_excl_scan(int v, int *wsum) {
     return res;
 }
 
+// With `passes` set (npp > 0), also the work table of the matrix-core layer:
+// every slot's pairs in passes of npp, passes[0] = their number, then
+// passes[1 + 2k], passes[2 + 2k] = (slot, pass index) in slot order.
 template <int NT>
 __global__ __launch_bounds__(NT) void bucket_kernel(int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ perm, int32_t *__restrict__ inv,
                                                     int32_t *__restrict__ active, const int32_t *__restrict__ idx,
-                                                    int T, int K, int E) {
+                                                    int T, int K, int E, int32_t *__restrict__ passes, int npp) {
     extern __shared__ int sm[];
     int *cnt = sm;                                        // [E]
     int *run = sm + E;                                    // [E]
@@ -558,6 +561,21 @@ __global__ __launch_bounds__(NT) void bucket_kernel(int32_t *__restrict__ counts
     if (tid == NT - 1) {
         offsets[E] = acc;  // the last thread's prefix + its own is the total
         active[0] = nacc;
+    }
+    if (passes) {  // uniform: every thread takes part in the scan
+        int np = 0;
+        for (int e = e0; e < e0 + per && e < E; ++e) np += (cnt[e] + npp - 1) / npp;
+        const int pbase = block_excl_scan<NT>(np, tmp);
+        int k = pbase, slot = nzbase;
+        for (int e = e0; e < e0 + per && e < E; ++e) {
+            if (cnt[e] == 0) continue;
+            for (int j = 0; j * npp < cnt[e]; ++j, ++k) {
+                passes[1 + 2 * k] = slot;
+                passes[2 + 2 * k] = j;
+            }
+            ++slot;
+        }
+        if (tid == NT - 1) passes[0] = k;
     }
     __syncthreads();
     const int tpc = (NT / K) < 64 ? (NT / K) : 64;  // tokens per chunk
@@ -634,9 +652,10 @@ size_t bucket_lds_bytes(int E) {
 }
 
 int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
-                  int T, int K, int E, hipStream_t st) {
+                  int T, int K, int E, hipStream_t st, int32_t *passes, int npp) {
     // one wavefront was measured slower for 16 pairs: its per-expert loops run 16x longer
-    bucket_kernel<1024><<<1, 1024, bucket_lds_bytes(E), st>>>(counts, offsets, perm, inv, active, idx, T, K, E);
+    bucket_kernel<1024><<<1, 1024, bucket_lds_bytes(E), st>>>(counts, offsets, perm, inv, active, idx, T, K, E,
+                                                              passes, npp);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

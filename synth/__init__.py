@@ -154,5 +154,6 @@ WORKLOADS = {
     "decode_b1": (SEED_BASE + 1, 1, 0.1, "exact"),
     "decode_b64": (SEED_BASE + 2, 64, 0.01, "exact"),
     "prefill_4096_idot": (SEED_BASE + 3, 4096, 0.01, "idot"),
+    "prefill_4096_exact": (SEED_BASE + 3, 4096, 0.01, "exact"),  # the same inputs, EXACT mode
     "block_256": (SEED_BASE + 4, 256, 0.1, "exact"),
 }

@@ -84,7 +84,7 @@ def check_block(k3g, src, bank, x, Wr, b, dense, K, tokens, mode=0):
         nrm_l = np.zeros(latent)
         for k in range(K):
             ex = src(int(idx[t, k]))
-            r = oracle.expert_glu(lat[t], ex, oracle.EXACT if mode == 0 else oracle.IDOT)
+            r = oracle.expert_glu(lat[t], ex, oracle.EXACT if (mode & 0xFF) == 0 else oracle.IDOT)
             W2 = np.abs(oracle.mxfp4_dequant(ex["w2p"], ex["w2s"]))
             ref += float(wts[t, k]) * r["y"].astype(np.float64)
             nrm_l += float(wts[t, k]) * (W2 @ np.abs(r["h"].astype(np.float64)))
@@ -110,23 +110,31 @@ def check_block(k3g, src, bank, x, Wr, b, dense, K, tokens, mode=0):
     return out
 
 
-def test_block_small(k3g):
-    H, L_, I, SI, E, K, T = 256, 128, 96, 64, 8, 2, 37
+@pytest.mark.parametrize("H,L_,I,SI,T,mfma", [(256, 128, 96, 64, 37, True),     # one workgroup per product
+                                               (512, 256, 128, 192, 100, True),  # K slices across segments
+                                               (224, 96, 96, 96, 37, False)],    # widths off 64: fp32 fma
+                         ids=["mfma_one_slice", "mfma_slices", "fma"])
+def test_block_small(k3g, H, L_, I, SI, T, mfma):
+    E, K = 8, 2
     src, bankt, bank = make_bank(k3g, 81, E, L_, I, 120, 123, 0.01)
     Wr, b = synth.router(81, E, H, 0.1)
     dense = synth.block_dense(81, hidden=H, latent=L_, shared_inter=SI, n_shared=2)
     x = synth.activations(81, T, H)
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L_, inter=I, hidden=H, sh_inter=SI, mode=0)
+    L = k3g.workspace_layout(k3g.OP_LATENT_BLOCK, sh)
+    assert bool(L["dxh"] and L["dxl"] and L["dxs"] and L["dpart"]) == mfma  # the form this shape takes
     out = check_block(k3g, src, bank, x, Wr, b, dense, K, tokens=range(T))
     # and against the oracle's whole block
     r = oracle.latent_block(x, Wr, b, dense, {e: src(e) for e in range(E)}, E, K, oracle.EXACT)
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
-def test_block_full_size_sampled(k3g, full_bank):
+@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+def test_block_full_size_sampled(k3g, full_bank, decode):
     src, bankt, bank = full_bank
     seed = synth.SEED_BASE + 4
     print("generating the block's dense weights", flush=True)
     Wr, b = synth.router(seed, 896, 7168, 0.1)
     dense = synth.block_dense(seed)
     x = synth.activations(seed, 256, 7168)
-    check_block(k3g, src, bank, x, Wr, b, dense, 16, tokens=[0, 255])
+    check_block(k3g, src, bank, x, Wr, b, dense, 16, tokens=[0, 255], mode=decode)

@@ -367,6 +367,57 @@ def test_layer_one_token_f4mma(k3g, case):
     check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=k3g.DECODE_MFMA)
 
 
+def check_pass_table(ws, L, E, npp=2):
+    """The bucket's work table for more tokens: every active expert's sorted
+    pairs npp at a time, in active order, then nothing."""
+    counts = ws_view(ws, L, "counts", E, np.int32)
+    active = ws_view(ws, L, "active", E + 1, np.int32)
+    want = [(s, j) for s, e in enumerate(active[1:1 + active[0]]) for j in range(-(-int(counts[e]) // npp))]
+    n = ws_view(ws, L, "passes", 1, np.int32)[0]
+    got = ws_view(ws, L, "passes", 1 + 2 * n, np.int32)[1:].reshape(-1, 2)
+    assert n == len(want)
+    assert [tuple(r) for r in got.tolist()] == want
+
+
+@pytest.mark.parametrize("case", ["ragged", "skewed", "wide_range", "topp", "one_expert"])
+def test_layer_tokens_f4mma(k3g, case):
+    # more tokens on the FP4 matrix cores: a workgroup takes one expert's sorted
+    # pairs two at a time (odd counts leave a one-pair pass)
+    E, latent, inter, T, K = 24, 1024, 512, 9, 6
+    if case == "skewed":
+        E, latent, inter, T, K = 6, 512, 1024, 40, 2
+    if case == "one_expert":
+        E, latent, inter, T, K = 4, 512, 512, 7, 1
+    src, bankt, bank = make_bank(k3g, 62, E, latent, inter, 110, 140, 0.02)
+    x = synth.activations(62, T, latent)
+    if case == "wide_range":
+        x = (x * 10.0 ** np.random.default_rng(62).uniform(-20, 20, x.shape)).astype(np.float32)
+    W, b = synth.router(62, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K, top_p=0.6 if case == "topp" else 0.0)
+    if case == "skewed":  # every token on expert 0, the second choice spread
+        idx = np.stack([np.zeros(T, np.int32), (np.arange(T) % 5 + 1).astype(np.int32)], 1)
+        wts = np.full((T, K), 0.5, np.float32)
+    if case == "one_expert":
+        idx = np.full((T, K), 2, np.int32)
+        wts = np.ones((T, K), np.float32)
+    if case == "topp":
+        assert (idx < 0).any()
+    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | k3g.DECODE_MFMA)
+    assert L["xp"] and L["hp"] and L["passes"]
+    check_pass_table(ws, L, E)
+    xp = ws_view(ws, L, "xp", T * latent // 128 * 1280, np.uint8).reshape(T, -1)
+    for t in range(T):
+        check_pieces(xp[t], x[t])
+    Pv = int(np.count_nonzero(idx >= 0))
+    h = ws_view(ws, L, "h", Pv * inter, np.float32).reshape(Pv, inter)
+    hp = ws_view(ws, L, "hp", Pv * inter // 128 * 1280, np.uint8).reshape(Pv, -1)
+    for p in range(Pv):
+        check_pieces(hp[p], h[p])
+    y = check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=k3g.DECODE_MFMA)
+    yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.EXACT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
+
+
 # ---- K3_TOPP ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,n_in,E,K", [(1, 3584, 896, 16), (8, 512, 896, 20), (3, 256, 2000, 16), (300, 512, 896, 16)],
@@ -426,14 +477,15 @@ def test_layer_small_topp(k3g):
     assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
-def test_layer_decode_b64_full_sampled(k3g, full_bank):
+@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+def test_layer_decode_b64_full_sampled(k3g, full_bank, decode):
     src, bankt, bank = full_bank
     seed = synth.SEED_BASE + 2
     W, b = synth.router(seed, 896, 3584, 0.01)
     x = synth.activations(seed, 64, 3584)
     io, wo, _ = oracle.route(x, W, b, 16)
     # sampled outputs: three tokens checked pair by pair
-    check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=[0, 31, 63])
+    check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=[0, 31, 63], decode=decode)
 
 
 # ---- the routed-expert cache: host memory -> HBM ------------------------------------------
