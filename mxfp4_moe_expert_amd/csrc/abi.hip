@@ -48,12 +48,12 @@ int launch_moe_up_f4(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &ba
                      int latent, int inter, int max_slots, hipStream_t st);
 int launch_moe_down_f4(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
                        const int32_t *offsets, int latent, int inter, int max_slots, hipStream_t st);
-int f4_pairs_per_pass();
+int f4_pairs_per_pass(int n_pairs, int n_experts);
 int launch_moe_up_f4m(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const int32_t *active,
-                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int top_k, int latent,
-                      int inter, int n_pairs, int max_slots, hipStream_t st);
+                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int npp, int top_k,
+                      int latent, int inter, int n_pairs, int max_slots, hipStream_t st);
 int launch_moe_down_f4m(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
-                        const int32_t *offsets, const int32_t *passes, int latent, int inter, int n_pairs,
+                        const int32_t *offsets, const int32_t *passes, int npp, int latent, int inter, int n_pairs,
                         int max_slots, hipStream_t st);
 bool f4_shape_ok(int latent, int inter);
 bool f4_bank_ok(const BankDev &b);
@@ -239,7 +239,7 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
                 // the pass table: each expert with pairs takes ceil(pairs / npp)
                 // passes, fewer than P / npp + 1 per expert in all
                 if (s.n_tokens > 1) {
-                    const size_t npp = (size_t)f4_pairs_per_pass();
+                    const size_t npp = (size_t)f4_pairs_per_pass((int)P, s.n_experts);
                     o->passes = c.take(sizeof(int32_t) * (1 + 2 * ((P + npp - 1) / npp + std::min(P, E))));
                 }
             }
@@ -496,7 +496,7 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
     const bool f4m = f4 && n_tokens > 1 && L.passes;
     uint8_t *xp = (uint8_t *)(w + L.xp), *hp = (uint8_t *)(w + L.hp);
     int32_t *passes = f4m ? (int32_t *)(w + L.passes) : nullptr;
-    const int npp = f4_pairs_per_pass();
+    const int npp = f4_pairs_per_pass(P, E);
     if (f4 && n_tokens > 1 && !f4m) return K3G_EINVAL;  // a layout without the pass table
     switch (stage) {
         case K3G_STAGE_BUCKET:
@@ -507,7 +507,7 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(xq, xs, x, n_tokens, latent, xqb, st) : K3G_OK;
         case K3G_STAGE_UP:
             if (f4m)
-                return launch_moe_up_f4m(h, hp, xp, b, active, offsets, perm, passes, top_k, latent, inter, P,
+                return launch_moe_up_f4m(h, hp, xp, b, active, offsets, perm, passes, npp, top_k, latent, inter, P,
                                          max_slots, st);
             if (f4) return launch_moe_up_f4(h, hp, xp, b, r1, top_k, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
@@ -519,7 +519,8 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
             return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, hqb, st) : K3G_OK;
         case K3G_STAGE_DOWN:
             if (f4m)
-                return launch_moe_down_f4m(ypair, hp, b, active, offsets, passes, latent, inter, P, max_slots, st);
+                return launch_moe_down_f4m(ypair, hp, b, active, offsets, passes, npp, latent, inter, P, max_slots,
+                                           st);
             if (f4) return launch_moe_down_f4(ypair, hp, b, active, offsets, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
                        ? launch_moe_down_idot(ypair, hq, hqb, hs, b, active, offsets, perm, latent, inter, max_slots, st)

@@ -509,6 +509,182 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
     }
 }
 
+// Denser routing (several pairs per expert): four pairs a pass and eight
+// wavefronts a workgroup sharing them (their 4 x 1280 bytes per chunk stay in
+// LDS, up to 160 KB), each wavefront owning four row tiles (UP: w1 and w3 of
+// 32 rows; DOWN: 64 rows). The loop runs chunk by chunk over all four tiles,
+// so each B fragment read from LDS feeds four products and each A fragment
+// four (one per pair): 16 products per chunk for 4 A and 4 B fragments.
+// Operand A streams through a 3-deep ring of 2-chunk blocks; B of the next
+// chunk is read while this chunk's products issue.
+template <bool UP, int NCK>
+__global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
+    float *__restrict__ out, const uint8_t *__restrict__ pieces, uint8_t *__restrict__ hp, BankDev bank,
+    const int32_t *__restrict__ active, const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ passes, int top_k, int latent, int inter) {
+    constexpr int NPP = 4, WAVES = 8, TILES = 4;
+    constexpr int CPB = 2, NB = NCK / CPB, NBUF = 3;
+    constexpr int ROWS_W = UP ? 32 : 64;
+    constexpr int ngrp = 4 * NCK;
+    constexpr int VEC = NCK * f4::kChunkBytes;
+    extern __shared__ uint4 lds_b[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n_out = UP ? inter : latent;
+    const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
+    const int k = blockIdx.x / row_blocks;
+    if (k >= passes[0]) return;  // whole workgroup
+    const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
+    const int e = active[1 + slot];
+    const int p0 = offsets[e] + pass * NPP;
+    const int np = min(NPP, offsets[e + 1] - p0);
+    const int r0 = ((blockIdx.x - k * row_blocks) * WAVES + wave) * ROWS_W;
+    const bool live = r0 < n_out;
+
+    const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
+    constexpr uint32_t pitch_p = 16u * ngrp, pitch_s = ngrp;
+    rsrc_t rp[TILES], rs[TILES];
+    uint32_t vp[TILES], vs[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
+        const uint32_t row = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
+        rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
+        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vs[t] = row * pitch_s;
+    }
+    const uint32_t dead = live ? 0u : kOffRange;
+    uint4 A[NBUF][TILES][CPB];
+    uint2 S[NBUF][TILES];
+    auto load_block = [&](int kb) {
+        const int b = kb % NBUF;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+#pragma unroll
+            for (int c = 0; c < CPB; ++c)
+                A[b][t][c] = buf_load16(rp[t], vp[t], (uint32_t)(CPB * kb + c) * 64u + dead);
+            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs[t], (int)vs[t], (int)((uint32_t)(CPB * kb) * 4u + dead), 0);
+            S[b][t] = make_uint2(sv[0], sv[1]);
+        }
+    };
+    // B: the pass's four vectors of pieces into LDS
+    {
+        const uint32_t lb = lds_addr(lds_b);
+        constexpr int units = VEC / 1024;
+#pragma unroll
+        for (int q = 0; q < NPP; ++q) {
+            const int pq = p0 + min(q, np - 1);
+            const int v = UP ? perm[pq] / top_k : pq;
+            const uint8_t *src = pieces + (size_t)v * VEC;
+            for (int u = wave; u < units; u += WAVES)
+                dma16(src, 1024u * u + 16u * lane, lb + (uint32_t)(q * VEC) + 1024u * u);
+        }
+    }
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int PRO = NBUF - 1 < NB ? NBUF - 1 : NB;
+#pragma unroll
+    for (int kb = 0; kb < PRO; ++kb) load_block(kb);
+    wait_vm<PRO * TILES * (CPB + 1)>();
+    __syncthreads();
+
+    const uint32_t qsh = 8u * (uint32_t)(lane >> 4);
+    float4_t acc[NPP][TILES];
+#pragma unroll
+    for (int q = 0; q < NPP; ++q)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[q][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    int li = lane;
+    __asm__ volatile("" : "+v"(li));
+    const uint4 *bq = lds_b + li;
+    const uint32_t *sq = (const uint32_t *)lds_b + 256 + li;
+    uint4 Bv[2][NPP];
+    uint32_t Bs[2][NPP];
+    auto read_b = [&](int i) {
+#pragma unroll
+        for (int q = 0; q < NPP; ++q) {
+            Bv[i & 1][q] = bq[(q * VEC + i * f4::kChunkBytes) / 16];
+            Bs[i & 1][q] = sq[(q * VEC + i * f4::kChunkBytes) / 4];
+        }
+    };
+    read_b(0);
+#pragma unroll
+    for (int i = 0; i < NCK; ++i) {
+        const int kb = i / CPB, c = i % CPB, b = kb % NBUF;
+        if (c == 0 && kb + NBUF - 1 < NB) load_block(kb + NBUF - 1);
+        if (i + 1 < NCK) read_b(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+            const uint32_t sd = c == 0 ? S[b][t].x : S[b][t].y;
+            const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
+            const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
+            const uint4 a = A[b][t][c];
+            const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < NPP; ++q) {
+                const uint4 bv = Bv[i & 1][q];
+                const v8i_t B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
+                acc[q][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av, B, acc[q][t], 4, 4, 0,
+                                                                             (int)(sa & keep), 0, (int)Bs[i & 1][q]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < NPP; ++q)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) __asm__ volatile("" : "+v"(acc[q][t]));
+
+    // per pair: sum the 16 piece columns, then lane qd = lane & 15 holds row
+    // tile ts = qd >> 2, row 4 * (lane >> 4) + (qd & 3) (UP: g and u of the
+    // wavefront's two row tiles, lanes qd < 8)
+    const int qd = lane & 15, v = qd & 3;
+#pragma unroll
+    for (int q = 0; q < NPP; ++q) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                float sm = acc[q][t][vv];
+                sm += dpp<0xB1>(sm);
+                sm += dpp<0x4E>(sm);
+                sm += dpp<0x141>(sm);
+                sm += dpp<0x140>(sm);
+                acc[q][t][vv] = sm;
+            }
+        // values, not references: a lane-dependent choice of an array element
+        // by reference puts the accumulators on the stack
+        float pv[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+            const float4_t x = acc[q][t];
+            pv[t] = v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
+        }
+        const bool store = live && q < np;
+        const int pq = p0 + q;
+        if constexpr (UP) {
+            const int ts = (qd >> 2) & 1;
+            const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+            const float g = ts ? pv[2] : pv[0], u = ts ? pv[3] : pv[1];
+            const float hv = situ(g, u);
+            if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
+            const int j = lane & 31;
+            const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
+            const int g32 = r0 / kGroup;
+            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+            split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
+                        store && lane < 32);
+        } else {
+            const int ts = qd >> 2;
+            const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+            const float y = ts == 0 ? pv[0] : ts == 1 ? pv[1] : ts == 2 ? pv[2] : pv[3];
+            if (store) out[(size_t)pq * n_out + row] = y;
+        }
+    }
+}
+
 // The matrix-core path takes whole 4-chunk blocks (512 entries; a row's
 // scale bytes in 16-byte loads), whole 32-row blocks and whole 4-chunk groups
 // of h's pieces: in and out sizes multiples of 512, at most 4096 (B -- a
@@ -557,58 +733,69 @@ static int launch_f4_n(int n_in, float *out, const uint8_t *pieces, uint8_t *hp,
 }
 
 // More tokens: the bucket's pass table drives the grid (an upper bound on the
-// passes: every slot's last pass may be short).
-constexpr int kF4Npp = 2;  // pairs per pass
+// passes: every slot's last pass may be short). Two pairs a pass when experts
+// see few pairs each (the 4-wavefront kernel), four when they see several on
+// average (the 8-wavefront kernel).
+int f4_pairs_per_pass(int n_pairs, int n_experts) { return n_pairs >= 3 * n_experts ? 4 : 2; }
 
 template <bool UP, int NCK>
-static int launch_f4m(float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank, const int32_t *active,
-                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int top_k, int latent,
-                      int inter, int n_pairs, int max_slots, hipStream_t st) {
+static int launch_f4m(int npp, float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank,
+                      const int32_t *active, const int32_t *offsets, const int32_t *perm, const int32_t *passes,
+                      int top_k, int latent, int inter, int n_pairs, int max_slots, hipStream_t st) {
     const int n_out = UP ? inter : latent;
-    const int row_blocks = (n_out / f4::kRows + f4::kWaves - 1) / f4::kWaves;
-    const int64_t max_passes = (int64_t)(n_pairs + kF4Npp - 1) / kF4Npp + max_slots;
+    const int rows_wg = npp == 4 ? 8 * (UP ? 32 : 64) : f4::kWaves * f4::kRows;
+    const int row_blocks = (n_out + rows_wg - 1) / rows_wg;
+    const int64_t max_passes = (int64_t)(n_pairs + npp - 1) / npp + max_slots;
     const int64_t grid = max_passes * row_blocks;
     if (grid == 0) return K3G_OK;
     if (grid > 0x7fffffff) return K3G_EUNSUPPORTED;
-    const size_t lds = (size_t)kF4Npp * NCK * f4::kChunkBytes;  // up to 80 KB: above the 64 KB default
-    if (lds > 65536 &&
-        hipFuncSetAttribute((const void *)moe_f4m_kernel<UP, NCK, kF4Npp>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return K3G_EHIP;
-    moe_f4m_kernel<UP, NCK, kF4Npp><<<(unsigned)grid, f4::kWaves * kWave, lds, st>>>(
-        out, pieces, hp, bank, active, offsets, perm, passes, top_k, latent, inter);
+    const size_t lds = (size_t)npp * NCK * f4::kChunkBytes;  // above the 64 KB default from 26 chunks on
+    if (npp == 4) {
+        if (lds > 65536 && hipFuncSetAttribute((const void *)moe_f4q_kernel<UP, NCK>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return K3G_EHIP;
+        moe_f4q_kernel<UP, NCK><<<(unsigned)grid, 8 * kWave, lds, st>>>(out, pieces, hp, bank, active, offsets, perm,
+                                                                       passes, top_k, latent, inter);
+    } else if (npp == 2) {
+        if (lds > 65536 &&
+            hipFuncSetAttribute((const void *)moe_f4m_kernel<UP, NCK, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return K3G_EHIP;
+        moe_f4m_kernel<UP, NCK, 2><<<(unsigned)grid, f4::kWaves * kWave, lds, st>>>(
+            out, pieces, hp, bank, active, offsets, perm, passes, top_k, latent, inter);
+    } else {
+        return K3G_EINVAL;
+    }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
 template <bool UP>
-static int launch_f4m_n(int n_in, float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank,
+static int launch_f4m_n(int n_in, int npp, float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank,
                         const int32_t *active, const int32_t *offsets, const int32_t *perm, const int32_t *passes,
                         int top_k, int latent, int inter, int n_pairs, int max_slots, hipStream_t st) {
     switch (n_in / 128) {
-#define K3G_F4M(C)                                                                                                  \
-    case C:                                                                                                         \
-        return launch_f4m<UP, C>(out, pieces, hp, bank, active, offsets, perm, passes, top_k, latent, inter, n_pairs, \
-                                 max_slots, st);
+#define K3G_F4M(C)                                                                                                 \
+    case C:                                                                                                        \
+        return launch_f4m<UP, C>(npp, out, pieces, hp, bank, active, offsets, perm, passes, top_k, latent, inter,   \
+                                 n_pairs, max_slots, st);
         K3G_F4M(4) K3G_F4M(8) K3G_F4M(12) K3G_F4M(16) K3G_F4M(20) K3G_F4M(24) K3G_F4M(28) K3G_F4M(32)
 #undef K3G_F4M
         default: return K3G_EUNSUPPORTED;
     }
 }
 
-int f4_pairs_per_pass() { return kF4Npp; }
-
 int launch_moe_up_f4m(float *h, uint8_t *hp, const uint8_t *xp, const BankDev &bank, const int32_t *active,
-                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int top_k, int latent,
-                      int inter, int n_pairs, int max_slots, hipStream_t st) {
-    return launch_f4m_n<true>(latent, h, xp, hp, bank, active, offsets, perm, passes, top_k, latent, inter, n_pairs,
-                              max_slots, st);
+                      const int32_t *offsets, const int32_t *perm, const int32_t *passes, int npp, int top_k,
+                      int latent, int inter, int n_pairs, int max_slots, hipStream_t st) {
+    return launch_f4m_n<true>(latent, npp, h, xp, hp, bank, active, offsets, perm, passes, top_k, latent, inter,
+                              n_pairs, max_slots, st);
 }
 
 int launch_moe_down_f4m(float *ypair, const uint8_t *hp, const BankDev &bank, const int32_t *active,
-                        const int32_t *offsets, const int32_t *passes, int latent, int inter, int n_pairs,
+                        const int32_t *offsets, const int32_t *passes, int npp, int latent, int inter, int n_pairs,
                         int max_slots, hipStream_t st) {
-    return launch_f4m_n<false>(inter, ypair, hp, nullptr, bank, active, offsets, nullptr, passes, 1, latent, inter,
-                               n_pairs, max_slots, st);
+    return launch_f4m_n<false>(inter, npp, ypair, hp, nullptr, bank, active, offsets, nullptr, passes, 1, latent,
+                               inter, n_pairs, max_slots, st);
 }
 
 // The up-projection also writes the pieces of h (hp) for the down-projection.

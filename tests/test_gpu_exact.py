@@ -367,7 +367,13 @@ def test_layer_one_token_f4mma(k3g, case):
     check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=k3g.DECODE_MFMA)
 
 
-def check_pass_table(ws, L, E, npp=2):
+def pairs_per_pass(P, E):
+    """The layer takes four pairs a pass when P >= 3 E (several pairs per
+    expert on average), else two."""
+    return 4 if P >= 3 * E else 2
+
+
+def check_pass_table(ws, L, E, npp):
     """The bucket's work table for more tokens: every active expert's sorted
     pairs npp at a time, in active order, then nothing."""
     counts = ws_view(ws, L, "counts", E, np.int32)
@@ -379,32 +385,39 @@ def check_pass_table(ws, L, E, npp=2):
     assert [tuple(r) for r in got.tolist()] == want
 
 
-@pytest.mark.parametrize("case", ["ragged", "skewed", "wide_range", "topp", "one_expert"])
+@pytest.mark.parametrize("case", ["ragged", "skewed", "wide_range", "topp", "one_expert", "dense4", "dense4_topp"])
 def test_layer_tokens_f4mma(k3g, case):
     # more tokens on the FP4 matrix cores: a workgroup takes one expert's sorted
-    # pairs two at a time (odd counts leave a one-pair pass)
+    # pairs two or four at a time (short last passes of 1..3 pairs)
     E, latent, inter, T, K = 24, 1024, 512, 9, 6
-    if case == "skewed":
+    if case == "skewed":  # four a pass: 40 pairs on expert 0, 8 on each other
         E, latent, inter, T, K = 6, 512, 1024, 40, 2
     if case == "one_expert":
         E, latent, inter, T, K = 4, 512, 512, 7, 1
+    if case.startswith("dense4"):  # four a pass, every count mod 4 present
+        E, latent, inter, T, K = 10, 1536, 1024, 23, 4
     src, bankt, bank = make_bank(k3g, 62, E, latent, inter, 110, 140, 0.02)
     x = synth.activations(62, T, latent)
     if case == "wide_range":
         x = (x * 10.0 ** np.random.default_rng(62).uniform(-20, 20, x.shape)).astype(np.float32)
     W, b = synth.router(62, E, latent, 0.2)
-    idx, wts, _ = oracle.route(x, W, b, K, top_p=0.6 if case == "topp" else 0.0)
+    idx, wts, _ = oracle.route(x, W, b, K, top_p=0.6 if case.endswith("topp") else 0.0)
     if case == "skewed":  # every token on expert 0, the second choice spread
         idx = np.stack([np.zeros(T, np.int32), (np.arange(T) % 5 + 1).astype(np.int32)], 1)
         wts = np.full((T, K), 0.5, np.float32)
     if case == "one_expert":
         idx = np.full((T, K), 2, np.int32)
         wts = np.ones((T, K), np.float32)
-    if case == "topp":
+    if case.endswith("topp"):
         assert (idx < 0).any()
+    npp = pairs_per_pass(T * K, E)
+    assert npp == (4 if case in ("skewed", "dense4", "dense4_topp") else 2)
     y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | k3g.DECODE_MFMA)
     assert L["xp"] and L["hp"] and L["passes"]
-    check_pass_table(ws, L, E)
+    check_pass_table(ws, L, E, npp)
+    if case == "dense4":
+        counts = ws_view(ws, L, "counts", E, np.int32)
+        assert set((counts[counts > 0] % 4).tolist()) == {0, 1, 2, 3}, counts
     xp = ws_view(ws, L, "xp", T * latent // 128 * 1280, np.uint8).reshape(T, -1)
     for t in range(T):
         check_pieces(xp[t], x[t])
