@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_PEAK_I8_TOPS = 5000.0      # MI355X dense int8 matrix, published (tera-ops)
 MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+MFMA_PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4 matrix, published
 N_ROT = 64                 # distinct tokens the decode steps cycle through
 
 
@@ -108,15 +109,19 @@ def main():
     if args.workload == "decode_b1" and not args.no_secondary:
         # the other configurations on the same resident bank, shorter runs (not the headline)
         others = []
-        for wl, steps, warm, bf16, p in (("decode_b1", 100, 10, False, 0.9), ("decode_b64", 20, 3, False, 0.0),
-                                         ("prefill_4096_idot", 10, 2, False, 0.0),
-                                         ("prefill_4096_idot", 10, 2, True, 0.0)):
-            r, _ = run_workload(ctx, wl, steps, warm, bf16, top_p=p)
+        for wl, steps, warm, bf16, p, f4 in (("decode_b1", 100, 10, False, 0.9, False),
+                                             ("decode_b64", 20, 3, False, 0.0, False),
+                                             ("decode_b64", 20, 3, False, 0.0, True),
+                                             ("prefill_4096_idot", 10, 2, False, 0.0, False),
+                                             ("prefill_4096_idot", 10, 2, True, 0.0, False),
+                                             ("prefill_4096_exact", 5, 1, False, 0.0, True)):
+            r, _ = run_workload(ctx, wl, steps, warm, bf16, mfma_decode=f4, top_p=p)
             others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
                                              "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
-        # the full LatentMoE block at 256 tokens
+        # the full LatentMoE block at 256 tokens, the routed layer in both forms
         result["block_256"] = run_block(ctx, bank)
+        result["block_256_fp4_mfma"] = run_block(ctx, bank, mfma_decode=True)
         # the Vulkan-tier scale format: the same product with f32 per-group scales
         result["scale_format"] = run_scale_format(ctx)
         # the expert streaming tier: the bank in pinned host memory, an LRU of slots in HBM
@@ -284,6 +289,13 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
         "traffic": measured_traffic(workload, "moe_up"),
         "algorithmic_bytes_per_launch": int(up_alg),
     }
+    if f4:
+        # the FP4 matrix-core work the up kernel issues: every pair's w1 and w3
+        # rows against its 16 pieces of x (2 ops per multiply-add)
+        f4_ops = 2.0 * P * 2 * I * L * 16
+        f4_t = f4_ops / (stage_ms["up"] * 1e-3) / 1e12
+        roof["mfma_fp4_achieved_TFLOPs"] = round(f4_t, 1)
+        roof["mfma_fp4_frac"] = round(f4_t / MFMA_PEAK_FP4_TFLOPS, 4)
     if mode == k3g.IDOT:
         # matrix-core work of the up kernel: 2 ops per multiply-add, w1 and w3 rows, every pair
         up_ops = 2.0 * P * 2 * I * L
@@ -398,7 +410,8 @@ def run_block(ctx, bank, reps=10, mfma_decode=False):
     ms = e0.elapsed_time(e1) / reps
     # dense matrix work: down, up, and per shared expert w1, w3 and w2 (2 flops per product)
     flops = 2.0 * T * (2 * H * Lt + 2 * 3 * H * SI)
-    out_d = {"tokens": T, "ms_per_block": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+    out_d = {"tokens": T, "layer": "fp4-mfma" if mfma_decode else "vector",
+             "ms_per_block": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
              "dense_flops": flops, "dense_TFLOPs_if_all_time": round(flops / (ms * 1e-3) / 1e12, 1)}
     del dense, ws, out, x
     torch.cuda.empty_cache()
