@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
     ap.add_argument("--stream-steps", type=int, default=40,
                     help="decode steps per cache size in the streaming-tier measurement")
+    ap.add_argument("--expert-only", action="store_true",
+                    help="only time one expert on one token and the batch-1 product (for profiling) and exit")
     ap.add_argument("--block-only", action="store_true",
                     help="only time the 256-token LatentMoE block (for profiling) and exit")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -100,6 +102,9 @@ def main():
     print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
 
     ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager)
+    if args.expert_only:
+        print(json.dumps({"expert_b1": run_expert(ctx, bankt)}), flush=True)
+        return
     if args.block_only:
         print(json.dumps({"block_256": run_block(ctx, bank, mfma_decode=args.mfma_decode)}), flush=True)
         return
@@ -119,6 +124,8 @@ def main():
             others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
                                              "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
+        # one expert on one token, and the batch-1 product on one w1
+        result["expert_b1"] = run_expert(ctx, bankt)
         # the full LatentMoE block at 256 tokens, the routed layer in both forms
         result["block_256"] = run_block(ctx, bank)
         result["block_256_fp4_mfma"] = run_block(ctx, bank, mfma_decode=True)
@@ -416,6 +423,84 @@ def run_block(ctx, bank, reps=10, mfma_decode=False):
     del dense, ws, out, x
     torch.cuda.empty_cache()
     return out_d
+
+
+def run_expert(ctx, bankt, n_rot=64, reps=5):
+    """One SiTU-GLU expert on one token (k3g_expert_glu: 17,547,264 B of
+    weights + x and y), and the batch-1 product on one w1 (k3g_mxfp4_gemv,
+    3072 x 3584). Each call takes the next of n_rot experts spread over the
+    bank (1.12 GB, past the 256 MB Infinity Cache). Back to back: a HIP graph
+    of n_rot calls, HIP events around `reps` replays. Per launch: HIP events
+    around each call alone, the device idle before it."""
+    torch, k3g, synth, dev = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"]
+    L, I, E = synth.LATENT, synth.INTER, synth.N_EXPERTS
+    off, stride = k3g.bank_layout(L, I)
+    shapes = {"w1p": (I, L // 2), "w1s": (I, L // 32), "w3p": (I, L // 2), "w3s": (I, L // 32),
+              "w2p": (L, I // 2), "w2s": (L, I // 32)}
+    keys = ("w1p", "w1s", "w3p", "w3s", "w2p", "w2s")
+    experts = []
+    for i in range(n_rot):
+        e = (i * E) // n_rot
+        base = e * stride
+        experts.append({k: bankt[base + off[j]: base + off[j] + shapes[k][0] * shapes[k][1]].view(*shapes[k])
+                        for j, k in enumerate(keys)})
+    x = torch.from_numpy(synth.activations(ctx["seed_bank"], 1, L)[0]).to(dev)
+    y = torch.empty(L, dtype=torch.float32, device=dev)
+    yg = torch.empty(I, dtype=torch.float32, device=dev)
+    ws = k3g.workspace(k3g.OP_EXPERT_GLU, k3g.shape(n_tokens=1, top_k=1, n_experts=1, latent=L, inter=I,
+                                                     mode=k3g.EXACT))
+    stream = torch.cuda.current_stream()
+
+    def glu(i):
+        k3g.k3g_expert_glu(y, x, experts[i % n_rot], k3g.EXACT, ws)
+
+    def gemv(i):
+        ex = experts[i % n_rot]
+        k3g.k3g_mxfp4_gemv(yg, x, ex["w1p"], ex["w1s"])
+
+    def graph_us(fn):
+        for i in range(n_rot):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_rot):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * n_rot)
+
+    def launch_us(fn):
+        ts = []
+        for i in range(n_rot):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    up_b, dn_b = expert_bytes(L, I)
+    glu_bytes = up_b + dn_b + 2 * L * 4
+    gemv_bytes = up_b // 2 + L * 4 + I * 4
+    out = {"experts_rotated": n_rot, "timing": "graph: HIP events around replays of a graph of one call per "
+           "expert; per launch: median over the experts of HIP events around one call on an idle device"}
+    for name, fn, nbytes in (("expert_glu", glu, glu_bytes), ("gemv_w1", gemv, gemv_bytes)):
+        tg, tl = graph_us(fn), launch_us(fn)
+        out[name] = {"bytes": int(nbytes), "graph_us": round(tg, 2), "graph_GBps": round(nbytes / tg / 1e3, 1),
+                     "graph_hbm_frac": round(nbytes / tg / 1e3 / HBM_PEAK_GBS, 4),
+                     "launch_us": round(tl, 2), "launch_GBps": round(nbytes / tl / 1e3, 1)}
+    del experts, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_scale_format(ctx, n_mat=8, launches=64):

@@ -167,7 +167,32 @@ __device__ inline void load_x(float *xr, const float *x, int lane, int ngrp) {
     }
 }
 
-// y[r] for r in [0, rows): one matrix, one x. Items of rpi rows. F32S: the
+// x shared by every wavefront of the workgroup: copied once into LDS (a
+// float4 per thread per step), then each lane reads its groups from there
+// instead of every wavefront fetching the whole of x from L2.
+__device__ inline void stage_x(float *xs, const float *x, int len) {
+    for (int i = 4 * threadIdx.x; i < len; i += 4 * blockDim.x) *(float4 *)(xs + i) = *(const float4 *)(x + i);
+    __syncthreads();
+}
+
+template <int NG>
+__device__ inline void load_x_lds(float *xr, const float *xs, int lane, int ngrp) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = lane * NG + i;
+        const int gc = g < ngrp ? g : ngrp - 1;
+#pragma unroll
+        for (int j = 0; j < kGroup; j += 4) {
+            const float4 v = *(const float4 *)(xs + gc * kGroup + j);
+            xr[i * kGroup + j + 0] = v.x;
+            xr[i * kGroup + j + 1] = v.y;
+            xr[i * kGroup + j + 2] = v.z;
+            xr[i * kGroup + j + 3] = v.w;
+        }
+    }
+}
+
+// y[r] for r in [0, rows): one matrix, one x (staged in LDS). Items of rpi rows. F32S: the
 // scales are fp32 per group (the pages' Vulkan-tier format).
 template <int NG, bool LUT, bool F32S = false>
 __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *__restrict__ y, const float *__restrict__ x,
@@ -192,18 +217,32 @@ __global__ __launch_bounds__(K3G_GEMV_THREADS) K3G_OCC void gemv_kernel(float *_
         mat.pitch_s = 4u * (uint32_t)ngrp;
         mat.s = make_rsrc(scales, mat.pitch_s * (uint32_t)rows);
     }
-    float xr[NG * kGroup];
-    load_x<NG>(xr, x, lane, ngrp);
     const int n_items = (rows + rpi - 1) / rpi;
-    for (int item = blockIdx.x * waves + wave; item < n_items; item += gridDim.x * waves) {
+    int item = blockIdx.x * waves + wave;
+    RowData<NG> buf[K3G_PIPE];
+    // the first item's rows go out before x is staged, so the two waits overlap
+    if (item < n_items) {
+        const int r0 = item * rpi, r1 = min(rows, r0 + rpi);
+#pragma unroll
+        for (int st = 0; st < K3G_PIPE; ++st) {
+            load_row<NG, false, F32S>(buf[st], mat, min(r0 + st, r1 - 1), cols);
+            __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (see below)
+        }
+    }
+    extern __shared__ float xs_lds[];  // [in]
+    stage_x(xs_lds, x, in);
+    float xr[NG * kGroup];
+    load_x_lds<NG>(xr, xs_lds, lane, ngrp);
+    for (bool first = true; item < n_items; item += gridDim.x * waves, first = false) {
         const int r0 = item * rpi;
         const int r1 = min(rows, r0 + rpi);
         auto R = [&](int r) { return min(r, r1 - 1); };
-        RowData<NG> buf[K3G_PIPE];
+        if (!first) {
 #pragma unroll
-        for (int st = 0; st < K3G_PIPE; ++st) {
-            load_row<NG, false, F32S>(buf[st], mat, R(r0 + st), cols);
-            __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (see below)
+            for (int st = 0; st < K3G_PIPE; ++st) {
+                load_row<NG, false, F32S>(buf[st], mat, R(r0 + st), cols);
+                __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (see below)
+            }
         }
         float acc = 0.f;  // lane k holds row (r - r0) % 64 == k until its block of 64 is stored
         // every work item has at least one row: a do-while keeps the loads of x
@@ -470,6 +509,14 @@ static int pick_ng(int ngrp) {
     return 0;
 }
 
+// The LUT forms hold 64 KB of static LDS; with x in LDS beside it they are
+// above the 64 KB a kernel gets without asking.
+template <typename K>
+static bool allow_lds(K *kernel, bool lut, size_t dyn) {
+    return !lut || dyn == 0 ||
+           hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) == hipSuccess;
+}
+
 static int grid_for(int items, int waves_per_block) {
     // enough blocks to cover the items once, capped at 4 blocks per CU
     const int need = (items + waves_per_block - 1) / waves_per_block;
@@ -481,14 +528,16 @@ int launch_gemv(float *y, const float *x, const uint8_t *packed, const uint8_t *
     const int ngrp = in / kGroup;
     const int ng = pick_ng(ngrp);
     // rows per item: aim for ~2048 items so every SIMD of the chip has work
+    // rows per item: ~2048 items, at least one pipeline's worth of rows
     int rpi = rows / 2048;
-    if (rpi < 2) rpi = 2;
+    if (rpi < K3G_PIPE) rpi = K3G_PIPE;
+    const size_t xb = sizeof(float) * (size_t)in;  // x in LDS
     const int items = (rows + rpi - 1) / rpi;
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
     switch (ng) {
-        case 1: if (lut) gemv_kernel<1, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<1, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
-        case 2: if (lut) gemv_kernel<2, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<2, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
-        case 4: if (lut) gemv_kernel<4, true><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<4, false><<<grid, block, 0, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        case 1: if (!allow_lds(gemv_kernel<1, true>, lut, xb)) return K3G_EHIP; if (lut) gemv_kernel<1, true><<<grid, block, xb, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<1, false><<<grid, block, xb, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        case 2: if (!allow_lds(gemv_kernel<2, true>, lut, xb)) return K3G_EHIP; if (lut) gemv_kernel<2, true><<<grid, block, xb, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<2, false><<<grid, block, xb, st>>>(y, x, packed, scales, in, rows, rpi); break;
+        case 4: if (!allow_lds(gemv_kernel<4, true>, lut, xb)) return K3G_EHIP; if (lut) gemv_kernel<4, true><<<grid, block, xb, st>>>(y, x, packed, scales, in, rows, rpi); else gemv_kernel<4, false><<<grid, block, xb, st>>>(y, x, packed, scales, in, rows, rpi); break;
         default: return K3G_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
@@ -516,24 +565,27 @@ int launch_gemv_f32s(float *y, const float *x, const uint8_t *packed, const floa
                      hipStream_t st) {
     const int ngrp = in / kGroup;
     const int ng = pick_ng(ngrp);
+    // rows per item: ~2048 items, at least one pipeline's worth of rows
     int rpi = rows / 2048;
-    if (rpi < 2) rpi = 2;
+    if (rpi < K3G_PIPE) rpi = K3G_PIPE;
+    const size_t xb = sizeof(float) * (size_t)in;  // x in LDS
     const int items = (rows + rpi - 1) / rpi;
     const dim3 grid(grid_for(items, K3G_GEMV_THREADS / kWave)), block(K3G_GEMV_THREADS);
     const uint8_t *sc = (const uint8_t *)scales;
     switch (ng) {
-        case 1: gemv_kernel<1, false, true><<<grid, block, 0, st>>>(y, x, packed, sc, in, rows, rpi); break;
-        case 2: gemv_kernel<2, false, true><<<grid, block, 0, st>>>(y, x, packed, sc, in, rows, rpi); break;
-        case 4: gemv_kernel<4, false, true><<<grid, block, 0, st>>>(y, x, packed, sc, in, rows, rpi); break;
+        case 1: gemv_kernel<1, false, true><<<grid, block, xb, st>>>(y, x, packed, sc, in, rows, rpi); break;
+        case 2: gemv_kernel<2, false, true><<<grid, block, xb, st>>>(y, x, packed, sc, in, rows, rpi); break;
+        case 4: gemv_kernel<4, false, true><<<grid, block, xb, st>>>(y, x, packed, sc, in, rows, rpi); break;
         default: return K3G_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
-// Rows per work item: about `target` items in all, at least 8 rows each.
+// Rows per work item: about `target` items in all, at least one pipeline's
+// worth of rows each (a single expert is cut finer than a decode step's 16).
 static int rows_per_item(int max_slots, int rows, int target) {
     int rpi = (int)(((int64_t)max_slots * rows + target - 1) / target);
-    if (rpi < 8) rpi = 8;
+    if (rpi < K3G_PIPE) rpi = K3G_PIPE;
     return rpi > rows ? rows : rpi;
 }
 
