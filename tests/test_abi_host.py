@@ -87,3 +87,60 @@ def test_rejects_bad_arguments_before_any_launch(k3g):
     assert L.k3g_moe_layer(P(1 << 20), P(2 << 20), P(3 << 20), P(4 << 20), C.byref(bank128), 2, 2, 1, P(1 << 24),
                            1 << 24, None) == -2
     assert L.k3g_status_string(-3) == b"workspace too small"
+
+
+def region_sizes(L):
+    """Each region's room: the distance to the next region (or to the end)."""
+    starts = sorted((v, k) for k, v in L.items() if k != "total" and v)
+    room = {}
+    for i, (v, k) in enumerate(starts):
+        room[k] = (starts[i + 1][0] if i + 1 < len(starts) else L["total"]) - v
+    return room
+
+
+@pytest.mark.parametrize("T", [1, 64, 4096])
+def test_fp4_layer_workspace(k3g, T):
+    # K3G_DECODE_MFMA: x of every token and h of every pair as 16 e2m1 pieces
+    # (10 bytes per entry); more than one token also gets the table of passes,
+    # two pairs a pass below 3 pairs per expert on average, else four
+    E, K, lat, inter = 896, 16, 3584, 3072
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=lat, inter=inter, mode=k3g.EXACT | k3g.DECODE_MFMA)
+    L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
+    room = region_sizes(L)
+    P = T * K
+    assert room["xp"] >= T * lat // 128 * 1280
+    assert room["hp"] >= P * inter // 128 * 1280
+    if T == 1:
+        assert L["passes"] == 0
+    else:
+        npp = 4 if P >= 3 * E else 2
+        assert npp == (4 if T == 4096 else 2)
+        assert room["passes"] >= 4 * (1 + 2 * (-(-P // npp) + min(P, E)))
+    # the vector form has none of these regions
+    L0 = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=lat,
+                                                          inter=inter, mode=k3g.EXACT))
+    assert L0["xp"] == L0["hp"] == L0["passes"] == 0
+
+
+@pytest.mark.parametrize("H,lat,SI,mfma", [(7168, 3584, 6144, True), (256, 128, 64, True),
+                                           (224, 96, 96, False), (256, 128, 96, "no_shared")])
+def test_block_dense_workspace(k3g, H, lat, SI, mfma):
+    # the block's dense products on the bf16 matrix cores: three bf16 pieces per
+    # entry of x, of the normalised aggregate and of both shared h (tokens padded
+    # to 64), and the K-slice partials; widths off 64 keep the fp32 fma kernels
+    T = 256
+    sh = k3g.shape(n_tokens=T, top_k=16, n_experts=896, latent=lat, inter=3072 if lat == 3584 else 96,
+                   hidden=H, sh_inter=SI, mode=k3g.EXACT)
+    L = k3g.workspace_layout(k3g.OP_LATENT_BLOCK, sh)
+    room = region_sizes(L)
+    t64 = -(-T // 64) * 64
+    if mfma is False:
+        assert L["dxh"] == L["dxl"] == L["dxs"] == L["dpart"] == 0
+        return
+    assert room["dxh"] >= t64 * H * 6
+    if mfma == "no_shared":  # a shared width off 64: the shared pieces are absent, and so is the up form
+        assert L["dxs"] == 0 and L["dxl"] == 0
+        return
+    assert room["dxl"] >= t64 * lat * 6 and room["dxs"] >= 2 * t64 * SI * 6
+    # the partials hold the largest product's slices: at least one slice of each
+    assert room["dpart"] >= 4 * max(T * lat, 2 * T * SI, T * H)
