@@ -82,7 +82,8 @@ typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
  * (one ue8m0 scale per 32 entries each, entries below 2^-127 dropped); every
  * product is exact and sums are fp32, as in the vector form, so both meet the
  * same bound. With more than one token each workgroup takes one expert's
- * sorted pairs two at a time, so each weight row is read once per two pairs.
+ * sorted pairs 2, 4 or 8 at a time (by the average pairs per expert: below
+ * 3, below 6, else), so each weight row is read once per pass.
  * Needs latent and inter multiples of 512 (at most 4096) and a bank with
  * 16-byte aligned scale tensors and stride; otherwise the vector kernels run. */
 #define K3G_DECODE_MFMA 0x400

@@ -532,6 +532,10 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n_out = UP ? inter : latent;
     const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
+    // workgroup = (pass, row block), row blocks fastest: the workgroups running
+    // at once cover every row block of a few passes (an order with the passes
+    // fastest, for L2 sharing between the passes of one expert, measured
+    // slower: all of them then read the same rows of different experts)
     const int k = blockIdx.x / row_blocks;
     if (k >= passes[0]) return;  // whole workgroup
     const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
@@ -685,6 +689,187 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     }
 }
 
+// Dense routing (many pairs per expert): eight pairs a pass, so an expert's
+// weights stream once per eight pairs. Their pieces do not fit in LDS whole
+// (8 x 1280 bytes per chunk), so they stream through it chunk by chunk in a
+// ring of 3 buffers, two chunks ahead: wavefront w brings pair w's 1 KB of
+// pieces and 256 bytes of scales of each chunk (two DMA instructions, the same
+// count in every wavefront, so the waits are exact). Eight wavefronts, four
+// row tiles each (UP: w1 and w3 of 32 rows; DOWN: 64 rows); operand A in a
+// 4-deep ring of single chunks; per chunk each B fragment feeds four products
+// and each A fragment eight.
+template <bool UP, int NCK>
+__global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
+    float *__restrict__ out, const uint8_t *__restrict__ pieces, uint8_t *__restrict__ hp, BankDev bank,
+    const int32_t *__restrict__ active, const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ passes, int top_k, int latent, int inter) {
+    constexpr int NPP = 8, WAVES = 8, TILES = 4, NBUF = 4, NBB = 3;
+    constexpr int ROWS_W = UP ? 32 : 64;
+    constexpr int ngrp = 4 * NCK;
+    constexpr int VEC = NCK * f4::kChunkBytes;
+    constexpr int BBUF = NPP * f4::kChunkBytes;  // one chunk of all pairs: 10 KB
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[NBB * BBUF];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n_out = UP ? inter : latent;
+    const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
+    // workgroup = (pass, row block), row blocks fastest: the workgroups running
+    // at once cover every row block of a few passes (an order with the passes
+    // fastest, for L2 sharing between the passes of one expert, measured
+    // slower: all of them then read the same rows of different experts)
+    const int k = blockIdx.x / row_blocks;
+    if (k >= passes[0]) return;  // whole workgroup
+    const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
+    const int e = active[1 + slot];
+    const int p0 = offsets[e] + pass * NPP;
+    const int np = min(NPP, offsets[e + 1] - p0);
+    const int r0 = ((blockIdx.x - k * row_blocks) * WAVES + wave) * ROWS_W;
+    const bool live = r0 < n_out;
+
+    const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
+    constexpr uint32_t pitch_p = 16u * ngrp, pitch_s = ngrp;
+    rsrc_t rp[TILES], rs[TILES];
+    uint32_t vp[TILES], vs[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
+        const uint32_t row = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
+        rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
+        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vs[t] = row * pitch_s;
+    }
+    const uint32_t dead = live ? 0u : kOffRange;
+    uint4 A[NBUF][TILES];
+    uint32_t S[NBUF][TILES];
+    auto load_a = [&](int i) {
+        const int b = i % NBUF;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+            A[b][t] = buf_load16(rp[t], vp[t], (uint32_t)i * 64u + dead);
+            S[b][t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs[t], (int)vs[t], (int)((uint32_t)i * 4u + dead), 0);
+        }
+    };
+    // this wavefront's pair (the pass's last pair again past its end)
+    const int pw = p0 + min(wave, np - 1);
+    const uint8_t *src = pieces + (size_t)(UP ? perm[pw] / top_k : pw) * VEC;
+    const uint32_t lb = lds_addr(lds_b);
+    auto dma_b = [&](int i) {
+        const uint32_t dst = lb + (uint32_t)((i % NBB) * BBUF + wave * f4::kChunkBytes);
+        const uint8_t *s = src + (size_t)i * f4::kChunkBytes;
+        dma16(s, 16u * lane, dst);
+        dma4(s + 1024, 4u * lane, dst + 1024);
+    };
+    constexpr int VM_A = 2 * TILES;  // vector loads of one chunk of A
+    // prologue: B of chunks 0 and 1, then A of chunks 0 .. NBUF-2
+    dma_b(0);
+    if (NCK > 1) dma_b(1);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (i < NCK) load_a(i);
+    wait_vm<(NBUF - 1) * VM_A>();
+    __syncthreads();
+
+    const uint32_t qsh = 8u * (uint32_t)(lane >> 4);
+    float4_t acc[NPP][TILES];
+#pragma unroll
+    for (int q = 0; q < NPP; ++q)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[q][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    int li = lane;
+    __asm__ volatile("" : "+v"(li));
+#pragma unroll
+    for (int i = 0; i < NCK; ++i) {
+        const int b = i % NBUF;
+        // requests: B two chunks ahead, then A NBUF-1 chunks ahead
+        if (i + 2 < NCK) dma_b(i + 2);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + NBUF - 1 < NCK) load_a(i + NBUF - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 *bq = (const uint4 *)(lds_b + (i % NBB) * BBUF) + li;
+        const uint32_t *sq = (const uint32_t *)(lds_b + (i % NBB) * BBUF + 1024) + li;
+        uint32_t sa[TILES];
+        v8i_t Av[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+            sa[t] = __builtin_amdgcn_ubfe(S[b][t], qsh, 8);
+            const uint32_t keep = sa[t] == 255u ? 0u : ~0u;  // scale 255: the group is left out
+            const uint4 a = A[b][t];
+            Av[t] = v8i_t{(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
+            sa[t] &= keep;
+        }
+#pragma unroll
+        for (int q = 0; q < NPP; ++q) {
+            const uint4 bv = bq[q * (f4::kChunkBytes / 16)];
+            const uint32_t bs = sq[q * (f4::kChunkBytes / 4)];
+            const v8i_t B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < TILES; ++t)
+                acc[q][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av[t], B, acc[q][t], 4, 4, 0, (int)sa[t],
+                                                                             0, (int)bs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // chunk i+1's B is in LDS for every wavefront, and every wavefront is
+        // done with buffer i % 3 before chunk i+3 is brought into it. Issued
+        // after chunk i+1's B: A of chunk i+NBUF-2, B of chunk i+2, A of chunk
+        // i+NBUF-1 (when they exist)
+        if (i + 1 < NCK) {
+            if (i + NBUF - 1 < NCK) wait_vm<2 * VM_A + 2>();
+            else wait_vm<0>();
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NPP; ++q)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) __asm__ volatile("" : "+v"(acc[q][t]));
+
+    // per pair, as in the four-pair kernel
+    const int qd = lane & 15, v = qd & 3;
+#pragma unroll
+    for (int q = 0; q < NPP; ++q) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                float sm = acc[q][t][vv];
+                sm += dpp<0xB1>(sm);
+                sm += dpp<0x4E>(sm);
+                sm += dpp<0x141>(sm);
+                sm += dpp<0x140>(sm);
+                acc[q][t][vv] = sm;
+            }
+        float pv[TILES];  // values: a lane-dependent choice by reference would go through scratch
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+            const float4_t x = acc[q][t];
+            pv[t] = v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
+        }
+        const bool store = live && q < np;
+        const int pq = p0 + q;
+        if constexpr (UP) {
+            const int ts = (qd >> 2) & 1;
+            const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+            const float hv = situ(ts ? pv[2] : pv[0], ts ? pv[3] : pv[1]);
+            if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
+            const int j = lane & 31;
+            const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
+            const int g32 = r0 / kGroup;
+            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+            split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
+                        store && lane < 32);
+        } else {
+            const int ts = qd >> 2;
+            const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+            const float y = ts == 0 ? pv[0] : ts == 1 ? pv[1] : ts == 2 ? pv[2] : pv[3];
+            if (store) out[(size_t)pq * n_out + row] = y;
+        }
+    }
+}
+
 // The matrix-core path takes whole 4-chunk blocks (512 entries; a row's
 // scale bytes in 16-byte loads), whole 32-row blocks and whole 4-chunk groups
 // of h's pieces: in and out sizes multiples of 512, at most 4096 (B -- a
@@ -733,24 +918,30 @@ static int launch_f4_n(int n_in, float *out, const uint8_t *pieces, uint8_t *hp,
 }
 
 // More tokens: the bucket's pass table drives the grid (an upper bound on the
-// passes: every slot's last pass may be short). Two pairs a pass when experts
-// see few pairs each (the 4-wavefront kernel), four when they see several on
-// average (the 8-wavefront kernel).
-int f4_pairs_per_pass(int n_pairs, int n_experts) { return n_pairs >= 3 * n_experts ? 4 : 2; }
+// passes: every slot's last pass may be short). Pairs a pass by the average
+// pairs per expert: two below 3 (the 4-wavefront kernel), four below 6 (the
+// 8-wavefront kernel with the pairs resident in LDS), else eight (the
+// 8-wavefront kernel with the pairs streamed through LDS).
+int f4_pairs_per_pass(int n_pairs, int n_experts) {
+    return n_pairs >= 6 * n_experts ? 8 : n_pairs >= 3 * n_experts ? 4 : 2;
+}
 
 template <bool UP, int NCK>
 static int launch_f4m(int npp, float *out, const uint8_t *pieces, uint8_t *hp, const BankDev &bank,
                       const int32_t *active, const int32_t *offsets, const int32_t *perm, const int32_t *passes,
                       int top_k, int latent, int inter, int n_pairs, int max_slots, hipStream_t st) {
     const int n_out = UP ? inter : latent;
-    const int rows_wg = npp == 4 ? 8 * (UP ? 32 : 64) : f4::kWaves * f4::kRows;
+    const int rows_wg = npp >= 4 ? 8 * (UP ? 32 : 64) : f4::kWaves * f4::kRows;
     const int row_blocks = (n_out + rows_wg - 1) / rows_wg;
     const int64_t max_passes = (int64_t)(n_pairs + npp - 1) / npp + max_slots;
     const int64_t grid = max_passes * row_blocks;
     if (grid == 0) return K3G_OK;
     if (grid > 0x7fffffff) return K3G_EUNSUPPORTED;
     const size_t lds = (size_t)npp * NCK * f4::kChunkBytes;  // above the 64 KB default from 26 chunks on
-    if (npp == 4) {
+    if (npp == 8) {
+        moe_f4s_kernel<UP, NCK><<<(unsigned)grid, 8 * kWave, 0, st>>>(out, pieces, hp, bank, active, offsets, perm,
+                                                                     passes, top_k, latent, inter);
+    } else if (npp == 4) {
         if (lds > 65536 && hipFuncSetAttribute((const void *)moe_f4q_kernel<UP, NCK>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return K3G_EHIP;

@@ -113,8 +113,8 @@ def test_fp4_layer_workspace(k3g, T):
     if T == 1:
         assert L["passes"] == 0
     else:
-        npp = 4 if P >= 3 * E else 2
-        assert npp == (4 if T == 4096 else 2)
+        npp = 8 if P >= 6 * E else 4 if P >= 3 * E else 2
+        assert npp == (8 if T == 4096 else 2)
         assert room["passes"] >= 4 * (1 + 2 * (-(-P // npp) + min(P, E)))
     # the vector form has none of these regions
     L0 = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=lat,
