@@ -121,8 +121,8 @@ def main():
                                              ("prefill_4096_idot", 10, 2, True, 0.0, False),
                                              ("prefill_4096_exact", 5, 1, False, 0.0, True)):
             r, _ = run_workload(ctx, wl, steps, warm, bf16, mfma_decode=f4, top_p=p)
-            others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "stage_us",
-                                             "decode", "roofline", "steps", "warmup")})
+            others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "step_us",
+                                             "stage_us", "decode", "roofline", "steps", "warmup")})
         result["other_workloads"] = others
         # one expert on one token, and the batch-1 product on one w1
         result["expert_b1"] = run_expert(ctx, bankt)
@@ -225,10 +225,23 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     t_total = time.perf_counter() - t_start
     ms_per_step = 1e3 * t_total / steps
 
+    # the distribution of single steps (after the timed region): HIP events
+    # around each of up to 100 steps
+    stream = torch.cuda.current_stream()
+    n_single = min(100, max(steps, 10))
+    single = []
+    for i in range(n_single):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(i)
+        e1.record(stream)
+        single.append((e0, e1))
+    torch.cuda.synchronize()
+    single_us = np.array([a.elapsed_time(b) * 1e3 for a, b in single])
+
     # per-kernel times: each stage replayed over every input batch inside one
     # graph, bracketed by HIP events on the stream it runs on; the average
     # launch time is the elapsed time over the number of launches
-    stream = torch.cuda.current_stream()
     reps = 3
 
     def time_stage(st, m):
@@ -346,6 +359,9 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
             "seed_bank": ctx["seed_bank"], "seed_workload": wl_seed,
         },
         "tokens_per_s": round(tok_s, 1),
+        "step_us": {"n": int(n_single), "median": round(float(np.median(single_us)), 2),
+                    "best": round(float(single_us.min()), 2), "worst": round(float(single_us.max()), 2),
+                    "timing": "HIP events around each step, back to back"},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "decode": ("gfx950 FP4 MFMA on the stored nibbles, x and h as 16 e2m1 pieces" if f4 else
                    "gfx950 FP4->FP32 convert" if mode == k3g.EXACT else
