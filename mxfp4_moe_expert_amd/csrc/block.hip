@@ -164,7 +164,7 @@ constexpr int kStepBytes = 3 * 1024;           // one token tile, one step, thre
 constexpr int kBlockB = 4 * 2 * kStepBytes;    // 24 KB: one block of operand B
 constexpr int kNBUF = 3;        // operand-A ring depth (blocks)
 constexpr int kMaxSeg = 3;
-constexpr int kTargetWG = 512;  // two workgroups per CU
+constexpr int kTargetWG = 512;  // resident workgroups: two per CU
 }  // namespace dm
 
 struct DenseMSeg {
@@ -423,12 +423,14 @@ bool dense_mfma_ok(int T, int N, const int *K, int n_seg) {
     return true;
 }
 
-// Slices of K: enough workgroups to fill the chip, at least 4 blocks a slice.
+// Slices of K: as many as keep the grid within one round of resident
+// workgroups (two per CU; a second, mostly empty round would double the time),
+// at least 4 blocks a slice.
 int dense_slices(int T, int N, int K_total, bool glu) {
     const int rows_wg = dm::kWaves * (glu ? 32 : 64);
     const int64_t tiles = (int64_t)((N + rows_wg - 1) / rows_wg) * (dense_t64(T) / dm::kTok);
     const int nkb = K_total / dm::kKB;
-    int64_t s = (dm::kTargetWG + tiles - 1) / tiles;
+    int64_t s = dm::kTargetWG / tiles;
     s = s < nkb / 4 ? s : nkb / 4;
     return s < 1 ? 1 : (int)s;
 }

@@ -129,6 +129,21 @@ def test_block_small(k3g, H, L_, I, SI, T, mfma):
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
+@pytest.mark.parametrize("T,K,npp", [(32, 2, 2), (64, 4, 8)], ids=["two_a_pass", "eight_a_pass"])
+def test_block_f4mma_layer(k3g, T, K, npp):
+    # the block with its routed layer on the FP4 matrix cores (widths multiples
+    # of 512), at sizes where the layer takes 2 and 8 pairs a pass
+    H, L_, I, SI, E = 1024, 512, 512, 256, 24
+    assert (8 if T * K >= 6 * E else 4 if T * K >= 3 * E else 2) == npp
+    src, bankt, bank = make_bank(k3g, 83, E, L_, I, 118, 132, 0.01)
+    Wr, b = synth.router(83, E, H, 0.1)
+    dense = synth.block_dense(83, hidden=H, latent=L_, shared_inter=SI, n_shared=2)
+    x = synth.activations(83, T, H)
+    out = check_block(k3g, src, bank, x, Wr, b, dense, K, tokens=range(0, T, 7), mode=0x400)
+    r = oracle.latent_block(x, Wr, b, dense, {e: src(e) for e in range(E)}, E, K, oracle.EXACT)
+    assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
+
+
 @pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
 def test_block_full_size_sampled(k3g, full_bank, decode):
     src, bankt, bank = full_bank
