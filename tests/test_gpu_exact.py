@@ -434,6 +434,40 @@ def test_layer_tokens_f4mma(k3g, case):
     assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
+@pytest.mark.parametrize("T,K,E,npp", [(1, 4, 8, 0), (8, 2, 16, 2), (14, 2, 8, 4), (16, 3, 8, 8)],
+                         ids=["one_token", "two_a_pass", "four_a_pass", "eight_a_pass"])
+def test_layer_f4mma_max_width(k3g, T, K, E, npp):
+    # the widest shapes the matrix-core form takes (latent = inter = 4096: 32
+    # chunks; four pairs a pass then hold exactly 160 KB of LDS)
+    latent = inter = 4096
+    if T > 1:
+        assert pairs_per_pass(T * K, E) == npp
+    src, bankt, bank = make_bank(k3g, 64, E, latent, inter, 118, 132, 0.01)
+    x = synth.activations(64, T, latent)
+    W, b = synth.router(64, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K)
+    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | k3g.DECODE_MFMA)
+    assert L["xp"] and L["hp"] and bool(L["passes"]) == (T > 1)
+    if T > 1:
+        check_pass_table(ws, L, E, npp)
+    y = check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=k3g.DECODE_MFMA)
+    yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.EXACT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
+
+
+def test_layer_f4mma_all_dropped(k3g):
+    # every entry dropped (idx -1): no pairs, no passes, y = 0
+    E, latent, inter, T, K = 8, 512, 512, 5, 4
+    src, bankt, bank = make_bank(k3g, 65, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(65, T, latent)
+    idx = np.full((T, K), -1, np.int32)
+    wts = np.zeros((T, K), np.float32)
+    y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | k3g.DECODE_MFMA)
+    assert ws_view(ws, L, "passes", 1, np.int32)[0] == 0
+    assert ws_view(ws, L, "active", 1, np.int32)[0] == 0
+    assert np.array_equal(y, np.zeros_like(y))
+
+
 # ---- K3_TOPP ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,n_in,E,K", [(1, 3584, 896, 16), (8, 512, 896, 20), (3, 256, 2000, 16), (300, 512, 896, 16)],
