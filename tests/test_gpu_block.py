@@ -112,8 +112,9 @@ def check_block(k3g, src, bank, x, Wr, b, dense, K, tokens, mode=0):
 
 @pytest.mark.parametrize("H,L_,I,SI,T,mfma", [(256, 128, 96, 64, 37, True),     # one workgroup per product
                                                (512, 256, 128, 192, 100, True),  # K slices across segments
+                                               (512, 256, 128, 192, 1, True),    # one token: 63 padded
                                                (224, 96, 96, 96, 37, False)],    # widths off 64: fp32 fma
-                         ids=["mfma_one_slice", "mfma_slices", "fma"])
+                         ids=["mfma_one_slice", "mfma_slices", "mfma_one_token", "fma"])
 def test_block_small(k3g, H, L_, I, SI, T, mfma):
     E, K = 8, 2
     src, bankt, bank = make_bank(k3g, 81, E, L_, I, 120, 123, 0.01)
