@@ -77,7 +77,7 @@ def expert_bytes(latent, inter):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the path on a single MI355X and has no "
+        print("bench.py measures one GPU: the library runs the path on a single MI355X and has no "
               "multi-GPU mode; run it with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
 
