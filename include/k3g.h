@@ -235,7 +235,8 @@ int k3g_mxfp4_gemv_f32s(float *y, const float *x, const uint8_t *packed, const f
  * 25 tanh(u/25) (SiTU-GLU, [COLIBRI-K3] "Architecture notes"), y = w2 h.
  * y, x fp32 [latent], 16-byte aligned. In IDOT mode x and h are quantised per
  * 32-group to int8 first. ws: k3g_workspace_bytes(K3G_OP_EXPERT_GLU, ...) bytes,
- * 256-byte aligned. */
+ * 256-byte aligned. K3G_DECODE_LUT and K3G_IDOT_BF16 apply; K3G_DECODE_MFMA
+ * (a layer form) returns K3G_EUNSUPPORTED. */
 int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode,
                    void *ws, size_t ws_bytes, void *stream);
 

@@ -379,6 +379,9 @@ int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *pack
 int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void *ws, size_t ws_bytes,
                    void *stream) {
     if (!y || !x || !e || !ws) return K3G_EINVAL;
+    // the matrix-core form is a layer form (its work is cut by pairs and
+    // experts); one expert runs on the vector kernels, so the flag is refused
+    if (mode & K3G_DECODE_MFMA) return K3G_EUNSUPPORTED;
     const int latent = e->w1.in, inter = e->w1.rows;
     if (e->w3.in != latent || e->w3.rows != inter || e->w2.in != inter || e->w2.rows != latent) return K3G_EINVAL;
     K3G_TRY(mxfp4_ok(e->w1.packed, e->w1.scales, latent, inter));

@@ -86,6 +86,10 @@ def test_rejects_bad_arguments_before_any_launch(k3g):
     # a scale tensor off its 4-byte alignment
     assert L.k3g_moe_layer(P(1 << 20), P(2 << 20), P(3 << 20), P(4 << 20), C.byref(bank128), 2, 2, 1, P(1 << 24),
                            1 << 24, None) == -2
+    # one expert: the FP4 matrix-core form is a layer form, refused
+    mx = k3g.Mxfp4(1 << 20, 1 << 21, 64, 64)
+    ex = k3g.Expert(mx, mx, mx)
+    assert L.k3g_expert_glu(fake, P(4096), C.byref(ex), 0x400, fake, 1 << 24, None) == -5
     assert L.k3g_status_string(-3) == b"workspace too small"
 
 
