@@ -130,6 +130,20 @@ def test_block_small(k3g, H, L_, I, SI, T, mfma):
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
+def test_block_dense_wide_range(k3g):
+    # hidden-state entries over 30 decades: each entry's three bf16 pieces
+    # follow its own exponent, so the dense products keep the same bound
+    H, L_, I, SI, E, K, T = 512, 256, 128, 192, 8, 2, 24
+    src, bankt, bank = make_bank(k3g, 84, E, L_, I, 120, 123, 0.01)
+    Wr, b = synth.router(84, E, H, 0.1)
+    dense = synth.block_dense(84, hidden=H, latent=L_, shared_inter=SI, n_shared=2)
+    x = synth.activations(84, T, H)
+    x = (x * 10.0 ** np.random.default_rng(84).uniform(-15, 15, x.shape)).astype(np.float32)
+    sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L_, inter=I, hidden=H, sh_inter=SI, mode=0)
+    assert k3g.workspace_layout(k3g.OP_LATENT_BLOCK, sh)["dxh"]  # the matrix-core form
+    check_block(k3g, src, bank, x, Wr, b, dense, K, tokens=range(T))
+
+
 @pytest.mark.parametrize("T,K,npp", [(32, 2, 2), (64, 4, 8)], ids=["two_a_pass", "eight_a_pass"])
 def test_block_f4mma_layer(k3g, T, K, npp):
     # the block with its routed layer on the FP4 matrix cores (widths multiples
