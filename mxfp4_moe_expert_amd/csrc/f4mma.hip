@@ -1,5 +1,6 @@
-// f4mma.hip -- the one-token expert products on gfx950's block-scaled FP4
-// matrix cores.
+// f4mma.hip -- the expert products on gfx950's block-scaled FP4 matrix cores:
+// one token (moe_f4_kernel), and more tokens in passes of 2, 4 or 8 of an
+// expert's sorted pairs (moe_f4m_kernel, moe_f4q_kernel, moe_f4s_kernel).
 //
 // The product is the pages' exact one ("kimi-k3-in-c: 2.78 trillion
 // parameters, one CPU, 8 GB of RAM", section "Reduction one"): per row, every
@@ -33,6 +34,13 @@
 // Operand A uses the same k order: lane l = r + 16*q of a 16-row tile loads
 // the 16 bytes of group 4*i + q of row r, so one instruction reads 64
 // contiguous bytes of each of 16 rows.
+//
+// With more tokens every pair is its own 16 columns (its token's x pieces for
+// the up-projection, its own h pieces for the down-projection), so an A
+// fragment feeds one product per pair of a pass. The passes come from the
+// bucket's table (the pages sort a chunk's pairs by expert so that each
+// selected expert is read once: "Kimi K3 engine (c/kimi_k3.c)", section
+// "Chunked prefill"); here an expert is read once per pass.
 #include "k3g_common.h"
 
 // Build-time knob (the default is the shipped configuration): blocks of four
