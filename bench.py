@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_PEAK_I8_TOPS = 5000.0      # MI355X dense int8 matrix, published (tera-ops)
 MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 MFMA_PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4 matrix, published
+MFMA_PEAK_F64_TFLOPS = 78.6     # MI355X fp64 matrix, published
 N_ROT = 64                 # distinct tokens the decode steps cycle through
 
 
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of HIP graphs")
     ap.add_argument("--stream-steps", type=int, default=40,
                     help="decode steps per cache size in the streaming-tier measurement")
+    ap.add_argument("--achievable-only", action="store_true",
+                    help="only measure the matrix-core rates and a streaming read (the achievable peaks) and exit")
     ap.add_argument("--expert-only", action="store_true",
                     help="only time one expert on one token and the batch-1 product (for profiling) and exit")
     ap.add_argument("--block-only", action="store_true",
@@ -102,6 +105,9 @@ def main():
     print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
 
     ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager)
+    if args.achievable_only:
+        print(json.dumps({"achievable": run_achievable(ctx)}), flush=True)
+        return
     if args.expert_only:
         print(json.dumps({"expert_b1": run_expert(ctx, bankt)}), flush=True)
         return
@@ -126,6 +132,11 @@ def main():
         result["other_workloads"] = others
         # one expert on one token, and the batch-1 product on one w1
         result["expert_b1"] = run_expert(ctx, bankt)
+        # the achievable denominators: matrix-core rates and a streaming read
+        result["achievable"] = run_achievable(ctx)
+        ach = result["achievable"]["hbm_read"]["GBps"]
+        result["roofline"]["achievable_peak"] = ach
+        result["roofline"]["frac_of_achievable"] = round(result["roofline"]["achieved"] / ach, 4)
         # the full LatentMoE block at 256 tokens, the routed layer in both forms
         result["block_256"] = run_block(ctx, bank)
         result["block_256_fp4_mfma"] = run_block(ctx, bank, mfma_decode=True)
@@ -515,6 +526,47 @@ def run_expert(ctx, bankt, n_rot=64, reps=5):
                      "graph_hbm_frac": round(nbytes / tg / 1e3 / HBM_PEAK_GBS, 4),
                      "launch_us": round(tl, 2), "launch_GBps": round(nbytes / tl / 1e3, 1)}
     del experts, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_achievable(ctx, reps=3):
+    """What this chip sustains, beside the datasheet peaks: back-to-back matrix
+    products of each kind the path uses (no memory traffic), and one streaming
+    read of a 4 GiB buffer; HIP events around `reps` launches after a warm-up."""
+    torch, k3g = ctx["torch"], ctx["k3g"]
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, dtype=torch.int32, device=ctx["dev"])
+    products = 2048 * 4 * 4  # workgroups x wavefronts x independent products per round
+    kinds = {  # kind: (name, ops per instruction, rounds per launch, published dense peak in T(FL)OP/s)
+        0: ("int8", 2 * 32 * 32 * 32, 5000, MFMA_PEAK_I8_TOPS),
+        1: ("bf16", 2 * 16 * 16 * 32, 10000, MFMA_PEAK_BF16_TFLOPS),
+        2: ("fp4", 2 * 16 * 16 * 128, 10000, MFMA_PEAK_FP4_TFLOPS),
+        3: ("fp64", 2 * 16 * 16 * 4, 2500, MFMA_PEAK_F64_TFLOPS),
+    }
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {"timing": f"HIP events around {reps} launches after one warm-up launch", "matrix": {}}
+    for kind, (name, ops, rounds, peak) in kinds.items():
+        t = timed(lambda: k3g.k3g_probe_mfma_rate(kind, rounds, sink))
+        rate = products * rounds * ops / t / 1e12
+        out["matrix"][name] = {"achieved_TOPs": round(rate, 1), "peak": peak, "frac": round(rate / peak, 4)}
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=ctx["dev"])
+    t = timed(lambda: k3g.k3g_probe_read_rate(buf, sink))
+    gbs = buf.numel() / t / 1e9
+    out["hbm_read"] = {"bytes": buf.numel(), "GBps": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del buf
     torch.cuda.empty_cache()
     return out
 

@@ -390,6 +390,24 @@ int k3g_quantize_i8_groups(int8_t *q, float *s, const float *x, int n_rows, int 
 int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed,
                              int in, int rows, int n_tokens, void *stream);
 
+/* ---- measurement hooks (not part of the method) ---------------------------
+ * What the chip sustains, as roofline denominators beside the datasheet peaks.
+ * Each launches one kernel on `stream`; the caller times it. sink: a device
+ * uint32 the kernel may store to (rarely; keeps the work from being removed).
+ *
+ * k3g_probe_mfma_rate: 2048 workgroups of 4 wavefronts, each wavefront
+ * issuing `iters` rounds of 4 independent matrix products of one kind on
+ * register operands, no memory traffic. kind 0: v_mfma_i32_32x32x32_i8
+ * (65,536 ops each), 1: v_mfma_f32_16x16x32_bf16 (16,384 flops),
+ * 2: v_mfma_scale_f32_16x16x128_f8f6f4 on fp4 (65,536 flops),
+ * 3: v_mfma_f64_16x16x4_f64 (2,048 flops). Ops per launch =
+ * 2048 * 4 * iters * 4 * ops-per-instruction. K3G_EINVAL for a kind outside
+ * 0..3, iters < 1 or a null sink.
+ * k3g_probe_read_rate: reads `bytes` (a multiple of 16, buf 16-byte aligned)
+ * once with 16-byte loads. K3G_EINVAL otherwise. */
+int k3g_probe_mfma_rate(int kind, int iters, uint32_t *sink, void *stream);
+int k3g_probe_read_rate(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -114,6 +114,8 @@ def lib():
         L.k3g_latent_moe_block.argtypes = [P, P, P, i, i, i, P, sz, P]
         L.k3g_quantize_i8_groups.argtypes = [P, P, P, i, i, P]
         L.k3g_mxfp4_idot_groupsums.argtypes = [P, P, P, i, i, i, P]
+        L.k3g_probe_mfma_rate.argtypes = [i, i, P, P]
+        L.k3g_probe_read_rate.argtypes = [P, sz, P, P]
         _lib = L
     return _lib
 
@@ -392,6 +394,22 @@ def k3g_mxfp4_idot_groupsums(sums: torch.Tensor, q: torch.Tensor, packed: torch.
 
 
 # ---- bank packing (data placement only) -------------------------------------
+
+def k3g_probe_mfma_rate(kind: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """Measurement hook: back-to-back matrix products of one kind (0 int8,
+    1 bf16, 2 fp4, 3 fp64) with no memory traffic; the caller times it."""
+    _dev(sink, torch.int32, "sink")
+    _check("k3g_probe_mfma_rate", lib().k3g_probe_mfma_rate(kind, iters, _ptr(sink), _stream(stream)))
+
+
+def k3g_probe_read_rate(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement hook: one streaming read of the whole of `buf`."""
+    _dev(sink, torch.int32, "sink")
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check("k3g_probe_read_rate", lib().k3g_probe_read_rate(_ptr(buf), buf.numel() * buf.element_size(),
+                                                            _ptr(sink), _stream(stream)))
+
 
 def pack_bank(experts, n_experts: int, latent: int, inter: int, device="cuda", threads: int = 16):
     """Place experts' six byte arrays at the library's recommended offsets.

@@ -90,6 +90,12 @@ def test_rejects_bad_arguments_before_any_launch(k3g):
     mx = k3g.Mxfp4(1 << 20, 1 << 21, 64, 64)
     ex = k3g.Expert(mx, mx, mx)
     assert L.k3g_expert_glu(fake, P(4096), C.byref(ex), 0x400, fake, 1 << 24, None) == -5
+    # measurement hooks: kind, iteration count, sink; size and alignment of the read
+    assert L.k3g_probe_mfma_rate(4, 10, fake, None) == -1
+    assert L.k3g_probe_mfma_rate(0, 0, fake, None) == -1
+    assert L.k3g_probe_mfma_rate(1, 10, None, None) == -1
+    assert L.k3g_probe_read_rate(fake, 24, fake, None) == -1
+    assert L.k3g_probe_read_rate(P(4104), 64, fake, None) == -1
     assert L.k3g_status_string(-3) == b"workspace too small"
 
 

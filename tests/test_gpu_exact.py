@@ -468,6 +468,16 @@ def test_layer_f4mma_all_dropped(k3g):
     assert np.array_equal(y, np.zeros_like(y))
 
 
+def test_probe_hooks_run(k3g):
+    # the measurement hooks launch and finish (their rates are bench.py's business)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for kind in range(4):
+        k3g.k3g_probe_mfma_rate(kind, 4, sink)
+    buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    k3g.k3g_probe_read_rate(buf, sink)
+    torch.cuda.synchronize()
+
+
 # ---- K3_TOPP ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,n_in,E,K", [(1, 3584, 896, 16), (8, 512, 896, 20), (3, 256, 2000, 16), (300, 512, 896, 16)],
