@@ -12,11 +12,24 @@ Output: one JSON line (rank 0) with the whole-job throughput, the roofline of
 the dominant kernel (its HIP-event time on the stream it runs on) and the CPU
 oracle timed on a bounded sample on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_b1|decode_b64|prefill_4096_idot]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode_b1|decode_b64|prefill_4096_idot|prefill_4096_exact]
+                    [--mfma-decode] [--idot-bf16]
 
-The default run (decode_b1) also measures, on the same resident bank, short
-runs of the 64-token EXACT layer and the 4096-token IDOT layer (int8 and bf16
-matrix-core forms) and reports them under "other_workloads".
+The default run (decode_b1) also measures, on the same resident bank:
+  other_workloads     short runs of the 64-token EXACT layer (vector and FP4
+                      matrix-core forms), the 4096-token IDOT layer (int8 and
+                      bf16 matrix-core forms) and the 4096-token EXACT layer on
+                      the FP4 matrix cores;
+  expert_b1           one expert on one token and the one-matrix product;
+  achievable          the sustained matrix-core rates and streaming-read rate
+                      (the roofline's achievable denominators);
+  block_256[_fp4_mfma] the full LatentMoE block at 256 tokens, with either
+                      layer form;
+  scale_format        the same product with f32 per-group scales;
+  streaming_tier      decode steps with the bank in host memory and an LRU of
+                      expert slots in HBM.
+Every line carries per-step medians (step_us) and per-stage HIP-event times.
 """
 from __future__ import annotations
 
