@@ -25,6 +25,10 @@
  *  - No dimension has a default: a zero or negative size where a positive
  *    one is needed is K3G_EINVAL ([KIC-README] "2. The config reader that
  *    refuses to guess": an absent field is an error, never a default).
+ *  - An empty batch (n_tokens = 0) is not an error: the routing, layer,
+ *    layer-stage and block calls check their other scalar arguments, then
+ *    return K3G_OK with nothing enqueued; their data pointers and workspace
+ *    may then be null (a torch tensor with no elements has none).
  *
  * MXFP4 matrix layout ([COLIBRI-K3] "Weights"; [KIC-ARTICLE] "Reduction one")
  * --------------------------------------------------------------------------

@@ -434,11 +434,12 @@ int k3g_moe_route(int32_t *idx, float *wts, const float *x, const float *w_route
 int k3g_moe_route_topp(int32_t *idx, float *wts, const float *x, const float *w_router, const float *bias,
                        int n_tokens, int in, int n_experts, int top_k, float top_p, void *ws, size_t ws_bytes,
                        void *stream) {
-    if (!idx || !wts || !x || !w_router || !bias || !ws) return K3G_EINVAL;
     if (!(top_p >= 0.0f && top_p <= 1.0f)) return K3G_EINVAL;  // NaN too
     if (n_tokens < 0 || in <= 0 || n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > kMaxTopK ||
         top_k > n_experts)
         return K3G_EINVAL;
+    if (n_tokens == 0) return K3G_OK;  // nothing to route; the pointers may be null
+    if (!idx || !wts || !x || !w_router || !bias || !ws) return K3G_EINVAL;
     if (!aligned(x, 4) || !aligned(w_router, 4) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
         return K3G_EALIGN;
     k3g_shape s = {n_tokens, top_k, n_experts, 0, 0, 0, 0, 0};
@@ -454,10 +455,12 @@ int k3g_moe_route_topp(int32_t *idx, float *wts, const float *x, const float *w_
 
 static int layer_prepare(k3g_ws_layout *L, const float *y, const float *x, const int32_t *idx, const float *wts,
                          const k3g_expert_bank *bank, int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes) {
-    if (!y || !x || !idx || !wts || !bank || !bank->base || !ws) return K3G_EINVAL;
+    if (!bank || n_tokens < 0) return K3G_EINVAL;
     const int latent = bank->latent, inter = bank->inter, E = bank->n_experts;
     k3g_shape s = {n_tokens, top_k, E, latent, inter, 0, 0, mode};
     K3G_TRY(layout(L, K3G_OP_MOE_LAYER, s));
+    if (n_tokens == 0) return K3G_OK;  // the stages launch nothing; the pointers may be null
+    if (!y || !x || !idx || !wts || !bank->base || !ws) return K3G_EINVAL;
     if (ws_bytes < L->total) return K3G_ENOSPACE;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || !aligned(idx, 4) || !aligned(wts, 4))
         return K3G_EALIGN;
@@ -558,9 +561,11 @@ int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts
 
 extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w, int n_tokens, int top_k,
                                     int mode, void *ws, size_t ws_bytes, void *stream) {
-    if (!out || !x || !w || !ws || !w->w_router || !w->bias || !w->w_down || !w->w_up || !w->gamma || !w->bank.base)
-        return K3G_EINVAL;
+    if (!w || n_tokens < 0) return K3G_EINVAL;
     if (w->n_shared < 0 || w->n_shared > 2 || !(w->rms_eps >= 0.0f)) return K3G_EINVAL;
+    if (n_tokens == 0) return K3G_OK;  // nothing to do; out, x and ws may be null
+    if (!out || !x || !ws || !w->w_router || !w->bias || !w->w_down || !w->w_up || !w->gamma || !w->bank.base)
+        return K3G_EINVAL;
     for (int i = 0; i < w->n_shared; ++i)
         if (!w->sh_w1[i] || !w->sh_w3[i] || !w->sh_w2[i]) return K3G_EINVAL;
     const k3g_expert_bank *bank = &w->bank;

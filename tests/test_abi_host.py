@@ -154,3 +154,23 @@ def test_block_dense_workspace(k3g, H, lat, SI, mfma):
     assert room["dxl"] >= t64 * lat * 6 and room["dxs"] >= 2 * t64 * SI * 6
     # the partials hold the largest product's slices: at least one slice of each
     assert room["dpart"] >= 4 * max(T * lat, 2 * T * SI, T * H)
+
+
+def test_empty_batch_is_a_no_op(k3g):
+    # n_tokens = 0: the scalar arguments are still checked, then K3G_OK with
+    # nothing enqueued and no device touched, null pointers allowed
+    L = k3g.lib()
+    assert L.k3g_moe_route(None, None, None, None, None, 0, 64, 8, 2, None, 0, None) == 0
+    assert L.k3g_moe_route(None, None, None, None, None, 0, 64, 8, 9, None, 0, None) == -1  # top_k > E
+    assert L.k3g_moe_route_topp(None, None, None, None, None, 0, 64, 8, 2, 0.9, None, 0, None) == 0
+    bank = k3g.ExpertBank(4096, 4096, 8, 64, 64, (C.c_int64 * 6)(0, 2048, 2304, 4352, 4608, 6656))
+    for mode in (0, 0x100):
+        assert L.k3g_moe_layer(None, None, None, None, C.byref(bank), 0, 2, mode, None, 0, None) == 0
+    assert L.k3g_moe_layer(None, None, None, None, C.byref(bank), 0, 2, 7, None, 0, None) == -1  # bad mode
+    for stage in range(6):
+        assert L.k3g_moe_layer_stage(stage, None, None, None, None, C.byref(bank), 0, 2, 0, None, 0, None) == 0
+    w = k3g.BlockWeights()
+    w.n_shared, w.rms_eps = 2, 1e-5
+    assert L.k3g_latent_moe_block(None, None, C.byref(w), 0, 2, 0, None, 0, None) == 0
+    w.n_shared = 3
+    assert L.k3g_latent_moe_block(None, None, C.byref(w), 0, 2, 0, None, 0, None) == -1
