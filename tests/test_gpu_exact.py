@@ -468,6 +468,28 @@ def test_layer_f4mma_all_dropped(k3g):
     assert np.array_equal(y, np.zeros_like(y))
 
 
+def test_route_and_layer_at_the_limits(k3g):
+    # the largest routing the library takes: 2048 experts, top-64 (the
+    # one-wavefront top-k with 32 candidates a lane, the bucket over 2048
+    # counters), then the layer with 64 pairs a token
+    T, n_in, E, K = 3, 64, 2048, 64
+    W, b = synth.router(66, E, n_in, 0.1)
+    x = synth.activations(66, T, n_in)
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ws_r = k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=T, n_experts=E))
+    k3g.k3g_moe_route(idx, wts, dev(x), dev(W), dev(b), K, ws_r)
+    io, wo, _ = oracle.route(x, W, b, K)
+    assert np.array_equal(host(idx), io)
+    assert np.allclose(host(wts), wo, rtol=1e-6, atol=0)
+    latent, inter = 64, 64
+    src, bankt, bank = make_bank(k3g, 66, E, latent, inter, 120, 123, 0.01)
+    xl = synth.activations(67, T, latent)
+    y = check_layer_exact(k3g, src, bankt, bank, xl, io, wo)
+    yo = oracle.moe_layer(xl, io, wo, {int(e): src(int(e)) for e in np.unique(io)}, E, oracle.EXACT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
+
+
 def test_probe_hooks_run(k3g):
     # the measurement hooks launch and finish (their rates are bench.py's business)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
