@@ -130,6 +130,19 @@ def test_block_small(k3g, H, L_, I, SI, T, mfma):
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
+@pytest.mark.parametrize("mode", [1, 0x201], ids=["idot_int8", "idot_bf16"])
+def test_block_small_idot(k3g, mode):
+    # the block with its routed layer in the IDOT form (widths multiples of 128)
+    H, L_, I, SI, E, K, T = 512, 256, 128, 192, 8, 2, 40
+    src, bankt, bank = make_bank(k3g, 85, E, L_, I, 120, 123, 0.01)
+    Wr, b = synth.router(85, E, H, 0.1)
+    dense = synth.block_dense(85, hidden=H, latent=L_, shared_inter=SI, n_shared=2)
+    x = synth.activations(85, T, H)
+    out = check_block(k3g, src, bank, x, Wr, b, dense, K, tokens=range(0, T, 3), mode=mode)
+    r = oracle.latent_block(x, Wr, b, dense, {e: src(e) for e in range(E)}, E, K, oracle.IDOT)
+    assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
+
+
 def test_block_dense_wide_range(k3g):
     # hidden-state entries over 30 decades: each entry's three bf16 pieces
     # follow its own exponent, so the dense products keep the same bound

@@ -153,6 +153,9 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
         nrm = np.zeros(latent)
         for k in range(K):
             e = int(idx[t, k])
+            if e < 0:  # dropped by a K3_TOPP cut: not a pair, adds nothing
+                assert inv[t * K + k] == -1
+                continue
             ex = src(e)
             pos = int(inv[t * K + k])
             g, _, ng = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w1p"], ex["w1s"], full=True)
@@ -170,9 +173,9 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
             acc += float(wts[t, k]) * yp.astype(np.float64)
             nrm += abs(float(wts[t, k])) * np.abs(yp.astype(np.float64))
         assert_norm_close(yg[t], acc, nrm, what=f"idot combine t={t}")
-    # the bf16 form computes the same numbers bit for bit
+    # the bf16 form computes the same numbers bit for bit (over the pairs that exist)
     yb, wsb, Lb = run_layer_idot(k3g, bank, x, idx, wts, 0x200)
-    P = T * K
+    P = int(np.count_nonzero(idx >= 0))
     for name, width, dt in (("h", inter, np.float32), ("hq", inter, np.int8), ("ypair", latent, np.float32)):
         a = ws_view(ws, L, name, P * width, dt)
         b = ws_view(wsb, Lb, name, P * width, dt)
@@ -195,6 +198,19 @@ def test_layer_idot_small_many_tokens(k3g):
     W, b = synth.router(71, E, latent, 0.1)
     idx, wts, _ = oracle.route(x, W, b, K)
     check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 1, 137, 299])
+
+
+def test_layer_idot_topp(k3g):
+    # a K3_TOPP cut before the IDOT layer: dropped entries are no pairs
+    E, latent, inter, T, K = 12, 128, 256, 40, 4
+    src, bankt, bank = make_bank(k3g, 72, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(72, T, latent)
+    W, b = synth.router(72, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K, top_p=0.6)
+    assert (idx < 0).any()
+    y = check_layer_idot(k3g, src, bank, x, idx, wts, tokens=range(T))
+    yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.IDOT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
 def test_layer_idot_prefill_4096_sampled(k3g, full_bank):
