@@ -408,7 +408,9 @@ int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *pack
  * 2048 * 4 * iters * 4 * ops-per-instruction. K3G_EINVAL for a kind outside
  * 0..3, iters < 1 or a null sink.
  * k3g_probe_read_rate: reads `bytes` (a multiple of 16, buf 16-byte aligned)
- * once with 16-byte loads. K3G_EINVAL otherwise. */
+ * once with 16-byte loads, each wavefront taking 16 KB chunks in turn over
+ * 8,192 workgroups (any tail smaller than a chunk grid-strided). K3G_EINVAL
+ * otherwise. */
 int k3g_probe_mfma_rate(int kind, int iters, uint32_t *sink, void *stream);
 int k3g_probe_read_rate(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 

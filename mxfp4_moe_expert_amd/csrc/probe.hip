@@ -6,8 +6,12 @@
 // int8 32x32x32, bf16 16x16x32, block-scaled FP4 16x16x128, fp64 16x16x4) on
 // register operands; no memory traffic, four accumulators so that no product
 // waits for the one before.
-// k3g_probe_read_rate: a streaming read of a buffer (16-byte loads, four in
-// flight per lane), every byte once.
+// k3g_probe_read_rate: a streaming read of a buffer, every byte once. Each
+// wavefront takes 16 KB chunks in turn (sixteen 1 KB loads in flight, lane l
+// reading bytes 16l..16l+15 of each KB) over 8192 workgroups: of the read
+// orders tried on this chip (grid-stride with 4 or 8 loads in flight,
+// wave-contiguous chunks of 8 or 16 KB, 1024..8192 workgroups) this one reads
+// fastest, so it stands for what a streaming kernel can reach.
 // Both store to `sink` only when a result takes one particular value, so
 // the compiler must keep the work (the store itself is rare and harmless).
 #include "k3g_common.h"
@@ -74,17 +78,27 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_rate_kernel(uint32_t *sink
     }
 }
 
+constexpr int kReadBlocks = 8192;
+constexpr int kReadChunk = 16;  // 1 KB loads per wavefront chunk
+
 __global__ __launch_bounds__(kProbeThreads) void read_rate_kernel(const uint4 *__restrict__ buf, int64_t n16,
                                                                   uint32_t *sink) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    constexpr int64_t chunk16 = 64 * kReadChunk;  // 16-byte units per chunk
+    const int lane = (int)(threadIdx.x & 63);
+    const int64_t n_waves = (int64_t)gridDim.x * (kProbeThreads / 64);
+    const int64_t n_chunks = n16 / chunk16;
     uint32_t x = 0;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 v0 = buf[i], v1 = buf[i + stride], v2 = buf[i + 2 * stride], v3 = buf[i + 3 * stride];
-        x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-        x ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+    for (int64_t c = (int64_t)blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6); c < n_chunks; c += n_waves) {
+        const uint4 *p = buf + c * chunk16 + lane;
+        uint4 v[kReadChunk];
+#pragma unroll
+        for (int j = 0; j < kReadChunk; ++j) v[j] = p[j * 64];
+#pragma unroll
+        for (int j = 0; j < kReadChunk; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
     }
-    for (; i < n16; i += stride) {
+    // the tail that fills no whole chunk, grid-strided
+    for (int64_t i = n_chunks * chunk16 + (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * kProbeThreads) {
         const uint4 v = buf[i];
         x ^= v.x ^ v.y ^ v.z ^ v.w;
     }
@@ -111,7 +125,7 @@ int k3g_probe_mfma_rate(int kind, int iters, uint32_t *sink, void *stream) {
 
 int k3g_probe_read_rate(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
     if (!buf || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)buf & 15)) return K3G_EINVAL;
-    read_rate_kernel<<<kProbeBlocks, kProbeThreads, 0, (hipStream_t)stream>>>((const uint4 *)buf,
+    read_rate_kernel<<<kReadBlocks, kProbeThreads, 0, (hipStream_t)stream>>>((const uint4 *)buf,
                                                                               (int64_t)(bytes / 16), sink);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
