@@ -500,6 +500,25 @@ def test_probe_hooks_run(k3g):
     torch.cuda.synchronize()
 
 
+MAGIC = 0x9E3779B9 - (1 << 32)  # the read probe's sink value, as an int32
+
+
+@pytest.mark.parametrize("n16,unit", [(1024 * 256 + 3, 0), (1024 * 256 + 3, 1024 * 131 + 77),
+                                      (1024 * 256 + 3, 1024 * 256 - 1), (1024 * 256 + 3, 1024 * 256 + 2),
+                                      (5, 4)],
+                         ids=["first", "middle", "last_chunk", "tail", "under_one_chunk"])
+def test_probe_read_covers_every_unit_once(k3g, n16, unit):
+    # one 16-byte unit holds the sink value, every other byte is zero: the
+    # thread that reads it stores the value only if it read it exactly once
+    # (a second read cancels it in the XOR) and read nothing else non-zero
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device="cuda")
+    buf[unit * 4] = MAGIC
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    k3g.k3g_probe_read_rate(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == MAGIC
+
+
 # ---- K3_TOPP ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,n_in,E,K", [(1, 3584, 896, 16), (8, 512, 896, 20), (3, 256, 2000, 16), (300, 512, 896, 16)],
