@@ -123,11 +123,43 @@ int64_t k3o_mxfp4_bytes(int64_t rows, int64_t in)
 /* EXACT product on the packed layout.                                        */
 /* ------------------------------------------------------------------------ */
 
-/* y[r] = sum over groups g whose scale byte s != 255 of
- *        2^(s-127) * sum_{j in g} e2m1(n_rj) * x_j,
- * the group sum taken in double in column order, the scale applied once per
- * group, groups added in order, result rounded to float
- * ([KIC-ARTICLE] "Reduction one", the k3_matmul_mxfp4 kernel).
+/* The EXACT product of one packed row with x, in two passes:
+ *   1. gsum[g] = the dot product of group g's 32 decoded weights (e2m1 values,
+ *      exact in double) with x's 32 entries, products and additions in double,
+ *      columns in increasing order (the pages give one double accumulator per
+ *      group: [KIC-ARTICLE] "Reduction one");
+ *   2. y = sum over the groups in increasing order of 2^(s_g-127) * gsum[g],
+ *      leaving out every group whose scale byte is 255 (the format's NaN code,
+ *      which the pages' kernel treats as a group of zeros, same section).
+ * The normaliser sum_j |w_j||x_j| of the tolerance is formed the same way. */
+static double mxfp4_row_exact(const uint8_t *row, const uint8_t *srow, const float *x,
+                              int ngrp, double *gsum, double *gabs, double *nrm)
+{
+    for (int g = 0; g < ngrp; ++g) {
+        double d = 0.0, a = 0.0;
+        for (int c = 0; c < K3O_GROUP; ++c) {
+            const int j = g * K3O_GROUP + c;
+            const double w = e2m1_val[nibble(row, j)];
+            const double xv = (double)x[j];
+            d += w * xv;
+            a += fabs(w) * fabs(xv);
+        }
+        gsum[g] = d;
+        gabs[g] = a;
+    }
+    double y = 0.0, n = 0.0;
+    for (int g = 0; g < ngrp; ++g) {
+        const uint8_t code = srow[g];
+        if (code == 255)
+            continue;
+        y += e8m0_val[code] * gsum[g];
+        n += e8m0_val[code] * gabs[g];
+    }
+    *nrm = n;
+    return y;
+}
+
+/* y[r] = the EXACT product of row r (mxfp4_row_exact), rounded to float once.
  * Optional: y64 = the double result before rounding; nrm = sum_j |w_rj||x_j|
  * (the normaliser of the tolerance). Returns 0, or -1 on bad arguments. */
 int k3o_mxfp4_gemv(float *y, double *y64, double *nrm, const float *x,
@@ -138,29 +170,24 @@ int k3o_mxfp4_gemv(float *y, double *y64, double *nrm, const float *x,
     if (group != K3O_GROUP || in <= 0 || in % K3O_GROUP || rows < 0)
         return -1;
     const int ngrp = in / K3O_GROUP;
-#pragma omp parallel for schedule(static)
-    for (int r = 0; r < rows; ++r) {
-        const uint8_t *pr = packed + (size_t)r * (size_t)(in / 2);
-        const uint8_t *sr = scales + (size_t)r * (size_t)ngrp;
-        double acc = 0.0, n = 0.0;
-        for (int g = 0; g < ngrp; ++g) {
-            const uint8_t sb = sr[g];
-            if (sb == 255)
-                continue; /* NaN scale: the group contributes nothing */
-            double sub = 0.0, subn = 0.0;
-            for (int j = g * K3O_GROUP; j < (g + 1) * K3O_GROUP; ++j) {
-                const double v = e2m1_val[nibble(pr, j)];
-                sub += v * (double)x[j];
-                subn += fabs(v) * fabs((double)x[j]);
-            }
-            acc += sub * e8m0_val[sb];
-            n += subn * e8m0_val[sb];
+#pragma omp parallel
+    {
+        double *gsum = malloc(sizeof(double) * (size_t)ngrp);
+        double *gabs = malloc(sizeof(double) * (size_t)ngrp);
+#pragma omp for schedule(static)
+        for (int r = 0; r < rows; ++r) {
+            double n;
+            const double v = mxfp4_row_exact(packed + (size_t)r * (size_t)(in / 2),
+                                             scales + (size_t)r * (size_t)ngrp, x, ngrp,
+                                             gsum, gabs, &n);
+            y[r] = (float)v;
+            if (y64)
+                y64[r] = v;
+            if (nrm)
+                nrm[r] = n;
         }
-        y[r] = (float)acc;
-        if (y64)
-            y64[r] = acc;
-        if (nrm)
-            nrm[r] = n;
+        free(gsum);
+        free(gabs);
     }
     return 0;
 }
@@ -189,25 +216,6 @@ int k3o_mxfp4_dequant(double *W, const uint8_t *packed, const uint8_t *scales,
 /* Dense products in the pages' fixed order.                                  */
 /* ------------------------------------------------------------------------ */
 
-/* One output of a dense product with four double accumulators split by i%4,
- * combined as (a0+a1)+(a2+a3), then the tail; separate multiply and add
- * ([KIC-ARTICLE] "A floating-point contract, not a convention", k3_matmul). */
-static double dot4_f32(const float *w, const float *x, int in)
-{
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int i = 0;
-    for (; i + 3 < in; i += 4) {
-        a0 += (double)w[i] * (double)x[i];
-        a1 += (double)w[i + 1] * (double)x[i + 1];
-        a2 += (double)w[i + 2] * (double)x[i + 2];
-        a3 += (double)w[i + 3] * (double)x[i + 3];
-    }
-    double acc = (a0 + a1) + (a2 + a3);
-    for (; i < in; ++i)
-        acc += (double)w[i] * (double)x[i];
-    return acc;
-}
-
 /* bfloat16 bits -> float: the 16 bits are the high half of a float32, so the
  * widening is exact. */
 static inline double bf16_to_double(uint16_t b)
@@ -218,36 +226,41 @@ static inline double bf16_to_double(uint16_t b)
     return (double)f;
 }
 
-/* Same order for bf16 weights (the pages say k3_matmul_bf16 mirrors k3_matmul). */
-static double dot4_bf16(const uint16_t *w, const float *x, int in, double *nrm)
+/* Dense dot products, the plain definition: every product w_i * x_i is formed
+ * in double (exact for fp32 and bf16 operands: at most 24 + 24 significant
+ * bits), and the products are added into one double in increasing i. The
+ * pages fix an order per output so that results do not depend on threads
+ * ([KIC-ARTICLE] "A floating-point contract, not a convention"); this oracle's
+ * order is plain index order. Optional *absdot = sum_i |w_i||x_i|. */
+static double dot_f32_in_order(const float *w, const float *x, int n)
 {
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0, n = 0.0;
-    int i = 0;
-    for (; i + 3 < in; i += 4) {
-        a0 += bf16_to_double(w[i]) * (double)x[i];
-        a1 += bf16_to_double(w[i + 1]) * (double)x[i + 1];
-        a2 += bf16_to_double(w[i + 2]) * (double)x[i + 2];
-        a3 += bf16_to_double(w[i + 3]) * (double)x[i + 3];
-    }
-    double acc = (a0 + a1) + (a2 + a3);
-    for (; i < in; ++i)
-        acc += bf16_to_double(w[i]) * (double)x[i];
-    if (nrm) {
-        for (i = 0; i < in; ++i)
-            n += fabs(bf16_to_double(w[i])) * fabs((double)x[i]);
-        *nrm = n;
-    }
-    return acc;
+    double s = 0.0;
+    for (int i = 0; i < n; ++i)
+        s += (double)x[i] * (double)w[i];
+    return s;
 }
 
-/* y[o] = sum_i W[o][i] x[i] for fp32 W, in the fixed four-accumulator order. */
+static double dot_bf16_in_order(const uint16_t *w, const float *x, int n, double *absdot)
+{
+    double s = 0.0, a = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const double wi = bf16_to_double(w[i]);
+        s += (double)x[i] * wi;
+        a += fabs((double)x[i]) * fabs(wi);
+    }
+    if (absdot)
+        *absdot = a;
+    return s;
+}
+
+/* y[o] = sum_i W[o][i] x[i] for fp32 W, in index order. */
 int k3o_matmul_f32(double *y, const float *x, const float *W, int in, int out)
 {
     if (in <= 0 || out < 0)
         return -1;
 #pragma omp parallel for schedule(static)
     for (int o = 0; o < out; ++o)
-        y[o] = dot4_f32(W + (size_t)o * in, x, in);
+        y[o] = dot_f32_in_order(W + (size_t)o * in, x, in);
     return 0;
 }
 
@@ -258,7 +271,7 @@ int k3o_matmul_bf16(double *y, double *nrm, const float *x, const uint16_t *W, i
         return -1;
 #pragma omp parallel for schedule(static)
     for (int o = 0; o < out; ++o)
-        y[o] = dot4_bf16(W + (size_t)o * in, x, in, nrm ? &nrm[o] : NULL);
+        y[o] = dot_bf16_in_order(W + (size_t)o * in, x, in, nrm ? &nrm[o] : NULL);
     return 0;
 }
 
@@ -449,9 +462,9 @@ int k3o_expert_glu(float *y, float *g, float *u, float *h, const float *x,
     return 0;
 }
 
-/* Routing, step 1: logits[t][e] = sum_i W[e][i] x[t][i] in double, in the
- * fixed four-accumulator order of k3_matmul. fp32 x fp32 products are exact in
- * double, so only the additions round. */
+/* Routing, step 1: logits[t][e] = sum_i W[e][i] x[t][i] in double, added in
+ * index order. fp32 x fp32 products are exact in double, so only the
+ * additions round. */
 int k3o_route_logits(double *logits, const float *x, const float *W, int n_tokens, int in, int n_experts)
 {
     if (in <= 0 || n_tokens < 0 || n_experts <= 0)
@@ -459,7 +472,7 @@ int k3o_route_logits(double *logits, const float *x, const float *W, int n_token
 #pragma omp parallel for schedule(static) collapse(2)
     for (int t = 0; t < n_tokens; ++t)
         for (int e = 0; e < n_experts; ++e)
-            logits[(size_t)t * n_experts + e] = dot4_f32(W + (size_t)e * in, x + (size_t)t * in, in);
+            logits[(size_t)t * n_experts + e] = dot_f32_in_order(W + (size_t)e * in, x + (size_t)t * in, in);
     return 0;
 }
 

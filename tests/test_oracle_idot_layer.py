@@ -5,6 +5,8 @@ int8 activations, integer dots against the doubled e2m1 values, which are
 exact int8). Layer and block: same page, "Architecture notes" (Stable
 LatentMoE).
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -140,6 +142,136 @@ def test_rmsnorm_unit_rms():
     g = synth.uniform_f32(70, 1, 512, 0.5, 1.5)
     ng = oracle.rmsnorm(a, g, eps=1e-5)
     assert np.allclose(ng / g, oracle.rmsnorm(a, np.ones(512, np.float32), eps=1e-5), rtol=1e-6)
+
+
+def test_rmsnorm_closed_forms_place_eps_inside_the_root():
+    """RMSNorm n_i = gamma_i * a_i / sqrt(mean(a^2) + eps), eps = 1e-5 ("kimi-k3-in-c"
+    README, config struct: rms_eps; "Kimi K3 engine (c/kimi_k3.c)", "Architecture
+    notes": the norm on the aggregate). Closed forms on vectors whose sums of squares
+    are exact in double, including values with mean(a^2) below eps, where eps inside
+    the root and eps added to the root give answers that differ by 30%."""
+    L = 64
+    gamma = synth.uniform_f32(71, 0, L, 0.5, 1.5)
+    for c in (3.0, 3.0 * 2.0 ** -10, 2.0 ** -12, -5.0 * 2.0 ** -9):
+        a = np.full(L, c, np.float32)
+        n = oracle.rmsnorm(a, gamma)
+        want = gamma.astype(np.float64) * c / math.sqrt(c * c + 1e-5)
+        assert np.allclose(n, want.astype(np.float32), rtol=2.0 ** -22, atol=0), c
+        outside = gamma.astype(np.float64) * c / (abs(c) + 1e-5)
+        if c * c < 2e-5:
+            assert np.all(np.abs(n - outside) > 0.05 * np.abs(outside))
+    # one nonzero entry: the mean is over all L entries, not over the nonzero ones
+    c = 0.01
+    a = np.zeros(L, np.float32)
+    a[5] = np.float32(c)
+    n = oracle.rmsnorm(a, gamma)
+    cf = float(np.float32(c))
+    want = float(gamma[5]) * cf / math.sqrt(cf * cf / L + 1e-5)
+    assert abs(float(n[5]) - want) <= 2.0 ** -22 * abs(want)
+    assert np.all(np.delete(n, 5) == 0.0)
+    # a zero vector stays zero (eps keeps the root positive)
+    assert np.all(oracle.rmsnorm(np.zeros(L, np.float32), gamma) == 0.0)
+
+
+# E2M1 codes of the values the block fixture uses (OCP table, tests/golden/e2m1_ocp.txt)
+_E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+_BF16 = {1.0: 0x3F80, -1.0: 0xBF80, 0.5: 0x3F00, 2.0: 0x4000, -0.5: 0xBF00}
+
+
+def _selection_mxfp4(rows, cols, col_of_row, value, scale=127):
+    """An MXFP4 matrix whose row r holds `value` at column col_of_row(r) and 0 elsewhere."""
+    codes = np.zeros((rows, cols), np.uint8)
+    for r in range(rows):
+        codes[r, col_of_row(r)] = _E2M1_CODE[abs(value)] | (8 if value < 0 else 0)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.full((rows, cols // 32), scale, np.uint8)
+    return packed, scales
+
+
+def _selection_bf16(rows, cols, col_of_row, value_of_row):
+    W = np.zeros((rows, cols), np.uint16)
+    for r in range(rows):
+        W[r, col_of_row(r)] = _BF16[value_of_row(r)]
+    return W
+
+
+def _situ(g, u):
+    return 4.0 * math.tanh(g / 4.0) * (1.0 / (1.0 + math.exp(-g))) * 25.0 * math.tanh(u / 25.0)
+
+
+def test_block_assembly_closed_form():
+    """The block's assembly against values worked out by hand, with weights that are
+    0/+-1 selections (every product exact), so that what the router reads, where the
+    norm's gamma and eps enter and how the addends combine are fixed independently of
+    the oracle's own functions ("Kimi K3 engine (c/kimi_k3.c)", "Architecture notes":
+    router on the hidden state, down-projection to the latent, routed experts, norm on
+    the aggregate, up-projection, two shared SiTU-GLU experts added unweighted)."""
+    H, L, I, SI, E, K, T = 64, 32, 32, 32, 4, 2, 3
+    x = synth.activations(81, T, H)
+    x[1] *= np.float32(0.03)     # this token's aggregate has mean square below eps
+    x[2] *= np.float32(3.0)
+    # router: expert e reads hidden entry 40 + e only, which the down-projection drops
+    Wr = np.zeros((E, H), np.float32)
+    for e in range(E):
+        Wr[e, 40 + e] = 1.0
+    bias = np.array([0.0, 0.0, 0.0, 0.0], np.float32)
+    # down-projection keeps the first L hidden entries
+    dense = dict(
+        w_down=_selection_bf16(L, H, lambda r: r, lambda r: 1.0),
+        # up-projection: out_i = +n_i for i < L, -n_{i-L} for i >= L
+        w_up=_selection_bf16(H, L, lambda i: i % L, lambda i: 1.0 if i < L else -1.0),
+        gamma=synth.uniform_f32(81, 1, L, 0.5, 1.5),
+    )
+    # shared expert s: g_r = x[(r + 5s) % 64], u_r = 2 x[(3r + s) % 64], out_i += +-0.5 h_{(i + s) % SI}
+    for s_ in range(2):
+        dense[f"sh_w1_{s_}"] = _selection_bf16(SI, H, lambda r, s_=s_: (r + 5 * s_) % H, lambda r: 1.0)
+        dense[f"sh_w3_{s_}"] = _selection_bf16(SI, H, lambda r, s_=s_: (3 * r + s_) % H, lambda r: 2.0)
+        dense[f"sh_w2_{s_}"] = _selection_bf16(H, SI, lambda i, s_=s_: (i + s_) % SI,
+                                               lambda i: 0.5 if i % 2 == 0 else -0.5)
+    # routed expert e: g_r = v1[e] lat_r, u_r = v3[e] lat_{(r+1)%L} (w1 = gate, w3 = up),
+    # y_i = v2[e] h_{(i+2)%I}; expert 1's w1 scale byte 128 doubles its gate
+    v1, v3, v2 = [1.0, 2.0, 0.5, 3.0], [1.0, 0.5, 2.0, 1.5], [1.0, -2.0, 4.0, 0.5]
+    experts = {}
+    for e in range(E):
+        w1p, w1s = _selection_mxfp4(I, L, lambda r: r, v1[e], 128 if e == 1 else 127)
+        w3p, w3s = _selection_mxfp4(I, L, lambda r: (r + 1) % L, v3[e])
+        w2p, w2s = _selection_mxfp4(L, I, lambda i: (i + 2) % I, v2[e])
+        experts[e] = dict(w1p=w1p, w1s=w1s, w3p=w3p, w3s=w3s, w2p=w2p, w2s=w2s)
+    r = oracle.latent_block(x, Wr, bias, dense, experts, E, K, oracle.EXACT)
+
+    f32 = lambda v: float(np.float32(v))
+    for t in range(T):
+        xt = [float(v) for v in x[t]]
+        # routing on the hidden state: logits are x[40..43]; top-2, ties to the lower id
+        logit = xt[40:44]
+        sel = sorted(range(E), key=lambda e: (-logit[e], e))[:K]
+        assert list(r["idx"][t]) == sel
+        sig = [1.0 / (1.0 + math.exp(-logit[e])) for e in sel]
+        w = [f32(sg / (sig[0] + sig[1])) for sg in sig]
+        assert np.allclose(r["wts"][t], w, rtol=1e-7, atol=0)
+        lat = xt[:L]
+        assert list(r["lat"][t]) == [f32(v) for v in lat]
+        agg = [0.0] * L
+        for k, e in enumerate(sel):
+            gate = 2.0 if e == 1 else 1.0
+            h = [f32(_situ(f32(gate * v1[e] * lat[q]), f32(v3[e] * lat[(q + 1) % L]))) for q in range(I)]
+            y = [f32(v2[e] * h[(i + 2) % I]) for i in range(L)]
+            for i in range(L):
+                agg[i] += float(r["wts"][t, k]) * y[i]
+        agg = [f32(v) for v in agg]
+        assert np.allclose(r["agg"][t], agg, rtol=1e-6, atol=1e-30)
+        ms = sum(v * v for v in agg) / L
+        n = [f32(agg[i] / math.sqrt(ms + 1e-5) * float(dense["gamma"][i])) for i in range(L)]
+        assert np.allclose(r["n"][t], n, rtol=1e-6, atol=1e-30)
+        out = [n[i % L] if i < L else -n[i % L] for i in range(H)]
+        for s_ in range(2):
+            hs = [f32(_situ(xt[(q + 5 * s_) % H], f32(2.0 * xt[(3 * q + s_) % H]))) for q in range(SI)]
+            for i in range(H):
+                out[i] += (0.5 if i % 2 == 0 else -0.5) * hs[(i + s_) % SI]
+        assert np.allclose(r["out"][t], np.array(out, np.float32), rtol=1e-6, atol=1e-30)
+    # token 1 is in the regime where eps decides the scale of n
+    agg1 = r["agg"][1].astype(np.float64)
+    assert np.mean(agg1 ** 2) < 1e-5
 
 
 def test_block_small_composes():

@@ -102,13 +102,21 @@ def test_logits_fixed_order_and_exactness():
     lg = oracle.route_logits(x, W)
     ref = x.astype(np.float64) @ W.astype(np.float64).T
     assert np.all(np.abs(lg - ref) <= 1e-13 * (np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T))
-    # the documented four-accumulator order, checked on a case where order matters
-    w = np.array([1e16, 1.0, -1e16, 1.0, 1.0], np.float32)
-    xv = np.ones((1, 5), np.float32)
-    # a0 = 1e16(+tail 1.0 later), a1 = 1, a2 = -1e16, a3 = 1 -> (a0+a1)+(a2+a3) = 0 in double, then + 1
-    got = oracle.route_logits(xv, w[None, :])[0, 0]
-    a0, a1, a2, a3 = float(np.float32(1e16)), 1.0, -float(np.float32(1e16)), 1.0
-    assert got == ((a0 + a1) + (a2 + a3)) + 1.0
+    # exactly rounded reference (math.fsum of the exact double products): the
+    # in-order double sum stays within n*2^-53 of sum|w x| (the standard bound)
+    import math
+    for t in range(2):
+        for e in range(0, 64, 7):
+            exact = math.fsum((x[t].astype(np.float64) * W[e].astype(np.float64)).tolist())
+            ab = float(np.abs(x[t].astype(np.float64)) @ np.abs(W[e].astype(np.float64)))
+            assert abs(lg[t, e] - exact) <= 3584 * 2.0 ** -53 * ab
+    # the documented order (index order, one double accumulator), on a case
+    # where the order decides the result: 2^53 + 1 rounds back to 2^53 (ties to
+    # even), so 1 + 2^53 - 2^53 gives 0 in index order while the exact sum is 1
+    w = np.array([1.0, 2.0 ** 53, -(2.0 ** 53), 1.0], np.float32)
+    xv = np.ones((1, 4), np.float32)
+    assert oracle.route_logits(xv, w[None, :])[0, 0] == 1.0  # 0 + 1 at the end
+    assert oracle.route_logits(xv[:, :3], w[None, :3])[0, 0] == 0.0
 
 
 # ---- K3_TOPP ("Kimi K3 engine (c/kimi_k3.c)", "Streaming design" and its table of
