@@ -528,8 +528,8 @@ __global__ __launch_bounds__(NT) void bucket_kernel(int32_t *__restrict__ counts
     extern __shared__ int sm[];
     int *cnt = sm;                                        // [E]
     int *run = sm + E;                                    // [E]
-    int *tmp = sm + 2 * E;                                // [NT / 64]
-    unsigned long long *mask = (unsigned long long *)(sm + 2 * E + 16 + ((2 * E) & 1));  // [E]
+    int *tmp = sm + 2 * E;                                // [NT / 64], then the repeat flag
+    unsigned long long *mask = (unsigned long long *)(sm + 2 * E + 18);  // [E], 8-byte aligned
     const int tid = threadIdx.x;
     const int P = T * K;
     for (int e = tid; e < E; e += NT) { cnt[e] = 0; mask[e] = 0ull; }
@@ -579,24 +579,46 @@ __global__ __launch_bounds__(NT) void bucket_kernel(int32_t *__restrict__ counts
     }
     __syncthreads();
     const int tpc = (NT / K) < 64 ? (NT / K) : 64;  // tokens per chunk
+    // A pair's rank among its expert's pairs of the chunk is the number of
+    // earlier tokens of the chunk that name the expert: one mask bit per token.
+    // That count is a pair count only while no token names an expert twice, so
+    // a chunk where one does (the OR finds its own bit already set) is placed
+    // by one thread in (token, k) order instead.
+    static_assert(NT / 64 <= 16, "the scan scratch holds 16 wavefront sums");
+    int *dup = tmp + NT / 64;                             // [1], after the scan scratch
+    if (tid == 0) *dup = 0;
+    __syncthreads();
     for (int c0 = 0; c0 < T; c0 += tpc) {
         const int lt = tid / K, k = tid - lt * K;
         const int t = c0 + lt;
         int e = 0;
         const bool live = lt < tpc && t < T && (unsigned)(e = idx[t * K + k]) < (unsigned)E;
-        if (live) atomicOr(&mask[e], 1ull << lt);
+        if (live && (atomicOr(&mask[e], 1ull << lt) & (1ull << lt))) *dup = 1;
         __syncthreads();
-        if (live) {
-            const int rank = __popcll(mask[e] & ((1ull << lt) - 1ull));
-            const int pos = run[e] + rank;
-            perm[pos] = t * K + k;
-            inv[t * K + k] = pos;
+        const bool serial = *dup != 0;
+        if (!serial) {
+            if (live) {
+                const int rank = __popcll(mask[e] & ((1ull << lt) - 1ull));
+                const int pos = run[e] + rank;
+                perm[pos] = t * K + k;
+                inv[t * K + k] = pos;
+            }
+        } else if (tid == 0) {
+            const int t1 = c0 + tpc < T ? c0 + tpc : T;
+            for (int q = c0 * K; q < t1 * K; ++q) {
+                const int eq = idx[q];
+                if ((unsigned)eq >= (unsigned)E) continue;
+                const int pos = run[eq]++;
+                perm[pos] = q;
+                inv[q] = pos;
+            }
         }
         __syncthreads();
         for (int ee = tid; ee < E; ee += NT) {
-            run[ee] += __popcll(mask[ee]);
+            if (!serial) run[ee] += __popcll(mask[ee]);
             mask[ee] = 0ull;
         }
+        if (tid == 0) *dup = 0;
         __syncthreads();
     }
 }
@@ -648,6 +670,7 @@ int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bia
 }
 
 size_t bucket_lds_bytes(int E) {
+    // cnt, run [E]; the scan scratch [16] and the repeat flag; alignment; mask [E]
     return sizeof(int) * (size_t)(2 * E + 16 + 2) + sizeof(unsigned long long) * (size_t)E;
 }
 

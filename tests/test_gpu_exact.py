@@ -291,6 +291,24 @@ def test_layer_small_ragged(k3g, decode):
     assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
+@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+def test_layer_repeated_ids(k3g, decode):
+    # tokens that name one expert twice or three times, in both 64-token chunks
+    # of the bucket: every pair gets its own sorted slot, (expert, token, k) order
+    E, latent, inter, T, K = 10, 256, 256, 70, 3
+    src, bankt, bank = make_bank(k3g, 52, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(52, T, latent)
+    W, b = synth.router(52, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K)
+    idx[0, 2] = idx[0, 0]
+    idx[5, 1] = idx[5, 0]
+    idx[5, 2] = idx[5, 0]
+    idx[63, 2] = idx[63, 1]
+    idx[64, 1] = idx[64, 0]
+    idx[69, 2] = idx[69, 0]
+    check_layer_exact(k3g, src, bankt, bank, x, idx, wts, decode=decode)
+
+
 def test_layer_skewed_routing(k3g):
     # many tokens on few experts: per-expert loops over several pairs
     E, latent, inter, T, K = 6, 256, 128, 40, 2

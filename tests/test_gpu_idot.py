@@ -140,6 +140,13 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
     yg, ws, L = run_layer_idot(k3g, bank, x, idx, wts, 0)
     P = T * K
     inv = ws_view(ws, L, "inv", P, np.int32)
+    perm = ws_view(ws, L, "perm", P, np.int32)
+    # the bucket: every pair its own slot, stable by (expert, token, k)
+    flat = idx.ravel()
+    pid = np.flatnonzero(flat >= 0)
+    Pv = pid.size
+    assert np.array_equal(perm[:Pv], pid[np.argsort(flat[pid].astype(np.int64) * T + pid // K, kind="stable")])
+    assert np.array_equal(inv[perm[:Pv]], np.arange(Pv, dtype=np.int32))
     xq = ws_view(ws, L, "xq", T * latent, np.int8).reshape(T, latent)
     xs = ws_view(ws, L, "xs", T * latent // 32, np.float32).reshape(T, latent // 32)
     qo, so = oracle.quant_i8_groups(x)
@@ -198,6 +205,23 @@ def test_layer_idot_small_many_tokens(k3g):
     W, b = synth.router(71, E, latent, 0.1)
     idx, wts, _ = oracle.route(x, W, b, K)
     check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 1, 137, 299])
+
+
+@pytest.mark.parametrize("T", [1, 70])
+def test_layer_idot_repeated_ids(k3g, T):
+    # a token naming one expert more than once: each pair has its own slot
+    E, latent, inter, K = 10, 128, 256, 4
+    src, bankt, bank = make_bank(k3g, 73, E, latent, inter, 120, 123, 0.01)
+    x = synth.activations(73, T, latent)
+    W, b = synth.router(73, E, latent, 0.2)
+    idx, wts, _ = oracle.route(x, W, b, K)
+    idx[0, 3] = idx[0, 1]
+    if T > 1:
+        idx[3, 1] = idx[3, 2] = idx[3, 0]
+        idx[64, 3] = idx[64, 0]
+    y = check_layer_idot(k3g, src, bank, x, idx, wts, tokens=range(T))
+    yo = oracle.moe_layer(x, idx, wts, {e: src(e) for e in range(E)}, E, oracle.IDOT)
+    assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
 def test_layer_idot_topp(k3g):
