@@ -324,6 +324,28 @@ int k3g_latent_moe_block(float *out, const float *x, const k3g_block_weights *w,
                          int n_tokens, int top_k, int mode, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* ---- the layer without a caller workspace --------------------------------- */
+
+/* Bytes of the library's static scratch array (64 MiB). */
+#define K3G_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid hipMalloc): k3g_moe_layer with its
+ * workspace in a file-scope device array of K3G_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends. Same
+ * arguments, kernels and results as k3g_moe_layer, without ws and ws_bytes;
+ * allocates nothing. A shape whose k3g_workspace_bytes(K3G_OP_MOE_LAYER, ...)
+ * exceeds the array returns K3G_ENOSPACE with nothing enqueued (at top_k 16:
+ * 64 decode tokens in every mode). Every call on one GPU shares that GPU's
+ * array: calls that overlap on the device (other streams, or other threads)
+ * race, and the array keeps whatever the last call left in it (no call reads
+ * what an earlier one left). The first call on a device looks up the array's
+ * address there (that device current) and keeps it. */
+int k3g_moe_layer_static(float *y, const float *x, const int32_t *idx, const float *wts,
+                         const k3g_expert_bank *bank, int n_tokens, int top_k, int mode,
+                         void *stream);
+size_t k3g_static_scratch_bytes(void);
+
 /* ---- the routed-expert cache: host memory -> HBM (streaming tier) -------- */
 
 /* The pages stream experts from storage through an LRU of expert slots

@@ -111,6 +111,9 @@ def lib():
         L.k3g_moe_route_topp.argtypes = [P, P, P, P, P, i, i, i, i, C.c_float, P, sz, P]
         L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
         L.k3g_moe_layer_stage.argtypes = [i, P, P, P, P, P, i, i, i, P, sz, P]
+        L.k3g_moe_layer_static.argtypes = [P, P, P, P, P, i, i, i, P]
+        L.k3g_static_scratch_bytes.restype = sz
+        L.k3g_static_scratch_bytes.argtypes = []
         L.k3g_latent_moe_block.argtypes = [P, P, P, i, i, i, P, sz, P]
         L.k3g_quantize_i8_groups.argtypes = [P, P, P, i, i, P]
         L.k3g_mxfp4_idot_groupsums.argtypes = [P, P, P, i, i, i, P]
@@ -312,6 +315,26 @@ def k3g_moe_layer(y: torch.Tensor, x: torch.Tensor, idx: torch.Tensor, wts: torc
     _check("k3g_moe_layer", lib().k3g_moe_layer(_ptr(y), _ptr(x), _ptr(idx), _ptr(wts), C.byref(bank),
                                                  T, K, mode, _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def k3g_moe_layer_static(y: torch.Tensor, x: torch.Tensor, idx: torch.Tensor, wts: torch.Tensor,
+                         bank: ExpertBank, mode: int, stream=None) -> torch.Tensor:
+    """k3g_moe_layer on the library's static scratch array (no workspace argument)."""
+    _dev(y, torch.float32, "y")
+    _dev(x, torch.float32, "x")
+    _dev(idx, torch.int32, "idx")
+    _dev(wts, torch.float32, "wts")
+    T, latent = x.shape
+    K = idx.shape[1]
+    if latent != bank.latent or y.shape != x.shape or wts.shape != idx.shape or idx.shape[0] != T:
+        raise ValueError("shape mismatch")
+    _check("k3g_moe_layer_static", lib().k3g_moe_layer_static(_ptr(y), _ptr(x), _ptr(idx), _ptr(wts),
+                                                               C.byref(bank), T, K, mode, _stream(stream)))
+    return y
+
+
+def static_scratch_bytes() -> int:
+    return int(lib().k3g_static_scratch_bytes())
 
 
 STAGE_BUCKET, STAGE_QUANT_X, STAGE_UP, STAGE_QUANT_H, STAGE_DOWN, STAGE_COMBINE = range(6)
