@@ -133,15 +133,22 @@ def main():
     if args.workload == "decode_b1" and not args.no_secondary:
         # the other configurations on the same resident bank, shorter runs (not the headline)
         others = []
+        cpu_lines = {}
         for wl, steps, warm, bf16, p, f4 in (("decode_b1", 100, 10, False, 0.9, False),
                                              ("decode_b64", 20, 3, False, 0.0, False),
                                              ("decode_b64", 20, 3, False, 0.0, True),
                                              ("prefill_4096_idot", 10, 2, False, 0.0, False),
                                              ("prefill_4096_idot", 10, 2, True, 0.0, False),
                                              ("prefill_4096_exact", 5, 1, False, 0.0, True)):
-            r, _ = run_workload(ctx, wl, steps, warm, bf16, mfma_decode=f4, top_p=p)
-            others.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "step_us",
-                                             "stage_us", "decode", "roofline", "steps", "warmup")})
+            r, h = run_workload(ctx, wl, steps, warm, bf16, mfma_decode=f4, top_p=p)
+            rec = {k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "step_us",
+                                     "stage_us", "decode", "roofline", "steps", "warmup")}
+            if not args.no_cpu_baseline and wl != "decode_b1":
+                key = (wl, h[-1])  # the oracle does not depend on the GPU form
+                if key not in cpu_lines:
+                    cpu_lines[key] = cpu_baseline(args, src, *h, budget=args.cpu_seconds / 2)
+                rec["cpu_baseline"] = cpu_lines[key]
+            others.append(rec)
         result["other_workloads"] = others
         # one expert on one token, and the batch-1 product on one w1
         result["expert_b1"] = run_expert(ctx, bankt)
@@ -292,7 +299,15 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * n_rot)
 
-    stage_ms = {name: time_stage(st, mode | form) for name, st in stages}
+    # stages that enqueue nothing in this form are reported as null, not timed:
+    # one EXACT token ranks its route entries inside the up kernel (no bucket
+    # launch), and the FP4 matrix-core up kernel writes h's pieces itself
+    empty = set()
+    if T == 1 and mode == k3g.EXACT:
+        empty.add("bucket")
+    if f4:
+        empty.add("quant_h")
+    stage_ms = {name: (None if name in empty else time_stage(st, mode | form)) for name, st in stages}
     # the same products in the other decode forms: the LDS byte-pair table, and the
     # FP4 matrix cores (x split into pieces first) or the vector convert
     lut_ms, alt_ms = {}, {}
@@ -323,6 +338,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     if mode == k3g.IDOT:
         up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * 4
 
+    # the tag of this form in the names of the committed counter summaries
+    form_tag = "fp4_mfma" if f4 else "bf16" if form == k3g.IDOT_BF16 else ""
     gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     tok_s = T / (ms_per_step * 1e-3)
     up_gbs = up_alg / (stage_ms["up"] * 1e-3) / 1e9
@@ -333,7 +350,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(up_gbs / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(workload, "moe_up"),
+        "traffic": measured_traffic(workload, "moe_up", form_tag),
         "algorithmic_bytes_per_launch": int(up_alg),
     }
     if f4:
@@ -356,7 +373,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
             "unit": "TFLOP/s",
             "ops": "int8 multiply-adds x 2" if not form else "bf16 multiply-adds x 2 (exact int8 values)",
             "frac": round(tops / peak, 4),
-            "traffic": measured_traffic(workload, "moe_up"),
+            "traffic": measured_traffic(workload, "moe_up", form_tag),
             "algorithmic_ops_per_launch": up_ops,
             "hbm_achieved_GBps": round(up_gbs, 1),
             "hbm_frac": round(up_gbs / HBM_PEAK_GBS, 4),
@@ -389,7 +406,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
         "step_us": {"n": int(n_single), "median": round(float(np.median(single_us)), 2),
                     "best": round(float(single_us.min()), 2), "worst": round(float(single_us.max()), 2),
                     "timing": "HIP events around each step, back to back"},
-        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "stage_us": {k: (None if v is None else round(v * 1e3, 2)) for k, v in stage_ms.items()},
         "decode": ("gfx950 FP4 MFMA on the stored nibbles, x and h as 16 e2m1 pieces" if f4 else
                    "gfx950 FP4->FP32 convert" if mode == k3g.EXACT else
                    "bf16 MFMA on exact int8 values" if form else "int8 MFMA"),
@@ -406,23 +423,21 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     return result, (xs_host, W, b, alg_bytes, T, mode)
 
 
-# the sources of the decode expert kernels whose counters profiles/ holds
-TRAFFIC_SOURCES = ("gemv.hip", "k3g_common.h")
-
-
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, kernel, form=""):
     """HBM bytes per launch (read + write) of `kernel` from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, scaled by the copy calibration; None when no
-    summary exists for this workload or the kernel sources (TRAFFIC_SOURCES)
-    changed since."""
+    FETCH_SIZE / WRITE_SIZE summary `profiles/<workload>[_<form>]_traffic.json`,
+    scaled by the copy calibration it records; None when no summary exists or
+    the kernel sources it lists have changed since it was taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    name = f"{workload}_{form}_traffic.json" if form else f"{workload}_traffic.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     doc = json.load(open(path))
     csrc = os.path.join(ROOT, "mxfp4_moe_expert_amd", "csrc")
-    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in TRAFFIC_SOURCES)).hexdigest()
+    srcs = doc.get("sources", ["gemv.hip", "k3g_common.h"])
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in srcs)).hexdigest()
     if sha != doc.get("source_sha256") or kernel not in doc.get("kernels", {}):
         return None
     k = doc["kernels"][kernel]
@@ -730,41 +745,72 @@ def copy_calibration(torch, gib):
                       "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode):
+def host_facts():
+    """The host the oracle runs on: CPU model, logical CPUs, OpenMP threads."""
+    import oracle
+
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "omp_threads": oracle.threads()}
+
+
+def cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode, budget=None, max_experts=320, max_tokens=64):
     """The oracle, as it is, on a bounded sample of the same workload: whole
-    steps (route + layer) for as many of the bench's tokens as fit the budget."""
+    steps (fp64 route + layer) of one token at a time. The sample is the
+    bench's first tokens, as many (up to max_tokens) as use at most
+    max_experts distinct experts between them (their bytes drawn beforehand,
+    untimed); passes over the sample repeat until the time budget is spent.
+    One token a step: GB/s over the step's algorithmic bytes. More tokens: the
+    oracle's cost grows linearly with the tokens (each token's pairs are
+    computed on their own, and routing is per token), so the sample's tokens/s
+    stands for the batch's."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
     K = 16
-    done = 0
-    spent = 0.0
-    tokens = 0
+    budget = args.cpu_seconds if budget is None else budget
     xs_flat = np.concatenate(xs_host, 0)
-    cache = {}
-    while spent < args.cpu_seconds:
-        i = done % xs_flat.shape[0]  # the bench's tokens, cycled until the budget is spent
-        x = xs_flat[i:i + 1]
-        io, wo, _ = oracle.route(x, W, b, K)  # noqa: F841 (timed below with the layer)
-        for e in io.ravel():                                   # generation is not timed
-            if int(e) not in cache:
-                cache[int(e)] = src(int(e))
-        experts = {int(e): cache[int(e)] for e in io.ravel()}
-        t = time.perf_counter()
-        io, wo, _ = oracle.route(x, W, b, K)
-        oracle.moe_layer(x, io, wo, experts, 896, oracle.EXACT if mode == 0 else oracle.IDOT)
-        spent += time.perf_counter() - t
-        done += 1
-        tokens += 1
-    bytes_per_token = alg_bytes / T if T == 1 else None
-    return {
-        "value": round(bytes_per_token * tokens / spent / 1e9, 3) if bytes_per_token else round(tokens / spent, 3),
-        "unit": "GB/s" if bytes_per_token else "tokens/s",
-        "tokens_per_s": round(tokens / spent, 4),
-        "cores": oracle.threads(),
-        "kind": "oracle",
-        "sample": f"{tokens} decode tokens, each a whole step (fp64 router + top-16 + 16 SiTU-GLU experts "
-                  f"+ combine), {spent:.1f} s",
-    }
+    sample, used = [], set()
+    for i in range(min(max_tokens, xs_flat.shape[0])):
+        io, _, _ = oracle.route(xs_flat[i:i + 1], W, b, K)
+        ids = {int(e) for e in io.ravel()}
+        if sample and len(used | ids) > max_experts:
+            break
+        used |= ids
+        sample.append(i)
+    with ThreadPoolExecutor(16) as pool:
+        experts = dict(zip(sorted(used), pool.map(src, sorted(used))))
+    spent, tokens = 0.0, 0
+    while spent < budget:
+        for i in sample:
+            x = xs_flat[i:i + 1]
+            t = time.perf_counter()
+            io, wo, _ = oracle.route(x, W, b, K)
+            oracle.moe_layer(x, io, wo, {int(e): experts[int(e)] for e in io.ravel()}, 896,
+                             oracle.EXACT if mode == 0 else oracle.IDOT)
+            spent += time.perf_counter() - t
+            tokens += 1
+    del experts
+    facts = host_facts()
+    what = "EXACT" if mode == 0 else "IDOT"
+    desc = (f"{tokens} token steps over the workload's first {len(sample)} tokens ({len(used)} distinct experts), "
+            f"one token at a time, each a whole step (fp64 router + top-16 + 16 {what} SiTU-GLU experts + "
+            f"combine), {spent:.1f} s")
+    if T == 1:
+        return {"value": round(alg_bytes * tokens / spent / 1e9, 3), "unit": "GB/s",
+                "tokens_per_s": round(tokens / spent, 4), "cores": facts["omp_threads"], **facts,
+                "kind": "oracle", "sample": desc}
+    return {"value": round(tokens / spent, 4), "unit": "tokens/s", "cores": facts["omp_threads"], **facts,
+            "kind": "oracle",
+            "sample": desc + f"; of a {T}-token batch: the oracle's work is linear in the tokens, so the "
+                             f"sample's rate stands for the batch's"}
 
 
 if __name__ == "__main__":

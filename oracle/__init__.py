@@ -54,6 +54,7 @@ def lib():
         L.k3o_matmul_bf16.argtypes = [P, P, P, P, i, i]
         L.k3o_situ.restype = C.c_double
         L.k3o_situ.argtypes = [C.c_double] * 4
+        L.k3o_situ_vec.argtypes = [P, P, P, i]
         L.k3o_quant_i8_groups.argtypes = [P, P, P, i, i]
         L.k3o_idot_groupsums.argtypes = [P, P, P, i, i, i]
         L.k3o_mxfp4_gemv_idot.argtypes = [P, P, P, P, P, P, P, i, i]
@@ -164,11 +165,11 @@ def situ(g: float, u: float, b1: float = SITU_B1, b2: float = SITU_B2) -> float:
 
 def situ_vec(g, u):
     """Elementwise SiTU of float32 arrays, each value rounded to float32."""
-    g = np.asarray(g, np.float32).ravel()
-    u = np.asarray(u, np.float32).ravel()
-    L = lib()
-    return np.array([L.k3o_situ(float(a), float(b), SITU_B1, SITU_B2) for a, b in zip(g, u)],
-                    dtype=np.float64).astype(np.float32)
+    g = _c(np.asarray(g, np.float32).ravel(), np.float32)
+    u = _c(np.asarray(u, np.float32).ravel(), np.float32)
+    h = np.empty(g.shape[0], np.float32)
+    _chk(lib().k3o_situ_vec(_p(h), _p(g), _p(u), g.shape[0]), "situ_vec")
+    return h
 
 
 # -- IDOT ------------------------------------------------------------------

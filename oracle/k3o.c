@@ -291,6 +291,17 @@ double k3o_situ(double g, double u, double b1, double b2)
     return b1 * tanh(g / b1) * sig * b2 * tanh(u / b2);
 }
 
+/* Elementwise h[i] = SiTU(g[i], u[i]) with b1 = 4, b2 = 25, each value
+ * computed in double and rounded to float once. */
+int k3o_situ_vec(float *h, const float *g, const float *u, int n)
+{
+    if (n < 0)
+        return -1;
+    for (int i = 0; i < n; ++i)
+        h[i] = (float)k3o_situ((double)g[i], (double)u[i], 4.0, 25.0);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* IDOT: int8 activations against doubled e2m1 values.                        */
 /* ------------------------------------------------------------------------ */

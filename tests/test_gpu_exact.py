@@ -256,14 +256,15 @@ def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0)
     h = ws_view(ws, L, "h", P * inter, np.float32).reshape(P, inter)
     ypair = ws_view(ws, L, "ypair", P * latent, np.float32).reshape(P, latent)
     tokens = range(T) if tokens is None else tokens
+    # up and down, pair by pair, grouped by expert (each expert's bytes drawn once)
+    by_expert = {}
     for t in tokens:
-        acc_ref = np.zeros(latent)
-        nrm_c = np.zeros(latent)
         for k in range(K):
-            e = int(idx[t, k])
-            if e < 0:  # dropped: contributes nothing
-                continue
-            ex = src(e)
+            if int(idx[t, k]) >= 0:  # dropped entries are no pairs
+                by_expert.setdefault(int(idx[t, k]), []).append((t, k))
+    for e, tk in sorted(by_expert.items()):
+        ex = src(e)
+        for t, k in tk:
             pos = inv[t * K + k]
             g, _, ng = oracle.mxfp4_gemv(x[t], ex["w1p"], ex["w1s"], full=True)
             u, _, nu = oracle.mxfp4_gemv(x[t], ex["w3p"], ex["w3s"], full=True)
@@ -271,9 +272,16 @@ def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0)
             assert_within(h[pos], ho, situ_tolerance(g, u, ng, nu), g, u, f"layer h t={t} k={k}")
             y2, _, n2 = oracle.mxfp4_gemv(h[pos], ex["w2p"], ex["w2s"], full=True)
             assert_norm_close(ypair[pos], y2, n2, what=f"layer down t={t} k={k}")
+    # combine, isolated: the weighted sum of the GPU's own pair outputs
+    for t in tokens:
+        acc_ref = np.zeros(latent)
+        nrm_c = np.zeros(latent)
+        for k in range(K):
+            if int(idx[t, k]) < 0:  # dropped: contributes nothing
+                continue
+            pos = inv[t * K + k]
             acc_ref += float(wts[t, k]) * ypair[pos].astype(np.float64)
             nrm_c += abs(float(wts[t, k])) * np.abs(ypair[pos].astype(np.float64))
-        # combine, isolated: the weighted sum of the GPU's own pair outputs
         assert_norm_close(y[t], acc_ref, nrm_c, what=f"combine t={t}")
     return y
 
@@ -603,8 +611,9 @@ def test_layer_decode_b64_full_sampled(k3g, full_bank, decode):
     W, b = synth.router(seed, 896, 3584, 0.01)
     x = synth.activations(seed, 64, 3584)
     io, wo, _ = oracle.route(x, W, b, 16)
-    # sampled outputs: three tokens checked pair by pair
-    check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=[0, 31, 63], decode=decode)
+    # every token, pair by pair (all 1,024 pairs), each stage on the GPU's own input
+    print(f"decode_b64 form {decode:#x}: checking 1024 pairs on the oracle", flush=True)
+    check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=range(64), decode=decode)
 
 
 # ---- the routed-expert cache: host memory -> HBM ------------------------------------------

@@ -134,7 +134,11 @@ def run_layer_idot(k3g, bank, x, idx, wts, form):
     return host(y), ws, L
 
 
-def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
+def check_layer_idot(k3g, src, bank, x, idx, wts, tokens, experts=()):
+    """Stage by stage against the oracle: every pair of the given tokens and
+    every pair of the given experts (h, its quantisation, the down product),
+    grouped by expert; the combine of the given tokens on the GPU's own pair
+    outputs; and the bf16 form against the int8 form bit for bit."""
     T, K = idx.shape
     latent, inter, E = bank.latent, bank.inter, bank.n_experts
     yg, ws, L = run_layer_idot(k3g, bank, x, idx, wts, 0)
@@ -147,24 +151,24 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
     Pv = pid.size
     assert np.array_equal(perm[:Pv], pid[np.argsort(flat[pid].astype(np.int64) * T + pid // K, kind="stable")])
     assert np.array_equal(inv[perm[:Pv]], np.arange(Pv, dtype=np.int32))
+    assert np.all(inv[flat < 0] == -1)  # dropped by a K3_TOPP cut: not a pair
     xq = ws_view(ws, L, "xq", T * latent, np.int8).reshape(T, latent)
     xs = ws_view(ws, L, "xs", T * latent // 32, np.float32).reshape(T, latent // 32)
     qo, so = oracle.quant_i8_groups(x)
     assert np.array_equal(xq, qo) and np.array_equal(xs.view(np.uint32), so.view(np.uint32))
 
-    def rows_of(name, count, dtype, width):
-        return lambda pos: ws_view_rows(ws, L, name, pos, width, dtype)
-
+    by_expert = {}
     for t in tokens:
-        acc = np.zeros(latent)
-        nrm = np.zeros(latent)
         for k in range(K):
-            e = int(idx[t, k])
-            if e < 0:  # dropped by a K3_TOPP cut: not a pair, adds nothing
-                assert inv[t * K + k] == -1
-                continue
-            ex = src(e)
-            pos = int(inv[t * K + k])
+            if int(idx[t, k]) >= 0:
+                by_expert.setdefault(int(idx[t, k]), set()).add(t * K + k)
+    for e in experts:
+        by_expert.setdefault(int(e), set()).update(int(p) for p in pid[flat[pid] == e])
+    for e, ps in sorted(by_expert.items()):
+        ex = src(e)
+        for p in sorted(ps):
+            t, k = divmod(p, K)
+            pos = int(inv[p])
             g, _, ng = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w1p"], ex["w1s"], full=True)
             u, _, nu = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w3p"], ex["w3s"], full=True)
             hg = ws_view_rows(ws, L, "h", pos, inter, np.float32)
@@ -177,15 +181,24 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens):
             y2, _, n2 = oracle.mxfp4_gemv_idot(qh, sh_, ex["w2p"], ex["w2s"], full=True)
             yp = ws_view_rows(ws, L, "ypair", pos, latent, np.float32)
             assert_norm_close(yp, y2, n2, what=f"idot down t={t} k={k}")
-            acc += float(wts[t, k]) * yp.astype(np.float64)
-            nrm += abs(float(wts[t, k])) * np.abs(yp.astype(np.float64))
-        assert_norm_close(yg[t], acc, nrm, what=f"idot combine t={t}")
+    # the combine of every token, on the GPU's own pair outputs
+    ypair = ws_view(ws, L, "ypair", Pv * latent, np.float32).reshape(Pv, latent)
+    for t0 in range(0, T, 256):
+        t1 = min(T, t0 + 256)
+        acc = np.zeros((t1 - t0, latent))
+        nrm = np.zeros((t1 - t0, latent))
+        for k in range(K):
+            live = idx[t0:t1, k] >= 0
+            w = np.where(live, wts[t0:t1, k], 0.0).astype(np.float64)[:, None]
+            yp = ypair[np.where(live, inv[np.arange(t0, t1) * K + k], 0)].astype(np.float64)
+            acc += w * yp
+            nrm += np.abs(w) * np.abs(yp)
+        assert_norm_close(yg[t0:t1], acc, nrm, what=f"idot combine tokens {t0}..{t1 - 1}")
     # the bf16 form computes the same numbers bit for bit (over the pairs that exist)
     yb, wsb, Lb = run_layer_idot(k3g, bank, x, idx, wts, 0x200)
-    P = int(np.count_nonzero(idx >= 0))
     for name, width, dt in (("h", inter, np.float32), ("hq", inter, np.int8), ("ypair", latent, np.float32)):
-        a = ws_view(ws, L, name, P * width, dt)
-        b = ws_view(wsb, Lb, name, P * width, dt)
+        a = ws_view(ws, L, name, Pv * width, dt)
+        b = ws_view(wsb, Lb, name, Pv * width, dt)
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"bf16 form differs in {name}"
     assert np.array_equal(yg.view(np.uint32), yb.view(np.uint32)), "bf16 form differs in y"
     return yg
@@ -244,4 +257,13 @@ def test_layer_idot_prefill_4096_sampled(k3g, full_bank):
     x = synth.activations(seed, 4096, 3584)
     print("routing 4096 tokens on the oracle", flush=True)
     idx, wts, _ = oracle.route(x, W, b, 16)
-    check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 2047, 4095])
+    counts = np.bincount(idx.ravel(), minlength=896)
+    # every pair of four experts: the fullest (past the int8 kernel's 96-token
+    # chunk, so its second chunk and a partial tile are checked), the emptiest
+    # in use, and two of middling load
+    order = np.argsort(counts, kind="stable")
+    used = order[counts[order] > 0]
+    experts = [int(used[-1]), int(used[0]), int(used[len(used) // 2]), int(used[len(used) // 3])]
+    assert counts[experts[0]] > 96 and counts[experts[0]] % 16 != 0
+    print(f"checking every pair of experts {experts} ({counts[experts].tolist()} pairs)", flush=True)
+    check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 2047, 4095], experts=experts)

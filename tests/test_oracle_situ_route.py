@@ -21,6 +21,14 @@ from tests.conftest import read_table
 GU = [(-30.0, 7.0), (-3.0, -2.0), (-0.5, 40.0), (0.25, 0.1), (1.0, -1.0), (2.5, 12.0), (9.0, 100.0)]
 
 
+def test_situ_vec_is_the_scalar_formula_elementwise():
+    g = synth.normal_f32(13, 500, 6.0, key=1)
+    u = synth.normal_f32(13, 500, 40.0, key=2)
+    h = oracle.situ_vec(g, u)
+    want = np.array([np.float32(oracle.situ(float(a), float(b))) for a, b in zip(g, u)])
+    assert np.array_equal(h, want)
+
+
 @pytest.mark.parametrize("g,u", GU)
 def test_situ_odd_even_parts(g, u):
     hp = oracle.situ(g, u)

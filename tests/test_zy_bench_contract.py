@@ -38,3 +38,6 @@ def test_bench_line_contract():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["nproc"] >= 1 and cb["cpu_model"] and cb["omp_threads"] == cb["cores"]
+    # a stage that enqueues nothing in this form is null, not a timed empty graph
+    assert d["stage_us"]["bucket"] is None and d["stage_us"]["up"] > 0
