@@ -305,7 +305,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     empty = set()
     if T == 1 and mode == k3g.EXACT:
         empty.add("bucket")
-    if f4:
+    if f4 or mode == k3g.IDOT:  # these up kernels write the down product's operand themselves
         empty.add("quant_h")
     stage_ms = {name: (None if name in empty else time_stage(st, mode | form)) for name, st in stages}
     # the same products in the other decode forms: the LDS byte-pair table, and the
@@ -335,8 +335,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     router_b = E * L * 4 + E * 4
     alg_bytes = n_exp * (up_b + dn_b) + router_b + 2 * T * L * 4
     up_alg = n_exp * up_b + T * L * 4 + P * I * 4       # weights once, x in, h out
-    if mode == k3g.IDOT:
-        up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * 4
+    if mode == k3g.IDOT:  # int8 x and its scales in; h out quantised (int8, or bf16 in that form) with its scales
+        up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * (2 if form else 1) + P * (I // 32) * 4
 
     # the tag of this form in the names of the committed counter summaries
     form_tag = "fp4_mfma" if f4 else "bf16" if form == k3g.IDOT_BF16 else ""

@@ -157,8 +157,10 @@ typedef struct {
  *   inv     int32 [P]                    pair id -> sorted position
  *   active  int32 [n_experts+1]          [0] = number of experts with pairs, then their ids ascending
  *   xq, xs  int8 [T][latent], float [T][latent/32]   IDOT activations
- *   h       float [P][inter]             SiTU output per sorted pair
- *   hq, hs  int8 [P][inter], float [P][inter/32]      IDOT h
+ *   h       float [P][inter]             SiTU output per sorted pair (EXACT only)
+ *   hq, hs  int8 [P][inter], float [P][inter/32]      IDOT h, quantised by the
+ *           up kernel (no fp32 h in IDOT; hq absent in the bf16 form, where
+ *           hqb holds the same values)
  *   ypair   float [P][latent]            expert output per sorted pair, unweighted
  *   idx, wts int32/float [T][top_k]      block routing
  *   lat, agg, nrm  float [T][latent]     block stages
@@ -288,9 +290,14 @@ int k3g_moe_layer(float *y, const float *x, const int32_t *idx, const float *wts
  * caller can place events between them to time each kernel:
  *   BUCKET   stable sort of the pairs by expert (counts, offsets, perm, inv, active)
  *   QUANT_X  IDOT: x -> xq, xs; K3G_DECODE_MFMA: x -> xp
- *   UP       per expert and row: g = w1 a, u = w3 a, h = SiTU(g, u)
- *   QUANT_H  IDOT: h -> hq, hs (with K3G_DECODE_MFMA, UP writes hp itself
- *            and this stage enqueues nothing)
+ *   UP       per expert and row: g = w1 a, u = w3 a, h = SiTU(g, u) (IDOT:
+ *            written quantised per 32-group, as the down product takes it)
+ *   QUANT_H  enqueues nothing in every mode: the IDOT up-projection writes
+ *            h quantised (hq or hqb, and hs) and the K3G_DECODE_MFMA one its
+ *            pieces (hp) themselves; the stage is kept so that stage numbers
+ *            stay fixed
+ *   (BUCKET enqueues nothing for one token in EXACT mode: the up-projection
+ *   ranks the route entries and writes the bucket itself.)
  *   DOWN     per expert and row: ypair = w2 h
  *   COMBINE  y[t] = sum_k wts[t][k] * ypair[inv[t*top_k+k]]
  * Arguments as k3g_moe_layer; every stage validates them the same way and

@@ -28,9 +28,9 @@ int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv
 int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, uint16_t *qb, hipStream_t st);
 int launch_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *packed, int in, int rows, int n_tokens,
                           hipStream_t st);
-int launch_moe_up_idot(float *h, const int8_t *xq, const uint16_t *xqb, const float *xs, const BankDev &bank, const int32_t *active,
-                       const int32_t *offsets, const int32_t *perm, int top_k, int latent, int inter, int max_slots,
-                       hipStream_t st);
+int launch_moe_up_idot(int8_t *hq, uint16_t *hqb, float *hs, const int8_t *xq, const uint16_t *xqb, const float *xs,
+                       const BankDev &bank, const int32_t *active, const int32_t *offsets, const int32_t *perm,
+                       int top_k, int latent, int inter, int max_slots, hipStream_t st);
 int launch_moe_down_idot(float *ypair, const int8_t *hq, const uint16_t *hqb, const float *hs, const BankDev &bank, const int32_t *active,
                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
                          hipStream_t st);
@@ -178,16 +178,18 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
         case K3G_OP_EXPERT_GLU: {
             if (s.latent <= 0 || s.inter <= 0 || s.latent % kGroup || s.inter % kGroup || !mode_ok(s.mode))
                 return K3G_EINVAL;
-            o->h = c.take(sizeof(float) * s.inter);
-            if (base_mode(s.mode) == K3G_IDOT) {
+            if (base_mode(s.mode) == K3G_IDOT) {  // h only quantised (the up kernel writes it so)
                 o->xq = c.take((size_t)s.latent);
                 o->xs = c.take(sizeof(float) * (s.latent / kGroup));
-                o->hq = c.take((size_t)s.inter);
                 o->hs = c.take(sizeof(float) * (s.inter / kGroup));
                 if (bf16_of(s.mode)) {
                     o->xqb = c.take(sizeof(uint16_t) * s.latent);
                     o->hqb = c.take(sizeof(uint16_t) * s.inter);
+                } else {
+                    o->hq = c.take((size_t)s.inter);
                 }
+            } else {
+                o->h = c.take(sizeof(float) * s.inter);
             }
             break;
         }
@@ -221,16 +223,17 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
             o->perm = c.take(sizeof(int32_t) * (P ? P : 1));
             o->inv = c.take(sizeof(int32_t) * (P ? P : 1));
             o->active = c.take(sizeof(int32_t) * (E + 1));
-            o->h = c.take(sizeof(float) * (P ? P : 1) * s.inter);
+            if (base_mode(s.mode) != K3G_IDOT) o->h = c.take(sizeof(float) * (P ? P : 1) * s.inter);
             o->ypair = c.take(sizeof(float) * (P ? P : 1) * s.latent);
-            if (base_mode(s.mode) == K3G_IDOT) {
+            if (base_mode(s.mode) == K3G_IDOT) {  // h only quantised (the up kernel writes it so)
                 o->xq = c.take((T ? T : 1) * (size_t)s.latent);
                 o->xs = c.take(sizeof(float) * (T ? T : 1) * (s.latent / kGroup));
-                o->hq = c.take((P ? P : 1) * (size_t)s.inter);
                 o->hs = c.take(sizeof(float) * (P ? P : 1) * (s.inter / kGroup));
                 if (bf16_of(s.mode)) {
                     o->xqb = c.take(sizeof(uint16_t) * (T ? T : 1) * s.latent);
                     o->hqb = c.take(sizeof(uint16_t) * (P ? P : 1) * s.inter);
+                } else {
+                    o->hq = c.take((P ? P : 1) * (size_t)s.inter);
                 }
             }
             if (f4_layer(s.mode, s.n_tokens, s.latent, s.inter)) {  // 10 bytes per entry
@@ -409,19 +412,18 @@ int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode, void
     b.off[W2P] = e->w2.packed - e->w1.packed;
     b.off[W2S] = e->w2.scales - e->w1.packed;
     char *w = (char *)ws;
-    float *h = (float *)(w + L.h);
+    float *h = L.h ? (float *)(w + L.h) : nullptr;
     hipStream_t st = S(stream);
     if (base_mode(mode) == K3G_EXACT) {
         K3G_TRY(launch_moe_up_exact(h, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut_of(mode), Route1{},
                                     st));
         return launch_moe_down_exact(y, h, b, nullptr, nullptr, nullptr, latent, inter, 1, false, lut_of(mode), st);
     }
-    int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
+    int8_t *xq = (int8_t *)(w + L.xq), *hq = L.hq ? (int8_t *)(w + L.hq) : nullptr;
     float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
     uint16_t *xqb = L.xqb ? (uint16_t *)(w + L.xqb) : nullptr, *hqb = L.hqb ? (uint16_t *)(w + L.hqb) : nullptr;
     K3G_TRY(launch_quant_i8(xq, xs, x, 1, latent, xqb, st));
-    K3G_TRY(launch_moe_up_idot(h, xq, xqb, xs, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, st));
-    K3G_TRY(launch_quant_i8(hq, hs, h, 1, inter, hqb, st));
+    K3G_TRY(launch_moe_up_idot(hq, hqb, hs, xq, xqb, xs, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, st));
     return launch_moe_down_idot(y, hq, hqb, hs, b, nullptr, nullptr, nullptr, latent, inter, 1, st);
 }
 
@@ -485,8 +487,8 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
     char *w = (char *)ws;
     int32_t *counts = (int32_t *)(w + L.counts), *offsets = (int32_t *)(w + L.offsets);
     int32_t *perm = (int32_t *)(w + L.perm), *inv = (int32_t *)(w + L.inv), *active = (int32_t *)(w + L.active);
-    float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
-    int8_t *xq = (int8_t *)(w + L.xq), *hq = (int8_t *)(w + L.hq);
+    float *h = L.h ? (float *)(w + L.h) : nullptr, *ypair = (float *)(w + L.ypair);
+    int8_t *xq = (int8_t *)(w + L.xq), *hq = L.hq ? (int8_t *)(w + L.hq) : nullptr;
     float *xs = (float *)(w + L.xs), *hs = (float *)(w + L.hs);
     uint16_t *xqb = L.xqb ? (uint16_t *)(w + L.xqb) : nullptr, *hqb = L.hqb ? (uint16_t *)(w + L.hqb) : nullptr;
     const int P = n_tokens * top_k;
@@ -517,12 +519,14 @@ static int layer_stage(int stage, const k3g_ws_layout &L, float *y, const float 
                                          max_slots, st);
             if (f4) return launch_moe_up_f4(h, hp, xp, b, r1, top_k, latent, inter, max_slots, st);
             return base_mode(mode) == K3G_IDOT
-                       ? launch_moe_up_idot(h, xq, xqb, xs, b, active, offsets, perm, top_k, latent, inter, max_slots, st)
+                       ? launch_moe_up_idot(hq, hqb, hs, xq, xqb, xs, b, active, offsets, perm, top_k, latent, inter,
+                                            max_slots, st)
                        : launch_moe_up_exact(h, x, b, active, offsets, perm, top_k, latent, inter, max_slots, P,
                                              lut_of(mode), r1, st);
         case K3G_STAGE_QUANT_H:
-            if (f4) return K3G_OK;  // the up-projection wrote hp
-            return base_mode(mode) == K3G_IDOT ? launch_quant_i8(hq, hs, h, P, inter, hqb, st) : K3G_OK;
+            // nothing to launch: the FP4 matrix-core up-projection writes hp, and the
+            // IDOT up-projection writes hq (or hqb) and hs, itself
+            return K3G_OK;
         case K3G_STAGE_DOWN:
             if (f4m)
                 return launch_moe_down_f4m(ypair, hp, b, active, offsets, passes, npp, latent, inter, P, max_slots,

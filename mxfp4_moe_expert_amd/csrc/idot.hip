@@ -218,7 +218,8 @@ __device__ inline void lds_load4(const void *src, void *lds) {
 
 template <bool UP>
 __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
-    float *__restrict__ out, const int8_t *__restrict__ aq, const float *__restrict__ as, BankDev bank, const int32_t *__restrict__ active,
+    float *__restrict__ out, int8_t *__restrict__ hq_out, float *__restrict__ hs_out, const int8_t *__restrict__ aq,
+    const float *__restrict__ as, BankDev bank, const int32_t *__restrict__ active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int n_in, int n_out,
     int max_slots) {
     constexpr int GB = 4;                     // groups per block
@@ -239,6 +240,7 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t sc_lds[2][IX_WAVES][64];   // a row's 4 scale bytes (x2)
     __shared__ __attribute__((aligned(16))) float ws_lds[IX_WAVES][GB][32];
     __shared__ int row_lds[NTOK];
+    __shared__ float amax_lds[IX_WAVES][NTOK];  // UP: per wavefront and token, max |h| over its 16 rows
     const int tid = threadIdx.x, lane = tid & 63, wl = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int ngrp = n_in / kGroup;
@@ -396,24 +398,61 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
                     __syncthreads();
                 }
                 // results: lane holds token col of each tile, rows 8q + 4*half + 0..3 in slots 4q..4q+3
+                if constexpr (UP) {
+                    // h = SiTU(g, u) of the wavefront's 16 rows, quantised per 32-group of h:
+                    // the two wavefronts wl and wl^1 hold the halves of one group, so the
+                    // group's maximum meets through LDS
+                    float hv[NTL][8];
+                    float m[NTL];
 #pragma unroll
-                for (int tt = 0; tt < NTL; ++tt) {
-                    const int i = tt * 32 + col;
-                    if (i < n_tok) {
-                        float *dst = out + (size_t)(c0 + i) * n_out + rbase + 4 * half;
+                    for (int tt = 0; tt < NTL; ++tt) {
+                        m[tt] = 0.f;
 #pragma unroll
-                        for (int q = 0; q < (UP ? 2 : 4); ++q) {
-                            float r4[4];
+                        for (int q = 0; q < 2; ++q)
 #pragma unroll
-                            for (int b = 0; b < 4; ++b)
-                                r4[b] = UP ? situ(acc[tt][4 * q + b], acc[tt][8 + 4 * q + b]) : acc[tt][4 * q + b];
-                            const int r0 = rbase + 8 * q + 4 * half;
-                            if (r0 + 3 < n_out && ((uintptr_t)(dst + 8 * q) & 15) == 0) {
-                                *(float4 *)(dst + 8 * q) = make_float4(r4[0], r4[1], r4[2], r4[3]);
-                            } else {
+                            for (int b = 0; b < 4; ++b) {
+                                hv[tt][4 * q + b] = situ(acc[tt][4 * q + b], acc[tt][8 + 4 * q + b]);
+                                m[tt] = __builtin_fmaxf(m[tt], __builtin_fabsf(hv[tt][4 * q + b]));
+                            }
+                        m[tt] = __builtin_fmaxf(m[tt], __shfl_xor(m[tt], 32));
+                        if (half == 0) amax_lds[wl][32 * tt + col] = m[tt];
+                    }
+                    __syncthreads();
+                    const int ngo = n_out / kGroup;
 #pragma unroll
-                                for (int b = 0; b < 4; ++b)
-                                    if (r0 + b < n_out) dst[8 * q + b] = r4[b];
+                    for (int tt = 0; tt < NTL; ++tt) {
+                        const int i = tt * 32 + col;
+                        const float sc = idot_group_scale(__builtin_fmaxf(m[tt], amax_lds[wl ^ 1][i]));
+                        if (i < n_tok) {
+                            const size_t pos = (size_t)(c0 + i);
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                const int q0 = idot_quant(hv[tt][4 * q + 0], sc), q1 = idot_quant(hv[tt][4 * q + 1], sc);
+                                const int q2 = idot_quant(hv[tt][4 * q + 2], sc), q3 = idot_quant(hv[tt][4 * q + 3], sc);
+                                *(uint32_t *)(hq_out + pos * n_out + rbase + 8 * q + 4 * half) =
+                                    (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
+                                    ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)q3 << 24);
+                            }
+                            if (half == 0 && (wl & 1) == 0) hs_out[pos * ngo + rbase / kGroup] = sc;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < NTL; ++tt) {
+                        const int i = tt * 32 + col;
+                        if (i < n_tok) {
+                            float *dst = out + (size_t)(c0 + i) * n_out + rbase + 4 * half;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int r0 = rbase + 8 * q + 4 * half;
+                                if (r0 + 3 < n_out && ((uintptr_t)(dst + 8 * q) & 15) == 0) {
+                                    *(float4 *)(dst + 8 * q) =
+                                        make_float4(acc[tt][4 * q], acc[tt][4 * q + 1], acc[tt][4 * q + 2], acc[tt][4 * q + 3]);
+                                } else {
+#pragma unroll
+                                    for (int b = 0; b < 4; ++b)
+                                        if (r0 + b < n_out) dst[8 * q + b] = acc[tt][4 * q + b];
+                                }
                             }
                         }
                     }
@@ -429,29 +468,36 @@ __global__ __launch_bounds__(IX_WAVES * 64, 1) void moe_idot_kernel(
     }
 }
 
-int launch_idot_bf16(bool up, float *out, const uint16_t *aqb, const float *as, const BankDev &bank,
-                     const int32_t *active, const int32_t *offsets, const int32_t *perm, int top_k, int n_in,
-                     int n_out, int max_slots, hipStream_t st);
+int launch_idot_bf16(bool up, float *out, int8_t *hq, uint16_t *hqb, float *hs, const uint16_t *aqb, const float *as,
+                     const BankDev &bank, const int32_t *active, const int32_t *offsets, const int32_t *perm,
+                     int top_k, int n_in, int n_out, int max_slots, hipStream_t st);
 
-int launch_moe_up_idot(float *h, const int8_t *xq, const uint16_t *xqb, const float *xs, const BankDev &bank,
-                       const int32_t *active, const int32_t *offsets, const int32_t *perm, int top_k, int latent,
-                       int inter, int max_slots, hipStream_t st) {
-    if (xqb) return launch_idot_bf16(true, h, xqb, xs, bank, active, offsets, perm, top_k, latent, inter, max_slots, st);
+// UP: the SiTU output of every pair, quantised per 32-group of h as the down
+// product takes it: hq int8 [P][inter] (int8 form) or hqb its bf16 copy (bf16
+// form), and hs fp32 [P][inter/32]. No fp32 h is written.
+int launch_moe_up_idot(int8_t *hq, uint16_t *hqb, float *hs, const int8_t *xq, const uint16_t *xqb, const float *xs,
+                       const BankDev &bank, const int32_t *active, const int32_t *offsets, const int32_t *perm,
+                       int top_k, int latent, int inter, int max_slots, hipStream_t st) {
+    if (xqb)
+        return launch_idot_bf16(true, nullptr, nullptr, hqb, hs, xqb, xs, bank, active, offsets, perm, top_k, latent,
+                                inter, max_slots, st);
     const int items = max_slots * ((inter + 16 * IX_WAVES - 1) / (16 * IX_WAVES));
     const int blocks = items < 16384 ? items : 16384;
-    moe_idot_kernel<true><<<blocks, IX_WAVES * 64, 0, st>>>(h, xq, xs, bank, active, offsets, perm, top_k, latent,
-                                                            inter, max_slots);
+    moe_idot_kernel<true><<<blocks, IX_WAVES * 64, 0, st>>>(nullptr, hq, hs, xq, xs, bank, active, offsets, perm,
+                                                            top_k, latent, inter, max_slots);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
 int launch_moe_down_idot(float *ypair, const int8_t *hq, const uint16_t *hqb, const float *hs, const BankDev &bank,
                          const int32_t *active, const int32_t *offsets, const int32_t *perm, int latent, int inter,
                          int max_slots, hipStream_t st) {
-    if (hqb) return launch_idot_bf16(false, ypair, hqb, hs, bank, active, offsets, perm, 1, inter, latent, max_slots, st);
+    if (hqb)
+        return launch_idot_bf16(false, ypair, nullptr, nullptr, nullptr, hqb, hs, bank, active, offsets, perm, 1, inter,
+                                latent, max_slots, st);
     const int items = max_slots * ((latent + 32 * IX_WAVES - 1) / (32 * IX_WAVES));
     const int blocks = items < 16384 ? items : 16384;
-    moe_idot_kernel<false><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, hq, hs, bank, active, offsets, perm, 1, inter,
-                                                             latent, max_slots);
+    moe_idot_kernel<false><<<blocks, IX_WAVES * 64, 0, st>>>(ypair, nullptr, nullptr, hq, hs, bank, active, offsets,
+                                                             perm, 1, inter, latent, max_slots);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

@@ -92,7 +92,8 @@ constexpr int min_loads(int nt) { return W_LD + tok_instr(nt) / NW + (sx_instr(n
 
 template <bool UP>
 __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
-    float *__restrict__ out, const uint16_t *__restrict__ aqb, const float *__restrict__ as, BankDev bank,
+    float *__restrict__ out, int8_t *__restrict__ hq_out, uint16_t *__restrict__ hqb_out, float *__restrict__ hs_out,
+    const uint16_t *__restrict__ aqb, const float *__restrict__ as, BankDev bank,
     const int32_t *__restrict__ active, const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
     int top_k, int n_in, int n_out, int max_slots, int row_blocks) {
     using namespace ib;
@@ -288,23 +289,59 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
                 }
             }
             // results: lane holds token col of each tile and rows 4*quad + v of each A tile;
-            // n_out is a multiple of 128 and out 16-byte aligned, so a lane's four rows
-            // are one float4 that lies wholly inside or wholly outside the matrix
+            // n_out is a multiple of 128: a wavefront's rows are all inside the matrix or
+            // all past it (the last row block of a width that is an odd multiple of 128)
+            if constexpr (UP) {
+                // h = SiTU(g, u) of the wavefront's 32 rows (one 32-group of h) for each
+                // token, quantised here: the group's maximum over the 8 values of each of
+                // the 4 lanes that hold the token, then q and s of the group
+                const int hrow = rb * (WG_AR / 2) + wl * 32;  // the group's first row
+                const bool rows_in = hrow < n_out;
+                const int ngo = n_out / kGroup;
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int i = 16 * tt + col;
-                float *dst = out + (size_t)(c0 + min(i, n_tok - 1)) * n_out;
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int i = 16 * tt + col;
+                    float hv[2][4];
+                    float amax = 0.f;
 #pragma unroll
-                for (int k = 0; k < (UP ? 2 : 4); ++k) {
-                    const int r0 = UP ? rb * (WG_AR / 2) + wl * 32 + 16 * k + 4 * quad : rb * WG_AR + wl * 64 + 16 * k + 4 * quad;
-                    float4 r4;
-                    if (UP) {
-                        r4 = make_float4(situ(acc[k][tt][0], acc[k + 2][tt][0]), situ(acc[k][tt][1], acc[k + 2][tt][1]),
-                                         situ(acc[k][tt][2], acc[k + 2][tt][2]), situ(acc[k][tt][3], acc[k + 2][tt][3]));
-                    } else {
-                        r4 = make_float4(acc[k][tt][0], acc[k][tt][1], acc[k][tt][2], acc[k][tt][3]);
+                    for (int k = 0; k < 2; ++k)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            hv[k][v] = situ(acc[k][tt][v], acc[k + 2][tt][v]);
+                            amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[k][v]));
+                        }
+                    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+                    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+                    const float sc = idot_group_scale(amax);
+                    if (i < n_tok && rows_in) {
+                        const size_t pos = (size_t)(c0 + i);
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const size_t at = pos * n_out + hrow + 16 * k + 4 * quad;
+                            const int q0 = idot_quant(hv[k][0], sc), q1 = idot_quant(hv[k][1], sc);
+                            const int q2 = idot_quant(hv[k][2], sc), q3 = idot_quant(hv[k][3], sc);
+                            if (hqb_out) {
+                                *(uint2 *)(hqb_out + at) = make_uint2(i8_bf16_bits(q0) | (i8_bf16_bits(q1) << 16),
+                                                                      i8_bf16_bits(q2) | (i8_bf16_bits(q3) << 16));
+                            } else {
+                                *(uint32_t *)(hq_out + at) = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
+                                                             ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)q3 << 24);
+                            }
+                        }
+                        if (quad == 0) hs_out[pos * ngo + hrow / kGroup] = sc;
                     }
-                    if (i < n_tok && r0 < n_out) *(float4 *)(dst + r0) = r4;
+                }
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int i = 16 * tt + col;
+                    float *dst = out + (size_t)(c0 + min(i, n_tok - 1)) * n_out;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int r0 = rb * WG_AR + wl * 64 + 16 * k + 4 * quad;
+                        if (i < n_tok && r0 < n_out)
+                            *(float4 *)(dst + r0) = make_float4(acc[k][tt][0], acc[k][tt][1], acc[k][tt][2], acc[k][tt][3]);
+                    }
                 }
             }
         };
@@ -321,12 +358,13 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
     }
 }
 
-// UP: h[pos][r] = SiTU(w1[r] . x, w3[r] . x) for every pair of every active
-// expert; DOWN: ypair[pos][r] = w2[r] . h[pos]. Operands as the IDOT stages
-// leave them: bf16 copies of the int8 activations and their fp32 group scales.
-int launch_idot_bf16(bool up, float *out, const uint16_t *aqb, const float *as, const BankDev &bank,
-                     const int32_t *active, const int32_t *offsets, const int32_t *perm, int top_k, int n_in,
-                     int n_out, int max_slots, hipStream_t st) {
+// UP: h = SiTU(w1 . x, w3 . x) for every pair of every active expert, written
+// quantised per 32-group (hq int8, or hqb as bf16, and hs [pair][inter/32]);
+// DOWN: ypair[pos][r] = w2[r] . h[pos]. Operands as the IDOT stages leave them:
+// bf16 copies of the int8 activations and their fp32 group scales.
+int launch_idot_bf16(bool up, float *out, int8_t *hq, uint16_t *hqb, float *hs, const uint16_t *aqb, const float *as,
+                     const BankDev &bank, const int32_t *active, const int32_t *offsets, const int32_t *perm,
+                     int top_k, int n_in, int n_out, int max_slots, hipStream_t st) {
     const int per_block = up ? ib::WG_AR / 2 : ib::WG_AR;
     const int row_blocks = (n_out + per_block - 1) / per_block;
     const int64_t items = (int64_t)max_slots * row_blocks;
@@ -334,11 +372,11 @@ int launch_idot_bf16(bool up, float *out, const uint16_t *aqb, const float *as, 
     if (items > (int64_t)1 << 30) return K3G_EUNSUPPORTED;
     const dim3 grid((unsigned)items), block(ib::NW * 64);
     if (up)
-        moe_idot_bf16_kernel<true><<<grid, block, 0, st>>>(out, aqb, as, bank, active, offsets, perm, top_k, n_in,
-                                                           n_out, max_slots, row_blocks);
+        moe_idot_bf16_kernel<true><<<grid, block, 0, st>>>(nullptr, hq, hqb, hs, aqb, as, bank, active, offsets, perm,
+                                                           top_k, n_in, n_out, max_slots, row_blocks);
     else
-        moe_idot_bf16_kernel<false><<<grid, block, 0, st>>>(out, aqb, as, bank, active, offsets, perm, top_k, n_in,
-                                                            n_out, max_slots, row_blocks);
+        moe_idot_bf16_kernel<false><<<grid, block, 0, st>>>(out, nullptr, nullptr, nullptr, aqb, as, bank, active,
+                                                            offsets, perm, top_k, n_in, n_out, max_slots, row_blocks);
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 

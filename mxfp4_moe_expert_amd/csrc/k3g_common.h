@@ -178,6 +178,19 @@ __device__ inline float situ(float g, float u) {
     return 4.0f * tanh_fast(g * 0.25f) * sig * (25.0f * tanh_fast(u * 0.04f));
 }
 
+// ---- IDOT quantisation of one value ("Kimi K3 engine (c/kimi_k3.c)", "Streaming
+// design", K3_IDOT: per-32-group int8 activations) ---------------------------------
+// With s = max|v|/127 of the value's 32-group (fp32, correctly rounded): q =
+// rint(v / s) with the division correctly rounded and ties to even, clamped to
+// +-127; a group whose maximum is 0 has s = 0 and q = 0.
+__device__ inline float idot_group_scale(float amax) { return amax / 127.0f; }
+__device__ inline int idot_quant(float v, float s) {
+    return s == 0.0f ? 0 : (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(v / s), -127.0f), 127.0f);
+}
+// An int8 value as bf16 bits: its fp32 form has at most 8 significant bits, so
+// the top half of the fp32 bits is exact.
+__device__ inline uint32_t i8_bf16_bits(int q) { return __builtin_bit_cast(uint32_t, (float)q) >> 16; }
+
 // ---- one token: its route entries in the bucket's order -------------------------
 // With a single token the bucket (pairs sorted by expert, then token) is a
 // small permutation of the K route entries, which a wavefront can rank on its

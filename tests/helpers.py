@@ -89,3 +89,34 @@ def make_bank(k3g, seed, E, latent, inter, lo=118, hi=132, p255=0.001):
     src = ExpertSource(seed, latent, inter, lo, hi, p255)
     bankt, bank = k3g.pack_bank(src, E, latent, inter)
     return src, bankt, bank
+
+
+def bf16_bits_to_i8(b):
+    """bf16 bit patterns of small integers (the bf16 copy of int8 values) -> int8."""
+    f = (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    assert np.all(f == np.round(f)) and np.all(np.abs(f) <= 127)
+    return f.astype(np.int8)
+
+
+def check_quantised_h(q, s, g, u, ng, nu, what="h"):
+    """IDOT h as the up kernel writes it: quantised per 32-group (q int8 [inter],
+    s fp32 [inter/32]) from its own fp32 SiTU output, which lies within
+    situ_tolerance of SiTU(g, u) of the oracle's products. So q*s must lie within
+    that bound plus half a quantisation step of the oracle's h; each group's
+    largest |q| is 127 (all zero where s = 0); and s is the group's max|h|/127
+    to the same bound."""
+    q = np.asarray(q, np.int8).astype(np.int64)
+    s = np.asarray(s, np.float32).astype(np.float64)
+    ho = situ64(g, u)
+    tol = situ_tolerance(g, u, ng, nu)
+    sg = np.repeat(s, 32)
+    err = np.abs(q * sg - ho)
+    bad = err > tol + 0.5 * sg * (1 + 1e-6) + 1e-30
+    assert not bad.any(), (f"{what}: {bad.sum()} dequantised values off; first {np.flatnonzero(bad)[:5]}: "
+                           f"q*s {(q * sg)[bad][:3]} ref {ho[bad][:3]} tol {tol[bad][:3]} s {sg[bad][:3]}")
+    qg = np.abs(q).reshape(-1, 32)
+    assert np.all(qg.max(1)[s > 0] == 127), f"{what}: a group's largest |q| is not 127"
+    assert np.all(qg[s == 0] == 0) and np.all(s >= 0), f"{what}: a zero scale with nonzero q"
+    amax = np.abs(ho).reshape(-1, 32).max(1)
+    tg = tol.reshape(-1, 32).max(1)
+    assert np.all(np.abs(127 * s - amax) <= tg + 1e-6 * amax + 1e-30), f"{what}: group scales off"

@@ -44,8 +44,16 @@ def test_workspace_layout(k3g):
     L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
     P = 4096 * 16
     regions = {"counts": 896 * 4, "offsets": 897 * 4, "perm": P * 4, "inv": P * 4, "active": 897 * 4,
-               "h": P * 3072 * 4, "ypair": P * 3584 * 4, "xq": 4096 * 3584, "xs": 4096 * 112 * 4,
+               "ypair": P * 3584 * 4, "xq": 4096 * 3584, "xs": 4096 * 112 * 4,
                "hq": P * 3072, "hs": P * 96 * 4}
+    # IDOT keeps h only quantised (hq, or its bf16 copy hqb in the bf16 form): no fp32 h
+    assert L["h"] == 0 and L["hqb"] == 0
+    Lb = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584,
+                                                          inter=3072, mode=k3g.IDOT | k3g.IDOT_BF16))
+    assert Lb["h"] == 0 and Lb["hq"] == 0 and Lb["hqb"] > 0 and Lb["xqb"] > 0
+    Le = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=64, top_k=16, n_experts=896, latent=3584,
+                                                          inter=3072, mode=k3g.EXACT))
+    assert Le["h"] > 0 and Le["hq"] == 0
     spans = sorted((L[n], L[n] + sz) for n, sz in regions.items())
     for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
         assert a1 <= b0, "regions overlap"

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from tests.helpers import assert_norm_close, make_bank, situ_tolerance
+from tests.helpers import assert_norm_close, bf16_bits_to_i8, check_quantised_h, make_bank, situ_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -67,22 +67,23 @@ def check_block_layer_token(ws, L, t, lat_t, idx_t, wts_t, agg_t, src, latent, i
     for k in range(K):
         ex = src(int(idx_t[k]))
         pos = int(inv[k])
-        h = ws_view(ws, L, "h", inter, np.float32, first=pos * inter)
         if idot:
             g, _, ng = oracle.mxfp4_gemv_idot(qo[0], so[0], ex["w1p"], ex["w1s"], full=True)
             u, _, nu = oracle.mxfp4_gemv_idot(qo[0], so[0], ex["w3p"], ex["w3s"], full=True)
+            # IDOT keeps h only quantised: hq (int8 form) or its bf16 copy, and hs
+            if L["hq"]:
+                hq = ws_view(ws, L, "hq", inter, np.int8, first=pos * inter)
+            else:
+                hq = bf16_bits_to_i8(ws_view(ws, L, "hqb", inter, np.uint16, first=pos * inter))
+            hs = ws_view(ws, L, "hs", inter // 32, np.float32, first=pos * (inter // 32))
+            check_quantised_h(hq, hs, g, u, ng, nu, f"block layer h t={t} k={k}")
+            y2, _, n2 = oracle.mxfp4_gemv_idot(hq, hs, ex["w2p"], ex["w2s"], full=True)
         else:
+            h = ws_view(ws, L, "h", inter, np.float32, first=pos * inter)
             g, _, ng = oracle.mxfp4_gemv(lat_t, ex["w1p"], ex["w1s"], full=True)
             u, _, nu = oracle.mxfp4_gemv(lat_t, ex["w3p"], ex["w3s"], full=True)
-        bad = np.abs(h.astype(np.float64) - oracle.situ_vec(g, u)) > situ_tolerance(g, u, ng, nu)
-        assert not bad.any(), f"block layer h t={t} k={k}: {np.flatnonzero(bad)[:5]}"
-        if idot:
-            hq = ws_view(ws, L, "hq", inter, np.int8, first=pos * inter)
-            hs = ws_view(ws, L, "hs", inter // 32, np.float32, first=pos * (inter // 32))
-            qh, sh_ = oracle.quant_i8_groups(h)
-            assert np.array_equal(hq, qh[0]) and np.array_equal(hs, sh_[0])
-            y2, _, n2 = oracle.mxfp4_gemv_idot(qh, sh_, ex["w2p"], ex["w2s"], full=True)
-        else:
+            bad = np.abs(h.astype(np.float64) - oracle.situ_vec(g, u)) > situ_tolerance(g, u, ng, nu)
+            assert not bad.any(), f"block layer h t={t} k={k}: {np.flatnonzero(bad)[:5]}"
             y2, _, n2 = oracle.mxfp4_gemv(h, ex["w2p"], ex["w2s"], full=True)
         yp = ws_view(ws, L, "ypair", latent, np.float32, first=pos * latent)
         assert_norm_close(yp, y2, n2, what=f"block layer down t={t} k={k}")

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.helpers import assert_norm_close, make_bank, situ_tolerance
+from tests.helpers import assert_norm_close, bf16_bits_to_i8, check_quantised_h, make_bank
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,16 @@ def test_groupsums_bit_exact(k3g, T, rows, n_in):
     assert np.array_equal(host(sums), oracle.idot_groupsums(q, pk))
 
 
+def quantised_h(ws, L, row, inter):
+    """Pair row `row` of the quantised h the up kernel wrote: (q int8, s fp32),
+    from hq (int8 form) or its bf16 copy hqb (bf16 form)."""
+    if L["hq"]:
+        q = ws_view_rows(ws, L, "hq", row, inter, np.int8)
+    else:
+        q = bf16_bits_to_i8(ws_view_rows(ws, L, "hqb", row, inter, np.uint16))
+    return q, ws_view_rows(ws, L, "hs", row, inter // 32, np.float32)
+
+
 def check_expert_idot(k3g, ex, x, latent, inter, form=0):
     mode = k3g.IDOT | form
     exd = {k: dev(v) for k, v in ex.items()}
@@ -83,6 +93,7 @@ def check_expert_idot(k3g, ex, x, latent, inter, form=0):
     sh = k3g.shape(latent=latent, inter=inter, mode=mode)
     ws = k3g.workspace(k3g.OP_EXPERT_GLU, sh)
     L = k3g.workspace_layout(k3g.OP_EXPERT_GLU, sh)
+    assert not L["h"]  # IDOT keeps h only quantised
     k3g.k3g_expert_glu(y, dev(x), exd, mode, ws)
     yg = host(y)
     xq = ws_view(ws, L, "xq", latent, np.int8)
@@ -91,14 +102,8 @@ def check_expert_idot(k3g, ex, x, latent, inter, form=0):
     assert np.array_equal(xq, qo[0]) and np.array_equal(xs, so[0])
     g, _, ng = oracle.mxfp4_gemv_idot(qo, so, ex["w1p"], ex["w1s"], full=True)
     u, _, nu = oracle.mxfp4_gemv_idot(qo, so, ex["w3p"], ex["w3s"], full=True)
-    hg = ws_view(ws, L, "h", inter, np.float32)
-    ho = oracle.situ_vec(g, u)
-    bad = np.abs(hg.astype(np.float64) - ho) > situ_tolerance(g, u, ng, nu)
-    assert not bad.any(), f"h: {bad.sum()} outside the bound, first {np.flatnonzero(bad)[:5]}"
-    hq = ws_view(ws, L, "hq", inter, np.int8)
-    hs = ws_view(ws, L, "hs", inter // 32, np.float32)
-    qh, sh_ = oracle.quant_i8_groups(hg)
-    assert np.array_equal(hq, qh[0]) and np.array_equal(hs, sh_[0])
+    qh, sh_ = quantised_h(ws, L, 0, inter)
+    check_quantised_h(qh, sh_, g, u, ng, nu, "idot glu h")
     y2, _, n2 = oracle.mxfp4_gemv_idot(qh, sh_, ex["w2p"], ex["w2s"], full=True)
     assert_norm_close(yg, y2, n2, what="idot glu down")
     return yg
@@ -171,13 +176,8 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens, experts=()):
             pos = int(inv[p])
             g, _, ng = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w1p"], ex["w1s"], full=True)
             u, _, nu = oracle.mxfp4_gemv_idot(qo[t], so[t], ex["w3p"], ex["w3s"], full=True)
-            hg = ws_view_rows(ws, L, "h", pos, inter, np.float32)
-            bad = np.abs(hg.astype(np.float64) - oracle.situ_vec(g, u)) > situ_tolerance(g, u, ng, nu)
-            assert not bad.any(), (t, k, np.flatnonzero(bad)[:5])
-            hq = ws_view_rows(ws, L, "hq", pos, inter, np.int8)
-            hs = ws_view_rows(ws, L, "hs", pos, inter // 32, np.float32)
-            qh, sh_ = oracle.quant_i8_groups(hg)
-            assert np.array_equal(hq, qh[0]) and np.array_equal(hs, sh_[0])
+            qh, sh_ = quantised_h(ws, L, pos, inter)
+            check_quantised_h(qh, sh_, g, u, ng, nu, f"idot h t={t} k={k}")
             y2, _, n2 = oracle.mxfp4_gemv_idot(qh, sh_, ex["w2p"], ex["w2s"], full=True)
             yp = ws_view_rows(ws, L, "ypair", pos, latent, np.float32)
             assert_norm_close(yp, y2, n2, what=f"idot down t={t} k={k}")
@@ -196,7 +196,9 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens, experts=()):
         assert_norm_close(yg[t0:t1], acc, nrm, what=f"idot combine tokens {t0}..{t1 - 1}")
     # the bf16 form computes the same numbers bit for bit (over the pairs that exist)
     yb, wsb, Lb = run_layer_idot(k3g, bank, x, idx, wts, 0x200)
-    for name, width, dt in (("h", inter, np.float32), ("hq", inter, np.int8), ("ypair", latent, np.float32)):
+    assert np.array_equal(ws_view(ws, L, "hq", Pv * inter, np.int8),
+                          bf16_bits_to_i8(ws_view(wsb, Lb, "hqb", Pv * inter, np.uint16))), "bf16 form differs in hq"
+    for name, width, dt in (("hs", inter // 32, np.float32), ("ypair", latent, np.float32)):
         a = ws_view(ws, L, name, Pv * width, dt)
         b = ws_view(wsb, Lb, name, Pv * width, dt)
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"bf16 form differs in {name}"
