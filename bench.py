@@ -24,8 +24,9 @@ The default run (decode_b1) also measures, on the same resident bank:
   expert_b1           one expert on one token and the one-matrix product;
   achievable          the sustained matrix-core rates and streaming-read rate
                       (the roofline's achievable denominators);
-  block_256[_fp4_mfma] the full LatentMoE block at 256 tokens, with either
-                      layer form;
+  block_256[_vector]  the full LatentMoE block at 256 tokens, with the
+                      library's default layer form (FP4 matrix cores) and the
+                      vector form;
   scale_format        the same product with f32 per-group scales;
   streaming_tier      decode steps with the bank in host memory and an LRU of
                       expert slots in HBM.
@@ -125,7 +126,7 @@ def main():
         print(json.dumps({"expert_b1": run_expert(ctx, bankt)}), flush=True)
         return
     if args.block_only:
-        print(json.dumps({"block_256": run_block(ctx, bank, mfma_decode=args.mfma_decode)}), flush=True)
+        print(json.dumps({"block_256": run_block(ctx, bank, form="mfma" if args.mfma_decode else None)}), flush=True)
         return
     result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16, args.mfma_decode)
     if not args.no_cpu_baseline:
@@ -161,8 +162,8 @@ def main():
         result["roofline"]["achievable_at_launch_size"] = ach_l
         result["roofline"]["frac_of_achievable_at_launch_size"] = round(result["roofline"]["achieved"] / ach_l, 4)
         # the full LatentMoE block at 256 tokens, the routed layer in both forms
-        result["block_256"] = run_block(ctx, bank)
-        result["block_256_fp4_mfma"] = run_block(ctx, bank, mfma_decode=True)
+        result["block_256"] = run_block(ctx, bank)  # the library's default form (FP4 matrix-core layer)
+        result["block_256_vector"] = run_block(ctx, bank, form="vector")
         # the Vulkan-tier scale format: the same product with f32 per-group scales
         result["scale_format"] = run_scale_format(ctx)
         # the expert streaming tier: the bank in pinned host memory, an LRU of slots in HBM
@@ -179,8 +180,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     wl_seed, T, bias_range, mode_name = synth.WORKLOADS[workload]
     mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
     form = k3g.IDOT_BF16 if (mode == k3g.IDOT and idot_bf16) else 0
-    if mode == k3g.EXACT and mfma_decode:
-        form = k3g.DECODE_MFMA
+    if mode == k3g.EXACT:  # the form is named explicitly (the library's default for T > 1 is the FP4 one)
+        form = k3g.DECODE_MFMA if mfma_decode else k3g.DECODE_VECTOR
 
     W, b = synth.router(wl_seed, E, L, bias_range)
     Wd = torch.from_numpy(W).to(dev)
@@ -313,7 +314,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     lut_ms, alt_ms = {}, {}
     if mode == k3g.EXACT and T == 1:
         lut_ms = {name: time_stage(st, mode | k3g.DECODE_LUT) for name, st in stages if name in ("up", "down")}
-        alt = mode if f4 else mode | k3g.DECODE_MFMA
+        alt = mode | k3g.DECODE_VECTOR if f4 else mode | k3g.DECODE_MFMA
         alt_ms = {name: time_stage(st, alt) for name, st in
                   [("quant_x", k3g.STAGE_QUANT_X), ("up", k3g.STAGE_UP), ("down", k3g.STAGE_DOWN)]
                   if f4 is False or name != "quant_x"}
@@ -396,7 +397,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
             "workload": workload,
             "tokens_per_step": T,
             "experts": E, "top_k": K, "latent": L, "inter": I,
-            "mode": mode_name + ("+bf16-mfma" if form == k3g.IDOT_BF16 else "+fp4-mfma" if form else ""),
+            "mode": mode_name + ("+bf16-mfma" if form == k3g.IDOT_BF16 else "+fp4-mfma" if f4 else ""),
             "distinct_experts_per_step": n_exp,
             "top_p": top_p,
             "algorithmic_bytes_per_step": int(alg_bytes),
@@ -444,14 +445,15 @@ def measured_traffic(workload, kernel, form=""):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
-def run_block(ctx, bank, reps=10, mfma_decode=False):
+def run_block(ctx, bank, reps=10, form=None):
     """The full LatentMoE block on 256 tokens (route on the 7168-wide hidden
     state, bf16 down-projection, the routed layer on the resident bank, RMSNorm,
     bf16 up-projection, two bf16 shared SiTU-GLU experts of 6144): HIP events
     around `reps` calls, and the dense parts' matrix work as a rate."""
     torch, k3g, synth, dev = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"]
     seed, T, bias_range, _ = synth.WORKLOADS["block_256"]
-    mode = k3g.EXACT | (k3g.DECODE_MFMA if mfma_decode else 0)
+    # form None: the library's default (the FP4 matrix-core layer at 256 tokens)
+    mode = k3g.EXACT | {None: 0, "vector": k3g.DECODE_VECTOR, "mfma": k3g.DECODE_MFMA}[form]
     H, Lt, SI, E, K = synth.HIDDEN, synth.LATENT, synth.SHARED_INTER, synth.N_EXPERTS, synth.TOP_K
     dense = {k: torch.from_numpy(v).to(dev) for k, v in synth.block_dense(seed).items()}
     W, b = synth.router(seed, E, H, bias_range)
@@ -475,7 +477,7 @@ def run_block(ctx, bank, reps=10, mfma_decode=False):
     ms = e0.elapsed_time(e1) / reps
     # dense matrix work: down, up, and per shared expert w1, w3 and w2 (2 flops per product)
     flops = 2.0 * T * (2 * H * Lt + 2 * 3 * H * SI)
-    out_d = {"tokens": T, "layer": "fp4-mfma" if mfma_decode else "vector",
+    out_d = {"tokens": T, "layer": "vector" if form == "vector" else "fp4-mfma",
              "ms_per_block": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
              "dense_flops": flops, "dense_TFLOPs_if_all_time": round(flops / (ms * 1e-3) / 1e12, 1)}
     del dense, ws, out, x

@@ -80,6 +80,14 @@ typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
  * to the int8 form bit for bit; the workspace gains bf16 copies of xq and hq. */
 #define K3G_IDOT_BF16 0x200
 
+/* Which kernels an EXACT layer runs on. With neither flag: the FP4 matrix
+ * cores (below) for more than one token when the shape and the bank fit them,
+ * the vector kernels otherwise (one token: the vector form is as fast and
+ * needs no split of x). K3G_DECODE_MFMA asks for the matrix cores at any
+ * token count, K3G_DECODE_VECTOR (or K3G_DECODE_LUT) for the vector kernels;
+ * the two together are K3G_EINVAL. */
+#define K3G_DECODE_VECTOR 0x800
+
 /* OR-ed into K3G_EXACT: run the layer on the FP4 matrix cores instead of the
  * vector kernels. The products use v_mfma_scale_f32_16x16x128_f8f6f4 on the
  * stored nibbles and scales, with x and h written as sums of 16 e2m1 vectors

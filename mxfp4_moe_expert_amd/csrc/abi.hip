@@ -109,18 +109,24 @@ struct Carver {
     }
 };
 
-inline int base_mode(int mode) { return mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_DECODE_MFMA); }
+constexpr int kFormFlags = K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_DECODE_MFMA | K3G_DECODE_VECTOR;
+inline int base_mode(int mode) { return mode & ~kFormFlags; }
 inline bool mode_ok(int mode) {
-    if (mode & ~(K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_DECODE_MFMA | 0xFF)) return false;
+    if (mode & ~(kFormFlags | 0xFF)) return false;
     if ((mode & K3G_IDOT_BF16) && base_mode(mode) != K3G_IDOT) return false;
-    if ((mode & (K3G_DECODE_LUT | K3G_DECODE_MFMA)) && base_mode(mode) != K3G_EXACT) return false;
+    if ((mode & (K3G_DECODE_LUT | K3G_DECODE_MFMA | K3G_DECODE_VECTOR)) && base_mode(mode) != K3G_EXACT) return false;
+    if ((mode & K3G_DECODE_MFMA) && (mode & (K3G_DECODE_LUT | K3G_DECODE_VECTOR))) return false;
     return base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT;
 }
 inline bool lut_of(int mode) { return (mode & K3G_DECODE_LUT) != 0; }
-// EXACT mode with K3G_DECODE_MFMA runs on the FP4 matrix cores when the shape
-// fits them (the bank's alignment is checked where the bank is known).
+// EXACT layers run on the FP4 matrix cores when the shape fits them (the
+// bank's alignment is checked where the bank is known): always with
+// K3G_DECODE_MFMA, by default with more than one token (the faster form
+// there), never with K3G_DECODE_VECTOR or K3G_DECODE_LUT (the vector kernels).
 inline bool f4_layer(int mode, int n_tokens, int latent, int inter) {
-    return n_tokens >= 1 && mode == (K3G_EXACT | K3G_DECODE_MFMA) && f4_shape_ok(latent, inter);
+    if (base_mode(mode) != K3G_EXACT || n_tokens < 1 || !f4_shape_ok(latent, inter)) return false;
+    if (mode & (K3G_DECODE_VECTOR | K3G_DECODE_LUT)) return false;
+    return (mode & K3G_DECODE_MFMA) || n_tokens > 1;
 }
 // The block's dense products on the bf16 matrix cores (x as three exact bf16
 // pieces): the down-projection and the shared GLUs read the pieces of the

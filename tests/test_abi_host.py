@@ -136,8 +136,23 @@ def test_fp4_layer_workspace(k3g, T):
         assert room["passes"] >= 4 * (1 + 2 * (-(-P // npp) + min(P, E)))
     # the vector form has none of these regions
     L0 = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=lat,
-                                                          inter=inter, mode=k3g.EXACT))
+                                                          inter=inter, mode=k3g.EXACT | k3g.DECODE_VECTOR))
     assert L0["xp"] == L0["hp"] == L0["passes"] == 0
+    # no form flag: the FP4 form for more than one token, the vector form for one
+    Ld = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=lat,
+                                                          inter=inter, mode=k3g.EXACT))
+    assert Ld == (L0 if T == 1 else L)
+
+
+def test_form_flags_exclude_each_other(k3g):
+    sh = lambda m: k3g.shape(n_tokens=4, top_k=2, n_experts=8, latent=512, inter=512, mode=m)  # noqa: E731
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.DECODE_MFMA | k3g.DECODE_VECTOR)) == 0
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.DECODE_MFMA | k3g.DECODE_LUT)) == 0
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.IDOT | k3g.DECODE_VECTOR)) == 0
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.DECODE_VECTOR)) > 0
+    # widths off the matrix cores' multiples of 512: the vector kernels whatever the flags say
+    sh2 = k3g.shape(n_tokens=4, top_k=2, n_experts=8, latent=256, inter=512, mode=k3g.EXACT)
+    assert k3g.workspace_layout(k3g.OP_MOE_LAYER, sh2)["xp"] == 0
 
 
 @pytest.mark.parametrize("H,lat,SI,mfma", [(7168, 3584, 6144, True), (256, 128, 64, True),

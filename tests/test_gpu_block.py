@@ -202,7 +202,7 @@ def test_block_f4mma_layer(k3g, T, K, npp):
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
-@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+@pytest.mark.parametrize("decode", [0x800, 0], ids=["vector", "default_f4mma"])
 def test_block_full_size_sampled(k3g, full_bank, decode):
     src, bankt, bank = full_bank
     seed = synth.SEED_BASE + 4

@@ -299,11 +299,11 @@ def test_layer_small_ragged(k3g, decode):
     assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
-@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+@pytest.mark.parametrize("decode", [0x800, 0x400], ids=["vector", "f4mma"])
 def test_layer_repeated_ids(k3g, decode):
     # tokens that name one expert twice or three times, in both 64-token chunks
     # of the bucket: every pair gets its own sorted slot, (expert, token, k) order
-    E, latent, inter, T, K = 10, 256, 256, 70, 3
+    E, latent, inter, T, K = 10, 512, 512, 70, 3
     src, bankt, bank = make_bank(k3g, 52, E, latent, inter, 120, 123, 0.01)
     x = synth.activations(52, T, latent)
     W, b = synth.router(52, E, latent, 0.2)
@@ -604,13 +604,16 @@ def test_layer_small_topp(k3g):
     assert np.allclose(y, yo, rtol=1e-3, atol=1e-3 * np.abs(yo).max())
 
 
-@pytest.mark.parametrize("decode", [0, 0x400], ids=["cvt", "f4mma"])
+@pytest.mark.parametrize("decode", [0x800, 0], ids=["vector", "default_f4mma"])
 def test_layer_decode_b64_full_sampled(k3g, full_bank, decode):
     src, bankt, bank = full_bank
     seed = synth.SEED_BASE + 2
     W, b = synth.router(seed, 896, 3584, 0.01)
     x = synth.activations(seed, 64, 3584)
     io, wo, _ = oracle.route(x, W, b, 16)
+    # with no form flag, more than one token runs on the FP4 matrix cores (x split into pieces)
+    sh = k3g.shape(n_tokens=64, top_k=16, n_experts=896, latent=3584, inter=3072, mode=k3g.EXACT | decode)
+    assert bool(k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)["xp"]) == (decode == 0)
     # every token, pair by pair (all 1,024 pairs), each stage on the GPU's own input
     print(f"decode_b64 form {decode:#x}: checking 1024 pairs on the oracle", flush=True)
     check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=range(64), decode=decode)
