@@ -64,7 +64,10 @@ def parse():
                     help="IDOT workloads: run the group dots on the bf16 matrix cores (same results)")
     ap.add_argument("--mfma-decode", action="store_true",
                     help="EXACT workloads and the block: the expert products on the FP4 matrix cores (x and h as "
-                         "e2m1 pieces) instead of the vector kernels (same bound)")
+                         "e2m1 pieces) whatever the token count")
+    ap.add_argument("--vector-decode", action="store_true",
+                    help="EXACT workloads and the block: the vector kernels whatever the token count (without "
+                         "either flag: the library's default, vector for one token, FP4 matrix cores for more)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="decode_b1 only: skip the short runs of the 64-token and 4096-token workloads")
@@ -81,6 +84,9 @@ def parse():
                     help="only copy a GIB-sized buffer 5 times (a plain copy of known size, for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--bank-experts", type=int, default=0,
+                    help="diagnostic: a bank (and router) of this many experts instead of 896, to compare a "
+                         "kernel's rate on a smaller allocation (not a configuration of the method)")
     return ap.parse_args()
 
 
@@ -111,14 +117,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    L, I, E = synth.LATENT, synth.INTER, synth.N_EXPERTS
+    L, I, E = synth.LATENT, synth.INTER, (args.bank_experts or synth.N_EXPERTS)
     seed_bank = synth.SEED_BASE + 1
     t0 = time.time()
     src = lambda e: synth.expert(seed_bank, e)  # noqa: E731
     bankt, bank = k3g.pack_bank(src, E, L, I)
     print(f"# setup {time.time() - t0:.1f}s: bank {bankt.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
 
-    ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager)
+    ctx = dict(torch=torch, k3g=k3g, synth=synth, dev=dev, bank=bank, seed_bank=seed_bank, eager=args.eager,
+               n_experts=E)
+    form_arg = "mfma" if args.mfma_decode else "vector" if args.vector_decode else None
     if args.achievable_only:
         print(json.dumps({"achievable": run_achievable(ctx)}), flush=True)
         return
@@ -126,22 +134,22 @@ def main():
         print(json.dumps({"expert_b1": run_expert(ctx, bankt)}), flush=True)
         return
     if args.block_only:
-        print(json.dumps({"block_256": run_block(ctx, bank, form="mfma" if args.mfma_decode else None)}), flush=True)
+        print(json.dumps({"block_256": run_block(ctx, bank, form=form_arg)}), flush=True)
         return
-    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16, args.mfma_decode)
+    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16, form_arg)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, src, *host)
     if args.workload == "decode_b1" and not args.no_secondary:
         # the other configurations on the same resident bank, shorter runs (not the headline)
         others = []
         cpu_lines = {}
-        for wl, steps, warm, bf16, p, f4 in (("decode_b1", 100, 10, False, 0.9, False),
-                                             ("decode_b64", 20, 3, False, 0.0, False),
-                                             ("decode_b64", 20, 3, False, 0.0, True),
-                                             ("prefill_4096_idot", 10, 2, False, 0.0, False),
-                                             ("prefill_4096_idot", 10, 2, True, 0.0, False),
-                                             ("prefill_4096_exact", 5, 1, False, 0.0, True)):
-            r, h = run_workload(ctx, wl, steps, warm, bf16, mfma_decode=f4, top_p=p)
+        for wl, steps, warm, bf16, p, fm in (("decode_b1", 100, 10, False, 0.9, None),
+                                             ("decode_b64", 20, 3, False, 0.0, None),
+                                             ("decode_b64", 20, 3, False, 0.0, "vector"),
+                                             ("prefill_4096_idot", 10, 2, False, 0.0, None),
+                                             ("prefill_4096_idot", 10, 2, True, 0.0, None),
+                                             ("prefill_4096_exact", 5, 1, False, 0.0, None)):
+            r, h = run_workload(ctx, wl, steps, warm, bf16, form_name=fm, top_p=p)
             rec = {k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "step_us",
                                      "stage_us", "decode", "roofline", "steps", "warmup")}
             if not args.no_cpu_baseline and wl != "decode_b1":
@@ -172,16 +180,16 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top_p=0.0):
+def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=0.0):
     """Measure one workload on the resident bank. Returns the result record and
     what the CPU baseline needs (the same inputs)."""
     torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
-    L, I, E, K = synth.LATENT, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    L, I, E, K = synth.LATENT, synth.INTER, ctx["n_experts"], synth.TOP_K
     wl_seed, T, bias_range, mode_name = synth.WORKLOADS[workload]
     mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
     form = k3g.IDOT_BF16 if (mode == k3g.IDOT and idot_bf16) else 0
-    if mode == k3g.EXACT:  # the form is named explicitly (the library's default for T > 1 is the FP4 one)
-        form = k3g.DECODE_MFMA if mfma_decode else k3g.DECODE_VECTOR
+    if mode == k3g.EXACT:  # None: the library's default (vector for one token, FP4 matrix cores for more)
+        form = {None: 0, "vector": k3g.DECODE_VECTOR, "mfma": k3g.DECODE_MFMA}[form_name]
 
     W, b = synth.router(wl_seed, E, L, bias_range)
     Wd = torch.from_numpy(W).to(dev)
@@ -199,8 +207,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     sh = k3g.shape(n_tokens=T, top_k=K, n_experts=E, latent=L, inter=I, mode=mode | form)
     ws = [k3g.workspace(k3g.OP_MOE_LAYER, sh) for _ in range(n_rot)]
 
-    # one token in EXACT mode on the FP4 matrix cores: QUANT_X splits x into pieces
-    f4 = form == k3g.DECODE_MFMA
+    # the FP4 matrix-core form (QUANT_X splits x into pieces): asked for, or the default here
+    f4 = bool(k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)["xp"])
     stages = [("route", None), ("bucket", k3g.STAGE_BUCKET)]
     if mode == k3g.IDOT or f4:
         stages.append(("quant_x", k3g.STAGE_QUANT_X))
@@ -210,6 +218,9 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
     stages += [("down", k3g.STAGE_DOWN), ("combine", k3g.STAGE_COMBINE)]
 
     ws_by_mode = {mode | form: ws}
+    if f4 and form == 0:  # name the form the default took, so the per-stage calls below see the same one
+        form = k3g.DECODE_MFMA
+        ws_by_mode = {mode | form: ws}
 
     def stage(r, st, m=mode | form):
         if st is None:
@@ -340,7 +351,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, mfma_decode=False, top
         up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * (2 if form else 1) + P * (I // 32) * 4
 
     # the tag of this form in the names of the committed counter summaries
-    form_tag = "fp4_mfma" if f4 else "bf16" if form == k3g.IDOT_BF16 else ""
+    form_tag = ("fp4_mfma" if f4 else "bf16" if form == k3g.IDOT_BF16 else
+                "vector" if (mode == k3g.EXACT and T > 1) else "")
     gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     tok_s = T / (ms_per_step * 1e-3)
     up_gbs = up_alg / (stage_ms["up"] * 1e-3) / 1e9
