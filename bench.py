@@ -24,6 +24,8 @@ The default run (decode_b1) also measures, on the same resident bank:
   expert_b1           one expert on one token and the one-matrix product;
   achievable          the sustained matrix-core rates and streaming-read rate
                       (the roofline's achievable denominators);
+  launch_costs        a launch, a dependent second launch and an in-launch
+                      handoff between workgroups (the bound on one expert);
   block_256[_vector]  the full LatentMoE block at 256 tokens, with the
                       library's default layer form (FP4 matrix cores) and the
                       vector form;
@@ -169,6 +171,8 @@ def main():
         ach_l = result["achievable"]["hbm_read_at_launch_size"]["GBps"]
         result["roofline"]["achievable_at_launch_size"] = ach_l
         result["roofline"]["frac_of_achievable_at_launch_size"] = round(result["roofline"]["achieved"] / ach_l, 4)
+        # what a launch and a handoff between workgroups cost (the bound on one expert)
+        result["launch_costs"] = run_launch_costs(ctx)
         # the full LatentMoE block at 256 tokens, the routed layer in both forms
         result["block_256"] = run_block(ctx, bank)  # the library's default form (FP4 matrix-core layer)
         result["block_256_vector"] = run_block(ctx, bank, form="vector")
@@ -623,6 +627,43 @@ def run_achievable(ctx, reps=3, launch_bytes=None):
                                           "GBps": round(size / t / 1e9, 1)}
     del buf
     torch.cuda.empty_cache()
+    return out
+
+
+def run_launch_costs(ctx, launches=64, reps=5):
+    """Per launch, back to back in a HIP graph of `launches` calls (HIP events
+    around `reps` replays): a grid of n one-wavefront workgroups that each store
+    one value (mode 0), the same followed by a dependent one-workgroup launch
+    that sums them (mode 1), and the sum done in the same launch by the
+    workgroup that counts last on a device counter after an agent-scope release
+    by every workgroup (mode 2). Results are checked against the exact sum."""
+    torch, k3g, dev = ctx["torch"], ctx["k3g"], ctx["dev"]
+    stream = torch.cuda.current_stream()
+    out = {"timing": f"HIP events around {reps} replays of a graph of {launches} calls"}
+    for n in (64, 256, 896):
+        buf = torch.zeros(n + 1, dtype=torch.float32, device=dev)
+        cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+        want = 0.5 * n * (n - 1) / 2
+        rec = {}
+        for mode, name in ((0, "one_launch_us"), (1, "two_dependent_launches_us"), (2, "one_launch_last_arriver_us")):
+            k3g.k3g_probe_handoff(mode, buf, cnt)
+            torch.cuda.synchronize()
+            if mode:
+                assert abs(float(buf[n]) - want) <= 1e-6 * want + 1e-6, (mode, n, float(buf[n]), want)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(launches):
+                    k3g.k3g_probe_handoff(mode, buf, cnt)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rec[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * launches), 2)
+        out[f"workgroups_{n}"] = rec
     return out
 
 

@@ -451,6 +451,17 @@ int k3g_mxfp4_idot_groupsums(int32_t *sums, const int8_t *q, const uint8_t *pack
 int k3g_probe_mfma_rate(int kind, int iters, uint32_t *sink, void *stream);
 int k3g_probe_read_rate(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
+/* k3g_probe_handoff: the cost of handing data from every workgroup of a launch
+ * to one consumer. n_wg workgroups of 64 threads each store one float to
+ * buf[i]; mode 0: nothing more (a launch of that grid); mode 1: a second,
+ * dependent launch of one workgroup sums buf[0..n_wg) into buf[n_wg]; mode 2:
+ * in the same launch, each workgroup releases at agent scope and adds one to
+ * *counter, and the workgroup that adds last acquires, sums into buf[n_wg] and
+ * sets *counter back to zero. buf float [n_wg + 1]; counter a device uint32
+ * that is zero before the first mode-2 call (each call leaves it at zero).
+ * 1 <= n_wg <= 65536; K3G_EINVAL otherwise. */
+int k3g_probe_handoff(int mode, int n_wg, float *buf, uint32_t *counter, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,6 +120,7 @@ def lib():
         L.k3g_mxfp4_idot_groupsums.argtypes = [P, P, P, i, i, i, P]
         L.k3g_probe_mfma_rate.argtypes = [i, i, P, P]
         L.k3g_probe_read_rate.argtypes = [P, sz, P, P]
+        L.k3g_probe_handoff.argtypes = [i, i, P, P, P]
         _lib = L
     return _lib
 
@@ -433,6 +434,15 @@ def k3g_probe_read_rate(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> N
         raise ValueError("buf must be a contiguous device tensor")
     _check("k3g_probe_read_rate", lib().k3g_probe_read_rate(_ptr(buf), buf.numel() * buf.element_size(),
                                                             _ptr(sink), _stream(stream)))
+
+
+def k3g_probe_handoff(mode: int, buf: torch.Tensor, counter: torch.Tensor, stream=None) -> None:
+    """Measurement hook: a handoff from every workgroup of a launch to one consumer
+    (buf float [n_wg + 1]; counter int32 [1], zero before the first mode-2 call)."""
+    _dev(buf, torch.float32, "buf")
+    _dev(counter, torch.int32, "counter")
+    _check("k3g_probe_handoff", lib().k3g_probe_handoff(mode, buf.numel() - 1, _ptr(buf), _ptr(counter),
+                                                        _stream(stream)))
 
 
 def pack_bank(experts, n_experts: int, latent: int, inter: int, device="cuda", threads: int = 16):

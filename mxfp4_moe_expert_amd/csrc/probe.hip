@@ -14,6 +14,11 @@
 // fastest, so it stands for what a streaming kernel can reach.
 // Both store to `sink` only when a result takes one particular value, so
 // the compiler must keep the work (the store itself is rare and harmless).
+// k3g_probe_handoff: what handing data from every workgroup of a launch to
+// one consumer costs, by the two ways a kernel can do it: a second,
+// dependent launch, or inside the launch with an agent-scope release by each
+// workgroup, a device counter, and an acquire by the workgroup that counts
+// last (the pattern a one-launch expert or a fused route would need).
 #include "k3g_common.h"
 #include "k3g.h"
 
@@ -109,7 +114,59 @@ __global__ __launch_bounds__(kProbeThreads) void read_rate_kernel(const uint4 *_
 
 using namespace k3g;
 
+namespace k3g {
+
+// Each workgroup stores one value; with MODE 2 it then releases (agent scope)
+// and counts itself, and the workgroup that counts last acquires, sums every
+// value into buf[n] and sets the counter back to zero.
+template <int MODE>
+__global__ __launch_bounds__(64) void handoff_produce_kernel(float *buf, uint32_t *counter, int n) {
+    const int lane = threadIdx.x;
+    if (lane == 0) buf[blockIdx.x] = (float)blockIdx.x * 0.5f;
+    if constexpr (MODE == 2) {
+        __shared__ int last;
+        if (lane == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (uint32_t)n - 1;
+        }
+        __syncthreads();
+        if (!last) return;
+        if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        float sum = 0.f;
+        for (int i = lane; i < n; i += kWave) sum += buf[i];
+        sum = wave_sum(sum);
+        if (lane == 0) buf[n] = sum;
+    }
+}
+
+// The dependent second launch: one workgroup sums the n values.
+__global__ __launch_bounds__(64) void handoff_consume_kernel(float *buf, int n) {
+    float sum = 0.f;
+    for (int i = threadIdx.x; i < n; i += kWave) sum += buf[i];
+    sum = wave_sum(sum);
+    if (threadIdx.x == 0) buf[n] = sum;
+}
+
+}  // namespace k3g
+
 extern "C" {
+
+int k3g_probe_handoff(int mode, int n_wg, float *buf, uint32_t *counter, void *stream) {
+    using namespace k3g;
+    if (mode < 0 || mode > 2 || n_wg < 1 || n_wg > 65536 || !buf || (mode == 2 && !counter)) return K3G_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    switch (mode) {
+        case 0: handoff_produce_kernel<0><<<n_wg, 64, 0, st>>>(buf, counter, n_wg); break;
+        case 1:
+            handoff_produce_kernel<0><<<n_wg, 64, 0, st>>>(buf, counter, n_wg);
+            handoff_consume_kernel<<<1, 64, 0, st>>>(buf, n_wg);
+            break;
+        default: handoff_produce_kernel<2><<<n_wg, 64, 0, st>>>(buf, counter, n_wg); break;
+    }
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
 
 int k3g_probe_mfma_rate(int kind, int iters, uint32_t *sink, void *stream) {
     if (!sink || kind < 0 || kind > 3 || iters < 1) return K3G_EINVAL;

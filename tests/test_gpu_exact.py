@@ -190,7 +190,9 @@ def test_expert_glu_small_ragged(k3g):
                                              (300, 3584, 896, 16, 0.01), (5, 128, 1000, 16, 0.05),
                                              (2, 96, 1024, 16, 0.05), (4, 64, 130, 16, 0.05),
                                              (20, 200, 40, 5, 0.3), (9, 130, 70, 8, 0.2),
-                                             (600, 256, 896, 16, 0.01)])
+                                             (600, 256, 896, 16, 0.01), (1, 7168, 896, 16, 0.1),
+                                             (1, 200, 40, 5, 0.3), (1, 96, 1024, 16, 0.05),
+                                             (1, 256, 1000, 20, 0.05), (1, 130, 70, 8, 0.2)])
 def test_route_matches_oracle(k3g, T, n_in, E, K, bias):
     print(f"route T={T} in={n_in} E={E} K={K}", flush=True)
     seed = 3000 + T
@@ -209,6 +211,40 @@ def test_route_matches_oracle(k3g, T, n_in, E, K, bias):
     assert np.all(np.abs(lg - lo) <= 1e-14 * nl)
     assert np.array_equal(host(idx), io)
     assert np.allclose(host(wts), wo, rtol=1e-6, atol=0)
+
+
+def test_route_one_token_repeated_and_in_a_graph(k3g):
+    # one token's routing: calls back to back on changing tokens, then the same
+    # calls captured in a graph and replayed several times, with eager work
+    # between the replays, every result against the oracle
+    E, n_in, K = 896, 3584, 16
+    W, b = synth.router(3101, E, n_in, 0.1)
+    xs = synth.activations(3101, 12, n_in)
+    Wd, bd = dev(W), dev(b)
+    ws = k3g.workspace(k3g.OP_MOE_ROUTE, k3g.shape(n_tokens=1, n_experts=E))
+    want = [oracle.route(xs[i:i + 1], W, b, K)[:2] for i in range(12)]
+    xd = [dev(xs[i:i + 1]) for i in range(12)]
+    idx = [torch.empty((1, K), dtype=torch.int32, device="cuda") for _ in range(12)]
+    wts = [torch.empty((1, K), dtype=torch.float32, device="cuda") for _ in range(12)]
+    for i in range(12):
+        k3g.k3g_moe_route(idx[i], wts[i], xd[i], Wd, bd, K, ws)
+    for i in range(12):
+        assert np.array_equal(host(idx[i]), want[i][0]) and np.allclose(host(wts[i]), want[i][1], rtol=1e-6, atol=0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(12):
+            k3g.k3g_moe_route(idx[i], wts[i], xd[i], Wd, bd, K, ws)
+    for rep in range(4):
+        for t in idx:
+            t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(12):
+            assert np.array_equal(host(idx[i]), want[i][0]), (rep, i)
+            assert np.allclose(host(wts[i]), want[i][1], rtol=1e-6, atol=0)
+        k3g.k3g_moe_route(idx[0], wts[0], xd[5], Wd, bd, K, ws)  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx[0]), want[5][0])
 
 
 # ---- the MoE layer --------------------------------------------------------------------
@@ -524,6 +560,20 @@ def test_probe_hooks_run(k3g):
     buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
     k3g.k3g_probe_read_rate(buf, sink)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", [1, 7, 256, 896])
+def test_probe_handoff_sums(k3g, n):
+    # the dependent launch and the last-arriver handoff both deliver every
+    # workgroup's value (0.5 * i) to the consumer, call after call; the counter
+    # is left at zero
+    buf = torch.zeros(n + 1, dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    want = 0.5 * n * (n - 1) / 2
+    for mode in (1, 2, 2, 1, 2):
+        buf[n] = -1.0
+        k3g.k3g_probe_handoff(mode, buf, cnt)
+        assert float(host(buf)[n]) == want and int(host(cnt)[0]) == 0, mode
 
 
 MAGIC = 0x9E3779B9 - (1 << 32)  # the read probe's sink value, as an int32
