@@ -10,8 +10,13 @@
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer (HBM of the current HIP device)
  *    unless its comment says host. The caller owns all memory: weights,
- *    inputs, outputs and workspace. The library allocates nothing and keeps
- *    no mutable global state.
+ *    inputs, outputs and workspace. The compute calls allocate nothing and
+ *    keep no state between calls. Three exceptions, each stated where it is
+ *    declared: the expert cache object (k3g_cache_create allocates it on the
+ *    host, and k3g_cache_prepare its pinned host staging on first use, both
+ *    freed by k3g_cache_destroy); the static device scratch array of
+ *    k3g_moe_layer_static (held by every GPU the library runs on); and the
+ *    measurement hooks, which allocate nothing either.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on `stream` and returns without
  *    synchronising. Results are valid once the stream reaches that point.
