@@ -261,6 +261,13 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
     ra3 = make_rsrc(GLU ? a.w3 : a.seg[0].w, GLU ? (uint32_t)((uint64_t)a.seg[0].K * 2 * a.N) : 0u);
     auto seg_of = [&](int kb) { return kb >= a.kb_start[2] ? 2 : kb >= a.kb_start[1] ? 1 : 0; };
     uint4 A[kNBUF][4][2];
+    // Block kb of A into ring slot `slot`. Issued on every step, also where
+    // there is no block left to fetch (then block kb is the current one,
+    // loaded again into the free slot): the compiler's waits for a slot then
+    // count the same loads on every path, instead of waiting, on the path that
+    // issues them, for the loads just issued. (No load here may be past the
+    // range: such a load can return before older ones, and the counted waits
+    // assume loads complete in the order they were issued.)
     auto load_a = [&](int kb, int slot) {
         const int s = seg_of(kb);
         const uint32_t K2 = 2u * (uint32_t)a.seg[s].K;
@@ -320,34 +327,46 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < kNBUF - 1; ++j)
-            if (kb0 + j < kb1) load_a(kb0 + j, j);
+        for (int j = 0; j < kNBUF - 1; ++j) load_a(min(kb0 + j, kb1 - 1), j);
         wait_vm<0>();
         __syncthreads();
     }
-    // main loop, unrolled by the ring depth so that every ring slot is static
-    for (int kb = kb0; kb < kb1; kb += kNBUF) {
+    // one block: B of the next into the other LDS buffer, A of the one after
+    // next into the ring, this block's products; then the next block's B is
+    // in LDS (vmcnt: only the 8 A loads, issued after the DMA, may still be in
+    // flight), and every wavefront is done with this buffer before it is
+    // filled again
+    auto step = [&](int k, int j) {  // j = (k - kb0) % kNBUF
+        const int buf = (k - kb0) & 1;
+        if (k + 1 < kb1) dma_b(k + 1, buf ^ 1);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const bool na = k + kNBUF - 1 < kb1;
+        load_a(na ? k + kNBUF - 1 : k, (j + kNBUF - 1) % kNBUF);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j, buf);
+        __builtin_amdgcn_sched_barrier(0);
+        // (where there is no block left to fetch, the compiler may drop the
+        // extra A loads, whose values are never read: then nothing but the
+        // DMA may be counted)
+        if (na)
+            wait_vm<8>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+    };
+    // whole rounds of the ring (every ring slot static, no branch inside),
+    // then the last one or two blocks
+    const int nblk = kb1 - kb0, nround = nblk / kNBUF;
+    for (int rd = 0; rd < nround; ++rd) {
+        const int kb = kb0 + rd * kNBUF;
 #pragma unroll
-        for (int j = 0; j < kNBUF; ++j) {
-            const int k = kb + j;
-            if (k < kb1) {  // uniform
-                const int buf = (k - kb0) & 1;
-                const bool nb = k + 1 < kb1, na = k + kNBUF - 1 < kb1;
-                if (nb) dma_b(k + 1, buf ^ 1);
-                __asm__ volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                if (na) load_a(k + kNBUF - 1, (j + kNBUF - 1) % kNBUF);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(j, buf);
-                __builtin_amdgcn_sched_barrier(0);
-                // the next block's B is in LDS, and every wavefront is done
-                // with this buffer before it is filled again
-                if (na) wait_vm<8>();
-                else wait_vm<0>();
-                __syncthreads();
-            }
-        }
+        for (int j = 0; j < kNBUF; ++j) step(kb + j, j);
     }
+    static_assert(kNBUF == 3, "the tail below takes at most two blocks");
+    const int kt = kb0 + nround * kNBUF;
+    if (kt < kb1) step(kt, 0);
+    if (kt + 1 < kb1) step(kt + 1, 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -41,6 +41,8 @@
 // bucket's table (the pages sort a chunk's pairs by expert so that each
 // selected expert is read once: "Kimi K3 engine (c/kimi_k3.c)", section
 // "Chunked prefill"); here an expert is read once per pass.
+#include <atomic>
+
 #include "k3g_common.h"
 
 // Build-time knob (the default is the shipped configuration): blocks of four
@@ -79,6 +81,10 @@ __device__ inline void split_group(float r, uint8_t *out, int q, bool store) {
     // dropped.
     const uint32_t mb = __builtin_bit_cast(uint32_t, m);
     const int x0 = int(mb >> 23) - 129 + ((mb & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+    // lane e keeps dword e >> 3 of pieces (e & 7) and (e & 7) + 8, so that the
+    // 16 pieces go out in two 128-byte stores a half-wavefront, and lane e < 16
+    // writes piece e's scale
+    uint32_t keep0 = 0, keep1 = 0;
 #pragma unroll
     for (int p = 0; p < f4::kPieces; ++p) {
         const int x = max(x0 - 2 * p, -126);
@@ -91,9 +97,17 @@ __device__ inline void split_group(float r, uint8_t *out, int q, bool store) {
         w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0xB1, 0xF, 0xF, false);
         w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x4E, 0xF, 0xF, false);
         w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x141, 0xF, 0xF, false);
-        const int lane = p + 16 * q;
-        if (store && (e & 7) == 0) *(uint32_t *)(out + 16 * lane + 4 * (e >> 3)) = w;
-        if (store && e == 0) *(uint32_t *)(out + 1024 + 4 * lane) = (uint32_t)(x + 127);
+        if ((e & 7) == (p & 7)) {
+            if (p < 8)
+                keep0 = w;
+            else
+                keep1 = w;
+        }
+    }
+    if (store) {
+        *(uint32_t *)(out + 16 * ((e & 7) + 16 * q) + 4 * (e >> 3)) = keep0;
+        *(uint32_t *)(out + 16 * ((e & 7) + 8 + 16 * q) + 4 * (e >> 3)) = keep1;
+        if (e < 16) *(uint32_t *)(out + 1024 + 4 * (e + 16 * q)) = (uint32_t)(max(x0 - 2 * e, -126) + 127);
     }
 }
 
@@ -119,10 +133,11 @@ int launch_split(uint8_t *dst, const float *src, int n_vec, int len, int src_str
 
 // ---- the products -------------------------------------------------------------
 
-// Out-of-range soffset: a buffer load past the resource's range returns 0
-// without touching memory, so a wavefront with no rows still runs the same
-// straight-line code (and the barrier) without reading anything.
-constexpr uint32_t kOffRange = 0x80000000u;
+// A wavefront with no rows (its first row past the output) still runs the
+// same straight-line code and barriers: it reads the expert's first rows and
+// stores nothing. (Its loads stay in range: a load past a buffer's range
+// returns at once, possibly before older loads, and the counted waits here
+// assume loads complete in the order they were issued.)
 
 // UP:   tiles (w1, rows r0..r0+15), (w3, r0..r0+15), (w1, r0+16..), (w3, r0+16..);
 //       h[pos][r] = SiTU(g, u) for the 32 rows, and the 16 pieces of this
@@ -202,15 +217,13 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4_kernel(
         vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
-    // block k: tile k / (NCK/4), chunks 4*(k % (NCK/4)) .. +3 (a dead wavefront's
-    // loads are all past the range: zeros, no memory traffic)
-    const uint32_t dead = live ? 0u : kOffRange;
+    // block k: tile k / (NCK/4), chunks 4*(k % (NCK/4)) .. +3
     uint4 A[NBUF][CPB], S[NBUF];
     auto load_block = [&](int k) {
         const int t = k / (NCK / CPB), c0 = CPB * (k % (NCK / CPB)), b = k % NBUF;
 #pragma unroll
-        for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u + dead);
-        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u + dead);
+        for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u);
+        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u);
     };
     // the bucket: wavefront 0 of workgroup b writes counts and offsets
     // [64b, 64b + 64) (workgroup 0 also perm, inv, active)
@@ -377,13 +390,12 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
         vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
-    const uint32_t dead = live ? 0u : kOffRange;
     uint4 A[NBUF][CPB], S[NBUF];
     auto load_block = [&](int kb) {
         const int t = kb / (NCK / CPB), c0 = CPB * (kb % (NCK / CPB)), b = kb % NBUF;
 #pragma unroll
-        for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u + dead);
-        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u + dead);
+        for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u);
+        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u);
     };
     // B: the pass's NPP vectors of pieces into LDS, then the first weight blocks
     {
@@ -523,8 +535,17 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
 // 32 rows; DOWN: 64 rows). The loop runs chunk by chunk over all four tiles,
 // so each B fragment read from LDS feeds four products and each A fragment
 // four (one per pair): 16 products per chunk for 4 A and 4 B fragments.
-// Operand A streams through a 3-deep ring of 2-chunk blocks; B of the next
-// chunk is read while this chunk's products issue.
+// Operand A streams through a 3-deep ring of 2-chunk blocks, each block's
+// scale dwords with it (one 16-byte load a row covers two blocks); B of the
+// next chunk is read while this chunk's products issue.
+//
+// The grid is persistent: one workgroup per CU (the LDS holds one), walking
+// the items (pass, row block), row blocks fastest, gridDim apart. When an
+// item's products are done, the next item's B (into the LDS, once every
+// wavefront has read its last chunk) and its first weight blocks are
+// requested before this item's epilogue, so the epilogue's vector work and
+// stores and the next item's first loads overlap instead of leaving the
+// CU's memory pipe idle between workgroups.
 template <bool UP, int NCK>
 __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     float *__restrict__ out, const uint8_t *__restrict__ pieces, uint8_t *__restrict__ hp, BankDev bank,
@@ -532,6 +553,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     const int32_t *__restrict__ passes, int top_k, int latent, int inter) {
     constexpr int NPP = 4, WAVES = 8, TILES = 4;
     constexpr int CPB = 2, NB = NCK / CPB, NBUF = 3;
+    static_assert(NB % 2 == 0, "a scale load covers two blocks");
     constexpr int ROWS_W = UP ? 32 : 64;
     constexpr int ngrp = 4 * NCK;
     constexpr int VEC = NCK * f4::kChunkBytes;
@@ -539,161 +561,194 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n_out = UP ? inter : latent;
+    // (row blocks fastest: the workgroups running at once cover every row
+    // block of a few passes; an order with the passes fastest, for L2 sharing
+    // between the passes of one expert, measured slower: all of them then
+    // read the same rows of different experts)
     const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
-    // workgroup = (pass, row block), row blocks fastest: the workgroups running
-    // at once cover every row block of a few passes (an order with the passes
-    // fastest, for L2 sharing between the passes of one expert, measured
-    // slower: all of them then read the same rows of different experts)
-    const int k = blockIdx.x / row_blocks;
-    if (k >= passes[0]) return;  // whole workgroup
-    const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
-    const int e = active[1 + slot];
-    const int p0 = offsets[e] + pass * NPP;
-    const int np = min(NPP, offsets[e + 1] - p0);
-    const int r0 = ((blockIdx.x - k * row_blocks) * WAVES + wave) * ROWS_W;
-    const bool live = r0 < n_out;
+    const int n_items = passes[0] * row_blocks;
+    int item = blockIdx.x;
+    if (item >= n_items) return;  // whole workgroup
 
-    const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
+    // the current item
+    int p0 = 0, np = 0, r0 = 0;
+    bool live = false;
     constexpr uint32_t pitch_p = 16u * ngrp, pitch_s = ngrp;
     rsrc_t rp[TILES], rs[TILES];
     uint32_t vp[TILES], vs[TILES];
+    auto setup = [&](int it) {
+        const int k = it / row_blocks;
+        const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
+        const int e = active[1 + slot];
+        p0 = offsets[e] + pass * NPP;
+        np = min(NPP, offsets[e + 1] - p0);
+        r0 = ((it - k * row_blocks) * WAVES + wave) * ROWS_W;
+        live = r0 < n_out;
+        const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
-        const uint32_t row = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t) + (lane & 15));
-        rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
-        rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
-        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
-        vs[t] = row * pitch_s;
-    }
-    const uint32_t dead = live ? 0u : kOffRange;
+        for (int t = 0; t < TILES; ++t) {
+            const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
+            const uint32_t row = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t) + (lane & 15));
+            rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
+            rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
+            vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+            vs[t] = row * pitch_s;
+        }
+    };
     uint4 A[NBUF][TILES][CPB];
-    uint2 S[NBUF][TILES];
+    uint4 S[2][TILES];  // scale dwords of blocks 2m and 2m + 1 in S[m % 2]
     auto load_block = [&](int kb) {
         const int b = kb % NBUF;
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
 #pragma unroll
             for (int c = 0; c < CPB; ++c)
-                A[b][t][c] = buf_load16(rp[t], vp[t], (uint32_t)(CPB * kb + c) * 64u + dead);
-            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs[t], (int)vs[t], (int)((uint32_t)(CPB * kb) * 4u + dead), 0);
-            S[b][t] = make_uint2(sv[0], sv[1]);
+                A[b][t][c] = buf_load16(rp[t], vp[t], (uint32_t)(CPB * kb + c) * 64u);
+            if (kb % 2 == 0) S[(kb / 2) % 2][t] = buf_load16(rs[t], vs[t], (uint32_t)(CPB * kb) * 4u);
         }
     };
-    // B: the pass's four vectors of pieces into LDS
-    {
+    // B: the item's four vectors of pieces into LDS (a short pass repeats its
+    // last pair)
+    auto load_b = [&]() {
         const uint32_t lb = lds_addr(lds_b);
         constexpr int units = VEC / 1024;
 #pragma unroll
         for (int q = 0; q < NPP; ++q) {
             const int pq = p0 + min(q, np - 1);
-            const int v = UP ? perm[pq] / top_k : pq;
-            const uint8_t *src = pieces + (size_t)v * VEC;
+            const int vec = UP ? perm[pq] / top_k : pq;
+            const uint8_t *src = pieces + (size_t)vec * VEC;
             for (int u = wave; u < units; u += WAVES)
                 dma16(src, 1024u * u + 16u * lane, lb + (uint32_t)(q * VEC) + 1024u * u);
         }
-    }
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+    };
     constexpr int PRO = NBUF - 1 < NB ? NBUF - 1 : NB;
+    auto prologue = [&]() {
+        load_b();
+        __asm__ volatile("" ::: "memory");  // the weight loads stay after the DMA
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < PRO; ++kb) load_block(kb);
-    wait_vm<PRO * TILES * (CPB + 1)>();
+        for (int kb = 0; kb < PRO; ++kb) load_block(kb);
+    };
+    setup(item);
+    prologue();
+    wait_vm<0>();
     __syncthreads();
 
     const uint32_t qsh = 8u * (uint32_t)(lane >> 4);
-    float4_t acc[NPP][TILES];
-#pragma unroll
-    for (int q = 0; q < NPP; ++q)
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) acc[q][t] = float4_t{0.f, 0.f, 0.f, 0.f};
     int li = lane;
     __asm__ volatile("" : "+v"(li));
     const uint4 *bq = lds_b + li;
     const uint32_t *sq = (const uint32_t *)lds_b + 256 + li;
-    uint4 Bv[2][NPP];
-    uint32_t Bs[2][NPP];
-    auto read_b = [&](int i) {
+    const int qd = lane & 15, v = qd & 3;
+    while (true) {
+        float4_t acc[NPP][TILES];
 #pragma unroll
-        for (int q = 0; q < NPP; ++q) {
-            Bv[i & 1][q] = bq[(q * VEC + i * f4::kChunkBytes) / 16];
-            Bs[i & 1][q] = sq[(q * VEC + i * f4::kChunkBytes) / 4];
-        }
-    };
-    read_b(0);
+        for (int q = 0; q < NPP; ++q)
 #pragma unroll
-    for (int i = 0; i < NCK; ++i) {
-        const int kb = i / CPB, c = i % CPB, b = kb % NBUF;
-        if (c == 0 && kb + NBUF - 1 < NB) load_block(kb + NBUF - 1);
-        if (i + 1 < NCK) read_b(i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-            const uint32_t sd = c == 0 ? S[b][t].x : S[b][t].y;
-            const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
-            const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
-            const uint4 a = A[b][t][c];
-            const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
+            for (int t = 0; t < TILES; ++t) acc[q][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        uint4 Bv[2][NPP];
+        uint32_t Bs[2][NPP];
+        auto read_b = [&](int i) {
 #pragma unroll
             for (int q = 0; q < NPP; ++q) {
-                const uint4 bv = Bv[i & 1][q];
-                const v8i_t B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
-                acc[q][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av, B, acc[q][t], 4, 4, 0,
-                                                                             (int)(sa & keep), 0, (int)Bs[i & 1][q]);
+                Bv[i & 1][q] = bq[(q * VEC + i * f4::kChunkBytes) / 16];
+                Bs[i & 1][q] = sq[(q * VEC + i * f4::kChunkBytes) / 4];
             }
+        };
+        read_b(0);
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int kb = i / CPB, c = i % CPB, b = kb % NBUF;
+            if (c == 0 && kb + NBUF - 1 < NB) load_block(kb + NBUF - 1);
+            if (i + 1 < NCK) read_b(i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) {
+                const uint4 s4 = S[(kb / 2) % 2][t];
+                const int sw = 2 * (kb % 2) + c;
+                const uint32_t sd = sw == 0 ? s4.x : sw == 1 ? s4.y : sw == 2 ? s4.z : s4.w;
+                const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
+                const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
+                const uint4 a = A[b][t][c];
+                const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
+#pragma unroll
+                for (int q = 0; q < NPP; ++q) {
+                    const uint4 bv = Bv[i & 1][q];
+                    const v8i_t B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
+                    acc[q][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av, B, acc[q][t], 4, 4, 0,
+                                                                                 (int)(sa & keep), 0, (int)Bs[i & 1][q]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < NPP; ++q)
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) __asm__ volatile("" : "+v"(acc[q][t]));
+
+        // this item's epilogue inputs; then the next item's first loads
+        const int cp0 = p0, cnp = np, cr0 = r0;
+        const bool clive = live;
+        const int next = item + (int)gridDim.x;
+        const bool more = next < n_items;
+        __syncthreads();  // every wavefront has read its last chunk of B
+        if (more) {
+            setup(next);
+            prologue();
         }
         __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int q = 0; q < NPP; ++q)
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) __asm__ volatile("" : "+v"(acc[q][t]));
 
-    // per pair: sum the 16 piece columns, then lane qd = lane & 15 holds row
-    // tile ts = qd >> 2, row 4 * (lane >> 4) + (qd & 3) (UP: g and u of the
-    // wavefront's two row tiles, lanes qd < 8)
-    const int qd = lane & 15, v = qd & 3;
+        // per pair: sum the 16 piece columns, then lane qd = lane & 15 holds row
+        // tile ts = qd >> 2, row 4 * (lane >> 4) + (qd & 3) (UP: g and u of the
+        // wavefront's two row tiles, lanes qd < 8)
 #pragma unroll
-    for (int q = 0; q < NPP; ++q) {
+        for (int q = 0; q < NPP; ++q) {
 #pragma unroll
-        for (int t = 0; t < TILES; ++t)
+            for (int t = 0; t < TILES; ++t)
 #pragma unroll
-            for (int vv = 0; vv < 4; ++vv) {
-                float sm = acc[q][t][vv];
-                sm += dpp<0xB1>(sm);
-                sm += dpp<0x4E>(sm);
-                sm += dpp<0x141>(sm);
-                sm += dpp<0x140>(sm);
-                acc[q][t][vv] = sm;
+                for (int vv = 0; vv < 4; ++vv) {
+                    float sm = acc[q][t][vv];
+                    sm += dpp<0xB1>(sm);
+                    sm += dpp<0x4E>(sm);
+                    sm += dpp<0x141>(sm);
+                    sm += dpp<0x140>(sm);
+                    acc[q][t][vv] = sm;
+                }
+            // values, not references: a lane-dependent choice of an array element
+            // by reference puts the accumulators on the stack
+            float pv[TILES];
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) {
+                const float4_t x = acc[q][t];
+                pv[t] = v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
             }
-        // values, not references: a lane-dependent choice of an array element
-        // by reference puts the accumulators on the stack
-        float pv[TILES];
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-            const float4_t x = acc[q][t];
-            pv[t] = v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
+            const bool store = clive && q < cnp;
+            const int pq = cp0 + q;
+            if constexpr (UP) {
+                const int ts = (qd >> 2) & 1;
+                const int row = cr0 + 16 * ts + 4 * (lane >> 4) + v;
+                const float g = ts ? pv[2] : pv[0], u = ts ? pv[3] : pv[1];
+                const float hv = situ(g, u);
+                if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
+                // this pair's group of h as pieces for the down-projection
+                const int j = lane & 31;
+                const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
+                const int g32 = cr0 / kGroup;
+                const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+                split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
+                            store && lane < 32);
+            } else {
+                const int ts = qd >> 2;
+                const int row = cr0 + 16 * ts + 4 * (lane >> 4) + v;
+                const float y = ts == 0 ? pv[0] : ts == 1 ? pv[1] : ts == 2 ? pv[2] : pv[3];
+                if (store) out[(size_t)pq * n_out + row] = y;
+            }
         }
-        const bool store = live && q < np;
-        const int pq = p0 + q;
-        if constexpr (UP) {
-            const int ts = (qd >> 2) & 1;
-            const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
-            const float g = ts ? pv[2] : pv[0], u = ts ? pv[3] : pv[1];
-            const float hv = situ(g, u);
-            if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
-            const int j = lane & 31;
-            const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
-            const int g32 = r0 / kGroup;
-            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
-            split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
-                        store && lane < 32);
-        } else {
-            const int ts = qd >> 2;
-            const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
-            const float y = ts == 0 ? pv[0] : ts == 1 ? pv[1] : ts == 2 ? pv[2] : pv[3];
-            if (store) out[(size_t)pq * n_out + row] = y;
-        }
+        if (!more) break;
+        // the next item's B and first blocks (and this epilogue's stores)
+        wait_vm<0>();
+        __syncthreads();
+        item = next;
     }
 }
 
@@ -747,15 +802,14 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
         vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
-    const uint32_t dead = live ? 0u : kOffRange;
     uint4 A[NBUF][TILES];
     uint32_t S[NBUF][TILES];
     auto load_a = [&](int i) {
         const int b = i % NBUF;
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
-            A[b][t] = buf_load16(rp[t], vp[t], (uint32_t)i * 64u + dead);
-            S[b][t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs[t], (int)vs[t], (int)((uint32_t)i * 4u + dead), 0);
+            A[b][t] = buf_load16(rp[t], vp[t], (uint32_t)i * 64u);
+            S[b][t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs[t], (int)vs[t], (int)((uint32_t)i * 4u), 0);
         }
     };
     // this wavefront's pair (the pass's last pair again past its end)
@@ -883,6 +937,19 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
 // of h's pieces: in and out sizes multiples of 512, at most 4096 (B -- a
 // vector's pieces, 40 bytes per entry -- in LDS); scale tensors and bank
 // stride 16-byte aligned. (Other shapes and banks use the vector kernels.)
+// The current device's compute units (cached per device; 0 on error).
+static int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 bool f4_shape_ok(int latent, int inter) {
     auto ok = [](int n) { return n % 512 == 0 && n >= 512 && n <= 4096; };
     return ok(latent) && ok(inter);
@@ -953,7 +1020,10 @@ static int launch_f4m(int npp, float *out, const uint8_t *pieces, uint8_t *hp, c
         if (lds > 65536 && hipFuncSetAttribute((const void *)moe_f4q_kernel<UP, NCK>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return K3G_EHIP;
-        moe_f4q_kernel<UP, NCK><<<(unsigned)grid, 8 * kWave, lds, st>>>(out, pieces, hp, bank, active, offsets, perm,
+        const int n_cu = cu_count();  // persistent: one workgroup per CU
+        if (n_cu <= 0) return K3G_EHIP;
+        const int64_t pgrid = grid < n_cu ? grid : n_cu;
+        moe_f4q_kernel<UP, NCK><<<(unsigned)pgrid, 8 * kWave, lds, st>>>(out, pieces, hp, bank, active, offsets, perm,
                                                                        passes, top_k, latent, inter);
     } else if (npp == 2) {
         if (lds > 65536 &&
