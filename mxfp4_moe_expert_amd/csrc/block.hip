@@ -8,6 +8,8 @@
 //
 // The dense weights are bf16 (widened exactly to fp32); activations stay fp32
 // and every product accumulates in fp32, so nothing is rounded to bf16.
+#include <algorithm>
+
 #include "k3g_common.h"
 
 namespace k3g {
@@ -162,9 +164,11 @@ constexpr int kTok = 64;        // tokens per workgroup
 constexpr int kKB = 64;         // entries per block (two steps)
 constexpr int kStepBytes = 3 * 1024;           // one token tile, one step, three pieces
 constexpr int kBlockB = 4 * 2 * kStepBytes;    // 24 KB: one block of operand B
-constexpr int kNBUF = 3;        // operand-A ring depth (blocks)
+#ifndef K3G_DENSE_NBUF
+#define K3G_DENSE_NBUF 3
+#endif
+constexpr int kNBUF = K3G_DENSE_NBUF;  // operand-A ring depth (blocks)
 constexpr int kMaxSeg = 3;
-constexpr int kTargetWG = 512;  // resident workgroups: two per CU
 }  // namespace dm
 
 struct DenseMSeg {
@@ -301,24 +305,31 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
 
     int li = lane;
     __asm__ volatile("" : "+v"(li));
+    // B fragments two-deep: the next (step, token tile)'s three are read from
+    // LDS while this one's twelve products issue
     auto compute = [&](int slot, int buf) {
         const uint4 *bb = (const uint4 *)(lds + buf * kBlockB) + li;
         __asm__ volatile("" ::: "memory");
+        bf16x8_t B[2][3];
+        auto read_b = [&](int it) {  // it = 4 * step + token tile
+            const int st = it / 4, t = it % 4;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int p = 0; p < 3; ++p) B[it & 1][p] = __builtin_bit_cast(bf16x8_t, bb[((t * 2 + st) * 3 + p) * 64]);
+        };
+        read_b(0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                bf16x8_t B[3];
+        for (int it = 0; it < 8; ++it) {
+            const int st = it / 4, t = it % 4;
+            if (it + 1 < 8) read_b(it + 1);
+            __builtin_amdgcn_sched_barrier(0);  // the reads go out ahead of the products
 #pragma unroll
-                for (int p = 0; p < 3; ++p) B[p] = __builtin_bit_cast(bf16x8_t, bb[((t * 2 + st) * 3 + p) * 64]);
+            for (int i = 0; i < 4; ++i) {
+                const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, A[slot][i][st]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, A[slot][i][st]);
-#pragma unroll
-                    for (int p = 0; p < 3; ++p)
-                        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, B[p], acc[i][t], 0, 0, 0);
-                }
+                for (int p = 0; p < 3; ++p)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, B[it & 1][p], acc[i][t], 0, 0, 0);
             }
+        }
     };
 
     // prologue: B of the first block, A of the first two
@@ -363,10 +374,10 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
 #pragma unroll
         for (int j = 0; j < kNBUF; ++j) step(kb + j, j);
     }
-    static_assert(kNBUF == 3, "the tail below takes at most two blocks");
     const int kt = kb0 + nround * kNBUF;
-    if (kt < kb1) step(kt, 0);
-    if (kt + 1 < kb1) step(kt + 1, 1);
+#pragma unroll
+    for (int j = 0; j < kNBUF - 1; ++j)
+        if (kt + j < kb1) step(kt + j, j);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -442,16 +453,27 @@ bool dense_mfma_ok(int T, int N, const int *K, int n_seg) {
     return true;
 }
 
-// Slices of K: as many as keep the grid within one round of resident
-// workgroups (two per CU; a second, mostly empty round would double the time),
-// at least 4 blocks a slice.
+// Slices of K. A cost model in block-steps of the busiest CU: the items
+// (tiles x slices) spread evenly over the chip's 256 CUs; the busiest runs
+// ceil(items / 256) of them, each ceil(nkb / S) blocks plus about two for its
+// prologue and partial stores, and a CU with one workgroup is counted as slow
+// as with two (one wavefront a SIMD leaves the matrix cores half idle). The
+// partials' round trip (written, then read by the reduction) adds about one
+// block-step per 4 MB. At least 4 blocks a slice.
 int dense_slices(int T, int N, int K_total, bool glu) {
     const int rows_wg = dm::kWaves * (glu ? 32 : 64);
     const int64_t tiles = (int64_t)((N + rows_wg - 1) / rows_wg) * (dense_t64(T) / dm::kTok);
     const int nkb = K_total / dm::kKB;
-    int64_t s = dm::kTargetWG / tiles;
-    s = s < nkb / 4 ? s : nkb / 4;
-    return s < 1 ? 1 : (int)s;
+    const int max_s = nkb / 4 > 1 ? nkb / 4 : 1;
+    const double part_bytes = 8.0 * (glu ? 2 : 1) * (double)dense_t64(T) * N;  // per slice, both ways
+    int best = 1;
+    double best_cost = 1e300;
+    for (int s = 1; s <= max_s; ++s) {
+        const int64_t per_cu = std::max<int64_t>((tiles * s + 255) / 256, 2);
+        const double cost = (double)per_cu * ((nkb + s - 1) / s + 2) + s * part_bytes / (4.0 * (1 << 20));
+        if (cost < best_cost) best_cost = cost, best = s;
+    }
+    return best;
 }
 
 int launch_split3(uint8_t *xb, const float *x, int T, int K, int ld, hipStream_t st) {

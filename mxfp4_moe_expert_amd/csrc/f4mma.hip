@@ -701,6 +701,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         // per pair: sum the 16 piece columns, then lane qd = lane & 15 holds row
         // tile ts = qd >> 2, row 4 * (lane >> 4) + (qd & 3) (UP: g and u of the
         // wavefront's two row tiles, lanes qd < 8)
+        float hvs[NPP];  // UP: this lane's h of each pair
 #pragma unroll
         for (int q = 0; q < NPP; ++q) {
 #pragma unroll
@@ -730,18 +731,30 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
                 const float g = ts ? pv[2] : pv[0], u = ts ? pv[3] : pv[1];
                 const float hv = situ(g, u);
                 if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
-                // this pair's group of h as pieces for the down-projection
-                const int j = lane & 31;
-                const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
-                const int g32 = cr0 / kGroup;
-                const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
-                split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
-                            store && lane < 32);
+                hvs[q] = hv;
             } else {
                 const int ts = qd >> 2;
                 const int row = cr0 + 16 * ts + 4 * (lane >> 4) + v;
                 const float y = ts == 0 ? pv[0] : ts == 1 ? pv[1] : ts == 2 ? pv[2] : pv[3];
                 if (store) out[(size_t)pq * n_out + row] = y;
+            }
+        }
+        if constexpr (UP) {
+            // each pair's group of h (the wavefront's 32 rows) as pieces for the
+            // down-projection, two pairs a call: pair q in lanes 0..31, q + 1 in
+            // lanes 32..63 (entry e of the group in lane e of its half)
+            const int j = lane & 31;
+            const int src = 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3);
+            const int g32 = cr0 / kGroup;
+            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+            const int hi = lane >> 5;
+#pragma unroll
+            for (int q = 0; q < NPP; q += 2) {
+                const float h0 = __shfl(hvs[q], src), h1 = __shfl(hvs[q + 1], src);
+                const int qq = q + hi;
+                const bool store = clive && qq < cnp;
+                split_group(hi ? h1 : h0, hp + (size_t)(store ? cp0 + qq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes,
+                            g32 & 3, store);
             }
         }
         if (!more) break;
