@@ -493,6 +493,7 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
     // block's columns), then lane q < 8 of each 16 holds row 16*ts + 4*(lane >> 4) + v
     const int qd = lane & 15, ts = (qd >> 2) & 1, v = qd & 3;
     const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
+    float hvs[NPP];  // UP: this lane's h of each pair
 #pragma unroll
     for (int q = 0; q < NPP; ++q) {
 #pragma unroll
@@ -515,16 +516,27 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
         if constexpr (UP) {
             const float hv = situ(sel(acc[q][0], acc[q][2]), sel(acc[q][1], acc[q][3]));
             if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
-            // this pair's group of h as pieces for the down-projection
-            const int j = lane & 31;
-            const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
-            const int g32 = r0 / kGroup;
-            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
-            split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
-                        store && lane < 32);
+            hvs[q] = hv;
         } else {
             const float y = sel(acc[q][0], acc[q][1]);
             if (store && qd < 8) out[(size_t)pq * n_out + row] = y;
+        }
+    }
+    if constexpr (UP) {
+        // each pair's group of h as pieces for the down-projection, two pairs
+        // a call: pair q in lanes 0..31, q + 1 in lanes 32..63
+        const int j = lane & 31;
+        const int src = 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3);
+        const int g32 = r0 / kGroup;
+        const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+        const int hi = lane >> 5;
+#pragma unroll
+        for (int q = 0; q < NPP; q += 2) {
+            const float h0 = __shfl(hvs[q], src), h1 = __shfl(hvs[q + 1], src);
+            const int qq = q + hi;
+            const bool store = live && qq < np;
+            split_group(hi ? h1 : h0, hp + (size_t)(store ? p0 + qq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes,
+                        g32 & 3, store);
         }
     }
 }
@@ -904,6 +916,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
 
     // per pair, as in the four-pair kernel
     const int qd = lane & 15, v = qd & 3;
+    float hvs[NPP];  // UP: this lane's h of each pair
 #pragma unroll
     for (int q = 0; q < NPP; ++q) {
 #pragma unroll
@@ -930,17 +943,29 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
             const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
             const float hv = situ(ts ? pv[2] : pv[0], ts ? pv[3] : pv[1]);
             if (store && qd < 8) out[(size_t)pq * n_out + row] = hv;
-            const int j = lane & 31;
-            const float hj = __shfl(hv, 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3));
-            const int g32 = r0 / kGroup;
-            const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
-            split_group(hj, hp + (size_t)(store ? pq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes, g32 & 3,
-                        store && lane < 32);
+            hvs[q] = hv;
         } else {
             const int ts = qd >> 2;
             const int row = r0 + 16 * ts + 4 * (lane >> 4) + v;
             const float y = ts == 0 ? pv[0] : ts == 1 ? pv[1] : ts == 2 ? pv[2] : pv[3];
             if (store) out[(size_t)pq * n_out + row] = y;
+        }
+    }
+    if constexpr (UP) {
+        // each pair's group of h as pieces for the down-projection, two pairs
+        // a call: pair q in lanes 0..31, q + 1 in lanes 32..63
+        const int j = lane & 31;
+        const int src = 16 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3);
+        const int g32 = r0 / kGroup;
+        const size_t hstride = (size_t)(inter / 128) * f4::kChunkBytes;
+        const int hi = lane >> 5;
+#pragma unroll
+        for (int q = 0; q < NPP; q += 2) {
+            const float h0 = __shfl(hvs[q], src), h1 = __shfl(hvs[q + 1], src);
+            const int qq = q + hi;
+            const bool store = live && qq < np;
+            split_group(hi ? h1 : h0, hp + (size_t)(store ? p0 + qq : 0) * hstride + (g32 >> 2) * f4::kChunkBytes,
+                        g32 & 3, store);
         }
     }
 }
