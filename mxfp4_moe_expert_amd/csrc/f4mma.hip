@@ -51,6 +51,11 @@
 #ifndef K3G_F4_NBUF
 #define K3G_F4_NBUF 6
 #endif
+// Consecutive passes per XCD group in the four-pair kernel's item order (0:
+// plain order).
+#ifndef K3G_F4Q_GROUP
+#define K3G_F4Q_GROUP 4
+#endif
 
 namespace k3g {
 
@@ -579,7 +584,22 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     // read the same rows of different experts)
     const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
     const int n_items = passes[0] * row_blocks;
-    int item = blockIdx.x;
+    // XCD-aware order: workgroup w runs on XCD w % 8 (the dispatcher deals
+    // workgroups round the XCDs); the items come in groups of G consecutive
+    // passes (all their row blocks), group g on XCD g % 8, so the row blocks
+    // of a pass share its B, and the passes of one expert its weights,
+    // through that XCD's L2
+    constexpr int G = K3G_F4Q_GROUP;
+    const bool xcd = G > 0 && gridDim.x % 8 == 0;
+    const int per = xcd ? (int)gridDim.x / 8 : (int)gridDim.x;
+    const int gi = G * row_blocks;
+    auto item_at = [&](int L) {  // the workgroup's L-th item (its own sequence)
+        if (!xcd) return L;
+        const int x = (int)blockIdx.x % 8;
+        return (x + 8 * (L / gi)) * gi + L % gi;
+    };
+    int loc = xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
+    int item = item_at(loc);
     if (item >= n_items) return;  // whole workgroup
 
     // the current item
@@ -701,7 +721,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         // this item's epilogue inputs; then the next item's first loads
         const int cp0 = p0, cnp = np, cr0 = r0;
         const bool clive = live;
-        const int next = item + (int)gridDim.x;
+        const int next = item_at(loc + per);
         const bool more = next < n_items;
         __syncthreads();  // every wavefront has read its last chunk of B
         if (more) {
@@ -774,6 +794,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         wait_vm<0>();
         __syncthreads();
         item = next;
+        loc += per;
     }
 }
 
@@ -1060,7 +1081,8 @@ static int launch_f4m(int npp, float *out, const uint8_t *pieces, uint8_t *hp, c
             return K3G_EHIP;
         const int n_cu = cu_count();  // persistent: one workgroup per CU
         if (n_cu <= 0) return K3G_EHIP;
-        const int64_t pgrid = grid < n_cu ? grid : n_cu;
+        const int64_t g8 = (grid + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+        const int64_t pgrid = g8 < n_cu ? g8 : n_cu;
         moe_f4q_kernel<UP, NCK><<<(unsigned)pgrid, 8 * kWave, lds, st>>>(out, pieces, hp, bank, active, offsets, perm,
                                                                        passes, top_k, latent, inter);
     } else if (npp == 2) {
