@@ -52,9 +52,12 @@
 #define K3G_F4_NBUF 6
 #endif
 // Consecutive passes per XCD group in the four-pair kernel's item order (0:
-// plain order).
+// plain order), and in the eight-pair kernel's.
 #ifndef K3G_F4Q_GROUP
 #define K3G_F4Q_GROUP 4
+#endif
+#ifndef K3G_F4S_GROUP
+#define K3G_F4S_GROUP 4
 #endif
 
 namespace k3g {
@@ -143,6 +146,15 @@ int launch_split(uint8_t *dst, const float *src, int n_vec, int len, int src_str
 // stores nothing. (Its loads stay in range: a load past a buffer's range
 // returns at once, possibly before older loads, and the counted waits here
 // assume loads complete in the order they were issued.)
+
+// Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups round the
+// XCDs). In a grid of whole rounds of 8 groups of gi consecutive items, group
+// g goes to XCD g % 8: workgroup b takes item xcd_item(b, gi). Items past the
+// end exit.
+__device__ inline int xcd_item(int b, int gi) {
+    const int x = b % 8, loc = b / 8;
+    return (x + 8 * (loc / gi)) * gi + loc % gi;
+}
 
 // UP:   tiles (w1, rows r0..r0+15), (w3, r0..r0+15), (w1, r0+16..), (w3, r0+16..);
 //       h[pos][r] = SiTU(g, u) for the 32 rows, and the 16 pieces of this
@@ -371,13 +383,16 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n_out = UP ? inter : latent;
     const int row_blocks = (n_out / f4::kRows + f4::kWaves - 1) / f4::kWaves;
-    const int k = blockIdx.x / row_blocks;
+    // (plain order: about one pair per expert leaves nothing for XCD groups of
+    // passes to share; they measured slower here)
+    const int item = (int)blockIdx.x;
+    const int k = item / row_blocks;
     if (k >= passes[0]) return;  // whole workgroup
     const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
     const int e = active[1 + slot];
     const int p0 = offsets[e] + pass * NPP;
     const int np = min(NPP, offsets[e + 1] - p0);
-    const int blk32 = (blockIdx.x - k * row_blocks) * f4::kWaves + wave;
+    const int blk32 = (item - k * row_blocks) * f4::kWaves + wave;
     const bool live = blk32 < n_out / f4::kRows;
 
     // the wavefront's tiles: buffer resources, and this lane's row offsets
@@ -552,9 +567,10 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
 // 32 rows; DOWN: 64 rows). The loop runs chunk by chunk over all four tiles,
 // so each B fragment read from LDS feeds four products and each A fragment
 // four (one per pair): 16 products per chunk for 4 A and 4 B fragments.
-// Operand A streams through a 3-deep ring of 2-chunk blocks, each block's
-// scale dwords with it (one 16-byte load a row covers two blocks); B of the
-// next chunk is read while this chunk's products issue.
+// Operand A streams through a 3-deep ring of 2-chunk blocks; an item's scale
+// bytes come in two 16-byte loads a tile, handed to the lanes chunk by chunk
+// by ds_bpermute; B of the next chunk is read while this chunk's products
+// issue.
 //
 // The grid is persistent: one workgroup per CU (the LDS holds one), walking
 // the items (pass, row block), row blocks fastest, gridDim apart. When an
@@ -628,15 +644,28 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         }
     };
     uint4 A[NBUF][TILES][CPB];
-    uint4 S[2][TILES];  // scale dwords of blocks 2m and 2m + 1 in S[m % 2]
     auto load_block = [&](int kb) {
         const int b = kb % NBUF;
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) {
+        for (int t = 0; t < TILES; ++t)
 #pragma unroll
             for (int c = 0; c < CPB; ++c)
                 A[b][t][c] = buf_load16(rp[t], vp[t], (uint32_t)(CPB * kb + c) * 64u);
-            if (kb % 2 == 0) S[(kb / 2) % 2][t] = buf_load16(rs[t], vs[t], (uint32_t)(CPB * kb) * 4u);
+    };
+    // The item's scale bytes, once: lane (r, q) of a tile holds bytes
+    // [16 (q + 4j), +16) of row r in SW[j] (4 lanes, 64 bytes a row per load;
+    // a window past the row's last byte -- never read -- is moved back into
+    // it, so no load leaves the matrix). Chunk i's group q of row r, byte
+    // 4i + q, then sits in lane (r, (i / 4) % 4), window i / 16, dword i % 4,
+    // byte q: one ds_bpermute a tile and chunk brings it to lane (r, q).
+    constexpr int NSW = (NCK + 15) / 16;
+    uint4 SW[NSW][TILES];
+    auto load_sw = [&]() {
+#pragma unroll
+        for (int j = 0; j < NSW; ++j) {
+            const uint32_t off = (uint32_t)min(16 * ((lane >> 4) + 4 * j), ngrp - 16);
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) SW[j][t] = buf_load16(rs[t], vs[t] + off, 0u);
         }
     };
     // B: the item's four vectors of pieces into LDS (a short pass repeats its
@@ -658,6 +687,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         load_b();
         __asm__ volatile("" ::: "memory");  // the weight loads stay after the DMA
         __builtin_amdgcn_sched_barrier(0);
+        load_sw();
 #pragma unroll
         for (int kb = 0; kb < PRO; ++kb) load_block(kb);
     };
@@ -680,11 +710,23 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
             for (int t = 0; t < TILES; ++t) acc[q][t] = float4_t{0.f, 0.f, 0.f, 0.f};
         uint4 Bv[2][NPP];
         uint32_t Bs[2][NPP];
+        // chunk i's scale dword per tile (byte q is lane (r, q)'s), brought in at
+        // the chunk's start (two of them, held a chunk ahead, spill registers)
+        uint32_t Sd[1][TILES];
         auto read_b = [&](int i) {
 #pragma unroll
             for (int q = 0; q < NPP; ++q) {
                 Bv[i & 1][q] = bq[(q * VEC + i * f4::kChunkBytes) / 16];
                 Bs[i & 1][q] = sq[(q * VEC + i * f4::kChunkBytes) / 4];
+            }
+        };
+        auto read_s = [&](int i) {
+            const int src = 4 * ((lane & 15) + 16 * ((i / 4) % 4));  // byte address of the source lane
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) {
+                const uint4 w = SW[i / 16][t];
+                const uint32_t d = i % 4 == 0 ? w.x : i % 4 == 1 ? w.y : i % 4 == 2 ? w.z : w.w;
+                Sd[0][t] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)d);
             }
         };
         read_b(0);
@@ -693,13 +735,11 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
             const int kb = i / CPB, c = i % CPB, b = kb % NBUF;
             if (c == 0 && kb + NBUF - 1 < NB) load_block(kb + NBUF - 1);
             if (i + 1 < NCK) read_b(i + 1);
+            read_s(i);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < TILES; ++t) {
-                const uint4 s4 = S[(kb / 2) % 2][t];
-                const int sw = 2 * (kb % 2) + c;
-                const uint32_t sd = sw == 0 ? s4.x : sw == 1 ? s4.y : sw == 2 ? s4.z : s4.w;
-                const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
+                const uint32_t sa = __builtin_amdgcn_ubfe(Sd[0][t], qsh, 8);
                 const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
                 const uint4 a = A[b][t][c];
                 const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
@@ -822,17 +862,18 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n_out = UP ? inter : latent;
     const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
-    // workgroup = (pass, row block), row blocks fastest: the workgroups running
-    // at once cover every row block of a few passes (an order with the passes
-    // fastest, for L2 sharing between the passes of one expert, measured
-    // slower: all of them then read the same rows of different experts)
-    const int k = blockIdx.x / row_blocks;
+    // workgroup = (pass, row block), row blocks fastest within groups of
+    // K3G_F4S_GROUP consecutive passes, each group on one XCD: the row blocks
+    // of a pass share its B, and the passes of one expert its weights, through
+    // that XCD's L2 (the launch rounds the grid to whole rounds of 8 groups)
+    const int item = xcd_item((int)blockIdx.x, K3G_F4S_GROUP * row_blocks);
+    const int k = item / row_blocks;
     if (k >= passes[0]) return;  // whole workgroup
     const int slot = passes[1 + 2 * k], pass = passes[2 + 2 * k];
     const int e = active[1 + slot];
     const int p0 = offsets[e] + pass * NPP;
     const int np = min(NPP, offsets[e + 1] - p0);
-    const int r0 = ((blockIdx.x - k * row_blocks) * WAVES + wave) * ROWS_W;
+    const int r0 = ((item - k * row_blocks) * WAVES + wave) * ROWS_W;
     const bool live = r0 < n_out;
 
     const uint8_t *eb = bank.base + (int64_t)e * bank.stride;
@@ -1071,9 +1112,13 @@ static int launch_f4m(int npp, float *out, const uint8_t *pieces, uint8_t *hp, c
     const int64_t grid = max_passes * row_blocks;
     if (grid == 0) return K3G_OK;
     if (grid > 0x7fffffff) return K3G_EUNSUPPORTED;
+    // the eight-pair kernel: whole rounds of 8 XCD groups
+    const int64_t round8 = 8 * (int64_t)K3G_F4S_GROUP * row_blocks;
+    const int64_t gridx = (grid + round8 - 1) / round8 * round8;
+    if (gridx > 0x7fffffff) return K3G_EUNSUPPORTED;
     const size_t lds = (size_t)npp * NCK * f4::kChunkBytes;  // above the 64 KB default from 26 chunks on
     if (npp == 8) {
-        moe_f4s_kernel<UP, NCK><<<(unsigned)grid, 8 * kWave, 0, st>>>(out, pieces, hp, bank, active, offsets, perm,
+        moe_f4s_kernel<UP, NCK><<<(unsigned)gridx, 8 * kWave, 0, st>>>(out, pieces, hp, bank, active, offsets, perm,
                                                                      passes, top_k, latent, inter);
     } else if (npp == 4) {
         if (lds > 65536 && hipFuncSetAttribute((const void *)moe_f4q_kernel<UP, NCK>,
