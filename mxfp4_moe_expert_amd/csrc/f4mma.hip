@@ -52,9 +52,12 @@
 #define K3G_F4_NBUF 6
 #endif
 // Consecutive passes per XCD group in the four-pair kernel's item order (0:
-// plain order), and in the eight-pair kernel's.
+// plain order; the up-projection's own), and in the eight-pair kernel's.
 #ifndef K3G_F4Q_GROUP
 #define K3G_F4Q_GROUP 4
+#endif
+#ifndef K3G_F4Q_GROUP_UP
+#define K3G_F4Q_GROUP_UP 8
 #endif
 #ifndef K3G_F4S_GROUP
 #define K3G_F4S_GROUP 4
@@ -605,16 +608,23 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     // passes (all their row blocks), group g on XCD g % 8, so the row blocks
     // of a pass share its B, and the passes of one expert its weights,
     // through that XCD's L2
-    constexpr int G = K3G_F4Q_GROUP;
+    constexpr int G = UP ? K3G_F4Q_GROUP_UP : K3G_F4Q_GROUP;
     const bool xcd = G > 0 && gridDim.x % 8 == 0;
     const int per = xcd ? (int)gridDim.x / 8 : (int)gridDim.x;
     const int gi = G * row_blocks;
+    // Where a group's items divide evenly among the XCD's workgroups, each
+    // takes a run of ipw consecutive items (row blocks of one pass, mostly),
+    // and loads the pass's B once for the run.
+    const bool runs = xcd && gi % per == 0;
+    const int ipw = runs ? gi / per : 1;
     auto item_at = [&](int L) {  // the workgroup's L-th item (its own sequence)
         if (!xcd) return L;
         const int x = (int)blockIdx.x % 8;
+        if (runs) return (x + 8 * (L / ipw)) * gi + ((int)blockIdx.x / 8) * ipw + L % ipw;
         return (x + 8 * (L / gi)) * gi + L % gi;
     };
-    int loc = xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
+    const int step_loc = runs ? 1 : per;
+    int loc = !xcd ? (int)blockIdx.x : runs ? 0 : (int)blockIdx.x / 8;
     int item = item_at(loc);
     if (item >= n_items) return;  // whole workgroup
 
@@ -683,8 +693,8 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         }
     };
     constexpr int PRO = NBUF - 1 < NB ? NBUF - 1 : NB;
-    auto prologue = [&]() {
-        load_b();
+    auto prologue = [&](bool with_b) {
+        if (with_b) load_b();
         __asm__ volatile("" ::: "memory");  // the weight loads stay after the DMA
         __builtin_amdgcn_sched_barrier(0);
         load_sw();
@@ -692,7 +702,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         for (int kb = 0; kb < PRO; ++kb) load_block(kb);
     };
     setup(item);
-    prologue();
+    prologue(true);
     wait_vm<0>();
     __syncthreads();
 
@@ -761,12 +771,13 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         // this item's epilogue inputs; then the next item's first loads
         const int cp0 = p0, cnp = np, cr0 = r0;
         const bool clive = live;
-        const int next = item_at(loc + per);
+        const int next = item_at(loc + step_loc);
         const bool more = next < n_items;
+        const bool same_b = next / row_blocks == item / row_blocks;  // the same pass: B stays
         __syncthreads();  // every wavefront has read its last chunk of B
         if (more) {
             setup(next);
-            prologue();
+            prologue(!same_b);
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -834,7 +845,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
         wait_vm<0>();
         __syncthreads();
         item = next;
-        loc += per;
+        loc += step_loc;
     }
 }
 
