@@ -64,8 +64,11 @@ int dense_t64(int T);
 bool dense_mfma_ok(int T, int N, const int *K, int n_seg);
 int dense_slices(int T, int N, int K_total, bool glu);
 int launch_split3(uint8_t *xb, const float *x, int T, int K, int ld, hipStream_t st);
+int launch_combine_norm(float *agg, float *nrm, uint8_t *xb, const float *ypair, const float *wts,
+                        const int32_t *inv, const float *gamma, int T, int top_k, int len, float eps,
+                        hipStream_t st);
 int launch_dense_mfma(float *out, uint8_t *xb_out, float *part, const uint16_t *const *w, const uint8_t *const *xb,
-                      const int *K, int n_seg, const uint16_t *w3, int T, int N, hipStream_t st);
+                      const int *K, int n_seg, const uint16_t *w3, int T, int N, hipStream_t st, uint8_t *xp_out = nullptr);
 }  // namespace k3g
 
 using namespace k3g;
@@ -617,24 +620,40 @@ extern "C" int k3g_latent_moe_block(float *out, const float *x, const k3g_block_
     uint8_t *dxh = (uint8_t *)(b + L.dxh), *dxl = (uint8_t *)(b + L.dxl), *dxs = (uint8_t *)(b + L.dxs);
     float *dpart = (float *)(b + L.dpart);
     const size_t t64 = (size_t)dense_t64(T);
+    // does the routed layer split lat into e2m1 pieces (FP4 matrix cores)?
+    const bool f4x = dp.down && T > 1 && f4_layer(mode, T, latent, bank->inter) && f4_bank_ok(bank_dev(*bank)) &&
+                     L.xp && L.hp && L.passes && latent % 128 == 0;
+    uint8_t *xp = (uint8_t *)(b + L.xp);
     // down-projection into the latent space
     if (dp.down) {
         K3G_TRY(launch_split3(dxh, x, T, hidden, hidden, st));
         const uint16_t *wd[1] = {w->w_down};
         const uint8_t *xd[1] = {dxh};
         const int kd[1] = {hidden};
-        K3G_TRY(launch_dense_mfma(lat, nullptr, dpart, wd, xd, kd, 1, nullptr, T, latent, st));
+        // the FP4 layer's e2m1 pieces of lat from the same reduction (its
+        // split stage then has nothing to do)
+        K3G_TRY(launch_dense_mfma(lat, nullptr, dpart, wd, xd, kd, 1, nullptr, T, latent, st, f4x ? xp : nullptr));
     } else {
         const DenseSeg down = {w->w_down, x, hidden};
         K3G_TRY(launch_dense(lat, &down, 1, T, latent, st));
     }
-    // the routed experts on the latent tokens
-    for (int stage = K3G_STAGE_BUCKET; stage <= K3G_STAGE_COMBINE; ++stage)
-        K3G_TRY(layer_stage(stage, L, agg, lat, idx, wts, bank, T, top_k, mode, ws, st));
-    // RMSNorm of the aggregate, the shared experts, and the up-projection
-    K3G_TRY(launch_rmsnorm(nrm, agg, w->gamma, T, latent, w->rms_eps, st));
+    // the routed experts on the latent tokens; on the matrix-core path their
+    // combine, the RMSNorm of the aggregate and the pieces of the normed
+    // aggregate for the up-projection are one kernel
+    const bool fused = dp.up && latent % 32 == 0 && latent <= 4096;
+    const int last = fused ? K3G_STAGE_DOWN : K3G_STAGE_COMBINE;
+    for (int stage = K3G_STAGE_BUCKET; stage <= last; ++stage)
+        if (!(f4x && stage == K3G_STAGE_QUANT_X))
+            K3G_TRY(layer_stage(stage, L, agg, lat, idx, wts, bank, T, top_k, mode, ws, st));
+    if (fused) {
+        K3G_TRY(launch_combine_norm(agg, nrm, dxl, (const float *)(b + L.ypair), wts, (const int32_t *)(b + L.inv),
+                                    w->gamma, T, top_k, latent, w->rms_eps, st));
+    } else {
+        K3G_TRY(launch_rmsnorm(nrm, agg, w->gamma, T, latent, w->rms_eps, st));
+    }
+    // the shared experts and the up-projection
     if (dp.up) {
-        K3G_TRY(launch_split3(dxl, nrm, T, latent, latent, st));
+        if (!fused) K3G_TRY(launch_split3(dxl, nrm, T, latent, latent, st));
         const uint16_t *wu[3] = {w->w_up, nullptr, nullptr};
         const uint8_t *xu[3] = {dxl, nullptr, nullptr};
         int ku[3] = {latent, 0, 0};

@@ -235,6 +235,87 @@ __global__ __launch_bounds__(256) void split3_kernel(uint8_t *__restrict__ xb, c
     store_pieces8(xb, K / 32, t, c, v);
 }
 
+int dense_t64(int T);
+
+// ---- combine, RMSNorm and the up-projection's pieces in one pass ------------------
+// agg[t] = sum over k of wts[t][k] * ypair[inv[t][k]] (the layer's combine: fma
+// in k order, a dropped pair adding nothing), n[t] = agg[t] / sqrt(mean(agg^2)
+// + eps) * gamma as rmsnorm_kernel, and the three bf16 pieces of n (zero for
+// the padding tokens T..T64-1). One workgroup a token; thread c takes entries
+// 8c..8c+7 (len a multiple of 8, at most 4096).
+__global__ __launch_bounds__(512) void combine_norm_kernel(float *__restrict__ agg, float *__restrict__ nrm,
+                                                           uint8_t *__restrict__ xb, const float *__restrict__ ypair,
+                                                           const float *__restrict__ wts,
+                                                           const int32_t *__restrict__ inv,
+                                                           const float *__restrict__ gamma, int T, int top_k,
+                                                           int len, float eps) {
+    __shared__ float part[8];
+    const int t = blockIdx.x, c = threadIdx.x;
+    const int nc = len / 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t >= T) {  // padding token: zero pieces
+        if (c < nc) store_pieces8(xb, len / 32, t, c, v);
+        return;
+    }
+    if (c < nc) {
+        for (int k0 = 0; k0 < top_k; k0 += 8) {
+            float w[8];
+            float4 a[8], b[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {  // a block's loads go out before its sums
+                const int k = min(k0 + kk, top_k - 1);
+                const int pos = inv[t * top_k + k];
+                const bool live = k0 + kk < top_k && pos >= 0;
+                const float *src = ypair + (size_t)(pos >= 0 ? pos : 0) * len + 8 * c;
+                const float4 a0 = *(const float4 *)src, b0 = *(const float4 *)(src + 4);
+                w[kk] = live ? wts[t * top_k + k] : 0.0f;
+                a[kk] = live ? a0 : make_float4(0.f, 0.f, 0.f, 0.f);
+                b[kk] = live ? b0 : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                v[0] = __builtin_fmaf(w[kk], a[kk].x, v[0]);
+                v[1] = __builtin_fmaf(w[kk], a[kk].y, v[1]);
+                v[2] = __builtin_fmaf(w[kk], a[kk].z, v[2]);
+                v[3] = __builtin_fmaf(w[kk], a[kk].w, v[3]);
+                v[4] = __builtin_fmaf(w[kk], b[kk].x, v[4]);
+                v[5] = __builtin_fmaf(w[kk], b[kk].y, v[5]);
+                v[6] = __builtin_fmaf(w[kk], b[kk].z, v[6]);
+                v[7] = __builtin_fmaf(w[kk], b[kk].w, v[7]);
+            }
+        }
+        float *dst = agg + (size_t)t * len + 8 * c;
+        *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4 *)(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
+    ss = wave_sum(ss);
+    if ((c & (kWave - 1)) == 0) part[c / kWave] = ss;
+    __syncthreads();
+    const float tot = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+    const float rms = sqrtf(tot / (float)len + eps);
+    if (c < nc) {
+        float n[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) n[j] = v[j] / rms * gamma[8 * c + j];
+        float *dst = nrm + (size_t)t * len + 8 * c;
+        *(float4 *)dst = make_float4(n[0], n[1], n[2], n[3]);
+        *(float4 *)(dst + 4) = make_float4(n[4], n[5], n[6], n[7]);
+        store_pieces8(xb, len / 32, t, c, n);
+    }
+}
+
+int launch_combine_norm(float *agg, float *nrm, uint8_t *xb, const float *ypair, const float *wts,
+                        const int32_t *inv, const float *gamma, int T, int top_k, int len, float eps,
+                        hipStream_t st) {
+    if (T == 0) return K3G_OK;
+    if (len % 32 || len > 4096 || top_k < 1) return K3G_EUNSUPPORTED;
+    combine_norm_kernel<<<dense_t64(T), 512, 0, st>>>(agg, nrm, xb, ypair, wts, inv, gamma, T, top_k, len, eps);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
 template <bool GLU>
 __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(DenseMArgs a) {
     using namespace dm;
@@ -486,8 +567,12 @@ int launch_split3(uint8_t *xb, const float *x, int T, int K, int ld, hipStream_t
 
 // out (+ pieces of out when xb_out) = sum over segments of W_s x_s; GLU (one
 // segment, w3 given): out = SiTU(W1 x, W3 x). part holds S * G * T * N floats.
+int launch_reduce_split(float *out, uint8_t *dst, const float *part, int S, int T, int len, hipStream_t st);
+
+// xp_out (not with GLU or xb_out): also the e2m1 pieces of out, as the FP4
+// layer's split writes them, from the same reduction.
 int launch_dense_mfma(float *out, uint8_t *xb_out, float *part, const uint16_t *const *w, const uint8_t *const *xb,
-                      const int *K, int n_seg, const uint16_t *w3, int T, int N, hipStream_t st) {
+                      const int *K, int n_seg, const uint16_t *w3, int T, int N, hipStream_t st, uint8_t *xp_out) {
     if (T == 0) return K3G_OK;
     if (n_seg < 1 || n_seg > dm::kMaxSeg || (w3 && n_seg != 1) || !dense_mfma_ok(T, N, K, n_seg) ||
         (xb_out && N % 64))  // the pieces feed a product whose K is this N
@@ -523,6 +608,7 @@ int launch_dense_mfma(float *out, uint8_t *xb_out, float *part, const uint16_t *
     else dense_mfma_kernel<false><<<grid, dm::kWaves * kWave, 0, st>>>(a);
     if (hipGetLastError() != hipSuccess) return K3G_EHIP;
     const int64_t n = (int64_t)dense_t64(T) * (N / 8);
+    if (xp_out && !glu && !xb_out) return launch_reduce_split(out, xp_out, part, a.S, T, N, st);
     if (glu) dense_reduce_kernel<true><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(out, xb_out, part, a.S, T,
                                                                                    dense_t64(T), N);
     else dense_reduce_kernel<false><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(out, xb_out, part, a.S, T,

@@ -134,6 +134,31 @@ __global__ __launch_bounds__(256) void split_kernel(uint8_t *__restrict__ dst, c
     split_group(r, dst + (size_t)v * (ngrp / 4) * f4::kChunkBytes + (g >> 2) * f4::kChunkBytes, g & 3, live);
 }
 
+// The sum of S partial products [S][T][len] (slices added in order, as the
+// dense products' reduction does) into out [T][len], and its pieces, as
+// split_kernel writes them, into dst. One half-wavefront per 32-entry group.
+__global__ __launch_bounds__(256) void reduce_split_kernel(float *__restrict__ out, uint8_t *__restrict__ dst,
+                                                           const float *__restrict__ part, int S, int T, int ngrp) {
+    const int64_t gid = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
+    const bool live = gid < (int64_t)T * ngrp;
+    const int t = live ? (int)(gid / ngrp) : 0, g = live ? (int)(gid - (int64_t)t * ngrp) : 0;
+    const int len = ngrp * kGroup;
+    const int n = g * kGroup + (threadIdx.x & 31);
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[((size_t)s * T + t) * len + n];
+    if (live) out[(size_t)t * len + n] = v;
+    split_group(v, dst + (size_t)t * (ngrp / 4) * f4::kChunkBytes + (g >> 2) * f4::kChunkBytes, g & 3, live);
+}
+
+int launch_reduce_split(float *out, uint8_t *dst, const float *part, int S, int T, int len, hipStream_t st) {
+    const int ngrp = len / kGroup;
+    const int64_t groups = (int64_t)T * ngrp;
+    if (groups == 0) return K3G_OK;
+    if (len % 128) return K3G_EUNSUPPORTED;
+    reduce_split_kernel<<<(unsigned)((groups + 7) / 8), 256, 0, st>>>(out, dst, part, S, T, ngrp);
+    return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
+}
+
 int launch_split(uint8_t *dst, const float *src, int n_vec, int len, int src_stride, hipStream_t st) {
     const int ngrp = len / kGroup;
     const int groups = n_vec * ngrp;
