@@ -491,10 +491,15 @@ def run_block(ctx, bank, reps=10, form=None):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # the routed layer's distinct experts (from the routing the block wrote)
+    L = k3g.workspace_layout(k3g.OP_LATENT_BLOCK, sh)
+    idx = ws[L["idx"]: L["idx"] + 4 * T * K].view(torch.int32).cpu().numpy()
+    distinct = int(len(set(idx.tolist()) - {-1}))
     # dense matrix work: down, up, and per shared expert w1, w3 and w2 (2 flops per product)
     flops = 2.0 * T * (2 * H * Lt + 2 * 3 * H * SI)
     out_d = {"tokens": T, "layer": "vector" if form == "vector" else "fp4-mfma",
              "ms_per_block": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+             "distinct_experts": distinct,
              "dense_flops": flops, "dense_TFLOPs_if_all_time": round(flops / (ms * 1e-3) / 1e12, 1)}
     del dense, ws, out, x
     torch.cuda.empty_cache()
