@@ -159,16 +159,19 @@ int launch_rmsnorm(float *n, const float *a, const float *gamma, int T, int len,
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 namespace dm {
-constexpr int kWaves = 4;
-constexpr int kTok = 64;        // tokens per workgroup
+constexpr int kTok = 64;        // token padding (and the small tile's tokens)
 constexpr int kKB = 64;         // entries per block (two steps)
 constexpr int kStepBytes = 3 * 1024;           // one token tile, one step, three pieces
-constexpr int kBlockB = 4 * 2 * kStepBytes;    // 24 KB: one block of operand B
 #ifndef K3G_DENSE_NBUF
 #define K3G_DENSE_NBUF 3
 #endif
-constexpr int kNBUF = K3G_DENSE_NBUF;  // operand-A ring depth (blocks)
+constexpr int kNBUF = K3G_DENSE_NBUF;  // operand-A ring depth (blocks), small tile
 constexpr int kMaxSeg = 3;
+// Two tiles: W = 4 wavefronts x (64 rows, 64 tokens), two workgroups a CU;
+// W = 8 wavefronts x (64 rows, 128 tokens), one workgroup a CU (96 KB of
+// LDS), which loads half the bytes per product: the weights once per 128
+// tokens, the activations' pieces once per 512 rows.
+constexpr int block_b(int W) { return W * 2 * kStepBytes; }  // one block of operand B
 }  // namespace dm
 
 struct DenseMSeg {
@@ -316,10 +319,15 @@ int launch_combine_norm(float *agg, float *nrm, uint8_t *xb, const float *ypair,
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;
 }
 
-template <bool GLU>
-__global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(DenseMArgs a) {
+// W wavefronts, each with 64 output rows (GLU: 32 of W1 and the same 32 of W3)
+// and W token tiles of 16; the workgroup's W token tiles of operand B are
+// staged in LDS, wavefront w bringing tile w.
+template <bool GLU, int W>
+__global__ __launch_bounds__(W * kWave, 8 / W) void dense_mfma_kernel(DenseMArgs a) {
     using namespace dm;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockB];
+    constexpr int kBlockB = block_b(W);
+    constexpr int NB = W == 8 ? 2 : kNBUF;  // the big tile: 128 accumulators, a 2-deep ring
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * kBlockB
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // XCD-aware order: consecutive workgroups go round the 8 XCDs, so item
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
     const int sl = rest % a.S, rb = rest / a.S;
     const int kb0 = (int)((int64_t)a.nkb * sl / a.S), kb1 = (int)((int64_t)a.nkb * (sl + 1) / a.S);
     constexpr int ROWS_W = GLU ? 32 : 64;  // output rows per wavefront
-    const int r0 = (rb * kWaves + wave) * ROWS_W;
+    const int r0 = (rb * W + wave) * ROWS_W;
 
     // operand A: four tiles of 16 rows; lane (i = l%16, q = l/16) reads 16 B at
     // entry 8q of a step for row i of its tile
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
                           (uint32_t)((s < a.n_seg ? (uint64_t)a.seg[s].K : 0) * 2 * (uint64_t)a.N));
     ra3 = make_rsrc(GLU ? a.w3 : a.seg[0].w, GLU ? (uint32_t)((uint64_t)a.seg[0].K * 2 * a.N) : 0u);
     auto seg_of = [&](int kb) { return kb >= a.kb_start[2] ? 2 : kb >= a.kb_start[1] ? 1 : 0; };
-    uint4 A[kNBUF][4][2];
+    uint4 A[NB][4][2];
     // Block kb of A into ring slot `slot`. Issued on every step, also where
     // there is no block left to fetch (then block kb is the current one,
     // loaded again into the free slot): the compiler's waits for a slot then
@@ -359,7 +367,9 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
         const uint32_t soff = 128u * (uint32_t)(kb - a.kb_start[s]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = r0 + (GLU ? 16 * (i & 1) : 16 * i) + (lane & 15);
+            // rows past N (the last row block) read row N - 1 and store nothing:
+            // the wavefront's counted waits also cover the B tile it brings
+            const int row = min(r0 + (GLU ? 16 * (i & 1) : 16 * i) + (lane & 15), a.N - 1);
             const uint32_t v = (uint32_t)row * K2 + 16u * (uint32_t)(lane >> 4);
             const rsrc_t r = (GLU && i >= 2) ? ra3 : (s == 0 ? ra[0] : s == 1 ? ra[1] : ra[2]);
 #pragma unroll
@@ -371,18 +381,18 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
     auto dma_b = [&](int kb, int buf) {
         const int s = seg_of(kb);
         const int nks = a.seg[s].K / 32;
-        const int ttg = tb * 4 + wave;
+        const int ttg = tb * W + wave;
         const uint8_t *src = a.seg[s].xb + ((size_t)ttg * nks + 2 * (kb - a.kb_start[s])) * kStepBytes;
 #pragma unroll
         for (int j = 0; j < 6; ++j)
             dma16(src, 1024u * j + 16u * lane, lb + (uint32_t)(buf * kBlockB + wave * 2 * kStepBytes + 1024 * j));
     };
 
-    float4_t acc[4][4];
+    float4_t acc[4][W];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < W; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
     int li = lane;
     __asm__ volatile("" : "+v"(li));
@@ -392,16 +402,16 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
         const uint4 *bb = (const uint4 *)(lds + buf * kBlockB) + li;
         __asm__ volatile("" ::: "memory");
         bf16x8_t B[2][3];
-        auto read_b = [&](int it) {  // it = 4 * step + token tile
-            const int st = it / 4, t = it % 4;
+        auto read_b = [&](int it) {  // it = W * step + token tile
+            const int st = it / W, t = it % W;
 #pragma unroll
             for (int p = 0; p < 3; ++p) B[it & 1][p] = __builtin_bit_cast(bf16x8_t, bb[((t * 2 + st) * 3 + p) * 64]);
         };
         read_b(0);
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int st = it / 4, t = it % 4;
-            if (it + 1 < 8) read_b(it + 1);
+        for (int it = 0; it < 2 * W; ++it) {
+            const int st = it / W, t = it % W;
+            if (it + 1 < 2 * W) read_b(it + 1);
             __builtin_amdgcn_sched_barrier(0);  // the reads go out ahead of the products
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < kNBUF - 1; ++j) load_a(min(kb0 + j, kb1 - 1), j);
+        for (int j = 0; j < NB - 1; ++j) load_a(min(kb0 + j, kb1 - 1), j);
         wait_vm<0>();
         __syncthreads();
     }
@@ -428,13 +438,13 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
     // in LDS (vmcnt: only the 8 A loads, issued after the DMA, may still be in
     // flight), and every wavefront is done with this buffer before it is
     // filled again
-    auto step = [&](int k, int j) {  // j = (k - kb0) % kNBUF
+    auto step = [&](int k, int j) {  // j = (k - kb0) % NB
         const int buf = (k - kb0) & 1;
         if (k + 1 < kb1) dma_b(k + 1, buf ^ 1);
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        const bool na = k + kNBUF - 1 < kb1;
-        load_a(na ? k + kNBUF - 1 : k, (j + kNBUF - 1) % kNBUF);
+        const bool na = k + NB - 1 < kb1;
+        load_a(na ? k + NB - 1 : k, (j + NB - 1) % NB);
         __builtin_amdgcn_sched_barrier(0);
         compute(j, buf);
         __builtin_amdgcn_sched_barrier(0);
@@ -449,30 +459,30 @@ __global__ __launch_bounds__(dm::kWaves * kWave, 2) void dense_mfma_kernel(Dense
     };
     // whole rounds of the ring (every ring slot static, no branch inside),
     // then the last one or two blocks
-    const int nblk = kb1 - kb0, nround = nblk / kNBUF;
+    const int nblk = kb1 - kb0, nround = nblk / NB;
     for (int rd = 0; rd < nround; ++rd) {
-        const int kb = kb0 + rd * kNBUF;
+        const int kb = kb0 + rd * NB;
 #pragma unroll
-        for (int j = 0; j < kNBUF; ++j) step(kb + j, j);
+        for (int j = 0; j < NB; ++j) step(kb + j, j);
     }
-    const int kt = kb0 + nround * kNBUF;
+    const int kt = kb0 + nround * NB;
 #pragma unroll
-    for (int j = 0; j < kNBUF - 1; ++j)
+    for (int j = 0; j < NB - 1; ++j)
         if (kt + j < kb1) step(kt + j, j);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) __asm__ volatile("" : "+v"(acc[i][t]));
+        for (int t = 0; t < W; ++t) __asm__ volatile("" : "+v"(acc[i][t]));
 
     // lane l holds token 16t + l%16 and rows 4(l/16)..+3 of each tile
-    const int tok0 = tb * kTok + (lane & 15);
+    const int tok0 = tb * 16 * W + (lane & 15);
     const int G = GLU ? 2 : 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int g = GLU ? i >> 1 : 0;
         const int n = r0 + (GLU ? 16 * (i & 1) : 16 * i) + 4 * (lane >> 4);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < W; ++t) {
             const int tok = tok0 + 16 * t;
             if (tok < a.T && n < a.N) {
                 float *dst = a.part + (((size_t)sl * G + g) * a.T + tok) * a.N + n;
@@ -534,24 +544,34 @@ bool dense_mfma_ok(int T, int N, const int *K, int n_seg) {
     return true;
 }
 
-// Slices of K. A cost model in block-steps of the busiest CU: the items
-// (tiles x slices) spread evenly over the chip's 256 CUs; the busiest runs
-// ceil(items / 256) of them, each ceil(nkb / S) blocks plus about two for its
-// prologue and partial stores, and a CU with one workgroup is counted as slow
-// as with two (one wavefront a SIMD leaves the matrix cores half idle). The
-// partials' round trip (written, then read by the reduction) adds about one
-// block-step per 4 MB. At least 4 blocks a slice.
+// The tile: 128 tokens a workgroup where the padded batch is a whole number
+// of them, else 64.
+static int dense_w(int T) { return dense_t64(T) % 128 == 0 ? 8 : 4; }
+
+// Slices of K. A cost model in block-steps of the busiest CU, a block-step
+// being one workgroup's block of the small tile (four wavefronts' products on
+// one block of 64 entries): the items (tiles x slices) spread evenly over the
+// chip's 256 CUs; the busiest runs ceil(items / 256) of them, each ceil(nkb /
+// S) blocks plus about two for its prologue and partial stores. Small tile: a
+// CU with one workgroup is counted as slow as with two (one wavefront a SIMD
+// leaves the matrix cores half idle). Big tile: one workgroup a CU, each block
+// four block-steps of work. The partials' round trip (written, then read by
+// the reduction) adds about one block-step per 4 MB. At least 4 blocks a
+// slice.
 int dense_slices(int T, int N, int K_total, bool glu) {
-    const int rows_wg = dm::kWaves * (glu ? 32 : 64);
-    const int64_t tiles = (int64_t)((N + rows_wg - 1) / rows_wg) * (dense_t64(T) / dm::kTok);
+    const int W = dense_w(T);
+    const int rows_wg = W * (glu ? 32 : 64);
+    const int64_t tiles = (int64_t)((N + rows_wg - 1) / rows_wg) * (dense_t64(T) / (16 * W));
     const int nkb = K_total / dm::kKB;
     const int max_s = nkb / 4 > 1 ? nkb / 4 : 1;
     const double part_bytes = 8.0 * (glu ? 2 : 1) * (double)dense_t64(T) * N;  // per slice, both ways
     int best = 1;
     double best_cost = 1e300;
     for (int s = 1; s <= max_s; ++s) {
-        const int64_t per_cu = std::max<int64_t>((tiles * s + 255) / 256, 2);
-        const double cost = (double)per_cu * ((nkb + s - 1) / s + 2) + s * part_bytes / (4.0 * (1 << 20));
+        const int64_t rounds = (tiles * s + 255) / 256;
+        const double work = W == 8 ? 4.0 * (double)rounds * ((nkb + s - 1) / s + 1)
+                                   : (double)std::max<int64_t>(rounds, 2) * ((nkb + s - 1) / s + 2);
+        const double cost = work + s * part_bytes / (4.0 * (1 << 20));
         if (cost < best_cost) best_cost = cost, best = s;
     }
     return best;
@@ -597,15 +617,26 @@ int launch_dense_mfma(float *out, uint8_t *xb_out, float *part, const uint16_t *
     a.T = T;
     a.nkb = kt / dm::kKB;
     a.S = dense_slices(T, N, kt, glu);
-    const int rows_wg = dm::kWaves * (glu ? 32 : 64);
+    const int W = dense_w(T);
+    const int rows_wg = W * (glu ? 32 : 64);
     a.row_blocks = (N + rows_wg - 1) / rows_wg;
-    a.tok_blocks = dense_t64(T) / dm::kTok;
+    a.tok_blocks = dense_t64(T) / (16 * W);
     const int64_t items = (int64_t)a.row_blocks * a.S * a.tok_blocks;
     if (items > (1 << 30)) return K3G_EUNSUPPORTED;
     a.n_items = (int)items;
     const unsigned grid = (unsigned)((items + 7) / 8 * 8);  // a whole number per XCD
-    if (glu) dense_mfma_kernel<true><<<grid, dm::kWaves * kWave, 0, st>>>(a);
-    else dense_mfma_kernel<false><<<grid, dm::kWaves * kWave, 0, st>>>(a);
+    const size_t lds = 2 * (size_t)dm::block_b(W);
+    if (W == 8) {
+        // 96 KB of LDS: above the 64 KB a launch gets by default
+        const void *f = glu ? (const void *)dense_mfma_kernel<true, 8> : (const void *)dense_mfma_kernel<false, 8>;
+        if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return K3G_EHIP;
+        if (glu) dense_mfma_kernel<true, 8><<<grid, 8 * kWave, lds, st>>>(a);
+        else dense_mfma_kernel<false, 8><<<grid, 8 * kWave, lds, st>>>(a);
+    } else {
+        if (glu) dense_mfma_kernel<true, 4><<<grid, 4 * kWave, lds, st>>>(a);
+        else dense_mfma_kernel<false, 4><<<grid, 4 * kWave, lds, st>>>(a);
+    }
     if (hipGetLastError() != hipSuccess) return K3G_EHIP;
     const int64_t n = (int64_t)dense_t64(T) * (N / 8);
     if (xp_out && !glu && !xb_out) return launch_reduce_split(out, xp_out, part, a.S, T, N, st);

@@ -143,8 +143,9 @@ def check_block(k3g, src, bank, x, Wr, b, dense, K, tokens, mode=0):
 @pytest.mark.parametrize("H,L_,I,SI,T,mfma", [(256, 128, 96, 64, 37, True),     # one workgroup per product
                                                (512, 256, 128, 192, 100, True),  # K slices across segments
                                                (512, 256, 128, 192, 1, True),    # one token: 63 padded
+                                               (1024, 512, 128, 320, 200, True),  # 128-token tiles, ragged
                                                (224, 96, 96, 96, 37, False)],    # widths off 64: fp32 fma
-                         ids=["mfma_one_slice", "mfma_slices", "mfma_one_token", "fma"])
+                         ids=["mfma_one_slice", "mfma_slices", "mfma_one_token", "mfma_big_tile", "fma"])
 def test_block_small(k3g, H, L_, I, SI, T, mfma):
     E, K = 8, 2
     src, bankt, bank = make_bank(k3g, 81, E, L_, I, 120, 123, 0.01)
@@ -173,10 +174,11 @@ def test_block_small_idot(k3g, mode):
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
-def test_block_dense_wide_range(k3g):
+@pytest.mark.parametrize("T", [24, 128], ids=["tile64", "tile128"])
+def test_block_dense_wide_range(k3g, T):
     # hidden-state entries over 30 decades: each entry's three bf16 pieces
     # follow its own exponent, so the dense products keep the same bound
-    H, L_, I, SI, E, K, T = 512, 256, 128, 192, 8, 2, 24
+    H, L_, I, SI, E, K = 512, 256, 128, 192, 8, 2
     src, bankt, bank = make_bank(k3g, 84, E, L_, I, 120, 123, 0.01)
     Wr, b = synth.router(84, E, H, 0.1)
     dense = synth.block_dense(84, hidden=H, latent=L_, shared_inter=SI, n_shared=2)
