@@ -331,15 +331,16 @@ __global__ __launch_bounds__(W * kWave, 8 / W) void dense_mfma_kernel(DenseMArgs
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // XCD-aware order: consecutive workgroups go round the 8 XCDs, so item
-    // w = (XCD, position) keeps each XCD on a contiguous run of items, where
-    // the token blocks of one (row block, slice) are neighbours and share the
-    // weights through that XCD's L2
+    // w = (XCD, position) keeps each XCD on a contiguous run of items. Items
+    // run token blocks fastest, then row blocks, then K slices: the token
+    // blocks of one (row block, slice) share its weights, and an XCD's row
+    // blocks share one or two slices of operand B, through that XCD's L2
     const int per_xcd = (int)(gridDim.x / 8);
     const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (item >= a.n_items) return;  // whole workgroup
     const int tb = item % a.tok_blocks;
     const int rest = item / a.tok_blocks;
-    const int sl = rest % a.S, rb = rest / a.S;
+    const int rb = rest % a.row_blocks, sl = rest / a.row_blocks;
     const int kb0 = (int)((int64_t)a.nkb * sl / a.S), kb1 = (int)((int64_t)a.nkb * (sl + 1) / a.S);
     constexpr int ROWS_W = GLU ? 32 : 64;  // output rows per wavefront
     const int r0 = (rb * W + wave) * ROWS_W;
