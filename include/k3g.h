@@ -163,7 +163,9 @@ typedef struct {
 /* Byte offsets of the regions of a workspace, for the stage-by-stage checks
  * of a test (0 = region absent; every region is 256-byte aligned). P =
  * n_tokens * top_k pairs, sorted by (expert, token).
- *   logits  double [T][n_experts]        router logits
+ *   logits  double [T][n_experts]        router logits; from 129 tokens up, where
+ *           the product's K range is split across workgroups, the
+ *           splits' partial sums follow in the same region
  *   counts  int32 [n_experts]            pairs per expert
  *   offsets int32 [n_experts+1]          exclusive prefix sum of counts
  *   perm    int32 [P]                    sorted position -> pair id t*top_k+k

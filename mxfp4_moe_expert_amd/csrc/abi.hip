@@ -21,6 +21,7 @@ int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, con
 int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
                    int latent, hipStream_t st);
 int launch_logits(double *logits, const float *x, const float *W, int T, int in, int E, hipStream_t st);
+int logits_planes(int T, int E);
 int launch_topk(int32_t *idx, float *wts, const double *logits, const float *bias, int T, int E, int K,
                 double top_p, hipStream_t st);
 int launch_bucket(int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active, const int32_t *idx,
@@ -177,6 +178,13 @@ bool shape_ok_layer(const k3g_shape &s) {
            s.latent % kGroup == 0 && s.inter % kGroup == 0 && mode_ok(s.mode);
 }
 
+// The logits, and after them the partial planes of a K-split logits product.
+inline size_t logits_bytes(int T, int E) {
+    const size_t n = sizeof(double) * (size_t)(T > 0 ? T : 0) * E;
+    const int planes = T > 0 ? logits_planes(T, E) : 1;
+    return planes > 1 ? n * (1 + planes) : n;
+}
+
 // Regions are laid out from offset 256 so that 0 can mean "absent".
 int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
     memset(o, 0, sizeof *o);
@@ -204,7 +212,7 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
         }
         case K3G_OP_MOE_ROUTE: {
             if (s.n_tokens < 0 || s.n_experts < 1 || s.n_experts > kMaxExperts) return K3G_EINVAL;
-            o->logits = c.take(sizeof(double) * T * s.n_experts);
+            o->logits = c.take(logits_bytes(s.n_tokens, s.n_experts));
             break;
         }
         case K3G_OP_MOE_LAYER:
@@ -213,7 +221,7 @@ int layout(k3g_ws_layout *o, int op, const k3g_shape &s) {
             const size_t P = T * s.top_k, E = s.n_experts;
             if (op == K3G_OP_LATENT_BLOCK) {
                 if (s.hidden <= 0 || s.sh_inter <= 0) return K3G_EINVAL;
-                o->logits = c.take(sizeof(double) * T * E);
+                o->logits = c.take(logits_bytes(s.n_tokens, s.n_experts));
                 o->idx = c.take(sizeof(int32_t) * P);
                 o->wts = c.take(sizeof(float) * P);
                 o->lat = c.take(sizeof(float) * T * s.latent);

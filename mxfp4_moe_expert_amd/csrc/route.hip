@@ -176,6 +176,133 @@ __global__ __launch_bounds__(SPLIT * 64) void logits_mfma_kernel(double *__restr
     }
 }
 
+// ---- logits, many tokens: 64 x 64 tiles, K split across workgroups -----------
+// The same products as logits_mfma_kernel on a tile of 64 tokens x 64 experts
+// (16 accumulator tiles a wavefront: each operand load feeds four times the
+// products of a 32 x 32 tile). Workgroup (x, y, z) takes K-split z of tile
+// (x, y); its 8 wavefronts take consecutive slices of that split and add their
+// tiles in a fixed order through LDS: wavefront w + 4 into w, then 0..3 in
+// order. With KS splits the workgroup writes its sum to partial plane z and
+// logits_sum_kernel adds the planes in order, so the result does not depend
+// on timing.
+constexpr int kLT = 4;                                      // 16-row tiles per side
+constexpr size_t kLTLds = (size_t)4 * kLT * kLT * 4 * 64 * sizeof(double);  // 128 KB
+
+template <bool VEC>
+__global__ __launch_bounds__(512) void logits_tile_kernel(double *__restrict__ out, const float *__restrict__ x,
+                                                          const float *__restrict__ W, int T, int in, int E,
+                                                          int KS) {
+    extern __shared__ double red_lt[];  // [4][kLT * kLT][4][64]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r = lane & 15;
+    const int t0 = blockIdx.y * 16 * kLT, e0 = blockIdx.x * 16 * kLT;
+    const int nk = (in + 15) / 16;
+    const int z = blockIdx.z;
+    const int za = (int)((int64_t)nk * z / KS), zb = (int)((int64_t)nk * (z + 1) / KS);
+    const int ka = za + (int)((int64_t)(zb - za) * wave / 8), kb = za + (int)((int64_t)(zb - za) * (wave + 1) / 8);
+    const float *xr[kLT], *wr[kLT];
+#pragma unroll
+    for (int i = 0; i < kLT; ++i) xr[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * in;
+#pragma unroll
+    for (int j = 0; j < kLT; ++j) wr[j] = W + (size_t)min(e0 + 16 * j + r, E - 1) * in;
+    v4d acc[kLT][kLT];
+#pragma unroll
+    for (int i = 0; i < kLT; ++i)
+#pragma unroll
+        for (int j = 0; j < kLT; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+    // NS steps of operands loaded back to back, then consumed (steps past the
+    // slice read zeros)
+    constexpr int NS = 2;
+    for (int k0 = ka; k0 < kb; k0 += NS) {
+        float a[NS][kLT][4], b[NS][kLT][4];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const int k = (k0 + st) * 16 + 4 * q;
+            const bool live = k0 + st < kb;
+            if (VEC && live && k + 4 <= in) {
+#pragma unroll
+                for (int i = 0; i < kLT; ++i) {
+                    const float4 v = *(const float4 *)(xr[i] + k);
+                    a[st][i][0] = v.x; a[st][i][1] = v.y; a[st][i][2] = v.z; a[st][i][3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < kLT; ++j) {
+                    const float4 v = *(const float4 *)(wr[j] + k);
+                    b[st][j][0] = v.x; b[st][j][1] = v.y; b[st][j][2] = v.z; b[st][j][3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool in_k = live && k + c < in;
+#pragma unroll
+                    for (int i = 0; i < kLT; ++i) a[st][i][c] = in_k ? xr[i][k + c] : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < kLT; ++j) b[st][j][c] = in_k ? wr[j][k + c] : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < kLT; ++i)
+#pragma unroll
+                    for (int j = 0; j < kLT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[st][i][c], (double)b[st][j][c],
+                                                                        acc[i][j], 0, 0, 0);
+    }
+    // the 8 slices' tiles: w + 4 into w, then planes 0..3 in order
+    auto plane = [&](int p, int blk, int v) -> double & { return red_lt[((p * kLT * kLT + blk) * 4 + v) * 64 + lane]; };
+    if (wave >= 4) {
+#pragma unroll
+        for (int i = 0; i < kLT; ++i)
+#pragma unroll
+            for (int j = 0; j < kLT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) plane(wave - 4, i * kLT + j, v) = acc[i][j][v];
+    }
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+        for (int i = 0; i < kLT; ++i)
+#pragma unroll
+            for (int j = 0; j < kLT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][j][v] += plane(wave, i * kLT + j, v);
+    }
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+        for (int i = 0; i < kLT; ++i)
+#pragma unroll
+            for (int j = 0; j < kLT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) plane(wave, i * kLT + j, v) = acc[i][j][v];
+    }
+    __syncthreads();
+    // output element (block, v, lane): token 16*bi + lane/16 + 4*v, expert 16*bj + lane%16
+    double *dst = out + (size_t)z * T * E;
+    for (int o = threadIdx.x; o < kLT * kLT * 256; o += 512) {
+        const int blk = o >> 8, v = (o >> 6) & 3, ln = o & 63;
+        const int base = (blk * 4 + v) * 64 + ln, pl = kLT * kLT * 4 * 64;
+        const double sum = ((red_lt[base] + red_lt[pl + base]) + red_lt[2 * pl + base]) + red_lt[3 * pl + base];
+        const int t = t0 + 16 * (blk / kLT) + (ln >> 4) + 4 * v;
+        const int e = e0 + 16 * (blk % kLT) + (ln & 15);
+        if (t < T && e < E) dst[(size_t)t * E + e] = sum;
+    }
+}
+
+// logits = the KS partial planes added in order
+__global__ __launch_bounds__(256) void logits_sum_kernel(double *__restrict__ logits, const double *__restrict__ part,
+                                                         int64_t n, int KS) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    double s = part[i];
+    for (int z = 1; z < KS; ++z) s += part[(size_t)z * n + i];
+    logits[i] = s;
+}
+
 // ---- top-k: one wavefront per token, candidates in registers ---------------------
 // The order is "larger biased score first, equal scores to the lower expert
 // id". Round k picks, over all lanes, the best candidate that comes strictly
@@ -631,6 +758,23 @@ __global__ __launch_bounds__(NT) void bucket_kernel(int32_t *__restrict__ counts
 
 // ---- host launchers -----------------------------------------------------------
 
+// K splits of the 64 x 64 logits tiles (more than 128 tokens): enough
+// workgroups for the chip's 256 CUs, at most 8 (logits_planes, which sizes the
+// workspace), and each wavefront at least two steps of 16 columns. With more
+// than one split the partial planes follow the logits in the same workspace
+// region.
+int logits_planes(int T, int E) {
+    if (T <= 128) return 1;
+    const int64_t tiles = (int64_t)((E + 63) / 64) * ((T + 63) / 64);
+    if (tiles >= 192) return 1;
+    const int ks = (int)(256 / tiles);
+    return ks < 8 ? (ks > 1 ? ks : 1) : 8;
+}
+int logits_splits(int T, int in, int E) {
+    const int ks = logits_planes(T, E), nk = (in + 15) / 16;
+    return ks < nk / 16 ? ks : (nk / 16 > 1 ? nk / 16 : 1);
+}
+
 int launch_logits(double *logits, const float *x, const float *W, int T, int in, int E, hipStream_t st) {
     if (T == 0) return K3G_OK;
     if (T <= 8) {
@@ -652,16 +796,22 @@ int launch_logits(double *logits, const float *x, const float *W, int T, int in,
             const dim3 grid((E + 31) / 32, (T + 15) / 16);
             if (vec) logits_mfma_kernel<1, 2, 8, true><<<grid, 512, 0, st>>>(logits, x, W, T, in, E);
             else logits_mfma_kernel<1, 2, 8, false><<<grid, 512, 0, st>>>(logits, x, W, T, in, E);
-        } else if (T <= 256) {
-            // two token tiles a wavefront: each operand load feeds twice the
-            // products (256 tokens: 133 -> 104 us; at 64 tokens, 40 -> 58 us)
-            const dim3 grid((E + 31) / 32, (T + 31) / 32);
-            if (vec) logits_mfma_kernel<2, 2, 8, true><<<grid, 512, 0, st>>>(logits, x, W, T, in, E);
-            else logits_mfma_kernel<2, 2, 8, false><<<grid, 512, 0, st>>>(logits, x, W, T, in, E);
         } else {
-            const dim3 grid((E + 31) / 32, (T + 31) / 32);
-            if (vec) logits_mfma_kernel<2, 2, 4, true><<<grid, 256, 0, st>>>(logits, x, W, T, in, E);
-            else logits_mfma_kernel<2, 2, 4, false><<<grid, 256, 0, st>>>(logits, x, W, T, in, E);
+            // 64 x 64 tiles; K split across workgroups while the tiles alone
+            // would leave the chip short of workgroups
+            const int KS = logits_splits(T, in, E);
+            const dim3 grid((E + 63) / 64, (T + 63) / 64, KS);
+            double *dst = KS > 1 ? logits + (size_t)T * E : logits;
+            const void *f = vec ? (const void *)logits_tile_kernel<true> : (const void *)logits_tile_kernel<false>;
+            if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLTLds) != hipSuccess)
+                return K3G_EHIP;
+            if (vec) logits_tile_kernel<true><<<grid, 512, kLTLds, st>>>(dst, x, W, T, in, E, KS);
+            else logits_tile_kernel<false><<<grid, 512, kLTLds, st>>>(dst, x, W, T, in, E, KS);
+            if (KS > 1) {
+                if (hipGetLastError() != hipSuccess) return K3G_EHIP;
+                const int64_t n = (int64_t)T * E;
+                logits_sum_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(logits, dst, n, KS);
+            }
         }
     }
     return hipGetLastError() == hipSuccess ? K3G_OK : K3G_EHIP;

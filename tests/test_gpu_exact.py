@@ -193,7 +193,8 @@ def test_expert_glu_small_ragged(k3g):
                                              (600, 256, 896, 16, 0.01), (1, 7168, 896, 16, 0.1),
                                              (1, 200, 40, 5, 0.3), (1, 96, 1024, 16, 0.05),
                                              (1, 256, 1000, 20, 0.05), (1, 130, 70, 8, 0.2),
-                                             (200, 7168, 896, 16, 0.1), (160, 130, 70, 8, 0.2)])
+                                             (200, 7168, 896, 16, 0.1), (160, 130, 70, 8, 0.2),
+                                             (250, 1030, 200, 8, 0.1), (4096, 256, 896, 16, 0.01)])
 def test_route_matches_oracle(k3g, T, n_in, E, K, bias):
     print(f"route T={T} in={n_in} E={E} K={K}", flush=True)
     seed = 3000 + T
