@@ -59,6 +59,9 @@
 #ifndef K3G_F4Q_GROUP_UP
 #define K3G_F4Q_GROUP_UP 8
 #endif
+#ifndef K3G_F4_FRIENDLY
+#define K3G_F4_FRIENDLY 1
+#endif
 #ifndef K3G_F4S_GROUP
 #define K3G_F4S_GROUP 4
 #endif
@@ -408,6 +411,7 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
     constexpr int VEC = NCK * f4::kChunkBytes;  // one vector's pieces
     extern __shared__ uint4 lds_b[];
     const int lane = threadIdx.x & (kWave - 1);
+    const int psrc = 4 * (4 * (lane & 15) + (lane >> 4));  // row-friendly loads: see to_operand
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n_out = UP ? inter : latent;
     const int row_blocks = (n_out / f4::kRows + f4::kWaves - 1) / f4::kWaves;
@@ -432,10 +436,12 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
         const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
-        const uint32_t row = (uint32_t)(r0 + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        const uint32_t rt = (uint32_t)(r0 + 16 * (UP ? t >> 1 : t));
+        const uint32_t row = rt + (uint32_t)(lane & 15);
         rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
         rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
-        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vp[t] = K3G_F4_FRIENDLY ? (rt + (uint32_t)(lane >> 2)) * pitch_p + 16u * (uint32_t)(lane & 3)
+                                : row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
     uint4 A[NBUF][CPB], S[NBUF];
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
             const uint32_t sd = c == 0 ? S[b].x : c == 1 ? S[b].y : c == 2 ? S[b].z : S[b].w;
             const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
             const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
-            const uint4 a = A[b][c];
+            const uint4 a = K3G_F4_FRIENDLY ? to_operand(A[b][c], psrc) : A[b][c];
             const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
 #pragma unroll
             for (int q = 0; q < NPP; ++q) {
@@ -671,10 +677,12 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
             const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
-            const uint32_t row = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t) + (lane & 15));
+            const uint32_t rt = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t));
+            const uint32_t row = rt + (uint32_t)(lane & 15);
             rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
             rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
-            vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+            vp[t] = K3G_F4_FRIENDLY ? (rt + (uint32_t)(lane >> 2)) * pitch_p + 16u * (uint32_t)(lane & 3)
+                                    : row * pitch_p + 16u * (uint32_t)(lane >> 4);
             vs[t] = row * pitch_s;
         }
     };
@@ -737,6 +745,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
     const uint4 *bq = lds_b + li;
     const uint32_t *sq = (const uint32_t *)lds_b + 256 + li;
     const int qd = lane & 15, v = qd & 3;
+    const int psrc = 4 * (4 * (lane & 15) + (lane >> 4));  // byte address of the lane loaded for (r, q)
     while (true) {
         float4_t acc[NPP][TILES];
 #pragma unroll
@@ -776,7 +785,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
             for (int t = 0; t < TILES; ++t) {
                 const uint32_t sa = __builtin_amdgcn_ubfe(Sd[0][t], qsh, 8);
                 const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
-                const uint4 a = A[b][t][c];
+                const uint4 a = K3G_F4_FRIENDLY ? to_operand(A[b][t][c], psrc) : A[b][t][c];
                 const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
 #pragma unroll
                 for (int q = 0; q < NPP; ++q) {
@@ -895,6 +904,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
     constexpr int BBUF = NPP * f4::kChunkBytes;  // one chunk of all pairs: 10 KB
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[NBB * BBUF];
     const int lane = threadIdx.x & (kWave - 1);
+    const int psrc = 4 * (4 * (lane & 15) + (lane >> 4));  // row-friendly loads: see to_operand
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n_out = UP ? inter : latent;
     const int row_blocks = (n_out + WAVES * ROWS_W - 1) / (WAVES * ROWS_W);
@@ -919,10 +929,12 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
         const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
-        const uint32_t row = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        const uint32_t rt = (uint32_t)((live ? r0 : 0) + 16 * (UP ? t >> 1 : t));
+        const uint32_t row = rt + (uint32_t)(lane & 15);
         rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
         rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
-        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vp[t] = K3G_F4_FRIENDLY ? (rt + (uint32_t)(lane >> 2)) * pitch_p + 16u * (uint32_t)(lane & 3)
+                                : row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
     uint4 A[NBUF][TILES];
@@ -982,7 +994,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
         for (int t = 0; t < TILES; ++t) {
             sa[t] = __builtin_amdgcn_ubfe(S[b][t], qsh, 8);
             const uint32_t keep = sa[t] == 255u ? 0u : ~0u;  // scale 255: the group is left out
-            const uint4 a = A[b][t];
+            const uint4 a = K3G_F4_FRIENDLY ? to_operand(A[b][t], psrc) : A[b][t];
             Av[t] = v8i_t{(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
             sa[t] &= keep;
         }

@@ -322,6 +322,19 @@ __device__ inline void dma4(const void *base, uint32_t voff, uint32_t lds) {
                      : "m0");
 }
 
+// Row-friendly operand loads: for a 16-row x 64-byte matrix-core operand
+// (16 bytes a lane), lane 4r + q reads bytes [16q, 16q + 16) of row r, so
+// each four lanes take 64 contiguous bytes of one row (the L2 serves that
+// several times faster than 16 rows in consecutive lanes). The instruction
+// wants row r, quarter q in lane r + 16q; ds_bpermute brings it from lane
+// 4r + q, whose byte address is psrc = 4 * (4 * (lane % 16) + lane / 16).
+__device__ inline uint4 to_operand(uint4 a, int psrc) {
+    return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(psrc, (int)a.x),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(psrc, (int)a.y),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(psrc, (int)a.z),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(psrc, (int)a.w));
+}
+
 template <int N>
 __device__ inline void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
