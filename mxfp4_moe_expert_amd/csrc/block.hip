@@ -369,10 +369,9 @@ __global__ __launch_bounds__(W * kWave, 8 / W) void dense_mfma_kernel(DenseMArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             // rows past N (the last row block) read row N - 1 and store nothing:
-            // the wavefront's counted waits also cover the B tile it brings.
-            // Row-friendly order: lane 4r + q reads row r's bytes 16q.. (to_operand)
-            const int row = min(r0 + (GLU ? 16 * (i & 1) : 16 * i) + (lane >> 2), a.N - 1);
-            const uint32_t v = (uint32_t)row * K2 + 16u * (uint32_t)(lane & 3);
+            // the wavefront's counted waits also cover the B tile it brings
+            const int row = min(r0 + (GLU ? 16 * (i & 1) : 16 * i) + (lane & 15), a.N - 1);
+            const uint32_t v = (uint32_t)row * K2 + 16u * (uint32_t)(lane >> 4);
             const rsrc_t r = (GLU && i >= 2) ? ra3 : (s == 0 ? ra[0] : s == 1 ? ra[1] : ra[2]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) A[slot][i][h] = buf_load16(r, v, soff + 64u * h);
@@ -398,7 +397,6 @@ __global__ __launch_bounds__(W * kWave, 8 / W) void dense_mfma_kernel(DenseMArgs
 
     int li = lane;
     __asm__ volatile("" : "+v"(li));
-    const int psrc = 4 * (4 * (lane & 15) + (lane >> 4));  // see to_operand
     // B fragments two-deep: the next (step, token tile)'s three are read from
     // LDS while this one's twelve products issue
     auto compute = [&](int slot, int buf) {
@@ -418,7 +416,7 @@ __global__ __launch_bounds__(W * kWave, 8 / W) void dense_mfma_kernel(DenseMArgs
             __builtin_amdgcn_sched_barrier(0);  // the reads go out ahead of the products
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, to_operand(A[slot][i][st], psrc));
+                const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, A[slot][i][st]);
 #pragma unroll
                 for (int p = 0; p < 3; ++p)
                     acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, B[it & 1][p], acc[i][t], 0, 0, 0);
