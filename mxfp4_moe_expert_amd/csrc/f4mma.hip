@@ -259,10 +259,12 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4_kernel(
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
         const int mp = UP ? ((t & 1) ? W3P : W1P) : W2P;
-        const uint32_t row = (uint32_t)(r0 + 16 * (UP ? t >> 1 : t) + (lane & 15));
+        const uint32_t rt = (uint32_t)(r0 + 16 * (UP ? t >> 1 : t));
+        const uint32_t row = rt + (uint32_t)(lane & 15);
         rp[t] = make_rsrc(eb + bank.off[mp], pitch_p * (uint32_t)n_out);
         rs[t] = make_rsrc(eb + bank.off[mp + 1], pitch_s * (uint32_t)n_out);
-        vp[t] = row * pitch_p + 16u * (uint32_t)(lane >> 4);
+        vp[t] = K3G_F4_FRIENDLY ? (rt + (uint32_t)(lane >> 2)) * pitch_p + 16u * (uint32_t)(lane & 3)
+                                : row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
     // block k: tile k / (NCK/4), chunks 4*(k % (NCK/4)) .. +3
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4_kernel(
             const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
             // scale 255: the group is left out (its data zeroed, its scale made finite)
             const uint32_t keep = sa == 255u ? 0u : ~0u;
-            const uint4 a = A[b][c];
+            const uint4 a = K3G_F4_FRIENDLY ? to_operand(A[b][c], 4 * (4 * (lane & 15) + (lane >> 4))) : A[b][c];
             const v8i_t Av = {(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
             float4_t &ac = acc[t][c & 1];
             ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Av, B, ac, 4, 4, 0, (int)(sa & keep), 0,
