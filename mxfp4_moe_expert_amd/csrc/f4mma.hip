@@ -892,8 +892,9 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4q_kernel(
 // pieces and 256 bytes of scales of each chunk (two DMA instructions, the same
 // count in every wavefront, so the waits are exact). Eight wavefronts, four
 // row tiles each (UP: w1 and w3 of 32 rows; DOWN: 64 rows); operand A in a
-// 4-deep ring of single chunks; per chunk each B fragment feeds four products
-// and each A fragment eight.
+// 4-deep ring of single chunks (row-friendly loads); the rows' scale bytes in
+// windows loaded once an item, as the four-pair kernel takes them; per chunk
+// each B fragment feeds four products and each A fragment eight.
 template <bool UP, int NCK>
 __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
     float *__restrict__ out, const uint8_t *__restrict__ pieces, uint8_t *__restrict__ hp, BankDev bank,
@@ -940,15 +941,16 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
         vs[t] = row * pitch_s;
     }
     uint4 A[NBUF][TILES];
-    uint32_t S[NBUF][TILES];
     auto load_a = [&](int i) {
         const int b = i % NBUF;
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-            A[b][t] = buf_load16(rp[t], vp[t], (uint32_t)i * 64u);
-            S[b][t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs[t], (int)vs[t], (int)((uint32_t)i * 4u), 0);
-        }
+        for (int t = 0; t < TILES; ++t) A[b][t] = buf_load16(rp[t], vp[t], (uint32_t)i * 64u);
     };
+    // the item's scale bytes, once, as the four-pair kernel takes them: lane
+    // (r, q) of a tile holds bytes [16 (q + 4j), +16) of row r in SW[j]; chunk
+    // i's byte for lane (r, q) comes by one ds_bpermute a tile
+    constexpr int NSW = (NCK + 15) / 16;
+    uint4 SW[NSW][TILES];
     // this wavefront's pair (the pass's last pair again past its end)
     const int pw = p0 + min(wave, np - 1);
     const uint8_t *src = pieces + (size_t)(UP ? perm[pw] / top_k : pw) * VEC;
@@ -959,12 +961,18 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
         dma16(s, 16u * lane, dst);
         dma4(s + 1024, 4u * lane, dst + 1024);
     };
-    constexpr int VM_A = 2 * TILES;  // vector loads of one chunk of A
-    // prologue: B of chunks 0 and 1, then A of chunks 0 .. NBUF-2
+    constexpr int VM_A = TILES;  // vector loads of one chunk of A
+    // prologue: B of chunks 0 and 1, the scale windows, then A of chunks 0 .. NBUF-2
     dma_b(0);
     if (NCK > 1) dma_b(1);
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        const uint32_t off = (uint32_t)min(16 * ((lane >> 4) + 4 * j), ngrp - 16);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) SW[j][t] = buf_load16(rs[t], vs[t] + off, 0u);
+    }
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i)
         if (i < NCK) load_a(i);
@@ -992,9 +1000,12 @@ __global__ __launch_bounds__(8 * kWave, 1) void moe_f4s_kernel(
         const uint32_t *sq = (const uint32_t *)(lds_b + (i % NBB) * BBUF + 1024) + li;
         uint32_t sa[TILES];
         v8i_t Av[TILES];
+        const int ssrc = 4 * ((lane & 15) + 16 * ((i / 4) % 4));  // byte address of the source lane
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
-            sa[t] = __builtin_amdgcn_ubfe(S[b][t], qsh, 8);
+            const uint4 w = SW[i / 16][t];
+            const uint32_t d = i % 4 == 0 ? w.x : i % 4 == 1 ? w.y : i % 4 == 2 ? w.z : w.w;
+            sa[t] = __builtin_amdgcn_ubfe((uint32_t)__builtin_amdgcn_ds_bpermute(ssrc, (int)d), qsh, 8);
             const uint32_t keep = sa[t] == 255u ? 0u : ~0u;  // scale 255: the group is left out
             const uint4 a = K3G_F4_FRIENDLY ? to_operand(A[b][t], psrc) : A[b][t];
             Av[t] = v8i_t{(int)(a.x & keep), (int)(a.y & keep), (int)(a.z & keep), (int)(a.w & keep), 0, 0, 0, 0};
