@@ -268,7 +268,7 @@ def ws_view(ws, L, name, count, dtype):
     return host(ws[L[name]:L[name] + nbytes]).view(dtype)
 
 
-def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0):
+def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0, experts=()):
     T, K = idx.shape
     latent, inter = bank.latent, bank.inter
     y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | decode)
@@ -300,6 +300,10 @@ def check_layer_exact(k3g, src, bankt, bank, x, idx, wts, tokens=None, decode=0)
         for k in range(K):
             if int(idx[t, k]) >= 0:  # dropped entries are no pairs
                 by_expert.setdefault(int(idx[t, k]), []).append((t, k))
+    for e in experts:  # and every pair of these experts
+        for t, k in zip(*np.nonzero(idx == e)):
+            if (int(t), int(k)) not in by_expert.setdefault(int(e), []):
+                by_expert[int(e)].append((int(t), int(k)))
     for e, tk in sorted(by_expert.items()):
         ex = src(e)
         for t, k in tk:
@@ -669,6 +673,30 @@ def test_layer_decode_b64_full_sampled(k3g, full_bank, decode):
     # every token, pair by pair (all 1,024 pairs), each stage on the GPU's own input
     print(f"decode_b64 form {decode:#x}: checking 1024 pairs on the oracle", flush=True)
     check_layer_exact(k3g, src, None, bank, x, io, wo, tokens=range(64), decode=decode)
+
+
+def test_layer_exact_prefill_4096_sampled(k3g, full_bank):
+    # the 4096-token EXACT layer in its default form: the FP4 matrix cores,
+    # eight pairs a pass (the eight-pair kernel at its real widths)
+    src, bankt, bank = full_bank
+    seed = synth.SEED_BASE + 3
+    W, b = synth.router(seed, 896, 3584, 0.01)
+    x = synth.activations(seed, 4096, 3584)
+    print("routing 4096 tokens on the oracle", flush=True)
+    idx, wts, _ = oracle.route(x, W, b, 16)
+    sh = k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584, inter=3072, mode=k3g.EXACT)
+    assert k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)["passes"]  # the multi-pair FP4 form
+    assert 4096 * 16 >= 6 * 896  # eight pairs a pass
+    counts = np.bincount(idx.ravel(), minlength=896)
+    # every pair of four experts: the fullest (several passes, the last one
+    # short), the emptiest in use, and two of middling load
+    order = np.argsort(counts, kind="stable")
+    used = order[counts[order] > 0]
+    full = next(int(e) for e in used[::-1] if counts[e] % 8)
+    experts = [full, int(used[0]), int(used[len(used) // 2]), int(used[len(used) // 3])]
+    assert counts[full] > 8
+    print(f"checking every pair of experts {experts} ({counts[experts].tolist()} pairs)", flush=True)
+    check_layer_exact(k3g, src, None, bank, x, idx, wts, tokens=[0, 2047, 4095], experts=experts)
 
 
 # ---- the routed-expert cache: host memory -> HBM ------------------------------------------
