@@ -446,13 +446,16 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
                                 : row * pitch_p + 16u * (uint32_t)(lane >> 4);
         vs[t] = row * pitch_s;
     }
-    uint4 A[NBUF][CPB], S[NBUF];
+    uint4 A[NBUF][CPB];
     auto load_block = [&](int kb) {
         const int t = kb / (NCK / CPB), c0 = CPB * (kb % (NCK / CPB)), b = kb % NBUF;
 #pragma unroll
         for (int c = 0; c < CPB; ++c) A[b][c] = buf_load16(rp[t], vp[t], (uint32_t)(c0 + c) * 64u);
-        S[b] = buf_load16(rs[t], vs[t], (uint32_t)c0 * 4u);
     };
+    // the rows' scale bytes in windows, once, as the four-pair kernel takes
+    // them (chunk i's byte for lane (r, q) comes by one ds_bpermute)
+    constexpr int NSW = (NCK + 15) / 16;
+    uint4 SW[NSW][TILES];
     // B: the pass's NPP vectors of pieces into LDS, then the first weight blocks
     {
         const uint32_t lb = lds_addr(lds_b);
@@ -470,8 +473,14 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
     __builtin_amdgcn_sched_barrier(0);
     constexpr int PRO = NBUF - 1 < NB ? NBUF - 1 : NB;
 #pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        const uint32_t off = (uint32_t)min(16 * ((lane >> 4) + 4 * j), ngrp - 16);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) SW[j][t] = buf_load16(rs[t], vs[t] + off, 0u);
+    }
+#pragma unroll
     for (int kb = 0; kb < PRO; ++kb) load_block(kb);
-    wait_vm<PRO * (CPB + 1)>();
+    wait_vm<PRO * CPB>();
     __syncthreads();
 
     const uint32_t qsh = 8u * (uint32_t)(lane >> 4);
@@ -509,10 +518,13 @@ __global__ __launch_bounds__(f4::kWaves * kWave, 2) void moe_f4m_kernel(
             }
     };
     auto compute = [&](int kb) {
-        const int t = kb / (NCK / CPB), b = kb % NBUF;
+        const int t = kb / (NCK / CPB), b = kb % NBUF, c0 = CPB * (kb % (NCK / CPB));
 #pragma unroll
         for (int c = 0; c < CPB; ++c) {
-            const uint32_t sd = c == 0 ? S[b].x : c == 1 ? S[b].y : c == 2 ? S[b].z : S[b].w;
+            const int i = c0 + c;
+            const uint4 w = SW[i / 16][t];
+            const uint32_t d = i % 4 == 0 ? w.x : i % 4 == 1 ? w.y : i % 4 == 2 ? w.z : w.w;
+            const uint32_t sd = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane & 15) + 16 * ((i / 4) % 4)), (int)d);
             const uint32_t sa = __builtin_amdgcn_ubfe(sd, qsh, 8);
             const uint32_t keep = sa == 255u ? 0u : ~0u;  // scale 255: the group is left out
             const uint4 a = K3G_F4_FRIENDLY ? to_operand(A[b][c], psrc) : A[b][c];
