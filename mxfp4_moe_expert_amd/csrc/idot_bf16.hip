@@ -28,7 +28,9 @@
 // Global-to-LDS loads (global_load_lds) bring weights, scale bytes, tokens
 // and token scales without passing through registers; a stage is requested
 // three blocks before it is used. LDS layouts (per stage):
-//   weights [wave tile 0..31][group 0..1][row 0..15] 16-byte chunks
+//   weights [wave tile 0..31][row 0..15][group 0..1] 16-byte chunks, so the
+//           two lanes of a row in a load read 32 contiguous bytes (the L2
+//           serves rows in consecutive lanes several times slower)
 //           (a fragment read: lane (i, q) reads dword q of row i: 2-way banks)
 //   scales  [tile][row 0..15][4 dwords]: the scale bytes of 16 groups, loaded
 //           once per 8 stages into one of two windows; the tiles ordered
@@ -134,8 +136,9 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
     uint32_t w_off[W_LD];
 #pragma unroll
     for (int m = 0; m < W_LD; ++m) {
+        // [tile][row][group]: the GB lanes of a row read its GB x 16 contiguous bytes
         const int s = 64 * (wl + NW * m) + lane;
-        const int wt = s / (GB * 16), j = (s / 16) % GB, i = s % 16;
+        const int wt = s / (GB * 16), i = (s % (GB * 16)) / GB, j = s % GB;
         w_off[m] = arow(wt >> 2, wt & 3, i) * pitch + 16u * (uint32_t)j;
     }
     const uint8_t *w_base = pk[wl & 1];
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
                     bf16x8_t a[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const uint32_t w = wq[(((wl * 4 + k) * GB + j) * 16 + col) * 4 + quad];
+                        const uint32_t w = wq[(((wl * 4 + k) * 16 + col) * GB + j) * 4 + quad];
                         const uint32_t sd = wsd[(((((k >> 1) * NW + wl) << 1) + (k & 1)) * 16 + col) * 4 + sdw];
                         const uint32_t sb = (sd >> (8 * (gsel + j))) & 0xFFu;
                         const bool skip = sb == 255u;
