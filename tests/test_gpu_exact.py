@@ -454,7 +454,7 @@ def check_pass_table(ws, L, E, npp):
 
 
 @pytest.mark.parametrize("case", ["ragged", "skewed", "wide_range", "topp", "one_expert", "mid4", "dense4",
-                                  "dense4_topp"])
+                                  "dense4_topp", "width20_4", "width20_8"])
 def test_layer_tokens_f4mma(k3g, case):
     # more tokens on the FP4 matrix cores: a workgroup takes one expert's sorted
     # pairs two or four at a time (short last passes of 1..3 pairs)
@@ -467,6 +467,12 @@ def test_layer_tokens_f4mma(k3g, case):
         E, latent, inter, T, K = 10, 1536, 1024, 23, 4
     if case == "mid4":  # four a pass (between 3 and 6 pairs per expert)
         E, latent, inter, T, K = 24, 1024, 512, 20, 4
+    # 20 chunks of 128 along latent: the rows' scale bytes end inside the second
+    # 64-byte window the kernels load them in (four and eight pairs a pass)
+    if case == "width20_4":
+        E, latent, inter, T, K = 24, 2560, 1536, 20, 4
+    if case == "width20_8":
+        E, latent, inter, T, K = 10, 2560, 1536, 23, 4
     src, bankt, bank = make_bank(k3g, 62, E, latent, inter, 110, 140, 0.02)
     x = synth.activations(62, T, latent)
     if case == "wide_range":
@@ -482,7 +488,7 @@ def test_layer_tokens_f4mma(k3g, case):
     if case.endswith("topp"):
         assert (idx < 0).any()
     npp = pairs_per_pass(T * K, E)
-    assert npp == {"skewed": 8, "dense4": 8, "dense4_topp": 8, "mid4": 4}.get(case, 2)
+    assert npp == {"skewed": 8, "dense4": 8, "dense4_topp": 8, "mid4": 4, "width20_4": 4, "width20_8": 8}.get(case, 2)
     y, ws, L = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | k3g.DECODE_MFMA)
     assert L["xp"] and L["hp"] and L["passes"]
     check_pass_table(ws, L, E, npp)
