@@ -179,6 +179,25 @@ def test_block_dense_workspace(k3g, H, lat, SI, mfma):
     assert room["dpart"] >= 4 * max(T * lat, 2 * T * SI, T * H)
 
 
+@pytest.mark.parametrize("T,E,planes", [(1, 896, 1), (128, 896, 1), (129, 896, 6), (256, 896, 4),
+                                         (320, 896, 3), (1024, 896, 1), (250, 200, 8), (4096, 896, 1)])
+def test_route_logits_region(k3g, T, E, planes):
+    # more than 128 tokens: 64 x 64 logits tiles, the K range split while the
+    # tiles are fewer than 192 (workgroups for the chip's 256 CUs, at most 8
+    # splits), the splits' partial planes after the logits in the same region
+    sh = k3g.shape(n_tokens=T, top_k=8, n_experts=E, latent=128, inter=128, mode=k3g.EXACT)
+    tiles = -(-E // 64) * -(-T // 64)
+    assert planes == (1 if T <= 128 or tiles >= 192 else min(8, max(1, 256 // tiles)))
+    want = T * E * 8 * (1 + planes if planes > 1 else 1)
+    for op in (k3g.OP_MOE_ROUTE, k3g.OP_LATENT_BLOCK):
+        sb = sh if op == k3g.OP_MOE_ROUTE else k3g.shape(n_tokens=T, top_k=8, n_experts=E, latent=128,
+                                                          inter=128, hidden=256, sh_inter=64, mode=k3g.EXACT)
+        L = k3g.workspace_layout(op, sb)
+        assert region_sizes(L)["logits"] >= want
+        if op == k3g.OP_MOE_ROUTE:  # the route op holds the logits region alone
+            assert L["total"] >= L["logits"] + want
+
+
 def test_empty_batch_is_a_no_op(k3g):
     # n_tokens = 0: the scalar arguments are still checked, then K3G_OK with
     # nothing enqueued and no device touched, null pointers allowed
