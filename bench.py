@@ -14,12 +14,12 @@ oracle timed on a bounded sample on the host cores.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload decode_b1|decode_b64|prefill_4096_idot|prefill_4096_exact]
-                    [--mfma-decode] [--idot-bf16]
+                    [--mfma-decode] [--idot-int8]
 
 The default run (decode_b1) also measures, on the same resident bank:
   other_workloads     short runs of the 64-token EXACT layer (vector and FP4
-                      matrix-core forms), the 4096-token IDOT layer (int8 and
-                      bf16 matrix-core forms) and the 4096-token EXACT layer on
+                      matrix-core forms), the 4096-token IDOT layer (bf16 and
+                      int8 matrix-core forms) and the 4096-token EXACT layer on
                       the FP4 matrix cores;
   expert_b1           one expert on one token and the one-matrix product;
   achievable          the sustained matrix-core rates and streaming-read rate
@@ -62,8 +62,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b64", "prefill_4096_idot", "prefill_4096_exact"])
-    ap.add_argument("--idot-bf16", action="store_true",
-                    help="IDOT workloads: run the group dots on the bf16 matrix cores (same results)")
+    ap.add_argument("--idot-int8", action="store_true",
+                    help="IDOT workloads: run the group dots on the int8 matrix cores (same results; without it the "
+                         "library's default, the bf16 matrix cores)")
     ap.add_argument("--mfma-decode", action="store_true",
                     help="EXACT workloads and the block: the expert products on the FP4 matrix cores (x and h as "
                          "e2m1 pieces) whatever the token count")
@@ -138,20 +139,20 @@ def main():
     if args.block_only:
         print(json.dumps({"block_256": run_block(ctx, bank, form=form_arg)}), flush=True)
         return
-    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_bf16, form_arg)
+    result, host = run_workload(ctx, args.workload, args.steps, args.warmup, args.idot_int8, form_arg)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, src, *host)
     if args.workload == "decode_b1" and not args.no_secondary:
         # the other configurations on the same resident bank, shorter runs (not the headline)
         others = []
         cpu_lines = {}
-        for wl, steps, warm, bf16, p, fm in (("decode_b1", 100, 10, False, 0.9, None),
+        for wl, steps, warm, int8, p, fm in (("decode_b1", 100, 10, False, 0.9, None),
                                              ("decode_b64", 20, 3, False, 0.0, None),
                                              ("decode_b64", 20, 3, False, 0.0, "vector"),
                                              ("prefill_4096_idot", 10, 2, False, 0.0, None),
                                              ("prefill_4096_idot", 10, 2, True, 0.0, None),
                                              ("prefill_4096_exact", 5, 1, False, 0.0, None)):
-            r, h = run_workload(ctx, wl, steps, warm, bf16, form_name=fm, top_p=p)
+            r, h = run_workload(ctx, wl, steps, warm, int8, form_name=fm, top_p=p)
             rec = {k: r[k] for k in ("config", "ms_per_step", "value", "unit", "tokens_per_s", "step_us",
                                      "stage_us", "decode", "roofline", "steps", "warmup")}
             if not args.no_cpu_baseline and wl != "decode_b1":
@@ -184,14 +185,16 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=0.0):
+def run_workload(ctx, workload, steps, warmup, idot_int8, form_name=None, top_p=0.0):
     """Measure one workload on the resident bank. Returns the result record and
     what the CPU baseline needs (the same inputs)."""
     torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
     L, I, E, K = synth.LATENT, synth.INTER, ctx["n_experts"], synth.TOP_K
     wl_seed, T, bias_range, mode_name = synth.WORKLOADS[workload]
     mode = k3g.IDOT if mode_name == "idot" else k3g.EXACT
-    form = k3g.IDOT_BF16 if (mode == k3g.IDOT and idot_bf16) else 0
+    form = 0
+    if mode == k3g.IDOT:  # named either way (the bf16 form is the library's default)
+        form = k3g.IDOT_INT8 if idot_int8 else k3g.IDOT_BF16
     if mode == k3g.EXACT:  # None: the library's default (vector for one token, FP4 matrix cores for more)
         form = {None: 0, "vector": k3g.DECODE_VECTOR, "mfma": k3g.DECODE_MFMA}[form_name]
 
@@ -352,7 +355,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=
     alg_bytes = n_exp * (up_b + dn_b) + router_b + 2 * T * L * 4
     up_alg = n_exp * up_b + T * L * 4 + P * I * 4       # weights once, x in, h out
     if mode == k3g.IDOT:  # int8 x and its scales in; h out quantised (int8, or bf16 in that form) with its scales
-        up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * (2 if form else 1) + P * (I // 32) * 4
+        up_alg = n_exp * up_b + T * L + T * (L // 32) * 4 + P * I * (2 if form == k3g.IDOT_BF16 else 1) + P * (I // 32) * 4
 
     # the tag of this form in the names of the committed counter summaries
     form_tag = ("fp4_mfma" if f4 else "bf16" if form == k3g.IDOT_BF16 else
@@ -380,7 +383,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=
     if mode == k3g.IDOT:
         # matrix-core work of the up kernel: 2 ops per multiply-add, w1 and w3 rows, every pair
         up_ops = 2.0 * P * 2 * I * L
-        peak = MFMA_PEAK_BF16_TFLOPS if form else MFMA_PEAK_I8_TOPS
+        bf16 = form == k3g.IDOT_BF16
+        peak = MFMA_PEAK_BF16_TFLOPS if bf16 else MFMA_PEAK_I8_TOPS
         tops = up_ops / (stage_ms["up"] * 1e-3) / 1e12
         roof = {
             "kernel": "moe_up (IDOT group dots of w1 and w3 for every pair, SiTU)",
@@ -388,7 +392,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=
             "achieved": round(tops, 1),
             "peak": peak,
             "unit": "TFLOP/s",
-            "ops": "int8 multiply-adds x 2" if not form else "bf16 multiply-adds x 2 (exact int8 values)",
+            "ops": "bf16 multiply-adds x 2 (exact int8 values)" if bf16 else "int8 multiply-adds x 2",
             "frac": round(tops / peak, 4),
             "traffic": measured_traffic(workload, "moe_up", form_tag),
             "algorithmic_ops_per_launch": up_ops,
@@ -413,7 +417,8 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=
             "workload": workload,
             "tokens_per_step": T,
             "experts": E, "top_k": K, "latent": L, "inter": I,
-            "mode": mode_name + ("+bf16-mfma" if form == k3g.IDOT_BF16 else "+fp4-mfma" if f4 else ""),
+            "mode": mode_name + ("+bf16-mfma" if form == k3g.IDOT_BF16 else "+int8-mfma" if form == k3g.IDOT_INT8
+                                 else "+fp4-mfma" if f4 else ""),
             "distinct_experts_per_step": n_exp,
             "top_p": top_p,
             "algorithmic_bytes_per_step": int(alg_bytes),
@@ -426,7 +431,7 @@ def run_workload(ctx, workload, steps, warmup, idot_bf16, form_name=None, top_p=
         "stage_us": {k: (None if v is None else round(v * 1e3, 2)) for k, v in stage_ms.items()},
         "decode": ("gfx950 FP4 MFMA on the stored nibbles, x and h as 16 e2m1 pieces" if f4 else
                    "gfx950 FP4->FP32 convert" if mode == k3g.EXACT else
-                   "bf16 MFMA on exact int8 values" if form else "int8 MFMA"),
+                   "bf16 MFMA on exact int8 values" if form == k3g.IDOT_BF16 else "int8 MFMA"),
         ("stage_us_vector_cvt_decode" if f4 else "stage_us_fp4_mfma_decode"):
             {k: round(v * 1e3, 2) for k, v in alt_ms.items()},
         "stage_us_lds_lut_decode": {k: round(v * 1e3, 2) for k, v in lut_ms.items()},

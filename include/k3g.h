@@ -65,10 +65,12 @@ typedef enum {
 } k3g_status;
 
 /* EXACT: fp32 activations, exact e2m1 products, fp32 accumulation.
- * IDOT:  activations quantised per 32-group to int8, int32 group dots on the
- *        matrix cores ([COLIBRI-K3] "Streaming design", K3_IDOT). The IDOT
- *        kernels need latent and inter to be multiples of 128 and the scale
- *        tensors 4-byte aligned (K3G_EUNSUPPORTED / K3G_EALIGN otherwise). */
+ * IDOT:  activations quantised per 32-group to int8, integer group dots
+ *        ([COLIBRI-K3] "Streaming design", K3_IDOT), on the bf16 matrix cores
+ *        by default (K3G_IDOT_BF16) or on the int8 ones (K3G_IDOT_INT8), with
+ *        the same results bit for bit. The IDOT kernels need latent and inter
+ *        to be multiples of 128 and the scale tensors 4-byte aligned
+ *        (K3G_EUNSUPPORTED / K3G_EALIGN otherwise). */
 typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
 
 /* OR-ed into `mode` of the EXACT calls: decode the nibbles through the
@@ -77,13 +79,19 @@ typedef enum { K3G_EXACT = 0, K3G_IDOT = 1 } k3g_mode;
  * (the default). Both give the same values: e2m1 codes are exact in either. */
 #define K3G_DECODE_LUT 0x100
 
-/* OR-ed into K3G_IDOT: compute the same group dots on the bf16 matrix cores
- * instead of the int8 ones. The int8 activations are widened to bf16 and the
+/* OR-ed into K3G_IDOT (the default form; the flag names it): the group dots
+ * on the bf16 matrix cores. The int8 activations are widened to bf16 and the
  * e2m1 values carry their group's power-of-two scale (both exact), so each
  * group's fp32 result is exactly I * 2^(s-128) and the per-group epilogue is
  * one fma instead of a convert, a multiply and an fma. Results are identical
- * to the int8 form bit for bit; the workspace gains bf16 copies of xq and hq. */
+ * to the int8 form bit for bit; the workspace holds bf16 copies of xq and hq. */
 #define K3G_IDOT_BF16 0x200
+
+/* OR-ed into K3G_IDOT: the group dots on the int8 matrix cores
+ * (v_mfma_i32_32x32x32_i8, int32 group sums, then a convert, a multiply and an
+ * fma per result and group). K3G_IDOT_BF16 and K3G_IDOT_INT8 together are
+ * K3G_EINVAL. */
+#define K3G_IDOT_INT8 0x1000
 
 /* Which kernels an EXACT layer runs on. With neither flag: the FP4 matrix
  * cores (below) for more than one token when the shape and the bank fit them,
@@ -181,7 +189,7 @@ typedef struct {
  *   lat, agg, nrm  float [T][latent]     block stages
  *   shh     float [T][sh_inter]          block shared-expert SiTU output
  *   layer   the MoE layer's own workspace inside the block's
- *   xqb, hqb  uint16 (bf16) copies of xq and hq (K3G_IDOT_BF16 only)
+ *   xqb, hqb  uint16 (bf16) copies of xq and hq (the bf16 IDOT form only)
  *   xp, hp    layer with K3G_DECODE_MFMA: each token's x and each pair's h as
  *             16 e2m1 pieces, 1280 bytes per 128 entries (operand B of the
  *             instruction and its block scales)
@@ -256,7 +264,7 @@ int k3g_mxfp4_gemv_f32s(float *y, const float *x, const uint8_t *packed, const f
  * 25 tanh(u/25) (SiTU-GLU, [COLIBRI-K3] "Architecture notes"), y = w2 h.
  * y, x fp32 [latent], 16-byte aligned. In IDOT mode x and h are quantised per
  * 32-group to int8 first. ws: k3g_workspace_bytes(K3G_OP_EXPERT_GLU, ...) bytes,
- * 256-byte aligned. K3G_DECODE_LUT and K3G_IDOT_BF16 apply; K3G_DECODE_MFMA
+ * 256-byte aligned. K3G_DECODE_LUT and the IDOT form flags apply; K3G_DECODE_MFMA
  * (a layer form) returns K3G_EUNSUPPORTED. */
 int k3g_expert_glu(float *y, const float *x, const k3g_expert *e, int mode,
                    void *ws, size_t ws_bytes, void *stream);

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libk3g.so")
 EXACT = 0
 IDOT = 1
 DECODE_LUT = 0x100  # OR into the EXACT mode: decode through the LDS byte-pair table
-IDOT_BF16 = 0x200  # OR into the IDOT mode: the same group dots on the bf16 matrix cores
+IDOT_BF16 = 0x200  # OR into the IDOT mode: the group dots on the bf16 matrix cores (the default form)
+IDOT_INT8 = 0x1000  # OR into the IDOT mode: the same group dots on the int8 matrix cores
 DECODE_MFMA = 0x400  # OR into the EXACT mode: the expert products on the FP4 matrix cores (x and h as e2m1 pieces)
 DECODE_VECTOR = 0x800  # OR into the EXACT mode: the vector kernels (the default for one token; more tokens default to MFMA)
 OP_EXPERT_GLU = 1

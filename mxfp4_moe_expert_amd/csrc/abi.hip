@@ -113,11 +113,12 @@ struct Carver {
     }
 };
 
-constexpr int kFormFlags = K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_DECODE_MFMA | K3G_DECODE_VECTOR;
+constexpr int kFormFlags = K3G_DECODE_LUT | K3G_IDOT_BF16 | K3G_IDOT_INT8 | K3G_DECODE_MFMA | K3G_DECODE_VECTOR;
 inline int base_mode(int mode) { return mode & ~kFormFlags; }
 inline bool mode_ok(int mode) {
     if (mode & ~(kFormFlags | 0xFF)) return false;
-    if ((mode & K3G_IDOT_BF16) && base_mode(mode) != K3G_IDOT) return false;
+    if ((mode & (K3G_IDOT_BF16 | K3G_IDOT_INT8)) && base_mode(mode) != K3G_IDOT) return false;
+    if ((mode & K3G_IDOT_BF16) && (mode & K3G_IDOT_INT8)) return false;
     if ((mode & (K3G_DECODE_LUT | K3G_DECODE_MFMA | K3G_DECODE_VECTOR)) && base_mode(mode) != K3G_EXACT) return false;
     if ((mode & K3G_DECODE_MFMA) && (mode & (K3G_DECODE_LUT | K3G_DECODE_VECTOR))) return false;
     return base_mode(mode) == K3G_EXACT || base_mode(mode) == K3G_IDOT;
@@ -170,7 +171,8 @@ inline int idot_shape_ok(int mode, int latent, int inter, int n_tokens = 1, int 
         return K3G_EUNSUPPORTED;
     return K3G_OK;
 }
-inline bool bf16_of(int mode) { return (mode & K3G_IDOT_BF16) != 0; }
+// IDOT runs on the bf16 matrix cores unless K3G_IDOT_INT8 asks for the int8 ones
+inline bool bf16_of(int mode) { return base_mode(mode) == K3G_IDOT && !(mode & K3G_IDOT_INT8); }
 
 bool shape_ok_layer(const k3g_shape &s) {
     return s.n_tokens >= 0 && s.top_k >= 1 && s.top_k <= kMaxTopK && s.n_experts >= 1 &&

@@ -40,17 +40,21 @@ def test_bank_layout_matches_census(k3g):
 
 
 def test_workspace_layout(k3g):
-    sh = k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584, inter=3072, mode=k3g.IDOT)
+    sh = k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584, inter=3072, mode=k3g.IDOT | k3g.IDOT_INT8)
     L = k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)
     P = 4096 * 16
     regions = {"counts": 896 * 4, "offsets": 897 * 4, "perm": P * 4, "inv": P * 4, "active": 897 * 4,
                "ypair": P * 3584 * 4, "xq": 4096 * 3584, "xs": 4096 * 112 * 4,
                "hq": P * 3072, "hs": P * 96 * 4}
-    # IDOT keeps h only quantised (hq, or its bf16 copy hqb in the bf16 form): no fp32 h
-    assert L["h"] == 0 and L["hqb"] == 0
+    # IDOT keeps h only quantised (hq in the int8 form, its bf16 copy hqb in the bf16 one): no fp32 h
+    assert L["h"] == 0 and L["hqb"] == 0 and L["xqb"] == 0
     Lb = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584,
                                                           inter=3072, mode=k3g.IDOT | k3g.IDOT_BF16))
     assert Lb["h"] == 0 and Lb["hq"] == 0 and Lb["hqb"] > 0 and Lb["xqb"] > 0
+    # the bf16 form is the default: the bare mode lays the workspace out as the flagged one
+    Ld = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=4096, top_k=16, n_experts=896, latent=3584,
+                                                          inter=3072, mode=k3g.IDOT))
+    assert Ld == Lb
     Le = k3g.workspace_layout(k3g.OP_MOE_LAYER, k3g.shape(n_tokens=64, top_k=16, n_experts=896, latent=3584,
                                                           inter=3072, mode=k3g.EXACT))
     assert Le["h"] > 0 and Le["hq"] == 0
@@ -149,6 +153,9 @@ def test_form_flags_exclude_each_other(k3g):
     assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.DECODE_MFMA | k3g.DECODE_VECTOR)) == 0
     assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.DECODE_MFMA | k3g.DECODE_LUT)) == 0
     assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.IDOT | k3g.DECODE_VECTOR)) == 0
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.IDOT | k3g.IDOT_BF16 | k3g.IDOT_INT8)) == 0
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.IDOT_INT8)) == 0
+    assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.IDOT | k3g.IDOT_INT8)) > 0
     assert k3g.workspace_bytes(k3g.OP_MOE_LAYER, sh(k3g.EXACT | k3g.DECODE_VECTOR)) > 0
     # widths off the matrix cores' multiples of 512: the vector kernels whatever the flags say
     sh2 = k3g.shape(n_tokens=4, top_k=2, n_experts=8, latent=256, inter=512, mode=k3g.EXACT)

@@ -161,7 +161,7 @@ def test_block_small(k3g, H, L_, I, SI, T, mfma):
     assert np.all(np.abs(out - r["out"]) <= 1e-3 * r["onorm"])
 
 
-@pytest.mark.parametrize("mode", [1, 0x201], ids=["idot_int8", "idot_bf16"])
+@pytest.mark.parametrize("mode", [0x1001, 1], ids=["idot_int8", "idot_bf16_default"])
 def test_block_small_idot(k3g, mode):
     # the block with its routed layer in the IDOT form (widths multiples of 128)
     H, L_, I, SI, E, K, T = 512, 256, 128, 192, 8, 2, 40

@@ -1,5 +1,6 @@
-"""GPU parity of the IDOT path (int8 activations; int8 matrix cores, or the
-bf16 matrix cores on the same exact values with K3G_IDOT_BF16).
+"""GPU parity of the IDOT path (int8 activations; the group dots on the bf16
+matrix cores by default, or on the int8 ones with K3G_IDOT_INT8, on the same
+exact values).
 
 Bit-exact: the quantised activations (q, s), the int32 group sums, and the
 two forms' outputs against each other. fp32 outputs: within 1e-5 *
@@ -109,7 +110,7 @@ def check_expert_idot(k3g, ex, x, latent, inter, form=0):
     return yg
 
 
-FORMS = [0, 0x200]  # int8 matrix cores; K3G_IDOT_BF16
+FORMS = [0x1000, 0x200]  # K3G_IDOT_INT8; K3G_IDOT_BF16 (the default form, named)
 
 
 @pytest.mark.parametrize("form", FORMS)
@@ -146,7 +147,7 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens, experts=()):
     outputs; and the bf16 form against the int8 form bit for bit."""
     T, K = idx.shape
     latent, inter, E = bank.latent, bank.inter, bank.n_experts
-    yg, ws, L = run_layer_idot(k3g, bank, x, idx, wts, 0)
+    yg, ws, L = run_layer_idot(k3g, bank, x, idx, wts, 0x1000)
     P = T * K
     inv = ws_view(ws, L, "inv", P, np.int32)
     perm = ws_view(ws, L, "perm", P, np.int32)

@@ -33,7 +33,8 @@ def layer_static(k3g, y, x, idx, wts, bank, mode):
                                           k3g.C.byref(bank), T, K, mode, torch.cuda.current_stream().cuda_stream)
 
 
-@pytest.mark.parametrize("mode", [0x800, 0, 1], ids=["exact_vector", "exact_default_f4mma", "idot"])
+@pytest.mark.parametrize("mode", [0x800, 0, 1, 0x1001],
+                         ids=["exact_vector", "exact_default_f4mma", "idot_bf16_default", "idot_int8"])
 def test_layer_static_equals_layer(k3g, mode):
     E, latent, inter, K = 24, 1024, 512, 4
     src, bankt, bank = make_bank(k3g, 91, E, latent, inter, 118, 132, 0.01)
