@@ -24,14 +24,19 @@
 //     DOWN: w2 rows r..r+63.
 //   Operand B is up to 128 tokens (8 tiles of 16) of the expert, all of them
 //   in one pass when the expert has no more, so its weights are read once.
-// The K loop runs over blocks of two groups through a 4-stage ring in LDS.
-// Global-to-LDS loads (global_load_lds) bring weights, scale bytes, tokens
-// and token scales without passing through registers; a stage is requested
-// three blocks before it is used. LDS layouts (per stage):
-//   weights [wave tile 0..31][row 0..15][group 0..1] 16-byte chunks, so the
-//           two lanes of a row in a load read 32 contiguous bytes (the L2
-//           serves rows in consecutive lanes several times slower)
-//           (a fragment read: lane (i, q) reads dword q of row i: 2-way banks)
+// The K loop runs over blocks of two groups. Global-to-LDS loads
+// (global_load_lds) bring weights, scale bytes, tokens and token scales
+// without passing through registers. Tokens and their scales go through a
+// 4-stage ring of blocks, each requested three blocks before it is used;
+// the weights through a ring of two stages of four groups (two blocks), each
+// requested two blocks before its first use. LDS layouts:
+//   weights [wavefront][tile 0..3][row 0..15][4 chunks of 16 bytes] per stage:
+//           one load per tile, the four consecutive lanes of a row reading its
+//           64 contiguous bytes (the L2 serves 64-byte row pieces far faster
+//           than 32-byte ones or rows in consecutive lanes); row r's chunk c
+//           sits in slot c ^ ((r / 4) % 4), so the fragment reads of one
+//           group (lane (i, q): dword q of row i) fall in 64 distinct banks.
+//           Each wavefront loads and reads only its own rows.
 //   scales  [tile][row 0..15][4 dwords]: the scale bytes of 16 groups, loaded
 //           once per 8 stages into one of two windows; the tiles ordered
 //           (matrix, wavefront, tile within the matrix)
@@ -46,26 +51,27 @@ namespace k3g {
 namespace ib {
 
 constexpr int NW = 8;             // wavefronts per workgroup
-constexpr int GB = 2;             // groups per stage
-constexpr int S = 4;              // stages in the ring
+constexpr int GB = 2;             // groups per block (token stage)
+constexpr int S = 4;              // token stages in the ring
+constexpr int WGS = 4;            // groups per weight stage (two blocks)
 constexpr int TMAX = 8;           // token tiles (of 16) per pass
 constexpr int NTOK = 16 * TMAX;   // tokens per pass
 constexpr int WG_AR = NW * 64;    // operand-A rows per workgroup
 constexpr int TCH = 4 * GB + 1;   // 16-byte chunks per token row in LDS (with the pad)
-constexpr int W_BYTES = WG_AR * GB * 16;     // 16 KB
+constexpr int W_BYTES = WG_AR * WGS * 16;    // 32 KB per weight stage
 constexpr int T_BYTES = NTOK * TCH * 16;     // 18 KB
 constexpr int SWG = 16;                      // groups per window of staged scale bytes
 constexpr int SW_BYTES = WG_AR * SWG;        // 8 KB: 4 dwords of scale bytes per A row
 constexpr int SW_LD = SW_BYTES / 256 / NW;   // scale-window loads per wavefront: 4
 constexpr int SX_BYTES = NTOK * GB * 4;      // 1 KB
-constexpr int W_LD = W_BYTES / 1024 / NW;    // weight loads per wavefront and stage: 2
+constexpr int W_LD = W_BYTES / 1024 / NW;    // weight loads per wavefront and stage: 4, one per tile
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct Lds {
-    char w[S][W_BYTES];
+    char w[2][W_BYTES];
     char t[S][T_BYTES];
     uint32_t ws[2][WG_AR * SWG / 4];
     float sx[S][NTOK * GB];
@@ -86,9 +92,9 @@ __device__ inline bf16x8_t fp4x8_bf16(uint32_t w, float scale) {
 // them fall on wavefront wl (instruction n goes to wavefront n % NW).
 constexpr int tok_instr(int nt) { return (nt * 16 * TCH + 63) / 64; }
 constexpr int sx_instr(int nt) { return (nt * 16 * GB + 63) / 64; }
-// The fewest loads any wavefront issues per stage (the vmcnt bound).
-// (The scale-window loads that every eighth stage adds only make the bound conservative.)
-constexpr int min_loads(int nt) { return W_LD + tok_instr(nt) / NW + (sx_instr(nt) >= NW ? 1 : 0); }
+// The fewest token and token-scale loads any wavefront issues per block (the
+// vmcnt bound; the weight and scale-window loads only add to what is in flight).
+constexpr int min_tok_loads(int nt) { return tok_instr(nt) / NW + (sx_instr(nt) >= NW ? 1 : 0); }
 
 }  // namespace ib
 
@@ -131,17 +137,18 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
         const int r = UP ? rb * (WG_AR / 2) + w * 32 + (k & 1) * 16 + i : rb * WG_AR + w * 64 + k * 16 + i;
         return (uint32_t)min(r, n_out - 1);
     };
-    // weight loads: instruction n = wl + NW*m fills LDS slots 64n + lane, i.e. wave
-    // tiles 2n and 2n+1 (wavefront n/2, tiles k = 2(n%2), 2(n%2)+1: one matrix, n%2 = wl%2)
-    uint32_t w_off[W_LD];
+    // weight loads: this wavefront's tile k, one instruction per weight stage;
+    // lane 4r + c reads chunk c ^ ((r / 4) % 4) of row r. n_out is a multiple of
+    // 128, so a wavefront's rows are all inside the matrix or all past it: the
+    // latter read the matrix's first rows instead (their results are dropped).
+    const int w_row0 = (UP ? rb * (WG_AR / 2) + wl * 32 : rb * WG_AR + wl * 64) < n_out ? 0 : -1;
+    const uint8_t *w_tile[4];
 #pragma unroll
-    for (int m = 0; m < W_LD; ++m) {
-        // [tile][row][group]: the GB lanes of a row read its GB x 16 contiguous bytes
-        const int s = 64 * (wl + NW * m) + lane;
-        const int wt = s / (GB * 16), i = (s % (GB * 16)) / GB, j = s % GB;
-        w_off[m] = arow(wt >> 2, wt & 3, i) * pitch + 16u * (uint32_t)j;
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t r = w_row0 < 0 ? (uint32_t)(UP ? (k & 1) * 16 : k * 16) : arow(wl, k, 0);
+        w_tile[k] = pk[k >> 1] + (size_t)r * pitch;
     }
-    const uint8_t *w_base = pk[wl & 1];
+    const uint32_t w_off = (uint32_t)(lane >> 2) * pitch + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     // scale bytes, staged per window of 16 groups: tile slot ((k>>1)*NW + w)*2 + (k&1)
     // holds wavefront w's tile k, 16 rows x 4 dwords; instruction n = wl + NW*m fills
     // tile slot n (one matrix: n >> 4 = m >> 1), lane -> (row lane/4, dword lane%4)
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
         return arow(s_w, s_k, lane >> 2) * (uint32_t)ngrp;
     };
     const int n_dw = ngrp / 4;  // scale dwords per row
-    const uint32_t lds_w = lds_addr(&L.w[0][0]), lds_t = lds_addr(&L.t[0][0]);
+    const uint32_t lds_w = lds_addr(&L.w[0][0]) + 4096u * (uint32_t)wl, lds_t = lds_addr(&L.t[0][0]);
     const uint32_t lds_ws = lds_addr(&L.ws[0][0]), lds_sx = lds_addr(&L.sx[0][0]);
     const uint32_t tok_row_bytes = (uint32_t)n_in * 2u;
 
@@ -169,8 +176,10 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
             constexpr int NT = decltype(nt_c)::value;
             constexpr int TI = tok_instr(NT), SI = sx_instr(NT);
             constexpr int TPW = (TI + NW - 1) / NW;  // token loads per wavefront, at most
-            // waiting for block b leaves the loads of blocks b+1 and b+2 in flight
-            constexpr int VM = (S - 2) * min_loads(NT);
+            // waiting for block b (its tokens, and the weight stage it reads) leaves
+            // at least the token loads of blocks b+1 and b+2 in flight: weight stage
+            // c is requested at block 2c - 2 before the tokens of block 2c + 1
+            constexpr int VM = (S - 2) * min_tok_loads(NT);
             // token loads of this lane: instruction n = wl + NW*m, slot 64n + lane -> (token, chunk)
             uint32_t t_off[TPW];
 #pragma unroll
@@ -187,25 +196,23 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
                 const int tk = min(s / GB, NT * 16 - 1);
                 x_off = ((uint32_t)L.rows[tk] * (uint32_t)ngrp + (uint32_t)(s % GB)) * 4u;
             }
-            // The loads of one stage, as NPART parts of one instruction each (or
-            // none): 0..W_LD-1 weights, then tokens, token scales, and every
-            // eighth stage the scale window. Block b requests stage b+3 right
-            // after its barrier.
-            constexpr int NPART = W_LD + TPW + 1 + SW_LD;
-            constexpr int NSPREAD = W_LD + TPW + 1;  // the parts every stage has
+            // The token loads of one block, as NPART parts of one instruction
+            // each (or none): tokens, token scales, and every eighth block the
+            // scale window. Block b requests block b+3 right after its barrier,
+            // and an even block b the weight stage b/2 + 1 before that.
+            constexpr int NPART = TPW + 1 + SW_LD;
+            constexpr int NSPREAD = TPW + 1;  // the parts every block has
             auto fetch_part = [&](int blk, int part) {
                 const int buf = blk % S;
                 const int g0 = blk * GB;
-                if (part < W_LD) {
-                    dma16(w_base + 16 * g0, w_off[part], lds_w + buf * W_BYTES + 1024 * (wl + NW * part));
-                } else if (part < W_LD + TPW) {
-                    const int m = part - W_LD;
+                if (part < TPW) {
+                    const int m = part;
                     if (wl + NW * m < TI)
                         dma16((const char *)aqb + 64 * g0, t_off[m], lds_t + buf * T_BYTES + 1024 * (wl + NW * m));
-                } else if (part == W_LD + TPW) {
+                } else if (part == TPW) {
                     if (wl < SI) dma4(as + g0, x_off, lds_sx + buf * SX_BYTES + 256 * wl);
                 } else if ((blk & 7) == 0) {  // the scale window of groups [g0, g0 + 16)
-                    const int m = part - (W_LD + TPW + 1);
+                    const int m = part - (TPW + 1);
                     const int wdw = g0 / 4, wb = (blk >> 3) & 1;
                     dma4(sc[m >> 1], s_off(m) + 4u * (uint32_t)min(wdw + (lane & 3), n_dw - 1),
                          lds_ws + wb * SW_BYTES + 256 * (wl + NW * m));
@@ -215,6 +222,12 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
 #pragma unroll
                 for (int part = 0; part < NPART; ++part) fetch_part(blk, part);
             };
+            // weight stage c: groups [4c, 4c + 4) of the wavefront's 4 tiles
+            auto fetch_w = [&](int c) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    dma16(w_tile[k] + 64 * c, w_off, lds_w + (c & 1) * W_BYTES + 1024 * k);
+            };
 
             f32x4_t acc[4][NT];
 #pragma unroll
@@ -222,6 +235,7 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) acc[k][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+            fetch_w(0);  // n_blocks is even: at least one weight stage
 #pragma unroll
             for (int b = 0; b < S - 1; ++b)
                 if (b < n_blocks) fetch(b);
@@ -229,6 +243,7 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
                 if (blk + S - 2 < n_blocks) wait_vm<VM>();
                 else wait_vm<0>();
                 __syncthreads();  // block blk is in LDS for all; block blk-1's buffer is free
+                if (!(blk & 1) && blk + 2 < n_blocks) fetch_w((blk >> 1) + 1);
                 const bool more = blk + S - 1 < n_blocks;  // a stage to request during this block
                 if (more) {
 #pragma unroll
@@ -241,7 +256,7 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
                 const int buf = blk % S;
                 const int gsel = (blk * GB) & 3;            // byte of group 2*blk in its dword
                 const int sdw = (blk & 7) >> 1;              // that dword in the window
-                const uint32_t *wq = (const uint32_t *)&L.w[buf][0];
+                const uint32_t *wq = (const uint32_t *)&L.w[(blk >> 1) & 1][4096 * wl];
                 const uint32_t *wsd = &L.ws[(blk >> 3) & 1][0];
                 const char *tb = &L.t[buf][0];
                 const float *sxb = &L.sx[buf][0];
@@ -250,7 +265,8 @@ __global__ __launch_bounds__(ib::NW * 64, 1) void moe_idot_bf16_kernel(
                     bf16x8_t a[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const uint32_t w = wq[(((wl * 4 + k) * 16 + col) * GB + j) * 4 + quad];
+                        const int jj = 2 * (blk & 1) + j;  // the group in the weight stage
+                        const uint32_t w = wq[(k * 16 + col) * 16 + 4 * (jj ^ ((col >> 2) & 3)) + quad];
                         const uint32_t sd = wsd[(((((k >> 1) * NW + wl) << 1) + (k & 1)) * 16 + col) * 4 + sdw];
                         const uint32_t sb = (sd >> (8 * (gsel + j))) & 0xFFu;
                         const bool skip = sb == 255u;
