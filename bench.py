@@ -14,7 +14,7 @@ oracle timed on a bounded sample on the host cores.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload decode_b1|decode_b64|prefill_4096_idot|prefill_4096_exact]
-                    [--mfma-decode] [--idot-int8]
+                    [--mfma-decode] [--idot-int8 | --idot-bf16]
 
 The default run (decode_b1) also measures, on the same resident bank:
   other_workloads     short runs of the 64-token EXACT layer (vector and FP4
@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--idot-int8", action="store_true",
                     help="IDOT workloads: run the group dots on the int8 matrix cores (same results; without it the "
                          "library's default, the bf16 matrix cores)")
+    ap.add_argument("--idot-bf16", action="store_true",
+                    help="IDOT workloads: the bf16 matrix-core form, named (the default)")
     ap.add_argument("--mfma-decode", action="store_true",
                     help="EXACT workloads and the block: the expert products on the FP4 matrix cores (x and h as "
                          "e2m1 pieces) whatever the token count")
@@ -90,7 +92,10 @@ def parse():
     ap.add_argument("--bank-experts", type=int, default=0,
                     help="diagnostic: a bank (and router) of this many experts instead of 896, to compare a "
                          "kernel's rate on a smaller allocation (not a configuration of the method)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.idot_int8 and args.idot_bf16:
+        ap.error("--idot-int8 and --idot-bf16 name different forms")
+    return args
 
 
 def expert_bytes(latent, inter):
