@@ -83,6 +83,8 @@ def parse():
                     help="only measure the matrix-core rates and a streaming read (the achievable peaks) and exit")
     ap.add_argument("--expert-only", action="store_true",
                     help="only time one expert on one token and the batch-1 product (for profiling) and exit")
+    ap.add_argument("--stream-only", action="store_true",
+                    help="only the expert streaming tier (bank in host memory, LRU of slots in HBM)")
     ap.add_argument("--block-only", action="store_true",
                     help="only time the 256-token LatentMoE block (for profiling) and exit")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -140,6 +142,10 @@ def main():
         return
     if args.expert_only:
         print(json.dumps({"expert_b1": run_expert(ctx, bankt)}), flush=True)
+        return
+    if args.stream_only:
+        print(json.dumps({"streaming_tier": run_stream(ctx, bankt, configs=((64, 0.1), (256, 0.1), (256, 0.01)),
+                                                       steps=args.stream_steps)}), flush=True)
         return
     if args.block_only:
         print(json.dumps({"block_256": run_block(ctx, bank, form=form_arg)}), flush=True)
@@ -734,7 +740,11 @@ def run_stream(ctx, bankt, configs, steps):
     workload's router (the bias makes some experts hot), 0.01 near-flat use
     (the pages' trained router is balanced to flat use). Host clock around
     `steps` steps after 8 warm-up steps; also the bare pinned host -> HBM copy
-    rate of one expert (17.5 MB) at a time."""
+    rate of one expert (17.5 MB) at a time. Each configuration runs twice from
+    an empty cache with the same tokens: the layer after all of the step's
+    copies (k3g_cache_prepare, then k3g_moe_layer), and the pipelined step
+    (k3g_cache_decode_step: the resident experts' products during the first
+    copy, each copied expert's as soon as its copy lands)."""
     torch, k3g, synth, dev, bank = ctx["torch"], ctx["k3g"], ctx["synth"], ctx["dev"], ctx["bank"]
     L, I, E, K = synth.LATENT, synth.INTER, synth.N_EXPERTS, synth.TOP_K
     off, stride = k3g.bank_layout(L, I)
@@ -765,33 +775,45 @@ def run_stream(ctx, bankt, configs, steps):
         Wd, bd = torch.from_numpy(W).to(dev), torch.from_numpy(b).to(dev)
         arena_t = torch.empty(n_slots * stride, dtype=torch.uint8, device=dev)
         arena = k3g.bank_struct(arena_t, n_slots, L, I, off, stride)
-        cache = k3g.ExpertCache(host, E, arena)
         sh = k3g.shape(n_tokens=1, top_k=K, n_experts=n_slots, latent=L, inter=I, mode=k3g.EXACT)
         ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
 
-        def step(r):
-            k3g.k3g_moe_route(idx, wts, xs[r % n_rot], Wd, bd, K, ws_r)
-            cache.prepare(idx_slot, idx.cpu().numpy(), copy_stream)
-            k3g.k3g_moe_layer(y, xs[r % n_rot], idx_slot, wts, arena, k3g.EXACT, ws)
+        def measure(piped):
+            cache = k3g.ExpertCache(host, E, arena)
 
-        for r in range(8):
-            step(r)
-        torch.cuda.synchronize()
-        s0, _, _ = cache.query()
-        t0 = time.perf_counter()
-        for r in range(steps):
-            step(8 + r)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        s1, _, _ = cache.query()
-        copied = s1["bytes_copied"] - s0["bytes_copied"]
-        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+            def step(r):
+                k3g.k3g_moe_route(idx, wts, xs[r % n_rot], Wd, bd, K, ws_r)
+                if piped:
+                    cache.decode_step(y[0], xs[r % n_rot][0], idx.cpu().numpy()[0], wts[0], k3g.EXACT, ws,
+                                      copy_stream)
+                else:
+                    cache.prepare(idx_slot, idx.cpu().numpy(), copy_stream)
+                    k3g.k3g_moe_layer(y, xs[r % n_rot], idx_slot, wts, arena, k3g.EXACT, ws)
+
+            for r in range(8):
+                step(r)
+            torch.cuda.synchronize()
+            s0, _, _ = cache.query()
+            t0 = time.perf_counter()
+            for r in range(steps):
+                step(8 + r)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            s1, _, _ = cache.query()
+            cache.close()
+            copied = s1["bytes_copied"] - s0["bytes_copied"]
+            hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+            return dt, copied, hits, misses
+
+        dt, copied, hits, misses = measure(False)
+        dtp, copied_p, _, _ = measure(True)
         runs.append({"slots": n_slots, "arena_GB": round(n_slots * stride / 1e9, 2), "router_bias_range": bias_range,
                      "steps": steps,
                      "ms_per_step": round(1e3 * dt / steps, 3), "tokens_per_s": round(steps / dt, 1),
                      "hit_rate": round(hits / max(1, hits + misses), 4),
-                     "copy_GBps": round(copied / dt / 1e9, 2)})
-        cache.close()
+                     "copy_GBps": round(copied / dt / 1e9, 2),
+                     "piped_ms_per_step": round(1e3 * dtp / steps, 3), "piped_tokens_per_s": round(steps / dtp, 1),
+                     "piped_copy_GBps": round(copied_p / dtp / 1e9, 2)})
         del arena_t, ws
         torch.cuda.empty_cache()
     out["runs"] = runs

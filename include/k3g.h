@@ -428,6 +428,28 @@ int k3g_cache_complete(k3g_cache *c);
 int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n_tokens, int top_k,
                       void *copy_stream, void *stream);
 
+/* One decode token through the layer on the arena, with the expert copies
+ * overlapped with the products, one expert at a time ([COLIBRI-K3] "Streaming
+ * design", K3_PIPE: expert j's products run while expert j+1 is read). The
+ * step is planned as k3g_cache_prepare plans it. On copy_stream, after the
+ * work already on `stream`: each missing expert's copy (host-address order),
+ * each followed by an event. On `stream`: the pairs whose experts are
+ * resident first, then each missing expert's pair once its copy has landed
+ * (up-projection with SiTU, then down-projection, per pair), then the
+ * weighted combine in k order. The result equals k3g_moe_layer on the arena
+ * with the step's slot ids bit for bit.
+ *   y, x: device float [latent] (16-byte aligned); idx: host int32 [top_k],
+ *   expert ids (-1 = a dropped entry, K3_TOPP); wts: device float [top_k].
+ *   mode: K3G_EXACT on the vector kernels (K3G_DECODE_VECTOR and
+ *   K3G_DECODE_LUT allowed); other modes K3G_EUNSUPPORTED.
+ *   ws: a k3g_moe_layer workspace for one token, top_k, the arena's shape and
+ *   the same mode (256-byte aligned, ws_bytes >= k3g_workspace_bytes).
+ * The host staging of the cache is reused: the call waits for the previous
+ * step's host-to-device copy of it before planning. 1 <= top_k <= 64;
+ * K3G_ENOSPACE as k3g_cache_plan, with nothing enqueued. */
+int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t *idx, const float *wts, int top_k,
+                          int mode, void *ws, size_t ws_bytes, void *copy_stream, void *stream);
+
 /* Counters, and optionally the expert -> slot map (int32 [n_total], -1 = not
  * resident) and the request histogram (uint64 [n_total]). */
 int k3g_cache_query(const k3g_cache *c, k3g_cache_stats *stats, int32_t *slot_of, uint64_t *hist);

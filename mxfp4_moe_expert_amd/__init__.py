@@ -109,6 +109,7 @@ def lib():
         L.k3g_cache_plan.argtypes = [P, P, P, P, P, P, i, i]
         L.k3g_cache_complete.argtypes = [P]
         L.k3g_cache_prepare.argtypes = [P, P, P, i, i, P, P]
+        L.k3g_cache_decode_step.argtypes = [P, P, P, P, P, i, i, P, C.c_size_t, P, P]
         L.k3g_cache_query.argtypes = [P, P, P, P]
         L.k3g_moe_route_topp.argtypes = [P, P, P, P, P, i, i, i, i, C.c_float, P, sz, P]
         L.k3g_moe_layer.argtypes = [P, P, P, P, P, i, i, i, P, sz, P]
@@ -541,6 +542,25 @@ class ExpertCache:
             raise ValueError("shape mismatch")
         _check("k3g_cache_prepare", lib().k3g_cache_prepare(self._c, _ptr(idx_slot), idx.ctypes.data, T, K,
                                                              C.c_void_p(copy_stream.cuda_stream), _stream(stream)))
+
+    def decode_step(self, y: torch.Tensor, x: torch.Tensor, idx, wts: torch.Tensor, mode: int, ws: torch.Tensor,
+                    copy_stream, stream=None):
+        """One decode token on the arena with each missing expert's copy
+        overlapped with the products (k3g_cache_decode_step). idx: the token's
+        expert ids on the host (top_k, -1 = dropped); y, x: device float32
+        [latent]; wts: device float32 [top_k]; ws: a one-token layer workspace."""
+        import numpy as np
+        idx = np.ascontiguousarray(np.asarray(idx).reshape(-1), dtype=np.int32)
+        K = idx.size
+        _dev(y, torch.float32, "y")
+        _dev(x, torch.float32, "x")
+        _dev(wts, torch.float32, "wts")
+        _dev(ws, torch.uint8, "ws")
+        if y.numel() != x.numel() or wts.numel() != K:
+            raise ValueError("shape mismatch")
+        _check("k3g_cache_decode_step", lib().k3g_cache_decode_step(
+            self._c, _ptr(y), _ptr(x), idx.ctypes.data, _ptr(wts), K, mode, _ptr(ws), ws.numel(),
+            C.c_void_p(copy_stream.cuda_stream), _stream(stream)))
 
     def query(self):
         """(stats dict, slot_of numpy int32 [n_total], histogram numpy uint64 [n_total])."""

@@ -300,6 +300,11 @@ int mxfp4_ok(const uint8_t *packed, const uint8_t *scales, int in, int rows) {
 
 }  // namespace
 
+namespace k3g {
+// the device check, for the entry points of the other sources (cache.hip)
+int device_ok() { return check_device(); }
+}  // namespace k3g
+
 extern "C" {
 
 const char *k3g_status_string(int status) {

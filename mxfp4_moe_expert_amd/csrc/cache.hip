@@ -13,6 +13,9 @@
 // so the layer runs unchanged on the slot bank. All state is host-side; the
 // copies go out on the caller's copy stream as hipMemcpyAsync, one per
 // missing expert (six tensors back to back = one copy), in host-address order.
+// The pages' loader threads that overlap expert j's products with expert
+// j+1's read become, for a decode token, an event after each copy and the
+// pair's two launches queued behind that event on the compute stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -21,12 +24,28 @@
 #include <new>
 #include <vector>
 
-#include "k3g.h"
+#include "k3g_common.h"
+
+namespace k3g {
+// launchers (gemv.hip) and the device check (abi.hip)
+int launch_moe_up_exact(float *h, const float *x, const BankDev &bank, const int32_t *active, const int32_t *offsets,
+                        const int32_t *perm, int top_k, int latent, int inter, int max_slots, int n_pairs, bool lut,
+                        const Route1 &rt, hipStream_t st);
+int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, const int32_t *active,
+                          const int32_t *offsets, const int32_t *perm, int latent, int inter, int max_slots,
+                          bool multi_pairs, bool lut, hipStream_t st);
+int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
+                   int latent, hipStream_t st);
+int device_ok();
+}  // namespace k3g
 
 namespace {
 
 constexpr int32_t kEmpty = -1;     // slot holds nothing, free to take
 constexpr int32_t kInflight = -2;  // slot reserved by this batch's prefetch
+constexpr int kPipeMax = 64;       // pairs of one decode step (the largest top_k)
+
+inline bool is_aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
@@ -45,6 +64,7 @@ struct k3g_cache {
     int64_t tick = 0;
     k3g_cache_stats stats{};
     hipEvent_t ev_prev = nullptr, ev_copy = nullptr;
+    hipEvent_t ev_pipe[kPipeMax] = {};  // one per copy of a pipelined decode step
     int32_t *idx_stage = nullptr;    // pinned host staging of the rewritten ids
     size_t idx_stage_n = 0;
 };
@@ -73,6 +93,8 @@ void k3g_cache_destroy(k3g_cache *c) {
     if (!c) return;
     if (c->ev_prev) (void)hipEventDestroy(c->ev_prev);
     if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+    for (hipEvent_t e : c->ev_pipe)
+        if (e) (void)hipEventDestroy(e);
     if (c->idx_stage) (void)hipHostFree(c->idx_stage);
     delete c;
 }
@@ -167,19 +189,19 @@ int k3g_cache_complete(k3g_cache *c) {
     return K3G_OK;
 }
 
-int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n_tokens, int top_k,
-                      void *copy_stream, void *stream) {
-    if (!c || !c->host_bank || n_tokens < 0 || top_k < 1) return K3G_EINVAL;
-    const size_t P = (size_t)n_tokens * top_k;
-    if (P == 0) return K3G_OK;
-    if (!idx || !idx_slot) return K3G_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// The events, and the pinned staging of P ids: the previous step's copy of
+// the staging must be done before it is written again.
+int stage_for(k3g_cache *c, size_t P) {
     if (!c->ev_prev) {
         if (hipEventCreateWithFlags(&c->ev_prev, hipEventDisableTiming) != hipSuccess ||
             hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming) != hipSuccess)
             return K3G_EHIP;
     }
-    // the staging buffer is reused: the previous step's copy of it must be done
-    if (c->ev_copy && hipEventSynchronize(c->ev_copy) != hipSuccess) return K3G_EHIP;
+    if (hipEventSynchronize(c->ev_copy) != hipSuccess) return K3G_EHIP;
     if (c->idx_stage_n < P) {
         if (c->idx_stage) (void)hipHostFree(c->idx_stage);
         c->idx_stage = nullptr;
@@ -188,6 +210,21 @@ int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n
             return K3G_ENOSPACE;
         c->idx_stage_n = P;
     }
+    return K3G_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n_tokens, int top_k,
+                      void *copy_stream, void *stream) {
+    if (!c || !c->host_bank || n_tokens < 0 || top_k < 1) return K3G_EINVAL;
+    const size_t P = (size_t)n_tokens * top_k;
+    if (P == 0) return K3G_OK;
+    if (!idx || !idx_slot) return K3G_EINVAL;
+    const int rs = stage_for(c, P);
+    if (rs != K3G_OK) return rs;
     c->step_copies_e.resize((size_t)c->n_slots);
     c->step_copies_s.resize((size_t)c->n_slots);
     int32_t nc = 0;
@@ -209,6 +246,96 @@ int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n
         return K3G_EHIP;
     if (hipEventRecord(c->ev_copy, cs) != hipSuccess || hipStreamWaitEvent(st, c->ev_copy, 0) != hipSuccess)
         return K3G_EHIP;
+    return k3g_cache_complete(c);
+}
+
+int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t *idx, const float *wts, int top_k,
+                          int mode, void *ws, size_t ws_bytes, void *copy_stream, void *stream) {
+    using namespace k3g;
+    if (!c || !c->host_bank || !y || !x || !idx || !wts || !ws || top_k < 1 || top_k > kPipeMax) return K3G_EINVAL;
+    // one token on the vector kernels: EXACT, the LDS table optional
+    if ((mode & ~(K3G_DECODE_LUT | K3G_DECODE_VECTOR)) != K3G_EXACT) return K3G_EUNSUPPORTED;
+    const k3g_expert_bank &A = c->arena;
+    const int latent = A.latent, inter = A.inter;
+    k3g_shape sh = {1, top_k, A.n_experts, latent, inter, 0, 0, mode};
+    k3g_ws_layout L;
+    int rc = k3g_workspace_layout(&L, K3G_OP_MOE_LAYER, &sh);
+    if (rc != K3G_OK) return rc;
+    if (ws_bytes < L.total) return K3G_ENOSPACE;
+    if (!is_aligned(x, 16) || !is_aligned(y, 16) || !is_aligned(ws, 256) || !is_aligned(wts, 4)) return K3G_EALIGN;
+    if ((uintptr_t)y < (uintptr_t)x + sizeof(float) * latent && (uintptr_t)x < (uintptr_t)y + sizeof(float) * latent)
+        return K3G_EINVAL;
+    if (!A.base) return K3G_EINVAL;
+    if (latent / kGroup > 256 || inter / kGroup > 256) return K3G_EUNSUPPORTED;
+    for (int i = 0; i < 6; i += 2)
+        if (!is_aligned(A.base + A.off[i], 16) || A.stride % 16) return K3G_EALIGN;
+    for (int i = 1; i < 6; i += 2)
+        if (!is_aligned(A.base + A.off[i], 4)) return K3G_EALIGN;
+    for (int k = 0; k < top_k; ++k)
+        if (idx[k] < -1 || idx[k] >= c->n_total) return K3G_EINVAL;
+    if ((rc = device_ok()) != K3G_OK) return rc;
+    if ((rc = stage_for(c, (size_t)top_k)) != K3G_OK) return rc;
+    for (int i = 0; i < kPipeMax; ++i)
+        if (!c->ev_pipe[i] && hipEventCreateWithFlags(&c->ev_pipe[i], hipEventDisableTiming) != hipSuccess)
+            return K3G_EHIP;
+
+    // the plan: slot of each pair, and the copies (at most one per pair)
+    int32_t slot[kPipeMax];
+    c->step_copies_e.resize((size_t)c->n_slots);
+    c->step_copies_s.resize((size_t)c->n_slots);
+    int32_t nc = 0;
+    if ((rc = k3g_cache_plan(c, slot, c->step_copies_e.data(), c->step_copies_s.data(), &nc, idx, 1, top_k)) !=
+        K3G_OK)
+        return rc;
+    // pair k's products go to ypair row k, so the combine reads row k for pair k
+    for (int k = 0; k < top_k; ++k) c->idx_stage[k] = slot[k] >= 0 ? k : -1;
+
+    char *w = (char *)ws;
+    float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
+    int32_t *inv = (int32_t *)(w + L.inv);
+    const bool lut = (mode & K3G_DECODE_LUT) != 0;
+    hipStream_t cs = (hipStream_t)copy_stream, st = (hipStream_t)stream;
+    auto pair = [&](int k) {
+        BankDev b;
+        b.base = A.base + (size_t)slot[k] * A.stride;
+        b.stride = 0;
+        for (int i = 0; i < 6; ++i) b.off[i] = A.off[i];
+        float *hk = h + (size_t)k * inter;
+        const int r = launch_moe_up_exact(hk, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut, Route1{},
+                                          st);
+        if (r != K3G_OK) return r;
+        return launch_moe_down_exact(ypair + (size_t)k * latent, hk, b, nullptr, nullptr, nullptr, latent, inter, 1,
+                                     false, lut, st);
+    };
+    auto copied = [&](int k) {
+        for (int32_t i = 0; i < nc; ++i)
+            if (c->step_copies_s[i] == slot[k]) return i;
+        return -1;
+    };
+    // the slots about to be overwritten may still be read by work already on
+    // `stream`: the copies start after it
+    if (hipEventRecord(c->ev_prev, st) != hipSuccess || hipStreamWaitEvent(cs, c->ev_prev, 0) != hipSuccess)
+        return K3G_EHIP;
+    const size_t stride = (size_t)A.stride;
+    for (int32_t i = 0; i < nc; ++i) {
+        const uint8_t *src = c->host_bank + (size_t)c->step_copies_e[i] * stride;
+        uint8_t *dst = const_cast<uint8_t *>(A.base) + (size_t)c->step_copies_s[i] * stride;
+        if (hipMemcpyAsync(dst, src, stride, hipMemcpyHostToDevice, cs) != hipSuccess ||
+            hipEventRecord(c->ev_pipe[i], cs) != hipSuccess)
+            return K3G_EHIP;
+    }
+    if (hipMemcpyAsync(inv, c->idx_stage, sizeof(int32_t) * top_k, hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipEventRecord(c->ev_copy, st) != hipSuccess)
+        return K3G_EHIP;
+    // the resident experts' pairs, then each copied expert's once it has landed
+    for (int k = 0; k < top_k; ++k)
+        if (slot[k] >= 0 && copied(k) < 0 && (rc = pair(k)) != K3G_OK) return rc;
+    for (int32_t i = 0; i < nc; ++i) {
+        if (hipStreamWaitEvent(st, c->ev_pipe[i], 0) != hipSuccess) return K3G_EHIP;
+        for (int k = 0; k < top_k; ++k)
+            if (slot[k] == c->step_copies_s[i] && (rc = pair(k)) != K3G_OK) return rc;
+    }
+    if ((rc = launch_combine(y, ypair, wts, inv, 1, top_k, latent, st)) != K3G_OK) return rc;
     return k3g_cache_complete(c);
 }
 

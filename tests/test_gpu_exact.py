@@ -780,3 +780,98 @@ def test_cache_layer_decode_full(k3g, full_bank, decode):
     steps.append(steps[0])  # a repeated token: all hits if its experts are still resident
     stats, ref = run_cached_steps(k3g, bankt, bank, 32, steps, decode)
     assert stats["misses"] == ref.misses and stats["bytes_copied"] == ref.misses * bank.stride
+
+
+def run_piped_steps(k3g, bankt, bank, n_slots, steps, mode=0):
+    """Each decode token through k3g_cache_decode_step (each missing expert's
+    copy overlapped with the products, one expert at a time) on one arena, and
+    through k3g_cache_prepare + k3g_moe_layer on a second arena with a cache of
+    its own: the same policy on the same history, so the slot maps and the
+    counters agree, and both results equal the layer on the resident bank bit
+    for bit (the same kernels' rows on the same bytes, combined in k order)."""
+    E, latent, inter = bank.n_experts, bank.latent, bank.inter
+    off, stride = k3g.bank_layout(latent, inter)
+    host_bank = torch.empty(E * stride, dtype=torch.uint8, pin_memory=True)
+    host_bank.copy_(bankt[:E * stride])
+    caches = []
+    for _ in range(2):
+        arena_t = torch.zeros(n_slots * stride, dtype=torch.uint8, device="cuda")
+        arena = k3g.bank_struct(arena_t, n_slots, latent, inter, off, stride)
+        caches.append((k3g.ExpertCache(host_bank, E, arena), arena, arena_t))
+    (piped, arena_p, _), (staged, arena_s, _) = caches
+    copy_stream = torch.cuda.Stream()
+    for r, (x, idx, wts) in enumerate(steps):
+        K = idx.shape[1]
+        print(f"piped decode step {r} mode {mode:#x}", flush=True)
+        y_full, _, _ = run_layer(k3g, x, idx, wts, bank, k3g.EXACT | mode)
+        idx_slot = torch.empty((1, K), dtype=torch.int32, device="cuda")
+        staged.prepare(idx_slot, idx, copy_stream)
+        y_s, _, _ = run_layer_dev(k3g, x, idx_slot, wts, arena_s, k3g.EXACT | mode)
+        sh = k3g.shape(n_tokens=1, top_k=K, n_experts=n_slots, latent=latent, inter=inter, mode=k3g.EXACT | mode)
+        ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+        y_p = torch.full((latent,), float("nan"), dtype=torch.float32, device="cuda")
+        piped.decode_step(y_p, dev(x[0]), idx[0], dev(wts[0]), k3g.EXACT | mode, ws, copy_stream)
+        y_p = host(y_p)
+        assert np.array_equal(y_s.view(np.uint32), y_full.view(np.uint32))
+        assert np.array_equal(y_p.view(np.uint32), y_full[0].view(np.uint32)), f"piped step {r} differs"
+    (sp, so_p, hi_p), (ss, so_s, hi_s) = piped.query(), staged.query()
+    assert sp == ss and np.array_equal(so_p, so_s) and np.array_equal(hi_p, hi_s)
+    for c, _, _ in caches:
+        c.close()
+    return sp
+
+
+@pytest.mark.parametrize("mode", [0, 0x100], ids=["cvt", "lut"])
+def test_cache_decode_step_small(k3g, mode):
+    E, latent, inter, K = 24, 256, 128, 4
+    src, bankt, bank = make_bank(k3g, 83, E, latent, inter, 120, 123, 0.01)
+    W, b = synth.router(83, E, latent, 0.05)  # 22 of the 24 experts used: hits, misses and evictions
+    steps = []
+    for r in range(14):
+        x = synth.activations(83, 1, latent, key=r)
+        idx, wts, _ = oracle.route(x, W, b, K, top_p=0.8 if r % 3 == 2 else 0.0)
+        steps.append((x, idx, wts))
+    steps.append(steps[1])  # a repeated token
+    stats = run_piped_steps(k3g, bankt, bank, 9, steps, mode)
+    assert stats["evictions"] > 0 and stats["hits"] > 0 and stats["misses"] > 0
+
+
+def test_cache_decode_step_full(k3g, full_bank):
+    # one token per step, 896 experts in host memory, 32 slots in HBM
+    src, bankt, bank = full_bank
+    W, b = synth.router(synth.SEED_BASE + 2, 896, 3584, 0.1)
+    steps = []
+    for r in range(5):
+        x = synth.activations(synth.SEED_BASE + 2, 1, 3584, key=r)
+        idx, wts, _ = oracle.route(x, W, b, 16)
+        steps.append((x, idx, wts))
+    steps.append(steps[0])
+    stats = run_piped_steps(k3g, bankt, bank, 32, steps)
+    assert stats["misses"] > 0
+
+
+def test_cache_decode_step_refuses(k3g):
+    E, latent, inter = 8, 256, 128
+    src, bankt, bank = make_bank(k3g, 84, E, latent, inter, 120, 123, 0.0)
+    off, stride = k3g.bank_layout(latent, inter)
+    host = torch.empty(E * stride, dtype=torch.uint8, pin_memory=True)
+    host.copy_(bankt[:E * stride])
+    arena_t = torch.zeros(4 * stride, dtype=torch.uint8, device="cuda")
+    cache = k3g.ExpertCache(host, E, k3g.bank_struct(arena_t, 4, latent, inter, off, stride))
+    cs = torch.cuda.Stream()
+    y = torch.empty(latent, dtype=torch.float32, device="cuda")
+    x = torch.zeros(latent, dtype=torch.float32, device="cuda")
+    w = torch.ones(2, dtype=torch.float32, device="cuda")
+    sh = k3g.shape(n_tokens=1, top_k=2, n_experts=4, latent=latent, inter=inter, mode=k3g.EXACT)
+    ws = k3g.workspace(k3g.OP_MOE_LAYER, sh)
+    lib = k3g.lib()
+    call = lambda idx, mode, nbytes: lib.k3g_cache_decode_step(  # noqa: E731
+        cache._c, y.data_ptr(), x.data_ptr(), np.asarray(idx, np.int32).ctypes.data, w.data_ptr(), 2, mode,
+        ws.data_ptr(), nbytes, k3g.C.c_void_p(cs.cuda_stream), k3g.C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert call([0, 1], k3g.IDOT, ws.numel()) == -5  # K3G_EUNSUPPORTED: the vector kernels only
+    assert call([0, 1], k3g.DECODE_MFMA, ws.numel()) == -5
+    assert call([0, 9], k3g.EXACT, ws.numel()) == -1  # K3G_EINVAL: an expert id past the host bank
+    assert call([0, 1], k3g.EXACT, 0) == -3  # K3G_ENOSPACE: the workspace
+    stats, _, _ = cache.query()
+    assert stats["steps"] == 0  # nothing planned by a refused call
+    cache.close()

@@ -94,3 +94,21 @@ def test_library_planner_matches_the_oracle(k3g, seed):
     assert slot_of.tolist() == [ref.where.get(e, -1) for e in range(n_total)]
     assert stats["misses"] > 0 and stats["hits"] > 0 and stats["evictions"] > 0
     cache.close()
+
+
+def test_decode_step_refuses_on_the_host(k3g):
+    # no cache, or a plan-only cache (no host bank to copy from): K3G_EINVAL
+    # before any device work, and nothing planned
+    L = k3g.lib()
+    fake = k3g.C.c_void_p(4096)
+    idx = np.array([0, 1], np.int32)
+    assert L.k3g_cache_decode_step(None, fake, fake, idx.ctypes.data, fake, 2, 0, fake, 1 << 20, None, None) == -1
+    arena = k3g.ExpertBank()
+    arena.base = None
+    arena.stride = 4096
+    arena.n_experts = 4
+    cache = k3g.ExpertCache(None, 8, arena)
+    assert L.k3g_cache_decode_step(cache._c, fake, fake, idx.ctypes.data, fake, 2, 0, fake, 1 << 20, None,
+                                   None) == -1
+    assert cache.query()[0]["steps"] == 0
+    cache.close()
