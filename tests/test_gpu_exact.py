@@ -875,3 +875,20 @@ def test_cache_decode_step_refuses(k3g):
     stats, _, _ = cache.query()
     assert stats["steps"] == 0  # nothing planned by a refused call
     cache.close()
+
+
+def test_cache_decode_step_edges(k3g):
+    # a token whose entries are all dropped (no pairs, no copies: y = 0), then
+    # top_k = 1, each against the layer on the arena after k3g_cache_prepare
+    E, latent, inter = 8, 256, 128
+    src, bankt, bank = make_bank(k3g, 87, E, latent, inter, 120, 123, 0.01)
+    W, b = synth.router(87, E, latent, 0.1)
+    x = synth.activations(87, 1, latent)
+    idx2, wts2, _ = oracle.route(x, W, b, 2)
+    idx1, wts1, _ = oracle.route(x, W, b, 1)
+    dropped = np.full((1, 2), -1, np.int32)
+    steps = [(x, dropped, wts2), (x, idx2, wts2)]
+    stats = run_piped_steps(k3g, bankt, bank, 3, steps)
+    assert stats["misses"] == 2 and stats["hits"] == 0
+    stats = run_piped_steps(k3g, bankt, bank, 3, [(x, idx1, wts1), (x, idx1, wts1)])
+    assert stats["misses"] == 1 and stats["hits"] == 1
