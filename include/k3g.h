@@ -434,9 +434,10 @@ int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n
  * step is planned as k3g_cache_prepare plans it. On copy_stream, after the
  * work already on `stream`: each missing expert's copy (host-address order),
  * each followed by an event. On `stream`: the pairs whose experts are
- * resident first, then each missing expert's pair once its copy has landed
- * (up-projection with SiTU, then down-projection, per pair), then the
- * weighted combine in k order. The result equals k3g_moe_layer on the arena
+ * resident first, in one up-projection (with SiTU) and one down-projection
+ * launch over a pair table copied ahead of the experts, then each missing
+ * expert's pair once its copy has landed (its own up and down launch), then
+ * the weighted combine in k order. The result equals k3g_moe_layer on the arena
  * with the step's slot ids bit for bit.
  *   y, x: device float [latent] (16-byte aligned); idx: host int32 [top_k],
  *   expert ids (-1 = a dropped entry, K3_TOPP); wts: device float [top_k].

@@ -65,6 +65,7 @@ struct k3g_cache {
     k3g_cache_stats stats{};
     hipEvent_t ev_prev = nullptr, ev_copy = nullptr;
     hipEvent_t ev_pipe[kPipeMax] = {};  // one per copy of a pipelined decode step
+    hipEvent_t ev_meta = nullptr;       // its pair table has landed
     int32_t *idx_stage = nullptr;    // pinned host staging of the rewritten ids
     size_t idx_stage_n = 0;
 };
@@ -95,6 +96,7 @@ void k3g_cache_destroy(k3g_cache *c) {
     if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
     for (hipEvent_t e : c->ev_pipe)
         if (e) (void)hipEventDestroy(e);
+    if (c->ev_meta) (void)hipEventDestroy(c->ev_meta);
     if (c->idx_stage) (void)hipHostFree(c->idx_stage);
     delete c;
 }
@@ -274,10 +276,13 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
     for (int k = 0; k < top_k; ++k)
         if (idx[k] < -1 || idx[k] >= c->n_total) return K3G_EINVAL;
     if ((rc = device_ok()) != K3G_OK) return rc;
-    if ((rc = stage_for(c, (size_t)top_k)) != K3G_OK) return rc;
+    const int E = A.n_experts;
+    // staging: inv [top_k], active [E + 1], offsets [E + 1], perm [top_k]
+    if ((rc = stage_for(c, (size_t)(2 * top_k + 2 * (E + 1)))) != K3G_OK) return rc;
     for (int i = 0; i < kPipeMax; ++i)
         if (!c->ev_pipe[i] && hipEventCreateWithFlags(&c->ev_pipe[i], hipEventDisableTiming) != hipSuccess)
             return K3G_EHIP;
+    if (!c->ev_meta && hipEventCreateWithFlags(&c->ev_meta, hipEventDisableTiming) != hipSuccess) return K3G_EHIP;
 
     // the plan: slot of each pair, and the copies (at most one per pair)
     int32_t slot[kPipeMax];
@@ -287,36 +292,75 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
     if ((rc = k3g_cache_plan(c, slot, c->step_copies_e.data(), c->step_copies_s.data(), &nc, idx, 1, top_k)) !=
         K3G_OK)
         return rc;
-    // pair k's products go to ypair row k, so the combine reads row k for pair k
-    for (int k = 0; k < top_k; ++k) c->idx_stage[k] = slot[k] >= 0 ? k : -1;
-
-    char *w = (char *)ws;
-    float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
-    int32_t *inv = (int32_t *)(w + L.inv);
-    const bool lut = (mode & K3G_DECODE_LUT) != 0;
-    hipStream_t cs = (hipStream_t)copy_stream, st = (hipStream_t)stream;
-    auto pair = [&](int k) {
-        BankDev b;
-        b.base = A.base + (size_t)slot[k] * A.stride;
-        b.stride = 0;
-        for (int i = 0; i < 6; ++i) b.off[i] = A.off[i];
-        float *hk = h + (size_t)k * inter;
-        const int r = launch_moe_up_exact(hk, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut, Route1{},
-                                          st);
-        if (r != K3G_OK) return r;
-        return launch_moe_down_exact(ypair + (size_t)k * latent, hk, b, nullptr, nullptr, nullptr, latent, inter, 1,
-                                     false, lut, st);
-    };
-    auto copied = [&](int k) {
+    auto copy_of = [&](int k) {
         for (int32_t i = 0; i < nc; ++i)
             if (c->step_copies_s[i] == slot[k]) return i;
         return -1;
     };
+    // The pair table. The resident experts' pairs come first, in slot order,
+    // as one bucket (active slots, offsets by slot, perm = pair), so that one
+    // up and one down launch take them all; then each copied expert's pairs
+    // in copy order. inv: pair -> row of h and ypair (-1: dropped entry).
+    int32_t *st_inv = c->idx_stage, *st_act = st_inv + top_k, *st_off = st_act + (E + 1), *st_perm = st_off + (E + 1);
+    for (int s = 0; s <= E; ++s) st_off[s] = 0;
+    int n_hit = 0;
+    for (int k = 0; k < top_k; ++k)
+        if (slot[k] >= 0 && copy_of(k) < 0) {
+            ++st_off[slot[k] + 1];
+            ++n_hit;
+        }
+    int n_hit_slots = 0;
+    for (int s = 0; s < E; ++s) {
+        if (st_off[s + 1] > 0) st_act[1 + n_hit_slots++] = s;
+        st_off[s + 1] += st_off[s];
+    }
+    st_act[0] = n_hit_slots;
+    int next = n_hit;
+    for (int k = 0; k < top_k; ++k) st_inv[k] = -1;
+    for (int s = 0, pos = 0; s < E && pos < n_hit; ++s)
+        for (int k = 0; k < top_k; ++k)
+            if (slot[k] == s && copy_of(k) < 0) {
+                st_perm[pos] = k;
+                st_inv[k] = pos++;
+            }
+    for (int32_t i = 0; i < nc; ++i)
+        for (int k = 0; k < top_k; ++k)
+            if (slot[k] == c->step_copies_s[i]) st_inv[k] = next++;
+
+    char *w = (char *)ws;
+    float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
+    int32_t *inv = (int32_t *)(w + L.inv), *active = (int32_t *)(w + L.active);
+    int32_t *offsets = (int32_t *)(w + L.offsets), *perm = (int32_t *)(w + L.perm);
+    const bool lut = (mode & K3G_DECODE_LUT) != 0;
+    hipStream_t cs = (hipStream_t)copy_stream, st = (hipStream_t)stream;
+    BankDev bank;
+    bank.base = A.base;
+    bank.stride = A.stride;
+    for (int i = 0; i < 6; ++i) bank.off[i] = A.off[i];
+    // one copied expert's pair: up-projection with SiTU, then down-projection, at its row
+    auto pair = [&](int k) {
+        BankDev b = bank;
+        b.base = A.base + (size_t)slot[k] * A.stride;
+        b.stride = 0;
+        const size_t row = (size_t)st_inv[k];
+        float *hk = h + row * inter;
+        const int r = launch_moe_up_exact(hk, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut, Route1{},
+                                          st);
+        if (r != K3G_OK) return r;
+        return launch_moe_down_exact(ypair + row * latent, hk, b, nullptr, nullptr, nullptr, latent, inter, 1, false,
+                                     lut, st);
+    };
     // the slots about to be overwritten may still be read by work already on
-    // `stream`: the copies start after it
+    // `stream`: the copy stream starts after it, with the pair table first
     if (hipEventRecord(c->ev_prev, st) != hipSuccess || hipStreamWaitEvent(cs, c->ev_prev, 0) != hipSuccess)
         return K3G_EHIP;
     const size_t stride = (size_t)A.stride;
+    if (hipMemcpyAsync(inv, st_inv, sizeof(int32_t) * top_k, hipMemcpyHostToDevice, cs) != hipSuccess ||
+        hipMemcpyAsync(active, st_act, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, cs) != hipSuccess ||
+        hipMemcpyAsync(offsets, st_off, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, cs) != hipSuccess ||
+        hipMemcpyAsync(perm, st_perm, sizeof(int32_t) * top_k, hipMemcpyHostToDevice, cs) != hipSuccess ||
+        hipEventRecord(c->ev_meta, cs) != hipSuccess)
+        return K3G_EHIP;
     for (int32_t i = 0; i < nc; ++i) {
         const uint8_t *src = c->host_bank + (size_t)c->step_copies_e[i] * stride;
         uint8_t *dst = const_cast<uint8_t *>(A.base) + (size_t)c->step_copies_s[i] * stride;
@@ -324,12 +368,18 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
             hipEventRecord(c->ev_pipe[i], cs) != hipSuccess)
             return K3G_EHIP;
     }
-    if (hipMemcpyAsync(inv, c->idx_stage, sizeof(int32_t) * top_k, hipMemcpyHostToDevice, st) != hipSuccess ||
-        hipEventRecord(c->ev_copy, st) != hipSuccess)
+    // the staging is read by the table's copies: the next step waits for them
+    if (hipStreamWaitEvent(st, c->ev_meta, 0) != hipSuccess || hipEventRecord(c->ev_copy, st) != hipSuccess)
         return K3G_EHIP;
-    // the resident experts' pairs, then each copied expert's once it has landed
-    for (int k = 0; k < top_k; ++k)
-        if (slot[k] >= 0 && copied(k) < 0 && (rc = pair(k)) != K3G_OK) return rc;
+    // the resident experts' pairs in one up and one down launch, then each
+    // copied expert's pair once its copy has landed
+    if (n_hit > 0) {
+        if ((rc = launch_moe_up_exact(h, x, bank, active, offsets, perm, top_k, latent, inter, n_hit_slots, n_hit,
+                                      lut, Route1{}, st)) != K3G_OK ||
+            (rc = launch_moe_down_exact(ypair, h, bank, active, offsets, perm, latent, inter, n_hit_slots, false, lut,
+                                        st)) != K3G_OK)
+            return rc;
+    }
     for (int32_t i = 0; i < nc; ++i) {
         if (hipStreamWaitEvent(st, c->ev_pipe[i], 0) != hipSuccess) return K3G_EHIP;
         for (int k = 0; k < top_k; ++k)
