@@ -315,14 +315,18 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
         st_off[s + 1] += st_off[s];
     }
     st_act[0] = n_hit_slots;
-    int next = n_hit;
-    for (int k = 0; k < top_k; ++k) st_inv[k] = -1;
-    for (int s = 0, pos = 0; s < E && pos < n_hit; ++s)
-        for (int k = 0; k < top_k; ++k)
-            if (slot[k] == s && copy_of(k) < 0) {
-                st_perm[pos] = k;
-                st_inv[k] = pos++;
-            }
+    int next = 0;
+    for (int k = 0; k < top_k; ++k) {
+        st_inv[k] = -1;
+        if (slot[k] < 0 || copy_of(k) >= 0) continue;
+        int at = next++;  // stable insertion by slot: equal slots keep k order
+        while (at > 0 && slot[st_perm[at - 1]] > slot[k]) {
+            st_perm[at] = st_perm[at - 1];
+            --at;
+        }
+        st_perm[at] = k;
+    }
+    for (int pos = 0; pos < n_hit; ++pos) st_inv[st_perm[pos]] = pos;
     for (int32_t i = 0; i < nc; ++i)
         for (int k = 0; k < top_k; ++k)
             if (slot[k] == c->step_copies_s[i]) st_inv[k] = next++;
