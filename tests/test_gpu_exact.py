@@ -887,8 +887,12 @@ def test_cache_decode_step_edges(k3g):
     idx2, wts2, _ = oracle.route(x, W, b, 2)
     idx1, wts1, _ = oracle.route(x, W, b, 1)
     dropped = np.full((1, 2), -1, np.int32)
-    steps = [(x, dropped, wts2), (x, idx2, wts2)]
+    e0 = int(idx2[0, 0])
+    e_new = next(e for e in range(E) if e not in idx2[0])
+    twice_hit = np.array([[e0, e0]], np.int32)  # one resident expert named twice
+    twice_miss = np.array([[e_new, e_new]], np.int32)  # one missing expert named twice: one copy
+    steps = [(x, dropped, wts2), (x, idx2, wts2), (x, twice_hit, wts2), (x, twice_miss, wts2)]
     stats = run_piped_steps(k3g, bankt, bank, 3, steps)
-    assert stats["misses"] == 2 and stats["hits"] == 0
+    assert stats["misses"] == 3 and stats["hits"] > 0
     stats = run_piped_steps(k3g, bankt, bank, 3, [(x, idx1, wts1), (x, idx1, wts1)])
     assert stats["misses"] == 1 and stats["hits"] == 1
