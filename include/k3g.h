@@ -437,12 +437,13 @@ int k3g_cache_prepare(k3g_cache *c, int32_t *idx_slot, const int32_t *idx, int n
  * resident first, in one up-projection (with SiTU) and one down-projection
  * launch over a pair table copied ahead of the experts, then each missing
  * expert's pair once its copy has landed (its own up and down launch), then
- * the weighted combine in k order. The result equals k3g_moe_layer on the arena
+ * the weighted combine in k order; in IDOT mode x is quantised first. The result equals k3g_moe_layer on the arena
  * with the step's slot ids bit for bit.
  *   y, x: device float [latent] (16-byte aligned); idx: host int32 [top_k],
  *   expert ids (-1 = a dropped entry, K3_TOPP); wts: device float [top_k].
  *   mode: K3G_EXACT on the vector kernels (K3G_DECODE_VECTOR and
- *   K3G_DECODE_LUT allowed); other modes K3G_EUNSUPPORTED.
+ *   K3G_DECODE_LUT allowed), or K3G_IDOT in either form (widths multiples of
+ *   128); K3G_DECODE_MFMA is K3G_EUNSUPPORTED.
  *   ws: a k3g_moe_layer workspace for one token, top_k, the arena's shape and
  *   the same mode (256-byte aligned, ws_bytes >= k3g_workspace_bytes).
  * The host staging of the cache is reused: the call waits for the previous

@@ -36,6 +36,13 @@ int launch_moe_down_exact(float *ypair, const float *h, const BankDev &bank, con
                           bool multi_pairs, bool lut, hipStream_t st);
 int launch_combine(float *y, const float *ypair, const float *wts, const int32_t *inv, int n_tokens, int top_k,
                    int latent, hipStream_t st);
+int launch_quant_i8(int8_t *q, float *s, const float *x, int n_rows, int in, uint16_t *qb, hipStream_t st);
+int launch_moe_up_idot(int8_t *hq, uint16_t *hqb, float *hs, const int8_t *xq, const uint16_t *xqb, const float *xs,
+                       const BankDev &bank, const int32_t *active, const int32_t *offsets, const int32_t *perm,
+                       int top_k, int latent, int inter, int max_slots, hipStream_t st);
+int launch_moe_down_idot(float *ypair, const int8_t *hq, const uint16_t *hqb, const float *hs, const BankDev &bank,
+                         const int32_t *active, const int32_t *offsets, const int32_t *perm, int latent, int inter,
+                         int max_slots, hipStream_t st);
 int device_ok();
 }  // namespace k3g
 
@@ -255,10 +262,13 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
                           int mode, void *ws, size_t ws_bytes, void *copy_stream, void *stream) {
     using namespace k3g;
     if (!c || !c->host_bank || !y || !x || !idx || !wts || !ws || top_k < 1 || top_k > kPipeMax) return K3G_EINVAL;
-    // one token on the vector kernels: EXACT, the LDS table optional
-    if ((mode & ~(K3G_DECODE_LUT | K3G_DECODE_VECTOR)) != K3G_EXACT) return K3G_EUNSUPPORTED;
+    // EXACT on the vector kernels (the LDS table optional), or IDOT in either form;
+    // the FP4 matrix-core form is a layer form and is refused
+    if (mode & K3G_DECODE_MFMA) return K3G_EUNSUPPORTED;
+    const bool idot = (mode & 0xFF) == K3G_IDOT;
     const k3g_expert_bank &A = c->arena;
     const int latent = A.latent, inter = A.inter;
+    if (idot && (latent % 128 || inter % 128)) return K3G_EUNSUPPORTED;
     k3g_shape sh = {1, top_k, A.n_experts, latent, inter, 0, 0, mode};
     k3g_ws_layout L;
     int rc = k3g_workspace_layout(&L, K3G_OP_MOE_LAYER, &sh);
@@ -332,7 +342,11 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
             if (slot[k] == c->step_copies_s[i]) st_inv[k] = next++;
 
     char *w = (char *)ws;
-    float *h = (float *)(w + L.h), *ypair = (float *)(w + L.ypair);
+    float *h = L.h ? (float *)(w + L.h) : nullptr, *ypair = (float *)(w + L.ypair);
+    // IDOT: x quantised per 32-group (and its bf16 copy in that form); h only quantised
+    int8_t *xq = idot ? (int8_t *)(w + L.xq) : nullptr, *hq = L.hq ? (int8_t *)(w + L.hq) : nullptr;
+    float *xs = idot ? (float *)(w + L.xs) : nullptr, *hs = idot ? (float *)(w + L.hs) : nullptr;
+    uint16_t *xqb = L.xqb ? (uint16_t *)(w + L.xqb) : nullptr, *hqb = L.hqb ? (uint16_t *)(w + L.hqb) : nullptr;
     int32_t *inv = (int32_t *)(w + L.inv), *active = (int32_t *)(w + L.active);
     int32_t *offsets = (int32_t *)(w + L.offsets), *perm = (int32_t *)(w + L.perm);
     const bool lut = (mode & K3G_DECODE_LUT) != 0;
@@ -347,6 +361,16 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
         b.base = A.base + (size_t)slot[k] * A.stride;
         b.stride = 0;
         const size_t row = (size_t)st_inv[k];
+        if (idot) {
+            int8_t *hqk = hq ? hq + row * inter : nullptr;
+            uint16_t *hqbk = hqb ? hqb + row * inter : nullptr;
+            float *hsk = hs + row * (inter / kGroup);
+            const int r = launch_moe_up_idot(hqk, hqbk, hsk, xq, xqb, xs, b, nullptr, nullptr, nullptr, 1, latent,
+                                             inter, 1, st);
+            if (r != K3G_OK) return r;
+            return launch_moe_down_idot(ypair + row * latent, hqk, hqbk, hsk, b, nullptr, nullptr, nullptr, latent,
+                                        inter, 1, st);
+        }
         float *hk = h + row * inter;
         const int r = launch_moe_up_exact(hk, x, b, nullptr, nullptr, nullptr, 1, latent, inter, 1, 1, lut, Route1{},
                                           st);
@@ -372,12 +396,19 @@ int k3g_cache_decode_step(k3g_cache *c, float *y, const float *x, const int32_t 
             hipEventRecord(c->ev_pipe[i], cs) != hipSuccess)
             return K3G_EHIP;
     }
+    if (idot && (rc = launch_quant_i8(xq, xs, x, 1, latent, xqb, st)) != K3G_OK) return rc;
     // the staging is read by the table's copies: the next step waits for them
     if (hipStreamWaitEvent(st, c->ev_meta, 0) != hipSuccess || hipEventRecord(c->ev_copy, st) != hipSuccess)
         return K3G_EHIP;
     // the resident experts' pairs in one up and one down launch, then each
     // copied expert's pair once its copy has landed
-    if (n_hit > 0) {
+    if (n_hit > 0 && idot) {
+        if ((rc = launch_moe_up_idot(hq, hqb, hs, xq, xqb, xs, bank, active, offsets, perm, top_k, latent, inter,
+                                     n_hit_slots, st)) != K3G_OK ||
+            (rc = launch_moe_down_idot(ypair, hq, hqb, hs, bank, active, offsets, perm, latent, inter, n_hit_slots,
+                                       st)) != K3G_OK)
+            return rc;
+    } else if (n_hit > 0) {
         if ((rc = launch_moe_up_exact(h, x, bank, active, offsets, perm, top_k, latent, inter, n_hit_slots, n_hit,
                                       lut, Route1{}, st)) != K3G_OK ||
             (rc = launch_moe_down_exact(ypair, h, bank, active, offsets, perm, latent, inter, n_hit_slots, false, lut,

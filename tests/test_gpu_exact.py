@@ -821,7 +821,7 @@ def run_piped_steps(k3g, bankt, bank, n_slots, steps, mode=0):
     return sp
 
 
-@pytest.mark.parametrize("mode", [0, 0x100], ids=["cvt", "lut"])
+@pytest.mark.parametrize("mode", [0, 0x100, 1, 0x1001], ids=["cvt", "lut", "idot_bf16", "idot_int8"])
 def test_cache_decode_step_small(k3g, mode):
     E, latent, inter, K = 24, 256, 128, 4
     src, bankt, bank = make_bank(k3g, 83, E, latent, inter, 120, 123, 0.01)
@@ -836,7 +836,8 @@ def test_cache_decode_step_small(k3g, mode):
     assert stats["evictions"] > 0 and stats["hits"] > 0 and stats["misses"] > 0
 
 
-def test_cache_decode_step_full(k3g, full_bank):
+@pytest.mark.parametrize("mode", [0, 1], ids=["exact", "idot"])
+def test_cache_decode_step_full(k3g, full_bank, mode):
     # one token per step, 896 experts in host memory, 32 slots in HBM
     src, bankt, bank = full_bank
     W, b = synth.router(synth.SEED_BASE + 2, 896, 3584, 0.1)
@@ -846,7 +847,7 @@ def test_cache_decode_step_full(k3g, full_bank):
         idx, wts, _ = oracle.route(x, W, b, 16)
         steps.append((x, idx, wts))
     steps.append(steps[0])
-    stats = run_piped_steps(k3g, bankt, bank, 32, steps)
+    stats = run_piped_steps(k3g, bankt, bank, 32, steps, mode)
     assert stats["misses"] > 0
 
 
@@ -868,8 +869,8 @@ def test_cache_decode_step_refuses(k3g):
     call = lambda idx, mode, nbytes: lib.k3g_cache_decode_step(  # noqa: E731
         cache._c, y.data_ptr(), x.data_ptr(), np.asarray(idx, np.int32).ctypes.data, w.data_ptr(), 2, mode,
         ws.data_ptr(), nbytes, k3g.C.c_void_p(cs.cuda_stream), k3g.C.c_void_p(torch.cuda.current_stream().cuda_stream))
-    assert call([0, 1], k3g.IDOT, ws.numel()) == -5  # K3G_EUNSUPPORTED: the vector kernels only
-    assert call([0, 1], k3g.DECODE_MFMA, ws.numel()) == -5
+    assert call([0, 1], k3g.DECODE_MFMA, ws.numel()) == -5  # K3G_EUNSUPPORTED: a layer form
+    assert call([0, 1], k3g.IDOT | k3g.DECODE_VECTOR, ws.numel()) == -1  # K3G_EINVAL: not a mode
     assert call([0, 9], k3g.EXACT, ws.numel()) == -1  # K3G_EINVAL: an expert id past the host bank
     assert call([0, 1], k3g.EXACT, 0) == -3  # K3G_ENOSPACE: the workspace
     stats, _, _ = cache.query()
