@@ -40,6 +40,8 @@ def lib():
         i = C.c_int
         L.k3o_threads.restype = i
         L.k3o_threads.argtypes = []
+        L.k3o_set_threads.restype = None
+        L.k3o_set_threads.argtypes = [i]
         L.k3o_e2m1.restype = C.c_double
         L.k3o_e2m1.argtypes = [i]
         L.k3o_e2m1_doubled.restype = i
@@ -86,6 +88,11 @@ def _chk(rc, what):
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().k3o_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's later parallel loops (results do not depend on it)."""
+    lib().k3o_set_threads(int(n))
 
 
 # -- format ----------------------------------------------------------------

@@ -45,6 +45,17 @@ int k3o_threads(void)
 #endif
 }
 
+/* Set the threads of the calling thread's later OpenMP regions (n >= 1).
+ * The results do not depend on it: each output is summed by one thread. */
+void k3o_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Format tables, built from the bit-field definitions (never copied).        */
 /* ------------------------------------------------------------------------ */

@@ -39,5 +39,8 @@ def test_bench_line_contract():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     assert cb["nproc"] >= 1 and cb["cpu_model"] and cb["omp_threads"] == cb["cores"]
+    # and the same steps on one thread
+    one = cb["single_thread"]
+    assert one["threads"] == 1 and one["token_steps"] >= 1 and one["value"] > 0
     # a stage that enqueues nothing in this form is null, not a timed empty graph
     assert d["stage_us"]["bucket"] is None and d["stage_us"]["up"] > 0
