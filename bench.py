@@ -175,6 +175,8 @@ def main():
         result["other_workloads"] = others
         # one expert on one token, and the batch-1 product on one w1
         result["expert_b1"] = run_expert(ctx, bankt)
+        if not args.no_cpu_baseline:
+            result["expert_b1"]["cpu_baseline"] = cpu_expert(args, ctx, src)
         # the achievable denominators: matrix-core rates and a streaming read
         result["achievable"] = run_achievable(ctx, launch_bytes=result["roofline"]["algorithmic_bytes_per_launch"])
         ach = result["achievable"]["hbm_read"]["GBps"]
@@ -187,6 +189,8 @@ def main():
         result["launch_costs"] = run_launch_costs(ctx)
         # the full LatentMoE block at 256 tokens, the routed layer in both forms
         result["block_256"] = run_block(ctx, bank)  # the library's default form (FP4 matrix-core layer)
+        if not args.no_cpu_baseline:
+            result["block_256"]["cpu_baseline"] = cpu_block(args, ctx, src)
         result["block_256_vector"] = run_block(ctx, bank, form="vector")
         # the Vulkan-tier scale format: the same product with f32 per-group scales
         result["scale_format"] = run_scale_format(ctx)
@@ -923,6 +927,84 @@ def cpu_baseline(args, src, xs_host, W, b, alg_bytes, T, mode, budget=None, max_
             "kind": "oracle",
             "sample": desc + f"; of a {T}-token batch: the oracle's work is linear in the tokens, so the "
                              f"sample's rate stands for the batch's", "single_thread": one}
+
+
+def cpu_expert(args, ctx, src, n_experts=8):
+    """The oracle's one expert on one token (EXACT), on n_experts of the same
+    experts the GPU line rotates over (drawn beforehand), for a quarter of the
+    CPU time budget on all OpenMP threads and then on one thread: GB/s over
+    the same algorithmic bytes as expert_b1.expert_glu."""
+    import oracle
+
+    synth = ctx["synth"]
+    L, I, E = synth.LATENT, synth.INTER, synth.N_EXPERTS
+    ids = [(i * E) // 64 for i in range(n_experts)]  # the first of the 64 the GPU rotates over
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(16) as pool:
+        experts = list(pool.map(src, ids))
+    x = synth.activations(ctx["seed_bank"], 1, L)[0]
+    up_b, dn_b = expert_bytes(L, I)
+    nbytes = up_b + dn_b + 2 * L * 4
+    budget = args.cpu_seconds / 4
+
+    def timed(limit):
+        spent, n = 0.0, 0
+        while spent < limit or n == 0:
+            t = time.perf_counter()
+            oracle.expert_glu(x, experts[n % len(experts)], oracle.EXACT)
+            spent += time.perf_counter() - t
+            n += 1
+        return spent, n
+
+    spent, n = timed(budget)
+    n_all = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        spent1, n1 = timed(budget / 4)
+    finally:
+        oracle.set_threads(n_all)
+    facts = host_facts()
+    return {"value": round(nbytes * n / spent / 1e9, 3), "unit": "GB/s", "cores": facts["omp_threads"], **facts,
+            "kind": "oracle", "calls_per_s": round(n / spent, 3),
+            "sample": f"{n} calls of the oracle's EXACT expert on one token over {len(experts)} of the rotated "
+                      f"experts, {spent:.1f} s",
+            "single_thread": {"value": round(nbytes * n1 / spent1 / 1e9, 3), "threads": 1, "calls": n1,
+                              "seconds": round(spent1, 2)}}
+
+
+def cpu_block(args, ctx, src, n_tokens=4):
+    """The oracle's whole LatentMoE block (route, down-projection, routed EXACT
+    layer, RMSNorm, up-projection, two shared experts) on the block workload's
+    first n_tokens tokens (their experts drawn beforehand), repeated for a
+    quarter of the CPU time budget on all OpenMP threads: tokens/s. The block's
+    work is per token, so the sample's rate stands for the 256-token batch's."""
+    import oracle
+
+    synth = ctx["synth"]
+    seed, T, bias_range, _ = synth.WORKLOADS["block_256"]
+    H, E, K = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K
+    dense = synth.block_dense(seed)
+    W, b = synth.router(seed, E, H, bias_range)
+    x = synth.activations(seed, T, H)[:n_tokens]
+    io, _, _ = oracle.route(x, W, b, K)
+    from concurrent.futures import ThreadPoolExecutor
+
+    ids = sorted(set(io.ravel().tolist()) - {-1})
+    with ThreadPoolExecutor(16) as pool:
+        experts = dict(zip(ids, pool.map(src, ids)))
+    spent, n = 0.0, 0
+    while spent < args.cpu_seconds / 4 or n == 0:
+        t = time.perf_counter()
+        oracle.latent_block(x, W, b, dense, experts, E, K, oracle.EXACT)
+        spent += time.perf_counter() - t
+        n += 1
+    facts = host_facts()
+    return {"value": round(n * n_tokens / spent, 4), "unit": "tokens/s", "cores": facts["omp_threads"], **facts,
+            "kind": "oracle",
+            "sample": f"{n} runs of the oracle's block on the workload's first {n_tokens} tokens "
+                      f"({len(experts)} distinct experts), {spent:.1f} s; of a {T}-token batch: the block's work "
+                      f"is per token, so the sample's rate stands for the batch's"}
 
 
 if __name__ == "__main__":
