@@ -694,12 +694,16 @@ def test_layer_exact_prefill_4096_sampled(k3g, full_bank):
     assert k3g.workspace_layout(k3g.OP_MOE_LAYER, sh)["passes"]  # the multi-pair FP4 form
     assert 4096 * 16 >= 6 * 896  # eight pairs a pass
     counts = np.bincount(idx.ravel(), minlength=896)
-    # every pair of four experts: the fullest (several passes, the last one
-    # short), the emptiest in use, and two of middling load
+    # every pair of 32 experts: the fullest with a short last pass (several
+    # passes), the next three fullest, the two emptiest in use, and 26 spread
+    # evenly through the load order
     order = np.argsort(counts, kind="stable")
     used = order[counts[order] > 0]
     full = next(int(e) for e in used[::-1] if counts[e] % 8)
-    experts = [full, int(used[0]), int(used[len(used) // 2]), int(used[len(used) // 3])]
+    n = len(used)
+    picks = [full] + [int(e) for e in used[::-1][:4] if int(e) != full][:3] + [int(used[0]), int(used[1])]
+    picks += [int(used[(i * n) // 27]) for i in range(1, 27)]
+    experts = list(dict.fromkeys(picks))
     assert counts[full] > 8
     print(f"checking every pair of experts {experts} ({counts[experts].tolist()} pairs)", flush=True)
     check_layer_exact(k3g, src, None, bank, x, idx, wts, tokens=[0, 2047, 4095], experts=experts)

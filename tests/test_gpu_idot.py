@@ -261,12 +261,16 @@ def test_layer_idot_prefill_4096_sampled(k3g, full_bank):
     print("routing 4096 tokens on the oracle", flush=True)
     idx, wts, _ = oracle.route(x, W, b, 16)
     counts = np.bincount(idx.ravel(), minlength=896)
-    # every pair of four experts: the fullest (past the int8 kernel's 96-token
-    # chunk, so its second chunk and a partial tile are checked), the emptiest
-    # in use, and two of middling load
+    # every pair of 32 experts: the four fullest (the fullest past the int8
+    # kernel's 96-token chunk, so its second chunk and a partial tile are
+    # checked), the two emptiest in use, and 26 spread evenly through the load
+    # order
     order = np.argsort(counts, kind="stable")
     used = order[counts[order] > 0]
-    experts = [int(used[-1]), int(used[0]), int(used[len(used) // 2]), int(used[len(used) // 3])]
+    n = len(used)
+    picks = [int(e) for e in used[::-1][:4]] + [int(used[0]), int(used[1])]
+    picks += [int(used[(i * n) // 27]) for i in range(1, 27)]
+    experts = list(dict.fromkeys(picks))
     assert counts[experts[0]] > 96 and counts[experts[0]] % 16 != 0
     print(f"checking every pair of experts {experts} ({counts[experts].tolist()} pairs)", flush=True)
     check_layer_idot(k3g, src, bank, x, idx, wts, tokens=[0, 2047, 4095], experts=experts)
