@@ -213,4 +213,4 @@ def test_block_full_size_sampled(k3g, full_bank, decode):
     dense = synth.block_dense(seed)
     x = synth.activations(seed, 256, 7168)
     print(f"block 256 form {decode:#x}: checking tokens stage by stage", flush=True)
-    check_block(k3g, src, bank, x, Wr, b, dense, 16, tokens=[*range(0, 256, 8), 255], mode=decode)
+    check_block(k3g, src, bank, x, Wr, b, dense, 16, tokens=[*range(0, 256, 4), 255], mode=decode)
