@@ -38,7 +38,7 @@
 //           group (lane (i, q): dword q of row i) fall in 64 distinct banks.
 //           Each wavefront loads and reads only its own rows.
 //   scales  [tile][row 0..15][4 dwords]: the scale bytes of 16 groups, loaded
-//           once per 8 stages into one of two windows; the tiles ordered
+//           once per 8 blocks into one of two windows; the tiles ordered
 //           (matrix, wavefront, tile within the matrix)
 //   tokens  [token 0..127][8 chunks + 1 pad] (conflict-free 16-byte reads)
 //   s_x     [token 0..127][group 0..1]
@@ -64,7 +64,6 @@ constexpr int SWG = 16;                      // groups per window of staged scal
 constexpr int SW_BYTES = WG_AR * SWG;        // 8 KB: 4 dwords of scale bytes per A row
 constexpr int SW_LD = SW_BYTES / 256 / NW;   // scale-window loads per wavefront: 4
 constexpr int SX_BYTES = NTOK * GB * 4;      // 1 KB
-constexpr int W_LD = W_BYTES / 1024 / NW;    // weight loads per wavefront and stage: 4, one per tile
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
