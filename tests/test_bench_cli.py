@@ -21,3 +21,11 @@ def test_bench_refuses_a_multi_rank_launch():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_bench_refuses_both_idot_forms():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "prefill_4096_idot",
+                        "--idot-int8", "--idot-bf16"], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "different forms" in r.stderr
+    assert r.stdout == ""
