@@ -195,6 +195,13 @@ def check_layer_idot(k3g, src, bank, x, idx, wts, tokens, experts=()):
             acc += w * yp
             nrm += np.abs(w) * np.abs(yp)
         assert_norm_close(yg[t0:t1], acc, nrm, what=f"idot combine tokens {t0}..{t1 - 1}")
+    # every pair's quantised h, whole: each 32-group's largest |q| is 127 with
+    # s > 0 (s = max|h| / 127), or the group is all zero with s = 0
+    hq_all = ws_view(ws, L, "hq", Pv * inter, np.int8).reshape(Pv, inter // 32, 32).astype(np.int32)
+    hs_all = ws_view(ws, L, "hs", Pv * inter // 32, np.float32).reshape(Pv, inter // 32)
+    gmax = np.abs(hq_all).max(axis=2)
+    assert np.all(np.isfinite(hs_all)) and np.all(hs_all >= 0)
+    assert np.all(np.where(hs_all > 0, gmax == 127, gmax == 0)), "a group of h is not quantised to its maximum"
     # the bf16 form computes the same numbers bit for bit (over the pairs that exist)
     yb, wsb, Lb = run_layer_idot(k3g, bank, x, idx, wts, 0x200)
     assert np.array_equal(ws_view(ws, L, "hq", Pv * inter, np.int8),
